@@ -1,0 +1,235 @@
+/*
+ * ls.h — C ABI of the layer-streamed LoRA library (liblsq.so), MI355X / gfx950.
+ *
+ * What the library computes.  A frozen decoder stack lives in pinned host RAM, each
+ * layer either NF4-packed (4-bit codes, one absmax per 64 weights, optionally a
+ * second 8-bit level over the absmax values) or plain bf16.  Every layer is copied
+ * into a small device pool on a dedicated copy stream so that the next layer loads
+ * while the current one computes, and is copied again for the recompute backward
+ * ("Soup: Fine-Tuning an 8B Model on a 4 GB Laptop GPU, One Layer at a Time",
+ * first paragraph; the lachieslifestyle.com Soup how-to, section "What Soup layer
+ * streaming changes"; "Soup CLI fine-tunes Llama-3.1-8B on a 4 GB laptop GPU ...",
+ * second paragraph).  Every projection p in {q,k,v,o,gate,up,down} computes
+ *     Y = X dequant(W_p)^T + (alpha/r) (X A_p^T) B_p^T
+ * and the backward returns dX plus dA_p, dB_p for the trainable adapters
+ * ("Fine-Tuning an 8B Parameter Model on a 4 GB Laptop GPU", section "LoRA and
+ * QLoRA: Train a Fraction of the Parameters").  The layer is the Llama-style
+ * pre-norm decoder (RMSNorm, rotary q/k, causal grouped-query attention, SwiGLU).
+ *
+ * Conventions for every entry point.
+ *  - Plain C types only.  "Device pointer" = memory from hipMalloc (or a torch CUDA
+ *    tensor's data_ptr()) on the context's device; "host pointer" = ordinary memory.
+ *  - bf16 tensors are passed as void* / uint16_t* holding IEEE bfloat16 bit patterns,
+ *    row-major.  Activations are token-major [T, features], T = batch * seq, token
+ *    t = b * seq + s (position s inside its sequence).
+ *  - Weights are [out_features, in_features] row-major.  LoRA A_p is [r, in] and
+ *    B_p is [out, r], both float32.
+ *  - Every call returns an ls_status; no exception crosses the ABI.  A failing call
+ *    leaves a message for ls_last_error().  LS_ERR_HIP is sticky: once a HIP call
+ *    has failed, every later call on that context returns LS_ERR_HIP.
+ *  - Calls on one context must not run concurrently from several host threads.
+ */
+#ifndef LS_H_
+#define LS_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum ls_status {
+  LS_OK = 0,
+  LS_ERR_INVALID = 1, /* bad argument: null pointer, size out of range, bad config */
+  LS_ERR_STATE = 2,   /* call out of order (e.g. backward before forward, unstaged layer) */
+  LS_ERR_BUDGET = 3,  /* the device-memory plan exceeds the budget; nothing allocated */
+  LS_ERR_OOM = 4,     /* an allocation (pinned host or device) failed */
+  LS_ERR_HIP = 5      /* a HIP runtime call or kernel launch failed (sticky) */
+} ls_status;
+
+enum { LS_QUANT_NF4 = 0, LS_QUANT_BF16 = 1 };
+
+/* Projection indices, also the bit positions of ls_config.lora_mask. */
+enum { LS_PROJ_Q = 0, LS_PROJ_K, LS_PROJ_V, LS_PROJ_O, LS_PROJ_GATE, LS_PROJ_UP, LS_PROJ_DOWN, LS_N_PROJ };
+
+/*
+ * Stack description.  Field meaning follows the streaming configuration the
+ * lachieslifestyle.com how-to shows in "Step 5: Enable 4-bit layer streaming"
+ * (quantization 4bit|none, stream_buffers, lora r / alpha / target modules).
+ */
+typedef struct ls_config {
+  int32_t n_layers;        /* >= 1 */
+  int32_t hidden;          /* model width h, multiple of 64 */
+  int32_t n_heads;         /* query heads */
+  int32_t n_kv_heads;      /* key/value heads; n_heads % n_kv_heads == 0 */
+  int32_t head_dim;        /* 64 or 128; n_heads * head_dim and n_kv_heads * head_dim multiples of 64 */
+  int32_t intermediate;    /* SwiGLU width I, multiple of 16 */
+  float rms_eps;           /* RMSNorm epsilon */
+  float rope_theta;        /* rotary base */
+  int32_t quant;           /* LS_QUANT_NF4 or LS_QUANT_BF16 */
+  int32_t nf4_block;       /* must be 64 */
+  int32_t double_quant;    /* NF4 only: 1 = 8-bit absmax codes per group of 256 blocks */
+  int32_t lora_r;          /* 1..64 */
+  float lora_alpha;        /* LoRA scale is lora_alpha / lora_r */
+  uint32_t lora_mask;      /* bit p set = adapter on projection p (bits 0..6) */
+  int32_t n_buffers;       /* device slots in the streaming pool, >= 2 */
+  int32_t max_tokens;      /* upper bound on batch * seq for every call */
+  int32_t max_seq;         /* upper bound on seq (attention scratch is sized by it) */
+  int32_t resident;        /* 1 = keep every layer on the device (same blob layout;
+                              parity reference for the streamed mode) */
+  uint64_t vram_budget;    /* bytes the plan may use; 0 = free device memory */
+  int32_t profile;         /* 1 = time copies and per-layer compute with HIP events */
+} ls_config;
+
+/* Host-side source weights for one layer (bf16 bit patterns, host pointers). */
+typedef struct ls_layer_host {
+  const uint16_t* w[LS_N_PROJ]; /* [out, in] row-major per projection */
+  const uint16_t* g1;           /* [hidden] RMSNorm weight before attention */
+  const uint16_t* g2;           /* [hidden] RMSNorm weight before the MLP */
+} ls_layer_host;
+
+/* Kernel classes timed when ls_config.profile = 1. */
+enum {
+  LS_KC_GEMM_FWD = 0, /* fused dequant GEMM, W orientation (forward and recompute) */
+  LS_KC_GEMM_BWD = 1, /* fused dequant GEMM, W^T orientation (dX) */
+  LS_KC_ATTN = 2,     /* attention products and softmax */
+  LS_KC_LORA = 3,     /* LoRA down projection and dA / dB / G products, operand conversion */
+  LS_KC_GLUE = 4,     /* RMSNorm, rotary embedding, SwiGLU */
+  LS_KC_N = 5
+};
+
+typedef struct ls_stats {
+  uint64_t blob_bytes;         /* bytes of one layer blob (same host and device) */
+  uint64_t store_bytes;        /* pinned host bytes of the whole store */
+  uint64_t device_bytes;       /* device bytes the plan allocated */
+  uint64_t h2d_bytes;          /* host->device layer bytes copied since create */
+  uint64_t h2d_copies;         /* layer copies since create */
+  uint64_t slot_hits;          /* layer reads served by a slot that already held it */
+  double last_copy_ms;         /* profile=1: summed copy time of the last fwd+bwd */
+  double last_compute_ms;      /* profile=1: summed per-layer compute time of last fwd+bwd */
+  double last_overlap_ms;      /* profile=1: copy time that overlapped compute */
+  double last_span_ms;         /* profile=1: first event to last event of last fwd+bwd */
+  /* profile=1, per kernel class, over the last forward (+ backward): launches, summed
+   * launch durations from HIP events on the compute stream, and the algorithmic
+   * FLOPs and bytes of those launches (2*M*N*K per contraction; operands read once,
+   * results written once). */
+  uint64_t k_launches[LS_KC_N];
+  double k_ms[LS_KC_N];
+  double k_flop[LS_KC_N];
+  double k_bytes[LS_KC_N];
+} ls_stats;
+
+typedef struct ls_ctx ls_ctx;
+
+/*
+ * ls_create — validate cfg, plan device memory, refuse if over budget, allocate.
+ *   cfg:            host pointer, read during the call only.
+ *   compute_stream: hipStream_t to run kernels on (NULL: the library makes one).
+ *   copy_stream:    hipStream_t for host->device layer copies (NULL: library makes
+ *                   one).  Must differ from compute_stream.
+ *   out:            receives the context.
+ * The plan is checked against cfg->vram_budget (or the device's free memory when 0)
+ * before any allocation; if it does not fit the call returns LS_ERR_BUDGET and
+ * allocates nothing (the pages' pre-flight refusal of runs that will not fit:
+ * the lachieslifestyle.com how-to, "Step 7: Train and keep the log").  The library
+ * owns the pinned store, the device slots, checkpoints and workspaces.
+ */
+ls_status ls_create(const ls_config* cfg, void* compute_stream, void* copy_stream, ls_ctx** out);
+
+/*
+ * ls_plan_bytes — the device and pinned-host bytes ls_create would allocate for cfg.
+ * Pure host computation, no HIP call.  Returns LS_ERR_INVALID for a bad cfg.
+ */
+ls_status ls_plan_bytes(const ls_config* cfg, uint64_t* device_bytes, uint64_t* host_bytes,
+                        uint64_t* blob_bytes);
+
+/*
+ * ls_stage_layer — encode one layer into the pinned store (NF4 packing with
+ * blockwise absmax and optional double quantisation, or a bf16 copy) on the host
+ * CPU.  Synchronous: the caller's buffers may be freed on return.  A resident
+ * context also copies the blob to its device copy of the layer.
+ * Errors: LS_ERR_INVALID (layer index, null pointer), LS_ERR_STATE (a forward or
+ * backward is in flight: call ls_sync first).
+ */
+ls_status ls_stage_layer(ls_ctx* ctx, int32_t layer, const ls_layer_host* w);
+
+/*
+ * ls_set_lora — register the adapter of (layer, proj).  A [r, in], B [out, r] and
+ * the gradient buffers dA, dB (same shapes) are float32 device pointers owned by the
+ * caller and borrowed until re-set or ls_destroy.  Projections outside lora_mask
+ * need no registration.  dA/dB may be NULL if no gradient is wanted.
+ */
+ls_status ls_set_lora(ls_ctx* ctx, int32_t layer, int32_t proj, const float* A, const float* B,
+                      float* dA, float* dB);
+
+/*
+ * ls_forward — enqueue the streamed forward over all layers on the compute stream.
+ *   X:      device bf16 [batch*seq, hidden], read during the call's GPU work.
+ *   Y:      device bf16 [batch*seq, hidden], the last layer's output.
+ *   lora_on: 0 runs every projection base-only.
+ *   Y_ref:  NULL, or device bf16 [batch*seq, hidden]: also run, per layer and on the
+ *           same streamed slot, the adapters-off reference pass from X (the DPO
+ *           reference model: "Soup CLI fine-tunes Llama-3.1-8B on a 4 GB laptop GPU
+ *           ...", third paragraph).
+ * The layer inputs are kept as bf16 checkpoints for ls_backward.  Asynchronous:
+ * returns after enqueueing.  Errors: LS_ERR_INVALID (sizes beyond max_tokens /
+ * max_seq, null pointers), LS_ERR_STATE (a layer not staged).
+ */
+ls_status ls_forward(ls_ctx* ctx, const void* X, int32_t batch, int32_t seq, int32_t lora_on,
+                     void* Y, void* Y_ref);
+
+/*
+ * ls_backward — enqueue the recompute backward: for l = L-1 .. 0 re-stream layer l,
+ * recompute its forward from the checkpoint, and back-propagate.
+ *   dY: device bf16 [T, hidden] gradient of the last layer's output.
+ *   dX: device bf16 [T, hidden] receives the gradient of the stack input.
+ *   accumulate: 0 = write dA/dB, 1 = add into the registered dA/dB buffers.
+ * Requires a preceding ls_forward with lora_on = 1 on this context (same T), else
+ * LS_ERR_STATE.  Deterministic: no atomics, fixed reduction order.
+ */
+ls_status ls_backward(ls_ctx* ctx, const void* dY, void* dX, int32_t accumulate);
+
+/* ls_sync — wait for both streams; returns the first deferred HIP error. */
+ls_status ls_sync(ls_ctx* ctx);
+
+/* ls_get_stats — counters since ls_create (host pointer out). */
+ls_status ls_get_stats(const ls_ctx* ctx, ls_stats* out);
+
+/* ls_last_error — message of the last failing call on ctx (or of the last failing
+ * ls_create when ctx is NULL).  Valid until the next call on the same context. */
+const char* ls_last_error(const ls_ctx* ctx);
+
+/* ls_destroy — wait for outstanding work and free everything the library owns. */
+void ls_destroy(ls_ctx* ctx);
+
+/*
+ * ls_nf4_codebook — the 16 float32 NF4 levels the library uses, written to out[16]
+ * (host pointer).  Computed on the host from the NormalFloat construction of the
+ * QLoRA paper that "Fine-Tuning an 8B Parameter Model on a 4 GB Laptop GPU",
+ * section "Quantization: Shrink the Weights", names.  No HIP call.
+ */
+void ls_nf4_codebook(float out[16]);
+
+/*
+ * ls_pack_nf4 — the library's host NF4 encoder for one tensor of numel bf16 values
+ * (host pointers; no HIP call).  packed[ceil(numel/2)] receives the nibbles (element
+ * 2k in the high nibble of byte k), absmax[ceil(numel/64)] the float32 block absmax.
+ * If double_quant, qabs[nblocks], scale2[ceil(nblocks/256)] and mean[1] also receive
+ * the second level (qabs/scale2/mean may be NULL otherwise).  n_threads <= 0 picks
+ * the machine's core count (capped at 16).
+ */
+ls_status ls_pack_nf4(const uint16_t* w, uint64_t numel, int32_t double_quant, int32_t n_threads,
+                      uint8_t* packed, float* absmax, uint8_t* qabs, float* scale2, float* mean);
+
+/*
+ * ls_read_weight — dequantise projection proj of a staged layer into device bf16
+ * out [out, in] through the same path the GEMMs use (copy of the blob to a device
+ * slot, then the dequant kernel).  Synchronous.  For checking the encoding.
+ */
+ls_status ls_read_weight(ls_ctx* ctx, int32_t layer, int32_t proj, void* out);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LS_H_ */

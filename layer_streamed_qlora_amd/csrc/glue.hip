@@ -1,0 +1,245 @@
+// Decoder glue around the projections: RMSNorm, rotary embedding, causal softmax,
+// SwiGLU (forward and backward) and small layout conversions of the LoRA operands.
+// All of it is HBM-bound elementwise / row-wise work: one pass over its operands,
+// float32 arithmetic, bf16 in and out.
+//
+// The layer is the Llama-style pre-norm decoder of the families the pages list (the
+// lachieslifestyle.com Soup how-to, section "Step 5: Enable 4-bit layer streaming").
+// RMSNorm: y = x g / sqrt(mean(x^2) + eps).  Rotary embedding in the rotate-half
+// form, angle pos * theta^(-2i/hd) taken from a host-computed table.  silu(z) =
+// z / (1 + exp(-z)).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "lsq_internal.hpp"
+
+namespace lsq {
+namespace {
+
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float bf(uint16_t h) { return __builtin_bit_cast(float, (uint32_t)h << 16); }
+__device__ __forceinline__ uint16_t tobf(float x) {
+  f32x2_t v = {x, 0.f};
+  return (uint16_t)(__builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t)) & 0xFFFFu);
+}
+
+template <int NT>
+__device__ __forceinline__ float block_sum(float v, float* red) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  __syncthreads();
+  if (l == 0) red[w] = v;
+  __syncthreads();
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < NT / 64; ++i) s += red[i];
+  return s;
+}
+
+// one 256-thread block per row
+__global__ void __launch_bounds__(256) k_rmsnorm_fwd(const uint16_t* x, const uint16_t* g, uint16_t* y, float* rstd,
+                                                     int D, float eps) {
+  __shared__ float red[4];
+  const int64_t row = blockIdx.x;
+  const uint16_t* xr = x + row * D;
+  float ss = 0.f;
+  for (int i = threadIdx.x; i < D; i += 256) { const float v = bf(xr[i]); ss += v * v; }
+  ss = block_sum<256>(ss, red);
+  const float r = 1.0f / sqrtf(ss / (float)D + eps);
+  if (threadIdx.x == 0 && rstd) rstd[row] = r;
+  uint16_t* yr = y + row * D;
+  for (int i = threadIdx.x; i < D; i += 256) yr[i] = tobf(bf(xr[i]) * r * bf(g[i]));
+}
+
+// dx = dres + r g dn - (r^3 / D) x sum(dn g x)
+__global__ void __launch_bounds__(256) k_rmsnorm_bwd(const float* dn, const uint16_t* x, const uint16_t* g,
+                                                     const float* rstd, const float* dres32, const uint16_t* dres16,
+                                                     float* dx32, uint16_t* dx16, int D) {
+  __shared__ float red[4];
+  const int64_t row = blockIdx.x;
+  const float* dnr = dn + row * D;
+  const uint16_t* xr = x + row * D;
+  float s = 0.f;
+  for (int i = threadIdx.x; i < D; i += 256) s += dnr[i] * bf(g[i]) * bf(xr[i]);
+  s = block_sum<256>(s, red);
+  const float r = rstd[row];
+  const float c = r * r * r / (float)D * s;
+  for (int i = threadIdx.x; i < D; i += 256) {
+    float v = r * bf(g[i]) * dnr[i] - c * bf(xr[i]);
+    if (dres32) v += dres32[row * D + i];
+    else if (dres16) v += bf(dres16[row * D + i]);
+    if (dx32) dx32[row * D + i] = v;
+    if (dx16) dx16[row * D + i] = tobf(v);
+  }
+}
+
+// x in place; one thread per (token, head, i < hd/2); tab = [seq][hd/2] (cos, sin)
+__global__ void k_rope(uint16_t* qk, int ld, int64_t n, int seq, int nh, int hd, const float2* tab, int inverse) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= n) return;
+  const int half = hd / 2;
+  const int i = (int)(idx % half);
+  const int64_t th = idx / half;
+  const int h = (int)(th % nh);
+  const int64_t t = th / nh;
+  const int pos = (int)(t % seq);
+  const float2 cs = tab[(int64_t)pos * half + i];
+  uint16_t* p = qk + t * ld + (int64_t)h * hd;
+  const float x1 = bf(p[i]), x2 = bf(p[i + half]);
+  float y1, y2;
+  if (!inverse) { y1 = x1 * cs.x - x2 * cs.y; y2 = x2 * cs.x + x1 * cs.y; }
+  else { y1 = x1 * cs.x + x2 * cs.y; y2 = x2 * cs.x - x1 * cs.y; }
+  p[i] = tobf(y1);
+  p[i + half] = tobf(y2);
+}
+
+// one wave per row; row r is query position r % seq of its (batch, head)
+__global__ void __launch_bounds__(256) k_softmax_causal(const float* S, uint16_t* P, int64_t n_rows, int seq) {
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= n_rows) return;
+  const int qi = (int)(row % seq);
+  const float* s = S + row * seq;
+  uint16_t* p = P + row * seq;
+  float mx = -INFINITY;
+  for (int j = lane; j <= qi; j += 64) mx = fmaxf(mx, s[j]);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+  float sum = 0.f;
+  for (int j = lane; j <= qi; j += 64) sum += __expf(s[j] - mx);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o, 64);
+  const float inv = 1.0f / sum;
+  for (int j = lane; j < seq; j += 64) p[j] = j <= qi ? tobf(__expf(s[j] - mx) * inv) : (uint16_t)0;
+}
+
+// dS = scale * P * (dP - sum_j P dP), zero above the diagonal
+__global__ void __launch_bounds__(256) k_softmax_bwd(const float* dP, const uint16_t* P, uint16_t* dS, int64_t n_rows,
+                                                     int seq, float scale) {
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= n_rows) return;
+  const int qi = (int)(row % seq);
+  const float* dp = dP + row * seq;
+  const uint16_t* p = P + row * seq;
+  uint16_t* ds = dS + row * seq;
+  float d = 0.f;
+  for (int j = lane; j <= qi; j += 64) d += bf(p[j]) * dp[j];
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) d += __shfl_xor(d, o, 64);
+  for (int j = lane; j < seq; j += 64) ds[j] = j <= qi ? tobf(scale * bf(p[j]) * (dp[j] - d)) : (uint16_t)0;
+}
+
+__device__ __forceinline__ float sigmoidf(float z) { return 1.0f / (1.0f + __expf(-z)); }
+
+__global__ void k_swiglu_fwd(const uint16_t* gu, int ldgu, int I, uint16_t* act, int64_t n) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= n) return;
+  const int64_t t = idx / I;
+  const int j = (int)(idx % I);
+  const float g = bf(gu[t * ldgu + j]), u = bf(gu[t * ldgu + I + j]);
+  act[t * I + j] = tobf(g * sigmoidf(g) * u);
+}
+
+__global__ void k_swiglu_bwd(const uint16_t* gu, int ldgu, const uint16_t* dact, int I, uint16_t* dgu, int64_t n) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= n) return;
+  const int64_t t = idx / I;
+  const int j = (int)(idx % I);
+  const float g = bf(gu[t * ldgu + j]), u = bf(gu[t * ldgu + I + j]);
+  const float da = bf(dact[t * I + j]);
+  const float sg = sigmoidf(g);
+  dgu[t * ldgu + j] = tobf(da * u * sg * (1.0f + g * (1.0f - sg)));
+  dgu[t * ldgu + I + j] = tobf(da * g * sg);
+}
+
+// dst[r, c] = scale * src[r, c] (transpose: dst[c, r]) for c < cols, 0 for cols <= c < pad_cols
+__global__ void k_f32_to_bf16(const float* src, int64_t lds, uint16_t* dst, int64_t ldd, int rows, int cols,
+                              int pad_cols, float scale, int transpose) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (int64_t)rows * pad_cols) return;
+  const int r = (int)(idx / pad_cols), c = (int)(idx % pad_cols);
+  const uint16_t v = c < cols ? tobf(scale * src[(int64_t)r * lds + c]) : (uint16_t)0;
+  if (transpose) dst[(int64_t)c * ldd + r] = v;
+  else dst[(int64_t)r * ldd + c] = v;
+}
+
+__global__ void k_fill_f32(float* p, int64_t n, float v) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx < n) p[idx] = v;
+}
+
+}  // namespace
+
+static inline unsigned blocks_for(int64_t n, int t) { return (unsigned)((n + t - 1) / t); }
+
+hipError_t launch_rmsnorm_fwd(const uint16_t* x, const uint16_t* g, uint16_t* y, float* rstd, int32_t T, int32_t D,
+                              float eps, hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_rmsnorm_fwd, dim3(T), dim3(256), 0, s, x, g, y, rstd, D, eps);
+  return hipGetLastError();
+}
+
+hipError_t launch_rmsnorm_bwd(const float* dn, const uint16_t* x, const uint16_t* g, const float* rstd,
+                              const float* dres32, const uint16_t* dres16, float* dx32, uint16_t* dx16, int32_t T,
+                              int32_t D, hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_rmsnorm_bwd, dim3(T), dim3(256), 0, s, dn, x, g, rstd, dres32, dres16, dx32, dx16, D);
+  return hipGetLastError();
+}
+
+hipError_t launch_rope_tab(uint16_t* qk, int32_t ld, int32_t T, int32_t seq, int32_t nh, int32_t hd, const float2* tab,
+                           int32_t inverse, hipStream_t s) {
+  const int64_t n = (int64_t)T * nh * (hd / 2);
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_rope, dim3(blocks_for(n, 256)), dim3(256), 0, s, qk, ld, n, seq, nh, hd, tab, inverse);
+  return hipGetLastError();
+}
+
+hipError_t launch_softmax_causal(const float* S, uint16_t* P, int64_t n_rows, int32_t seq, float, hipStream_t s) {
+  if (n_rows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_softmax_causal, dim3(blocks_for(n_rows, 4)), dim3(256), 0, s, S, P, n_rows, seq);
+  return hipGetLastError();
+}
+
+hipError_t launch_softmax_bwd(const float* dP, const uint16_t* P, uint16_t* dS, int64_t n_rows, int32_t seq,
+                              float scale, hipStream_t s) {
+  if (n_rows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_softmax_bwd, dim3(blocks_for(n_rows, 4)), dim3(256), 0, s, dP, P, dS, n_rows, seq, scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_swiglu_fwd(const uint16_t* gu, int32_t ldgu, int32_t I, uint16_t* act, int32_t T, hipStream_t s) {
+  const int64_t n = (int64_t)T * I;
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_swiglu_fwd, dim3(blocks_for(n, 256)), dim3(256), 0, s, gu, ldgu, I, act, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_swiglu_bwd(const uint16_t* gu, int32_t ldgu, const uint16_t* dact, int32_t I, uint16_t* dgu,
+                             int32_t T, hipStream_t s) {
+  const int64_t n = (int64_t)T * I;
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_swiglu_bwd, dim3(blocks_for(n, 256)), dim3(256), 0, s, gu, ldgu, dact, I, dgu, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_f32_to_bf16(const float* src, int64_t lds, uint16_t* dst, int64_t ldd, int32_t rows, int32_t cols,
+                              int32_t pad_cols, float scale, int32_t transpose, hipStream_t s) {
+  const int64_t n = (int64_t)rows * pad_cols;
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_f32_to_bf16, dim3(blocks_for(n, 256)), dim3(256), 0, s, src, lds, dst, ldd, rows, cols, pad_cols,
+                     scale, transpose);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_f32(float* p, int64_t n, float v, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_fill_f32, dim3(blocks_for(n, 256)), dim3(256), 0, s, p, n, v);
+  return hipGetLastError();
+}
+
+}  // namespace lsq

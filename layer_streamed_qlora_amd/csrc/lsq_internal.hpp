@@ -1,0 +1,146 @@
+// Internal declarations shared by the host runtime and the HIP kernels of liblsq.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#include "../../include/ls.h"
+
+namespace lsq {
+
+constexpr int kNF4Block = 64;     // weights per first-level absmax
+constexpr int kDQGroup = 256;     // absmax values per second-level scale
+constexpr int kAlign = 256;       // byte alignment of every piece of a layer blob
+
+inline uint64_t align_up(uint64_t x, uint64_t a) { return (x + a - 1) / a * a; }
+
+// ---------------------------------------------------------------- blob layout
+// One layer blob holds g1, g2 (bf16 [hidden]) and, per projection, either the NF4
+// pieces (packed codes, absmax or qabs+scale2+mean) or the bf16 matrix.  The same
+// layout is used in pinned host memory and in every device slot, so a streamed run
+// and a resident run read identical bytes at identical offsets.
+struct ProjLayout {
+  int32_t n_out = 0, n_in = 0;
+  uint64_t numel = 0, nblocks = 0, ngroups = 0;
+  uint64_t off_w = 0, bytes_w = 0;        // packed codes (NF4) or bf16 matrix
+  uint64_t off_absmax = 0;                // float32 [nblocks]   (NF4, no DQ)
+  uint64_t off_qabs = 0;                  // uint8  [nblocks]   (NF4 + DQ)
+  uint64_t off_scale2 = 0;                // float32 [ngroups]  (NF4 + DQ)
+  uint64_t off_mean = 0;                  // float32 [1]        (NF4 + DQ)
+};
+
+struct BlobLayout {
+  uint64_t off_g1 = 0, off_g2 = 0;
+  ProjLayout p[LS_N_PROJ];
+  uint64_t bytes = 0;
+};
+
+bool validate_config(const ls_config& c, const char** why);
+BlobLayout make_layout(const ls_config& c);
+void proj_dims(const ls_config& c, int proj, int32_t* n_out, int32_t* n_in);
+
+// ------------------------------------------------------------- host encoders
+void nf4_codebook_host(float out[16]);
+void pack_nf4_host(const uint16_t* w, uint64_t numel, bool double_quant, int n_threads,
+                   uint8_t* packed, float* absmax, uint8_t* qabs, float* scale2, float* mean);
+
+// ------------------------------------------------------------ kernel launches
+// All launches are asynchronous on `s` and return hipGetLastError().
+
+// Weight description handed to the fused dequant GEMMs (device pointers into a slot).
+struct WeightRef {
+  const uint8_t* w = nullptr;       // NF4 packed codes or bf16 matrix
+  const float* absmax = nullptr;    // NF4 without DQ
+  const uint8_t* qabs = nullptr;    // NF4 with DQ
+  const float* scale2 = nullptr;
+  const float* mean = nullptr;
+  int32_t n_out = 0, n_in = 0;
+};
+
+enum WFormat { WF_NF4 = 0, WF_NF4_DQ = 1, WF_BF16 = 2 };
+
+constexpr int kMaxGroups = 3;
+
+// Y[:, col0_g : col0_g + n_out_g] = X W_g^T + Aext[:, acol_g : acol_g + kx] Bext_g^T (+ R)
+// for up to three weights g that share the input X [M, K] (K = n_in of every g).
+struct FwdGroup {
+  WeightRef w;
+  int32_t out_col0 = 0;            // first output column of this group
+  int32_t ext_col0 = 0;            // first column of this group's extension operand in Aext
+  const uint16_t* bext = nullptr;  // bf16 [n_out, kx]: LoRA B (already in bf16), row stride kx
+};
+struct FwdArgs {
+  const uint16_t* x = nullptr; int32_t ldx = 0;     // bf16 [M, K]
+  int32_t M = 0, K = 0;
+  int32_t n_groups = 0;
+  FwdGroup g[kMaxGroups];
+  const uint16_t* aext = nullptr; int32_t ldaext = 0; int32_t kx = 0;   // bf16 [M, >=kx]; kx multiple of 16, 0 = none
+  const uint16_t* resid = nullptr; int32_t ldr = 0; // bf16 residual added to Y (nullable)
+  uint16_t* y = nullptr; int32_t ldy = 0;           // bf16 output
+  const float* levels = nullptr;                    // device float32[16] NF4 levels
+  int32_t format = WF_NF4;
+};
+hipError_t launch_gemm_fwd(const FwdArgs& a, hipStream_t s);
+
+// dX[M, N] = sum_g dY[:, acol_g : acol_g + n_out_g] W_g + Aext Bext^T, contraction over
+// the stacked n_out of up to three weights sharing n_in = N.
+struct BwdSeg {
+  WeightRef w;
+  int32_t a_col0 = 0;              // first column of this segment in dY
+};
+struct BwdArgs {
+  const uint16_t* dy = nullptr; int32_t lddy = 0;   // bf16 [M, sum n_out]
+  int32_t M = 0, N = 0;                             // N = n_in shared by the segments
+  int32_t n_segs = 0;
+  BwdSeg seg[kMaxGroups];
+  const uint16_t* aext = nullptr; int32_t ldaext = 0; int32_t kx = 0;   // bf16 [M, kx]
+  const uint16_t* bext = nullptr; int32_t ldbext = 0;                   // bf16 [N, kx]
+  float* out32 = nullptr; uint16_t* out16 = nullptr; int32_t ldo = 0;  // exactly one set
+  const float* levels = nullptr;
+  int32_t format = WF_NF4;
+};
+hipError_t launch_gemm_bwd(const BwdArgs& a, hipStream_t s);
+
+// Generic batched bf16 MFMA GEMM: C(m,n) = alpha * sum_k A(m,k) B(n,k) + beta * C(m,n).
+// Element addresses: A + zoffA + m*sAm + k*sAk with sAk == 1 (A_K) or sAm == 1 (A_M);
+// likewise B.  Batch z in [0, nz): zoff = (z / zdiv) * s1 + ((z % zdiv) / zgrp) * s2.
+struct ZStride { int64_t s1 = 0, s2 = 0; int32_t grp = 1; };
+struct GemmArgs {
+  const uint16_t* A = nullptr; int64_t sAm = 0, sAk = 0; ZStride zA;
+  const uint16_t* B = nullptr; int64_t sBn = 0, sBk = 0; ZStride zB;
+  void* C = nullptr; int64_t sCm = 0, sCn = 0; ZStride zC; int32_t c_f32 = 1;
+  int32_t M = 0, N = 0, K = 0, nz = 1, zdiv = 1;
+  float alpha = 1.f, beta = 0.f;
+  int32_t causal = 0;   // 1: skip tiles with n0 > m_last (C rows m, cols n); 2: limit k <= m_last
+};
+hipError_t launch_gemm_generic(const GemmArgs& a, hipStream_t s);
+
+// Glue kernels.
+hipError_t launch_rmsnorm_fwd(const uint16_t* x, const uint16_t* g, uint16_t* y, float* rstd,
+                              int32_t T, int32_t D, float eps, hipStream_t s);
+// dx = dres + rmsnorm_bwd(dn); writes float32 and/or bf16 (either may be null)
+hipError_t launch_rmsnorm_bwd(const float* dn, const uint16_t* x, const uint16_t* g, const float* rstd,
+                              const float* dres32, const uint16_t* dres16, float* dx32, uint16_t* dx16,
+                              int32_t T, int32_t D, hipStream_t s);
+// rotary embedding in place on the first nh heads of a token-major [T, ld] bf16
+// buffer; tab[pos * hd/2 + i] = (cos, sin) of pos * theta^(-2i/hd)
+hipError_t launch_rope_tab(uint16_t* qk, int32_t ld, int32_t T, int32_t seq, int32_t nh, int32_t hd,
+                           const float2* tab, int32_t inverse, hipStream_t s);
+hipError_t launch_fill_f32(float* p, int64_t n, float v, hipStream_t s);
+hipError_t gemm_dequant_init();
+// causal softmax over rows of S (float32 [rows, S]) -> P bf16; rows = nz * seq
+hipError_t launch_softmax_causal(const float* S, uint16_t* P, int64_t n_rows, int32_t seq, float scale,
+                                 hipStream_t s);
+// dS = P * (dP - rowsum(P * dP)) * scale, bf16 out; dP float32, P bf16
+hipError_t launch_softmax_bwd(const float* dP, const uint16_t* P, uint16_t* dS, int64_t n_rows, int32_t seq,
+                              float scale, hipStream_t s);
+hipError_t launch_swiglu_fwd(const uint16_t* gu, int32_t ldgu, int32_t I, uint16_t* act, int32_t T, hipStream_t s);
+hipError_t launch_swiglu_bwd(const uint16_t* gu, int32_t ldgu, const uint16_t* dact, int32_t I,
+                             uint16_t* dgu, int32_t T, hipStream_t s);
+// float32 [rows, cols] (row stride lds) -> bf16 [rows, ldd] scaled, columns >= cols zero up to ldd
+hipError_t launch_f32_to_bf16(const float* src, int64_t lds, uint16_t* dst, int64_t ldd, int32_t rows,
+                              int32_t cols, int32_t pad_cols, float scale, int32_t transpose, hipStream_t s);
+hipError_t launch_dequant(const WeightRef& w, int32_t format, const float* levels, uint16_t* out, hipStream_t s);
+
+}  // namespace lsq

@@ -1,0 +1,1052 @@
+// Host runtime of liblsq: pinned layer store, the device slot pool with its copy
+// stream and event fencing, the per-layer executor (forward, adapters-off reference
+// pass, recompute backward) and the C ABI declared in include/ls.h.
+//
+// What is streamed and when follows the pages: the frozen base stays in host RAM and
+// each decoder layer is copied into a two-buffer device pool so the next layer loads
+// while the current one computes; backward reads every layer again for the
+// checkpoint recomputation (the lachieslifestyle.com Soup how-to, section "What Soup
+// layer streaming changes"); the copies run on a dedicated stream and peak device
+// memory is bounded by one layer's worth of weights per slot ("Soup CLI fine-tunes
+// Llama-3.1-8B on a 4 GB laptop GPU ...", second paragraph); the DPO reference is the
+// same streamed layer with the adapters off (same page, third paragraph).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <array>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "lsq_internal.hpp"
+
+using namespace lsq;
+
+namespace {
+
+constexpr int kPad = 256;    // slack after every workspace region (8-element group loads)
+
+struct LoraReg {
+  const float* A = nullptr;
+  const float* B = nullptr;
+  float* dA = nullptr;
+  float* dB = nullptr;
+};
+
+// Byte offsets of every device region; the same function sizes the plan for
+// ls_plan_bytes and carves the single device allocation in ls_create.
+struct DevPlan {
+  uint64_t total = 0;
+  uint64_t slots = 0, ck = 0, xref = 0;
+  uint64_t n1 = 0, qkv = 0, att = 0, hb = 0, n2 = 0, gu = 0, act = 0, rstd1 = 0, rstd2 = 0;
+  uint64_t hs = 0, gs = 0, s32 = 0, p16 = 0, ds16 = 0;
+  uint64_t dya = 0, dyb = 0, dh32 = 0, dh16 = 0, dact = 0, dgu = 0, datt = 0, dqkv = 0, dn32 = 0;
+  uint64_t lora = 0, lora_per_layer = 0;
+  uint64_t levels = 0, rope = 0;
+  // per-layer LoRA operand offsets (relative to the layer's LoRA base)
+  uint64_t a16[LS_N_PROJ] = {}, bx16[LS_N_PROJ] = {};
+  uint64_t at_qkv = 0, at_o = 0, at_gu = 0, at_d = 0;
+  int n_slots = 0;
+};
+
+inline int r16_of(const ls_config& c) { return (c.lora_r + 15) / 16 * 16; }
+
+DevPlan make_plan(const ls_config& c, const BlobLayout& L) {
+  DevPlan P;
+  uint64_t off = 0;
+  auto take = [&](uint64_t bytes) { off = align_up(off, kAlign); uint64_t o = off; off += bytes + kPad; return o; };
+  const uint64_t T = (uint64_t)c.max_tokens, h = c.hidden, I = c.intermediate;
+  const uint64_t qd = (uint64_t)c.n_heads * c.head_dim, kvd = (uint64_t)c.n_kv_heads * c.head_dim;
+  const uint64_t qkvd = qd + 2 * kvd;
+  const uint64_t r16 = r16_of(c), R7 = 7 * r16;
+  const uint64_t att_elems = T * (uint64_t)c.n_heads * (uint64_t)c.max_seq;
+  P.n_slots = c.resident ? c.n_layers : c.n_buffers;
+  P.slots = take(L.bytes * (uint64_t)P.n_slots);
+  P.ck = take(2 * T * h * (uint64_t)c.n_layers);
+  P.xref = take(2 * 2 * T * h);
+  P.n1 = take(2 * T * h);
+  P.qkv = take(2 * T * qkvd);
+  P.att = take(2 * T * qd);
+  P.hb = take(2 * T * h);
+  P.n2 = take(2 * T * h);
+  P.gu = take(2 * T * 2 * I);
+  P.act = take(2 * T * I);
+  P.rstd1 = take(4 * T);
+  P.rstd2 = take(4 * T);
+  P.hs = take(2 * T * R7);
+  P.gs = take(2 * T * R7);
+  P.s32 = take(4 * att_elems);
+  P.p16 = take(2 * att_elems);
+  P.ds16 = take(2 * att_elems);
+  P.dya = take(2 * T * h);
+  P.dyb = take(2 * T * h);
+  P.dh32 = take(4 * T * h);
+  P.dh16 = take(2 * T * h);
+  P.dact = take(2 * T * I);
+  P.dgu = take(2 * T * 2 * I);
+  P.datt = take(2 * T * qd);
+  P.dqkv = take(2 * T * qkvd);
+  P.dn32 = take(4 * T * (std::max(h, qd)));
+  // LoRA operands in bf16, per layer
+  uint64_t lo = 0;
+  auto ltake = [&](uint64_t bytes) { lo = align_up(lo, kAlign); uint64_t o = lo; lo += bytes + kPad; return o; };
+  // A16 of projections that share an input are stacked contiguously, so one GEMM
+  // computes the whole group's s*X*A^T: [q|k|v] and [gate|up] are [n*r16, n_in].
+  P.a16[LS_PROJ_Q] = ltake(2 * 3 * r16 * h);
+  P.a16[LS_PROJ_K] = P.a16[LS_PROJ_Q] + 2 * r16 * h;
+  P.a16[LS_PROJ_V] = P.a16[LS_PROJ_Q] + 4 * r16 * h;
+  P.a16[LS_PROJ_O] = ltake(2 * r16 * qd);
+  P.a16[LS_PROJ_GATE] = ltake(2 * 2 * r16 * h);
+  P.a16[LS_PROJ_UP] = P.a16[LS_PROJ_GATE] + 2 * r16 * h;
+  P.a16[LS_PROJ_DOWN] = ltake(2 * r16 * I);
+  for (int p = 0; p < LS_N_PROJ; ++p) {
+    int32_t n_out, n_in;
+    proj_dims(c, p, &n_out, &n_in);
+    P.bx16[p] = ltake(2 * (uint64_t)n_out * r16);
+  }
+  // A^T stacked per group, [n_in, group_r16]: q|k|v, o, gate|up, down
+  P.at_qkv = ltake(2 * h * 3 * r16);
+  P.at_o = ltake(2 * qd * r16);
+  P.at_gu = ltake(2 * h * 2 * r16);
+  P.at_d = ltake(2 * I * r16);
+  P.lora_per_layer = align_up(lo, kAlign);
+  P.lora = take(P.lora_per_layer * (uint64_t)c.n_layers);
+  P.levels = take(64);
+  P.rope = take(8ull * (uint64_t)c.max_seq * (uint64_t)(c.head_dim / 2));
+  P.total = align_up(off, kAlign);
+  return P;
+}
+
+// Event-pair recorder for profile = 1.
+struct Prof {
+  std::vector<hipEvent_t> pool;
+  size_t used = 0;
+  struct KRec { int cls; size_t e0, e1; double flop, bytes; };
+  std::vector<KRec> krecs;
+  std::vector<std::pair<size_t, size_t>> copies, computes;
+  size_t origin = (size_t)-1;
+  hipError_t next(hipEvent_t* ev, size_t* idx) {
+    if (used == pool.size()) {
+      hipEvent_t e;
+      hipError_t r = hipEventCreate(&e);
+      if (r != hipSuccess) return r;
+      pool.push_back(e);
+    }
+    *idx = used;
+    *ev = pool[used++];
+    return hipSuccess;
+  }
+  void reset() { used = 0; krecs.clear(); copies.clear(); computes.clear(); origin = (size_t)-1; }
+};
+
+}  // namespace
+
+struct ls_ctx {
+  ls_config cfg{};
+  BlobLayout lay;
+  DevPlan plan;
+  int device = 0;
+  hipStream_t cs = nullptr, ps = nullptr;
+  bool own_cs = false, own_ps = false;
+  std::vector<uint8_t*> host;
+  std::vector<char> staged;
+  uint8_t* dbase = nullptr;
+  std::vector<int> slot_layer;
+  std::vector<hipEvent_t> ready, consumed;
+  std::vector<char> ready_rec, cons_rec;
+  std::vector<std::array<LoraReg, LS_N_PROJ>> lora;
+  float levels_h[16];
+  // state
+  bool fwd_valid = false, fwd_lora = false;
+  int fwd_T = 0, fwd_batch = 0, fwd_seq = 0;
+  bool in_flight = false;
+  ls_status sticky = LS_OK;
+  std::string err;
+  ls_stats stats{};
+  Prof prof;
+
+  template <class T> T* dp(uint64_t off) const { return reinterpret_cast<T*>(dbase + off); }
+};
+
+static std::string g_create_err;
+
+static ls_status fail(ls_ctx* c, ls_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  if (c) {
+    c->err = buf;
+    if (st == LS_ERR_HIP) c->sticky = LS_ERR_HIP;
+  } else {
+    g_create_err = buf;
+  }
+  return st;
+}
+
+#define HIPCHK(ctx, expr)                                                                    \
+  do {                                                                                       \
+    hipError_t _e = (expr);                                                                  \
+    if (_e != hipSuccess) return fail((ctx), LS_ERR_HIP, "%s failed: %s", #expr, hipGetErrorString(_e)); \
+  } while (0)
+
+// ------------------------------------------------------------------ profiling
+namespace {
+
+struct KTimer {
+  ls_ctx* c;
+  int cls;
+  double flop, bytes;
+  size_t i0 = 0;
+  bool on;
+  KTimer(ls_ctx* ctx, int k, double f, double b) : c(ctx), cls(k), flop(f), bytes(b), on(ctx->cfg.profile != 0) {
+    if (on) {
+      hipEvent_t e;
+      if (c->prof.next(&e, &i0) == hipSuccess) hipEventRecord(e, c->cs); else on = false;
+    }
+  }
+  ~KTimer() {
+    if (!on) return;
+    hipEvent_t e;
+    size_t i1;
+    if (c->prof.next(&e, &i1) == hipSuccess) {
+      hipEventRecord(e, c->cs);
+      c->prof.krecs.push_back({cls, i0, i1, flop, bytes});
+    }
+  }
+};
+
+struct Span {   // copy or per-layer compute interval
+  ls_ctx* c;
+  hipStream_t s;
+  bool copy;
+  size_t i0 = 0;
+  bool on;
+  Span(ls_ctx* ctx, hipStream_t st, bool is_copy) : c(ctx), s(st), copy(is_copy), on(ctx->cfg.profile != 0) {
+    if (on) {
+      hipEvent_t e;
+      if (c->prof.next(&e, &i0) == hipSuccess) {
+        if (c->prof.origin == (size_t)-1) c->prof.origin = i0;
+        hipEventRecord(e, s);
+      } else {
+        on = false;
+      }
+    }
+  }
+  ~Span() {
+    if (!on) return;
+    hipEvent_t e;
+    size_t i1;
+    if (c->prof.next(&e, &i1) == hipSuccess) {
+      hipEventRecord(e, s);
+      (copy ? c->prof.copies : c->prof.computes).push_back({i0, i1});
+    }
+  }
+};
+
+void collect_profile(ls_ctx* c) {
+  Prof& P = c->prof;
+  for (int k = 0; k < LS_KC_N; ++k) {
+    c->stats.k_launches[k] = 0;
+    c->stats.k_ms[k] = c->stats.k_flop[k] = c->stats.k_bytes[k] = 0.0;
+  }
+  c->stats.last_copy_ms = c->stats.last_compute_ms = c->stats.last_overlap_ms = c->stats.last_span_ms = 0.0;
+  if (!c->cfg.profile || P.origin == (size_t)-1) return;
+  auto el = [&](size_t a, size_t b) {
+    float ms = 0.f;
+    hipEventElapsedTime(&ms, P.pool[a], P.pool[b]);
+    return (double)ms;
+  };
+  for (const auto& r : P.krecs) {
+    c->stats.k_launches[r.cls] += 1;
+    c->stats.k_ms[r.cls] += el(r.e0, r.e1);
+    c->stats.k_flop[r.cls] += r.flop;
+    c->stats.k_bytes[r.cls] += r.bytes;
+  }
+  std::vector<std::pair<double, double>> cp, cm;
+  double last = 0.0;
+  for (auto& iv : P.copies) { cp.push_back({el(P.origin, iv.first), el(P.origin, iv.second)}); last = std::max(last, cp.back().second); }
+  for (auto& iv : P.computes) { cm.push_back({el(P.origin, iv.first), el(P.origin, iv.second)}); last = std::max(last, cm.back().second); }
+  double cps = 0, cms = 0, ov = 0;
+  for (auto& a : cp) cps += a.second - a.first;
+  for (auto& a : cm) cms += a.second - a.first;
+  for (auto& a : cp)
+    for (auto& b : cm) {
+      const double lo = std::max(a.first, b.first), hi = std::min(a.second, b.second);
+      if (hi > lo) ov += hi - lo;
+    }
+  c->stats.last_copy_ms = cps;
+  c->stats.last_compute_ms = cms;
+  c->stats.last_overlap_ms = ov;
+  c->stats.last_span_ms = last;
+}
+
+// ------------------------------------------------------------------ pool
+uint8_t* slot_ptr(ls_ctx* c, int layer) {
+  const int s = c->cfg.resident ? layer : layer % c->cfg.n_buffers;
+  return c->dbase + c->plan.slots + (uint64_t)s * c->lay.bytes;
+}
+
+// Enqueue on the copy stream: bring layer l into its slot unless the slot still holds it.
+ls_status ensure_copy(ls_ctx* c, int l) {
+  if (c->cfg.resident) return LS_OK;
+  const int s = l % c->cfg.n_buffers;
+  if (c->slot_layer[s] == l) { c->stats.slot_hits++; return LS_OK; }
+  if (c->cons_rec[s]) HIPCHK(c, hipStreamWaitEvent(c->ps, c->consumed[s], 0));
+  {
+    Span sp(c, c->ps, true);
+    HIPCHK(c, hipMemcpyAsync(slot_ptr(c, l), c->host[l], c->lay.bytes, hipMemcpyHostToDevice, c->ps));
+  }
+  HIPCHK(c, hipEventRecord(c->ready[s], c->ps));
+  c->ready_rec[s] = 1;
+  c->slot_layer[s] = l;
+  c->stats.h2d_bytes += c->lay.bytes;
+  c->stats.h2d_copies += 1;
+  return LS_OK;
+}
+
+ls_status use_layer(ls_ctx* c, int l) {
+  if (c->cfg.resident) return LS_OK;
+  const int s = l % c->cfg.n_buffers;
+  if (c->ready_rec[s]) HIPCHK(c, hipStreamWaitEvent(c->cs, c->ready[s], 0));
+  return LS_OK;
+}
+
+ls_status release_layer(ls_ctx* c, int l) {
+  if (c->cfg.resident) return LS_OK;
+  const int s = l % c->cfg.n_buffers;
+  HIPCHK(c, hipEventRecord(c->consumed[s], c->cs));
+  c->cons_rec[s] = 1;
+  return LS_OK;
+}
+
+// ------------------------------------------------------------------ executor
+struct Dims {
+  int T, batch, seq, h, hq, hkv, hd, qd, kvd, qkvd, I, r, r16, R7;
+  float s;
+};
+
+Dims dims_of(const ls_ctx* c, int batch, int seq) {
+  Dims d;
+  const ls_config& g = c->cfg;
+  d.T = batch * seq; d.batch = batch; d.seq = seq;
+  d.h = g.hidden; d.hq = g.n_heads; d.hkv = g.n_kv_heads; d.hd = g.head_dim;
+  d.qd = d.hq * d.hd; d.kvd = d.hkv * d.hd; d.qkvd = d.qd + 2 * d.kvd;
+  d.I = g.intermediate; d.r = g.lora_r; d.r16 = r16_of(g); d.R7 = 7 * d.r16;
+  d.s = g.lora_alpha / (float)g.lora_r;
+  return d;
+}
+
+int wformat(const ls_config& c) {
+  if (c.quant == LS_QUANT_BF16) return WF_BF16;
+  return c.double_quant ? WF_NF4_DQ : WF_NF4;
+}
+
+WeightRef wref(const ls_ctx* c, const uint8_t* blob, int p) {
+  const ProjLayout& P = c->lay.p[p];
+  WeightRef w;
+  w.w = blob + P.off_w;
+  if (c->cfg.quant == LS_QUANT_NF4) {
+    if (c->cfg.double_quant) {
+      w.qabs = blob + P.off_qabs;
+      w.scale2 = reinterpret_cast<const float*>(blob + P.off_scale2);
+      w.mean = reinterpret_cast<const float*>(blob + P.off_mean);
+    } else {
+      w.absmax = reinterpret_cast<const float*>(blob + P.off_absmax);
+    }
+  }
+  w.n_out = P.n_out;
+  w.n_in = P.n_in;
+  return w;
+}
+
+bool lora_active(const ls_ctx* c, int l, int p) {
+  return ((c->cfg.lora_mask >> p) & 1u) && c->lora[l][p].A && c->lora[l][p].B;
+}
+
+uint16_t* lora_base(ls_ctx* c, int l) { return c->dp<uint16_t>(c->plan.lora + (uint64_t)l * c->plan.lora_per_layer); }
+uint16_t* lora_at(ls_ctx* c, int l, uint64_t off) { return reinterpret_cast<uint16_t*>(reinterpret_cast<uint8_t*>(lora_base(c, l)) + off); }
+
+double wbytes(const ls_ctx* c, int p) {   // stored bytes of projection p in a blob
+  const ProjLayout& P = c->lay.p[p];
+  if (c->cfg.quant == LS_QUANT_BF16) return (double)P.bytes_w;
+  return (double)P.bytes_w + (c->cfg.double_quant ? (double)P.nblocks + 4.0 * P.ngroups : 4.0 * P.nblocks);
+}
+
+// bf16 copies of the adapters: A16 [r16, in], Bx16 [out, r16], A^T stacked per group.
+ls_status prep_lora(ls_ctx* c, int l, const Dims& d) {
+  const int gcol[LS_N_PROJ] = {0, 1, 2, 0, 0, 1, 0};
+  const uint64_t at_off[LS_N_PROJ] = {c->plan.at_qkv, c->plan.at_qkv, c->plan.at_qkv, c->plan.at_o,
+                                      c->plan.at_gu, c->plan.at_gu, c->plan.at_d};
+  const int gsize[LS_N_PROJ] = {3, 3, 3, 1, 2, 2, 1};
+  for (int p = 0; p < LS_N_PROJ; ++p) {
+    if (!lora_active(c, l, p)) continue;
+    const ProjLayout& P = c->lay.p[p];
+    const LoraReg& R = c->lora[l][p];
+    KTimer kt(c, LS_KC_LORA, 0.0, 4.0 * d.r * ((double)P.n_in + P.n_out) + 2.0 * 3 * d.r * ((double)P.n_in + P.n_out));
+    HIPCHK(c, launch_f32_to_bf16(R.A, P.n_in, lora_at(c, l, c->plan.a16[p]), P.n_in, d.r, P.n_in, P.n_in, 1.f, 0, c->cs));
+    HIPCHK(c, launch_f32_to_bf16(R.B, d.r, lora_at(c, l, c->plan.bx16[p]), d.r16, P.n_out, d.r, d.r16, 1.f, 0, c->cs));
+    HIPCHK(c, launch_f32_to_bf16(R.A, P.n_in, lora_at(c, l, at_off[p]) + gcol[p] * d.r16, (int64_t)gsize[p] * d.r16,
+                                 d.r, P.n_in, P.n_in, 1.f, 1, c->cs));
+  }
+  return LS_OK;
+}
+
+// Hs[:, col0 .. col0 + ng*r16) = s * X A_group^T
+ls_status lora_down(ls_ctx* c, int l, const Dims& d, const uint16_t* x, int ldx, int p0, int ng, int K) {
+  bool any = false;
+  for (int p = p0; p < p0 + ng; ++p) any |= lora_active(c, l, p);
+  if (!any) return LS_OK;
+  GemmArgs g;
+  g.A = x; g.sAm = ldx; g.sAk = 1;
+  g.B = lora_at(c, l, c->plan.a16[p0]); g.sBn = K; g.sBk = 1;
+  g.C = c->dp<uint16_t>(c->plan.hs) + p0 * d.r16; g.sCm = d.R7; g.sCn = 1; g.c_f32 = 0;
+  g.M = d.T; g.N = ng * d.r16; g.K = K; g.alpha = d.s;
+  KTimer kt(c, LS_KC_LORA, 2.0 * d.T * ng * d.r * K, 2.0 * d.T * K + 2.0 * ng * d.r * K + 2.0 * d.T * ng * d.r);
+  HIPCHK(c, launch_gemm_generic(g, c->cs));
+  return LS_OK;
+}
+
+double fwd_gemm_flop(const Dims& d, int n_out, int K, bool lora) { return 2.0 * d.T * n_out * K + (lora ? 2.0 * d.T * n_out * d.r : 0.0); }
+
+// Materialised causal attention forward: S = c Q K^T, P = softmax(S), O = P V.
+ls_status attn_fwd(ls_ctx* c, const Dims& d, const uint16_t* qkv, uint16_t* out) {
+  const int S = d.seq, nrep = d.hq / d.hkv;
+  const float scale = 1.0f / std::sqrt((float)d.hd);
+  const int64_t SS = (int64_t)S * S;
+  float* s32 = c->dp<float>(c->plan.s32);
+  uint16_t* p16 = c->dp<uint16_t>(c->plan.p16);
+  const double fl = 2.0 * d.batch * d.hq * (double)S * (S + 1) / 2 * d.hd;
+  {
+    GemmArgs g;
+    g.A = qkv; g.sAm = d.qkvd; g.sAk = 1; g.zA = {(int64_t)S * d.qkvd, d.hd, 1};
+    g.B = qkv + d.qd; g.sBn = d.qkvd; g.sBk = 1; g.zB = {(int64_t)S * d.qkvd, d.hd, nrep};
+    g.C = s32; g.sCm = S; g.sCn = 1; g.zC = {(int64_t)d.hq * SS, SS, 1}; g.c_f32 = 1;
+    g.M = S; g.N = S; g.K = d.hd; g.nz = d.batch * d.hq; g.zdiv = d.hq; g.alpha = scale; g.causal = 1;
+    KTimer kt(c, LS_KC_ATTN, fl, 2.0 * d.T * (d.qd + d.kvd) + 4.0 * d.batch * d.hq * SS / 2);
+    HIPCHK(c, launch_gemm_generic(g, c->cs));
+  }
+  {
+    KTimer kt(c, LS_KC_ATTN, 0.0, 6.0 * d.batch * d.hq * SS / 2);
+    HIPCHK(c, launch_softmax_causal(s32, p16, (int64_t)d.batch * d.hq * S, S, 1.f, c->cs));
+  }
+  {
+    GemmArgs g;
+    g.A = p16; g.sAm = S; g.sAk = 1; g.zA = {(int64_t)d.hq * SS, SS, 1};
+    g.B = qkv + d.qd + d.kvd; g.sBn = 1; g.sBk = d.qkvd; g.zB = {(int64_t)S * d.qkvd, d.hd, nrep};
+    g.C = out; g.sCm = d.qd; g.sCn = 1; g.zC = {(int64_t)S * d.qd, d.hd, 1}; g.c_f32 = 0;
+    g.M = S; g.N = d.hd; g.K = S; g.nz = d.batch * d.hq; g.zdiv = d.hq; g.causal = 2;
+    KTimer kt(c, LS_KC_ATTN, fl, 2.0 * d.batch * d.hq * SS / 2 + 2.0 * d.T * (d.kvd + d.qd));
+    HIPCHK(c, launch_gemm_generic(g, c->cs));
+  }
+  return LS_OK;
+}
+
+// Attention backward from dO (datt), recomputed P (p16) and q, k, v -> dq, dk, dv in dqkv.
+ls_status attn_bwd(ls_ctx* c, const Dims& d, const uint16_t* qkv, const uint16_t* dout, uint16_t* dqkv) {
+  const int S = d.seq, nrep = d.hq / d.hkv;
+  const float scale = 1.0f / std::sqrt((float)d.hd);
+  const int64_t SS = (int64_t)S * S;
+  float* dp32 = c->dp<float>(c->plan.s32);
+  uint16_t* p16 = c->dp<uint16_t>(c->plan.p16);
+  uint16_t* ds16 = c->dp<uint16_t>(c->plan.ds16);
+  const double fl = 2.0 * d.batch * d.hq * (double)S * (S + 1) / 2 * d.hd;
+  {   // dP = dO V^T
+    GemmArgs g;
+    g.A = dout; g.sAm = d.qd; g.sAk = 1; g.zA = {(int64_t)S * d.qd, d.hd, 1};
+    g.B = qkv + d.qd + d.kvd; g.sBn = d.qkvd; g.sBk = 1; g.zB = {(int64_t)S * d.qkvd, d.hd, nrep};
+    g.C = dp32; g.sCm = S; g.sCn = 1; g.zC = {(int64_t)d.hq * SS, SS, 1}; g.c_f32 = 1;
+    g.M = S; g.N = S; g.K = d.hd; g.nz = d.batch * d.hq; g.zdiv = d.hq; g.causal = 1;
+    KTimer kt(c, LS_KC_ATTN, fl, 2.0 * d.T * (d.qd + d.kvd) + 4.0 * d.batch * d.hq * SS / 2);
+    HIPCHK(c, launch_gemm_generic(g, c->cs));
+  }
+  {
+    KTimer kt(c, LS_KC_ATTN, 0.0, 8.0 * d.batch * d.hq * SS / 2);
+    HIPCHK(c, launch_softmax_bwd(dp32, p16, ds16, (int64_t)d.batch * d.hq * S, S, scale, c->cs));
+  }
+  {   // dQ = dS K
+    GemmArgs g;
+    g.A = ds16; g.sAm = S; g.sAk = 1; g.zA = {(int64_t)d.hq * SS, SS, 1};
+    g.B = qkv + d.qd; g.sBn = 1; g.sBk = d.qkvd; g.zB = {(int64_t)S * d.qkvd, d.hd, nrep};
+    g.C = dqkv; g.sCm = d.qkvd; g.sCn = 1; g.zC = {(int64_t)S * d.qkvd, d.hd, 1}; g.c_f32 = 0;
+    g.M = S; g.N = d.hd; g.K = S; g.nz = d.batch * d.hq; g.zdiv = d.hq; g.causal = 2;
+    KTimer kt(c, LS_KC_ATTN, fl, 2.0 * d.batch * d.hq * SS / 2 + 2.0 * d.T * (d.kvd + d.qd));
+    HIPCHK(c, launch_gemm_generic(g, c->cs));
+  }
+  // dK = sum over the group's heads dS^T Q, dV = sum P^T dO (fixed head order)
+  for (int r = 0; r < nrep; ++r) {
+    GemmArgs g;
+    g.A = ds16 + (int64_t)r * SS; g.sAm = 1; g.sAk = S; g.zA = {(int64_t)d.hq * SS, (int64_t)nrep * SS, 1};
+    g.B = qkv + (int64_t)r * d.hd; g.sBn = 1; g.sBk = d.qkvd; g.zB = {(int64_t)S * d.qkvd, (int64_t)nrep * d.hd, 1};
+    g.C = dqkv + d.qd; g.sCm = d.qkvd; g.sCn = 1; g.zC = {(int64_t)S * d.qkvd, d.hd, 1}; g.c_f32 = 0;
+    g.M = S; g.N = d.hd; g.K = S; g.nz = d.batch * d.hkv; g.zdiv = d.hkv; g.causal = 3; g.beta = r ? 1.f : 0.f;
+    KTimer kt(c, LS_KC_ATTN, fl / d.hq * d.hkv, 2.0 * d.batch * d.hkv * SS / 2 + 2.0 * d.T * 2 * d.kvd);
+    HIPCHK(c, launch_gemm_generic(g, c->cs));
+    GemmArgs v = g;
+    v.A = p16 + (int64_t)r * SS;
+    v.B = dout + (int64_t)r * d.hd; v.sBk = d.qd; v.zB = {(int64_t)S * d.qd, (int64_t)nrep * d.hd, 1};
+    v.C = dqkv + d.qd + d.kvd;
+    KTimer kv(c, LS_KC_ATTN, fl / d.hq * d.hkv, 2.0 * d.batch * d.hkv * SS / 2 + 2.0 * d.T * 2 * d.kvd);
+    HIPCHK(c, launch_gemm_generic(v, c->cs));
+  }
+  return LS_OK;
+}
+
+enum FwdMode { MODE_FWD = 0, MODE_RECOMPUTE = 1 };
+
+// One decoder layer forward from x_in (bf16 [T, h]).  MODE_FWD writes x_out; the
+// recompute keeps every intermediate and skips the down projection, whose output
+// the backward does not need.
+ls_status layer_forward(ls_ctx* c, int l, const uint8_t* blob, const Dims& d, const uint16_t* x_in, uint16_t* x_out,
+                        bool lora, FwdMode mode) {
+  const ls_config& g = c->cfg;
+  const int fmt = wformat(g);
+  const float* lv = c->dp<float>(c->plan.levels);
+  uint16_t* n1 = c->dp<uint16_t>(c->plan.n1);
+  uint16_t* qkv = c->dp<uint16_t>(c->plan.qkv);
+  uint16_t* att = c->dp<uint16_t>(c->plan.att);
+  uint16_t* hb = c->dp<uint16_t>(c->plan.hb);
+  uint16_t* n2 = c->dp<uint16_t>(c->plan.n2);
+  uint16_t* gu = c->dp<uint16_t>(c->plan.gu);
+  uint16_t* act = c->dp<uint16_t>(c->plan.act);
+  uint16_t* hs = c->dp<uint16_t>(c->plan.hs);
+  const uint16_t* g1 = reinterpret_cast<const uint16_t*>(blob + c->lay.off_g1);
+  const uint16_t* g2 = reinterpret_cast<const uint16_t*>(blob + c->lay.off_g2);
+  const double tb = 2.0 * d.T;
+
+  {
+    KTimer kt(c, LS_KC_GLUE, 0.0, 2 * tb * d.h);
+    HIPCHK(c, launch_rmsnorm_fwd(x_in, g1, n1, c->dp<float>(c->plan.rstd1), d.T, d.h, g.rms_eps, c->cs));
+  }
+  if (lora) { ls_status st = lora_down(c, l, d, n1, d.h, LS_PROJ_Q, 3, d.h); if (st) return st; }
+  {
+    FwdArgs f;
+    f.x = n1; f.ldx = d.h; f.M = d.T; f.K = d.h; f.n_groups = 3;
+    const int cols[3] = {0, d.qd, d.qd + d.kvd};
+    for (int i = 0; i < 3; ++i) {
+      f.g[i].w = wref(c, blob, LS_PROJ_Q + i);
+      f.g[i].out_col0 = cols[i];
+      f.g[i].ext_col0 = (LS_PROJ_Q + i) * d.r16;
+      f.g[i].bext = lora && lora_active(c, l, LS_PROJ_Q + i) ? lora_at(c, l, c->plan.bx16[LS_PROJ_Q + i]) : nullptr;
+    }
+    f.aext = hs; f.ldaext = d.R7; f.kx = lora ? d.r16 : 0;
+    f.y = qkv; f.ldy = d.qkvd; f.levels = lv; f.format = fmt;
+    KTimer kt(c, LS_KC_GEMM_FWD, fwd_gemm_flop(d, d.qkvd, d.h, lora),
+              tb * d.h + wbytes(c, 0) + wbytes(c, 1) + wbytes(c, 2) + tb * d.qkvd);
+    HIPCHK(c, launch_gemm_fwd(f, c->cs));
+  }
+  {
+    KTimer kt(c, LS_KC_GLUE, 0.0, 2 * tb * (d.qd + d.kvd));
+    HIPCHK(c, launch_rope_tab(qkv, d.qkvd, d.T, d.seq, d.hq + d.hkv, d.hd, c->dp<float2>(c->plan.rope), 0, c->cs));
+  }
+  { ls_status st = attn_fwd(c, d, qkv, att); if (st) return st; }
+  if (lora) { ls_status st = lora_down(c, l, d, att, d.qd, LS_PROJ_O, 1, d.qd); if (st) return st; }
+  {
+    FwdArgs f;
+    f.x = att; f.ldx = d.qd; f.M = d.T; f.K = d.qd; f.n_groups = 1;
+    f.g[0].w = wref(c, blob, LS_PROJ_O);
+    f.g[0].ext_col0 = LS_PROJ_O * d.r16;
+    f.g[0].bext = lora && lora_active(c, l, LS_PROJ_O) ? lora_at(c, l, c->plan.bx16[LS_PROJ_O]) : nullptr;
+    f.aext = hs; f.ldaext = d.R7; f.kx = lora ? d.r16 : 0;
+    f.resid = x_in; f.ldr = d.h;
+    f.y = hb; f.ldy = d.h; f.levels = lv; f.format = fmt;
+    KTimer kt(c, LS_KC_GEMM_FWD, fwd_gemm_flop(d, d.h, d.qd, lora), tb * d.qd + wbytes(c, 3) + 2 * tb * d.h);
+    HIPCHK(c, launch_gemm_fwd(f, c->cs));
+  }
+  {
+    KTimer kt(c, LS_KC_GLUE, 0.0, 2 * tb * d.h);
+    HIPCHK(c, launch_rmsnorm_fwd(hb, g2, n2, c->dp<float>(c->plan.rstd2), d.T, d.h, g.rms_eps, c->cs));
+  }
+  if (lora) { ls_status st = lora_down(c, l, d, n2, d.h, LS_PROJ_GATE, 2, d.h); if (st) return st; }
+  {
+    FwdArgs f;
+    f.x = n2; f.ldx = d.h; f.M = d.T; f.K = d.h; f.n_groups = 2;
+    for (int i = 0; i < 2; ++i) {
+      const int p = LS_PROJ_GATE + i;
+      f.g[i].w = wref(c, blob, p);
+      f.g[i].out_col0 = i * d.I;
+      f.g[i].ext_col0 = p * d.r16;
+      f.g[i].bext = lora && lora_active(c, l, p) ? lora_at(c, l, c->plan.bx16[p]) : nullptr;
+    }
+    f.aext = hs; f.ldaext = d.R7; f.kx = lora ? d.r16 : 0;
+    f.y = gu; f.ldy = 2 * d.I; f.levels = lv; f.format = fmt;
+    KTimer kt(c, LS_KC_GEMM_FWD, fwd_gemm_flop(d, 2 * d.I, d.h, lora), tb * d.h + wbytes(c, 4) + wbytes(c, 5) + tb * 2 * d.I);
+    HIPCHK(c, launch_gemm_fwd(f, c->cs));
+  }
+  {
+    KTimer kt(c, LS_KC_GLUE, 0.0, 3 * tb * d.I);
+    HIPCHK(c, launch_swiglu_fwd(gu, 2 * d.I, d.I, act, d.T, c->cs));
+  }
+  if (lora) { ls_status st = lora_down(c, l, d, act, d.I, LS_PROJ_DOWN, 1, d.I); if (st) return st; }
+  if (mode == MODE_RECOMPUTE) return LS_OK;
+  {
+    FwdArgs f;
+    f.x = act; f.ldx = d.I; f.M = d.T; f.K = d.I; f.n_groups = 1;
+    f.g[0].w = wref(c, blob, LS_PROJ_DOWN);
+    f.g[0].ext_col0 = LS_PROJ_DOWN * d.r16;
+    f.g[0].bext = lora && lora_active(c, l, LS_PROJ_DOWN) ? lora_at(c, l, c->plan.bx16[LS_PROJ_DOWN]) : nullptr;
+    f.aext = hs; f.ldaext = d.R7; f.kx = lora ? d.r16 : 0;
+    f.resid = hb; f.ldr = d.h;
+    f.y = x_out; f.ldy = d.h; f.levels = lv; f.format = fmt;
+    KTimer kt(c, LS_KC_GEMM_FWD, fwd_gemm_flop(d, d.h, d.I, lora), tb * d.I + wbytes(c, 6) + 2 * tb * d.h);
+    HIPCHK(c, launch_gemm_fwd(f, c->cs));
+  }
+  return LS_OK;
+}
+
+// LoRA gradient products of projection p: Gs_p = s dY_p Bx16_p (bf16, into Gs),
+// dB_p = dY_p^T Hs_p, dA_p = Gs_p^T X_p (float32, written or accumulated).
+ls_status lora_grads_G(ls_ctx* c, int l, const Dims& d, int p, const uint16_t* dy, int lddy) {
+  if (!lora_active(c, l, p)) return LS_OK;
+  const ProjLayout& P = c->lay.p[p];
+  GemmArgs g;
+  g.A = dy; g.sAm = lddy; g.sAk = 1;
+  g.B = lora_at(c, l, c->plan.bx16[p]); g.sBn = 1; g.sBk = d.r16;
+  g.C = c->dp<uint16_t>(c->plan.gs) + p * d.r16; g.sCm = d.R7; g.sCn = 1; g.c_f32 = 0;
+  g.M = d.T; g.N = d.r16; g.K = P.n_out; g.alpha = d.s;
+  KTimer kt(c, LS_KC_LORA, 2.0 * d.T * P.n_out * d.r, 2.0 * d.T * P.n_out + 2.0 * P.n_out * d.r + 2.0 * d.T * d.r);
+  HIPCHK(c, launch_gemm_generic(g, c->cs));
+  return LS_OK;
+}
+
+ls_status lora_grads_AB(ls_ctx* c, int l, const Dims& d, int p, const uint16_t* dy, int lddy, const uint16_t* x, int ldx,
+                        float beta) {
+  if (!lora_active(c, l, p)) return LS_OK;
+  const ProjLayout& P = c->lay.p[p];
+  const LoraReg& R = c->lora[l][p];
+  if (R.dB) {
+    GemmArgs g;
+    g.A = dy; g.sAm = 1; g.sAk = lddy;
+    g.B = c->dp<uint16_t>(c->plan.hs) + p * d.r16; g.sBn = 1; g.sBk = d.R7;
+    g.C = R.dB; g.sCm = d.r; g.sCn = 1; g.c_f32 = 1;
+    g.M = P.n_out; g.N = d.r; g.K = d.T; g.beta = beta;
+    KTimer kt(c, LS_KC_LORA, 2.0 * d.T * P.n_out * d.r, 2.0 * d.T * P.n_out + 2.0 * d.T * d.r + 4.0 * P.n_out * d.r);
+    HIPCHK(c, launch_gemm_generic(g, c->cs));
+  }
+  if (R.dA) {
+    GemmArgs g;
+    g.A = x; g.sAm = 1; g.sAk = ldx;
+    g.B = c->dp<uint16_t>(c->plan.gs) + p * d.r16; g.sBn = 1; g.sBk = d.R7;
+    g.C = R.dA; g.sCm = 1; g.sCn = P.n_in; g.c_f32 = 1;
+    g.M = P.n_in; g.N = d.r; g.K = d.T; g.beta = beta;
+    KTimer kt(c, LS_KC_LORA, 2.0 * d.T * P.n_in * d.r, 2.0 * d.T * P.n_in + 2.0 * d.T * d.r + 4.0 * P.n_in * d.r);
+    HIPCHK(c, launch_gemm_generic(g, c->cs));
+  }
+  return LS_OK;
+}
+
+ls_status layer_backward(ls_ctx* c, int l, const uint8_t* blob, const Dims& d, const uint16_t* x_in, const uint16_t* dy,
+                         uint16_t* dx, float beta) {
+  ls_status st = layer_forward(c, l, blob, d, x_in, nullptr, true, MODE_RECOMPUTE);
+  if (st) return st;
+  const ls_config& g = c->cfg;
+  const int fmt = wformat(g);
+  const float* lv = c->dp<float>(c->plan.levels);
+  uint16_t* n1 = c->dp<uint16_t>(c->plan.n1);
+  uint16_t* qkv = c->dp<uint16_t>(c->plan.qkv);
+  uint16_t* att = c->dp<uint16_t>(c->plan.att);
+  uint16_t* hb = c->dp<uint16_t>(c->plan.hb);
+  uint16_t* n2 = c->dp<uint16_t>(c->plan.n2);
+  uint16_t* gu = c->dp<uint16_t>(c->plan.gu);
+  uint16_t* act = c->dp<uint16_t>(c->plan.act);
+  uint16_t* gs = c->dp<uint16_t>(c->plan.gs);
+  float* dh32 = c->dp<float>(c->plan.dh32);
+  uint16_t* dh16 = c->dp<uint16_t>(c->plan.dh16);
+  uint16_t* dact = c->dp<uint16_t>(c->plan.dact);
+  uint16_t* dgu = c->dp<uint16_t>(c->plan.dgu);
+  uint16_t* datt = c->dp<uint16_t>(c->plan.datt);
+  uint16_t* dqkv = c->dp<uint16_t>(c->plan.dqkv);
+  float* dn32 = c->dp<float>(c->plan.dn32);
+  const uint16_t* g1 = reinterpret_cast<const uint16_t*>(blob + c->lay.off_g1);
+  const uint16_t* g2 = reinterpret_cast<const uint16_t*>(blob + c->lay.off_g2);
+  const double tb = 2.0 * d.T;
+  auto bwd_flop = [&](int n_out, int n_in) { return 2.0 * d.T * n_out * n_in + 2.0 * d.T * n_in * d.r; };
+
+  // ---- down: y = h + act W_d^T + LoRA
+  if ((st = lora_grads_G(c, l, d, LS_PROJ_DOWN, dy, d.h))) return st;
+  if ((st = lora_grads_AB(c, l, d, LS_PROJ_DOWN, dy, d.h, act, d.I, beta))) return st;
+  {
+    BwdArgs b;
+    b.dy = dy; b.lddy = d.h; b.M = d.T; b.N = d.I; b.n_segs = 1;
+    b.seg[0].w = wref(c, blob, LS_PROJ_DOWN); b.seg[0].a_col0 = 0;
+    b.aext = gs + LS_PROJ_DOWN * d.r16; b.ldaext = d.R7; b.kx = d.r16;
+    b.bext = lora_at(c, l, c->plan.at_d); b.ldbext = d.r16;
+    b.out16 = dact; b.ldo = d.I; b.levels = lv; b.format = fmt;
+    KTimer kt(c, LS_KC_GEMM_BWD, bwd_flop(d.h, d.I), tb * d.h + wbytes(c, 6) + tb * d.I);
+    HIPCHK(c, launch_gemm_bwd(b, c->cs));
+  }
+  {
+    KTimer kt(c, LS_KC_GLUE, 0.0, 5 * tb * d.I);
+    HIPCHK(c, launch_swiglu_bwd(gu, 2 * d.I, dact, d.I, dgu, d.T, c->cs));
+  }
+  // ---- gate / up
+  for (int i = 0; i < 2; ++i) {
+    const int p = LS_PROJ_GATE + i;
+    if ((st = lora_grads_G(c, l, d, p, dgu + i * d.I, 2 * d.I))) return st;
+    if ((st = lora_grads_AB(c, l, d, p, dgu + i * d.I, 2 * d.I, n2, d.h, beta))) return st;
+  }
+  {
+    BwdArgs b;
+    b.dy = dgu; b.lddy = 2 * d.I; b.M = d.T; b.N = d.h; b.n_segs = 2;
+    b.seg[0].w = wref(c, blob, LS_PROJ_GATE); b.seg[0].a_col0 = 0;
+    b.seg[1].w = wref(c, blob, LS_PROJ_UP); b.seg[1].a_col0 = d.I;
+    b.aext = gs + LS_PROJ_GATE * d.r16; b.ldaext = d.R7; b.kx = 2 * d.r16;
+    b.bext = lora_at(c, l, c->plan.at_gu); b.ldbext = 2 * d.r16;
+    b.out32 = dn32; b.ldo = d.h; b.levels = lv; b.format = fmt;
+    KTimer kt(c, LS_KC_GEMM_BWD, 2 * bwd_flop(d.I, d.h), tb * 2 * d.I + wbytes(c, 4) + wbytes(c, 5) + 2 * tb * d.h);
+    HIPCHK(c, launch_gemm_bwd(b, c->cs));
+  }
+  {
+    KTimer kt(c, LS_KC_GLUE, 0.0, 4 * tb * d.h);
+    HIPCHK(c, launch_rmsnorm_bwd(dn32, hb, g2, c->dp<float>(c->plan.rstd2), nullptr, dy, dh32, dh16, d.T, d.h, c->cs));
+  }
+  // ---- o: h = x + att W_o^T + LoRA
+  if ((st = lora_grads_G(c, l, d, LS_PROJ_O, dh16, d.h))) return st;
+  if ((st = lora_grads_AB(c, l, d, LS_PROJ_O, dh16, d.h, att, d.qd, beta))) return st;
+  {
+    BwdArgs b;
+    b.dy = dh16; b.lddy = d.h; b.M = d.T; b.N = d.qd; b.n_segs = 1;
+    b.seg[0].w = wref(c, blob, LS_PROJ_O); b.seg[0].a_col0 = 0;
+    b.aext = gs + LS_PROJ_O * d.r16; b.ldaext = d.R7; b.kx = d.r16;
+    b.bext = lora_at(c, l, c->plan.at_o); b.ldbext = d.r16;
+    b.out16 = datt; b.ldo = d.qd; b.levels = lv; b.format = fmt;
+    KTimer kt(c, LS_KC_GEMM_BWD, bwd_flop(d.h, d.qd), tb * d.h + wbytes(c, 3) + tb * d.qd);
+    HIPCHK(c, launch_gemm_bwd(b, c->cs));
+  }
+  if ((st = attn_bwd(c, d, qkv, datt, dqkv))) return st;
+  {
+    KTimer kt(c, LS_KC_GLUE, 0.0, 2 * tb * (d.qd + d.kvd));
+    HIPCHK(c, launch_rope_tab(dqkv, d.qkvd, d.T, d.seq, d.hq + d.hkv, d.hd, c->dp<float2>(c->plan.rope), 1, c->cs));
+  }
+  // ---- q, k, v
+  const int cols[3] = {0, d.qd, d.qd + d.kvd};
+  for (int i = 0; i < 3; ++i) {
+    const int p = LS_PROJ_Q + i;
+    if ((st = lora_grads_G(c, l, d, p, dqkv + cols[i], d.qkvd))) return st;
+    if ((st = lora_grads_AB(c, l, d, p, dqkv + cols[i], d.qkvd, n1, d.h, beta))) return st;
+  }
+  {
+    BwdArgs b;
+    b.dy = dqkv; b.lddy = d.qkvd; b.M = d.T; b.N = d.h; b.n_segs = 3;
+    for (int i = 0; i < 3; ++i) { b.seg[i].w = wref(c, blob, LS_PROJ_Q + i); b.seg[i].a_col0 = cols[i]; }
+    b.aext = gs; b.ldaext = d.R7; b.kx = 3 * d.r16;
+    b.bext = lora_at(c, l, c->plan.at_qkv); b.ldbext = 3 * d.r16;
+    b.out32 = dn32; b.ldo = d.h; b.levels = lv; b.format = fmt;
+    KTimer kt(c, LS_KC_GEMM_BWD, bwd_flop(d.qkvd, d.h), tb * d.qkvd + wbytes(c, 0) + wbytes(c, 1) + wbytes(c, 2) + 2 * tb * d.h);
+    HIPCHK(c, launch_gemm_bwd(b, c->cs));
+  }
+  {
+    KTimer kt(c, LS_KC_GLUE, 0.0, 4 * tb * d.h);
+    HIPCHK(c, launch_rmsnorm_bwd(dn32, x_in, g1, c->dp<float>(c->plan.rstd1), dh32, nullptr, nullptr, dx, d.T, d.h, c->cs));
+  }
+  return LS_OK;
+}
+
+uint16_t* ckpt(ls_ctx* c, int l) {
+  return c->dp<uint16_t>(c->plan.ck) + (uint64_t)l * c->cfg.max_tokens * c->cfg.hidden;
+}
+
+ls_status check_usable(ls_ctx* c) {
+  if (!c) return LS_ERR_INVALID;
+  if (c->sticky != LS_OK) return c->sticky;
+  return LS_OK;
+}
+
+}  // namespace
+
+// ======================================================================= C ABI
+extern "C" {
+
+void ls_nf4_codebook(float out[16]) { nf4_codebook_host(out); }
+
+ls_status ls_pack_nf4(const uint16_t* w, uint64_t numel, int32_t double_quant, int32_t n_threads, uint8_t* packed,
+                      float* absmax, uint8_t* qabs, float* scale2, float* mean) {
+  if (!w || !packed || !absmax || (double_quant && (!qabs || !scale2 || !mean))) return LS_ERR_INVALID;
+  if (numel == 0) return LS_OK;
+  pack_nf4_host(w, numel, double_quant != 0, n_threads, packed, absmax, qabs, scale2, mean);
+  return LS_OK;
+}
+
+ls_status ls_plan_bytes(const ls_config* cfg, uint64_t* device_bytes, uint64_t* host_bytes, uint64_t* blob_bytes) {
+  if (!cfg) return LS_ERR_INVALID;
+  const char* why = nullptr;
+  if (!validate_config(*cfg, &why)) { g_create_err = why; return LS_ERR_INVALID; }
+  const BlobLayout L = make_layout(*cfg);
+  const DevPlan P = make_plan(*cfg, L);
+  if (device_bytes) *device_bytes = P.total;
+  if (host_bytes) *host_bytes = L.bytes * (uint64_t)cfg->n_layers;
+  if (blob_bytes) *blob_bytes = L.bytes;
+  return LS_OK;
+}
+
+ls_status ls_create(const ls_config* cfg, void* compute_stream, void* copy_stream, ls_ctx** out) {
+  if (!cfg || !out) return fail(nullptr, LS_ERR_INVALID, "null cfg or out");
+  *out = nullptr;
+  const char* why = nullptr;
+  if (!validate_config(*cfg, &why)) return fail(nullptr, LS_ERR_INVALID, "invalid config: %s", why);
+  if (compute_stream && compute_stream == copy_stream) return fail(nullptr, LS_ERR_INVALID, "copy stream must differ from compute stream");
+  const BlobLayout L = make_layout(*cfg);
+  const DevPlan P = make_plan(*cfg, L);
+  uint64_t budget = cfg->vram_budget;
+  if (budget == 0) {
+    size_t fr = 0, tot = 0;
+    hipError_t e = hipMemGetInfo(&fr, &tot);
+    if (e != hipSuccess) return fail(nullptr, LS_ERR_HIP, "hipMemGetInfo failed: %s", hipGetErrorString(e));
+    budget = fr;
+  }
+  if (P.total > budget)
+    return fail(nullptr, LS_ERR_BUDGET, "device plan %llu bytes exceeds budget %llu bytes",
+                (unsigned long long)P.total, (unsigned long long)budget);
+
+  ls_ctx* c = new ls_ctx();
+  c->cfg = *cfg;
+  c->lay = L;
+  c->plan = P;
+  auto bail = [&](ls_status st) { g_create_err = c->err; ls_destroy(c); return st; };
+  if (hipGetDevice(&c->device) != hipSuccess) { c->err = "hipGetDevice failed"; return bail(LS_ERR_HIP); }
+  if (compute_stream) c->cs = (hipStream_t)compute_stream;
+  else if (hipStreamCreateWithFlags(&c->cs, hipStreamNonBlocking) == hipSuccess) c->own_cs = true;
+  else { c->err = "compute stream creation failed"; return bail(LS_ERR_HIP); }
+  if (copy_stream) c->ps = (hipStream_t)copy_stream;
+  else if (hipStreamCreateWithFlags(&c->ps, hipStreamNonBlocking) == hipSuccess) c->own_ps = true;
+  else { c->err = "copy stream creation failed"; return bail(LS_ERR_HIP); }
+  if (gemm_dequant_init() != hipSuccess) { c->err = "kernel attribute setup failed"; return bail(LS_ERR_HIP); }
+
+  const int nb = cfg->resident ? cfg->n_layers : cfg->n_buffers;
+  c->slot_layer.assign(nb, -1);
+  c->ready.resize(nb);
+  c->consumed.resize(nb);
+  c->ready_rec.assign(nb, 0);
+  c->cons_rec.assign(nb, 0);
+  for (int i = 0; i < nb; ++i) {
+    if (hipEventCreateWithFlags(&c->ready[i], hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&c->consumed[i], hipEventDisableTiming) != hipSuccess) {
+      c->err = "event creation failed";
+      return bail(LS_ERR_HIP);
+    }
+  }
+  c->lora.resize(cfg->n_layers);
+  c->staged.assign(cfg->n_layers, 0);
+  c->host.assign(cfg->n_layers, nullptr);
+  for (int l = 0; l < cfg->n_layers; ++l) {
+    if (hipHostMalloc((void**)&c->host[l], L.bytes, hipHostMallocDefault) != hipSuccess) {
+      c->host[l] = nullptr;
+      c->err = "pinned host allocation of the layer store failed";
+      return bail(LS_ERR_OOM);
+    }
+    std::memset(c->host[l], 0, L.bytes);
+  }
+  if (hipMalloc((void**)&c->dbase, P.total) != hipSuccess) {
+    c->dbase = nullptr;
+    c->err = "device allocation failed";
+    return bail(LS_ERR_OOM);
+  }
+  // zero the whole plan once: unused LoRA columns and padding must read as 0
+  if (hipMemsetAsync(c->dbase, 0, P.total, c->cs) != hipSuccess) { c->err = "device memset failed"; return bail(LS_ERR_HIP); }
+  // NF4 levels and the rotary table, computed on the host
+  nf4_codebook_host(c->levels_h);
+  std::vector<float2> rope((size_t)cfg->max_seq * (cfg->head_dim / 2));
+  for (int pos = 0; pos < cfg->max_seq; ++pos)
+    for (int i = 0; i < cfg->head_dim / 2; ++i) {
+      const double ang = (double)pos * std::pow((double)cfg->rope_theta, -2.0 * i / (double)cfg->head_dim);
+      rope[(size_t)pos * (cfg->head_dim / 2) + i] = make_float2((float)std::cos(ang), (float)std::sin(ang));
+    }
+  if (hipMemcpyAsync(c->dbase + P.levels, c->levels_h, 64, hipMemcpyHostToDevice, c->cs) != hipSuccess ||
+      hipMemcpyAsync(c->dbase + P.rope, rope.data(), rope.size() * sizeof(float2), hipMemcpyHostToDevice, c->cs) != hipSuccess ||
+      hipStreamSynchronize(c->cs) != hipSuccess) {
+    c->err = "upload of tables failed";
+    return bail(LS_ERR_HIP);
+  }
+  c->stats.blob_bytes = L.bytes;
+  c->stats.store_bytes = L.bytes * (uint64_t)cfg->n_layers;
+  c->stats.device_bytes = P.total;
+  *out = c;
+  return LS_OK;
+}
+
+ls_status ls_stage_layer(ls_ctx* c, int32_t layer, const ls_layer_host* w) {
+  if (ls_status st = check_usable(c)) return st;
+  if (!w || layer < 0 || layer >= c->cfg.n_layers) return fail(c, LS_ERR_INVALID, "bad layer index or null weights");
+  if (!w->g1 || !w->g2) return fail(c, LS_ERR_INVALID, "null norm weights");
+  for (int p = 0; p < LS_N_PROJ; ++p)
+    if (!w->w[p]) return fail(c, LS_ERR_INVALID, "null weight for projection %d", p);
+  if (c->in_flight) return fail(c, LS_ERR_STATE, "a forward/backward is in flight: call ls_sync first");
+  uint8_t* blob = c->host[layer];
+  std::memcpy(blob + c->lay.off_g1, w->g1, 2ull * c->cfg.hidden);
+  std::memcpy(blob + c->lay.off_g2, w->g2, 2ull * c->cfg.hidden);
+  for (int p = 0; p < LS_N_PROJ; ++p) {
+    const ProjLayout& P = c->lay.p[p];
+    if (c->cfg.quant == LS_QUANT_BF16) {
+      std::memcpy(blob + P.off_w, w->w[p], P.bytes_w);
+      continue;
+    }
+    if (c->cfg.double_quant) {
+      std::vector<float> absmax(P.nblocks);
+      pack_nf4_host(w->w[p], P.numel, true, 0, blob + P.off_w, absmax.data(), blob + P.off_qabs,
+                    reinterpret_cast<float*>(blob + P.off_scale2), reinterpret_cast<float*>(blob + P.off_mean));
+    } else {
+      pack_nf4_host(w->w[p], P.numel, false, 0, blob + P.off_w, reinterpret_cast<float*>(blob + P.off_absmax), nullptr,
+                    nullptr, nullptr);
+    }
+  }
+  c->staged[layer] = 1;
+  // a slot holding the old contents of this layer is stale now
+  for (auto& sl : c->slot_layer)
+    if (sl == layer) sl = -1;
+  if (c->cfg.resident) {
+    HIPCHK(c, hipMemcpyAsync(slot_ptr(c, layer), blob, c->lay.bytes, hipMemcpyHostToDevice, c->ps));
+    HIPCHK(c, hipStreamSynchronize(c->ps));
+    c->stats.h2d_bytes += c->lay.bytes;
+    c->stats.h2d_copies += 1;
+  }
+  return LS_OK;
+}
+
+ls_status ls_set_lora(ls_ctx* c, int32_t layer, int32_t proj, const float* A, const float* B, float* dA, float* dB) {
+  if (ls_status st = check_usable(c)) return st;
+  if (layer < 0 || layer >= c->cfg.n_layers || proj < 0 || proj >= LS_N_PROJ)
+    return fail(c, LS_ERR_INVALID, "bad layer or projection index");
+  if (!A || !B) return fail(c, LS_ERR_INVALID, "null A or B");
+  c->lora[layer][proj] = {A, B, dA, dB};
+  return LS_OK;
+}
+
+ls_status ls_forward(ls_ctx* c, const void* X, int32_t batch, int32_t seq, int32_t lora_on, void* Y, void* Y_ref) {
+  if (ls_status st = check_usable(c)) return st;
+  const int64_t T = (int64_t)batch * seq;
+  if (batch < 0 || seq < 0 || T > c->cfg.max_tokens || seq > c->cfg.max_seq)
+    return fail(c, LS_ERR_INVALID, "batch*seq must be in 0..max_tokens and seq <= max_seq");
+  if (seq % 8 != 0) return fail(c, LS_ERR_INVALID, "seq must be a multiple of 8");
+  if (T > 0 && (!X || !Y)) return fail(c, LS_ERR_INVALID, "null X or Y");
+  for (int l = 0; l < c->cfg.n_layers; ++l)
+    if (!c->staged[l]) return fail(c, LS_ERR_STATE, "layer %d not staged", l);
+  c->fwd_valid = false;
+  c->prof.reset();
+  c->in_flight = true;
+  if (T == 0) {
+    c->fwd_valid = true; c->fwd_lora = lora_on != 0; c->fwd_T = 0; c->fwd_batch = batch; c->fwd_seq = seq;
+    return LS_OK;
+  }
+  const Dims d = dims_of(c, batch, seq);
+  const int L = c->cfg.n_layers;
+  const bool lora = lora_on != 0;
+  HIPCHK(c, hipMemcpyAsync(ckpt(c, 0), X, 2ull * T * d.h, hipMemcpyDeviceToDevice, c->cs));
+  uint16_t* xr[2] = {c->dp<uint16_t>(c->plan.xref), c->dp<uint16_t>(c->plan.xref) + (uint64_t)c->cfg.max_tokens * d.h};
+  ls_status st;
+  if ((st = ensure_copy(c, 0))) return st;
+  for (int l = 0; l < L; ++l) {
+    for (int k = 1; k < c->cfg.n_buffers && l + k < L; ++k)
+      if ((st = ensure_copy(c, l + k))) return st;
+    if ((st = use_layer(c, l))) return st;
+    {
+      Span sp(c, c->cs, false);
+      const uint8_t* blob = slot_ptr(c, l);
+      if (lora && (st = prep_lora(c, l, d))) return st;
+      uint16_t* out = l + 1 < L ? ckpt(c, l + 1) : (uint16_t*)Y;
+      if ((st = layer_forward(c, l, blob, d, ckpt(c, l), out, lora, MODE_FWD))) return st;
+      if (Y_ref) {
+        const uint16_t* rin = l == 0 ? (const uint16_t*)X : xr[(l - 1) & 1];
+        uint16_t* rout = l + 1 < L ? xr[l & 1] : (uint16_t*)Y_ref;
+        if ((st = layer_forward(c, l, blob, d, rin, rout, false, MODE_FWD))) return st;
+      }
+    }
+    if ((st = release_layer(c, l))) return st;
+  }
+  c->fwd_valid = true; c->fwd_lora = lora; c->fwd_T = (int)T; c->fwd_batch = batch; c->fwd_seq = seq;
+  return LS_OK;
+}
+
+ls_status ls_backward(ls_ctx* c, const void* dY, void* dX, int32_t accumulate) {
+  if (ls_status st = check_usable(c)) return st;
+  if (!c->fwd_valid) return fail(c, LS_ERR_STATE, "ls_backward needs a preceding ls_forward");
+  if (!c->fwd_lora) return fail(c, LS_ERR_STATE, "ls_backward needs a forward with lora_on = 1");
+  const int L = c->cfg.n_layers;
+  const float beta = accumulate ? 1.f : 0.f;
+  c->in_flight = true;
+  if (c->fwd_T == 0) {
+    if (!accumulate)
+      for (int l = 0; l < L; ++l)
+        for (int p = 0; p < LS_N_PROJ; ++p) {
+          if (!lora_active(c, l, p)) continue;
+          const ProjLayout& P = c->lay.p[p];
+          if (c->lora[l][p].dA) HIPCHK(c, launch_fill_f32(c->lora[l][p].dA, (int64_t)c->cfg.lora_r * P.n_in, 0.f, c->cs));
+          if (c->lora[l][p].dB) HIPCHK(c, launch_fill_f32(c->lora[l][p].dB, (int64_t)c->cfg.lora_r * P.n_out, 0.f, c->cs));
+        }
+    return LS_OK;
+  }
+  if (!dY || !dX) return fail(c, LS_ERR_INVALID, "null dY or dX");
+  const Dims d = dims_of(c, c->fwd_batch, c->fwd_seq);
+  uint16_t* ping[2] = {c->dp<uint16_t>(c->plan.dya), c->dp<uint16_t>(c->plan.dyb)};
+  const uint16_t* cur = (const uint16_t*)dY;
+  ls_status st;
+  if ((st = ensure_copy(c, L - 1))) return st;
+  for (int l = L - 1; l >= 0; --l) {
+    for (int k = 1; k < c->cfg.n_buffers && l - k >= 0; ++k)
+      if ((st = ensure_copy(c, l - k))) return st;
+    if ((st = use_layer(c, l))) return st;
+    uint16_t* out = l == 0 ? (uint16_t*)dX : ping[l & 1];
+    {
+      Span sp(c, c->cs, false);
+      if ((st = layer_backward(c, l, slot_ptr(c, l), d, ckpt(c, l), cur, out, beta))) return st;
+    }
+    if ((st = release_layer(c, l))) return st;
+    cur = out;
+  }
+  return LS_OK;
+}
+
+ls_status ls_sync(ls_ctx* c) {
+  if (!c) return LS_ERR_INVALID;
+  if (c->sticky != LS_OK) return c->sticky;
+  HIPCHK(c, hipStreamSynchronize(c->ps));
+  HIPCHK(c, hipStreamSynchronize(c->cs));
+  HIPCHK(c, hipGetLastError());
+  c->in_flight = false;
+  collect_profile(c);
+  return LS_OK;
+}
+
+ls_status ls_get_stats(const ls_ctx* c, ls_stats* out) {
+  if (!c || !out) return LS_ERR_INVALID;
+  *out = c->stats;
+  return LS_OK;
+}
+
+const char* ls_last_error(const ls_ctx* c) { return c ? c->err.c_str() : g_create_err.c_str(); }
+
+void ls_destroy(ls_ctx* c) {
+  if (!c) return;
+  if (c->cs) hipStreamSynchronize(c->cs);
+  if (c->ps) hipStreamSynchronize(c->ps);
+  for (auto e : c->prof.pool) hipEventDestroy(e);
+  for (auto e : c->ready) if (e) hipEventDestroy(e);
+  for (auto e : c->consumed) if (e) hipEventDestroy(e);
+  if (c->dbase) hipFree(c->dbase);
+  for (auto p : c->host) if (p) hipHostFree(p);
+  if (c->own_cs && c->cs) hipStreamDestroy(c->cs);
+  if (c->own_ps && c->ps) hipStreamDestroy(c->ps);
+  delete c;
+}
+
+ls_status ls_read_weight(ls_ctx* c, int32_t layer, int32_t proj, void* out) {
+  if (ls_status st = check_usable(c)) return st;
+  if (layer < 0 || layer >= c->cfg.n_layers || proj < 0 || proj >= LS_N_PROJ || !out)
+    return fail(c, LS_ERR_INVALID, "bad layer/projection index or null out");
+  if (!c->staged[layer]) return fail(c, LS_ERR_STATE, "layer %d not staged", layer);
+  if (c->in_flight) return fail(c, LS_ERR_STATE, "a forward/backward is in flight: call ls_sync first");
+  ls_status st;
+  if ((st = ensure_copy(c, layer))) return st;
+  if ((st = use_layer(c, layer))) return st;
+  HIPCHK(c, launch_dequant(wref(c, slot_ptr(c, layer), proj), wformat(c->cfg), c->dp<float>(c->plan.levels),
+                           (uint16_t*)out, c->cs));
+  if ((st = release_layer(c, layer))) return st;
+  HIPCHK(c, hipStreamSynchronize(c->cs));
+  HIPCHK(c, hipStreamSynchronize(c->ps));
+  return LS_OK;
+}
+
+}  // extern "C"

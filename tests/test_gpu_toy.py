@@ -1,0 +1,132 @@
+"""GPU parity of the HIP path against the oracle on the toy stack (2 layers, hidden
+256, 4/4 heads x 64, SwiGLU 688, NF4 block 64, LoRA r 8 / alpha 16, 1 x 128), plus the
+identities the pages state, all through the C ABI."""
+import numpy as np
+import pytest
+
+from layer_streamed_qlora_amd import synth
+import lsq_harness as H
+
+pytestmark = pytest.mark.gpu
+
+TOY = synth.WORKLOADS["toy"]
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+@pytest.fixture(scope="module")
+def toy_oracle():
+    w = TOY
+    x, dy = synth.activations(w)
+    src = [synth.layer_weights(w, l) for l in range(w.n_layers)]
+    loras = [synth.layer_lora(w, l) for l in range(w.n_layers)]
+    ora = H.oracle_step(w, src, loras, x, dy, w.batch, w.seq, with_ref=True)
+    return x, dy, ora
+
+
+@pytest.mark.parametrize("dq", [False, True])
+def test_dequant_bitwise(dq):
+    w = TOY.with_(double_quant=dq)
+    say("case: dequant bitwise toy dq=", dq)
+    run = H.GpuRun(w, [0, 1])
+    enc, _ = H.oracle_layers(w, run.src)
+    for l in range(2):
+        for pi, p in enumerate(H.PROJS):
+            got = run.read_weight(l, pi)
+            want = H.onf4.bf16_bits(enc[l][p].dequant())
+            assert np.array_equal(got, want), (l, p, int(np.sum(got != want)))
+    run.close()
+
+
+def test_toy_stack_parity(toy_oracle):
+    x, dy, ora = toy_oracle
+    say("case: toy stack parity, streamed, 2 slots")
+    run = H.GpuRun(TOY, [0, 1])
+    gpu = run.step(x, dy, TOY.batch, TOY.seq, with_ref=True)
+    run.close()
+    errs, fails = H.compare(gpu, ora)
+    errs["Y_ref"] = H.rel_l2(gpu["Y_ref"], ora["Y_ref"])
+    say({k: f"{v:.2e}" for k, v in errs.items()})
+    assert not fails, fails
+    assert errs["Y_ref"] <= 1e-2
+
+
+def test_toy_streamed_equals_resident_bitwise():
+    w = TOY
+    x, dy = synth.activations(w)
+    outs = []
+    for resident in (0, 1):
+        say("case: toy streamed vs resident, resident =", resident)
+        run = H.GpuRun(w, [0, 1], resident=resident)
+        outs.append(run.step(x, dy, w.batch, w.seq, with_ref=True))
+        run.close()
+    a, b = outs
+    for k in ("Y", "Y_ref", "dX"):
+        assert np.array_equal(a[k].view(np.uint32), b[k].view(np.uint32)), k
+    for l in range(2):
+        for p in H.PROJS:
+            assert np.array_equal(a["dA"][l][p].view(np.uint32), b["dA"][l][p].view(np.uint32)), (l, p)
+            assert np.array_equal(a["dB"][l][p].view(np.uint32), b["dB"][l][p].view(np.uint32)), (l, p)
+
+
+def test_b_zero_is_base_only_and_reference_is_lora_off():
+    w = TOY
+    x, dy = synth.activations(w)
+    say("case: toy B = 0")
+    run = H.GpuRun(w, [0, 1], zero_b=True)
+    g0 = run.step(x, dy, w.batch, w.seq, with_ref=True)
+    off = run.step(x, dy, w.batch, w.seq, backward=False, lora_on=False)
+    run.close()
+    assert np.array_equal(g0["Y"], off["Y"])
+    assert np.array_equal(g0["Y"], g0["Y_ref"])
+    for l in range(2):
+        for p in H.PROJS:
+            assert np.all(g0["dA"][l][p] == 0), (l, p)
+
+
+def test_accumulate_adds():
+    w = TOY
+    x, dy = synth.activations(w)
+    say("case: toy accumulate")
+    run = H.GpuRun(w, [0, 1])
+    a = run.step(x, dy, w.batch, w.seq)
+    b = run.step(x, dy, w.batch, w.seq, accumulate=1)
+    run.close()
+    for l in range(2):
+        for p in H.PROJS:
+            assert np.array_equal(b["dA"][l][p], a["dA"][l][p] * 2), (l, p)
+            assert np.array_equal(b["dB"][l][p], a["dB"][l][p] * 2), (l, p)
+
+
+@pytest.mark.parametrize("batch,seq", [(3, 40), (2, 8)])
+def test_ragged_shapes(batch, seq):
+    """Token counts and sequence lengths that leave partial tiles everywhere."""
+    w = TOY.with_(batch=batch, seq=seq)
+    x, dy = synth.activations(w)
+    say("case: toy ragged", batch, seq)
+    run = H.GpuRun(w, [0, 1], max_tokens=128, max_seq=128)
+    gpu = run.step(x, dy, batch, seq)
+    src = run.src
+    run.close()
+    ora = H.oracle_step(w, src, [synth.layer_lora(w, l) for l in range(2)], x, dy, batch, seq)
+    errs, fails = H.compare(gpu, ora)
+    say({k: f"{v:.2e}" for k, v in errs.items() if k in ("Y", "dX")})
+    assert not fails, fails
+
+
+def test_empty_batch():
+    w = TOY
+    say("case: toy empty batch")
+    run = H.GpuRun(w, [0, 1])
+    for l in range(2):
+        for p in H.PROJS:
+            run.dA[l][p].fill_(7.0)
+            run.dB[l][p].fill_(7.0)
+    out = run.step(np.zeros((0, w.hidden), np.float32), np.zeros((0, w.hidden), np.float32), 0, 128)
+    run.close()
+    assert out["Y"].shape == (0, w.hidden)
+    for l in range(2):
+        for p in H.PROJS:
+            assert np.all(out["dA"][l][p] == 0) and np.all(out["dB"][l][p] == 0)
