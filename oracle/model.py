@@ -23,6 +23,17 @@ n_heads / n_kv_heads consecutive q heads; silu(z) = z / (1 + exp(-z)).
 Layout: activations are token-major [T, features] with T = batch * seq and token
 t = b * seq + s.  All arithmetic is float64.  The backward is derived by hand (chain
 rule written out below); tests pin it against central finite differences.
+
+Operand precision.  The pages give the compute dtype as bf16 (the QLoRA loading
+example in "Fine-Tuning an 8B Parameter Model on a 4 GB Laptop GPU" sets a 16-bit
+compute dtype for the 4-bit weights; its "Practical Advice" section recommends bf16),
+and the LoRA adapters are kept in full precision.  The reading taken: every matrix
+product takes bf16 operands (its inputs are rounded to bf16, nearest-even) and is
+accumulated exactly; nothing else is rounded.  The functions below take ``rnd``:
+the identity for exact arithmetic, or bf16 rounding for that reading.  The operands
+are: the input of each projection, the adapters A and B, s*H (forward) and s*G
+(backward), q and k after the rotary embedding, v, the probabilities P, and in the
+backward the output gradient of each projection, dO and dS of the attention.
 """
 from __future__ import annotations
 
@@ -31,6 +42,10 @@ from dataclasses import dataclass
 import numpy as np
 
 PROJS = ("q", "k", "v", "o", "gate", "up", "down")
+
+
+def _ident(x):
+    return x
 
 
 @dataclass(frozen=True)
@@ -93,8 +108,9 @@ def rope_bwd(dy, cos, sin):
     return np.concatenate([d1 * c + d2 * s, d2 * c - d1 * s], axis=-1)
 
 
-def attention_fwd(q, k, v, n_rep):
-    """q [B, S, Hq, hd], k/v [B, S, Hkv, hd] -> out [B, S, Hq, hd], probabilities P."""
+def attention_fwd(q, k, v, n_rep, rnd=_ident):
+    """q [B, S, Hq, hd], k/v [B, S, Hkv, hd] -> out [B, S, Hq, hd], probabilities P
+    (P is the operand of the second product, so it is returned after ``rnd``)."""
     b, s, hq, hd = q.shape
     kk = np.repeat(k, n_rep, axis=2)
     vv = np.repeat(v, n_rep, axis=2)
@@ -103,23 +119,25 @@ def attention_fwd(q, k, v, n_rep):
     scores = np.where(mask[None, None], -np.inf, scores)
     scores = scores - np.max(scores, axis=-1, keepdims=True)
     p = np.exp(scores)
-    p = p / np.sum(p, axis=-1, keepdims=True)
+    p = rnd(p / np.sum(p, axis=-1, keepdims=True))
     out = np.einsum("bhij,bjhd->bihd", p, vv)
     return out, p
 
 
-def attention_bwd(dout, q, k, v, p, n_rep):
+def attention_bwd(dout, q, k, v, p, n_rep, rnd=_ident):
     """dV = P^T dO; dP = dO V^T; dS = P (dP - rowsum(dP P)); dQ = c dS K; dK = c dS^T Q,
-    with dK, dV summed over the q heads that share a kv head."""
+    with dK, dV summed over the q heads that share a kv head.  dO and c dS are the
+    operands of the products (``rnd``)."""
     b, s, hq, hd = q.shape
     c = 1.0 / np.sqrt(hd)
+    dout = rnd(dout)
     kk = np.repeat(k, n_rep, axis=2)
     vv = np.repeat(v, n_rep, axis=2)
     dvv = np.einsum("bhij,bihd->bjhd", p, dout)
     dp = np.einsum("bihd,bjhd->bhij", dout, vv)
-    ds = p * (dp - np.sum(dp * p, axis=-1, keepdims=True))
-    dq = c * np.einsum("bhij,bjhd->bihd", ds, kk)
-    dkk = c * np.einsum("bhij,bihd->bjhd", ds, q)
+    ds = rnd(c * (p * (dp - np.sum(dp * p, axis=-1, keepdims=True))))
+    dq = np.einsum("bhij,bjhd->bihd", ds, kk)
+    dkk = np.einsum("bhij,bihd->bjhd", ds, q)
     hkv = hq // n_rep
     dk = dkk.reshape(b, s, hkv, n_rep, hd).sum(axis=3)
     dv = dvv.reshape(b, s, hkv, n_rep, hd).sum(axis=3)
@@ -136,29 +154,36 @@ def silu_grad(z):
 
 
 # ------------------------------------------------------------------ projections
-def lora_proj_fwd(x, w, a, b, s, lora_on=True):
-    """Y = X W^T + s (X A^T) B^T.  Returns (Y, H = X A^T or None)."""
+def lora_proj_fwd(x, w, a, b, s, lora_on=True, rnd=_ident):
+    """Y = X W^T + (s X A^T) B^T with operands X, A, B and s X A^T passed through
+    ``rnd``.  Returns (Y, Hs = s X A^T after ``rnd``, or None)."""
+    x = rnd(x)
     y = x @ w.T
     if not lora_on:
         return y, None
-    h = x @ a.T
-    return y + s * (h @ b.T), h
+    hs = rnd(s * (x @ rnd(a).T))
+    return y + hs @ rnd(b).T, hs
 
 
-def lora_proj_bwd(dy, x, w, a, b, h, s):
-    """Given dY for Y = X W^T + s H B^T, H = X A^T (W frozen):
-    G = dY B; dX = dY W + s G A; dB = s dY^T H; dA = s G^T X."""
-    g = dy @ b
-    dx = dy @ w + s * (g @ a)
-    db = s * (dy.T @ h)
-    da = s * (g.T @ x)
+def lora_proj_bwd(dy, x, w, a, b, hs, s, rnd=_ident):
+    """Given dY for Y = X W^T + Hs B^T, Hs = s X A^T (W frozen), with G = dY B:
+    dX = dY W + (s G) A; dB = dY^T Hs; dA = (s G)^T X.  dY, A, B, X and s G are
+    operands (``rnd``)."""
+    dy = rnd(dy)
+    x = rnd(x)
+    a = rnd(a)
+    gs = rnd(s * (dy @ rnd(b)))
+    dx = dy @ w + gs @ a
+    db = dy.T @ hs
+    da = gs.T @ x
     return dx, da, db
 
 
 # ----------------------------------------------------------------------- layer
-def layer_forward(x, weights, lora, shp: LayerShape, batch, seq, lora_on=True):
+def layer_forward(x, weights, lora, shp: LayerShape, batch, seq, lora_on=True, rnd=_ident):
     """One decoder layer.  x [T, h] float64; weights: dict proj -> W [out, in] plus
-    'g1', 'g2' [h]; lora: dict proj -> (A [r, in], B [out, r]).
+    'g1', 'g2' [h]; lora: dict proj -> (A [r, in], B [out, r]).  ``rnd`` is applied
+    to the operands of the matrix products.
     Returns (y, cache) where cache holds what the backward needs."""
     s = shp.scale
     hq, hkv, hd = shp.n_heads, shp.n_kv_heads, shp.head_dim
@@ -170,33 +195,33 @@ def layer_forward(x, weights, lora, shp: LayerShape, batch, seq, lora_on=True):
     outs = {}
     for p in ("q", "k", "v"):
         a, b = lora[p]
-        outs[p], hs[p] = lora_proj_fwd(n1, weights[p], a, b, s, lora_on)
+        outs[p], hs[p] = lora_proj_fwd(n1, weights[p], a, b, s, lora_on, rnd)
     cos, sin = rope_tables(seq, hd, shp.rope_theta)
-    q = rope_fwd(outs["q"].reshape(batch, seq, hq, hd), cos, sin)
-    k = rope_fwd(outs["k"].reshape(batch, seq, hkv, hd), cos, sin)
-    v = outs["v"].reshape(batch, seq, hkv, hd)
-    att, prob = attention_fwd(q, k, v, hq // hkv)
+    q = rnd(rope_fwd(outs["q"].reshape(batch, seq, hq, hd), cos, sin))
+    k = rnd(rope_fwd(outs["k"].reshape(batch, seq, hkv, hd), cos, sin))
+    v = rnd(outs["v"].reshape(batch, seq, hkv, hd))
+    att, prob = attention_fwd(q, k, v, hq // hkv, rnd)
     att = att.reshape(t, hq * hd)
     c.update(q=q, k=k, v=v, prob=prob, att=att, cos=cos, sin=sin)
     a, b = lora["o"]
-    o, hs["o"] = lora_proj_fwd(att, weights["o"], a, b, s, lora_on)
+    o, hs["o"] = lora_proj_fwd(att, weights["o"], a, b, s, lora_on, rnd)
     h = x + o
     n2, r2 = rmsnorm_fwd(h, weights["g2"], shp.rms_eps)
     c.update(h=h, n2=n2, r2=r2)
     a, b = lora["gate"]
-    gt, hs["gate"] = lora_proj_fwd(n2, weights["gate"], a, b, s, lora_on)
+    gt, hs["gate"] = lora_proj_fwd(n2, weights["gate"], a, b, s, lora_on, rnd)
     a, b = lora["up"]
-    up, hs["up"] = lora_proj_fwd(n2, weights["up"], a, b, s, lora_on)
+    up, hs["up"] = lora_proj_fwd(n2, weights["up"], a, b, s, lora_on, rnd)
     act = silu(gt) * up
     c.update(gt=gt, up=up, act=act)
     a, b = lora["down"]
-    d, hs["down"] = lora_proj_fwd(act, weights["down"], a, b, s, lora_on)
+    d, hs["down"] = lora_proj_fwd(act, weights["down"], a, b, s, lora_on, rnd)
     y = h + d
     c["hs"] = hs
     return y, c
 
 
-def layer_backward(dy, cache, weights, lora, shp: LayerShape, batch, seq):
+def layer_backward(dy, cache, weights, lora, shp: LayerShape, batch, seq, rnd=_ident):
     """Backward of ``layer_forward`` (LoRA on).  Returns (dx, grads) with grads a dict
     proj -> (dA [r, in], dB [out, r])."""
     s = shp.scale
@@ -206,7 +231,7 @@ def layer_backward(dy, cache, weights, lora, shp: LayerShape, batch, seq):
     grads = {}
     # y = h + down(act)
     a, b = lora["down"]
-    dact, da_, db_ = lora_proj_bwd(dy, cache["act"], weights["down"], a, b, hs["down"], s)
+    dact, da_, db_ = lora_proj_bwd(dy, cache["act"], weights["down"], a, b, hs["down"], s, rnd)
     grads["down"] = (da_, db_)
     dh = dy.copy()
     # act = silu(gt) * up
@@ -214,26 +239,26 @@ def layer_backward(dy, cache, weights, lora, shp: LayerShape, batch, seq):
     dgt = dact * up * silu_grad(gt)
     dup = dact * silu(gt)
     a, b = lora["gate"]
-    dn2_g, da_, db_ = lora_proj_bwd(dgt, cache["n2"], weights["gate"], a, b, hs["gate"], s)
+    dn2_g, da_, db_ = lora_proj_bwd(dgt, cache["n2"], weights["gate"], a, b, hs["gate"], s, rnd)
     grads["gate"] = (da_, db_)
     a, b = lora["up"]
-    dn2_u, da_, db_ = lora_proj_bwd(dup, cache["n2"], weights["up"], a, b, hs["up"], s)
+    dn2_u, da_, db_ = lora_proj_bwd(dup, cache["n2"], weights["up"], a, b, hs["up"], s, rnd)
     grads["up"] = (da_, db_)
     dh = dh + rmsnorm_bwd(dn2_g + dn2_u, cache["h"], weights["g2"], cache["r2"])
     # h = x + o(att)
     dx = dh.copy()
     a, b = lora["o"]
-    datt, da_, db_ = lora_proj_bwd(dh, cache["att"], weights["o"], a, b, hs["o"], s)
+    datt, da_, db_ = lora_proj_bwd(dh, cache["att"], weights["o"], a, b, hs["o"], s, rnd)
     grads["o"] = (da_, db_)
     dq, dk, dv = attention_bwd(datt.reshape(batch, seq, hq, hd), cache["q"], cache["k"],
-                               cache["v"], cache["prob"], hq // hkv)
+                               cache["v"], cache["prob"], hq // hkv, rnd)
     dq = rope_bwd(dq, cache["cos"], cache["sin"]).reshape(t, hq * hd)
     dk = rope_bwd(dk, cache["cos"], cache["sin"]).reshape(t, hkv * hd)
     dv = dv.reshape(t, hkv * hd)
     dn1 = np.zeros_like(cache["n1"])
     for p, dp in (("q", dq), ("k", dk), ("v", dv)):
         a, b = lora[p]
-        dxp, da_, db_ = lora_proj_bwd(dp, cache["n1"], weights[p], a, b, hs[p], s)
+        dxp, da_, db_ = lora_proj_bwd(dp, cache["n1"], weights[p], a, b, hs[p], s, rnd)
         grads[p] = (da_, db_)
         dn1 = dn1 + dxp
     dx = dx + rmsnorm_bwd(dn1, cache["x"], weights["g1"], cache["r1"])

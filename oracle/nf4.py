@@ -90,13 +90,13 @@ def nf4_codebook() -> np.ndarray:
 def nearest_level(n: np.ndarray, levels: np.ndarray) -> np.ndarray:
     """Index of the nearest level to each float32 n; ties go to the higher index.
 
-    Distances are formed in float64, where |n - level| is exact for float32 inputs.
+    The midpoints of adjacent levels are exact in float64; the nearest level is the
+    number of midpoints <= n (a tie sits exactly on a midpoint and counts it, so it
+    goes up).  The tests pin this against a brute-force argmin of |n - level|.
     """
-    n64 = np.asarray(n, dtype=np.float64)[..., None]
-    dist = np.abs(n64 - levels.astype(np.float64)[None, :])
-    # argmin returns the first minimum; scanning the reversed table makes ties pick
-    # the highest index.
-    return (15 - np.argmin(dist[..., ::-1], axis=-1)).astype(np.uint8)
+    lv = levels.astype(np.float64)
+    mids = (lv[:-1] + lv[1:]) / 2.0
+    return np.searchsorted(mids, np.asarray(n, dtype=np.float64), side="right").astype(np.uint8)
 
 
 def quantize_nf4(w_bf16: np.ndarray, block: int = NF4_BLOCK, chunk: int = 1 << 20):

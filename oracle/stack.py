@@ -18,10 +18,11 @@ So the stack is the plain composition of ``model.layer_forward`` over the layers
 backward recomputes each layer from its saved input (its checkpoint) and applies
 ``model.layer_backward`` in reverse order.
 
-Parity mode rounds to bf16 (round-to-nearest-even) exactly at: the input X and the
-upstream gradient dY, every layer output (= next layer's input and checkpoint), and
-every inter-layer dX.  The dequantised weights are bf16 by construction.  Everything
-inside a layer stays float64.  Exact mode rounds nowhere.
+Parity mode rounds to bf16 (round-to-nearest-even) at: the input X and the upstream
+gradient dY, every layer output (= next layer's input and checkpoint), every
+inter-layer dX, and the operands of every matrix product inside a layer (bf16 compute
+dtype, see ``model``).  The dequantised weights are bf16 by construction.  All
+accumulation is float64.  Exact mode rounds nowhere.
 """
 from __future__ import annotations
 
@@ -33,6 +34,14 @@ from .model import PROJS, LayerShape, layer_backward, layer_forward
 
 def _round(x, parity):
     return nf4.bf16_round(x).astype(np.float64) if parity else np.asarray(x, dtype=np.float64)
+
+
+def _bf16(x):
+    return nf4.bf16_round(x).astype(np.float64)
+
+
+def _rnd(parity):
+    return _bf16 if parity else (lambda x: x)
 
 
 # ----------------------------------------------------------------- base weights
@@ -76,7 +85,7 @@ def stack_forward(x, layer_weights, loras, shp: LayerShape, batch, seq, lora_on=
     ckpts = []
     for l in range(n_layers):
         ckpts.append(x)
-        y, _ = layer_forward(x, get(l), _lora64(loras[l]), shp, batch, seq, lora_on)
+        y, _ = layer_forward(x, get(l), _lora64(loras[l]), shp, batch, seq, lora_on, _rnd(parity))
         x = _round(y, parity)
     return x, ckpts
 
@@ -92,8 +101,8 @@ def stack_backward(dy, ckpts, layer_weights, loras, shp: LayerShape, batch, seq,
     for l in reversed(range(n_layers)):
         w = get(l)
         lo = _lora64(loras[l])
-        _, cache = layer_forward(ckpts[l], w, lo, shp, batch, seq, True)   # recompute
-        dx, grads[l] = layer_backward(dy, cache, w, lo, shp, batch, seq)
+        _, cache = layer_forward(ckpts[l], w, lo, shp, batch, seq, True, _rnd(parity))   # recompute
+        dx, grads[l] = layer_backward(dy, cache, w, lo, shp, batch, seq, _rnd(parity))
         dy = _round(dx, parity)
     return dy, grads
 

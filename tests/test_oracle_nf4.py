@@ -120,31 +120,36 @@ def test_bf16_round_float64_brute_force():
 
 
 # ------------------------------------------------------------------ quantiser pins
-def test_nearest_level_brute_force_equals_midpoint_search():
+def _nearest_brute(n, lv):
+    """argmin over the 16 levels of |n - level| in float64 (exact for float32 n),
+    scanning from the top so that ties pick the higher index."""
+    dist = np.abs(np.asarray(n, np.float64)[:, None] - lv.astype(np.float64)[None, :])
+    return (15 - np.argmin(dist[:, ::-1], axis=1)).astype(np.uint8)
+
+
+def test_nearest_level_equals_brute_force():
     lv = nf4.nf4_codebook()
     mids = (lv[:-1].astype(np.float64) + lv[1:].astype(np.float64)) / 2.0
     rng = np.random.default_rng(2)
     n = rng.uniform(-1, 1, size=1_000_000).astype(np.float32)
-    # add every float32 within a few ulps of each midpoint (covers exact ties)
+    # every float32 within a few ulps of each midpoint (covers exact ties)
     near = []
     for m in mids:
         f = np.float32(m)
         for k in range(-3, 4):
-            near.append(np.nextafter(f, np.float32(np.sign(k) * 2), dtype=np.float32) if k else f)
             f2 = f
             for _ in range(abs(k)):
                 f2 = np.nextafter(f2, np.float32(np.sign(k) * 2))
             near.append(f2)
-    n = np.concatenate([n, np.array(near, np.float32), lv])
-    got = nf4.nearest_level(n, lv)
-    want = np.searchsorted(mids, n.astype(np.float64), side="right")   # ties -> higher
-    assert np.array_equal(got, want.astype(np.uint8))
+    n = np.concatenate([n, np.array(near, np.float32), lv, -lv])
+    assert np.array_equal(nf4.nearest_level(n, lv), _nearest_brute(n, lv))
 
 
 def test_exact_tie_goes_to_higher_index():
     lv = np.arange(16, dtype=np.float32) / 8 - 1          # midpoints exactly representable
     n = np.array([(lv[3] + lv[4]) / 2], np.float32)
     assert nf4.nearest_level(n, lv)[0] == 4
+    assert _nearest_brute(n, lv)[0] == 4
 
 
 def test_nibble_order():
