@@ -1,0 +1,219 @@
+"""Throughput of the streamed LoRA training step (forward + recompute backward) at the
+Llama-3.1-8B shape on one MI355X, through the C ABI.
+
+Workload: 32 decoder layers, hidden 4096, 32/8 heads x 128, SwiGLU 14336; base
+weights ~ N(0, 0.02) in bf16, NF4-packed (block 64) with double-quantised absmax
+(8-bit, block 256) in pinned host RAM; LoRA r 16 / alpha 32 on all seven
+projections; batch 8 x seq 512 bf16 X ~ N(0, 1), dY ~ N(0, 1); every layer streamed
+through a two-slot device pool for the forward and again for the recompute
+backward.  Synthetic data, random weights (no checkpoints or datasets).
+
+One step = ls_forward + ls_backward + ls_sync; inputs are resident in HBM when the
+timed region starts.  Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def h2d_probe(torch, nbytes=256 << 20, reps=6):
+    """Best-of-N pinned host -> device copy rate (GB/s) on a side stream."""
+    src = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+    dst = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0")
+    s = torch.cuda.Stream()
+    best = float("inf")
+    with torch.cuda.stream(s):
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(s)
+            dst.copy_(src, non_blocking=True)
+            e1.record(s)
+            e1.synchronize()
+            best = min(best, e0.elapsed_time(e1))
+    return nbytes / (best * 1e-3) / 1e9
+
+
+def cpu_baseline(w, n_layers=1, batch=1, seq=512):
+    """The oracle, untuned, on a bounded sample: n_layers of the stack at batch x seq,
+    timed for one forward + recompute backward, scaled to the stack's depth."""
+    import numpy as np
+    from layer_streamed_qlora_amd import synth
+    from oracle import model, stack
+
+    sub = w.with_(n_layers=n_layers, batch=batch, seq=seq)
+    layers = [stack.dequant_layer(stack.quantize_layer(synth.layer_weights(w, l), w.quant, w.double_quant))
+              for l in range(n_layers)]
+    loras = [synth.layer_lora(w, l) for l in range(n_layers)]
+    x, dy = synth.activations(sub)
+    shp = model.LayerShape(w.hidden, w.n_heads, w.n_kv_heads, w.head_dim, w.intermediate, w.rms_eps,
+                           w.rope_theta, w.lora_r, w.lora_alpha)
+    t0 = time.perf_counter()
+    stack.train_step(x, dy, layers, loras, shp, batch, seq, parity=True)
+    dt = time.perf_counter() - t0
+    per_token_stack = dt * (w.n_layers / n_layers) / (batch * seq)
+    cores = int(os.environ.get("OMP_NUM_THREADS") or os.environ.get("OPENBLAS_NUM_THREADS") or os.cpu_count())
+    return {"value": 1.0 / per_token_stack, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{n_layers} of {w.n_layers} layers at batch {batch} x seq {seq}, one forward + recompute "
+                      f"backward in {dt:.2f} s, scaled by depth ({w.n_layers}/{n_layers})"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="llama8b")
+    ap.add_argument("--layers", type=int, default=0, help="override depth (0 = the workload's)")
+    ap.add_argument("--buffers", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-profile", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}); this build has no multi-GPU path.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from layer_streamed_qlora_amd import binding as B
+    from layer_streamed_qlora_amd import synth
+
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    w = synth.WORKLOADS[args.workload]
+    if args.layers:
+        w = w.with_(n_layers=args.layers)
+    T = w.tokens
+    profile = 0 if args.no_profile else 1
+    cfg = B.make_config(w, n_buffers=args.buffers, profile=profile)
+    t0 = time.time()
+    ctx = B.Context(cfg)
+    for l in range(w.n_layers):
+        dw = synth.device_layer_weights(w, l)
+        host = {k: v.view(torch.int16).cpu().numpy().view(np.uint16) for k, v in dw.items()}
+        ctx.stage_layer(l, host)
+        del dw, host
+    loras = [synth.device_lora(w, l) for l in range(w.n_layers)]
+    grads = []
+    for l in range(w.n_layers):
+        gl = {}
+        for i, p in enumerate(synth.PROJS):
+            a, b = loras[l][p]
+            da, db = torch.zeros_like(a), torch.zeros_like(b)
+            gl[p] = (da, db)
+            ctx.set_lora(l, i, a.data_ptr(), b.data_ptr(), da.data_ptr(), db.data_ptr())
+        grads.append(gl)
+    g = torch.Generator(device="cuda:0")
+    g.manual_seed(7)
+    X = torch.randn((T, w.hidden), generator=g, device="cuda:0").to(torch.bfloat16)
+    g.manual_seed(8)
+    dY = torch.randn((T, w.hidden), generator=g, device="cuda:0").to(torch.bfloat16)
+    Y = torch.empty_like(X)
+    dX = torch.empty_like(X)
+    torch.cuda.synchronize()
+    log(f"setup {time.time() - t0:.1f} s: {w.n_layers} layers staged, blob {ctx.stats().blob_bytes / 1e6:.2f} MB")
+    probe = h2d_probe(torch)
+    log(f"host-link probe {probe:.2f} GB/s")
+
+    def step():
+        ctx.forward(X.data_ptr(), w.batch, w.seq, 1, Y.data_ptr())
+        ctx.backward(dY.data_ptr(), dX.data_ptr(), 0)
+        ctx.sync()
+
+    for i in range(args.warmup):
+        step()
+        log(f"warmup step {i} done")
+    torch.cuda.synchronize()
+    s0 = ctx.stats()
+    acc = {"copy": 0.0, "compute": 0.0, "overlap": 0.0, "span": 0.0}
+    kacc = {k: [0, 0.0, 0.0, 0.0] for k in B.KERNEL_CLASSES}
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        step()
+        st = ctx.stats()
+        acc["copy"] += st.last_copy_ms
+        acc["compute"] += st.last_compute_ms
+        acc["overlap"] += st.last_overlap_ms
+        acc["span"] += st.last_span_ms
+        for j, k in enumerate(B.KERNEL_CLASSES):
+            kacc[k][0] += st.k_launches[j]
+            kacc[k][1] += st.k_ms[j]
+            kacc[k][2] += st.k_flop[j]
+            kacc[k][3] += st.k_bytes[j]
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    s1 = ctx.stats()
+    log(f"timed {args.steps} steps in {elapsed:.3f} s")
+    ms_per_step = elapsed / args.steps * 1e3
+    value = T * args.steps / elapsed
+    assert torch.isfinite(Y.float()).all() and torch.isfinite(dX.float()).all(), "non-finite output"
+
+    copies = (s1.h2d_copies - s0.h2d_copies) / args.steps
+    h2d_bytes = (s1.h2d_bytes - s0.h2d_bytes) / args.steps
+    out = {
+        "metric": "train tokens/s (fwd+bwd, streamed NF4 base) @Llama-3.1-8B shape",
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{args.workload}: Llama-3.1-8B-shaped decoder stack, {w.n_layers} layers, "
+                               f"hidden {w.hidden}, {w.n_heads}/{w.n_kv_heads} heads x {w.head_dim}, "
+                               f"SwiGLU {w.intermediate}, NF4 block 64 + double-quant absmax, "
+                               f"LoRA r {w.lora_r} alpha {int(w.lora_alpha)} on 7 projections, "
+                               f"streamed through {args.buffers} device slots",
+                   "batch": w.batch, "seq": w.seq, "tokens_per_step": T, "parallelism": "none (1 GPU)"},
+    }
+    if profile:
+        kern = {k: {"launches_per_step": v[0] / args.steps, "ms_per_step": v[1] / args.steps,
+                    "tflops": (v[2] / (v[1] * 1e-3) / 1e12) if v[1] > 0 else None,
+                    "avg_launch_ms": v[1] / v[0] if v[0] else None} for k, v in kacc.items()}
+        dom = max(("gemm_fwd", "gemm_bwd"), key=lambda k: kacc[k][1])
+        kl, kms, kfl, kby = kacc[dom]
+        achieved = kfl / (kms * 1e-3) / 1e12
+        out["roofline"] = {"bound": "mfma", "kernel": f"fused dequant GEMM ({dom})", "achieved": round(achieved, 1),
+                           "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                           "traffic": None, "avg_launch_ms": round(kms / kl, 4),
+                           "flop_per_launch": kfl / kl}
+        gemm_ms = kacc["gemm_fwd"][1] + kacc["gemm_bwd"][1]
+        gemm_fl = kacc["gemm_fwd"][2] + kacc["gemm_bwd"][2]
+        out["mfma"] = {"dequant_gemm_tflops": round(gemm_fl / (gemm_ms * 1e-3) / 1e12, 1),
+                       "frac_of_peak": round(gemm_fl / (gemm_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                       "kernels": kern}
+        copy_ms = acc["copy"] / args.steps
+        out["h2d"] = {"bytes_per_step": h2d_bytes, "copies_per_step": copies,
+                      "achieved_GBps": round(h2d_bytes / (copy_ms * 1e-3) / 1e9, 2) if copy_ms else None,
+                      "probe_GBps": round(probe, 2),
+                      "frac_of_probe": round(h2d_bytes / (copy_ms * 1e-3) / 1e9 / probe, 4) if copy_ms else None,
+                      "copy_ms_per_step": round(copy_ms, 3),
+                      "overlap_ms_per_step": round(acc["overlap"] / args.steps, 3),
+                      "copy_hidden_frac": round(acc["overlap"] / acc["copy"], 4) if acc["copy"] else None}
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        out["cpu_baseline"] = cpu_baseline(w)
+    ctx.close()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -312,10 +312,17 @@ __device__ __forceinline__ void mma_stage(const uint16_t* sa, const uint16_t* sw
 
 // Epilogue through LDS: half a tile (128 rows) at a time, each thread then moves
 // 4 consecutive columns per step with one 8- or 16-byte global access.
-// out(m, n) for m < M_lim, n < N_lim; resid (bf16) added when given.
-template <bool F32OUT>
+// out(m, n) for m < M_lim, n < N_lim; a bf16 or float32 residual is added first; the
+// rotary embedding (float32) is applied to columns below rope_cols (counted from the
+// start of the whole output, col_base = this group's first column) before rounding.
+struct Epi {
+  void* out = nullptr; int ldo = 0; bool f32 = false;
+  const uint16_t* r16 = nullptr; const float* r32 = nullptr; int ldr = 0;
+  const float2* rope_tab = nullptr; int rope_cols = 0, col_base = 0, seq = 1, hd = 128;
+};
+
 __device__ __forceinline__ void epilogue(Smem& sm, f32x16_t acc[4][4], int m0, int n0, int M_lim, int N_lim,
-                                         void* out, int ldo, const uint16_t* resid, int ldr) {
+                                         const Epi& E) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   constexpr int OP = BN + 4;
@@ -343,24 +350,41 @@ __device__ __forceinline__ void epilogue(Smem& sm, f32x16_t acc[4][4], int m0, i
       if (m >= M_lim || n >= N_lim) continue;
       const float4 v = *reinterpret_cast<const float4*>(&sm.u.out[r * OP + 4 * q]);
       float y[4] = {v.x, v.y, v.z, v.w};
-      const int64_t o = (int64_t)m * ldo + n;
-      if (resid) {
-        const int64_t ro = (int64_t)m * ldr + n;
-        if (n + 4 <= N_lim) {
-          const uint2 rr = *reinterpret_cast<const uint2*>(resid + ro);
-          y[0] += bf16_lo(rr.x); y[1] += bf16_hi(rr.x); y[2] += bf16_lo(rr.y); y[3] += bf16_hi(rr.y);
-        } else {
-          for (int e = 0; e < 4 && n + e < N_lim; ++e) y[e] += bf16_lo(resid[ro + e]);
+      const int gc = E.col_base + n;
+      if (gc < E.rope_cols) {
+        const int hh = E.hd / 2, i0 = gc % E.hd;
+        const int lo = i0 < hh;
+        const float4 pv = *reinterpret_cast<const float4*>(&sm.u.out[r * OP + 4 * q + (lo ? hh : -hh)]);
+        const float pr[4] = {pv.x, pv.y, pv.z, pv.w};
+        const float2* tab = E.rope_tab + (int64_t)(m % E.seq) * hh + (i0 % hh);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float2 cs = tab[e];
+          y[e] = lo ? y[e] * cs.x - pr[e] * cs.y : y[e] * cs.x + pr[e] * cs.y;
         }
       }
-      if constexpr (F32OUT) {
-        float* po = reinterpret_cast<float*>(out) + o;
-        if (n + 4 <= N_lim) *reinterpret_cast<float4*>(po) = make_float4(y[0], y[1], y[2], y[3]);
+      const int64_t o = (int64_t)m * E.ldo + n;
+      const bool full = n + 4 <= N_lim;
+      if (E.r16 || E.r32) {
+        const int64_t ro = (int64_t)m * E.ldr + n;
+        if (E.r32) {
+          if (full) { const float4 rr = *reinterpret_cast<const float4*>(E.r32 + ro); y[0] += rr.x; y[1] += rr.y; y[2] += rr.z; y[3] += rr.w; }
+          else for (int e = 0; e < 4 && n + e < N_lim; ++e) y[e] += E.r32[ro + e];
+        } else if (full) {
+          const uint2 rr = *reinterpret_cast<const uint2*>(E.r16 + ro);
+          y[0] += bf16_lo(rr.x); y[1] += bf16_hi(rr.x); y[2] += bf16_lo(rr.y); y[3] += bf16_hi(rr.y);
+        } else {
+          for (int e = 0; e < 4 && n + e < N_lim; ++e) y[e] += bf16_lo(E.r16[ro + e]);
+        }
+      }
+      if (E.f32) {
+        float* po = reinterpret_cast<float*>(E.out) + o;
+        if (full) *reinterpret_cast<float4*>(po) = make_float4(y[0], y[1], y[2], y[3]);
         else for (int e = 0; e < 4 && n + e < N_lim; ++e) po[e] = y[e];
       } else {
-        uint16_t* po = reinterpret_cast<uint16_t*>(out) + o;
+        uint16_t* po = reinterpret_cast<uint16_t*>(E.out) + o;
         const uint32_t p0 = pack_bf16x2(y[0], y[1]), p1 = pack_bf16x2(y[2], y[3]);
-        if (n + 4 <= N_lim) *reinterpret_cast<uint2*>(po) = make_uint2(p0, p1);
+        if (full) *reinterpret_cast<uint2*>(po) = make_uint2(p0, p1);
         else {
           const uint16_t h[4] = {(uint16_t)p0, (uint16_t)(p0 >> 16), (uint16_t)p1, (uint16_t)(p1 >> 16)};
           for (int e = 0; e < 4 && n + e < N_lim; ++e) po[e] = h[e];
@@ -446,8 +470,16 @@ __global__ void __launch_bounds__(NTHREADS, 1) k_gemm_fwd(FwdArgs args, int n_ti
     }
     __syncthreads();
   }
-  epilogue<false>(sm, acc, m0, n0, args.M, n_out, args.y + G.out_col0, args.ldy,
-                  args.resid ? args.resid + G.out_col0 : nullptr, args.ldr);
+  Epi E;
+  E.f32 = args.y32 != nullptr;
+  E.out = E.f32 ? (void*)(args.y32 + G.out_col0) : (void*)(args.y + G.out_col0);
+  E.ldo = args.ldy;
+  E.r16 = args.resid ? args.resid + G.out_col0 : nullptr;
+  E.r32 = args.resid32 ? args.resid32 + G.out_col0 : nullptr;
+  E.ldr = args.ldr;
+  E.rope_tab = args.rope_tab; E.rope_cols = args.rope_tab ? args.rope_cols : 0;
+  E.col_base = G.out_col0; E.seq = args.seq; E.hd = args.head_dim;
+  epilogue(sm, acc, m0, n0, args.M, n_out, E);
 }
 
 // ------------------------------------------------------------------ backward
@@ -521,8 +553,11 @@ __global__ void __launch_bounds__(NTHREADS, 1) k_gemm_bwd(BwdArgs args, int n_ti
     }
     __syncthreads();
   }
-  if (args.out32) epilogue<true>(sm, acc, m0, j0, args.M, args.N, args.out32, args.ldo, nullptr, 0);
-  else epilogue<false>(sm, acc, m0, j0, args.M, args.N, args.out16, args.ldo, nullptr, 0);
+  Epi E;
+  E.f32 = args.out32 != nullptr;
+  E.out = E.f32 ? (void*)args.out32 : (void*)args.out16;
+  E.ldo = args.ldo;
+  epilogue(sm, acc, m0, j0, args.M, args.N, E);
 }
 
 // --------------------------------------------------------- standalone dequant

@@ -39,40 +39,73 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
   return s;
 }
 
+template <class T> __device__ __forceinline__ float ld(const T* p, int64_t i);
+template <> __device__ __forceinline__ float ld<uint16_t>(const uint16_t* p, int64_t i) { return bf(p[i]); }
+template <> __device__ __forceinline__ float ld<float>(const float* p, int64_t i) { return p[i]; }
+
 // one 256-thread block per row
-__global__ void __launch_bounds__(256) k_rmsnorm_fwd(const uint16_t* x, const uint16_t* g, uint16_t* y, float* rstd,
+template <class XT>
+__global__ void __launch_bounds__(256) k_rmsnorm_fwd(const XT* x, const uint16_t* g, uint16_t* y, float* rstd,
                                                      int D, float eps) {
   __shared__ float red[4];
   const int64_t row = blockIdx.x;
-  const uint16_t* xr = x + row * D;
+  const XT* xr = x + row * D;
   float ss = 0.f;
-  for (int i = threadIdx.x; i < D; i += 256) { const float v = bf(xr[i]); ss += v * v; }
+  for (int i = threadIdx.x; i < D; i += 256) { const float v = ld(xr, i); ss += v * v; }
   ss = block_sum<256>(ss, red);
   const float r = 1.0f / sqrtf(ss / (float)D + eps);
   if (threadIdx.x == 0 && rstd) rstd[row] = r;
   uint16_t* yr = y + row * D;
-  for (int i = threadIdx.x; i < D; i += 256) yr[i] = tobf(bf(xr[i]) * r * bf(g[i]));
+  for (int i = threadIdx.x; i < D; i += 256) yr[i] = tobf(ld(xr, i) * r * bf(g[i]));
 }
 
 // dx = dres + r g dn - (r^3 / D) x sum(dn g x)
-__global__ void __launch_bounds__(256) k_rmsnorm_bwd(const float* dn, const uint16_t* x, const uint16_t* g,
+template <class XT>
+__global__ void __launch_bounds__(256) k_rmsnorm_bwd(const float* dn, const XT* x, const uint16_t* g,
                                                      const float* rstd, const float* dres32, const uint16_t* dres16,
                                                      float* dx32, uint16_t* dx16, int D) {
   __shared__ float red[4];
   const int64_t row = blockIdx.x;
   const float* dnr = dn + row * D;
-  const uint16_t* xr = x + row * D;
+  const XT* xr = x + row * D;
   float s = 0.f;
-  for (int i = threadIdx.x; i < D; i += 256) s += dnr[i] * bf(g[i]) * bf(xr[i]);
+  for (int i = threadIdx.x; i < D; i += 256) s += dnr[i] * bf(g[i]) * ld(xr, i);
   s = block_sum<256>(s, red);
   const float r = rstd[row];
   const float c = r * r * r / (float)D * s;
   for (int i = threadIdx.x; i < D; i += 256) {
-    float v = r * bf(g[i]) * dnr[i] - c * bf(xr[i]);
+    float v = r * bf(g[i]) * dnr[i] - c * ld(xr, i);
     if (dres32) v += dres32[row * D + i];
     else if (dres16) v += bf(dres16[row * D + i]);
     if (dx32) dx32[row * D + i] = v;
     if (dx16) dx16[row * D + i] = tobf(v);
+  }
+}
+
+// float32 -> bf16 with the inverse rotation on the first nh heads; one thread per
+// (token, column pair or lone column)
+__global__ void k_rope_bwd_convert(const float* src, uint16_t* dst, int ld, int64_t T, int seq, int nh, int hd,
+                                   const float2* tab) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int half = hd / 2;
+  const int rope_pairs = nh * half;                    // rotated column pairs per row
+  const int rest = ld - nh * hd;                        // plain columns per row
+  const int per_row = rope_pairs + rest;
+  if (idx >= T * per_row) return;
+  const int64_t t = idx / per_row;
+  const int c = (int)(idx % per_row);
+  const float* s = src + t * ld;
+  uint16_t* d = dst + t * ld;
+  if (c < rope_pairs) {
+    const int h = c / half, i = c % half;
+    const int col = h * hd + i;
+    const float2 cs = tab[(int64_t)(t % seq) * half + i];
+    const float d1 = s[col], d2 = s[col + half];
+    d[col] = tobf(d1 * cs.x + d2 * cs.y);
+    d[col + half] = tobf(d2 * cs.x - d1 * cs.y);
+  } else {
+    const int col = nh * hd + (c - rope_pairs);
+    d[col] = tobf(s[col]);
   }
 }
 
@@ -135,25 +168,25 @@ __global__ void __launch_bounds__(256) k_softmax_bwd(const float* dP, const uint
 
 __device__ __forceinline__ float sigmoidf(float z) { return 1.0f / (1.0f + __expf(-z)); }
 
-__global__ void k_swiglu_fwd(const uint16_t* gu, int ldgu, int I, uint16_t* act, int64_t n) {
+__global__ void k_swiglu_fwd(const float* gu, int I, uint16_t* act, int64_t n) {
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= n) return;
   const int64_t t = idx / I;
   const int j = (int)(idx % I);
-  const float g = bf(gu[t * ldgu + j]), u = bf(gu[t * ldgu + I + j]);
+  const float g = gu[t * 2 * I + j], u = gu[t * 2 * I + I + j];
   act[t * I + j] = tobf(g * sigmoidf(g) * u);
 }
 
-__global__ void k_swiglu_bwd(const uint16_t* gu, int ldgu, const uint16_t* dact, int I, uint16_t* dgu, int64_t n) {
+__global__ void k_swiglu_bwd(const float* gu, const float* dact, int I, uint16_t* dgu, int64_t n) {
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= n) return;
   const int64_t t = idx / I;
   const int j = (int)(idx % I);
-  const float g = bf(gu[t * ldgu + j]), u = bf(gu[t * ldgu + I + j]);
-  const float da = bf(dact[t * I + j]);
+  const float g = gu[t * 2 * I + j], u = gu[t * 2 * I + I + j];
+  const float da = dact[t * I + j];
   const float sg = sigmoidf(g);
-  dgu[t * ldgu + j] = tobf(da * u * sg * (1.0f + g * (1.0f - sg)));
-  dgu[t * ldgu + I + j] = tobf(da * g * sg);
+  dgu[t * 2 * I + j] = tobf(da * u * sg * (1.0f + g * (1.0f - sg)));
+  dgu[t * 2 * I + I + j] = tobf(da * g * sg);
 }
 
 // dst[r, c] = scale * src[r, c] (transpose: dst[c, r]) for c < cols, 0 for cols <= c < pad_cols
@@ -167,6 +200,18 @@ __global__ void k_f32_to_bf16(const float* src, int64_t lds, uint16_t* dst, int6
   else dst[(int64_t)r * ldd + c] = v;
 }
 
+// grid.y = job; grid-stride over the job's elements
+__global__ void k_convert_batch(ConvBatch b) {
+  const ConvJob& j = b.job[blockIdx.y];
+  const int64_t n = (int64_t)j.rows * j.pad_cols;
+  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < n; idx += (int64_t)gridDim.x * blockDim.x) {
+    const int r = (int)(idx / j.pad_cols), c = (int)(idx % j.pad_cols);
+    const uint16_t v = c < j.cols ? tobf(j.scale * j.src[(int64_t)r * j.lds + c]) : (uint16_t)0;
+    if (j.transpose) j.dst[(int64_t)c * j.ldd + r] = v;
+    else j.dst[(int64_t)r * j.ldd + c] = v;
+  }
+}
+
 __global__ void k_fill_f32(float* p, int64_t n, float v) {
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx < n) p[idx] = v;
@@ -176,18 +221,32 @@ __global__ void k_fill_f32(float* p, int64_t n, float v) {
 
 static inline unsigned blocks_for(int64_t n, int t) { return (unsigned)((n + t - 1) / t); }
 
-hipError_t launch_rmsnorm_fwd(const uint16_t* x, const uint16_t* g, uint16_t* y, float* rstd, int32_t T, int32_t D,
-                              float eps, hipStream_t s) {
+hipError_t launch_rmsnorm_fwd(const uint16_t* x16, const float* x32, const uint16_t* g, uint16_t* y, float* rstd,
+                              int32_t T, int32_t D, float eps, hipStream_t s) {
   if (T <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_rmsnorm_fwd, dim3(T), dim3(256), 0, s, x, g, y, rstd, D, eps);
+  if (x32) hipLaunchKernelGGL(k_rmsnorm_fwd<float>, dim3(T), dim3(256), 0, s, x32, g, y, rstd, D, eps);
+  else hipLaunchKernelGGL(k_rmsnorm_fwd<uint16_t>, dim3(T), dim3(256), 0, s, x16, g, y, rstd, D, eps);
   return hipGetLastError();
 }
 
-hipError_t launch_rmsnorm_bwd(const float* dn, const uint16_t* x, const uint16_t* g, const float* rstd,
-                              const float* dres32, const uint16_t* dres16, float* dx32, uint16_t* dx16, int32_t T,
-                              int32_t D, hipStream_t s) {
+hipError_t launch_rmsnorm_bwd(const float* dn, const uint16_t* x16, const float* x32, const uint16_t* g,
+                              const float* rstd, const float* dres32, const uint16_t* dres16, float* dx32,
+                              uint16_t* dx16, int32_t T, int32_t D, hipStream_t s) {
   if (T <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_rmsnorm_bwd, dim3(T), dim3(256), 0, s, dn, x, g, rstd, dres32, dres16, dx32, dx16, D);
+  if (x32)
+    hipLaunchKernelGGL(k_rmsnorm_bwd<float>, dim3(T), dim3(256), 0, s, dn, x32, g, rstd, dres32, dres16, dx32, dx16, D);
+  else
+    hipLaunchKernelGGL(k_rmsnorm_bwd<uint16_t>, dim3(T), dim3(256), 0, s, dn, x16, g, rstd, dres32, dres16, dx32, dx16, D);
+  return hipGetLastError();
+}
+
+hipError_t launch_rope_bwd_convert(const float* src, uint16_t* dst, int32_t ld, int32_t T, int32_t seq, int32_t nh,
+                                   int32_t hd, const float2* tab, hipStream_t s) {
+  const int64_t per_row = (int64_t)nh * (hd / 2) + (ld - nh * hd);
+  const int64_t n = (int64_t)T * per_row;
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_rope_bwd_convert, dim3(blocks_for(n, 256)), dim3(256), 0, s, src, dst, ld, (int64_t)T, seq, nh,
+                     hd, tab);
   return hipGetLastError();
 }
 
@@ -212,18 +271,17 @@ hipError_t launch_softmax_bwd(const float* dP, const uint16_t* P, uint16_t* dS, 
   return hipGetLastError();
 }
 
-hipError_t launch_swiglu_fwd(const uint16_t* gu, int32_t ldgu, int32_t I, uint16_t* act, int32_t T, hipStream_t s) {
+hipError_t launch_swiglu_fwd(const float* gu, int32_t I, uint16_t* act, int32_t T, hipStream_t s) {
   const int64_t n = (int64_t)T * I;
   if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_swiglu_fwd, dim3(blocks_for(n, 256)), dim3(256), 0, s, gu, ldgu, I, act, n);
+  hipLaunchKernelGGL(k_swiglu_fwd, dim3(blocks_for(n, 256)), dim3(256), 0, s, gu, I, act, n);
   return hipGetLastError();
 }
 
-hipError_t launch_swiglu_bwd(const uint16_t* gu, int32_t ldgu, const uint16_t* dact, int32_t I, uint16_t* dgu,
-                             int32_t T, hipStream_t s) {
+hipError_t launch_swiglu_bwd(const float* gu, const float* dact, int32_t I, uint16_t* dgu, int32_t T, hipStream_t s) {
   const int64_t n = (int64_t)T * I;
   if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_swiglu_bwd, dim3(blocks_for(n, 256)), dim3(256), 0, s, gu, ldgu, dact, I, dgu, n);
+  hipLaunchKernelGGL(k_swiglu_bwd, dim3(blocks_for(n, 256)), dim3(256), 0, s, gu, dact, I, dgu, n);
   return hipGetLastError();
 }
 
@@ -233,6 +291,12 @@ hipError_t launch_f32_to_bf16(const float* src, int64_t lds, uint16_t* dst, int6
   if (n <= 0) return hipSuccess;
   hipLaunchKernelGGL(k_f32_to_bf16, dim3(blocks_for(n, 256)), dim3(256), 0, s, src, lds, dst, ldd, rows, cols, pad_cols,
                      scale, transpose);
+  return hipGetLastError();
+}
+
+hipError_t launch_convert_batch(const ConvBatch& b, hipStream_t s) {
+  if (b.n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_convert_batch, dim3(64, b.n), dim3(256), 0, s, b);
   return hipGetLastError();
 }
 

@@ -76,8 +76,12 @@ struct FwdArgs {
   int32_t n_groups = 0;
   FwdGroup g[kMaxGroups];
   const uint16_t* aext = nullptr; int32_t ldaext = 0; int32_t kx = 0;   // bf16 [M, >=kx]; kx multiple of 16, 0 = none
-  const uint16_t* resid = nullptr; int32_t ldr = 0; // bf16 residual added to Y (nullable)
-  uint16_t* y = nullptr; int32_t ldy = 0;           // bf16 output
+  const uint16_t* resid = nullptr;                  // bf16 residual added to Y (nullable)
+  const float* resid32 = nullptr; int32_t ldr = 0;  // or float32 residual
+  uint16_t* y = nullptr; float* y32 = nullptr; int32_t ldy = 0;   // bf16 or float32 output
+  // rotary embedding on output columns [0, rope_cols) before rounding (q and k of
+  // the fused q|k|v projection): tab[pos * hd/2 + i] = (cos, sin), pos = row % seq
+  const float2* rope_tab = nullptr; int32_t rope_cols = 0, seq = 1, head_dim = 128;
   const float* levels = nullptr;                    // device float32[16] NF4 levels
   int32_t format = WF_NF4;
 };
@@ -112,17 +116,37 @@ struct GemmArgs {
   void* C = nullptr; int64_t sCm = 0, sCn = 0; ZStride zC; int32_t c_f32 = 1;
   int32_t M = 0, N = 0, K = 0, nz = 1, zdiv = 1;
   float alpha = 1.f, beta = 0.f;
-  int32_t causal = 0;   // 1: skip tiles with n0 > m_last (C rows m, cols n); 2: limit k <= m_last
+  int32_t causal = 0;   // 1: skip tiles with n0 > m_last; 2: contraction k <= m only; 3: k >= m only
+  // split-K: ksplit > 1 splits the contraction into ksplit chunks whose float32
+  // partial results go to `partial` ([ksplit][nz][M][N]); a second kernel sums the
+  // chunks in order (deterministic) and applies alpha / beta.
+  int32_t ksplit = 1;
+  float* partial = nullptr;
 };
 hipError_t launch_gemm_generic(const GemmArgs& a, hipStream_t s);
 
+// Batched float32 -> bf16 layout conversions (LoRA operands), one launch.
+struct ConvJob {
+  const float* src = nullptr; int64_t lds = 0;
+  uint16_t* dst = nullptr; int64_t ldd = 0;
+  int32_t rows = 0, cols = 0, pad_cols = 0, transpose = 0;
+  float scale = 1.f;
+};
+constexpr int kMaxConvJobs = 32;
+struct ConvBatch { ConvJob job[kMaxConvJobs]; int32_t n = 0; };
+hipError_t launch_convert_batch(const ConvBatch& b, hipStream_t s);
+
 // Glue kernels.
-hipError_t launch_rmsnorm_fwd(const uint16_t* x, const uint16_t* g, uint16_t* y, float* rstd,
+// x is bf16 (x16) or float32 (x32): exactly one is set
+hipError_t launch_rmsnorm_fwd(const uint16_t* x16, const float* x32, const uint16_t* g, uint16_t* y, float* rstd,
                               int32_t T, int32_t D, float eps, hipStream_t s);
-// dx = dres + rmsnorm_bwd(dn); writes float32 and/or bf16 (either may be null)
-hipError_t launch_rmsnorm_bwd(const float* dn, const uint16_t* x, const uint16_t* g, const float* rstd,
-                              const float* dres32, const uint16_t* dres16, float* dx32, uint16_t* dx16,
-                              int32_t T, int32_t D, hipStream_t s);
+// dx = dres + rmsnorm_bwd(dn); x bf16 or float32; writes float32 and/or bf16
+hipError_t launch_rmsnorm_bwd(const float* dn, const uint16_t* x16, const float* x32, const uint16_t* g,
+                              const float* rstd, const float* dres32, const uint16_t* dres16, float* dx32,
+                              uint16_t* dx16, int32_t T, int32_t D, hipStream_t s);
+// float32 [T, ld] -> bf16 [T, ld], inverse rotary embedding on the first nh heads
+hipError_t launch_rope_bwd_convert(const float* src, uint16_t* dst, int32_t ld, int32_t T, int32_t seq, int32_t nh,
+                                   int32_t hd, const float2* tab, hipStream_t s);
 // rotary embedding in place on the first nh heads of a token-major [T, ld] bf16
 // buffer; tab[pos * hd/2 + i] = (cos, sin) of pos * theta^(-2i/hd)
 hipError_t launch_rope_tab(uint16_t* qk, int32_t ld, int32_t T, int32_t seq, int32_t nh, int32_t hd,
@@ -135,9 +159,10 @@ hipError_t launch_softmax_causal(const float* S, uint16_t* P, int64_t n_rows, in
 // dS = P * (dP - rowsum(P * dP)) * scale, bf16 out; dP float32, P bf16
 hipError_t launch_softmax_bwd(const float* dP, const uint16_t* P, uint16_t* dS, int64_t n_rows, int32_t seq,
                               float scale, hipStream_t s);
-hipError_t launch_swiglu_fwd(const uint16_t* gu, int32_t ldgu, int32_t I, uint16_t* act, int32_t T, hipStream_t s);
-hipError_t launch_swiglu_bwd(const uint16_t* gu, int32_t ldgu, const uint16_t* dact, int32_t I,
-                             uint16_t* dgu, int32_t T, hipStream_t s);
+// gu float32 [T, 2I] (gate | up) -> act bf16 [T, I]
+hipError_t launch_swiglu_fwd(const float* gu, int32_t I, uint16_t* act, int32_t T, hipStream_t s);
+// gu float32, dact float32 [T, I] -> dgu bf16 [T, 2I]
+hipError_t launch_swiglu_bwd(const float* gu, const float* dact, int32_t I, uint16_t* dgu, int32_t T, hipStream_t s);
 // float32 [rows, cols] (row stride lds) -> bf16 [rows, ldd] scaled, columns >= cols zero up to ldd
 hipError_t launch_f32_to_bf16(const float* src, int64_t lds, uint16_t* dst, int64_t ldd, int32_t rows,
                               int32_t cols, int32_t pad_cols, float scale, int32_t transpose, hipStream_t s);

@@ -28,6 +28,17 @@ using namespace lsq;
 namespace {
 
 constexpr int kPad = 256;    // slack after every workspace region (8-element group loads)
+constexpr int kMaxSplit = 16;
+
+// K-split for a narrow product so that about two workgroups per CU are in flight.
+int auto_split(int M, int N, int K, int nz) {
+  const int tn = N <= 32 ? 32 : 64;
+  const long base = (long)((M + 127) / 128) * ((N + tn - 1) / tn) * nz;
+  int ks = (int)std::max(1L, 512 / std::max(1L, base));
+  ks = std::min(ks, kMaxSplit);
+  ks = std::min(ks, std::max(1, K / 256));
+  return ks;
+}
 
 struct LoraReg {
   const float* A = nullptr;
@@ -43,11 +54,11 @@ struct DevPlan {
   uint64_t slots = 0, ck = 0, xref = 0;
   uint64_t n1 = 0, qkv = 0, att = 0, hb = 0, n2 = 0, gu = 0, act = 0, rstd1 = 0, rstd2 = 0;
   uint64_t hs = 0, gs = 0, s32 = 0, p16 = 0, ds16 = 0;
-  uint64_t dya = 0, dyb = 0, dh32 = 0, dh16 = 0, dact = 0, dgu = 0, datt = 0, dqkv = 0, dn32 = 0;
-  uint64_t lora = 0, lora_per_layer = 0;
+  uint64_t dya = 0, dyb = 0, dh32 = 0, dh16 = 0, da32 = 0, dgu = 0, datt = 0, dqkv = 0, dqkv32 = 0, dn32 = 0;
+  uint64_t lora = 0, lora_per_layer = 0, partial = 0, partial_bytes = 0;
   uint64_t levels = 0, rope = 0;
   // per-layer LoRA operand offsets (relative to the layer's LoRA base)
-  uint64_t a16[LS_N_PROJ] = {}, bx16[LS_N_PROJ] = {};
+  uint64_t a16[LS_N_PROJ] = {}, bx16[LS_N_PROJ] = {}, bxt16[LS_N_PROJ] = {};
   uint64_t at_qkv = 0, at_o = 0, at_gu = 0, at_d = 0;
   int n_slots = 0;
 };
@@ -70,9 +81,9 @@ DevPlan make_plan(const ls_config& c, const BlobLayout& L) {
   P.n1 = take(2 * T * h);
   P.qkv = take(2 * T * qkvd);
   P.att = take(2 * T * qd);
-  P.hb = take(2 * T * h);
+  P.hb = take(4 * T * h);             // residual stream after attention, float32
   P.n2 = take(2 * T * h);
-  P.gu = take(2 * T * 2 * I);
+  P.gu = take(4 * T * 2 * I);         // gate | up outputs, float32
   P.act = take(2 * T * I);
   P.rstd1 = take(4 * T);
   P.rstd2 = take(4 * T);
@@ -85,10 +96,11 @@ DevPlan make_plan(const ls_config& c, const BlobLayout& L) {
   P.dyb = take(2 * T * h);
   P.dh32 = take(4 * T * h);
   P.dh16 = take(2 * T * h);
-  P.dact = take(2 * T * I);
+  P.da32 = take(4 * T * I);
   P.dgu = take(2 * T * 2 * I);
   P.datt = take(2 * T * qd);
   P.dqkv = take(2 * T * qkvd);
+  P.dqkv32 = take(4 * T * qkvd);
   P.dn32 = take(4 * T * (std::max(h, qd)));
   // LoRA operands in bf16, per layer
   uint64_t lo = 0;
@@ -106,6 +118,7 @@ DevPlan make_plan(const ls_config& c, const BlobLayout& L) {
     int32_t n_out, n_in;
     proj_dims(c, p, &n_out, &n_in);
     P.bx16[p] = ltake(2 * (uint64_t)n_out * r16);
+    P.bxt16[p] = ltake(2 * (uint64_t)n_out * r16);
   }
   // A^T stacked per group, [n_in, group_r16]: q|k|v, o, gate|up, down
   P.at_qkv = ltake(2 * h * 3 * r16);
@@ -114,6 +127,9 @@ DevPlan make_plan(const ls_config& c, const BlobLayout& L) {
   P.at_d = ltake(2 * I * r16);
   P.lora_per_layer = align_up(lo, kAlign);
   P.lora = take(P.lora_per_layer * (uint64_t)c.n_layers);
+  // split-K partials of the rank-r reductions: up to kMaxSplit chunks of [rows, r16]
+  P.partial_bytes = 4ull * kMaxSplit * std::max<uint64_t>(std::max<uint64_t>(T, I), std::max<uint64_t>(h, qkvd)) * r16;
+  P.partial = take(P.partial_bytes);
   P.levels = take(64);
   P.rope = take(8ull * (uint64_t)c.max_seq * (uint64_t)(c.head_dim / 2));
   P.total = align_up(off, kAlign);
@@ -377,22 +393,35 @@ double wbytes(const ls_ctx* c, int p) {   // stored bytes of projection p in a b
   return (double)P.bytes_w + (c->cfg.double_quant ? (double)P.nblocks + 4.0 * P.ngroups : 4.0 * P.nblocks);
 }
 
-// bf16 copies of the adapters: A16 [r16, in], Bx16 [out, r16], A^T stacked per group.
+// bf16 copies of the adapters, one launch per layer: A16 [r16, in], Bx16 [out, r16],
+// BxT16 [r16, out] and A^T stacked per group [in, group r16].
 ls_status prep_lora(ls_ctx* c, int l, const Dims& d) {
   const int gcol[LS_N_PROJ] = {0, 1, 2, 0, 0, 1, 0};
   const uint64_t at_off[LS_N_PROJ] = {c->plan.at_qkv, c->plan.at_qkv, c->plan.at_qkv, c->plan.at_o,
                                       c->plan.at_gu, c->plan.at_gu, c->plan.at_d};
   const int gsize[LS_N_PROJ] = {3, 3, 3, 1, 2, 2, 1};
+  ConvBatch cb;
+  double bytes = 0;
   for (int p = 0; p < LS_N_PROJ; ++p) {
     if (!lora_active(c, l, p)) continue;
     const ProjLayout& P = c->lay.p[p];
     const LoraReg& R = c->lora[l][p];
-    KTimer kt(c, LS_KC_LORA, 0.0, 4.0 * d.r * ((double)P.n_in + P.n_out) + 2.0 * 3 * d.r * ((double)P.n_in + P.n_out));
-    HIPCHK(c, launch_f32_to_bf16(R.A, P.n_in, lora_at(c, l, c->plan.a16[p]), P.n_in, d.r, P.n_in, P.n_in, 1.f, 0, c->cs));
-    HIPCHK(c, launch_f32_to_bf16(R.B, d.r, lora_at(c, l, c->plan.bx16[p]), d.r16, P.n_out, d.r, d.r16, 1.f, 0, c->cs));
-    HIPCHK(c, launch_f32_to_bf16(R.A, P.n_in, lora_at(c, l, at_off[p]) + gcol[p] * d.r16, (int64_t)gsize[p] * d.r16,
-                                 d.r, P.n_in, P.n_in, 1.f, 1, c->cs));
+    ConvJob j;
+    j.src = R.A; j.lds = P.n_in; j.dst = lora_at(c, l, c->plan.a16[p]); j.ldd = P.n_in;
+    j.rows = d.r; j.cols = P.n_in; j.pad_cols = P.n_in;
+    cb.job[cb.n++] = j;
+    j.src = R.B; j.lds = d.r; j.dst = lora_at(c, l, c->plan.bx16[p]); j.ldd = d.r16;
+    j.rows = P.n_out; j.cols = d.r; j.pad_cols = d.r16;
+    cb.job[cb.n++] = j;
+    j.dst = lora_at(c, l, c->plan.bxt16[p]); j.ldd = P.n_out; j.transpose = 1;
+    cb.job[cb.n++] = j;
+    j.src = R.A; j.lds = P.n_in; j.dst = lora_at(c, l, at_off[p]) + gcol[p] * d.r16; j.ldd = (int64_t)gsize[p] * d.r16;
+    j.rows = d.r; j.cols = P.n_in; j.pad_cols = P.n_in; j.transpose = 1;
+    cb.job[cb.n++] = j;
+    bytes += 4.0 * d.r * ((double)P.n_in + P.n_out) + 2.0 * 4 * d.r * ((double)P.n_in + P.n_out);
   }
+  KTimer kt(c, LS_KC_LORA, 0.0, bytes);
+  HIPCHK(c, launch_convert_batch(cb, c->cs));
   return LS_OK;
 }
 
@@ -446,8 +475,9 @@ ls_status attn_fwd(ls_ctx* c, const Dims& d, const uint16_t* qkv, uint16_t* out)
   return LS_OK;
 }
 
-// Attention backward from dO (datt), recomputed P (p16) and q, k, v -> dq, dk, dv in dqkv.
-ls_status attn_bwd(ls_ctx* c, const Dims& d, const uint16_t* qkv, const uint16_t* dout, uint16_t* dqkv) {
+// Attention backward from dO (datt), recomputed P (p16) and q, k, v -> float32 dq, dk,
+// dv in dqkv32 (dK, dV summed over a kv head's q heads in float32, fixed order).
+ls_status attn_bwd(ls_ctx* c, const Dims& d, const uint16_t* qkv, const uint16_t* dout, float* dqkv32) {
   const int S = d.seq, nrep = d.hq / d.hkv;
   const float scale = 1.0f / std::sqrt((float)d.hd);
   const int64_t SS = (int64_t)S * S;
@@ -472,7 +502,7 @@ ls_status attn_bwd(ls_ctx* c, const Dims& d, const uint16_t* qkv, const uint16_t
     GemmArgs g;
     g.A = ds16; g.sAm = S; g.sAk = 1; g.zA = {(int64_t)d.hq * SS, SS, 1};
     g.B = qkv + d.qd; g.sBn = 1; g.sBk = d.qkvd; g.zB = {(int64_t)S * d.qkvd, d.hd, nrep};
-    g.C = dqkv; g.sCm = d.qkvd; g.sCn = 1; g.zC = {(int64_t)S * d.qkvd, d.hd, 1}; g.c_f32 = 0;
+    g.C = dqkv32; g.sCm = d.qkvd; g.sCn = 1; g.zC = {(int64_t)S * d.qkvd, d.hd, 1}; g.c_f32 = 1;
     g.M = S; g.N = d.hd; g.K = S; g.nz = d.batch * d.hq; g.zdiv = d.hq; g.causal = 2;
     KTimer kt(c, LS_KC_ATTN, fl, 2.0 * d.batch * d.hq * SS / 2 + 2.0 * d.T * (d.kvd + d.qd));
     HIPCHK(c, launch_gemm_generic(g, c->cs));
@@ -482,14 +512,14 @@ ls_status attn_bwd(ls_ctx* c, const Dims& d, const uint16_t* qkv, const uint16_t
     GemmArgs g;
     g.A = ds16 + (int64_t)r * SS; g.sAm = 1; g.sAk = S; g.zA = {(int64_t)d.hq * SS, (int64_t)nrep * SS, 1};
     g.B = qkv + (int64_t)r * d.hd; g.sBn = 1; g.sBk = d.qkvd; g.zB = {(int64_t)S * d.qkvd, (int64_t)nrep * d.hd, 1};
-    g.C = dqkv + d.qd; g.sCm = d.qkvd; g.sCn = 1; g.zC = {(int64_t)S * d.qkvd, d.hd, 1}; g.c_f32 = 0;
+    g.C = dqkv32 + d.qd; g.sCm = d.qkvd; g.sCn = 1; g.zC = {(int64_t)S * d.qkvd, d.hd, 1}; g.c_f32 = 1;
     g.M = S; g.N = d.hd; g.K = S; g.nz = d.batch * d.hkv; g.zdiv = d.hkv; g.causal = 3; g.beta = r ? 1.f : 0.f;
     KTimer kt(c, LS_KC_ATTN, fl / d.hq * d.hkv, 2.0 * d.batch * d.hkv * SS / 2 + 2.0 * d.T * 2 * d.kvd);
     HIPCHK(c, launch_gemm_generic(g, c->cs));
     GemmArgs v = g;
     v.A = p16 + (int64_t)r * SS;
     v.B = dout + (int64_t)r * d.hd; v.sBk = d.qd; v.zB = {(int64_t)S * d.qd, (int64_t)nrep * d.hd, 1};
-    v.C = dqkv + d.qd + d.kvd;
+    v.C = dqkv32 + d.qd + d.kvd;
     KTimer kv(c, LS_KC_ATTN, fl / d.hq * d.hkv, 2.0 * d.batch * d.hkv * SS / 2 + 2.0 * d.T * 2 * d.kvd);
     HIPCHK(c, launch_gemm_generic(v, c->cs));
   }
@@ -509,9 +539,9 @@ ls_status layer_forward(ls_ctx* c, int l, const uint8_t* blob, const Dims& d, co
   uint16_t* n1 = c->dp<uint16_t>(c->plan.n1);
   uint16_t* qkv = c->dp<uint16_t>(c->plan.qkv);
   uint16_t* att = c->dp<uint16_t>(c->plan.att);
-  uint16_t* hb = c->dp<uint16_t>(c->plan.hb);
+  float* hb = c->dp<float>(c->plan.hb);
   uint16_t* n2 = c->dp<uint16_t>(c->plan.n2);
-  uint16_t* gu = c->dp<uint16_t>(c->plan.gu);
+  float* gu = c->dp<float>(c->plan.gu);
   uint16_t* act = c->dp<uint16_t>(c->plan.act);
   uint16_t* hs = c->dp<uint16_t>(c->plan.hs);
   const uint16_t* g1 = reinterpret_cast<const uint16_t*>(blob + c->lay.off_g1);
@@ -520,7 +550,7 @@ ls_status layer_forward(ls_ctx* c, int l, const uint8_t* blob, const Dims& d, co
 
   {
     KTimer kt(c, LS_KC_GLUE, 0.0, 2 * tb * d.h);
-    HIPCHK(c, launch_rmsnorm_fwd(x_in, g1, n1, c->dp<float>(c->plan.rstd1), d.T, d.h, g.rms_eps, c->cs));
+    HIPCHK(c, launch_rmsnorm_fwd(x_in, nullptr, g1, n1, c->dp<float>(c->plan.rstd1), d.T, d.h, g.rms_eps, c->cs));
   }
   if (lora) { ls_status st = lora_down(c, l, d, n1, d.h, LS_PROJ_Q, 3, d.h); if (st) return st; }
   {
@@ -535,13 +565,11 @@ ls_status layer_forward(ls_ctx* c, int l, const uint8_t* blob, const Dims& d, co
     }
     f.aext = hs; f.ldaext = d.R7; f.kx = lora ? d.r16 : 0;
     f.y = qkv; f.ldy = d.qkvd; f.levels = lv; f.format = fmt;
+    // q and k leave the GEMM rotated (rotary embedding applied in float32 before rounding)
+    f.rope_tab = c->dp<float2>(c->plan.rope); f.rope_cols = d.qd + d.kvd; f.seq = d.seq; f.head_dim = d.hd;
     KTimer kt(c, LS_KC_GEMM_FWD, fwd_gemm_flop(d, d.qkvd, d.h, lora),
               tb * d.h + wbytes(c, 0) + wbytes(c, 1) + wbytes(c, 2) + tb * d.qkvd);
     HIPCHK(c, launch_gemm_fwd(f, c->cs));
-  }
-  {
-    KTimer kt(c, LS_KC_GLUE, 0.0, 2 * tb * (d.qd + d.kvd));
-    HIPCHK(c, launch_rope_tab(qkv, d.qkvd, d.T, d.seq, d.hq + d.hkv, d.hd, c->dp<float2>(c->plan.rope), 0, c->cs));
   }
   { ls_status st = attn_fwd(c, d, qkv, att); if (st) return st; }
   if (lora) { ls_status st = lora_down(c, l, d, att, d.qd, LS_PROJ_O, 1, d.qd); if (st) return st; }
@@ -553,13 +581,13 @@ ls_status layer_forward(ls_ctx* c, int l, const uint8_t* blob, const Dims& d, co
     f.g[0].bext = lora && lora_active(c, l, LS_PROJ_O) ? lora_at(c, l, c->plan.bx16[LS_PROJ_O]) : nullptr;
     f.aext = hs; f.ldaext = d.R7; f.kx = lora ? d.r16 : 0;
     f.resid = x_in; f.ldr = d.h;
-    f.y = hb; f.ldy = d.h; f.levels = lv; f.format = fmt;
-    KTimer kt(c, LS_KC_GEMM_FWD, fwd_gemm_flop(d, d.h, d.qd, lora), tb * d.qd + wbytes(c, 3) + 2 * tb * d.h);
+    f.y32 = hb; f.ldy = d.h; f.levels = lv; f.format = fmt;
+    KTimer kt(c, LS_KC_GEMM_FWD, fwd_gemm_flop(d, d.h, d.qd, lora), tb * d.qd + wbytes(c, 3) + 3 * tb * d.h);
     HIPCHK(c, launch_gemm_fwd(f, c->cs));
   }
   {
     KTimer kt(c, LS_KC_GLUE, 0.0, 2 * tb * d.h);
-    HIPCHK(c, launch_rmsnorm_fwd(hb, g2, n2, c->dp<float>(c->plan.rstd2), d.T, d.h, g.rms_eps, c->cs));
+    HIPCHK(c, launch_rmsnorm_fwd(nullptr, hb, g2, n2, c->dp<float>(c->plan.rstd2), d.T, d.h, g.rms_eps, c->cs));
   }
   if (lora) { ls_status st = lora_down(c, l, d, n2, d.h, LS_PROJ_GATE, 2, d.h); if (st) return st; }
   {
@@ -573,13 +601,13 @@ ls_status layer_forward(ls_ctx* c, int l, const uint8_t* blob, const Dims& d, co
       f.g[i].bext = lora && lora_active(c, l, p) ? lora_at(c, l, c->plan.bx16[p]) : nullptr;
     }
     f.aext = hs; f.ldaext = d.R7; f.kx = lora ? d.r16 : 0;
-    f.y = gu; f.ldy = 2 * d.I; f.levels = lv; f.format = fmt;
-    KTimer kt(c, LS_KC_GEMM_FWD, fwd_gemm_flop(d, 2 * d.I, d.h, lora), tb * d.h + wbytes(c, 4) + wbytes(c, 5) + tb * 2 * d.I);
+    f.y32 = gu; f.ldy = 2 * d.I; f.levels = lv; f.format = fmt;
+    KTimer kt(c, LS_KC_GEMM_FWD, fwd_gemm_flop(d, 2 * d.I, d.h, lora), tb * d.h + wbytes(c, 4) + wbytes(c, 5) + 2 * tb * 2 * d.I);
     HIPCHK(c, launch_gemm_fwd(f, c->cs));
   }
   {
-    KTimer kt(c, LS_KC_GLUE, 0.0, 3 * tb * d.I);
-    HIPCHK(c, launch_swiglu_fwd(gu, 2 * d.I, d.I, act, d.T, c->cs));
+    KTimer kt(c, LS_KC_GLUE, 0.0, 5 * tb * d.I);
+    HIPCHK(c, launch_swiglu_fwd(gu, d.I, act, d.T, c->cs));
   }
   if (lora) { ls_status st = lora_down(c, l, d, act, d.I, LS_PROJ_DOWN, 1, d.I); if (st) return st; }
   if (mode == MODE_RECOMPUTE) return LS_OK;
@@ -590,9 +618,9 @@ ls_status layer_forward(ls_ctx* c, int l, const uint8_t* blob, const Dims& d, co
     f.g[0].ext_col0 = LS_PROJ_DOWN * d.r16;
     f.g[0].bext = lora && lora_active(c, l, LS_PROJ_DOWN) ? lora_at(c, l, c->plan.bx16[LS_PROJ_DOWN]) : nullptr;
     f.aext = hs; f.ldaext = d.R7; f.kx = lora ? d.r16 : 0;
-    f.resid = hb; f.ldr = d.h;
+    f.resid32 = hb; f.ldr = d.h;
     f.y = x_out; f.ldy = d.h; f.levels = lv; f.format = fmt;
-    KTimer kt(c, LS_KC_GEMM_FWD, fwd_gemm_flop(d, d.h, d.I, lora), tb * d.I + wbytes(c, 6) + 2 * tb * d.h);
+    KTimer kt(c, LS_KC_GEMM_FWD, fwd_gemm_flop(d, d.h, d.I, lora), tb * d.I + wbytes(c, 6) + 3 * tb * d.h);
     HIPCHK(c, launch_gemm_fwd(f, c->cs));
   }
   return LS_OK;
@@ -605,9 +633,10 @@ ls_status lora_grads_G(ls_ctx* c, int l, const Dims& d, int p, const uint16_t* d
   const ProjLayout& P = c->lay.p[p];
   GemmArgs g;
   g.A = dy; g.sAm = lddy; g.sAk = 1;
-  g.B = lora_at(c, l, c->plan.bx16[p]); g.sBn = 1; g.sBk = d.r16;
+  g.B = lora_at(c, l, c->plan.bxt16[p]); g.sBn = P.n_out; g.sBk = 1;
   g.C = c->dp<uint16_t>(c->plan.gs) + p * d.r16; g.sCm = d.R7; g.sCn = 1; g.c_f32 = 0;
   g.M = d.T; g.N = d.r16; g.K = P.n_out; g.alpha = d.s;
+  g.ksplit = auto_split(g.M, g.N, g.K, 1); g.partial = c->dp<float>(c->plan.partial);
   KTimer kt(c, LS_KC_LORA, 2.0 * d.T * P.n_out * d.r, 2.0 * d.T * P.n_out + 2.0 * P.n_out * d.r + 2.0 * d.T * d.r);
   HIPCHK(c, launch_gemm_generic(g, c->cs));
   return LS_OK;
@@ -624,6 +653,7 @@ ls_status lora_grads_AB(ls_ctx* c, int l, const Dims& d, int p, const uint16_t* 
     g.B = c->dp<uint16_t>(c->plan.hs) + p * d.r16; g.sBn = 1; g.sBk = d.R7;
     g.C = R.dB; g.sCm = d.r; g.sCn = 1; g.c_f32 = 1;
     g.M = P.n_out; g.N = d.r; g.K = d.T; g.beta = beta;
+    g.ksplit = auto_split(g.M, g.N, g.K, 1); g.partial = c->dp<float>(c->plan.partial);
     KTimer kt(c, LS_KC_LORA, 2.0 * d.T * P.n_out * d.r, 2.0 * d.T * P.n_out + 2.0 * d.T * d.r + 4.0 * P.n_out * d.r);
     HIPCHK(c, launch_gemm_generic(g, c->cs));
   }
@@ -633,6 +663,7 @@ ls_status lora_grads_AB(ls_ctx* c, int l, const Dims& d, int p, const uint16_t* 
     g.B = c->dp<uint16_t>(c->plan.gs) + p * d.r16; g.sBn = 1; g.sBk = d.R7;
     g.C = R.dA; g.sCm = 1; g.sCn = P.n_in; g.c_f32 = 1;
     g.M = P.n_in; g.N = d.r; g.K = d.T; g.beta = beta;
+    g.ksplit = auto_split(g.M, g.N, g.K, 1); g.partial = c->dp<float>(c->plan.partial);
     KTimer kt(c, LS_KC_LORA, 2.0 * d.T * P.n_in * d.r, 2.0 * d.T * P.n_in + 2.0 * d.T * d.r + 4.0 * P.n_in * d.r);
     HIPCHK(c, launch_gemm_generic(g, c->cs));
   }
@@ -649,14 +680,15 @@ ls_status layer_backward(ls_ctx* c, int l, const uint8_t* blob, const Dims& d, c
   uint16_t* n1 = c->dp<uint16_t>(c->plan.n1);
   uint16_t* qkv = c->dp<uint16_t>(c->plan.qkv);
   uint16_t* att = c->dp<uint16_t>(c->plan.att);
-  uint16_t* hb = c->dp<uint16_t>(c->plan.hb);
+  float* hb = c->dp<float>(c->plan.hb);
   uint16_t* n2 = c->dp<uint16_t>(c->plan.n2);
-  uint16_t* gu = c->dp<uint16_t>(c->plan.gu);
+  float* gu = c->dp<float>(c->plan.gu);
   uint16_t* act = c->dp<uint16_t>(c->plan.act);
   uint16_t* gs = c->dp<uint16_t>(c->plan.gs);
   float* dh32 = c->dp<float>(c->plan.dh32);
   uint16_t* dh16 = c->dp<uint16_t>(c->plan.dh16);
-  uint16_t* dact = c->dp<uint16_t>(c->plan.dact);
+  float* da32 = c->dp<float>(c->plan.da32);
+  float* dqkv32 = c->dp<float>(c->plan.dqkv32);
   uint16_t* dgu = c->dp<uint16_t>(c->plan.dgu);
   uint16_t* datt = c->dp<uint16_t>(c->plan.datt);
   uint16_t* dqkv = c->dp<uint16_t>(c->plan.dqkv);
@@ -675,13 +707,13 @@ ls_status layer_backward(ls_ctx* c, int l, const uint8_t* blob, const Dims& d, c
     b.seg[0].w = wref(c, blob, LS_PROJ_DOWN); b.seg[0].a_col0 = 0;
     b.aext = gs + LS_PROJ_DOWN * d.r16; b.ldaext = d.R7; b.kx = d.r16;
     b.bext = lora_at(c, l, c->plan.at_d); b.ldbext = d.r16;
-    b.out16 = dact; b.ldo = d.I; b.levels = lv; b.format = fmt;
-    KTimer kt(c, LS_KC_GEMM_BWD, bwd_flop(d.h, d.I), tb * d.h + wbytes(c, 6) + tb * d.I);
+    b.out32 = da32; b.ldo = d.I; b.levels = lv; b.format = fmt;
+    KTimer kt(c, LS_KC_GEMM_BWD, bwd_flop(d.h, d.I), tb * d.h + wbytes(c, 6) + 2 * tb * d.I);
     HIPCHK(c, launch_gemm_bwd(b, c->cs));
   }
   {
-    KTimer kt(c, LS_KC_GLUE, 0.0, 5 * tb * d.I);
-    HIPCHK(c, launch_swiglu_bwd(gu, 2 * d.I, dact, d.I, dgu, d.T, c->cs));
+    KTimer kt(c, LS_KC_GLUE, 0.0, 8 * tb * d.I);
+    HIPCHK(c, launch_swiglu_bwd(gu, da32, d.I, dgu, d.T, c->cs));
   }
   // ---- gate / up
   for (int i = 0; i < 2; ++i) {
@@ -702,7 +734,7 @@ ls_status layer_backward(ls_ctx* c, int l, const uint8_t* blob, const Dims& d, c
   }
   {
     KTimer kt(c, LS_KC_GLUE, 0.0, 4 * tb * d.h);
-    HIPCHK(c, launch_rmsnorm_bwd(dn32, hb, g2, c->dp<float>(c->plan.rstd2), nullptr, dy, dh32, dh16, d.T, d.h, c->cs));
+    HIPCHK(c, launch_rmsnorm_bwd(dn32, nullptr, hb, g2, c->dp<float>(c->plan.rstd2), nullptr, dy, dh32, dh16, d.T, d.h, c->cs));
   }
   // ---- o: h = x + att W_o^T + LoRA
   if ((st = lora_grads_G(c, l, d, LS_PROJ_O, dh16, d.h))) return st;
@@ -717,10 +749,10 @@ ls_status layer_backward(ls_ctx* c, int l, const uint8_t* blob, const Dims& d, c
     KTimer kt(c, LS_KC_GEMM_BWD, bwd_flop(d.h, d.qd), tb * d.h + wbytes(c, 3) + tb * d.qd);
     HIPCHK(c, launch_gemm_bwd(b, c->cs));
   }
-  if ((st = attn_bwd(c, d, qkv, datt, dqkv))) return st;
+  if ((st = attn_bwd(c, d, qkv, datt, dqkv32))) return st;
   {
-    KTimer kt(c, LS_KC_GLUE, 0.0, 2 * tb * (d.qd + d.kvd));
-    HIPCHK(c, launch_rope_tab(dqkv, d.qkvd, d.T, d.seq, d.hq + d.hkv, d.hd, c->dp<float2>(c->plan.rope), 1, c->cs));
+    KTimer kt(c, LS_KC_GLUE, 0.0, 3 * tb * d.qkvd);
+    HIPCHK(c, launch_rope_bwd_convert(dqkv32, dqkv, d.qkvd, d.T, d.seq, d.hq + d.hkv, d.hd, c->dp<float2>(c->plan.rope), c->cs));
   }
   // ---- q, k, v
   const int cols[3] = {0, d.qd, d.qd + d.kvd};
@@ -741,7 +773,7 @@ ls_status layer_backward(ls_ctx* c, int l, const uint8_t* blob, const Dims& d, c
   }
   {
     KTimer kt(c, LS_KC_GLUE, 0.0, 4 * tb * d.h);
-    HIPCHK(c, launch_rmsnorm_bwd(dn32, x_in, g1, c->dp<float>(c->plan.rstd1), dh32, nullptr, nullptr, dx, d.T, d.h, c->cs));
+    HIPCHK(c, launch_rmsnorm_bwd(dn32, x_in, nullptr, g1, c->dp<float>(c->plan.rstd1), dh32, nullptr, nullptr, dx, d.T, d.h, c->cs));
   }
   return LS_OK;
 }

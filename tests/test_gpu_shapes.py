@@ -1,0 +1,69 @@
+"""GPU parity against the oracle at the real layer shapes of the measured workloads
+(a few layers each, token counts the oracle finishes in seconds), and streamed ==
+resident bitwise at those shapes."""
+import numpy as np
+import pytest
+
+from layer_streamed_qlora_amd import synth
+import lsq_harness as H
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def parity_case(name, n_layers, batch, seq, seeds=None, with_ref=False):
+    w = synth.WORKLOADS[name].with_(batch=batch, seq=seq)
+    seeds = list(range(n_layers)) if seeds is None else seeds
+    x, dy = synth.activations(w)
+    say(f"case: {name} layers {seeds} batch {batch} seq {seq}: GPU")
+    run = H.GpuRun(w, seeds)
+    gpu = run.step(x, dy, batch, seq, with_ref=with_ref)
+    src = run.src
+    run.close()
+    say("oracle ...")
+    loras = [synth.layer_lora(w, s) for s in seeds]
+    ora = H.oracle_step(w, src, loras, x, dy, batch, seq, with_ref=with_ref)
+    errs, fails = H.compare(gpu, ora)
+    if with_ref:
+        errs["Y_ref"] = H.rel_l2(gpu["Y_ref"], ora["Y_ref"])
+        if errs["Y_ref"] > 1e-2:
+            fails.append(("Y_ref", errs["Y_ref"]))
+    worst = max((v for k, v in errs.items() if k.startswith("d")), default=0.0)
+    say({"Y": f"{errs['Y']:.2e}", "dX": f"{errs['dX']:.2e}", "worst grad": f"{worst:.2e}"})
+    assert not fails, fails
+
+
+def test_qwen3b_shape_bf16_base_512_tokens():
+    """bf16 base, GQA 16/2, SwiGLU 11008; 512 tokens exercise the split-K reductions."""
+    parity_case("qwen3b", 2, 1, 512)
+
+
+def test_llama8b_shape_nf4_dq_layers_0_1():
+    parity_case("llama8b", 2, 1, 128)
+
+
+def test_llama8b_shape_layer_31():
+    parity_case("llama8b", 1, 1, 128, seeds=[31])
+
+
+@pytest.mark.parametrize("name,n_layers,batch,seq", [("llama8b", 3, 2, 256), ("qwen3b", 3, 1, 512)])
+def test_streamed_equals_resident_bitwise(name, n_layers, batch, seq):
+    w = synth.WORKLOADS[name].with_(batch=batch, seq=seq)
+    x, dy = synth.activations(w)
+    weights = [synth.layer_weights(w, l) for l in range(n_layers)]
+    outs = []
+    for resident in (0, 1):
+        say(f"case: {name} streamed vs resident, resident={resident}")
+        run = H.GpuRun(w, list(range(n_layers)), resident=resident, weights=weights)
+        outs.append(run.step(x, dy, batch, seq, with_ref=True))
+        run.close()
+    a, b = outs
+    for k in ("Y", "Y_ref", "dX"):
+        assert np.array_equal(a[k].view(np.uint32), b[k].view(np.uint32)), k
+    for l in range(n_layers):
+        for p in H.PROJS:
+            assert np.array_equal(a["dA"][l][p].view(np.uint32), b["dA"][l][p].view(np.uint32)), (l, p)
+            assert np.array_equal(a["dB"][l][p].view(np.uint32), b["dB"][l][p].view(np.uint32)), (l, p)
