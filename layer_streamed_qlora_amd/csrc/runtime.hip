@@ -128,7 +128,7 @@ DevPlan make_plan(const ls_config& c, const BlobLayout& L) {
   P.lora_per_layer = align_up(lo, kAlign);
   P.lora = take(P.lora_per_layer * (uint64_t)c.n_layers);
   // split-K partials of the rank-r reductions: up to kMaxSplit chunks of [rows, r16]
-  P.partial_bytes = 4ull * kMaxSplit * std::max<uint64_t>(std::max<uint64_t>(T, I), std::max<uint64_t>(h, qkvd)) * r16;
+  P.partial_bytes = 4ull * kMaxSplit * std::max<uint64_t>(std::max<uint64_t>(T, I), std::max<uint64_t>(h, qkvd)) * 3 * r16;
   P.partial = take(P.partial_bytes);
   P.levels = take(64);
   P.rope = take(8ull * (uint64_t)c.max_seq * (uint64_t)(c.head_dim / 2));
@@ -435,6 +435,7 @@ ls_status lora_down(ls_ctx* c, int l, const Dims& d, const uint16_t* x, int ldx,
   g.B = lora_at(c, l, c->plan.a16[p0]); g.sBn = K; g.sBk = 1;
   g.C = c->dp<uint16_t>(c->plan.hs) + p0 * d.r16; g.sCm = d.R7; g.sCn = 1; g.c_f32 = 0;
   g.M = d.T; g.N = ng * d.r16; g.K = K; g.alpha = d.s;
+  g.ksplit = auto_split(g.M, g.N, g.K, 1); g.partial = c->dp<float>(c->plan.partial);
   KTimer kt(c, LS_KC_LORA, 2.0 * d.T * ng * d.r * K, 2.0 * d.T * K + 2.0 * ng * d.r * K + 2.0 * d.T * ng * d.r);
   HIPCHK(c, launch_gemm_generic(g, c->cs));
   return LS_OK;
