@@ -60,15 +60,18 @@ __device__ __forceinline__ float block_absmax(const WeightRef& w, uint64_t b) {
   }
 }
 
+// The 256-entry pair table at LDS offset 0: entry b = (level[b >> 4], level[b & 15]),
+// the two levels of one packed code byte (element 2k in the high nibble).  One 8-byte
+// LDS read per byte; the address is the byte value times 8.
+__device__ __forceinline__ uint32_t deq_byte(const float2* lut2, uint32_t byte, float am) {
+  const float2 l = lut2[byte];
+  return pack_bf16x2(l.x * am, l.y * am);      // fp32 multiply, RNE to bf16
+}
+
 // 8 codes (one dword, byte k = code[2k] << 4 | code[2k+1]) -> 4 dwords of bf16 pairs
-__device__ __forceinline__ void dequant8(uint32_t codes, float am, const float* lut, uint32_t out[4]) {
+__device__ __forceinline__ void dequant8(uint32_t codes, float am, const float2* lut2, uint32_t out[4]) {
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const uint32_t byte = (codes >> (8 * k)) & 0xFFu;
-    const float a = lut[byte >> 4] * am;
-    const float b = lut[byte & 15u] * am;
-    out[k] = pack_bf16x2(a, b);
-  }
+  for (int k = 0; k < 4; ++k) out[k] = deq_byte(lut2, (codes >> (8 * k)) & 0xFFu, am);
 }
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
@@ -93,6 +96,7 @@ __device__ __forceinline__ uint32_t bload4(rsrc_t r, uint32_t off) {
 }
 
 struct Smem {
+  float2 lut2[256];                  // must stay first: LDS offset 0
   union {
     struct {
       uint16_t a[2][TILE_ELEMS];
@@ -100,8 +104,12 @@ struct Smem {
     } k;
     float out[128 * (BN + 4)];       // epilogue staging, one half tile (128 rows) at a time
   } u;
-  float lut[16];
 };
+
+__device__ __forceinline__ void fill_lut2(Smem& sm, const float* levels) {
+  const int b = threadIdx.x;          // the first 256 threads, one entry each
+  if (b < 256) sm.lut2[b] = levels ? make_float2(levels[b >> 4], levels[b & 15]) : make_float2(0.f, 0.f);
+}
 
 // NF4 weight buffers as resources
 struct WRes {
@@ -159,14 +167,30 @@ __device__ __forceinline__ void load_a(ALoad& r, rsrc_t res, uint32_t base_off, 
     r.v[i] = bload16(res, ok ? off : kOOB);
   }
 }
-__device__ __forceinline__ void store_a(const ALoad& r, uint16_t* s) {
+__device__ __forceinline__ void load_a_part(ALoad& r, rsrc_t res, uint32_t base_off, int ld, int rows_left, int k0,
+                                            int klim, int q) {   // chunks 2q, 2q+1
   const int t = threadIdx.x;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 2 * q; i < 2 * q + 2; ++i) {
+    const int c = t + NTHREADS * i;
+    const int row = c >> 3, kc = (c & 7) * 8;
+    const bool ok = row < rows_left && k0 + kc < klim;
+    const uint32_t off = base_off + ((uint32_t)row * (uint32_t)ld + (uint32_t)(k0 + kc)) * 2u;
+    r.v[i] = bload16(res, ok ? off : kOOB);
+  }
+}
+__device__ __forceinline__ void store_a_part(const ALoad& r, uint16_t* s, int q) {   // chunks 2q, 2q+1
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int i = 2 * q; i < 2 * q + 2; ++i) {
     const int c = t + NTHREADS * i;
     const int row = c >> 3, kc = (c & 7) * 8;
     *reinterpret_cast<uint4*>(s + row * PITCH + kc) = r.v[i];
   }
+}
+__device__ __forceinline__ void store_a(const ALoad& r, uint16_t* s) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) store_a_part(r, s, q);
 }
 
 // ---- W operand, forward orientation: thread t owns row n0+t, k in [k0, k0+64)
@@ -203,20 +227,25 @@ struct WFwd {
       }
     }
   }
-  __device__ __forceinline__ void store(uint16_t* s, const float* lut) const {
+  // quarter q of the store: 16 of the thread's 64 elements
+  __device__ __forceinline__ void store_part(uint16_t* s, const float2* lut2, int q) const {
     uint16_t* row = s + threadIdx.x * PITCH;
     if constexpr (FMT == WF_BF16) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) *reinterpret_cast<uint4*>(row + 8 * i) = raw[i];
+      for (int i = 2 * q; i < 2 * q + 2; ++i) *reinterpret_cast<uint4*>(row + 8 * i) = raw[i];
     } else {
       const uint32_t* r32 = reinterpret_cast<const uint32_t*>(raw);
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {      // 8 dwords of codes = 64 elements
+      for (int d = 2 * q; d < 2 * q + 2; ++d) {      // 2 dwords of codes = 16 elements
         uint32_t o[4];
-        dequant8(r32[q], ALIGNED ? am[0] : am[q / 2], lut, o);
-        *reinterpret_cast<uint4*>(row + 8 * q) = make_uint4(o[0], o[1], o[2], o[3]);
+        dequant8(r32[d], ALIGNED ? am[0] : am[q], lut2, o);
+        *reinterpret_cast<uint4*>(row + 8 * d) = make_uint4(o[0], o[1], o[2], o[3]);
       }
     }
+  }
+  __device__ __forceinline__ void store(uint16_t* s, const float2* lut2) const {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) store_part(s, lut2, q);
   }
 };
 
@@ -258,7 +287,8 @@ struct WBwd {
       }
     }
   }
-  __device__ __forceinline__ void store(uint16_t* s, const float* lut) const {
+  // quarter q of the store: codes dword q of both rows (8 columns)
+  __device__ __forceinline__ void store_part(uint16_t* s, const float2* lut2, int q) const {
     const int p = threadIdx.x & 31, c = threadIdx.x >> 5;
     uint32_t* dst = reinterpret_cast<uint32_t*>(s + (32 * c) * PITCH + 2 * p);
     const int pitch32 = PITCH / 2;
@@ -266,47 +296,296 @@ struct WBwd {
       const uint32_t* r0 = reinterpret_cast<const uint32_t*>(&raw[0]);
       const uint32_t* r1 = reinterpret_cast<const uint32_t*>(&raw[4]);
 #pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        dst[(2 * q) * pitch32] = __builtin_amdgcn_perm(r1[q], r0[q], 0x05040100u);
-        dst[(2 * q + 1) * pitch32] = __builtin_amdgcn_perm(r1[q], r0[q], 0x07060302u);
+      for (int w = 4 * q; w < 4 * q + 4; ++w) {
+        dst[(2 * w) * pitch32] = __builtin_amdgcn_perm(r1[w], r0[w], 0x05040100u);
+        dst[(2 * w + 1) * pitch32] = __builtin_amdgcn_perm(r1[w], r0[w], 0x07060302u);
       }
     } else {
       const uint32_t* r0 = reinterpret_cast<const uint32_t*>(&raw[0]);
       const uint32_t* r1 = reinterpret_cast<const uint32_t*>(&raw[1]);
+      const float a0 = ALIGNED ? am[0][0] : am[0][q / 2];
+      const float a1 = ALIGNED ? am[1][0] : am[1][q / 2];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {           // 4 dwords per row = 32 codes
-        const float a0 = ALIGNED ? am[0][0] : am[0][q / 2];
-        const float a1 = ALIGNED ? am[1][0] : am[1][q / 2];
+      for (int k = 0; k < 4; ++k) {
+        const float2 l0 = lut2[(r0[q] >> (8 * k)) & 0xFFu], l1 = lut2[(r1[q] >> (8 * k)) & 0xFFu];
+        const int j = 8 * q + 2 * k;
+        dst[j * pitch32] = pack_bf16x2(l0.x * a0, l1.x * a1);
+        dst[(j + 1) * pitch32] = pack_bf16x2(l0.y * a0, l1.y * a1);
+      }
+    }
+  }
+  __device__ __forceinline__ void store(uint16_t* s, const float2* lut2) const {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const uint32_t b0 = (r0[q] >> (8 * k)) & 0xFFu, b1 = (r1[q] >> (8 * k)) & 0xFFu;
-          const int j = 8 * q + 2 * k;
-          dst[j * pitch32] = pack_bf16x2(lut[b0 >> 4] * a0, lut[b1 >> 4] * a1);
-          dst[(j + 1) * pitch32] = pack_bf16x2(lut[b0 & 15u] * a0, lut[b1 & 15u] * a1);
+    for (int q = 0; q < 4; ++q) store_part(s, lut2, q);
+  }
+};
+
+// ---------------------------------------------------------------- fast path
+// Used when every tile lies inside its matrices (K % 64 == 0, and in the W^T
+// orientation every stacked segment's rows % 64 == 0).  Per-lane offsets are loop
+// invariant; the K position moves in the scalar offset, so the loads cost no VALU.
+// Rows past the end of a buffer read as zero through the buffer range check.
+
+__device__ __forceinline__ uint4 bload16s(rsrc_t r, uint32_t voff, uint32_t soff) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint32_t bload4s(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+}
+__device__ __forceinline__ uint32_t bload1s(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, voff, soff, 0);
+}
+
+// fp32(fp32(fp32(c/127) * scale2) + mean), the two roundings kept apart
+__device__ __forceinline__ float dq_absmax(uint32_t code_byte, float scale2, float mean) {
+#pragma clang fp contract(off)
+  const float frac = (float)(int8_t)(uint8_t)code_byte / 127.0f;
+  const float prod = frac * scale2;
+  return prod + mean;
+}
+
+constexpr int NT_FAST = 512;    // fast path: 8 waves, two per SIMD
+
+// A operand: 256 rows x 64 columns of a K-contiguous bf16 matrix (row stride ld);
+// thread t moves 4 chunks of 16 B: rows (t >> 3) + 64 q, columns (t & 7) * 8.  The
+// row sits in the per-lane offset, which the buffer range check covers (rows past
+// the end read as zero); the column position is the scalar offset and stays inside
+// the row as long as the caller only asks for tiles below the row length.
+struct AFast {
+  uint4 v[4];
+  rsrc_t res;
+  uint32_t voff[4];
+  __device__ __forceinline__ void init(rsrc_t r, int ld) {
+    res = r;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      voff[q] = ((uint32_t)((threadIdx.x >> 3) + 64 * q) * (uint32_t)ld + (uint32_t)(threadIdx.x & 7) * 8u) * 2u;
+  }
+  __device__ __forceinline__ void load_q(uint32_t col0, int q) {   // col0 in elements
+    v[q] = bload16s(res, voff[q], col0 * 2u);
+  }
+  __device__ __forceinline__ void store_q(uint16_t* s, int q) const {
+    const int c = threadIdx.x + NT_FAST * q;
+    *reinterpret_cast<uint4*>(s + (c >> 3) * PITCH + (c & 7) * 8) = v[q];
+  }
+};
+
+// extension tile (rows x kx, kx <= 64, zero beyond) with 512 threads
+__device__ __forceinline__ void ext_tile(uint16_t* s, rsrc_t res, uint32_t col_off_bytes, int ld, int rows, int kx) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int c = threadIdx.x + NT_FAST * q;
+    const int row = c >> 3, kc = (c & 7) * 8;
+    const bool ok = row < rows && kc < kx;
+    const uint4 v = bload16(res, ok ? col_off_bytes + ((uint32_t)row * (uint32_t)ld + (uint32_t)kc) * 2u : kOOB);
+    *reinterpret_cast<uint4*>(s + row * PITCH + kc) = v;
+  }
+}
+
+// W operand, forward orientation: thread t owns row n0 + (t >> 1), k half 32 (t & 1)
+// of one NF4 block (both halves share the block's absmax).  Rows are in the checked
+// per-lane offset; load(k0) must only be called with k0 < K.
+template <int FMT>
+struct WFwdFast {
+  uint4 raw[FMT == WF_BF16 ? 4 : 1];
+  uint32_t blk;      // absmax word (NF4) or 8-bit code (DQ)
+  float s2;          // DQ second-level scale
+  rsrc_t codes, absq, sc2;
+  float mean;
+  uint32_t voff_w, voff_b, blk0;
+  __device__ __forceinline__ void init(const WeightRef& w, int n0) {
+    const int K = w.n_in;
+    const int rows = w.n_out - n0 < BN ? w.n_out - n0 : BN;
+    const uint32_t r = threadIdx.x >> 1, h = threadIdx.x & 1;
+    const uint32_t kblk = (uint32_t)K / kNF4Block;
+#pragma unroll
+    for (int i = 0; i < (FMT == WF_BF16 ? 4 : 1); ++i) raw[i] = make_uint4(0, 0, 0, 0);
+    blk = 0; s2 = 0.f;
+    if constexpr (FMT == WF_BF16) {
+      codes = make_rsrc(w.w + (uint64_t)n0 * K * 2, (uint64_t)(rows > 0 ? rows : 0) * K * 2);
+      voff_w = (r * (uint32_t)K + 32u * h) * 2u;
+    } else {
+      codes = make_rsrc(w.w + (uint64_t)n0 * K / 2, (uint64_t)(rows > 0 ? rows : 0) * K / 2);
+      voff_w = r * (uint32_t)K / 2u + 16u * h;
+      const uint64_t b0 = (uint64_t)n0 * kblk;
+      const uint64_t nb = (uint64_t)(rows > 0 ? rows : 0) * kblk;
+      voff_b = r * kblk;
+      blk0 = (uint32_t)(b0 + voff_b);
+      if constexpr (FMT == WF_NF4) {
+        absq = make_rsrc(w.absmax + b0, nb * 4);
+      } else {
+        absq = make_rsrc(w.qabs + b0, nb);
+        const uint64_t all = (uint64_t)w.n_out * kblk;
+        sc2 = make_rsrc(w.scale2, (all + kDQGroup - 1) / kDQGroup * 4);
+        mean = *w.mean;
+      }
+    }
+  }
+  __device__ __forceinline__ void load(int k0) {
+    if constexpr (FMT == WF_BF16) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) raw[i] = bload16s(codes, voff_w + 16u * i, (uint32_t)k0 * 2u);
+    } else {
+      raw[0] = bload16s(codes, voff_w, (uint32_t)k0 / 2u);
+      const uint32_t kb = (uint32_t)k0 / kNF4Block;
+      if constexpr (FMT == WF_NF4) {
+        blk = bload4s(absq, voff_b * 4u, kb * 4u);
+      } else {
+        blk = bload1s(absq, voff_b, kb);
+        s2 = __builtin_bit_cast(float, bload4s(sc2, ((blk0 + kb) / kDQGroup) * 4u, 0));
+      }
+    }
+  }
+  __device__ __forceinline__ float absmax() const {
+    if constexpr (FMT == WF_NF4) return __builtin_bit_cast(float, blk);
+    else return dq_absmax(blk, s2, mean);
+  }
+  // quarter q: 8 of the thread's 32 elements, one 16-byte LDS store
+  __device__ __forceinline__ void store_part(uint16_t* s, const float2* lut2, int q, float am) const {
+    uint16_t* dst = s + (threadIdx.x >> 1) * PITCH + 32 * (threadIdx.x & 1) + 8 * q;
+    if constexpr (FMT == WF_BF16) {
+      *reinterpret_cast<uint4*>(dst) = raw[q];
+    } else {
+      uint32_t o[4];
+      dequant8(reinterpret_cast<const uint32_t*>(&raw[0])[q], am, lut2, o);
+      *reinterpret_cast<uint4*>(dst) = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+  }
+};
+
+// W operand, backward orientation: thread t owns rows k0 + 2p, k0 + 2p + 1 (p = t & 31)
+// and 16 output columns j0 + 16c (c = t >> 5), inside one NF4 block per row.
+template <int FMT>
+struct WBwdFast {
+  uint4 raw[FMT == WF_BF16 ? 4 : 1];   // nf4: .x .y = row 0 codes, .z .w = row 1 codes
+  uint32_t blk[2];
+  float s2[2];
+  rsrc_t codes, absq, sc2;
+  float mean;
+  uint32_t voff_w[2], voff_b[2];
+  uint32_t jblk;     // J / 64
+  __device__ __forceinline__ void init_lane(int J) {
+    const uint32_t p = threadIdx.x & 31, c = threadIdx.x >> 5;
+    jblk = (uint32_t)J / kNF4Block;
+#pragma unroll
+    for (int i = 0; i < (FMT == WF_BF16 ? 4 : 1); ++i) raw[i] = make_uint4(0, 0, 0, 0);
+    blk[0] = blk[1] = 0; s2[0] = s2[1] = 0.f;
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const uint32_t row = 2 * p + r;
+      if constexpr (FMT == WF_BF16) voff_w[r] = (row * (uint32_t)J + 16u * c) * 2u;
+      else voff_w[r] = (row * (uint32_t)J + 16u * c) / 2u;
+      voff_b[r] = row * jblk + (c >> 2);
+    }
+  }
+  // tile (rows k0.., columns j0..) with k0 < n_out: every buffer is based at the
+  // tile's first element, so the range check (per-lane offset only) ends at the matrix
+  __device__ __forceinline__ void load(const WeightRef& w, int j0, int k0) {
+    const uint64_t J = (uint64_t)w.n_in;
+    const uint64_t numel = (uint64_t)w.n_out * J;
+    const uint64_t e0 = (uint64_t)k0 * J + (uint64_t)j0;
+    const uint64_t nb = numel / kNF4Block, b0 = e0 / kNF4Block;
+    if constexpr (FMT == WF_BF16) {
+      codes = make_rsrc(w.w + e0 * 2, (numel - e0) * 2);
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        raw[2 * r] = bload16s(codes, voff_w[r], 0);
+        raw[2 * r + 1] = bload16s(codes, voff_w[r] + 16u, 0);
+      }
+    } else {
+      codes = make_rsrc(w.w + e0 / 2, (numel - e0) / 2);
+      typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+      const u32x2 c0 = __builtin_amdgcn_raw_buffer_load_b64(codes, voff_w[0], 0, 0);
+      const u32x2 c1 = __builtin_amdgcn_raw_buffer_load_b64(codes, voff_w[1], 0, 0);
+      raw[0] = make_uint4(c0.x, c0.y, c1.x, c1.y);
+      if constexpr (FMT == WF_NF4) {
+        absq = make_rsrc(w.absmax + b0, (nb - b0) * 4);
+        blk[0] = bload4s(absq, voff_b[0] * 4u, 0);
+        blk[1] = bload4s(absq, voff_b[1] * 4u, 0);
+      } else {
+        absq = make_rsrc(w.qabs + b0, nb - b0);
+        sc2 = make_rsrc(w.scale2, (nb + kDQGroup - 1) / kDQGroup * 4);
+        mean = *w.mean;
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+          blk[r] = bload1s(absq, voff_b[r], 0);
+          s2[r] = __builtin_bit_cast(float, bload4s(sc2, (((uint32_t)b0 + voff_b[r]) / kDQGroup) * 4u, 0));
         }
+      }
+    }
+  }
+  __device__ __forceinline__ float absmax(int r) const {
+    if constexpr (FMT == WF_NF4) return __builtin_bit_cast(float, blk[r]);
+    else return dq_absmax(blk[r], s2[r], mean);
+  }
+  // quarter q: columns 4q .. 4q+3 of the thread's 16, both rows -> 4 dword stores
+  __device__ __forceinline__ void store_part(uint16_t* s, const float2* lut2, int q, float a0, float a1) const {
+    const int p = threadIdx.x & 31, c = threadIdx.x >> 5;
+    uint32_t* dst = reinterpret_cast<uint32_t*>(s + (16 * c + 4 * q) * PITCH + 2 * p);
+    constexpr int pitch32 = PITCH / 2;
+    if constexpr (FMT == WF_BF16) {
+      // row r dword w (columns 2w, 2w+1), w = 2q, 2q+1
+      const uint32_t* r0 = reinterpret_cast<const uint32_t*>(&raw[0]);
+      const uint32_t* r1 = reinterpret_cast<const uint32_t*>(&raw[2]);
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int w = 2 * q + u;
+        dst[(2 * u) * pitch32] = __builtin_amdgcn_perm(r1[w], r0[w], 0x05040100u);
+        dst[(2 * u + 1) * pitch32] = __builtin_amdgcn_perm(r1[w], r0[w], 0x07060302u);
+      }
+    } else {
+      const uint32_t* rr = reinterpret_cast<const uint32_t*>(&raw[0]);
+      const uint32_t sh = (q & 1) * 16;
+      const uint32_t w0 = rr[q >> 1] >> sh, w1 = rr[2 + (q >> 1)] >> sh;
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {   // code bytes 2q + k -> columns 4q + 2k, 4q + 2k + 1
+        const float2 l0 = lut2[(w0 >> (8 * k)) & 0xFFu], l1 = lut2[(w1 >> (8 * k)) & 0xFFu];
+        dst[(2 * k) * pitch32] = pack_bf16x2(l0.x * a0, l1.x * a1);
+        dst[(2 * k + 1) * pitch32] = pack_bf16x2(l0.y * a0, l1.y * a1);
       }
     }
   }
 };
 
-// ---- MFMA over one LDS stage
-template <int KSTEPS>
-__device__ __forceinline__ void mma_stage(const uint16_t* sa, const uint16_t* sw, f32x16_t acc[4][4]) {
+// ---- MFMA over one LDS stage (4 k16 steps), with fragments of step kk+1 read
+// while step kk's 16 MFMAs run, and a quarter of the next stage's stores (the
+// functor `work`) placed after each step's MFMAs so they execute in their shadow.
+// Wave layout of a 256 x 256 tile: NT / 64 waves, 2 along m (128 rows each) and
+// WNW = NT / 128 along n (256 / WNW columns each, JB = 8 / WNW blocks of 32).
+template <int NT> struct Layout {
+  static constexpr int WNW = NT / 128;
+  static constexpr int JB = 8 / WNW;
+};
+
+template <int NT, class Work>
+__device__ __forceinline__ void mma_stage(const uint16_t* sa, const uint16_t* sw, f32x16_t (&acc)[4][Layout<NT>::JB],
+                                          Work&& work) {
+  constexpr int WNW = Layout<NT>::WNW, JB = Layout<NT>::JB;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WNW, wn = wave % WNW;
   const uint16_t* pa = sa + (wm * 128 + (lane & 31)) * PITCH + (lane >> 5) * 8;
-  const uint16_t* pw = sw + (wn * 128 + (lane & 31)) * PITCH + (lane >> 5) * 8;
+  const uint16_t* pw = sw + (wn * (32 * JB) + (lane & 31)) * PITCH + (lane >> 5) * 8;
+  bf16x8_t fa[2][4], fb[2][JB];
 #pragma unroll
-  for (int kk = 0; kk < KSTEPS; ++kk) {
-    bf16x8_t a[4], b[4];
+  for (int i = 0; i < 4; ++i) fa[0][i] = *reinterpret_cast<const bf16x8_t*>(pa + i * 32 * PITCH);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const bf16x8_t*>(pa + i * 32 * PITCH + kk * 16);
+  for (int j = 0; j < JB; ++j) fb[0][j] = *reinterpret_cast<const bf16x8_t*>(pw + j * 32 * PITCH);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) b[j] = *reinterpret_cast<const bf16x8_t*>(pw + j * 32 * PITCH + kk * 16);
+  for (int kk = 0; kk < BK / 16; ++kk) {
+    const int c = kk & 1, n = c ^ 1;
+    if (kk + 1 < BK / 16) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) fa[n][i] = *reinterpret_cast<const bf16x8_t*>(pa + i * 32 * PITCH + (kk + 1) * 16);
+#pragma unroll
+      for (int j = 0; j < JB; ++j) fb[n][j] = *reinterpret_cast<const bf16x8_t*>(pw + j * 32 * PITCH + (kk + 1) * 16);
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+      for (int j = 0; j < JB; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[c][i], fb[c][j], acc[i][j], 0, 0, 0);
+    work(kk);
   }
 }
 
@@ -321,10 +600,12 @@ struct Epi {
   const float2* rope_tab = nullptr; int rope_cols = 0, col_base = 0, seq = 1, hd = 128;
 };
 
-__device__ __forceinline__ void epilogue(Smem& sm, f32x16_t acc[4][4], int m0, int n0, int M_lim, int N_lim,
-                                         const Epi& E) {
+template <int NT>
+__device__ __forceinline__ void epilogue(Smem& sm, f32x16_t (&acc)[4][Layout<NT>::JB], int m0, int n0, int M_lim,
+                                         int N_lim, const Epi& E) {
+  constexpr int WNW = Layout<NT>::WNW, JB = Layout<NT>::JB;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WNW, wn = wave % WNW;
   constexpr int OP = BN + 4;
   for (int half = 0; half < 2; ++half) {
     __syncthreads();
@@ -332,19 +613,19 @@ __device__ __forceinline__ void epilogue(Smem& sm, f32x16_t acc[4][4], int m0, i
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < JB; ++j)
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
             const int r = i * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
-            const int c = wn * 128 + j * 32 + (lane & 31);
+            const int c = wn * (32 * JB) + j * 32 + (lane & 31);
             sm.u.out[r * OP + c] = acc[i][j][v];
           }
     }
     __syncthreads();
     const int mbase = m0 + half * 128;
 #pragma unroll 4
-    for (int it = 0; it < 32; ++it) {
-      const int idx = threadIdx.x + NTHREADS * it;     // 128 rows x 64 quads
+    for (int it = 0; it < 8192 / NT; ++it) {
+      const int idx = threadIdx.x + NT * it;           // 128 rows x 64 quads
       const int r = idx >> 6, q = idx & 63;
       const int m = mbase + r, n = n0 + 4 * q;
       if (m >= M_lim || n >= N_lim) continue;
@@ -422,9 +703,9 @@ __global__ void __launch_bounds__(NTHREADS, 1) k_gemm_fwd(FwdArgs args, int n_ti
   const int K = args.K;
   const int n_out = G.w.n_out;
 
-  if (threadIdx.x < 16) sm.lut[threadIdx.x] = args.levels ? args.levels[threadIdx.x] : 0.f;
+  fill_lut2(sm, args.levels);
 
-  f32x16_t acc[4][4];
+  f32x16_t acc[4][Layout<NTHREADS>::JB];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -434,42 +715,47 @@ __global__ void __launch_bounds__(NTHREADS, 1) k_gemm_fwd(FwdArgs args, int n_ti
   const rsrc_t xres = make_rsrc(args.x + (int64_t)m0 * args.ldx, (uint64_t)(rows_left < BM ? rows_left : BM) * args.ldx * 2);
   const WRes wres = make_wres<FMT>(G.w);
   const int nk = (K + BK - 1) / BK;
-  // The low-rank term runs as one extra K tile of the same loop: A columns from
-  // aext (s*H, bf16), B columns from the bf16 copy of B, zero beyond kx.
-  const bool has_ext = args.kx > 0 && G.bext != nullptr;
-  ALoad ra, rb;
-  WFwd<FMT, ALIGNED> rw;
-  load_a(ra, xres, 0, args.ldx, rows_left, 0, K);
-  rw.load(wres, n_out, K, n0, 0);
-  __syncthreads();   // lut visible
-  store_a(ra, sm.u.k.a[0]);
-  rw.store(sm.u.k.w[0], sm.lut);
-  __syncthreads();
-  const int nsteps = nk + (has_ext ? 1 : 0);
-  for (int kt = 0; kt < nsteps; ++kt) {
-    const int cur = kt & 1;
-    const bool more = kt + 1 < nk;
-    const bool ext_next = has_ext && kt + 1 == nk;
-    if (more) {
-      load_a(ra, xres, 0, args.ldx, rows_left, (kt + 1) * BK, K);
-      rw.load(wres, n_out, K, n0, (kt + 1) * BK);
-    } else if (ext_next) {
-      const rsrc_t ares = make_rsrc(args.aext + (int64_t)m0 * args.ldaext, (uint64_t)(rows_left < BM ? rows_left : BM) * args.ldaext * 2);
-      const int brows = n_out - n0 < BN ? n_out - n0 : BN;
-      const rsrc_t bres = make_rsrc(G.bext + (int64_t)n0 * args.kx, (uint64_t)brows * args.kx * 2);
-      load_a(ra, ares, (uint32_t)G.ext_col0 * 2u, args.ldaext, rows_left, 0, args.kx);
-      load_a(rb, bres, 0, args.kx, brows, 0, args.kx);
-    }
-    mma_stage<BK / 16>(sm.u.k.a[cur], sm.u.k.w[cur], acc);
-    if (more) {
-      store_a(ra, sm.u.k.a[cur ^ 1]);
-      rw.store(sm.u.k.w[cur ^ 1], sm.lut);
-    } else if (ext_next) {
-      store_a(ra, sm.u.k.a[cur ^ 1]);
-      store_a(rb, sm.u.k.w[cur ^ 1]);
-    }
-    __syncthreads();
+  // Iteration 0 is the low-rank term: A columns from aext (s*H, bf16) against the bf16
+  // copy of B, zero beyond kx (all zero when the adapters are off).  Iterations
+  // 1..nk are the K tiles of X and W.  Two register sets keep tiles i+1 and i+2 in
+  // flight; tile i+1 is written to the other LDS stage while stage i is multiplied.
+  const int n_iter = nk + 1;
+  {
+    const bool has_ext = args.kx > 0 && G.bext != nullptr;
+    const rsrc_t ares = make_rsrc(has_ext ? args.aext + (int64_t)m0 * args.ldaext : args.x,
+                                  has_ext ? (uint64_t)(rows_left < BM ? rows_left : BM) * args.ldaext * 2 : 0);
+    const int brows = n_out - n0 < BN ? n_out - n0 : BN;
+    const rsrc_t bres = make_rsrc(has_ext ? G.bext + (int64_t)n0 * args.kx : args.x,
+                                  has_ext ? (uint64_t)brows * args.kx * 2 : 0);
+    ALoad ea, eb;
+    load_a(ea, ares, (uint32_t)G.ext_col0 * 2u, args.ldaext, rows_left, 0, args.kx);
+    load_a(eb, bres, 0, args.kx, brows, 0, args.kx);
+    store_a(ea, sm.u.k.a[0]);
+    store_a(eb, sm.u.k.w[0]);
   }
+
+  ALoad ra;
+  WFwd<FMT, ALIGNED> rw, rw_next;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) load_a_part(ra, xres, 0, args.ldx, rows_left, 0, K, q);
+    rw.load(wres, n_out, K, n0, 0);
+    rw_next.load(wres, n_out, K, n0, BK);
+    __syncthreads();
+    for (int it = 0; it < n_iter; ++it) {
+      const int cur = it & 1;
+      uint16_t* na = sm.u.k.a[cur ^ 1];
+      uint16_t* nw = sm.u.k.w[cur ^ 1];
+      const int k_next2 = (it + 1) * BK;
+      mma_stage<NTHREADS>(sm.u.k.a[cur], sm.u.k.w[cur], acc, [&](int q) {
+        store_a_part(ra, na, q);
+        load_a_part(ra, xres, 0, args.ldx, rows_left, k_next2, K, q);
+        rw.store_part(nw, sm.lut2, q);
+      });
+      rw = rw_next;
+      rw_next.load(wres, n_out, K, n0, (it + 2) * BK);
+      __syncthreads();
+    }
+
   Epi E;
   E.f32 = args.y32 != nullptr;
   E.out = E.f32 ? (void*)(args.y32 + G.out_col0) : (void*)(args.y + G.out_col0);
@@ -479,7 +765,7 @@ __global__ void __launch_bounds__(NTHREADS, 1) k_gemm_fwd(FwdArgs args, int n_ti
   E.ldr = args.ldr;
   E.rope_tab = args.rope_tab; E.rope_cols = args.rope_tab ? args.rope_cols : 0;
   E.col_base = G.out_col0; E.seq = args.seq; E.hd = args.head_dim;
-  epilogue(sm, acc, m0, n0, args.M, n_out, E);
+  epilogue<NTHREADS>(sm, acc, m0, n0, args.M, n_out, E);
 }
 
 // ------------------------------------------------------------------ backward
@@ -493,9 +779,9 @@ __global__ void __launch_bounds__(NTHREADS, 1) k_gemm_bwd(BwdArgs args, int n_ti
   const int nt = tile - mt * n_tiles;
   const int m0 = mt * BM, j0 = nt * BN;
 
-  if (threadIdx.x < 16) sm.lut[threadIdx.x] = args.levels ? args.levels[threadIdx.x] : 0.f;
+  fill_lut2(sm, args.levels);
 
-  f32x16_t acc[4][4];
+  f32x16_t acc[4][Layout<NTHREADS>::JB];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -509,55 +795,242 @@ __global__ void __launch_bounds__(NTHREADS, 1) k_gemm_bwd(BwdArgs args, int n_ti
     seg_tiles[s] = (args.seg[s].w.n_out + BK - 1) / BK;
     total_k += seg_tiles[s];
   }
-  ALoad ra, rb;
-  WBwd<FMT, ALIGNED> rw;
-  int cur_seg = -1;
-  WRes wres;
-  auto issue = [&](int idx) {
-    int s = 0;
-    while (idx >= seg_tiles[s]) { idx -= seg_tiles[s]; ++s; }
-    const BwdSeg& S = args.seg[s];
-    if (s != cur_seg) { wres = make_wres<FMT>(S.w); cur_seg = s; }
-    const int k0 = idx * BK;
-    load_a(ra, dres, (uint32_t)S.a_col0 * 2u, args.lddy, rows_left, k0, S.w.n_out);
-    rw.load(wres, S.w.n_in, k0, S.w.n_out, j0);
-  };
-  // The low-rank term (s*G against A^T) runs as one extra K tile of the same loop.
-  const bool has_ext = args.kx > 0;
-  issue(0);
-  __syncthreads();
-  store_a(ra, sm.u.k.a[0]);
-  rw.store(sm.u.k.w[0], sm.lut);
-  __syncthreads();
-  const int nsteps = total_k + (has_ext ? 1 : 0);
-  for (int kt = 0; kt < nsteps; ++kt) {
-    const int cur = kt & 1;
-    const bool more = kt + 1 < total_k;
-    const bool ext_next = has_ext && kt + 1 == total_k;
-    if (more) {
-      issue(kt + 1);
-    } else if (ext_next) {
-      const rsrc_t ares = make_rsrc(args.aext + (int64_t)m0 * args.ldaext, (uint64_t)(rows_left < BM ? rows_left : BM) * args.ldaext * 2);
-      const int brows = args.N - j0 < BN ? args.N - j0 : BN;
-      const rsrc_t bres = make_rsrc(args.bext + (int64_t)j0 * args.ldbext, (uint64_t)brows * args.ldbext * 2);
-      load_a(ra, ares, 0, args.ldaext, rows_left, 0, args.kx);
-      load_a(rb, bres, 0, args.ldbext, brows, 0, args.kx);
-    }
-    mma_stage<BK / 16>(sm.u.k.a[cur], sm.u.k.w[cur], acc);
-    if (more) {
-      store_a(ra, sm.u.k.a[cur ^ 1]);
-      rw.store(sm.u.k.w[cur ^ 1], sm.lut);
-    } else if (ext_next) {
-      store_a(ra, sm.u.k.a[cur ^ 1]);
-      store_a(rb, sm.u.k.w[cur ^ 1]);
-    }
-    __syncthreads();
+  // Iteration 0 is the low-rank term (s*G against A^T, bf16); iterations 1..total_k
+  // run over the K tiles of the stacked segments.  Same two-set pipeline as forward.
+  const int n_iter = total_k + 1;
+  {
+    const bool has_ext = args.kx > 0;
+    const rsrc_t ares = make_rsrc(has_ext ? args.aext + (int64_t)m0 * args.ldaext : args.dy,
+                                  has_ext ? (uint64_t)(rows_left < BM ? rows_left : BM) * args.ldaext * 2 : 0);
+    const int brows = args.N - j0 < BN ? args.N - j0 : BN;
+    const rsrc_t bres = make_rsrc(has_ext ? args.bext + (int64_t)j0 * args.ldbext : args.dy,
+                                  has_ext ? (uint64_t)brows * args.ldbext * 2 : 0);
+    ALoad ea, eb;
+    load_a(ea, ares, 0, args.ldaext, rows_left, 0, args.kx);
+    load_a(eb, bres, 0, args.ldbext, brows, 0, args.kx);
+    store_a(ea, sm.u.k.a[0]);
+    store_a(eb, sm.u.k.w[0]);
   }
+  // tile index t (0-based over the stacked segments) -> segment and row offset
+  auto seg_of = [&](int t, int& s_out, int& k0_out) {
+    int s = 0;
+    if (t >= total_k) { s_out = args.n_segs - 1; k0_out = (seg_tiles[s_out] + 1) * BK; return; }   // zeros
+    while (t >= seg_tiles[s]) { t -= seg_tiles[s]; ++s; }
+    s_out = s; k0_out = t * BK;
+  };
+    auto load_a_q = [&](ALoad& ra, int t, int q) {
+      int s, k0; seg_of(t, s, k0);
+      load_a_part(ra, dres, (uint32_t)args.seg[s].a_col0 * 2u, args.lddy, rows_left, k0, args.seg[s].w.n_out, q);
+    };
+    auto load_w = [&](WBwd<FMT, ALIGNED>& rw, int t) {
+      int s, k0; seg_of(t, s, k0);
+      const WRes wres = make_wres<FMT>(args.seg[s].w);
+      rw.load(wres, args.seg[s].w.n_in, k0, args.seg[s].w.n_out, j0);
+    };
+    ALoad ra;
+    WBwd<FMT, ALIGNED> rw, rw_next;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) load_a_q(ra, 0, q);
+    load_w(rw, 0);
+    load_w(rw_next, 1);
+    __syncthreads();
+    for (int it = 0; it < n_iter; ++it) {
+      const int cur = it & 1;
+      uint16_t* na = sm.u.k.a[cur ^ 1];
+      uint16_t* nw = sm.u.k.w[cur ^ 1];
+      mma_stage<NTHREADS>(sm.u.k.a[cur], sm.u.k.w[cur], acc, [&](int q) {
+        store_a_part(ra, na, q);
+        load_a_q(ra, it + 1, q);
+        rw.store_part(nw, sm.lut2, q);
+      });
+      rw = rw_next;
+      load_w(rw_next, it + 2);
+      __syncthreads();
+    }
+
   Epi E;
   E.f32 = args.out32 != nullptr;
   E.out = E.f32 ? (void*)args.out32 : (void*)args.out16;
   E.ldo = args.ldo;
-  epilogue(sm, acc, m0, j0, args.M, args.N, E);
+  epilogue<NTHREADS>(sm, acc, m0, j0, args.M, args.N, E);
+}
+
+// ------------------------------------------------- fast path, 512 threads
+// 8 waves (2 per SIMD: while one waits on LDS or memory the other issues), each
+// 128 x 64 of the tile.  Used when K % 64 == 0 (forward) or every stacked segment's
+// rows % 64 == 0 (backward), so no tile straddles the end of a row.
+template <int FMT>
+__global__ void __launch_bounds__(NT_FAST, 1) k_gemm_fwd_fast(FwdArgs args, int n_tiles, int total_tiles, int padded) {
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  Smem& sm = *reinterpret_cast<Smem*>(smem_raw);
+  const int tile = xcd_tile(blockIdx.x, padded);
+  if (tile >= total_tiles) return;
+  const int mt = tile / n_tiles;
+  int rest = tile - mt * n_tiles;
+  int g = 0;
+  for (; g < args.n_groups - 1; ++g) {
+    const int nt_g = (args.g[g].w.n_out + BN - 1) / BN;
+    if (rest < nt_g) break;
+    rest -= nt_g;
+  }
+  const FwdGroup& G = args.g[g];
+  const int m0 = mt * BM, n0 = rest * BN;
+  const int K = args.K;
+  const int n_out = G.w.n_out;
+
+  fill_lut2(sm, args.levels);
+
+  constexpr int JB = Layout<NT_FAST>::JB;
+  f32x16_t acc[4][JB];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < JB; ++j) acc[i][j] = f32x16_t{};
+
+  const int rows_left = args.M - m0;
+  const int arows = rows_left < BM ? rows_left : BM;
+  const rsrc_t xres = make_rsrc(args.x + (int64_t)m0 * args.ldx, (uint64_t)arows * args.ldx * 2);
+  const int nk = K / BK;
+  const int n_iter = nk + 1;   // iteration 0: the low-rank term (kx <= 64)
+  {
+    const bool has_ext = args.kx > 0 && G.bext != nullptr;
+    const int brows = n_out - n0 < BN ? n_out - n0 : BN;
+    const rsrc_t ares = make_rsrc(has_ext ? args.aext + (int64_t)m0 * args.ldaext : args.x,
+                                  has_ext ? (uint64_t)arows * args.ldaext * 2 : 0);
+    const rsrc_t bres = make_rsrc(has_ext ? G.bext + (int64_t)n0 * args.kx : args.x,
+                                  has_ext ? (uint64_t)brows * args.kx * 2 : 0);
+    ext_tile(sm.u.k.a[0], ares, (uint32_t)G.ext_col0 * 2u, args.ldaext, has_ext ? arows : 0, args.kx);
+    ext_tile(sm.u.k.w[0], bres, 0, args.kx, has_ext ? brows : 0, args.kx);
+  }
+  // A: one register set, each quarter reloaded for tile it+1 right after it is
+  // stored; W: current and next tile in registers.  Loads past K are skipped.
+  AFast ra;
+  ra.init(xres, args.ldx);
+  WFwdFast<FMT> rw, rw_next;
+  rw.init(G.w, n0);
+  rw_next.init(G.w, n0);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) ra.load_q(0, q);
+  rw.load(0);
+  if (BK < K) rw_next.load(BK);
+  __syncthreads();
+  for (int it = 0; it < n_iter; ++it) {
+    const int cur = it & 1;
+    uint16_t* na = sm.u.k.a[cur ^ 1];
+    uint16_t* nw = sm.u.k.w[cur ^ 1];
+    const int k_next = (it + 1) * BK;
+    const bool more = k_next < K;
+    const float am = FMT == WF_BF16 ? 0.f : rw.absmax();
+    mma_stage<NT_FAST>(sm.u.k.a[cur], sm.u.k.w[cur], acc, [&](int q) {
+      ra.store_q(na, q);
+      if (more) ra.load_q((uint32_t)k_next, q);
+      rw.store_part(nw, sm.lut2, q, am);
+    });
+    rw = rw_next;
+    if (k_next + BK < K) rw_next.load(k_next + BK);
+    __syncthreads();
+  }
+
+  Epi E;
+  E.f32 = args.y32 != nullptr;
+  E.out = E.f32 ? (void*)(args.y32 + G.out_col0) : (void*)(args.y + G.out_col0);
+  E.ldo = args.ldy;
+  E.r16 = args.resid ? args.resid + G.out_col0 : nullptr;
+  E.r32 = args.resid32 ? args.resid32 + G.out_col0 : nullptr;
+  E.ldr = args.ldr;
+  E.rope_tab = args.rope_tab; E.rope_cols = args.rope_tab ? args.rope_cols : 0;
+  E.col_base = G.out_col0; E.seq = args.seq; E.hd = args.head_dim;
+  epilogue<NT_FAST>(sm, acc, m0, n0, args.M, n_out, E);
+}
+
+template <int FMT>
+__global__ void __launch_bounds__(NT_FAST, 1) k_gemm_bwd_fast(BwdArgs args, int n_tiles, int total_tiles, int padded) {
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  Smem& sm = *reinterpret_cast<Smem*>(smem_raw);
+  const int tile = xcd_tile(blockIdx.x, padded);
+  if (tile >= total_tiles) return;
+  const int mt = tile / n_tiles;
+  const int nt = tile - mt * n_tiles;
+  const int m0 = mt * BM, j0 = nt * BN;
+
+  fill_lut2(sm, args.levels);
+
+  constexpr int JB = Layout<NT_FAST>::JB;
+  f32x16_t acc[4][JB];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < JB; ++j) acc[i][j] = f32x16_t{};
+
+  const int rows_left = args.M - m0;
+  const int arows = rows_left < BM ? rows_left : BM;
+  const rsrc_t dres = make_rsrc(args.dy + (int64_t)m0 * args.lddy, (uint64_t)arows * args.lddy * 2);
+  int seg_tiles[kMaxGroups];
+  int total_k = 0;
+  for (int s = 0; s < args.n_segs; ++s) {
+    seg_tiles[s] = args.seg[s].w.n_out / BK;
+    total_k += seg_tiles[s];
+  }
+  // iteration 0: the low-rank term (kx <= 64)
+  {
+    const bool has_ext = args.kx > 0;
+    const int brows = args.N - j0 < BN ? args.N - j0 : BN;
+    const rsrc_t ares = make_rsrc(has_ext ? args.aext + (int64_t)m0 * args.ldaext : args.dy,
+                                  has_ext ? (uint64_t)arows * args.ldaext * 2 : 0);
+    const rsrc_t bres = make_rsrc(has_ext ? args.bext + (int64_t)j0 * args.ldbext : args.dy,
+                                  has_ext ? (uint64_t)brows * args.ldbext * 2 : 0);
+    ext_tile(sm.u.k.a[0], ares, 0, args.ldaext, has_ext ? arows : 0, args.kx);
+    ext_tile(sm.u.k.w[0], bres, 0, args.ldbext, has_ext ? brows : 0, args.kx);
+  }
+  // stacked K tile t < total_k -> segment and first row
+  auto seg_of = [&](int t, int& s_out, int& k0_out) {
+    int s = 0;
+    while (t >= seg_tiles[s]) { t -= seg_tiles[s]; ++s; }
+    s_out = s; k0_out = t * BK;
+  };
+  AFast ra;
+  ra.init(dres, args.lddy);
+  WBwdFast<FMT> rw, rw_next;
+  rw.init_lane(args.N);
+  rw_next.init_lane(args.N);
+  auto load_w = [&](WBwdFast<FMT>& w, int t) {
+    if (t >= total_k) return;
+    int s, k0; seg_of(t, s, k0);
+    w.load(args.seg[s].w, j0, k0);
+  };
+  {
+    int s, k0; seg_of(0, s, k0);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) ra.load_q((uint32_t)(args.seg[s].a_col0 + k0), q);
+  }
+  load_w(rw, 0);
+  load_w(rw_next, 1);
+  __syncthreads();
+  const int n_iter = total_k + 1;
+  for (int it = 0; it < n_iter; ++it) {
+    const int cur = it & 1;
+    uint16_t* na = sm.u.k.a[cur ^ 1];
+    uint16_t* nw = sm.u.k.w[cur ^ 1];
+    const bool more = it + 1 < total_k;
+    uint32_t col = 0;
+    if (more) { int s, k0; seg_of(it + 1, s, k0); col = (uint32_t)(args.seg[s].a_col0 + k0); }
+    const float a0 = FMT == WF_BF16 ? 0.f : rw.absmax(0);
+    const float a1 = FMT == WF_BF16 ? 0.f : rw.absmax(1);
+    mma_stage<NT_FAST>(sm.u.k.a[cur], sm.u.k.w[cur], acc, [&](int q) {
+      ra.store_q(na, q);
+      if (more) ra.load_q(col, q);
+      rw.store_part(nw, sm.lut2, q, a0, a1);
+    });
+    rw = rw_next;
+    load_w(rw_next, it + 2);
+    __syncthreads();
+  }
+
+  Epi E;
+  E.f32 = args.out32 != nullptr;
+  E.out = E.f32 ? (void*)args.out32 : (void*)args.out16;
+  E.ldo = args.ldo;
+  epilogue<NT_FAST>(sm, acc, m0, j0, args.M, args.N, E);
 }
 
 // --------------------------------------------------------- standalone dequant
@@ -580,13 +1053,11 @@ __global__ void k_dequant(WeightRef w, const float* levels, uint16_t* out) {
 }
 
 template <class F>
-hipError_t launch_fmt(int format, bool aligned, F&& f) {
+hipError_t launch_fmt(int format, F&& f) {
   switch (format) {
-    case WF_NF4: return aligned ? f(std::integral_constant<int, WF_NF4>{}, std::true_type{})
-                                : f(std::integral_constant<int, WF_NF4>{}, std::false_type{});
-    case WF_NF4_DQ: return aligned ? f(std::integral_constant<int, WF_NF4_DQ>{}, std::true_type{})
-                                   : f(std::integral_constant<int, WF_NF4_DQ>{}, std::false_type{});
-    default: return f(std::integral_constant<int, WF_BF16>{}, std::true_type{});
+    case WF_NF4: return f(std::integral_constant<int, WF_NF4>{});
+    case WF_NF4_DQ: return f(std::integral_constant<int, WF_NF4_DQ>{});
+    default: return f(std::integral_constant<int, WF_BF16>{});
   }
 }
 
@@ -594,15 +1065,17 @@ hipError_t launch_fmt(int format, bool aligned, F&& f) {
 
 hipError_t launch_gemm_fwd(const FwdArgs& a, hipStream_t s) {
   if (a.M <= 0 || a.n_groups <= 0) return hipSuccess;
+  if (a.kx > BK) return hipErrorInvalidValue;   // one extension tile in the forward
   const int m_tiles = (a.M + BM - 1) / BM;
   int n_tiles = 0;
   for (int g = 0; g < a.n_groups; ++g) n_tiles += (a.g[g].w.n_out + BN - 1) / BN;
   const int total = m_tiles * n_tiles;
   const int padded = (total + 7) / 8 * 8;
-  const bool aligned = (a.K % BK) == 0;
-  return launch_fmt(a.format, aligned, [&](auto fmt, auto al) {
-    auto kern = k_gemm_fwd<decltype(fmt)::value, decltype(al)::value>;
-    hipLaunchKernelGGL(kern, dim3(padded), dim3(NTHREADS), sizeof(Smem), s, a, n_tiles, total, padded);
+  const bool fast = (a.K % BK) == 0 && (a.ldx % 8) == 0;
+  return launch_fmt(a.format, [&](auto fmt) {
+    constexpr int F = decltype(fmt)::value;
+    if (fast) hipLaunchKernelGGL(k_gemm_fwd_fast<F>, dim3(padded), dim3(NT_FAST), sizeof(Smem), s, a, n_tiles, total, padded);
+    else hipLaunchKernelGGL((k_gemm_fwd<F, false>), dim3(padded), dim3(NTHREADS), sizeof(Smem), s, a, n_tiles, total, padded);
     return hipGetLastError();
   });
 }
@@ -613,12 +1086,30 @@ hipError_t launch_gemm_bwd(const BwdArgs& a, hipStream_t s) {
   const int n_tiles = (a.N + BN - 1) / BN;
   const int total = m_tiles * n_tiles;
   const int padded = (total + 7) / 8 * 8;
-  const bool aligned = (a.N % BK) == 0;
-  return launch_fmt(a.format, aligned, [&](auto fmt, auto al) {
-    auto kern = k_gemm_bwd<decltype(fmt)::value, decltype(al)::value>;
-    hipLaunchKernelGGL(kern, dim3(padded), dim3(NTHREADS), sizeof(Smem), s, a, n_tiles, total, padded);
+  // fast path: whole NF4 blocks per W row, every segment a whole number of K tiles,
+  // 16-byte aligned activation rows
+  bool fast = (a.N % BK) == 0 && (a.lddy % 8) == 0;
+  for (int sg = 0; sg < a.n_segs; ++sg) fast = fast && (a.seg[sg].w.n_out % BK) == 0 && (a.seg[sg].a_col0 % 8) == 0;
+  // The kernel takes the first 64 low-rank columns as one extra K tile; wider
+  // low-rank terms (stacked q|k|v or gate|up at rank > 16) add the remaining columns
+  // into the float32 result with a second, generic MFMA GEMM.
+  if (a.kx > BK && !a.out32) return hipErrorInvalidValue;
+  BwdArgs k = a;
+  if (k.kx > BK) k.kx = BK;
+  hipError_t e = launch_fmt(a.format, [&](auto fmt) {
+    constexpr int F = decltype(fmt)::value;
+    if (fast) hipLaunchKernelGGL(k_gemm_bwd_fast<F>, dim3(padded), dim3(NT_FAST), sizeof(Smem), s, k, n_tiles, total, padded);
+    else hipLaunchKernelGGL((k_gemm_bwd<F, false>), dim3(padded), dim3(NTHREADS), sizeof(Smem), s, k, n_tiles, total, padded);
     return hipGetLastError();
   });
+  if (e != hipSuccess || a.kx <= BK) return e;
+  GemmArgs g;
+  g.A = a.aext + BK; g.sAm = a.ldaext; g.sAk = 1;
+  g.B = a.bext + BK; g.sBn = a.ldbext; g.sBk = 1;
+  g.C = a.out32; g.sCm = a.ldo; g.sCn = 1; g.c_f32 = 1;
+  g.M = a.M; g.N = a.N; g.K = a.kx - BK;
+  g.alpha = 1.f; g.beta = 1.f;
+  return launch_gemm_generic(g, s);
 }
 
 hipError_t launch_dequant(const WeightRef& w, int32_t format, const float* levels, uint16_t* out, hipStream_t s) {
@@ -639,16 +1130,18 @@ hipError_t gemm_dequant_init() {
     hipError_t r = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(Smem));
     if (r != hipSuccess) e = r;
   };
-  set((const void*)k_gemm_fwd<WF_NF4, true>);
   set((const void*)k_gemm_fwd<WF_NF4, false>);
-  set((const void*)k_gemm_fwd<WF_NF4_DQ, true>);
   set((const void*)k_gemm_fwd<WF_NF4_DQ, false>);
-  set((const void*)k_gemm_fwd<WF_BF16, true>);
-  set((const void*)k_gemm_bwd<WF_NF4, true>);
+  set((const void*)k_gemm_fwd<WF_BF16, false>);
   set((const void*)k_gemm_bwd<WF_NF4, false>);
-  set((const void*)k_gemm_bwd<WF_NF4_DQ, true>);
   set((const void*)k_gemm_bwd<WF_NF4_DQ, false>);
-  set((const void*)k_gemm_bwd<WF_BF16, true>);
+  set((const void*)k_gemm_bwd<WF_BF16, false>);
+  set((const void*)k_gemm_fwd_fast<WF_NF4>);
+  set((const void*)k_gemm_fwd_fast<WF_NF4_DQ>);
+  set((const void*)k_gemm_fwd_fast<WF_BF16>);
+  set((const void*)k_gemm_bwd_fast<WF_NF4>);
+  set((const void*)k_gemm_bwd_fast<WF_NF4_DQ>);
+  set((const void*)k_gemm_bwd_fast<WF_BF16>);
   return e;
 }
 

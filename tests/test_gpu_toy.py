@@ -130,3 +130,20 @@ def test_empty_batch():
     for l in range(2):
         for p in H.PROJS:
             assert np.all(out["dA"][l][p] == 0) and np.all(out["dB"][l][p] == 0)
+
+
+@pytest.mark.parametrize("rank", [3, 32, 64])
+def test_lora_ranks(rank):
+    """A rank padded up to 16, and ranks whose stacked low-rank terms in the backward
+    (3 r columns for q|k|v, 2 r for gate|up) are wider than one 64-column K tile."""
+    w = TOY.with_(lora_r=rank, lora_alpha=2.0 * rank)
+    x, dy = synth.activations(w)
+    say("case: toy lora rank", rank)
+    run = H.GpuRun(w, [0, 1])
+    gpu = run.step(x, dy, w.batch, w.seq)
+    src = run.src
+    run.close()
+    ora = H.oracle_step(w, src, [synth.layer_lora(w, l) for l in range(2)], x, dy, w.batch, w.seq)
+    errs, fails = H.compare(gpu, ora)
+    say({k: f"{v:.2e}" for k, v in errs.items() if k in ("Y", "dX")})
+    assert not fails, fails
