@@ -1,0 +1,482 @@
+// Causal grouped-query attention, flash style, gfx950 (CDNA4), 64-wide waves.
+//
+// Scores S = c Q K^T (c = 1/sqrt(hd)), causal mask, P = softmax(S), O = P V; the
+// backward gives dV = P^T dO, dP = dO V^T, dS = c P (dP - rowsum(dO * O)), dQ = dS K,
+// dK = dS^T Q, with dK and dV summed over the query heads that share a key/value head
+// ("Fine-Tuning an 8B Parameter Model on a 4 GB Laptop GPU": the decoder layer is the
+// Llama-3.1-8B one, grouped-query attention with rotary positions applied to q, k).
+//
+// Nothing of size seq x seq is stored.  The forward keeps a running maximum and sum
+// per query and writes O and the base-2 log-sum-exp L of the scaled scores; the
+// backward recomputes P = exp2(S c log2(e) - L) tile by tile.  Every product takes
+// bf16 operands (P and dS are rounded to bf16 as MFMA operands) and accumulates in
+// float32 on v_mfma_f32_32x32x16_bf16.
+//
+// MFMA operand layouts (lane = 0..63, 32 x 32 x 16): A[i][k] sits in lane
+// i + 32 (k / 8), element k % 8; B[k][j] in lane j + 32 (k / 8); the result C[i][j] in
+// lane j + 32 ((i / 4) % 2), register (i / 8) * 4 + i % 4.  A score tile computed as
+// C therefore leaves, in each lane, 16 rows for one column.  When that tile is reused
+// as an operand of a second product whose contraction runs over those rows, the
+// contraction index is taken in the permuted order the lane already holds (any
+// order sums to the same result); the other operand is read from LDS in that same
+// order.  Tiles read along the contraction in the transposed direction are kept
+// transposed in LDS ([d][row], built with byte permutes from row pairs).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <cmath>
+
+#include "lsq_internal.hpp"
+
+namespace lsq {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+constexpr int KB = 64;                  // rows (keys or queries) per streamed tile
+constexpr int PT = KB + 4;              // pitch of a transposed tile [d][row], elements
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));   // RNE
+}
+__device__ __forceinline__ float bf_lo(uint32_t u) { return __builtin_bit_cast(float, u << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t u) { return __builtin_bit_cast(float, u & 0xFFFF0000u); }
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint64_t bytes) {
+  const uint32_t n = bytes > 0xFFFFFFF0ull ? 0xFFFFFFF0u : (uint32_t)bytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)n, 0x00020000);
+}
+// 16 bytes at a range-checked per-lane offset (past the end: zeros)
+__device__ __forceinline__ uint4 bload16(rsrc_t r, uint32_t off) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ bf16x8_t as_bf8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
+__device__ __forceinline__ f32x16_t mfma(bf16x8_t a, bf16x8_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+// eight consecutive accumulator values (one k16 step of a reused score tile) as bf16
+__device__ __forceinline__ bf16x8_t pack8(const f32x16_t& x, int base) {
+  return as_bf8(make_uint4(pack2(x[base], x[base + 1]), pack2(x[base + 2], x[base + 3]),
+                           pack2(x[base + 4], x[base + 5]), pack2(x[base + 6], x[base + 7])));
+}
+// Operand fragment from a transposed LDS tile t[d][row]: lane (i + 32 hh) takes rows
+// r0 + 4 hh + {0..3} and r0 + 8 + 4 hh + {0..3} of line d = d0 + i, matching the row
+// order of pack8 over a C tile's registers 8 s .. 8 s + 7 (r0 = 16 s within the block).
+__device__ __forceinline__ bf16x8_t tfrag(const uint16_t* t, int d, int r0, int hh) {
+  const uint16_t* src = t + d * PT + r0 + 4 * hh;
+  const uint2 lo = *reinterpret_cast<const uint2*>(src);
+  const uint2 hi = *reinterpret_cast<const uint2*>(src + 8);
+  return as_bf8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+}
+
+// One 64-row tile of a head (rows row0.., hd columns) moved global -> LDS, optionally
+// row-major (pitch hd + 8) and/or transposed (pitch PT).  Unit u covers rows 2p, 2p+1
+// (p = u % 32) and 8 columns 8c (c = u / 32); NT threads.
+template <int HD, int NT>
+struct TileMover {
+  static constexpr int NU = 32 * (HD / 8) / NT;     // units per thread
+  uint4 v[NU][2];
+  __device__ __forceinline__ void load(rsrc_t res, int ld, int row0) {
+#pragma unroll
+    for (int i = 0; i < NU; ++i) {
+      const int u = threadIdx.x + NT * i, p = u & 31, c = u >> 5;
+#pragma unroll
+      for (int r = 0; r < 2; ++r)
+        v[i][r] = bload16(res, ((uint32_t)(row0 + 2 * p + r) * (uint32_t)ld + 8u * c) * 2u);
+    }
+  }
+  __device__ __forceinline__ void store_rows(uint16_t* s) const {
+#pragma unroll
+    for (int i = 0; i < NU; ++i) {
+      const int u = threadIdx.x + NT * i, p = u & 31, c = u >> 5;
+#pragma unroll
+      for (int r = 0; r < 2; ++r) *reinterpret_cast<uint4*>(s + (2 * p + r) * (HD + 8) + 8 * c) = v[i][r];
+    }
+  }
+  __device__ __forceinline__ void store_t(uint16_t* t) const {
+#pragma unroll
+    for (int i = 0; i < NU; ++i) {
+      const int u = threadIdx.x + NT * i, p = u & 31, c = u >> 5;
+      const uint32_t* r0 = reinterpret_cast<const uint32_t*>(&v[i][0]);
+      const uint32_t* r1 = reinterpret_cast<const uint32_t*>(&v[i][1]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {   // dword j = columns 8c + 2j, 8c + 2j + 1
+        *reinterpret_cast<uint32_t*>(t + (8 * c + 2 * j) * PT + 2 * p) = __builtin_amdgcn_perm(r1[j], r0[j], 0x05040100u);
+        *reinterpret_cast<uint32_t*>(t + (8 * c + 2 * j + 1) * PT + 2 * p) = __builtin_amdgcn_perm(r1[j], r0[j], 0x07060302u);
+      }
+    }
+  }
+};
+
+// Row fragments of a head kept in registers as the B operand of a product over d:
+// step s holds columns 16 s + 8 hh .. + 7 of row `row` (zeros past the end).
+template <int HD>
+__device__ __forceinline__ void row_frags(bf16x8_t (&f)[HD / 16], rsrc_t res, int ld, int row, int hh) {
+#pragma unroll
+  for (int s = 0; s < HD / 16; ++s) f[s] = as_bf8(bload16(res, ((uint32_t)row * (uint32_t)ld + 16u * s + 8u * hh) * 2u));
+}
+
+// ------------------------------------------------------------------ forward
+// Workgroup: 128 queries of one (batch, q head), 4 waves x 32 queries.  Per 64-key
+// tile each wave computes S^T = K Q^T (keys x queries: each lane holds one query),
+// updates the running max / sum, and accumulates O^T = V^T P^T.
+template <int HD>
+__global__ void __launch_bounds__(256) k_attn_fwd(AttnArgs a) {
+  constexpr int NS = HD / 16, ND = HD / 32, PR = HD + 8;
+  __shared__ __align__(16) uint16_t sk[KB * PR];
+  __shared__ __align__(16) uint16_t svt[HD * PT];
+  const int nqb = (a.S + 127) / 128;
+  const int qb = nqb - 1 - (int)blockIdx.x;          // longest rows first
+  const int bh = blockIdx.y, b = bh / a.hq, h = bh % a.hq, g = h / (a.hq / a.hkv);
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, ql = lane & 31, hh = lane >> 5;
+  const int qw = qb * 128 + 32 * w, q = qw + ql;
+  const uint64_t head_bytes = (uint64_t)a.S * a.ldqkv * 2;
+  const uint16_t* base = a.qkv + (int64_t)b * a.S * a.ldqkv;
+  const rsrc_t rq = make_rsrc(base + h * HD, head_bytes);
+  const rsrc_t rk = make_rsrc(base + a.qd + g * HD, head_bytes);
+  const rsrc_t rv = make_rsrc(base + a.qd + a.kvd + g * HD, head_bytes);
+  bf16x8_t qf[NS];
+  row_frags<HD>(qf, rq, a.ldqkv, q, hh);
+
+  const int last_key = min(qb * 128 + 127, a.S - 1);
+  const int n_kb = last_key / KB + 1;
+  const float cl = a.scale * kLog2e;
+  f32x16_t o[ND];
+#pragma unroll
+  for (int d = 0; d < ND; ++d) o[d] = f32x16_t{};
+  float m = -INFINITY, l = 0.f;
+  TileMover<HD, 256> tk, tv;
+  tk.load(rk, a.ldqkv, 0);
+  tv.load(rv, a.ldqkv, 0);
+  for (int kb = 0; kb < n_kb; ++kb) {
+    __syncthreads();                    // the previous tile is no longer read
+    tk.store_rows(sk);
+    tv.store_t(svt);
+    __syncthreads();
+    if (kb + 1 < n_kb) {
+      tk.load(rk, a.ldqkv, (kb + 1) * KB);
+      tv.load(rv, a.ldqkv, (kb + 1) * KB);
+    }
+    const int k0 = kb * KB;
+    if (k0 > qw + 31) continue;         // tile entirely after this wave's queries
+    f32x16_t s[2];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      s[kk] = f32x16_t{};
+#pragma unroll
+      for (int st = 0; st < NS; ++st)
+        s[kk] = mfma(*reinterpret_cast<const bf16x8_t*>(sk + (32 * kk + ql) * PR + 16 * st + 8 * hh), qf[st], s[kk]);
+    }
+    float mb = -INFINITY;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int key = k0 + 32 * kk + (v >> 2) * 8 + 4 * hh + (v & 3);
+        const float t = (key <= q && key < a.S) ? s[kk][v] * cl : -INFINITY;
+        s[kk][v] = t;
+        mb = fmaxf(mb, t);
+      }
+    mb = fmaxf(mb, __shfl_xor(mb, 32));
+    const float mn = fmaxf(m, mb);
+    const float mu = mn == -INFINITY ? 0.f : mn;
+    const float alpha = __builtin_amdgcn_exp2f(m - mu);
+    m = mn;
+    float ls = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const float p = __builtin_amdgcn_exp2f(s[kk][v] - mu);
+        s[kk][v] = p;
+        ls += p;
+      }
+    l = l * alpha + ls;
+#pragma unroll
+    for (int d = 0; d < ND; ++d) o[d] *= alpha;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        const bf16x8_t pb = pack8(s[kk], 8 * st);
+#pragma unroll
+        for (int d = 0; d < ND; ++d) o[d] = mfma(tfrag(svt, 32 * d + ql, 32 * kk + 16 * st, hh), pb, o[d]);
+      }
+  }
+  const float lt = l + __shfl_xor(l, 32);
+  if (q < a.S) {
+    const float inv = 1.f / lt;
+    uint16_t* dst = a.out + ((int64_t)b * a.S + q) * a.ldo + h * HD;
+#pragma unroll
+    for (int d = 0; d < ND; ++d)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int col = 32 * d + 8 * g4 + 4 * hh;
+        *reinterpret_cast<uint2*>(dst + col) = make_uint2(pack2(o[d][4 * g4] * inv, o[d][4 * g4 + 1] * inv),
+                                                          pack2(o[d][4 * g4 + 2] * inv, o[d][4 * g4 + 3] * inv));
+      }
+    if (hh == 0 && a.lse) a.lse[(int64_t)bh * a.S + q] = m + __builtin_amdgcn_logf(lt);
+  }
+}
+
+// ------------------------------------------------------- backward: rowsum(dO * O)
+template <int HD>
+__global__ void k_attn_dd(AttnArgs a) {
+  constexpr int TPR = HD / 8;                       // threads per (row, head)
+  const int64_t idx = (int64_t)blockIdx.x * (256 / TPR) + threadIdx.x / TPR;   // row * hq + head
+  const int part = threadIdx.x % TPR;
+  const int64_t n = (int64_t)a.batch * a.S * a.hq;
+  float acc = 0.f;
+  const bool ok = idx < n;
+  const int64_t row = ok ? idx / a.hq : 0;
+  const int head = ok ? (int)(idx % a.hq) : 0;
+  if (ok) {
+    const uint4 x = *reinterpret_cast<const uint4*>(a.dout + row * a.lddo + head * HD + 8 * part);
+    const uint4 y = *reinterpret_cast<const uint4*>(a.out + row * a.ldo + head * HD + 8 * part);
+    const uint32_t xs[4] = {x.x, x.y, x.z, x.w}, ys[4] = {y.x, y.y, y.z, y.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc += bf_lo(xs[j]) * bf_lo(ys[j]) + bf_hi(xs[j]) * bf_hi(ys[j]);
+  }
+#pragma unroll
+  for (int sh = TPR / 2; sh > 0; sh >>= 1) acc += __shfl_xor(acc, sh);
+  if (ok && part == 0) {
+    const int64_t bq = row / a.S, pos = row % a.S;
+    a.dd[(bq * a.hq + head) * a.S + pos] = acc;
+  }
+}
+
+// ------------------------------------------------------------ backward: dQ
+// Workgroup: 128 queries of one (batch, q head), 4 waves x 32 queries, over the key
+// tiles up to the diagonal: S^T = K Q^T and dP^T = V dO^T (keys x queries), dS, then
+// dQ^T += K^T dS^T.
+template <int HD>
+__global__ void __launch_bounds__(256) k_attn_dq(AttnArgs a) {
+  constexpr int NS = HD / 16, ND = HD / 32, PR = HD + 8;
+  __shared__ __align__(16) uint16_t sk[KB * PR];
+  __shared__ __align__(16) uint16_t sv[KB * PR];
+  __shared__ __align__(16) uint16_t skt[HD * PT];
+  const int nqb = (a.S + 127) / 128;
+  const int qb = nqb - 1 - (int)blockIdx.x;
+  const int bh = blockIdx.y, b = bh / a.hq, h = bh % a.hq, g = h / (a.hq / a.hkv);
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, ql = lane & 31, hh = lane >> 5;
+  const int qw = qb * 128 + 32 * w, q = qw + ql;
+  const uint64_t head_bytes = (uint64_t)a.S * a.ldqkv * 2;
+  const uint16_t* base = a.qkv + (int64_t)b * a.S * a.ldqkv;
+  const rsrc_t rq = make_rsrc(base + h * HD, head_bytes);
+  const rsrc_t rk = make_rsrc(base + a.qd + g * HD, head_bytes);
+  const rsrc_t rv = make_rsrc(base + a.qd + a.kvd + g * HD, head_bytes);
+  const rsrc_t rdo = make_rsrc(a.dout + (int64_t)b * a.S * a.lddo + h * HD, (uint64_t)a.S * a.lddo * 2);
+  bf16x8_t qf[NS], of[NS];
+  row_frags<HD>(qf, rq, a.ldqkv, q, hh);
+  row_frags<HD>(of, rdo, a.lddo, q, hh);
+  const bool qok = q < a.S;
+  const float L = qok ? a.lse[(int64_t)bh * a.S + q] : 0.f;
+  const float D = qok ? a.dd[(int64_t)bh * a.S + q] : 0.f;
+
+  const int last_key = min(qb * 128 + 127, a.S - 1);
+  const int n_kb = last_key / KB + 1;
+  const float cl = a.scale * kLog2e;
+  f32x16_t dq[ND];
+#pragma unroll
+  for (int d = 0; d < ND; ++d) dq[d] = f32x16_t{};
+  TileMover<HD, 256> tk, tv;
+  tk.load(rk, a.ldqkv, 0);
+  tv.load(rv, a.ldqkv, 0);
+  for (int kb = 0; kb < n_kb; ++kb) {
+    __syncthreads();
+    tk.store_rows(sk);
+    tk.store_t(skt);
+    tv.store_rows(sv);
+    __syncthreads();
+    if (kb + 1 < n_kb) {
+      tk.load(rk, a.ldqkv, (kb + 1) * KB);
+      tv.load(rv, a.ldqkv, (kb + 1) * KB);
+    }
+    const int k0 = kb * KB;
+    if (k0 > qw + 31) continue;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      f32x16_t s = f32x16_t{}, dp = f32x16_t{};
+#pragma unroll
+      for (int st = 0; st < NS; ++st) {
+        s = mfma(*reinterpret_cast<const bf16x8_t*>(sk + (32 * kk + ql) * PR + 16 * st + 8 * hh), qf[st], s);
+        dp = mfma(*reinterpret_cast<const bf16x8_t*>(sv + (32 * kk + ql) * PR + 16 * st + 8 * hh), of[st], dp);
+      }
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int key = k0 + 32 * kk + (v >> 2) * 8 + 4 * hh + (v & 3);
+        const bool ok = qok && key <= q && key < a.S;
+        const float p = ok ? __builtin_amdgcn_exp2f(s[v] * cl - L) : 0.f;
+        s[v] = a.scale * p * (dp[v] - D);
+      }
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        const bf16x8_t db = pack8(s, 8 * st);
+#pragma unroll
+        for (int d = 0; d < ND; ++d) dq[d] = mfma(tfrag(skt, 32 * d + ql, 32 * kk + 16 * st, hh), db, dq[d]);
+      }
+    }
+  }
+  if (qok) {
+    float* dst = a.dqkv + ((int64_t)b * a.S + q) * a.lddqkv + h * HD;
+#pragma unroll
+    for (int d = 0; d < ND; ++d)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4)
+        *reinterpret_cast<float4*>(dst + 32 * d + 8 * g4 + 4 * hh) =
+            make_float4(dq[d][4 * g4], dq[d][4 * g4 + 1], dq[d][4 * g4 + 2], dq[d][4 * g4 + 3]);
+  }
+}
+
+// -------------------------------------------------------- backward: dK, dV
+// Workgroup: 64 keys of one (batch, kv head), 2 waves x 32 keys, looping over the
+// group's q heads in order and, per head, over the 64-query tiles from the diagonal
+// on: S = Q K^T and dP = dO V^T (queries x keys: each lane holds one key), P, dS, then
+// dV += P^T dO and dK += dS^T Q.  The sums over heads and tiles stay in registers, in
+// a fixed order.
+template <int HD>
+__global__ void __launch_bounds__(128) k_attn_dkv(AttnArgs a) {
+  constexpr int NS = HD / 16, ND = HD / 32, PR = HD + 8;
+  __shared__ __align__(16) uint16_t sq[KB * PR];
+  __shared__ __align__(16) uint16_t sdo[KB * PR];
+  __shared__ __align__(16) uint16_t sqt[HD * PT];
+  __shared__ __align__(16) uint16_t sdot[HD * PT];
+  __shared__ __align__(16) float sL[KB];
+  __shared__ __align__(16) float sD[KB];
+  const int kb = blockIdx.x;
+  const int bg = blockIdx.y, b = bg / a.hkv, g = bg % a.hkv;
+  const int nrep = a.hq / a.hkv;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, kl = lane & 31, hh = lane >> 5;
+  const int kw0 = kb * KB + 32 * w, key = kw0 + kl;
+  const uint64_t head_bytes = (uint64_t)a.S * a.ldqkv * 2;
+  const uint16_t* base = a.qkv + (int64_t)b * a.S * a.ldqkv;
+  const rsrc_t rk = make_rsrc(base + a.qd + g * HD, head_bytes);
+  const rsrc_t rv = make_rsrc(base + a.qd + a.kvd + g * HD, head_bytes);
+  bf16x8_t kf[NS], vf[NS];
+  row_frags<HD>(kf, rk, a.ldqkv, key, hh);
+  row_frags<HD>(vf, rv, a.ldqkv, key, hh);
+  const float cl = a.scale * kLog2e;
+  f32x16_t dk[ND], dv[ND];
+#pragma unroll
+  for (int d = 0; d < ND; ++d) { dk[d] = f32x16_t{}; dv[d] = f32x16_t{}; }
+  const int n_qb = (a.S + KB - 1) / KB;
+  for (int r = 0; r < nrep; ++r) {
+    const int h = g * nrep + r;
+    const int64_t bh = (int64_t)b * a.hq + h;
+    const rsrc_t rq = make_rsrc(base + h * HD, head_bytes);
+    const rsrc_t rdo = make_rsrc(a.dout + (int64_t)b * a.S * a.lddo + h * HD, (uint64_t)a.S * a.lddo * 2);
+    for (int qb = kb; qb < n_qb; ++qb) {
+      const int q0 = qb * KB;
+      TileMover<HD, 128> tq, to;
+      tq.load(rq, a.ldqkv, q0);
+      to.load(rdo, a.lddo, q0);
+      float lv = 0.f, dv_ = 0.f;
+      if (threadIdx.x < KB && q0 + (int)threadIdx.x < a.S) {
+        lv = a.lse[bh * a.S + q0 + threadIdx.x];
+        dv_ = a.dd[bh * a.S + q0 + threadIdx.x];
+      }
+      __syncthreads();                  // the previous tiles are no longer read
+      tq.store_rows(sq);
+      tq.store_t(sqt);
+      to.store_rows(sdo);
+      to.store_t(sdot);
+      if (threadIdx.x < KB) { sL[threadIdx.x] = lv; sD[threadIdx.x] = dv_; }
+      __syncthreads();
+#pragma unroll
+      for (int qs = 0; qs < 2; ++qs) {
+        if (q0 + 32 * qs + 31 < kw0) continue;      // every query before this wave's keys
+        f32x16_t s = f32x16_t{}, dp = f32x16_t{};
+#pragma unroll
+        for (int st = 0; st < NS; ++st) {
+          s = mfma(*reinterpret_cast<const bf16x8_t*>(sq + (32 * qs + kl) * PR + 16 * st + 8 * hh), kf[st], s);
+          dp = mfma(*reinterpret_cast<const bf16x8_t*>(sdo + (32 * qs + kl) * PR + 16 * st + 8 * hh), vf[st], dp);
+        }
+        // C[i = query][j = key]: register v holds query 32 qs + (v / 4) * 8 + 4 hh + v % 4
+        f32x16_t ds;
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int qi = 32 * qs + 8 * g4 + 4 * hh;
+          const float4 L4 = *reinterpret_cast<const float4*>(&sL[qi]);
+          const float4 D4 = *reinterpret_cast<const float4*>(&sD[qi]);
+          const float Ls[4] = {L4.x, L4.y, L4.z, L4.w}, Ds[4] = {D4.x, D4.y, D4.z, D4.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int v = 4 * g4 + e, qg = q0 + qi + e;
+            const bool ok = key <= qg && qg < a.S && key < a.S;
+            const float p = ok ? __builtin_amdgcn_exp2f(s[v] * cl - Ls[e]) : 0.f;
+            s[v] = p;
+            ds[v] = a.scale * p * (dp[v] - Ds[e]);
+          }
+        }
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          const bf16x8_t pa = pack8(s, 8 * st), da = pack8(ds, 8 * st);
+#pragma unroll
+          for (int d = 0; d < ND; ++d) {
+            dv[d] = mfma(pa, tfrag(sdot, 32 * d + kl, 32 * qs + 16 * st, hh), dv[d]);
+            dk[d] = mfma(da, tfrag(sqt, 32 * d + kl, 32 * qs + 16 * st, hh), dk[d]);
+          }
+        }
+      }
+    }
+  }
+  // C[i = key][j = d]: lane (d + 32 hh), register v holds key (v / 4) * 8 + 4 hh + v % 4
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    const int kr = kw0 + (v >> 2) * 8 + 4 * hh + (v & 3);
+    if (kr >= a.S) continue;
+    float* row = a.dqkv + ((int64_t)b * a.S + kr) * a.lddqkv;
+#pragma unroll
+    for (int d = 0; d < ND; ++d) {
+      row[a.qd + g * HD + 32 * d + kl] = dk[d][v];
+      row[a.qd + a.kvd + g * HD + 32 * d + kl] = dv[d][v];
+    }
+  }
+}
+
+template <int HD>
+hipError_t fwd_hd(const AttnArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(k_attn_fwd<HD>, dim3((a.S + 127) / 128, a.batch * a.hq), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int HD>
+hipError_t bwd_hd(const AttnArgs& a, hipStream_t s) {
+  const int64_t rows = (int64_t)a.batch * a.S * a.hq;
+  const int per_block = 256 / (HD / 8);
+  hipLaunchKernelGGL(k_attn_dd<HD>, dim3((unsigned)((rows + per_block - 1) / per_block)), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(k_attn_dkv<HD>, dim3((a.S + KB - 1) / KB, a.batch * a.hkv), dim3(128), 0, s, a);
+  hipLaunchKernelGGL(k_attn_dq<HD>, dim3((a.S + 127) / 128, a.batch * a.hq), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+bool shape_ok(const AttnArgs& a) {
+  return (a.hd == 64 || a.hd == 128) && a.hkv > 0 && a.hq % a.hkv == 0 && a.ldqkv % 8 == 0 && a.ldo % 8 == 0 &&
+         a.qd % 8 == 0 && a.kvd % 8 == 0;
+}
+
+}  // namespace
+
+hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t s) {
+  if (a.batch <= 0 || a.S <= 0) return hipSuccess;
+  if (!shape_ok(a) || !a.qkv || !a.out) return hipErrorInvalidValue;
+  return a.hd == 64 ? fwd_hd<64>(a, s) : fwd_hd<128>(a, s);
+}
+
+hipError_t launch_attn_bwd(const AttnArgs& a, hipStream_t s) {
+  if (a.batch <= 0 || a.S <= 0) return hipSuccess;
+  if (!shape_ok(a) || !a.qkv || !a.out || !a.dout || !a.lse || !a.dd || !a.dqkv || a.lddo % 8 != 0 ||
+      a.lddqkv % 4 != 0)
+    return hipErrorInvalidValue;
+  return a.hd == 64 ? bwd_hd<64>(a, s) : bwd_hd<128>(a, s);
+}
+
+}  // namespace lsq

@@ -1,4 +1,4 @@
-// Decoder glue around the projections: RMSNorm, rotary embedding, causal softmax,
+// Decoder glue around the projections: RMSNorm, rotary embedding,
 // SwiGLU (forward and backward) and small layout conversions of the LoRA operands.
 // All of it is HBM-bound elementwise / row-wise work: one pass over its operands,
 // float32 arithmetic, bf16 in and out.
@@ -129,43 +129,6 @@ __global__ void k_rope(uint16_t* qk, int ld, int64_t n, int seq, int nh, int hd,
   p[i + half] = tobf(y2);
 }
 
-// one wave per row; row r is query position r % seq of its (batch, head)
-__global__ void __launch_bounds__(256) k_softmax_causal(const float* S, uint16_t* P, int64_t n_rows, int seq) {
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (row >= n_rows) return;
-  const int qi = (int)(row % seq);
-  const float* s = S + row * seq;
-  uint16_t* p = P + row * seq;
-  float mx = -INFINITY;
-  for (int j = lane; j <= qi; j += 64) mx = fmaxf(mx, s[j]);
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
-  float sum = 0.f;
-  for (int j = lane; j <= qi; j += 64) sum += __expf(s[j] - mx);
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o, 64);
-  const float inv = 1.0f / sum;
-  for (int j = lane; j < seq; j += 64) p[j] = j <= qi ? tobf(__expf(s[j] - mx) * inv) : (uint16_t)0;
-}
-
-// dS = scale * P * (dP - sum_j P dP), zero above the diagonal
-__global__ void __launch_bounds__(256) k_softmax_bwd(const float* dP, const uint16_t* P, uint16_t* dS, int64_t n_rows,
-                                                     int seq, float scale) {
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (row >= n_rows) return;
-  const int qi = (int)(row % seq);
-  const float* dp = dP + row * seq;
-  const uint16_t* p = P + row * seq;
-  uint16_t* ds = dS + row * seq;
-  float d = 0.f;
-  for (int j = lane; j <= qi; j += 64) d += bf(p[j]) * dp[j];
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) d += __shfl_xor(d, o, 64);
-  for (int j = lane; j < seq; j += 64) ds[j] = j <= qi ? tobf(scale * bf(p[j]) * (dp[j] - d)) : (uint16_t)0;
-}
-
 __device__ __forceinline__ float sigmoidf(float z) { return 1.0f / (1.0f + __expf(-z)); }
 
 __global__ void k_swiglu_fwd(const float* gu, int I, uint16_t* act, int64_t n) {
@@ -255,19 +218,6 @@ hipError_t launch_rope_tab(uint16_t* qk, int32_t ld, int32_t T, int32_t seq, int
   const int64_t n = (int64_t)T * nh * (hd / 2);
   if (n <= 0) return hipSuccess;
   hipLaunchKernelGGL(k_rope, dim3(blocks_for(n, 256)), dim3(256), 0, s, qk, ld, n, seq, nh, hd, tab, inverse);
-  return hipGetLastError();
-}
-
-hipError_t launch_softmax_causal(const float* S, uint16_t* P, int64_t n_rows, int32_t seq, float, hipStream_t s) {
-  if (n_rows <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_softmax_causal, dim3(blocks_for(n_rows, 4)), dim3(256), 0, s, S, P, n_rows, seq);
-  return hipGetLastError();
-}
-
-hipError_t launch_softmax_bwd(const float* dP, const uint16_t* P, uint16_t* dS, int64_t n_rows, int32_t seq,
-                              float scale, hipStream_t s) {
-  if (n_rows <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_softmax_bwd, dim3(blocks_for(n_rows, 4)), dim3(256), 0, s, dP, P, dS, n_rows, seq, scale);
   return hipGetLastError();
 }
 

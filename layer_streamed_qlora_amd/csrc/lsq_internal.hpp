@@ -125,6 +125,25 @@ struct GemmArgs {
 };
 hipError_t launch_gemm_generic(const GemmArgs& a, hipStream_t s);
 
+// Causal grouped-query attention over batch sequences of S tokens, flash style.
+// qkv: bf16 [batch * S, ldqkv], q heads at columns h * hd, k heads from qd, v heads
+// from qd + kvd; q head h reads kv head h / (hq / hkv).  hd is 64 or 128.
+struct AttnArgs {
+  const uint16_t* qkv = nullptr; int32_t ldqkv = 0;
+  int32_t qd = 0, kvd = 0;
+  int32_t batch = 0, S = 0, hq = 0, hkv = 0, hd = 0;
+  float scale = 0.f;                                  // 1 / sqrt(hd)
+  uint16_t* out = nullptr; int32_t ldo = 0;           // O, bf16 [batch * S, ldo] (backward: read)
+  float* lse = nullptr;                               // [batch * hq * S] base-2 log-sum-exp of scale * log2(e) * S
+  const uint16_t* dout = nullptr; int32_t lddo = 0;   // backward: dO, bf16 like O
+  float* dd = nullptr;                                // backward scratch [batch * hq * S]: rowsum(dO * O)
+  float* dqkv = nullptr; int32_t lddqkv = 0;          // backward: float32 dq | dk | dv, layout of qkv
+};
+// O and lse
+hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t s);
+// dq, dk, dv from dO, O, lse (dk, dv summed over each kv head's q heads)
+hipError_t launch_attn_bwd(const AttnArgs& a, hipStream_t s);
+
 // Batched float32 -> bf16 layout conversions (LoRA operands), one launch.
 struct ConvJob {
   const float* src = nullptr; int64_t lds = 0;
@@ -153,12 +172,6 @@ hipError_t launch_rope_tab(uint16_t* qk, int32_t ld, int32_t T, int32_t seq, int
                            const float2* tab, int32_t inverse, hipStream_t s);
 hipError_t launch_fill_f32(float* p, int64_t n, float v, hipStream_t s);
 hipError_t gemm_dequant_init();
-// causal softmax over rows of S (float32 [rows, S]) -> P bf16; rows = nz * seq
-hipError_t launch_softmax_causal(const float* S, uint16_t* P, int64_t n_rows, int32_t seq, float scale,
-                                 hipStream_t s);
-// dS = P * (dP - rowsum(P * dP)) * scale, bf16 out; dP float32, P bf16
-hipError_t launch_softmax_bwd(const float* dP, const uint16_t* P, uint16_t* dS, int64_t n_rows, int32_t seq,
-                              float scale, hipStream_t s);
 // gu float32 [T, 2I] (gate | up) -> act bf16 [T, I]
 hipError_t launch_swiglu_fwd(const float* gu, int32_t I, uint16_t* act, int32_t T, hipStream_t s);
 // gu float32, dact float32 [T, I] -> dgu bf16 [T, 2I]

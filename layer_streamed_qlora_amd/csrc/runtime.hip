@@ -53,7 +53,7 @@ struct DevPlan {
   uint64_t total = 0;
   uint64_t slots = 0, ck = 0, xref = 0;
   uint64_t n1 = 0, qkv = 0, att = 0, hb = 0, n2 = 0, gu = 0, act = 0, rstd1 = 0, rstd2 = 0;
-  uint64_t hs = 0, gs = 0, s32 = 0, p16 = 0, ds16 = 0;
+  uint64_t hs = 0, gs = 0, lse = 0, dd = 0;
   uint64_t dya = 0, dyb = 0, dh32 = 0, dh16 = 0, da32 = 0, dgu = 0, datt = 0, dqkv = 0, dqkv32 = 0, dn32 = 0;
   uint64_t lora = 0, lora_per_layer = 0, partial = 0, partial_bytes = 0;
   uint64_t levels = 0, rope = 0;
@@ -73,7 +73,6 @@ DevPlan make_plan(const ls_config& c, const BlobLayout& L) {
   const uint64_t qd = (uint64_t)c.n_heads * c.head_dim, kvd = (uint64_t)c.n_kv_heads * c.head_dim;
   const uint64_t qkvd = qd + 2 * kvd;
   const uint64_t r16 = r16_of(c), R7 = 7 * r16;
-  const uint64_t att_elems = T * (uint64_t)c.n_heads * (uint64_t)c.max_seq;
   P.n_slots = c.resident ? c.n_layers : c.n_buffers;
   P.slots = take(L.bytes * (uint64_t)P.n_slots);
   P.ck = take(2 * T * h * (uint64_t)c.n_layers);
@@ -89,9 +88,8 @@ DevPlan make_plan(const ls_config& c, const BlobLayout& L) {
   P.rstd2 = take(4 * T);
   P.hs = take(2 * T * R7);
   P.gs = take(2 * T * R7);
-  P.s32 = take(4 * att_elems);
-  P.p16 = take(2 * att_elems);
-  P.ds16 = take(2 * att_elems);
+  P.lse = take(4 * T * (uint64_t)c.n_heads);
+  P.dd = take(4 * T * (uint64_t)c.n_heads);
   P.dya = take(2 * T * h);
   P.dyb = take(2 * T * h);
   P.dh32 = take(4 * T * h);
@@ -443,87 +441,36 @@ ls_status lora_down(ls_ctx* c, int l, const Dims& d, const uint16_t* x, int ldx,
 
 double fwd_gemm_flop(const Dims& d, int n_out, int K, bool lora) { return 2.0 * d.T * n_out * K + (lora ? 2.0 * d.T * n_out * d.r : 0.0); }
 
-// Materialised causal attention forward: S = c Q K^T, P = softmax(S), O = P V.
+AttnArgs attn_args(ls_ctx* c, const Dims& d, const uint16_t* qkv, uint16_t* out) {
+  AttnArgs a;
+  a.qkv = qkv; a.ldqkv = d.qkvd; a.qd = d.qd; a.kvd = d.kvd;
+  a.batch = d.batch; a.S = d.seq; a.hq = d.hq; a.hkv = d.hkv; a.hd = d.hd;
+  a.scale = 1.0f / std::sqrt((float)d.hd);
+  a.out = out; a.ldo = d.qd;
+  a.lse = c->dp<float>(c->plan.lse);
+  return a;
+}
+
+// Causal attention forward, O = softmax(c Q K^T) V, plus the per-row log-sum-exp the
+// backward uses to rebuild P.
 ls_status attn_fwd(ls_ctx* c, const Dims& d, const uint16_t* qkv, uint16_t* out) {
-  const int S = d.seq, nrep = d.hq / d.hkv;
-  const float scale = 1.0f / std::sqrt((float)d.hd);
-  const int64_t SS = (int64_t)S * S;
-  float* s32 = c->dp<float>(c->plan.s32);
-  uint16_t* p16 = c->dp<uint16_t>(c->plan.p16);
-  const double fl = 2.0 * d.batch * d.hq * (double)S * (S + 1) / 2 * d.hd;
-  {
-    GemmArgs g;
-    g.A = qkv; g.sAm = d.qkvd; g.sAk = 1; g.zA = {(int64_t)S * d.qkvd, d.hd, 1};
-    g.B = qkv + d.qd; g.sBn = d.qkvd; g.sBk = 1; g.zB = {(int64_t)S * d.qkvd, d.hd, nrep};
-    g.C = s32; g.sCm = S; g.sCn = 1; g.zC = {(int64_t)d.hq * SS, SS, 1}; g.c_f32 = 1;
-    g.M = S; g.N = S; g.K = d.hd; g.nz = d.batch * d.hq; g.zdiv = d.hq; g.alpha = scale; g.causal = 1;
-    KTimer kt(c, LS_KC_ATTN, fl, 2.0 * d.T * (d.qd + d.kvd) + 4.0 * d.batch * d.hq * SS / 2);
-    HIPCHK(c, launch_gemm_generic(g, c->cs));
-  }
-  {
-    KTimer kt(c, LS_KC_ATTN, 0.0, 6.0 * d.batch * d.hq * SS / 2);
-    HIPCHK(c, launch_softmax_causal(s32, p16, (int64_t)d.batch * d.hq * S, S, 1.f, c->cs));
-  }
-  {
-    GemmArgs g;
-    g.A = p16; g.sAm = S; g.sAk = 1; g.zA = {(int64_t)d.hq * SS, SS, 1};
-    g.B = qkv + d.qd + d.kvd; g.sBn = 1; g.sBk = d.qkvd; g.zB = {(int64_t)S * d.qkvd, d.hd, nrep};
-    g.C = out; g.sCm = d.qd; g.sCn = 1; g.zC = {(int64_t)S * d.qd, d.hd, 1}; g.c_f32 = 0;
-    g.M = S; g.N = d.hd; g.K = S; g.nz = d.batch * d.hq; g.zdiv = d.hq; g.causal = 2;
-    KTimer kt(c, LS_KC_ATTN, fl, 2.0 * d.batch * d.hq * SS / 2 + 2.0 * d.T * (d.kvd + d.qd));
-    HIPCHK(c, launch_gemm_generic(g, c->cs));
-  }
+  const double fl = 4.0 * d.batch * d.hq * (double)d.seq * (d.seq + 1) / 2 * d.hd;
+  KTimer kt(c, LS_KC_ATTN, fl, 2.0 * d.T * (d.qkvd + d.qd) + 4.0 * d.T * d.hq);
+  HIPCHK(c, launch_attn_fwd(attn_args(c, d, qkv, out), c->cs));
   return LS_OK;
 }
 
-// Attention backward from dO (datt), recomputed P (p16) and q, k, v -> float32 dq, dk,
-// dv in dqkv32 (dK, dV summed over a kv head's q heads in float32, fixed order).
-ls_status attn_bwd(ls_ctx* c, const Dims& d, const uint16_t* qkv, const uint16_t* dout, float* dqkv32) {
-  const int S = d.seq, nrep = d.hq / d.hkv;
-  const float scale = 1.0f / std::sqrt((float)d.hd);
-  const int64_t SS = (int64_t)S * S;
-  float* dp32 = c->dp<float>(c->plan.s32);
-  uint16_t* p16 = c->dp<uint16_t>(c->plan.p16);
-  uint16_t* ds16 = c->dp<uint16_t>(c->plan.ds16);
-  const double fl = 2.0 * d.batch * d.hq * (double)S * (S + 1) / 2 * d.hd;
-  {   // dP = dO V^T
-    GemmArgs g;
-    g.A = dout; g.sAm = d.qd; g.sAk = 1; g.zA = {(int64_t)S * d.qd, d.hd, 1};
-    g.B = qkv + d.qd + d.kvd; g.sBn = d.qkvd; g.sBk = 1; g.zB = {(int64_t)S * d.qkvd, d.hd, nrep};
-    g.C = dp32; g.sCm = S; g.sCn = 1; g.zC = {(int64_t)d.hq * SS, SS, 1}; g.c_f32 = 1;
-    g.M = S; g.N = S; g.K = d.hd; g.nz = d.batch * d.hq; g.zdiv = d.hq; g.causal = 1;
-    KTimer kt(c, LS_KC_ATTN, fl, 2.0 * d.T * (d.qd + d.kvd) + 4.0 * d.batch * d.hq * SS / 2);
-    HIPCHK(c, launch_gemm_generic(g, c->cs));
-  }
-  {
-    KTimer kt(c, LS_KC_ATTN, 0.0, 8.0 * d.batch * d.hq * SS / 2);
-    HIPCHK(c, launch_softmax_bwd(dp32, p16, ds16, (int64_t)d.batch * d.hq * S, S, scale, c->cs));
-  }
-  {   // dQ = dS K
-    GemmArgs g;
-    g.A = ds16; g.sAm = S; g.sAk = 1; g.zA = {(int64_t)d.hq * SS, SS, 1};
-    g.B = qkv + d.qd; g.sBn = 1; g.sBk = d.qkvd; g.zB = {(int64_t)S * d.qkvd, d.hd, nrep};
-    g.C = dqkv32; g.sCm = d.qkvd; g.sCn = 1; g.zC = {(int64_t)S * d.qkvd, d.hd, 1}; g.c_f32 = 1;
-    g.M = S; g.N = d.hd; g.K = S; g.nz = d.batch * d.hq; g.zdiv = d.hq; g.causal = 2;
-    KTimer kt(c, LS_KC_ATTN, fl, 2.0 * d.batch * d.hq * SS / 2 + 2.0 * d.T * (d.kvd + d.qd));
-    HIPCHK(c, launch_gemm_generic(g, c->cs));
-  }
-  // dK = sum over the group's heads dS^T Q, dV = sum P^T dO (fixed head order)
-  for (int r = 0; r < nrep; ++r) {
-    GemmArgs g;
-    g.A = ds16 + (int64_t)r * SS; g.sAm = 1; g.sAk = S; g.zA = {(int64_t)d.hq * SS, (int64_t)nrep * SS, 1};
-    g.B = qkv + (int64_t)r * d.hd; g.sBn = 1; g.sBk = d.qkvd; g.zB = {(int64_t)S * d.qkvd, (int64_t)nrep * d.hd, 1};
-    g.C = dqkv32 + d.qd; g.sCm = d.qkvd; g.sCn = 1; g.zC = {(int64_t)S * d.qkvd, d.hd, 1}; g.c_f32 = 1;
-    g.M = S; g.N = d.hd; g.K = S; g.nz = d.batch * d.hkv; g.zdiv = d.hkv; g.causal = 3; g.beta = r ? 1.f : 0.f;
-    KTimer kt(c, LS_KC_ATTN, fl / d.hq * d.hkv, 2.0 * d.batch * d.hkv * SS / 2 + 2.0 * d.T * 2 * d.kvd);
-    HIPCHK(c, launch_gemm_generic(g, c->cs));
-    GemmArgs v = g;
-    v.A = p16 + (int64_t)r * SS;
-    v.B = dout + (int64_t)r * d.hd; v.sBk = d.qd; v.zB = {(int64_t)S * d.qd, (int64_t)nrep * d.hd, 1};
-    v.C = dqkv32 + d.qd + d.kvd;
-    KTimer kv(c, LS_KC_ATTN, fl / d.hq * d.hkv, 2.0 * d.batch * d.hkv * SS / 2 + 2.0 * d.T * 2 * d.kvd);
-    HIPCHK(c, launch_gemm_generic(v, c->cs));
-  }
+// Attention backward from dO (datt), O (att) and the log-sum-exp of the recompute ->
+// float32 dq, dk, dv in dqkv32 (dk, dv summed over a kv head's q heads, fixed order).
+ls_status attn_bwd(ls_ctx* c, const Dims& d, const uint16_t* qkv, const uint16_t* out, const uint16_t* dout,
+                   float* dqkv32) {
+  AttnArgs a = attn_args(c, d, qkv, const_cast<uint16_t*>(out));
+  a.dout = dout; a.lddo = d.qd;
+  a.dd = c->dp<float>(c->plan.dd);
+  a.dqkv = dqkv32; a.lddqkv = d.qkvd;
+  const double fl = 2.5 * 4.0 * d.batch * d.hq * (double)d.seq * (d.seq + 1) / 2 * d.hd;
+  KTimer kt(c, LS_KC_ATTN, fl, 2.0 * d.T * (d.qkvd + 2 * d.qd) + 4.0 * d.T * d.qkvd + 8.0 * d.T * d.hq);
+  HIPCHK(c, launch_attn_bwd(a, c->cs));
   return LS_OK;
 }
 
@@ -750,7 +697,7 @@ ls_status layer_backward(ls_ctx* c, int l, const uint8_t* blob, const Dims& d, c
     KTimer kt(c, LS_KC_GEMM_BWD, bwd_flop(d.h, d.qd), tb * d.h + wbytes(c, 3) + tb * d.qd);
     HIPCHK(c, launch_gemm_bwd(b, c->cs));
   }
-  if ((st = attn_bwd(c, d, qkv, datt, dqkv32))) return st;
+  if ((st = attn_bwd(c, d, qkv, att, datt, dqkv32))) return st;
   {
     KTimer kt(c, LS_KC_GLUE, 0.0, 3 * tb * d.qkvd);
     HIPCHK(c, launch_rope_bwd_convert(dqkv32, dqkv, d.qkvd, d.T, d.seq, d.hq + d.hkv, d.hd, c->dp<float2>(c->plan.rope), c->cs));
