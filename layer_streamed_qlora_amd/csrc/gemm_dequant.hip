@@ -372,14 +372,18 @@ struct AFast {
   }
 };
 
-// extension tile (rows x kx, kx <= 64, zero beyond) with 512 threads
-__device__ __forceinline__ void ext_tile(uint16_t* s, rsrc_t res, uint32_t col_off_bytes, int ld, int rows, int kx) {
+// extension tile with 512 threads: NQ * 64 rows; LDS columns [c_lo, c_lo + kx) take
+// source columns [0, kx) (kx <= 64), every other column of the 64 is zero
+template <int NQ = 4>
+__device__ __forceinline__ void ext_tile(uint16_t* s, rsrc_t res, uint32_t col_off_bytes, int ld, int rows, int kx,
+                                         int c_lo = 0) {
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
+  for (int q = 0; q < NQ; ++q) {
     const int c = threadIdx.x + NT_FAST * q;
     const int row = c >> 3, kc = (c & 7) * 8;
-    const bool ok = row < rows && kc < kx;
-    const uint4 v = bload16(res, ok ? col_off_bytes + ((uint32_t)row * (uint32_t)ld + (uint32_t)kc) * 2u : kOOB);
+    const int src = kc - c_lo;
+    const bool ok = row < rows && src >= 0 && src < kx;
+    const uint4 v = bload16(res, ok ? col_off_bytes + ((uint32_t)row * (uint32_t)ld + (uint32_t)src) * 2u : kOOB);
     *reinterpret_cast<uint4*>(s + row * PITCH + kc) = v;
   }
 }
@@ -395,10 +399,11 @@ struct WFwdFast {
   rsrc_t codes, absq, sc2;
   float mean;
   uint32_t voff_w, voff_b, blk0;
-  __device__ __forceinline__ void init(const WeightRef& w, int n0) {
+  // r: this thread's row within the tile of weight w starting at row n0; cap: tile rows
+  __device__ __forceinline__ void init(const WeightRef& w, int n0, uint32_t r, int cap) {
     const int K = w.n_in;
-    const int rows = w.n_out - n0 < BN ? w.n_out - n0 : BN;
-    const uint32_t r = threadIdx.x >> 1, h = threadIdx.x & 1;
+    const int rows = w.n_out - n0 < cap ? w.n_out - n0 : cap;
+    const uint32_t h = threadIdx.x & 1;
     const uint32_t kblk = (uint32_t)K / kNF4Block;
 #pragma unroll
     for (int i = 0; i < (FMT == WF_BF16 ? 4 : 1); ++i) raw[i] = make_uint4(0, 0, 0, 0);
@@ -598,7 +603,12 @@ struct Epi {
   void* out = nullptr; int ldo = 0; bool f32 = false;
   const uint16_t* r16 = nullptr; const float* r32 = nullptr; int ldr = 0;
   const float2* rope_tab = nullptr; int rope_cols = 0, col_base = 0, seq = 1, hd = 128;
+  // SwiGLU backward: the product is dact; with g, u from gu (float32 [M, ldgu], u at
+  // column + N_lim) write dgate, dup as bf16 into out ([M, ldo], dup at column + N_lim)
+  const float* gu = nullptr; int ldgu = 0;
 };
+
+__device__ __forceinline__ float sigmoid_f(float z) { return 1.0f / (1.0f + __expf(-z)); }
 
 template <int NT>
 __device__ __forceinline__ void epilogue(Smem& sm, f32x16_t (&acc)[4][Layout<NT>::JB], int m0, int n0, int M_lim,
@@ -631,6 +641,22 @@ __device__ __forceinline__ void epilogue(Smem& sm, f32x16_t (&acc)[4][Layout<NT>
       if (m >= M_lim || n >= N_lim) continue;
       const float4 v = *reinterpret_cast<const float4*>(&sm.u.out[r * OP + 4 * q]);
       float y[4] = {v.x, v.y, v.z, v.w};
+      if (E.gu) {   // N_lim % 4 == 0 here
+        const float4 g4 = *reinterpret_cast<const float4*>(E.gu + (int64_t)m * E.ldgu + n);
+        const float4 u4 = *reinterpret_cast<const float4*>(E.gu + (int64_t)m * E.ldgu + N_lim + n);
+        const float gs[4] = {g4.x, g4.y, g4.z, g4.w}, us[4] = {u4.x, u4.y, u4.z, u4.w};
+        float dg[4], du[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float sg = sigmoid_f(gs[e]);
+          dg[e] = y[e] * us[e] * sg * (1.0f + gs[e] * (1.0f - sg));
+          du[e] = y[e] * gs[e] * sg;
+        }
+        uint16_t* po = reinterpret_cast<uint16_t*>(E.out) + (int64_t)m * E.ldo + n;
+        *reinterpret_cast<uint2*>(po) = make_uint2(pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3]));
+        *reinterpret_cast<uint2*>(po + N_lim) = make_uint2(pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3]));
+        continue;
+      }
       const int gc = E.col_base + n;
       if (gc < E.rope_cols) {
         const int hh = E.hd / 2, i0 = gc % E.hd;
@@ -670,6 +696,53 @@ __device__ __forceinline__ void epilogue(Smem& sm, f32x16_t (&acc)[4][Layout<NT>
           const uint16_t h[4] = {(uint16_t)p0, (uint16_t)(p0 >> 16), (uint16_t)p1, (uint16_t)(p1 >> 16)};
           for (int e = 0; e < 4 && n + e < N_lim; ++e) po[e] = h[e];
         }
+      }
+    }
+  }
+}
+
+// SwiGLU forward epilogue of a paired tile: columns 0..127 are gate, 128..255 up, for
+// outputs j0 .. j0 + 127.  act = bf16(silu(g) u); with gu set, g and u are also kept in
+// float32 (gu [M, ldgu], up at column + I).
+template <int NT>
+__device__ __forceinline__ void epilogue_swiglu(Smem& sm, f32x16_t (&acc)[4][Layout<NT>::JB], int m0, int j0, int M_lim,
+                                                int I, uint16_t* act, int ldact, float* gu, int ldgu) {
+  constexpr int WNW = Layout<NT>::WNW, JB = Layout<NT>::JB;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave / WNW, wn = wave % WNW;
+  constexpr int OP = BN + 4;
+  for (int half = 0; half < 2; ++half) {
+    __syncthreads();
+    if (wm == half) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < JB; ++j)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int r = i * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
+            const int c = wn * (32 * JB) + j * 32 + (lane & 31);
+            sm.u.out[r * OP + c] = acc[i][j][v];
+          }
+    }
+    __syncthreads();
+    const int mbase = m0 + half * 128;
+#pragma unroll 4
+    for (int it = 0; it < 4096 / NT; ++it) {
+      const int idx = threadIdx.x + NT * it;           // 128 rows x 32 quads
+      const int r = idx >> 5, q = idx & 31;
+      const int m = mbase + r, j = j0 + 4 * q;
+      if (m >= M_lim || j >= I) continue;              // I % 4 == 0
+      const float4 g4 = *reinterpret_cast<const float4*>(&sm.u.out[r * OP + 4 * q]);
+      const float4 u4 = *reinterpret_cast<const float4*>(&sm.u.out[r * OP + 128 + 4 * q]);
+      const float gs[4] = {g4.x, g4.y, g4.z, g4.w}, us[4] = {u4.x, u4.y, u4.z, u4.w};
+      float a[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) a[e] = gs[e] * sigmoid_f(gs[e]) * us[e];
+      *reinterpret_cast<uint2*>(act + (int64_t)m * ldact + j) = make_uint2(pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]));
+      if (gu) {
+        *reinterpret_cast<float4*>(gu + (int64_t)m * ldgu + j) = g4;
+        *reinterpret_cast<float4*>(gu + (int64_t)m * ldgu + I + j) = u4;
       }
     }
   }
@@ -852,6 +925,7 @@ __global__ void __launch_bounds__(NTHREADS, 1) k_gemm_bwd(BwdArgs args, int n_ti
   E.f32 = args.out32 != nullptr;
   E.out = E.f32 ? (void*)args.out32 : (void*)args.out16;
   E.ldo = args.ldo;
+  E.gu = args.gu32; E.ldgu = args.ldgu;
   epilogue<NTHREADS>(sm, acc, m0, j0, args.M, args.N, E);
 }
 
@@ -859,7 +933,11 @@ __global__ void __launch_bounds__(NTHREADS, 1) k_gemm_bwd(BwdArgs args, int n_ti
 // 8 waves (2 per SIMD: while one waits on LDS or memory the other issues), each
 // 128 x 64 of the tile.  Used when K % 64 == 0 (forward) or every stacked segment's
 // rows % 64 == 0 (backward), so no tile straddles the end of a row.
-template <int FMT>
+// PAIRED (SwiGLU): groups 0 and 1 are gate and up with the same shape; a tile holds
+// gate rows 128 t.. (waves 0-3 load them) and the same up rows (waves 4-7), and its
+// epilogue writes silu(gate) * up.  The low-rank terms become one 2 kx wide extension:
+// [H_gate | H_up] against [B_gate | 0] for the gate half and [0 | B_up] for the up half.
+template <int FMT, bool PAIRED>
 __global__ void __launch_bounds__(NT_FAST, 1) k_gemm_fwd_fast(FwdArgs args, int n_tiles, int total_tiles, int padded) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   Smem& sm = *reinterpret_cast<Smem*>(smem_raw);
@@ -868,13 +946,16 @@ __global__ void __launch_bounds__(NT_FAST, 1) k_gemm_fwd_fast(FwdArgs args, int 
   const int mt = tile / n_tiles;
   int rest = tile - mt * n_tiles;
   int g = 0;
-  for (; g < args.n_groups - 1; ++g) {
-    const int nt_g = (args.g[g].w.n_out + BN - 1) / BN;
-    if (rest < nt_g) break;
-    rest -= nt_g;
+  if constexpr (!PAIRED) {
+    for (; g < args.n_groups - 1; ++g) {
+      const int nt_g = (args.g[g].w.n_out + BN - 1) / BN;
+      if (rest < nt_g) break;
+      rest -= nt_g;
+    }
   }
   const FwdGroup& G = args.g[g];
-  const int m0 = mt * BM, n0 = rest * BN;
+  const int m0 = mt * BM;
+  const int n0 = PAIRED ? rest * (BN / 2) : rest * BN;
   const int K = args.K;
   const int n_out = G.w.n_out;
 
@@ -891,8 +972,22 @@ __global__ void __launch_bounds__(NT_FAST, 1) k_gemm_fwd_fast(FwdArgs args, int 
   const int arows = rows_left < BM ? rows_left : BM;
   const rsrc_t xres = make_rsrc(args.x + (int64_t)m0 * args.ldx, (uint64_t)arows * args.ldx * 2);
   const int nk = K / BK;
-  const int n_iter = nk + 1;   // iteration 0: the low-rank term (kx <= 64)
-  {
+  const int n_iter = nk + 1;   // iteration 0: the low-rank term
+  if constexpr (PAIRED) {
+    const int kx = args.kx;
+    const bool has_ext = kx > 0;
+    const rsrc_t ares = make_rsrc(has_ext ? args.aext + (int64_t)m0 * args.ldaext : args.x,
+                                  has_ext ? (uint64_t)arows * args.ldaext * 2 : 0);
+    ext_tile(sm.u.k.a[0], ares, (uint32_t)G.ext_col0 * 2u, args.ldaext, has_ext ? arows : 0, 2 * kx);
+    const int brows = n_out - n0 < BN / 2 ? n_out - n0 : BN / 2;
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      const uint16_t* bx = args.g[hf].bext;
+      const bool on = has_ext && bx != nullptr;
+      const rsrc_t bres = make_rsrc(on ? bx + (int64_t)n0 * kx : args.x, on ? (uint64_t)brows * kx * 2 : 0);
+      ext_tile<2>(sm.u.k.w[0] + hf * (BN / 2) * PITCH, bres, 0, kx, on ? brows : 0, kx, hf * kx);
+    }
+  } else {
     const bool has_ext = args.kx > 0 && G.bext != nullptr;
     const int brows = n_out - n0 < BN ? n_out - n0 : BN;
     const rsrc_t ares = make_rsrc(has_ext ? args.aext + (int64_t)m0 * args.ldaext : args.x,
@@ -907,8 +1002,13 @@ __global__ void __launch_bounds__(NT_FAST, 1) k_gemm_fwd_fast(FwdArgs args, int 
   AFast ra;
   ra.init(xres, args.ldx);
   WFwdFast<FMT> rw, rw_next;
-  rw.init(G.w, n0);
-  rw_next.init(G.w, n0);
+  {
+    const WeightRef& wsel = PAIRED ? args.g[threadIdx.x >> 8].w : G.w;   // wave-uniform
+    const uint32_t r = PAIRED ? (threadIdx.x >> 1) & 127u : threadIdx.x >> 1;
+    const int cap = PAIRED ? BN / 2 : BN;
+    rw.init(wsel, n0, r, cap);
+    rw_next.init(wsel, n0, r, cap);
+  }
 #pragma unroll
   for (int q = 0; q < 4; ++q) ra.load_q(0, q);
   rw.load(0);
@@ -931,16 +1031,20 @@ __global__ void __launch_bounds__(NT_FAST, 1) k_gemm_fwd_fast(FwdArgs args, int 
     __syncthreads();
   }
 
-  Epi E;
-  E.f32 = args.y32 != nullptr;
-  E.out = E.f32 ? (void*)(args.y32 + G.out_col0) : (void*)(args.y + G.out_col0);
-  E.ldo = args.ldy;
-  E.r16 = args.resid ? args.resid + G.out_col0 : nullptr;
-  E.r32 = args.resid32 ? args.resid32 + G.out_col0 : nullptr;
-  E.ldr = args.ldr;
-  E.rope_tab = args.rope_tab; E.rope_cols = args.rope_tab ? args.rope_cols : 0;
-  E.col_base = G.out_col0; E.seq = args.seq; E.hd = args.head_dim;
-  epilogue<NT_FAST>(sm, acc, m0, n0, args.M, n_out, E);
+  if constexpr (PAIRED) {
+    epilogue_swiglu<NT_FAST>(sm, acc, m0, n0, args.M, n_out, args.y, args.ldy, args.gu32, args.ldgu);
+  } else {
+    Epi E;
+    E.f32 = args.y32 != nullptr;
+    E.out = E.f32 ? (void*)(args.y32 + G.out_col0) : (void*)(args.y + G.out_col0);
+    E.ldo = args.ldy;
+    E.r16 = args.resid ? args.resid + G.out_col0 : nullptr;
+    E.r32 = args.resid32 ? args.resid32 + G.out_col0 : nullptr;
+    E.ldr = args.ldr;
+    E.rope_tab = args.rope_tab; E.rope_cols = args.rope_tab ? args.rope_cols : 0;
+    E.col_base = G.out_col0; E.seq = args.seq; E.hd = args.head_dim;
+    epilogue<NT_FAST>(sm, acc, m0, n0, args.M, n_out, E);
+  }
 }
 
 template <int FMT>
@@ -1030,6 +1134,7 @@ __global__ void __launch_bounds__(NT_FAST, 1) k_gemm_bwd_fast(BwdArgs args, int 
   E.f32 = args.out32 != nullptr;
   E.out = E.f32 ? (void*)args.out32 : (void*)args.out16;
   E.ldo = args.ldo;
+  E.gu = args.gu32; E.ldgu = args.ldgu;
   epilogue<NT_FAST>(sm, acc, m0, j0, args.M, args.N, E);
 }
 
@@ -1072,9 +1177,24 @@ hipError_t launch_gemm_fwd(const FwdArgs& a, hipStream_t s) {
   const int total = m_tiles * n_tiles;
   const int padded = (total + 7) / 8 * 8;
   const bool fast = (a.K % BK) == 0 && (a.ldx % 8) == 0;
+  if (a.swiglu) {
+    // paired gate | up tiles: same shape, adjacent low-rank columns, 2 kx <= 64
+    if (!fast || a.n_groups != 2 || a.g[0].w.n_out != a.g[1].w.n_out || a.g[0].w.n_in != a.g[1].w.n_in ||
+        a.g[0].w.n_out % 4 != 0 || 2 * a.kx > BK || (a.kx > 0 && a.g[1].ext_col0 != a.g[0].ext_col0 + a.kx) ||
+        !a.y || a.y32 || a.resid || a.resid32 || a.rope_tab || a.ldy % 4 != 0 || (a.gu32 && a.ldgu % 4 != 0))
+      return hipErrorInvalidValue;
+    const int pt = (a.g[0].w.n_out + BN / 2 - 1) / (BN / 2);
+    const int ptotal = m_tiles * pt;
+    const int ppadded = (ptotal + 7) / 8 * 8;
+    return launch_fmt(a.format, [&](auto fmt) {
+      constexpr int F = decltype(fmt)::value;
+      hipLaunchKernelGGL((k_gemm_fwd_fast<F, true>), dim3(ppadded), dim3(NT_FAST), sizeof(Smem), s, a, pt, ptotal, ppadded);
+      return hipGetLastError();
+    });
+  }
   return launch_fmt(a.format, [&](auto fmt) {
     constexpr int F = decltype(fmt)::value;
-    if (fast) hipLaunchKernelGGL(k_gemm_fwd_fast<F>, dim3(padded), dim3(NT_FAST), sizeof(Smem), s, a, n_tiles, total, padded);
+    if (fast) hipLaunchKernelGGL((k_gemm_fwd_fast<F, false>), dim3(padded), dim3(NT_FAST), sizeof(Smem), s, a, n_tiles, total, padded);
     else hipLaunchKernelGGL((k_gemm_fwd<F, false>), dim3(padded), dim3(NTHREADS), sizeof(Smem), s, a, n_tiles, total, padded);
     return hipGetLastError();
   });
@@ -1094,6 +1214,8 @@ hipError_t launch_gemm_bwd(const BwdArgs& a, hipStream_t s) {
   // low-rank terms (stacked q|k|v or gate|up at rank > 16) add the remaining columns
   // into the float32 result with a second, generic MFMA GEMM.
   if (a.kx > BK && !a.out32) return hipErrorInvalidValue;
+  if (a.gu32 && (!a.out16 || a.out32 || a.N % 4 != 0 || a.ldo % 4 != 0 || a.ldgu % 4 != 0 || a.kx > BK))
+    return hipErrorInvalidValue;
   BwdArgs k = a;
   if (k.kx > BK) k.kx = BK;
   hipError_t e = launch_fmt(a.format, [&](auto fmt) {
@@ -1136,9 +1258,12 @@ hipError_t gemm_dequant_init() {
   set((const void*)k_gemm_bwd<WF_NF4, false>);
   set((const void*)k_gemm_bwd<WF_NF4_DQ, false>);
   set((const void*)k_gemm_bwd<WF_BF16, false>);
-  set((const void*)k_gemm_fwd_fast<WF_NF4>);
-  set((const void*)k_gemm_fwd_fast<WF_NF4_DQ>);
-  set((const void*)k_gemm_fwd_fast<WF_BF16>);
+  set((const void*)k_gemm_fwd_fast<WF_NF4, false>);
+  set((const void*)k_gemm_fwd_fast<WF_NF4, true>);
+  set((const void*)k_gemm_fwd_fast<WF_NF4_DQ, false>);
+  set((const void*)k_gemm_fwd_fast<WF_NF4_DQ, true>);
+  set((const void*)k_gemm_fwd_fast<WF_BF16, false>);
+  set((const void*)k_gemm_fwd_fast<WF_BF16, true>);
   set((const void*)k_gemm_bwd_fast<WF_NF4>);
   set((const void*)k_gemm_bwd_fast<WF_NF4_DQ>);
   set((const void*)k_gemm_bwd_fast<WF_BF16>);

@@ -140,18 +140,6 @@ __global__ void k_swiglu_fwd(const float* gu, int I, uint16_t* act, int64_t n) {
   act[t * I + j] = tobf(g * sigmoidf(g) * u);
 }
 
-__global__ void k_swiglu_bwd(const float* gu, const float* dact, int I, uint16_t* dgu, int64_t n) {
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= n) return;
-  const int64_t t = idx / I;
-  const int j = (int)(idx % I);
-  const float g = gu[t * 2 * I + j], u = gu[t * 2 * I + I + j];
-  const float da = dact[t * I + j];
-  const float sg = sigmoidf(g);
-  dgu[t * 2 * I + j] = tobf(da * u * sg * (1.0f + g * (1.0f - sg)));
-  dgu[t * 2 * I + I + j] = tobf(da * g * sg);
-}
-
 // dst[r, c] = scale * src[r, c] (transpose: dst[c, r]) for c < cols, 0 for cols <= c < pad_cols
 __global__ void k_f32_to_bf16(const float* src, int64_t lds, uint16_t* dst, int64_t ldd, int rows, int cols,
                               int pad_cols, float scale, int transpose) {
@@ -225,13 +213,6 @@ hipError_t launch_swiglu_fwd(const float* gu, int32_t I, uint16_t* act, int32_t 
   const int64_t n = (int64_t)T * I;
   if (n <= 0) return hipSuccess;
   hipLaunchKernelGGL(k_swiglu_fwd, dim3(blocks_for(n, 256)), dim3(256), 0, s, gu, I, act, n);
-  return hipGetLastError();
-}
-
-hipError_t launch_swiglu_bwd(const float* gu, const float* dact, int32_t I, uint16_t* dgu, int32_t T, hipStream_t s) {
-  const int64_t n = (int64_t)T * I;
-  if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_swiglu_bwd, dim3(blocks_for(n, 256)), dim3(256), 0, s, gu, dact, I, dgu, n);
   return hipGetLastError();
 }
 

@@ -84,6 +84,11 @@ struct FwdArgs {
   const float2* rope_tab = nullptr; int32_t rope_cols = 0, seq = 1, head_dim = 128;
   const float* levels = nullptr;                    // device float32[16] NF4 levels
   int32_t format = WF_NF4;
+  // SwiGLU: groups 0, 1 = gate, up (same shape, K % 64 == 0, up's low-rank columns
+  // right after gate's, 2 kx <= 64); y (bf16, [M, ldy]) = silu(gate) * up, and, if gu32
+  // is set, gate and up in float32 ([M, ldgu], up at column + n_out)
+  int32_t swiglu = 0;
+  float* gu32 = nullptr; int32_t ldgu = 0;
 };
 hipError_t launch_gemm_fwd(const FwdArgs& a, hipStream_t s);
 
@@ -103,6 +108,9 @@ struct BwdArgs {
   float* out32 = nullptr; uint16_t* out16 = nullptr; int32_t ldo = 0;  // exactly one set
   const float* levels = nullptr;
   int32_t format = WF_NF4;
+  // SwiGLU backward: the product is d(act); with gate, up from gu32 (float32 [M, ldgu],
+  // up at column + N) out16 receives dgate | dup (bf16 [M, ldo], dup at column + N)
+  const float* gu32 = nullptr; int32_t ldgu = 0;
 };
 hipError_t launch_gemm_bwd(const BwdArgs& a, hipStream_t s);
 
@@ -174,8 +182,6 @@ hipError_t launch_fill_f32(float* p, int64_t n, float v, hipStream_t s);
 hipError_t gemm_dequant_init();
 // gu float32 [T, 2I] (gate | up) -> act bf16 [T, I]
 hipError_t launch_swiglu_fwd(const float* gu, int32_t I, uint16_t* act, int32_t T, hipStream_t s);
-// gu float32, dact float32 [T, I] -> dgu bf16 [T, 2I]
-hipError_t launch_swiglu_bwd(const float* gu, const float* dact, int32_t I, uint16_t* dgu, int32_t T, hipStream_t s);
 // float32 [rows, cols] (row stride lds) -> bf16 [rows, ldd] scaled, columns >= cols zero up to ldd
 hipError_t launch_f32_to_bf16(const float* src, int64_t lds, uint16_t* dst, int64_t ldd, int32_t rows,
                               int32_t cols, int32_t pad_cols, float scale, int32_t transpose, hipStream_t s);

@@ -54,7 +54,7 @@ struct DevPlan {
   uint64_t slots = 0, ck = 0, xref = 0;
   uint64_t n1 = 0, qkv = 0, att = 0, hb = 0, n2 = 0, gu = 0, act = 0, rstd1 = 0, rstd2 = 0;
   uint64_t hs = 0, gs = 0, lse = 0, dd = 0;
-  uint64_t dya = 0, dyb = 0, dh32 = 0, dh16 = 0, da32 = 0, dgu = 0, datt = 0, dqkv = 0, dqkv32 = 0, dn32 = 0;
+  uint64_t dya = 0, dyb = 0, dh32 = 0, dh16 = 0, dgu = 0, datt = 0, dqkv = 0, dqkv32 = 0, dn32 = 0;
   uint64_t lora = 0, lora_per_layer = 0, partial = 0, partial_bytes = 0;
   uint64_t levels = 0, rope = 0;
   // per-layer LoRA operand offsets (relative to the layer's LoRA base)
@@ -94,7 +94,6 @@ DevPlan make_plan(const ls_config& c, const BlobLayout& L) {
   P.dyb = take(2 * T * h);
   P.dh32 = take(4 * T * h);
   P.dh16 = take(2 * T * h);
-  P.da32 = take(4 * T * I);
   P.dgu = take(2 * T * 2 * I);
   P.datt = take(2 * T * qd);
   P.dqkv = take(2 * T * qkvd);
@@ -538,6 +537,7 @@ ls_status layer_forward(ls_ctx* c, int l, const uint8_t* blob, const Dims& d, co
     HIPCHK(c, launch_rmsnorm_fwd(nullptr, hb, g2, n2, c->dp<float>(c->plan.rstd2), d.T, d.h, g.rms_eps, c->cs));
   }
   if (lora) { ls_status st = lora_down(c, l, d, n2, d.h, LS_PROJ_GATE, 2, d.h); if (st) return st; }
+  const bool fuse_swiglu = 2 * d.r16 <= 64;
   {
     FwdArgs f;
     f.x = n2; f.ldx = d.h; f.M = d.T; f.K = d.h; f.n_groups = 2;
@@ -549,11 +549,20 @@ ls_status layer_forward(ls_ctx* c, int l, const uint8_t* blob, const Dims& d, co
       f.g[i].bext = lora && lora_active(c, l, p) ? lora_at(c, l, c->plan.bx16[p]) : nullptr;
     }
     f.aext = hs; f.ldaext = d.R7; f.kx = lora ? d.r16 : 0;
-    f.y32 = gu; f.ldy = 2 * d.I; f.levels = lv; f.format = fmt;
-    KTimer kt(c, LS_KC_GEMM_FWD, fwd_gemm_flop(d, 2 * d.I, d.h, lora), tb * d.h + wbytes(c, 4) + wbytes(c, 5) + 2 * tb * 2 * d.I);
+    f.levels = lv; f.format = fmt;
+    // SwiGLU in the GEMM's epilogue (paired gate / up tiles) when both low-rank terms
+    // fit one 64-column extension; the recompute also keeps gate and up in float32
+    if (fuse_swiglu) {
+      f.swiglu = 1; f.y = act; f.ldy = d.I;
+      f.gu32 = mode == MODE_RECOMPUTE ? gu : nullptr; f.ldgu = 2 * d.I;
+    } else {
+      f.y32 = gu; f.ldy = 2 * d.I;
+    }
+    const double out_bytes = fuse_swiglu ? tb * d.I + (mode == MODE_RECOMPUTE ? 2 * tb * 2 * d.I : 0.0) : 2 * tb * 2 * d.I;
+    KTimer kt(c, LS_KC_GEMM_FWD, fwd_gemm_flop(d, 2 * d.I, d.h, lora), tb * d.h + wbytes(c, 4) + wbytes(c, 5) + out_bytes);
     HIPCHK(c, launch_gemm_fwd(f, c->cs));
   }
-  {
+  if (!fuse_swiglu) {
     KTimer kt(c, LS_KC_GLUE, 0.0, 5 * tb * d.I);
     HIPCHK(c, launch_swiglu_fwd(gu, d.I, act, d.T, c->cs));
   }
@@ -635,7 +644,6 @@ ls_status layer_backward(ls_ctx* c, int l, const uint8_t* blob, const Dims& d, c
   uint16_t* gs = c->dp<uint16_t>(c->plan.gs);
   float* dh32 = c->dp<float>(c->plan.dh32);
   uint16_t* dh16 = c->dp<uint16_t>(c->plan.dh16);
-  float* da32 = c->dp<float>(c->plan.da32);
   float* dqkv32 = c->dp<float>(c->plan.dqkv32);
   uint16_t* dgu = c->dp<uint16_t>(c->plan.dgu);
   uint16_t* datt = c->dp<uint16_t>(c->plan.datt);
@@ -655,13 +663,10 @@ ls_status layer_backward(ls_ctx* c, int l, const uint8_t* blob, const Dims& d, c
     b.seg[0].w = wref(c, blob, LS_PROJ_DOWN); b.seg[0].a_col0 = 0;
     b.aext = gs + LS_PROJ_DOWN * d.r16; b.ldaext = d.R7; b.kx = d.r16;
     b.bext = lora_at(c, l, c->plan.at_d); b.ldbext = d.r16;
-    b.out32 = da32; b.ldo = d.I; b.levels = lv; b.format = fmt;
-    KTimer kt(c, LS_KC_GEMM_BWD, bwd_flop(d.h, d.I), tb * d.h + wbytes(c, 6) + 2 * tb * d.I);
+    // SwiGLU backward in the epilogue: dgate | dup from d(act) and the recomputed gate, up
+    b.out16 = dgu; b.ldo = 2 * d.I; b.gu32 = gu; b.ldgu = 2 * d.I; b.levels = lv; b.format = fmt;
+    KTimer kt(c, LS_KC_GEMM_BWD, bwd_flop(d.h, d.I), tb * d.h + wbytes(c, 6) + 2 * tb * 2 * d.I + tb * 2 * d.I);
     HIPCHK(c, launch_gemm_bwd(b, c->cs));
-  }
-  {
-    KTimer kt(c, LS_KC_GLUE, 0.0, 8 * tb * d.I);
-    HIPCHK(c, launch_swiglu_bwd(gu, da32, d.I, dgu, d.T, c->cs));
   }
   // ---- gate / up
   for (int i = 0; i < 2; ++i) {
