@@ -12,117 +12,25 @@
 // bf16 operands (P and dS are rounded to bf16 as MFMA operands) and accumulates in
 // float32 on v_mfma_f32_32x32x16_bf16.
 //
-// MFMA operand layouts (lane = 0..63, 32 x 32 x 16): A[i][k] sits in lane
-// i + 32 (k / 8), element k % 8; B[k][j] in lane j + 32 (k / 8); the result C[i][j] in
-// lane j + 32 ((i / 4) % 2), register (i / 8) * 4 + i % 4.  A score tile computed as
-// C therefore leaves, in each lane, 16 rows for one column.  When that tile is reused
-// as an operand of a second product whose contraction runs over those rows, the
-// contraction index is taken in the permuted order the lane already holds (any
-// order sums to the same result); the other operand is read from LDS in that same
-// order.  Tiles read along the contraction in the transposed direction are kept
-// transposed in LDS ([d][row], built with byte permutes from row pairs).
+// Products over d keep one operand in registers as row fragments; products whose
+// contraction runs over a tile's rows reuse score tiles in the lanes' own row order
+// and read the other operand from a transposed LDS tile (tiles.hpp).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include <cmath>
 
 #include "lsq_internal.hpp"
+#include "tiles.hpp"
 
 namespace lsq {
 namespace {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
+using namespace tiles;
 
-constexpr int KB = 64;                  // rows (keys or queries) per streamed tile
-constexpr int PT = KB + 4;              // pitch of a transposed tile [d][row], elements
+constexpr int KB = kTileRows;   // rows (keys or queries) per streamed tile
+constexpr int PT = kTPitch;
 constexpr float kLog2e = 1.4426950408889634f;
-
-__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
-  f32x2_t v = {lo, hi};
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));   // RNE
-}
-__device__ __forceinline__ float bf_lo(uint32_t u) { return __builtin_bit_cast(float, u << 16); }
-__device__ __forceinline__ float bf_hi(uint32_t u) { return __builtin_bit_cast(float, u & 0xFFFF0000u); }
-
-__device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint64_t bytes) {
-  const uint32_t n = bytes > 0xFFFFFFF0ull ? 0xFFFFFFF0u : (uint32_t)bytes;
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)n, 0x00020000);
-}
-// 16 bytes at a range-checked per-lane offset (past the end: zeros)
-__device__ __forceinline__ uint4 bload16(rsrc_t r, uint32_t off) {
-  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
-  return make_uint4(v.x, v.y, v.z, v.w);
-}
-__device__ __forceinline__ bf16x8_t as_bf8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
-__device__ __forceinline__ f32x16_t mfma(bf16x8_t a, bf16x8_t b, f32x16_t c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-// eight consecutive accumulator values (one k16 step of a reused score tile) as bf16
-__device__ __forceinline__ bf16x8_t pack8(const f32x16_t& x, int base) {
-  return as_bf8(make_uint4(pack2(x[base], x[base + 1]), pack2(x[base + 2], x[base + 3]),
-                           pack2(x[base + 4], x[base + 5]), pack2(x[base + 6], x[base + 7])));
-}
-// Operand fragment from a transposed LDS tile t[d][row]: lane (i + 32 hh) takes rows
-// r0 + 4 hh + {0..3} and r0 + 8 + 4 hh + {0..3} of line d = d0 + i, matching the row
-// order of pack8 over a C tile's registers 8 s .. 8 s + 7 (r0 = 16 s within the block).
-__device__ __forceinline__ bf16x8_t tfrag(const uint16_t* t, int d, int r0, int hh) {
-  const uint16_t* src = t + d * PT + r0 + 4 * hh;
-  const uint2 lo = *reinterpret_cast<const uint2*>(src);
-  const uint2 hi = *reinterpret_cast<const uint2*>(src + 8);
-  return as_bf8(make_uint4(lo.x, lo.y, hi.x, hi.y));
-}
-
-// One 64-row tile of a head (rows row0.., hd columns) moved global -> LDS, optionally
-// row-major (pitch hd + 8) and/or transposed (pitch PT).  Unit u covers rows 2p, 2p+1
-// (p = u % 32) and 8 columns 8c (c = u / 32); NT threads.
-template <int HD, int NT>
-struct TileMover {
-  static constexpr int NU = 32 * (HD / 8) / NT;     // units per thread
-  uint4 v[NU][2];
-  __device__ __forceinline__ void load(rsrc_t res, int ld, int row0) {
-#pragma unroll
-    for (int i = 0; i < NU; ++i) {
-      const int u = threadIdx.x + NT * i, p = u & 31, c = u >> 5;
-#pragma unroll
-      for (int r = 0; r < 2; ++r)
-        v[i][r] = bload16(res, ((uint32_t)(row0 + 2 * p + r) * (uint32_t)ld + 8u * c) * 2u);
-    }
-  }
-  __device__ __forceinline__ void store_rows(uint16_t* s) const {
-#pragma unroll
-    for (int i = 0; i < NU; ++i) {
-      const int u = threadIdx.x + NT * i, p = u & 31, c = u >> 5;
-#pragma unroll
-      for (int r = 0; r < 2; ++r) *reinterpret_cast<uint4*>(s + (2 * p + r) * (HD + 8) + 8 * c) = v[i][r];
-    }
-  }
-  __device__ __forceinline__ void store_t(uint16_t* t) const {
-#pragma unroll
-    for (int i = 0; i < NU; ++i) {
-      const int u = threadIdx.x + NT * i, p = u & 31, c = u >> 5;
-      const uint32_t* r0 = reinterpret_cast<const uint32_t*>(&v[i][0]);
-      const uint32_t* r1 = reinterpret_cast<const uint32_t*>(&v[i][1]);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {   // dword j = columns 8c + 2j, 8c + 2j + 1
-        *reinterpret_cast<uint32_t*>(t + (8 * c + 2 * j) * PT + 2 * p) = __builtin_amdgcn_perm(r1[j], r0[j], 0x05040100u);
-        *reinterpret_cast<uint32_t*>(t + (8 * c + 2 * j + 1) * PT + 2 * p) = __builtin_amdgcn_perm(r1[j], r0[j], 0x07060302u);
-      }
-    }
-  }
-};
-
-// Row fragments of a head kept in registers as the B operand of a product over d:
-// step s holds columns 16 s + 8 hh .. + 7 of row `row` (zeros past the end).
-template <int HD>
-__device__ __forceinline__ void row_frags(bf16x8_t (&f)[HD / 16], rsrc_t res, int ld, int row, int hh) {
-#pragma unroll
-  for (int s = 0; s < HD / 16; ++s) f[s] = as_bf8(bload16(res, ((uint32_t)row * (uint32_t)ld + 16u * s + 8u * hh) * 2u));
-}
 
 // ------------------------------------------------------------------ forward
 // Workgroup: 128 queries of one (batch, q head), 4 waves x 32 queries.  Per 64-key

@@ -1,0 +1,162 @@
+// LoRA adapter gradients over the tokens of a step, gfx950.
+//
+// For a projection y = x W^T + s (x A^T) B^T the adapter gradients are dB = dY^T (s H)
+// and dA = (s G)^T X with H = x A^T and G = dY B ("Fine-Tuning an 8B Parameter Model on
+// a 4 GB Laptop GPU", section "LoRA and QLoRA: Train a Fraction of the Parameters":
+// only A and B are trained).  Each is a contraction over the T tokens of two
+// token-major bf16 matrices: C[m][n] = sum_t A[t][m] B[t][n], with m a feature of the
+// activation (up to 29568 of them) and n one of the r adapter columns.
+//
+// One launch computes several such products (one decoder stage's dA and dB).  A
+// workgroup owns 128 features x 64 adapter columns and a run of tokens; 64-token tiles
+// of both operands go to LDS transposed ([column][token], built with byte permutes from
+// token pairs) and feed v_mfma_f32_32x32x16_bf16 with the contraction over tokens.  The
+// token runs of one output tile write float32 partials that a second kernel adds in
+// run order, so results do not depend on scheduling.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "lsq_internal.hpp"
+#include "tiles.hpp"
+
+namespace lsq {
+namespace {
+
+using namespace tiles;
+
+constexpr int TM = 128, TN = 64, TT = kTileRows;
+constexpr int NT = 256;
+
+struct TcKArgs {
+  TcArgs a;
+  int32_t tile0[kMaxTcJobs + 1];
+  int32_t n_tiles[kMaxTcJobs];
+  int32_t ksplit = 1, chunk = 0;
+};
+
+// Result element of thread threadIdx.x, block jb, register v of a C tile at (m0, n0):
+// C[i = feature][j = column] sits in lane j + 32 hh, register v holding feature
+// 32 w + (v / 4) * 8 + 4 hh + v % 4.
+__device__ __forceinline__ void tc_put(const TcArgs& a, int job, int m0, int n0, int jb, int v, float val) {
+  const TcJob& J = a.job[job];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int m = m0 + 32 * w + (v >> 2) * 8 + 4 * (lane >> 5) + (v & 3);
+  const int n = n0 + 32 * jb + (lane & 31);
+  if (m >= J.M || n >= J.N) return;
+  const int d = n / J.ncols, nl = n - d * J.ncols;
+  if (nl >= J.nvalid || J.C[d] == nullptr) return;
+  float* c = J.C[d] + (int64_t)m * J.scm + (int64_t)nl * J.scn;
+  *c = a.beta != 0.f ? val + a.beta * *c : val;
+}
+
+__global__ void __launch_bounds__(NT) k_lora_tc(TcKArgs k) {
+  __shared__ __align__(16) uint16_t sA[TM * kTPitch];
+  __shared__ __align__(16) uint16_t sB[TN * kTPitch];
+  const TcArgs& a = k.a;
+  const int flat = (int)blockIdx.x / k.ksplit, split = (int)blockIdx.x - flat * k.ksplit;
+  int j = 0;
+  while (j + 1 < a.n_jobs && flat >= k.tile0[j + 1]) ++j;
+  const TcJob& J = a.job[j];
+  const int local = flat - k.tile0[j];
+  const int mt = local / k.n_tiles[j], nt = local - mt * k.n_tiles[j];
+  const int m0 = mt * TM, n0 = nt * TN;
+  const int t0 = split * k.chunk, t1 = min(a.T, t0 + k.chunk);
+  // buffers based at (token t0, column m0 / n0): tokens past T read as zero
+  const uint64_t rows = (uint64_t)(a.T - t0);
+  const rsrc_t ra = make_rsrc(J.A + (int64_t)t0 * J.lda + m0, (rows * J.lda - m0) * 2);
+  const rsrc_t rb = make_rsrc(J.B + (int64_t)t0 * J.ldb + n0, (rows * J.ldb - n0) * 2);
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, l32 = lane & 31, hh = lane >> 5;
+  const bool two = n0 + 32 < J.N;            // second 32-column block in use
+  f32x16_t acc[2] = {f32x16_t{}, f32x16_t{}};
+  TileMover<TM, NT> ta;
+  TileMover<TN, NT> tb;
+  const int nst = t1 > t0 ? (t1 - t0 + TT - 1) / TT : 0;
+  if (nst > 0) {
+    ta.load(ra, J.lda, 0);
+    tb.load(rb, J.ldb, 0);
+  }
+  for (int st = 0; st < nst; ++st) {
+    __syncthreads();                         // the previous tiles are no longer read
+    ta.store_t(sA);
+    tb.store_t(sB);
+    __syncthreads();
+    if (st + 1 < nst) {
+      ta.load(ra, J.lda, (st + 1) * TT);
+      tb.load(rb, J.ldb, (st + 1) * TT);
+    }
+#pragma unroll
+    for (int s = 0; s < TT / 16; ++s) {
+      const bf16x8_t af = tfrag(sA, 32 * w + l32, 16 * s, hh);
+      acc[0] = mfma(af, tfrag(sB, l32, 16 * s, hh), acc[0]);
+      if (two) acc[1] = mfma(af, tfrag(sB, 32 + l32, 16 * s, hh), acc[1]);
+    }
+  }
+  if (k.ksplit == 1) {
+#pragma unroll
+    for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) tc_put(a, j, m0, n0, jb, v, acc[jb][v]);
+    return;
+  }
+  float* part = a.partial + ((int64_t)flat * k.ksplit + split) * (TM * TN);
+#pragma unroll
+  for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) part[(jb * 16 + v) * NT + threadIdx.x] = acc[jb][v];
+}
+
+// Sum of the token runs of one output tile, in run order.
+__global__ void __launch_bounds__(NT) k_lora_tc_reduce(TcKArgs k) {
+  const TcArgs& a = k.a;
+  const int flat = blockIdx.x;
+  int j = 0;
+  while (j + 1 < a.n_jobs && flat >= k.tile0[j + 1]) ++j;
+  const int local = flat - k.tile0[j];
+  const int mt = local / k.n_tiles[j], nt = local - mt * k.n_tiles[j];
+  const float* base = a.partial + (int64_t)flat * k.ksplit * (TM * TN);
+#pragma unroll
+  for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      float sum = 0.f;
+      for (int sp = 0; sp < k.ksplit; ++sp) sum += base[(int64_t)sp * (TM * TN) + (jb * 16 + v) * NT + threadIdx.x];
+      tc_put(a, j, mt * TM, nt * TN, jb, v, sum);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_lora_tc(const TcArgs& a, hipStream_t s) {
+  if (a.T <= 0 || a.n_jobs <= 0) return hipSuccess;
+  if (a.n_jobs > kMaxTcJobs) return hipErrorInvalidValue;
+  TcKArgs k;
+  k.a = a;
+  int tiles = 0;
+  int64_t max_ld = 1;
+  for (int j = 0; j < a.n_jobs; ++j) {
+    const TcJob& J = a.job[j];
+    if (!J.A || !J.B || J.M <= 0 || J.N <= 0 || J.ncols <= 0 || J.N > 3 * J.ncols || J.lda % 8 || J.ldb % 8 ||
+        J.lda < J.M || J.ldb < J.N || (reinterpret_cast<uintptr_t>(J.A) & 15) || (reinterpret_cast<uintptr_t>(J.B) & 15))
+      return hipErrorInvalidValue;
+    k.tile0[j] = tiles;
+    k.n_tiles[j] = (J.N + TN - 1) / TN;
+    tiles += (J.M + TM - 1) / TM * k.n_tiles[j];
+    max_ld = std::max<int64_t>(max_ld, std::max(J.lda, J.ldb));
+  }
+  k.tile0[a.n_jobs] = tiles;
+  // token runs: about 1024 workgroups, within the partial buffer
+  int ks = std::max(1, std::min(32, 1024 / std::max(1, tiles)));
+  ks = std::min(ks, (a.T + TT - 1) / TT);
+  while (ks > 1 && (int64_t)tiles * ks * TM * TN > a.partial_floats) --ks;
+  if (!a.partial) ks = 1;
+  k.chunk = ((a.T + ks - 1) / ks + TT - 1) / TT * TT;
+  k.ksplit = (a.T + k.chunk - 1) / k.chunk;
+  if ((int64_t)(std::min(a.T, k.chunk) + TT) * max_ld * 2 >= (int64_t)1 << 31) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_lora_tc, dim3((unsigned)(tiles * k.ksplit)), dim3(NT), 0, s, k);
+  if (k.ksplit > 1) hipLaunchKernelGGL(k_lora_tc_reduce, dim3((unsigned)tiles), dim3(NT), 0, s, k);
+  return hipGetLastError();
+}
+
+}  // namespace lsq

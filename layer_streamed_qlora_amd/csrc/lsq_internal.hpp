@@ -133,6 +133,25 @@ struct GemmArgs {
 };
 hipError_t launch_gemm_generic(const GemmArgs& a, hipStream_t s);
 
+// Products over tokens for the LoRA gradients, several per launch:
+// C_d[m][n - d ncols] (=, or += with beta 1) sum_t A[t][m] B[t][n] for n in
+// [d ncols, (d + 1) ncols), kept where n - d ncols < nvalid and C_d is set.
+constexpr int kMaxTcJobs = 4;
+struct TcJob {
+  const uint16_t* A = nullptr; int32_t lda = 0; int32_t M = 0;   // bf16 [T, lda], 16-byte aligned
+  const uint16_t* B = nullptr; int32_t ldb = 0; int32_t N = 0;   // bf16 [T, ldb], N <= 3 ncols
+  float* C[3] = {nullptr, nullptr, nullptr};
+  int64_t scm = 0, scn = 0;                                      // element (m, n') at m scm + n' scn
+  int32_t ncols = 0, nvalid = 0;
+};
+struct TcArgs {
+  TcJob job[kMaxTcJobs]; int32_t n_jobs = 0;
+  int32_t T = 0;
+  float beta = 0.f;
+  float* partial = nullptr; int64_t partial_floats = 0;          // scratch for token runs
+};
+hipError_t launch_lora_tc(const TcArgs& a, hipStream_t s);
+
 // Causal grouped-query attention over batch sequences of S tokens, flash style.
 // qkv: bf16 [batch * S, ldqkv], q heads at columns h * hd, k heads from qd, v heads
 // from qd + kvd; q head h reads kv head h / (hq / hkv).  hd is 64 or 128.

@@ -599,31 +599,46 @@ ls_status lora_grads_G(ls_ctx* c, int l, const Dims& d, int p, const uint16_t* d
   return LS_OK;
 }
 
-ls_status lora_grads_AB(ls_ctx* c, int l, const Dims& d, int p, const uint16_t* dy, int lddy, const uint16_t* x, int ldx,
-                        float beta) {
-  if (!lora_active(c, l, p)) return LS_OK;
-  const ProjLayout& P = c->lay.p[p];
-  const LoraReg& R = c->lora[l][p];
-  if (R.dB) {
-    GemmArgs g;
-    g.A = dy; g.sAm = 1; g.sAk = lddy;
-    g.B = c->dp<uint16_t>(c->plan.hs) + p * d.r16; g.sBn = 1; g.sBk = d.R7;
-    g.C = R.dB; g.sCm = d.r; g.sCn = 1; g.c_f32 = 1;
-    g.M = P.n_out; g.N = d.r; g.K = d.T; g.beta = beta;
-    g.ksplit = auto_split(g.M, g.N, g.K, 1); g.partial = c->dp<float>(c->plan.partial);
-    KTimer kt(c, LS_KC_LORA, 2.0 * d.T * P.n_out * d.r, 2.0 * d.T * P.n_out + 2.0 * d.T * d.r + 4.0 * P.n_out * d.r);
-    HIPCHK(c, launch_gemm_generic(g, c->cs));
+// dA and dB of the n projections p0.. that share the input x (float32, written or,
+// with beta 1, accumulated), one launch: dA_p = Gs_p^T x over the stacked Gs columns
+// of the group, dB_p = dY_p^T Hs_p with dY_p at dy + (sum of the earlier n_out).
+ls_status lora_grads_AB(ls_ctx* c, int l, const Dims& d, int p0, int n, const uint16_t* dy, int lddy,
+                        const uint16_t* x, int ldx, float beta) {
+  TcArgs a;
+  a.T = d.T; a.beta = beta;
+  a.partial = c->dp<float>(c->plan.partial); a.partial_floats = (int64_t)(c->plan.partial_bytes / 4);
+  const int n_in = c->lay.p[p0].n_in;
+  double flop = 0.0, bytes = 0.0;
+  TcJob ja;
+  ja.A = x; ja.lda = ldx; ja.M = n_in;
+  ja.B = c->dp<uint16_t>(c->plan.gs) + p0 * d.r16; ja.ldb = d.R7; ja.N = n * d.r16;
+  ja.scm = 1; ja.scn = n_in; ja.ncols = d.r16; ja.nvalid = d.r;
+  bool any_a = false;
+  int col = 0;
+  for (int i = 0; i < n; ++i) {
+    const int p = p0 + i;
+    const ProjLayout& P = c->lay.p[p];
+    const LoraReg& R = c->lora[l][p];
+    const bool on = lora_active(c, l, p);
+    if (on && R.dA) { ja.C[i] = R.dA; any_a = true; flop += 2.0 * d.T * n_in * d.r; }
+    if (on && R.dB) {
+      TcJob jb;
+      jb.A = dy + col; jb.lda = lddy; jb.M = P.n_out;
+      jb.B = c->dp<uint16_t>(c->plan.hs) + p * d.r16; jb.ldb = d.R7; jb.N = d.r16;
+      jb.C[0] = R.dB; jb.scm = d.r; jb.scn = 1; jb.ncols = d.r16; jb.nvalid = d.r;
+      a.job[a.n_jobs++] = jb;
+      flop += 2.0 * d.T * P.n_out * d.r;
+      bytes += 2.0 * d.T * P.n_out + 2.0 * d.T * d.r16 + 4.0 * P.n_out * d.r;
+    }
+    col += P.n_out;
   }
-  if (R.dA) {
-    GemmArgs g;
-    g.A = x; g.sAm = 1; g.sAk = ldx;
-    g.B = c->dp<uint16_t>(c->plan.gs) + p * d.r16; g.sBn = 1; g.sBk = d.R7;
-    g.C = R.dA; g.sCm = 1; g.sCn = P.n_in; g.c_f32 = 1;
-    g.M = P.n_in; g.N = d.r; g.K = d.T; g.beta = beta;
-    g.ksplit = auto_split(g.M, g.N, g.K, 1); g.partial = c->dp<float>(c->plan.partial);
-    KTimer kt(c, LS_KC_LORA, 2.0 * d.T * P.n_in * d.r, 2.0 * d.T * P.n_in + 2.0 * d.T * d.r + 4.0 * P.n_in * d.r);
-    HIPCHK(c, launch_gemm_generic(g, c->cs));
+  if (any_a) {
+    a.job[a.n_jobs++] = ja;
+    bytes += 2.0 * d.T * n_in + 2.0 * d.T * n * d.r16 + 4.0 * n * n_in * d.r;
   }
+  if (a.n_jobs == 0) return LS_OK;
+  KTimer kt(c, LS_KC_LORA, flop, bytes);
+  HIPCHK(c, launch_lora_tc(a, c->cs));
   return LS_OK;
 }
 
@@ -656,7 +671,7 @@ ls_status layer_backward(ls_ctx* c, int l, const uint8_t* blob, const Dims& d, c
 
   // ---- down: y = h + act W_d^T + LoRA
   if ((st = lora_grads_G(c, l, d, LS_PROJ_DOWN, dy, d.h))) return st;
-  if ((st = lora_grads_AB(c, l, d, LS_PROJ_DOWN, dy, d.h, act, d.I, beta))) return st;
+  if ((st = lora_grads_AB(c, l, d, LS_PROJ_DOWN, 1, dy, d.h, act, d.I, beta))) return st;
   {
     BwdArgs b;
     b.dy = dy; b.lddy = d.h; b.M = d.T; b.N = d.I; b.n_segs = 1;
@@ -672,8 +687,8 @@ ls_status layer_backward(ls_ctx* c, int l, const uint8_t* blob, const Dims& d, c
   for (int i = 0; i < 2; ++i) {
     const int p = LS_PROJ_GATE + i;
     if ((st = lora_grads_G(c, l, d, p, dgu + i * d.I, 2 * d.I))) return st;
-    if ((st = lora_grads_AB(c, l, d, p, dgu + i * d.I, 2 * d.I, n2, d.h, beta))) return st;
   }
+  if ((st = lora_grads_AB(c, l, d, LS_PROJ_GATE, 2, dgu, 2 * d.I, n2, d.h, beta))) return st;
   {
     BwdArgs b;
     b.dy = dgu; b.lddy = 2 * d.I; b.M = d.T; b.N = d.h; b.n_segs = 2;
@@ -691,7 +706,7 @@ ls_status layer_backward(ls_ctx* c, int l, const uint8_t* blob, const Dims& d, c
   }
   // ---- o: h = x + att W_o^T + LoRA
   if ((st = lora_grads_G(c, l, d, LS_PROJ_O, dh16, d.h))) return st;
-  if ((st = lora_grads_AB(c, l, d, LS_PROJ_O, dh16, d.h, att, d.qd, beta))) return st;
+  if ((st = lora_grads_AB(c, l, d, LS_PROJ_O, 1, dh16, d.h, att, d.qd, beta))) return st;
   {
     BwdArgs b;
     b.dy = dh16; b.lddy = d.h; b.M = d.T; b.N = d.qd; b.n_segs = 1;
@@ -712,8 +727,8 @@ ls_status layer_backward(ls_ctx* c, int l, const uint8_t* blob, const Dims& d, c
   for (int i = 0; i < 3; ++i) {
     const int p = LS_PROJ_Q + i;
     if ((st = lora_grads_G(c, l, d, p, dqkv + cols[i], d.qkvd))) return st;
-    if ((st = lora_grads_AB(c, l, d, p, dqkv + cols[i], d.qkvd, n1, d.h, beta))) return st;
   }
+  if ((st = lora_grads_AB(c, l, d, LS_PROJ_Q, 3, dqkv, d.qkvd, n1, d.h, beta))) return st;
   {
     BwdArgs b;
     b.dy = dqkv; b.lddy = d.qkvd; b.M = d.T; b.N = d.h; b.n_segs = 3;
