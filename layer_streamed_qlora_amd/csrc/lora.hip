@@ -36,19 +36,20 @@ struct TcKArgs {
   int32_t ksplit = 1, chunk = 0;
 };
 
-// Result element of thread threadIdx.x, block jb, register v of a C tile at (m0, n0):
-// C[i = feature][j = column] sits in lane j + 32 hh, register v holding feature
-// 32 w + (v / 4) * 8 + 4 hh + v % 4.
-__device__ __forceinline__ void tc_put(const TcArgs& a, int job, int m0, int n0, int jb, int v, float val) {
-  const TcJob& J = a.job[job];
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+// Destination of result element (thread t, block jb, register v) of a C tile at
+// (m0, n0), or nullptr if it is not kept: C[i = feature][j = column] sits in lane
+// j + 32 hh, register v holding feature 32 w + (v / 4) * 8 + 4 hh + v % 4.
+__device__ __forceinline__ float* tc_dest(const TcJob& J, int m0, int n0, int t, int jb, int v) {
+  const int lane = t & 63, w = t >> 6;
   const int m = m0 + 32 * w + (v >> 2) * 8 + 4 * (lane >> 5) + (v & 3);
   const int n = n0 + 32 * jb + (lane & 31);
-  if (m >= J.M || n >= J.N) return;
+  if (m >= J.M || n >= J.N) return nullptr;
   const int d = n / J.ncols, nl = n - d * J.ncols;
-  if (nl >= J.nvalid || J.C[d] == nullptr) return;
-  float* c = J.C[d] + (int64_t)m * J.scm + (int64_t)nl * J.scn;
-  *c = a.beta != 0.f ? val + a.beta * *c : val;
+  if (nl >= J.nvalid || J.C[d] == nullptr) return nullptr;
+  return J.C[d] + (int64_t)m * J.scm + (int64_t)nl * J.scn;
+}
+__device__ __forceinline__ void tc_put(float* c, float val, float beta) {
+  *c = beta != 0.f ? val + beta * *c : val;
 }
 
 __global__ void __launch_bounds__(NT) k_lora_tc(TcKArgs k) {
@@ -97,33 +98,33 @@ __global__ void __launch_bounds__(NT) k_lora_tc(TcKArgs k) {
 #pragma unroll
     for (int jb = 0; jb < 2; ++jb)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) tc_put(a, j, m0, n0, jb, v, acc[jb][v]);
+      for (int v = 0; v < 16; ++v)
+        if (float* c = tc_dest(J, m0, n0, threadIdx.x, jb, v)) tc_put(c, acc[jb][v], a.beta);
     return;
   }
   float* part = a.partial + ((int64_t)flat * k.ksplit + split) * (TM * TN);
 #pragma unroll
   for (int jb = 0; jb < 2; ++jb)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) part[(jb * 16 + v) * NT + threadIdx.x] = acc[jb][v];
+    for (int v = 0; v < 16; ++v)
+      if (tc_dest(J, m0, n0, threadIdx.x, jb, v)) part[(jb * 16 + v) * NT + threadIdx.x] = acc[jb][v];
 }
 
-// Sum of the token runs of one output tile, in run order.
+// Sum of the token runs of one result element, in run order: block b covers element
+// slot e = b % 32 of tile b / 32 for all NT thread positions.
 __global__ void __launch_bounds__(NT) k_lora_tc_reduce(TcKArgs k) {
   const TcArgs& a = k.a;
-  const int flat = blockIdx.x;
+  const int flat = (int)blockIdx.x >> 5, e = (int)blockIdx.x & 31;
   int j = 0;
   while (j + 1 < a.n_jobs && flat >= k.tile0[j + 1]) ++j;
   const int local = flat - k.tile0[j];
   const int mt = local / k.n_tiles[j], nt = local - mt * k.n_tiles[j];
-  const float* base = a.partial + (int64_t)flat * k.ksplit * (TM * TN);
-#pragma unroll
-  for (int jb = 0; jb < 2; ++jb)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      float sum = 0.f;
-      for (int sp = 0; sp < k.ksplit; ++sp) sum += base[(int64_t)sp * (TM * TN) + (jb * 16 + v) * NT + threadIdx.x];
-      tc_put(a, j, mt * TM, nt * TN, jb, v, sum);
-    }
+  float* c = tc_dest(a.job[j], mt * TM, nt * TN, threadIdx.x, e >> 4, e & 15);
+  if (!c) return;
+  const float* src = a.partial + (int64_t)flat * k.ksplit * (TM * TN) + e * NT + threadIdx.x;
+  float sum = 0.f;
+  for (int sp = 0; sp < k.ksplit; ++sp) sum += src[(int64_t)sp * (TM * TN)];
+  tc_put(c, sum, a.beta);
 }
 
 }  // namespace
@@ -155,7 +156,7 @@ hipError_t launch_lora_tc(const TcArgs& a, hipStream_t s) {
   k.ksplit = (a.T + k.chunk - 1) / k.chunk;
   if ((int64_t)(std::min(a.T, k.chunk) + TT) * max_ld * 2 >= (int64_t)1 << 31) return hipErrorInvalidValue;
   hipLaunchKernelGGL(k_lora_tc, dim3((unsigned)(tiles * k.ksplit)), dim3(NT), 0, s, k);
-  if (k.ksplit > 1) hipLaunchKernelGGL(k_lora_tc_reduce, dim3((unsigned)tiles), dim3(NT), 0, s, k);
+  if (k.ksplit > 1) hipLaunchKernelGGL(k_lora_tc_reduce, dim3((unsigned)(tiles * 32)), dim3(NT), 0, s, k);
   return hipGetLastError();
 }
 
