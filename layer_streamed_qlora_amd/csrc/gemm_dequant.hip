@@ -81,6 +81,16 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint64_t bytes) {
   const uint32_t n = bytes > 0xFFFFFFF0ull ? 0xFFFFFFF0u : (uint32_t)bytes;
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)n, 0x00020000);
 }
+// Same, for a buffer the caller knows to be the same across the wave: the fields are
+// moved to scalar registers so the loads need no per-lane descriptor loop.
+__device__ __forceinline__ rsrc_t make_rsrc_wave(const void* p, uint64_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  const uint32_t n = __builtin_amdgcn_readfirstlane(bytes > 0xFFFFFFF0ull ? 0xFFFFFFF0u : (uint32_t)bytes);
+  void* q = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(q, (short)0, (int)n, 0x00020000);
+}
 __device__ __forceinline__ uint4 bload16(rsrc_t r, uint32_t off) {
   typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
   const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
@@ -393,68 +403,75 @@ __device__ __forceinline__ void ext_tile(uint16_t* s, rsrc_t res, uint32_t col_o
 // per-lane offset; load(k0) must only be called with k0 < K.
 template <int FMT>
 struct WFwdFast {
-  uint4 raw[FMT == WF_BF16 ? 4 : 1];
-  uint32_t blk;      // absmax word (NF4) or 8-bit code (DQ)
-  float s2;          // DQ second-level scale
+  // per-tile registers, carried from one K step to the next
+  struct Regs {
+    uint4 raw[FMT == WF_BF16 ? 4 : 1];
+    uint32_t blk;      // absmax word (NF4) or 8-bit code (DQ)
+    float s2;          // DQ second-level scale
+  };
+  // loop-invariant buffers and offsets
   rsrc_t codes, absq, sc2;
   float mean;
   uint32_t voff_w, voff_b, blk0;
+  __device__ __forceinline__ static void clear(Regs& R) {
+#pragma unroll
+    for (int i = 0; i < (FMT == WF_BF16 ? 4 : 1); ++i) R.raw[i] = make_uint4(0, 0, 0, 0);
+    R.blk = 0; R.s2 = 0.f;
+  }
   // r: this thread's row within the tile of weight w starting at row n0; cap: tile rows
   __device__ __forceinline__ void init(const WeightRef& w, int n0, uint32_t r, int cap) {
     const int K = w.n_in;
     const int rows = w.n_out - n0 < cap ? w.n_out - n0 : cap;
     const uint32_t h = threadIdx.x & 1;
     const uint32_t kblk = (uint32_t)K / kNF4Block;
-#pragma unroll
-    for (int i = 0; i < (FMT == WF_BF16 ? 4 : 1); ++i) raw[i] = make_uint4(0, 0, 0, 0);
-    blk = 0; s2 = 0.f;
+    mean = 0.f; voff_b = 0; blk0 = 0;
     if constexpr (FMT == WF_BF16) {
-      codes = make_rsrc(w.w + (uint64_t)n0 * K * 2, (uint64_t)(rows > 0 ? rows : 0) * K * 2);
+      codes = make_rsrc_wave(w.w + (uint64_t)n0 * K * 2, (uint64_t)(rows > 0 ? rows : 0) * K * 2);
       voff_w = (r * (uint32_t)K + 32u * h) * 2u;
     } else {
-      codes = make_rsrc(w.w + (uint64_t)n0 * K / 2, (uint64_t)(rows > 0 ? rows : 0) * K / 2);
+      codes = make_rsrc_wave(w.w + (uint64_t)n0 * K / 2, (uint64_t)(rows > 0 ? rows : 0) * K / 2);
       voff_w = r * (uint32_t)K / 2u + 16u * h;
       const uint64_t b0 = (uint64_t)n0 * kblk;
       const uint64_t nb = (uint64_t)(rows > 0 ? rows : 0) * kblk;
       voff_b = r * kblk;
       blk0 = (uint32_t)(b0 + voff_b);
       if constexpr (FMT == WF_NF4) {
-        absq = make_rsrc(w.absmax + b0, nb * 4);
+        absq = make_rsrc_wave(w.absmax + b0, nb * 4);
       } else {
-        absq = make_rsrc(w.qabs + b0, nb);
+        absq = make_rsrc_wave(w.qabs + b0, nb);
         const uint64_t all = (uint64_t)w.n_out * kblk;
-        sc2 = make_rsrc(w.scale2, (all + kDQGroup - 1) / kDQGroup * 4);
+        sc2 = make_rsrc_wave(w.scale2, (all + kDQGroup - 1) / kDQGroup * 4);
         mean = *w.mean;
       }
     }
   }
-  __device__ __forceinline__ void load(int k0) {
+  __device__ __forceinline__ void load(Regs& R, int k0) const {
     if constexpr (FMT == WF_BF16) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) raw[i] = bload16s(codes, voff_w + 16u * i, (uint32_t)k0 * 2u);
+      for (int i = 0; i < 4; ++i) R.raw[i] = bload16s(codes, voff_w + 16u * i, (uint32_t)k0 * 2u);
     } else {
-      raw[0] = bload16s(codes, voff_w, (uint32_t)k0 / 2u);
+      R.raw[0] = bload16s(codes, voff_w, (uint32_t)k0 / 2u);
       const uint32_t kb = (uint32_t)k0 / kNF4Block;
       if constexpr (FMT == WF_NF4) {
-        blk = bload4s(absq, voff_b * 4u, kb * 4u);
+        R.blk = bload4s(absq, voff_b * 4u, kb * 4u);
       } else {
-        blk = bload1s(absq, voff_b, kb);
-        s2 = __builtin_bit_cast(float, bload4s(sc2, ((blk0 + kb) / kDQGroup) * 4u, 0));
+        R.blk = bload1s(absq, voff_b, kb);
+        R.s2 = __builtin_bit_cast(float, bload4s(sc2, ((blk0 + kb) / kDQGroup) * 4u, 0));
       }
     }
   }
-  __device__ __forceinline__ float absmax() const {
-    if constexpr (FMT == WF_NF4) return __builtin_bit_cast(float, blk);
-    else return dq_absmax(blk, s2, mean);
+  __device__ __forceinline__ float absmax(const Regs& R) const {
+    if constexpr (FMT == WF_NF4) return __builtin_bit_cast(float, R.blk);
+    else return dq_absmax(R.blk, R.s2, mean);
   }
   // quarter q: 8 of the thread's 32 elements, one 16-byte LDS store
-  __device__ __forceinline__ void store_part(uint16_t* s, const float2* lut2, int q, float am) const {
+  __device__ __forceinline__ void store_part(const Regs& R, uint16_t* s, const float2* lut2, int q, float am) const {
     uint16_t* dst = s + (threadIdx.x >> 1) * PITCH + 32 * (threadIdx.x & 1) + 8 * q;
     if constexpr (FMT == WF_BF16) {
-      *reinterpret_cast<uint4*>(dst) = raw[q];
+      *reinterpret_cast<uint4*>(dst) = R.raw[q];
     } else {
       uint32_t o[4];
-      dequant8(reinterpret_cast<const uint32_t*>(&raw[0])[q], am, lut2, o);
+      dequant8(reinterpret_cast<const uint32_t*>(&R.raw[0])[q], am, lut2, o);
       *reinterpret_cast<uint4*>(dst) = make_uint4(o[0], o[1], o[2], o[3]);
     }
   }
@@ -464,19 +481,22 @@ struct WFwdFast {
 // and 16 output columns j0 + 16c (c = t >> 5), inside one NF4 block per row.
 template <int FMT>
 struct WBwdFast {
-  uint4 raw[FMT == WF_BF16 ? 4 : 1];   // nf4: .x .y = row 0 codes, .z .w = row 1 codes
-  uint32_t blk[2];
-  float s2[2];
-  rsrc_t codes, absq, sc2;
-  float mean;
+  struct Regs {
+    uint4 raw[FMT == WF_BF16 ? 4 : 1];   // nf4: .x .y = row 0 codes, .z .w = row 1 codes
+    uint32_t blk[2];
+    float s2[2];
+    float mean;
+  };
   uint32_t voff_w[2], voff_b[2];
   uint32_t jblk;     // J / 64
+  __device__ __forceinline__ static void clear(Regs& R) {
+#pragma unroll
+    for (int i = 0; i < (FMT == WF_BF16 ? 4 : 1); ++i) R.raw[i] = make_uint4(0, 0, 0, 0);
+    R.blk[0] = R.blk[1] = 0; R.s2[0] = R.s2[1] = 0.f; R.mean = 0.f;
+  }
   __device__ __forceinline__ void init_lane(int J) {
     const uint32_t p = threadIdx.x & 31, c = threadIdx.x >> 5;
     jblk = (uint32_t)J / kNF4Block;
-#pragma unroll
-    for (int i = 0; i < (FMT == WF_BF16 ? 4 : 1); ++i) raw[i] = make_uint4(0, 0, 0, 0);
-    blk[0] = blk[1] = 0; s2[0] = s2[1] = 0.f;
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
       const uint32_t row = 2 * p + r;
@@ -487,53 +507,54 @@ struct WBwdFast {
   }
   // tile (rows k0.., columns j0..) with k0 < n_out: every buffer is based at the
   // tile's first element, so the range check (per-lane offset only) ends at the matrix
-  __device__ __forceinline__ void load(const WeightRef& w, int j0, int k0) {
+  __device__ __forceinline__ void load(Regs& R, const WeightRef& w, int j0, int k0) const {
     const uint64_t J = (uint64_t)w.n_in;
     const uint64_t numel = (uint64_t)w.n_out * J;
     const uint64_t e0 = (uint64_t)k0 * J + (uint64_t)j0;
     const uint64_t nb = numel / kNF4Block, b0 = e0 / kNF4Block;
     if constexpr (FMT == WF_BF16) {
-      codes = make_rsrc(w.w + e0 * 2, (numel - e0) * 2);
+      const rsrc_t codes = make_rsrc(w.w + e0 * 2, (numel - e0) * 2);
 #pragma unroll
       for (int r = 0; r < 2; ++r) {
-        raw[2 * r] = bload16s(codes, voff_w[r], 0);
-        raw[2 * r + 1] = bload16s(codes, voff_w[r] + 16u, 0);
+        R.raw[2 * r] = bload16s(codes, voff_w[r], 0);
+        R.raw[2 * r + 1] = bload16s(codes, voff_w[r] + 16u, 0);
       }
     } else {
-      codes = make_rsrc(w.w + e0 / 2, (numel - e0) / 2);
+      const rsrc_t codes = make_rsrc(w.w + e0 / 2, (numel - e0) / 2);
       typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
       const u32x2 c0 = __builtin_amdgcn_raw_buffer_load_b64(codes, voff_w[0], 0, 0);
       const u32x2 c1 = __builtin_amdgcn_raw_buffer_load_b64(codes, voff_w[1], 0, 0);
-      raw[0] = make_uint4(c0.x, c0.y, c1.x, c1.y);
+      R.raw[0] = make_uint4(c0.x, c0.y, c1.x, c1.y);
       if constexpr (FMT == WF_NF4) {
-        absq = make_rsrc(w.absmax + b0, (nb - b0) * 4);
-        blk[0] = bload4s(absq, voff_b[0] * 4u, 0);
-        blk[1] = bload4s(absq, voff_b[1] * 4u, 0);
+        const rsrc_t absq = make_rsrc(w.absmax + b0, (nb - b0) * 4);
+        R.blk[0] = bload4s(absq, voff_b[0] * 4u, 0);
+        R.blk[1] = bload4s(absq, voff_b[1] * 4u, 0);
       } else {
-        absq = make_rsrc(w.qabs + b0, nb - b0);
-        sc2 = make_rsrc(w.scale2, (nb + kDQGroup - 1) / kDQGroup * 4);
-        mean = *w.mean;
+        const rsrc_t absq = make_rsrc(w.qabs + b0, nb - b0);
+        const rsrc_t sc2 = make_rsrc(w.scale2, (nb + kDQGroup - 1) / kDQGroup * 4);
+        R.mean = *w.mean;
 #pragma unroll
         for (int r = 0; r < 2; ++r) {
-          blk[r] = bload1s(absq, voff_b[r], 0);
-          s2[r] = __builtin_bit_cast(float, bload4s(sc2, (((uint32_t)b0 + voff_b[r]) / kDQGroup) * 4u, 0));
+          R.blk[r] = bload1s(absq, voff_b[r], 0);
+          R.s2[r] = __builtin_bit_cast(float, bload4s(sc2, (((uint32_t)b0 + voff_b[r]) / kDQGroup) * 4u, 0));
         }
       }
     }
   }
-  __device__ __forceinline__ float absmax(int r) const {
-    if constexpr (FMT == WF_NF4) return __builtin_bit_cast(float, blk[r]);
-    else return dq_absmax(blk[r], s2[r], mean);
+  __device__ __forceinline__ float absmax(const Regs& R, int r) const {
+    if constexpr (FMT == WF_NF4) return __builtin_bit_cast(float, R.blk[r]);
+    else return dq_absmax(R.blk[r], R.s2[r], R.mean);
   }
   // quarter q: columns 4q .. 4q+3 of the thread's 16, both rows -> 4 dword stores
-  __device__ __forceinline__ void store_part(uint16_t* s, const float2* lut2, int q, float a0, float a1) const {
+  __device__ __forceinline__ void store_part(const Regs& R, uint16_t* s, const float2* lut2, int q, float a0,
+                                             float a1) const {
     const int p = threadIdx.x & 31, c = threadIdx.x >> 5;
     uint32_t* dst = reinterpret_cast<uint32_t*>(s + (16 * c + 4 * q) * PITCH + 2 * p);
     constexpr int pitch32 = PITCH / 2;
     if constexpr (FMT == WF_BF16) {
       // row r dword w (columns 2w, 2w+1), w = 2q, 2q+1
-      const uint32_t* r0 = reinterpret_cast<const uint32_t*>(&raw[0]);
-      const uint32_t* r1 = reinterpret_cast<const uint32_t*>(&raw[2]);
+      const uint32_t* r0 = reinterpret_cast<const uint32_t*>(&R.raw[0]);
+      const uint32_t* r1 = reinterpret_cast<const uint32_t*>(&R.raw[2]);
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const int w = 2 * q + u;
@@ -541,7 +562,7 @@ struct WBwdFast {
         dst[(2 * u + 1) * pitch32] = __builtin_amdgcn_perm(r1[w], r0[w], 0x07060302u);
       }
     } else {
-      const uint32_t* rr = reinterpret_cast<const uint32_t*>(&raw[0]);
+      const uint32_t* rr = reinterpret_cast<const uint32_t*>(&R.raw[0]);
       const uint32_t sh = (q & 1) * 16;
       const uint32_t w0 = rr[q >> 1] >> sh, w1 = rr[2 + (q >> 1)] >> sh;
 #pragma unroll
@@ -1001,18 +1022,19 @@ __global__ void __launch_bounds__(NT_FAST, 1) k_gemm_fwd_fast(FwdArgs args, int 
   // stored; W: current and next tile in registers.  Loads past K are skipped.
   AFast ra;
   ra.init(xres, args.ldx);
-  WFwdFast<FMT> rw, rw_next;
+  WFwdFast<FMT> ws;
   {
     const WeightRef& wsel = PAIRED ? args.g[threadIdx.x >> 8].w : G.w;   // wave-uniform
     const uint32_t r = PAIRED ? (threadIdx.x >> 1) & 127u : threadIdx.x >> 1;
-    const int cap = PAIRED ? BN / 2 : BN;
-    rw.init(wsel, n0, r, cap);
-    rw_next.init(wsel, n0, r, cap);
+    ws.init(wsel, n0, r, PAIRED ? BN / 2 : BN);
   }
+  typename WFwdFast<FMT>::Regs rw, rw_next;
+  WFwdFast<FMT>::clear(rw);
+  WFwdFast<FMT>::clear(rw_next);
 #pragma unroll
   for (int q = 0; q < 4; ++q) ra.load_q(0, q);
-  rw.load(0);
-  if (BK < K) rw_next.load(BK);
+  ws.load(rw, 0);
+  if (BK < K) ws.load(rw_next, BK);
   __syncthreads();
   for (int it = 0; it < n_iter; ++it) {
     const int cur = it & 1;
@@ -1020,14 +1042,14 @@ __global__ void __launch_bounds__(NT_FAST, 1) k_gemm_fwd_fast(FwdArgs args, int 
     uint16_t* nw = sm.u.k.w[cur ^ 1];
     const int k_next = (it + 1) * BK;
     const bool more = k_next < K;
-    const float am = FMT == WF_BF16 ? 0.f : rw.absmax();
+    const float am = FMT == WF_BF16 ? 0.f : ws.absmax(rw);
     mma_stage<NT_FAST>(sm.u.k.a[cur], sm.u.k.w[cur], acc, [&](int q) {
       ra.store_q(na, q);
       if (more) ra.load_q((uint32_t)k_next, q);
-      rw.store_part(nw, sm.lut2, q, am);
+      ws.store_part(rw, nw, sm.lut2, q, am);
     });
     rw = rw_next;
-    if (k_next + BK < K) rw_next.load(k_next + BK);
+    if (k_next + BK < K) ws.load(rw_next, k_next + BK);
     __syncthreads();
   }
 
@@ -1094,13 +1116,15 @@ __global__ void __launch_bounds__(NT_FAST, 1) k_gemm_bwd_fast(BwdArgs args, int 
   };
   AFast ra;
   ra.init(dres, args.lddy);
-  WBwdFast<FMT> rw, rw_next;
-  rw.init_lane(args.N);
-  rw_next.init_lane(args.N);
-  auto load_w = [&](WBwdFast<FMT>& w, int t) {
+  WBwdFast<FMT> ws;
+  ws.init_lane(args.N);
+  typename WBwdFast<FMT>::Regs rw, rw_next;
+  WBwdFast<FMT>::clear(rw);
+  WBwdFast<FMT>::clear(rw_next);
+  auto load_w = [&](typename WBwdFast<FMT>::Regs& R, int t) {
     if (t >= total_k) return;
     int s, k0; seg_of(t, s, k0);
-    w.load(args.seg[s].w, j0, k0);
+    ws.load(R, args.seg[s].w, j0, k0);
   };
   {
     int s, k0; seg_of(0, s, k0);
@@ -1118,12 +1142,12 @@ __global__ void __launch_bounds__(NT_FAST, 1) k_gemm_bwd_fast(BwdArgs args, int 
     const bool more = it + 1 < total_k;
     uint32_t col = 0;
     if (more) { int s, k0; seg_of(it + 1, s, k0); col = (uint32_t)(args.seg[s].a_col0 + k0); }
-    const float a0 = FMT == WF_BF16 ? 0.f : rw.absmax(0);
-    const float a1 = FMT == WF_BF16 ? 0.f : rw.absmax(1);
+    const float a0 = FMT == WF_BF16 ? 0.f : ws.absmax(rw, 0);
+    const float a1 = FMT == WF_BF16 ? 0.f : ws.absmax(rw, 1);
     mma_stage<NT_FAST>(sm.u.k.a[cur], sm.u.k.w[cur], acc, [&](int q) {
       ra.store_q(na, q);
       if (more) ra.load_q(col, q);
-      rw.store_part(nw, sm.lut2, q, a0, a1);
+      ws.store_part(rw, nw, sm.lut2, q, a0, a1);
     });
     rw = rw_next;
     load_w(rw_next, it + 2);

@@ -45,27 +45,30 @@ def _rnd(parity):
 
 
 # ----------------------------------------------------------------- base weights
-def quantize_layer(src: dict, quant: str, double_quant: bool) -> dict:
+def quantize_layer(src: dict, quant: str, double_quant: bool, map_fn=map) -> dict:
     """Encode one layer's bf16 source weights the way the store holds them.
     Returns dict proj -> NF4Tensor (quant 'nf4') or float32 bf16 values (quant 'bf16'),
-    plus 'g1', 'g2' (bf16 values, kept as is)."""
+    plus 'g1', 'g2' (bf16 values, kept as is).  The projections are independent;
+    ``map_fn`` (e.g. a thread pool's map) only decides how they are visited."""
+    if quant not in ("nf4", "bf16"):
+        raise ValueError(quant)
+
+    def enc(p):
+        return nf4.NF4Tensor(src[p], double_quant) if quant == "nf4" else np.asarray(src[p], np.float32)
+
     out = {"g1": np.asarray(src["g1"], np.float32), "g2": np.asarray(src["g2"], np.float32)}
-    for p in PROJS:
-        if quant == "nf4":
-            out[p] = nf4.NF4Tensor(src[p], double_quant)
-        elif quant == "bf16":
-            out[p] = np.asarray(src[p], np.float32)
-        else:
-            raise ValueError(quant)
+    out.update(zip(PROJS, map_fn(enc, PROJS)))
     return out
 
 
-def dequant_layer(enc: dict) -> dict:
+def dequant_layer(enc: dict, map_fn=map) -> dict:
     """float64 weights the arithmetic uses (dequantised NF4 or the bf16 values)."""
-    w = {"g1": enc["g1"].astype(np.float64), "g2": enc["g2"].astype(np.float64)}
-    for p in PROJS:
+    def deq(p):
         t = enc[p]
-        w[p] = (t.dequant() if isinstance(t, nf4.NF4Tensor) else t).astype(np.float64)
+        return (t.dequant() if isinstance(t, nf4.NF4Tensor) else t).astype(np.float64)
+
+    w = {"g1": enc["g1"].astype(np.float64), "g2": enc["g2"].astype(np.float64)}
+    w.update(zip(PROJS, map_fn(deq, PROJS)))
     return w
 
 

@@ -110,8 +110,13 @@ class GpuRun:
 
 
 def oracle_layers(w, src_layers):
-    enc = [ostack.quantize_layer(lw, w.quant, w.double_quant) for lw in src_layers]
-    return enc, [ostack.dequant_layer(e) for e in enc]
+    """Encode and dequantise every layer on the oracle side, the seven projections of a
+    layer on a thread pool (numpy releases the interpreter lock in the heavy calls)."""
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(max_workers=7) as ex:
+        enc = [ostack.quantize_layer(lw, w.quant, w.double_quant, map_fn=ex.map) for lw in src_layers]
+        deq = [ostack.dequant_layer(e, map_fn=ex.map) for e in enc]
+    return enc, deq
 
 
 def oracle_step(w, src_layers, loras, x32, dy32, batch, seq, with_ref=False):

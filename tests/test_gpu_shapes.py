@@ -67,3 +67,33 @@ def test_streamed_equals_resident_bitwise(name, n_layers, batch, seq):
         for p in H.PROJS:
             assert np.array_equal(a["dA"][l][p].view(np.uint32), b["dA"][l][p].view(np.uint32)), (l, p)
             assert np.array_equal(a["dB"][l][p].view(np.uint32), b["dB"][l][p].view(np.uint32)), (l, p)
+
+
+def test_qwen32b_shape_layer_over_165mb():
+    """Qwen2.5-32B shape (NF4 + double quantisation): one streamed layer blob is 251.5 MB."""
+    parity_case("qwen32b", 1, 1, 128)
+
+
+def test_qwen32b_streamed_equals_resident_bitwise():
+    w = synth.WORKLOADS["qwen32b"].with_(batch=1, seq=128)
+    x, dy = synth.activations(w)
+    weights = [synth.layer_weights(w, l) for l in range(3)]
+    outs = []
+    for resident in (0, 1):
+        say(f"case: qwen32b streamed vs resident, resident={resident}")
+        run = H.GpuRun(w, [0, 1, 2], resident=resident, weights=weights)
+        outs.append(run.step(x, dy, 1, 128))
+        run.close()
+    a, b = outs
+    for k in ("Y", "dX"):
+        assert np.array_equal(a[k].view(np.uint32), b[k].view(np.uint32)), k
+    for l in range(3):
+        for p in H.PROJS:
+            assert np.array_equal(a["dA"][l][p].view(np.uint32), b["dA"][l][p].view(np.uint32)), (l, p)
+            assert np.array_equal(a["dB"][l][p].view(np.uint32), b["dB"][l][p].view(np.uint32)), (l, p)
+
+
+def test_qwen72b_dpo_shape_with_reference_pass():
+    """Qwen2.5-72B shape, DPO: policy forward, adapters-off reference forward on the same
+    streamed slot (452.8 MB blob), recompute backward."""
+    parity_case("qwen72b", 1, 1, 128, with_ref=True)
