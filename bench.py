@@ -71,6 +71,28 @@ def cpu_baseline(w, n_layers=1, batch=1, seq=512):
                       f"backward in {dt:.2f} s, scaled by depth ({w.n_layers}/{n_layers})"}
 
 
+def measured_traffic(kernel_class):
+    """HBM bytes per launch of the kernel class from the committed counter summary, or
+    None when the kernel source changed since the counters were taken."""
+    import hashlib
+    here = os.path.dirname(os.path.abspath(__file__))
+    path = os.path.join(here, "profiles", "llama8b_gemm_traffic.md")
+    try:
+        lines = open(path).read().splitlines()
+    except OSError:
+        return None
+    for line in lines:
+        if line.startswith("machine-readable: "):
+            rec = json.loads(line[len("machine-readable: "):])
+            if rec.get("class") != kernel_class:
+                return None
+            src = os.path.join(here, rec["kernel_source"])
+            if hashlib.sha256(open(src, "rb").read()).hexdigest() != rec["kernel_source_sha256"]:
+                return None
+            return float(rec["traffic_bytes_per_launch"])
+    return None
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -193,8 +215,8 @@ def main():
         achieved = kfl / (kms * 1e-3) / 1e12
         out["roofline"] = {"bound": "mfma", "kernel": f"fused dequant GEMM ({dom})", "achieved": round(achieved, 1),
                            "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                           "traffic": None, "avg_launch_ms": round(kms / kl, 4),
-                           "flop_per_launch": kfl / kl}
+                           "traffic": measured_traffic(dom), "avg_launch_ms": round(kms / kl, 4),
+                           "flop_per_launch": kfl / kl, "algorithmic_bytes_per_launch": kby / kl}
         gemm_ms = kacc["gemm_fwd"][1] + kacc["gemm_bwd"][1]
         gemm_fl = kacc["gemm_fwd"][2] + kacc["gemm_bwd"][2]
         out["mfma"] = {"dequant_gemm_tflops": round(gemm_fl / (gemm_ms * 1e-3) / 1e12, 1),
