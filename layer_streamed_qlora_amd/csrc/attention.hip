@@ -34,8 +34,10 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 // ------------------------------------------------------------------ forward
 // Workgroup: 128 queries of one (batch, q head), 4 waves x 32 queries.  Per 64-key
-// tile each wave computes S^T = K Q^T (keys x queries: each lane holds one query),
-// updates the running max / sum, and accumulates O^T = V^T P^T.
+// tile each wave computes S^T = K Q^T (keys x queries: each lane holds one query).
+// Two passes over the keys: the first finds each row's maximum and sum of exp, the
+// second forms the normalised P, rounds it to bf16 (the operand of the second
+// product) and accumulates O^T = V^T P^T.
 template <int HD>
 __global__ void __launch_bounds__(256) k_attn_fwd(AttnArgs a) {
   constexpr int NS = HD / 16, ND = HD / 32, PR = HD + 8;
@@ -57,15 +59,63 @@ __global__ void __launch_bounds__(256) k_attn_fwd(AttnArgs a) {
   const int last_key = min(qb * 128 + 127, a.S - 1);
   const int n_kb = last_key / KB + 1;
   const float cl = a.scale * kLog2e;
+  // scaled scores (base 2) of the key tile at k0 against this lane's query, masked
+  auto scores = [&](f32x16_t (&s)[2], int k0) {
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      s[kk] = f32x16_t{};
+#pragma unroll
+      for (int st = 0; st < NS; ++st)
+        s[kk] = mfma(*reinterpret_cast<const bf16x8_t*>(sk + (32 * kk + ql) * PR + 16 * st + 8 * hh), qf[st], s[kk]);
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int key = k0 + 32 * kk + (v >> 2) * 8 + 4 * hh + (v & 3);
+        s[kk][v] = (key <= q && key < a.S) ? s[kk][v] * cl : -INFINITY;
+      }
+    }
+  };
+  TileMover<HD, 256> tk, tv;
+  // pass 1: row maximum m and sum l of exp2(t - m) (each lane half sums its own keys)
+  float m = -INFINITY, l = 0.f;
+  tk.load(rk, a.ldqkv, 0);
+  for (int kb = 0; kb < n_kb; ++kb) {
+    __syncthreads();                    // the previous tile is no longer read
+    tk.store_rows(sk);
+    __syncthreads();
+    if (kb + 1 < n_kb) {
+      tk.load(rk, a.ldqkv, (kb + 1) * KB);
+    } else {                            // the second pass starts from key 0
+      tk.load(rk, a.ldqkv, 0);
+      tv.load(rv, a.ldqkv, 0);
+    }
+    const int k0 = kb * KB;
+    if (k0 > qw + 31) continue;         // tile entirely after this wave's queries
+    f32x16_t s[2];
+    scores(s, k0);
+    float mb = -INFINITY;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) mb = fmaxf(mb, s[kk][v]);
+    mb = fmaxf(mb, __shfl_xor(mb, 32));
+    const float mn = fmaxf(m, mb);
+    const float mu = mn == -INFINITY ? 0.f : mn;
+    float ls = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) ls += __builtin_amdgcn_exp2f(s[kk][v] - mu);
+    l = l * __builtin_amdgcn_exp2f(m - mu) + ls;
+    m = mn;
+  }
+  const float lt = l + __shfl_xor(l, 32);
+  const float inv = 1.f / lt;           // lt >= 1: the maximum's own term
+  // pass 2: P = exp2(t - m) / l, rounded to bf16, times V
   f32x16_t o[ND];
 #pragma unroll
   for (int d = 0; d < ND; ++d) o[d] = f32x16_t{};
-  float m = -INFINITY, l = 0.f;
-  TileMover<HD, 256> tk, tv;
-  tk.load(rk, a.ldqkv, 0);
-  tv.load(rv, a.ldqkv, 0);
   for (int kb = 0; kb < n_kb; ++kb) {
-    __syncthreads();                    // the previous tile is no longer read
+    __syncthreads();
     tk.store_rows(sk);
     tv.store_t(svt);
     __syncthreads();
@@ -74,42 +124,13 @@ __global__ void __launch_bounds__(256) k_attn_fwd(AttnArgs a) {
       tv.load(rv, a.ldqkv, (kb + 1) * KB);
     }
     const int k0 = kb * KB;
-    if (k0 > qw + 31) continue;         // tile entirely after this wave's queries
+    if (k0 > qw + 31) continue;
     f32x16_t s[2];
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      s[kk] = f32x16_t{};
-#pragma unroll
-      for (int st = 0; st < NS; ++st)
-        s[kk] = mfma(*reinterpret_cast<const bf16x8_t*>(sk + (32 * kk + ql) * PR + 16 * st + 8 * hh), qf[st], s[kk]);
-    }
-    float mb = -INFINITY;
+    scores(s, k0);
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int key = k0 + 32 * kk + (v >> 2) * 8 + 4 * hh + (v & 3);
-        const float t = (key <= q && key < a.S) ? s[kk][v] * cl : -INFINITY;
-        s[kk][v] = t;
-        mb = fmaxf(mb, t);
-      }
-    mb = fmaxf(mb, __shfl_xor(mb, 32));
-    const float mn = fmaxf(m, mb);
-    const float mu = mn == -INFINITY ? 0.f : mn;
-    const float alpha = __builtin_amdgcn_exp2f(m - mu);
-    m = mn;
-    float ls = 0.f;
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const float p = __builtin_amdgcn_exp2f(s[kk][v] - mu);
-        s[kk][v] = p;
-        ls += p;
-      }
-    l = l * alpha + ls;
-#pragma unroll
-    for (int d = 0; d < ND; ++d) o[d] *= alpha;
+      for (int v = 0; v < 16; ++v) s[kk][v] = __builtin_amdgcn_exp2f(s[kk][v] - m) * inv;
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
@@ -119,17 +140,18 @@ __global__ void __launch_bounds__(256) k_attn_fwd(AttnArgs a) {
         for (int d = 0; d < ND; ++d) o[d] = mfma(tfrag(svt, 32 * d + ql, 32 * kk + 16 * st, hh), pb, o[d]);
       }
   }
-  const float lt = l + __shfl_xor(l, 32);
   if (q < a.S) {
-    const float inv = 1.f / lt;
-    uint16_t* dst = a.out + ((int64_t)b * a.S + q) * a.ldo + h * HD;
+    const int64_t row = (int64_t)b * a.S + q;
+    uint16_t* dst = a.out + row * a.ldo + h * HD;
+    float* dst32 = a.out32 ? a.out32 + row * a.ldo + h * HD : nullptr;
 #pragma unroll
     for (int d = 0; d < ND; ++d)
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         const int col = 32 * d + 8 * g4 + 4 * hh;
-        *reinterpret_cast<uint2*>(dst + col) = make_uint2(pack2(o[d][4 * g4] * inv, o[d][4 * g4 + 1] * inv),
-                                                          pack2(o[d][4 * g4 + 2] * inv, o[d][4 * g4 + 3] * inv));
+        const float4 v4 = make_float4(o[d][4 * g4], o[d][4 * g4 + 1], o[d][4 * g4 + 2], o[d][4 * g4 + 3]);
+        *reinterpret_cast<uint2*>(dst + col) = make_uint2(pack2(v4.x, v4.y), pack2(v4.z, v4.w));
+        if (dst32) *reinterpret_cast<float4*>(dst32 + col) = v4;
       }
     if (hh == 0 && a.lse) a.lse[(int64_t)bh * a.S + q] = m + __builtin_amdgcn_logf(lt);
   }
@@ -147,11 +169,12 @@ __global__ void k_attn_dd(AttnArgs a) {
   const int64_t row = ok ? idx / a.hq : 0;
   const int head = ok ? (int)(idx % a.hq) : 0;
   if (ok) {
+    // O in float32 (the product P V before rounding): sum_d dO O = sum_j P_j dP_j
     const uint4 x = *reinterpret_cast<const uint4*>(a.dout + row * a.lddo + head * HD + 8 * part);
-    const uint4 y = *reinterpret_cast<const uint4*>(a.out + row * a.ldo + head * HD + 8 * part);
-    const uint32_t xs[4] = {x.x, x.y, x.z, x.w}, ys[4] = {y.x, y.y, y.z, y.w};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc += bf_lo(xs[j]) * bf_lo(ys[j]) + bf_hi(xs[j]) * bf_hi(ys[j]);
+    const float4 y0 = *reinterpret_cast<const float4*>(a.out32 + row * a.ldo + head * HD + 8 * part);
+    const float4 y1 = *reinterpret_cast<const float4*>(a.out32 + row * a.ldo + head * HD + 8 * part + 4);
+    acc = bf_lo(x.x) * y0.x + bf_hi(x.x) * y0.y + bf_lo(x.y) * y0.z + bf_hi(x.y) * y0.w +
+          bf_lo(x.z) * y1.x + bf_hi(x.z) * y1.y + bf_lo(x.w) * y1.z + bf_hi(x.w) * y1.w;
   }
 #pragma unroll
   for (int sh = TPR / 2; sh > 0; sh >>= 1) acc += __shfl_xor(acc, sh);
@@ -222,7 +245,7 @@ __global__ void __launch_bounds__(256) k_attn_dq(AttnArgs a) {
       for (int v = 0; v < 16; ++v) {
         const int key = k0 + 32 * kk + (v >> 2) * 8 + 4 * hh + (v & 3);
         const bool ok = qok && key <= q && key < a.S;
-        const float p = ok ? __builtin_amdgcn_exp2f(s[v] * cl - L) : 0.f;
+        const float p = ok ? bf16_value(__builtin_amdgcn_exp2f(s[v] * cl - L)) : 0.f;
         s[v] = a.scale * p * (dp[v] - D);
       }
 #pragma unroll
@@ -319,7 +342,7 @@ __global__ void __launch_bounds__(128) k_attn_dkv(AttnArgs a) {
           for (int e = 0; e < 4; ++e) {
             const int v = 4 * g4 + e, qg = q0 + qi + e;
             const bool ok = key <= qg && qg < a.S && key < a.S;
-            const float p = ok ? __builtin_amdgcn_exp2f(s[v] * cl - Ls[e]) : 0.f;
+            const float p = ok ? bf16_value(__builtin_amdgcn_exp2f(s[v] * cl - Ls[e])) : 0.f;
             s[v] = p;
             ds[v] = a.scale * p * (dp[v] - Ds[e]);
           }
@@ -381,7 +404,7 @@ hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t s) {
 
 hipError_t launch_attn_bwd(const AttnArgs& a, hipStream_t s) {
   if (a.batch <= 0 || a.S <= 0) return hipSuccess;
-  if (!shape_ok(a) || !a.qkv || !a.out || !a.dout || !a.lse || !a.dd || !a.dqkv || a.lddo % 8 != 0 ||
+  if (!shape_ok(a) || !a.qkv || !a.out32 || !a.dout || !a.lse || !a.dd || !a.dqkv || a.lddo % 8 != 0 ||
       a.lddqkv % 4 != 0)
     return hipErrorInvalidValue;
   return a.hd == 64 ? bwd_hd<64>(a, s) : bwd_hd<128>(a, s);

@@ -152,6 +152,23 @@ struct TcArgs {
 };
 hipError_t launch_lora_tc(const TcArgs& a, hipStream_t s);
 
+// Products over features for the LoRA down projections and gradients, several per
+// launch: out[t][n] = bf16(alpha * sum_k X[t][k] W[n][k]) for t < T, n < N.
+constexpr int kMaxFcJobs = 4;
+struct FcJob {
+  const uint16_t* X = nullptr; int32_t ldx = 0;   // bf16 [T, ldx], K contiguous, 16-byte aligned
+  const uint16_t* W = nullptr;                    // bf16 [N, K]
+  int32_t K = 0, N = 0;                           // K % 8 == 0
+  float alpha = 1.f;
+  uint16_t* out = nullptr; int32_t ldo = 0;       // bf16 [T, ldo]
+};
+struct FcArgs {
+  FcJob job[kMaxFcJobs]; int32_t n_jobs = 0;
+  int32_t T = 0;
+  float* partial = nullptr; int64_t partial_floats = 0;   // scratch for K runs
+};
+hipError_t launch_lora_fc(const FcArgs& a, hipStream_t s);
+
 // Causal grouped-query attention over batch sequences of S tokens, flash style.
 // qkv: bf16 [batch * S, ldqkv], q heads at columns h * hd, k heads from qd, v heads
 // from qd + kvd; q head h reads kv head h / (hq / hkv).  hd is 64 or 128.
@@ -160,7 +177,9 @@ struct AttnArgs {
   int32_t qd = 0, kvd = 0;
   int32_t batch = 0, S = 0, hq = 0, hkv = 0, hd = 0;
   float scale = 0.f;                                  // 1 / sqrt(hd)
-  uint16_t* out = nullptr; int32_t ldo = 0;           // O, bf16 [batch * S, ldo] (backward: read)
+  uint16_t* out = nullptr; int32_t ldo = 0;           // O, bf16 [batch * S, ldo]
+  float* out32 = nullptr;                             // O before rounding, float32, same layout (forward:
+                                                      // written if set; backward: read)
   float* lse = nullptr;                               // [batch * hq * S] base-2 log-sum-exp of scale * log2(e) * S
   const uint16_t* dout = nullptr; int32_t lddo = 0;   // backward: dO, bf16 like O
   float* dd = nullptr;                                // backward scratch [batch * hq * S]: rowsum(dO * O)

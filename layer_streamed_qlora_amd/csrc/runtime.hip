@@ -53,7 +53,7 @@ struct DevPlan {
   uint64_t total = 0;
   uint64_t slots = 0, ck = 0, xref = 0;
   uint64_t n1 = 0, qkv = 0, att = 0, hb = 0, n2 = 0, gu = 0, act = 0, rstd1 = 0, rstd2 = 0;
-  uint64_t hs = 0, gs = 0, lse = 0, dd = 0;
+  uint64_t hs = 0, gs = 0, lse = 0, dd = 0, o32 = 0;
   uint64_t dya = 0, dyb = 0, dh32 = 0, dh16 = 0, dgu = 0, datt = 0, dqkv = 0, dqkv32 = 0, dn32 = 0;
   uint64_t lora = 0, lora_per_layer = 0, partial = 0, partial_bytes = 0;
   uint64_t levels = 0, rope = 0;
@@ -90,6 +90,7 @@ DevPlan make_plan(const ls_config& c, const BlobLayout& L) {
   P.gs = take(2 * T * R7);
   P.lse = take(4 * T * (uint64_t)c.n_heads);
   P.dd = take(4 * T * (uint64_t)c.n_heads);
+  P.o32 = take(4 * T * qd);
   P.dya = take(2 * T * h);
   P.dyb = take(2 * T * h);
   P.dh32 = take(4 * T * h);
@@ -427,14 +428,14 @@ ls_status lora_down(ls_ctx* c, int l, const Dims& d, const uint16_t* x, int ldx,
   bool any = false;
   for (int p = p0; p < p0 + ng; ++p) any |= lora_active(c, l, p);
   if (!any) return LS_OK;
-  GemmArgs g;
-  g.A = x; g.sAm = ldx; g.sAk = 1;
-  g.B = lora_at(c, l, c->plan.a16[p0]); g.sBn = K; g.sBk = 1;
-  g.C = c->dp<uint16_t>(c->plan.hs) + p0 * d.r16; g.sCm = d.R7; g.sCn = 1; g.c_f32 = 0;
-  g.M = d.T; g.N = ng * d.r16; g.K = K; g.alpha = d.s;
-  g.ksplit = auto_split(g.M, g.N, g.K, 1); g.partial = c->dp<float>(c->plan.partial);
+  FcArgs a;
+  a.T = d.T;
+  a.partial = c->dp<float>(c->plan.partial); a.partial_floats = (int64_t)(c->plan.partial_bytes / 4);
+  FcJob& j = a.job[a.n_jobs++];
+  j.X = x; j.ldx = ldx; j.W = lora_at(c, l, c->plan.a16[p0]); j.K = K; j.N = ng * d.r16; j.alpha = d.s;
+  j.out = c->dp<uint16_t>(c->plan.hs) + p0 * d.r16; j.ldo = d.R7;
   KTimer kt(c, LS_KC_LORA, 2.0 * d.T * ng * d.r * K, 2.0 * d.T * K + 2.0 * ng * d.r * K + 2.0 * d.T * ng * d.r);
-  HIPCHK(c, launch_gemm_generic(g, c->cs));
+  HIPCHK(c, launch_lora_fc(a, c->cs));
   return LS_OK;
 }
 
@@ -451,11 +452,13 @@ AttnArgs attn_args(ls_ctx* c, const Dims& d, const uint16_t* qkv, uint16_t* out)
 }
 
 // Causal attention forward, O = softmax(c Q K^T) V, plus the per-row log-sum-exp the
-// backward uses to rebuild P.
-ls_status attn_fwd(ls_ctx* c, const Dims& d, const uint16_t* qkv, uint16_t* out) {
-  const double fl = 4.0 * d.batch * d.hq * (double)d.seq * (d.seq + 1) / 2 * d.hd;
-  KTimer kt(c, LS_KC_ATTN, fl, 2.0 * d.T * (d.qkvd + d.qd) + 4.0 * d.T * d.hq);
-  HIPCHK(c, launch_attn_fwd(attn_args(c, d, qkv, out), c->cs));
+// backward uses to rebuild P; out32 (nullable) keeps O before rounding for the backward.
+ls_status attn_fwd(ls_ctx* c, const Dims& d, const uint16_t* qkv, uint16_t* out, float* out32) {
+  const double fl = 6.0 * d.batch * d.hq * (double)d.seq * (d.seq + 1) / 2 * d.hd;   // scores twice
+  KTimer kt(c, LS_KC_ATTN, fl, 2.0 * d.T * (d.qkvd + d.qd) + 4.0 * d.T * d.hq + (out32 ? 4.0 * d.T * d.qd : 0.0));
+  AttnArgs a = attn_args(c, d, qkv, out);
+  a.out32 = out32;
+  HIPCHK(c, launch_attn_fwd(a, c->cs));
   return LS_OK;
 }
 
@@ -464,11 +467,12 @@ ls_status attn_fwd(ls_ctx* c, const Dims& d, const uint16_t* qkv, uint16_t* out)
 ls_status attn_bwd(ls_ctx* c, const Dims& d, const uint16_t* qkv, const uint16_t* out, const uint16_t* dout,
                    float* dqkv32) {
   AttnArgs a = attn_args(c, d, qkv, const_cast<uint16_t*>(out));
+  a.out32 = c->dp<float>(c->plan.o32);
   a.dout = dout; a.lddo = d.qd;
   a.dd = c->dp<float>(c->plan.dd);
   a.dqkv = dqkv32; a.lddqkv = d.qkvd;
   const double fl = 2.5 * 4.0 * d.batch * d.hq * (double)d.seq * (d.seq + 1) / 2 * d.hd;
-  KTimer kt(c, LS_KC_ATTN, fl, 2.0 * d.T * (d.qkvd + 2 * d.qd) + 4.0 * d.T * d.qkvd + 8.0 * d.T * d.hq);
+  KTimer kt(c, LS_KC_ATTN, fl, 2.0 * d.T * (d.qkvd + d.qd) + 4.0 * d.T * (d.qkvd + d.qd) + 8.0 * d.T * d.hq);
   HIPCHK(c, launch_attn_bwd(a, c->cs));
   return LS_OK;
 }
@@ -518,7 +522,7 @@ ls_status layer_forward(ls_ctx* c, int l, const uint8_t* blob, const Dims& d, co
               tb * d.h + wbytes(c, 0) + wbytes(c, 1) + wbytes(c, 2) + tb * d.qkvd);
     HIPCHK(c, launch_gemm_fwd(f, c->cs));
   }
-  { ls_status st = attn_fwd(c, d, qkv, att); if (st) return st; }
+  { ls_status st = attn_fwd(c, d, qkv, att, mode == MODE_RECOMPUTE ? c->dp<float>(c->plan.o32) : nullptr); if (st) return st; }
   if (lora) { ls_status st = lora_down(c, l, d, att, d.qd, LS_PROJ_O, 1, d.qd); if (st) return st; }
   {
     FwdArgs f;
@@ -585,17 +589,29 @@ ls_status layer_forward(ls_ctx* c, int l, const uint8_t* blob, const Dims& d, co
 
 // LoRA gradient products of projection p: Gs_p = s dY_p Bx16_p (bf16, into Gs),
 // dB_p = dY_p^T Hs_p, dA_p = Gs_p^T X_p (float32, written or accumulated).
-ls_status lora_grads_G(ls_ctx* c, int l, const Dims& d, int p, const uint16_t* dy, int lddy) {
-  if (!lora_active(c, l, p)) return LS_OK;
-  const ProjLayout& P = c->lay.p[p];
-  GemmArgs g;
-  g.A = dy; g.sAm = lddy; g.sAk = 1;
-  g.B = lora_at(c, l, c->plan.bxt16[p]); g.sBn = P.n_out; g.sBk = 1;
-  g.C = c->dp<uint16_t>(c->plan.gs) + p * d.r16; g.sCm = d.R7; g.sCn = 1; g.c_f32 = 0;
-  g.M = d.T; g.N = d.r16; g.K = P.n_out; g.alpha = d.s;
-  g.ksplit = auto_split(g.M, g.N, g.K, 1); g.partial = c->dp<float>(c->plan.partial);
-  KTimer kt(c, LS_KC_LORA, 2.0 * d.T * P.n_out * d.r, 2.0 * d.T * P.n_out + 2.0 * P.n_out * d.r + 2.0 * d.T * d.r);
-  HIPCHK(c, launch_gemm_generic(g, c->cs));
+// Gs_p = s dY_p Bx16_p (bf16, into Gs) for the n projections p0.. whose output
+// gradients sit side by side in dy (dY_p at dy + the sum of the earlier n_out), one launch.
+ls_status lora_grads_G(ls_ctx* c, int l, const Dims& d, int p0, int n, const uint16_t* dy, int lddy) {
+  FcArgs a;
+  a.T = d.T;
+  a.partial = c->dp<float>(c->plan.partial); a.partial_floats = (int64_t)(c->plan.partial_bytes / 4);
+  double flop = 0.0, bytes = 0.0;
+  int col = 0;
+  for (int i = 0; i < n; ++i) {
+    const int p = p0 + i;
+    const ProjLayout& P = c->lay.p[p];
+    if (lora_active(c, l, p)) {
+      FcJob& j = a.job[a.n_jobs++];
+      j.X = dy + col; j.ldx = lddy; j.W = lora_at(c, l, c->plan.bxt16[p]); j.K = P.n_out; j.N = d.r16;
+      j.alpha = d.s; j.out = c->dp<uint16_t>(c->plan.gs) + p * d.r16; j.ldo = d.R7;
+      flop += 2.0 * d.T * P.n_out * d.r;
+      bytes += 2.0 * d.T * P.n_out + 2.0 * P.n_out * d.r + 2.0 * d.T * d.r;
+    }
+    col += P.n_out;
+  }
+  if (a.n_jobs == 0) return LS_OK;
+  KTimer kt(c, LS_KC_LORA, flop, bytes);
+  HIPCHK(c, launch_lora_fc(a, c->cs));
   return LS_OK;
 }
 
@@ -670,7 +686,7 @@ ls_status layer_backward(ls_ctx* c, int l, const uint8_t* blob, const Dims& d, c
   auto bwd_flop = [&](int n_out, int n_in) { return 2.0 * d.T * n_out * n_in + 2.0 * d.T * n_in * d.r; };
 
   // ---- down: y = h + act W_d^T + LoRA
-  if ((st = lora_grads_G(c, l, d, LS_PROJ_DOWN, dy, d.h))) return st;
+  if ((st = lora_grads_G(c, l, d, LS_PROJ_DOWN, 1, dy, d.h))) return st;
   if ((st = lora_grads_AB(c, l, d, LS_PROJ_DOWN, 1, dy, d.h, act, d.I, beta))) return st;
   {
     BwdArgs b;
@@ -684,10 +700,7 @@ ls_status layer_backward(ls_ctx* c, int l, const uint8_t* blob, const Dims& d, c
     HIPCHK(c, launch_gemm_bwd(b, c->cs));
   }
   // ---- gate / up
-  for (int i = 0; i < 2; ++i) {
-    const int p = LS_PROJ_GATE + i;
-    if ((st = lora_grads_G(c, l, d, p, dgu + i * d.I, 2 * d.I))) return st;
-  }
+  if ((st = lora_grads_G(c, l, d, LS_PROJ_GATE, 2, dgu, 2 * d.I))) return st;
   if ((st = lora_grads_AB(c, l, d, LS_PROJ_GATE, 2, dgu, 2 * d.I, n2, d.h, beta))) return st;
   {
     BwdArgs b;
@@ -705,7 +718,7 @@ ls_status layer_backward(ls_ctx* c, int l, const uint8_t* blob, const Dims& d, c
     HIPCHK(c, launch_rmsnorm_bwd(dn32, nullptr, hb, g2, c->dp<float>(c->plan.rstd2), nullptr, dy, dh32, dh16, d.T, d.h, c->cs));
   }
   // ---- o: h = x + att W_o^T + LoRA
-  if ((st = lora_grads_G(c, l, d, LS_PROJ_O, dh16, d.h))) return st;
+  if ((st = lora_grads_G(c, l, d, LS_PROJ_O, 1, dh16, d.h))) return st;
   if ((st = lora_grads_AB(c, l, d, LS_PROJ_O, 1, dh16, d.h, att, d.qd, beta))) return st;
   {
     BwdArgs b;
@@ -724,10 +737,7 @@ ls_status layer_backward(ls_ctx* c, int l, const uint8_t* blob, const Dims& d, c
   }
   // ---- q, k, v
   const int cols[3] = {0, d.qd, d.qd + d.kvd};
-  for (int i = 0; i < 3; ++i) {
-    const int p = LS_PROJ_Q + i;
-    if ((st = lora_grads_G(c, l, d, p, dqkv + cols[i], d.qkvd))) return st;
-  }
+  if ((st = lora_grads_G(c, l, d, LS_PROJ_Q, 3, dqkv, d.qkvd))) return st;
   if ((st = lora_grads_AB(c, l, d, LS_PROJ_Q, 3, dqkv, d.qkvd, n1, d.h, beta))) return st;
   {
     BwdArgs b;

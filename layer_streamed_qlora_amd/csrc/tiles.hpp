@@ -29,6 +29,8 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
   f32x2_t v = {lo, hi};
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));   // RNE
 }
+// x rounded to bf16 (nearest even), as a float
+__device__ __forceinline__ float bf16_value(float x) { return __builtin_bit_cast(float, pack2(0.f, x) & 0xFFFF0000u); }
 __device__ __forceinline__ float bf_lo(uint32_t u) { return __builtin_bit_cast(float, u << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t u) { return __builtin_bit_cast(float, u & 0xFFFF0000u); }
 
