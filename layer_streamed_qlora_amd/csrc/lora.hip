@@ -16,8 +16,8 @@
 //
 // The other two products of the adapters, H = s x A^T and G = s dY B, contract over the
 // features of a token-major matrix ([T, K] against [N, K], N = r or a few stacked r):
-// `k_lora_fc` takes 128 tokens x 64 columns per workgroup over a run of K, the same
-// split and fixed-order sum, and writes bf16.
+// `k_lora_fc` takes 16 tokens x 64 columns per workgroup over all of K, its eight waves
+// on eighths of K added in a fixed order, and writes bf16.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -133,125 +133,76 @@ __global__ void __launch_bounds__(NT) k_lora_tc_reduce(TcKArgs k) {
 }
 
 // --------------------------------------------------------- feature contraction
-constexpr int FM = 128, FN = 64, FK = 64, FP = FK + 8;   // tokens, columns, K step, LDS pitch
+// v_mfma_f32_16x16x32_bf16: A[i][k] in lane i + 16 (k / 8), element k % 8; B[k][j] in
+// lane j + 16 (k / 8); C[i][j] in lane j + 16 (i / 4), register i % 4.
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+constexpr int FT = 16;     // tokens per workgroup
+constexpr int FN = 64;     // columns per workgroup (4 blocks of 16)
+constexpr int FU = 4;      // 32-wide K steps in flight per wave
+constexpr int FW = 8;      // waves per workgroup, each on 1/FW of K
 
 struct FcKArgs {
   FcArgs a;
   int32_t tile0[kMaxFcJobs + 1];
   int32_t n_tiles[kMaxFcJobs];
-  int32_t m_tiles = 0;
-  int32_t ksplit = 1, chunk = 0;
 };
 
-// 64 rows x 64 columns of a row-major bf16 matrix: 8 threads per row, 2 chunks each;
-// columns at or past klim and rows past the buffer's range read as zero.
-struct FcLoad {
-  uint4 v[2];
-  __device__ __forceinline__ void load(rsrc_t res, int ld, int row0, int col0, int klim) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int q = threadIdx.x + NT * i, row = q >> 3, cc = (q & 7) * 8;
-      const bool ok = col0 + cc < klim;
-      v[i] = bload16(res, ok ? ((uint32_t)(row0 + row) * (uint32_t)ld + (uint32_t)(col0 + cc)) * 2u : 0xFFFFFFF0u);
-    }
-  }
-  __device__ __forceinline__ void store(uint16_t* s) const {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int q = threadIdx.x + NT * i, row = q >> 3, cc = (q & 7) * 8;
-      *reinterpret_cast<uint4*>(s + row * FP + cc) = v[i];
-    }
-  }
-};
-
-// Destination column / token of result element (thread t, block jb, register v) of a
-// C tile at (t0, n0): C[i = token][j = column], lane j + 32 hh, register v holding
-// token 32 w + (v / 4) * 8 + 4 hh + v % 4.  Returns false if outside the job.
-__device__ __forceinline__ bool fc_pos(const FcJob& J, int T, int t0, int n0, int t, int jb, int v, int& tok, int& col) {
-  const int lane = t & 63, w = t >> 6;
-  tok = t0 + 32 * w + (v >> 2) * 8 + 4 * (lane >> 5) + (v & 3);
-  col = n0 + 32 * jb + (lane & 31);
-  return tok < T && col < J.N;
-}
-
-__global__ void __launch_bounds__(NT) k_lora_fc(FcKArgs k) {
-  __shared__ __align__(16) uint16_t sA[FM * FP];
-  __shared__ __align__(16) uint16_t sB[FN * FP];
+// Workgroup: 16 tokens x up to 64 columns over the whole of K.  Each of its FW waves
+// streams a contiguous 1/FW of K straight into MFMA operand registers (16 bytes per lane
+// per step); the partial products are added in LDS in wave order.
+__global__ void __launch_bounds__(FW * 64) k_lora_fc(FcKArgs k) {
+  __shared__ __align__(16) f32x4_t red[FW][4][64];    // [wave][column block][lane]
   const FcArgs& a = k.a;
-  const int flat = (int)blockIdx.x / k.ksplit, split = (int)blockIdx.x - flat * k.ksplit;
+  const int flat = blockIdx.x;
   int j = 0;
   while (j + 1 < a.n_jobs && flat >= k.tile0[j + 1]) ++j;
   const FcJob& J = a.job[j];
   const int local = flat - k.tile0[j];
   const int mt = local / k.n_tiles[j], nt = local - mt * k.n_tiles[j];
-  const int t0 = mt * FM, n0 = nt * FN;
-  const int kb = split * k.chunk, ke = min(J.K, kb + k.chunk);
+  const int t0 = mt * FT, n0 = nt * FN;
+  const int nb_used = min(4, (J.N - n0 + 15) / 16);
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int row = lane & 15, kg = (lane >> 4) * 8;
   const rsrc_t rx = make_rsrc(J.X + (int64_t)t0 * J.ldx, ((uint64_t)(a.T - t0) * J.ldx) * 2);
   const rsrc_t rw = make_rsrc(J.W + (int64_t)n0 * J.K, ((uint64_t)(J.N - n0) * J.K) * 2);
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, l32 = lane & 31, hh = lane >> 5;
-  const bool two = n0 + 32 < J.N;
-  f32x16_t acc[2] = {f32x16_t{}, f32x16_t{}};
-  FcLoad la0, la1, lb;
-  const int nst = ke > kb ? (ke - kb + FK - 1) / FK : 0;
-  if (nst > 0) {
-    la0.load(rx, J.ldx, 0, kb, ke);
-    la1.load(rx, J.ldx, 64, kb, ke);
-    lb.load(rw, J.K, 0, kb, ke);
-  }
-  for (int st = 0; st < nst; ++st) {
-    __syncthreads();
-    la0.store(sA);
-    la1.store(sA + 64 * FP);
-    lb.store(sB);
-    __syncthreads();
-    if (st + 1 < nst) {
-      const int kk = kb + (st + 1) * FK;
-      la0.load(rx, J.ldx, 0, kk, ke);
-      la1.load(rx, J.ldx, 64, kk, ke);
-      lb.load(rw, J.K, 0, kk, ke);
+  const uint32_t xoff = (uint32_t)row * (uint32_t)J.ldx * 2u;
+  const int steps = (J.K + 31) / 32;
+  const int per = (steps + FW - 1) / FW;
+  const int s_beg = w * per, s_end = min(steps, s_beg + per);
+  f32x4_t acc[4] = {f32x4_t{}, f32x4_t{}, f32x4_t{}, f32x4_t{}};
+  for (int s = s_beg; s < s_end; s += FU) {
+    bf16x8_t av[FU], bv[FU][4];
+#pragma unroll
+    for (int u = 0; u < FU; ++u) {
+      const int kk = (s + u) * 32 + kg;
+      const bool ok = s + u < s_end && kk < J.K;
+      av[u] = as_bf8(bload16(rx, ok ? xoff + (uint32_t)kk * 2u : 0xFFFFFFF0u));
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+        bv[u][nb] = as_bf8(bload16(rw, (ok && nb < nb_used) ? ((uint32_t)(16 * nb + row) * (uint32_t)J.K + (uint32_t)kk) * 2u
+                                                            : 0xFFFFFFF0u));
     }
 #pragma unroll
-    for (int s = 0; s < FK / 16; ++s) {
-      const bf16x8_t af = *reinterpret_cast<const bf16x8_t*>(sA + (32 * w + l32) * FP + 16 * s + 8 * hh);
-      acc[0] = mfma(af, *reinterpret_cast<const bf16x8_t*>(sB + l32 * FP + 16 * s + 8 * hh), acc[0]);
-      if (two) acc[1] = mfma(af, *reinterpret_cast<const bf16x8_t*>(sB + (32 + l32) * FP + 16 * s + 8 * hh), acc[1]);
-    }
+    for (int u = 0; u < FU; ++u)
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+        if (nb < nb_used) acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[u], bv[u][nb], acc[nb], 0, 0, 0);
   }
-  if (k.ksplit == 1) {
 #pragma unroll
-    for (int jb = 0; jb < 2; ++jb)
+  for (int nb = 0; nb < 4; ++nb) red[w][nb][lane] = acc[nb];
+  __syncthreads();
+  if (w >= nb_used) return;
+  const int nb = w;
+  f32x4_t sum = red[0][nb][lane];
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        int tok, col;
-        if (fc_pos(J, a.T, t0, n0, threadIdx.x, jb, v, tok, col))
-          J.out[(int64_t)tok * J.ldo + col] = (uint16_t)(pack2(J.alpha * acc[jb][v], 0.f) & 0xFFFFu);
-      }
-    return;
+  for (int ww = 1; ww < FW; ++ww) sum += red[ww][nb][lane];
+  const int col = n0 + 16 * nb + (lane & 15);
+  if (col >= J.N) return;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int tok = t0 + 4 * (lane >> 4) + v;
+    if (tok < a.T) J.out[(int64_t)tok * J.ldo + col] = (uint16_t)(pack2(J.alpha * sum[v], 0.f) & 0xFFFFu);
   }
-  float* part = a.partial + ((int64_t)flat * k.ksplit + split) * (FM * FN);
-#pragma unroll
-  for (int jb = 0; jb < 2; ++jb)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      int tok, col;
-      if (fc_pos(J, a.T, t0, n0, threadIdx.x, jb, v, tok, col)) part[(jb * 16 + v) * NT + threadIdx.x] = acc[jb][v];
-    }
-}
-
-__global__ void __launch_bounds__(NT) k_lora_fc_reduce(FcKArgs k) {
-  const FcArgs& a = k.a;
-  const int flat = (int)blockIdx.x >> 5, e = (int)blockIdx.x & 31;
-  int j = 0;
-  while (j + 1 < a.n_jobs && flat >= k.tile0[j + 1]) ++j;
-  const FcJob& J = a.job[j];
-  const int local = flat - k.tile0[j];
-  const int mt = local / k.n_tiles[j], nt = local - mt * k.n_tiles[j];
-  int tok, col;
-  if (!fc_pos(J, a.T, mt * FM, nt * FN, threadIdx.x, e >> 4, e & 15, tok, col)) return;
-  const float* src = a.partial + (int64_t)flat * k.ksplit * (FM * FN) + e * NT + threadIdx.x;
-  float sum = 0.f;
-  for (int sp = 0; sp < k.ksplit; ++sp) sum += src[(int64_t)sp * (FM * FN)];
-  J.out[(int64_t)tok * J.ldo + col] = (uint16_t)(pack2(J.alpha * sum, 0.f) & 0xFFFFu);
 }
 
 }  // namespace
@@ -296,31 +247,20 @@ hipError_t launch_lora_fc(const FcArgs& a, hipStream_t s) {
   if (a.n_jobs > kMaxFcJobs) return hipErrorInvalidValue;
   FcKArgs k;
   k.a = a;
-  k.m_tiles = (a.T + FM - 1) / FM;
-  int tiles = 0, kmax = 0;
-  int64_t max_ld = 1;
+  const int m_tiles = (a.T + FT - 1) / FT;
+  int tiles = 0;
   for (int j = 0; j < a.n_jobs; ++j) {
     const FcJob& J = a.job[j];
     if (!J.X || !J.W || !J.out || J.K <= 0 || J.N <= 0 || J.K % 8 || J.ldx % 8 || J.ldx < J.K ||
-        (reinterpret_cast<uintptr_t>(J.X) & 15) || (reinterpret_cast<uintptr_t>(J.W) & 15))
+        (reinterpret_cast<uintptr_t>(J.X) & 15) || (reinterpret_cast<uintptr_t>(J.W) & 15) ||
+        (uint64_t)FN * J.K * 2 >= (1ull << 31) || (uint64_t)FT * J.ldx * 2 + (uint64_t)J.K * 2 >= (1ull << 31))
       return hipErrorInvalidValue;
     k.tile0[j] = tiles;
     k.n_tiles[j] = (J.N + FN - 1) / FN;
-    tiles += k.m_tiles * k.n_tiles[j];
-    kmax = std::max(kmax, J.K);
-    max_ld = std::max<int64_t>(max_ld, std::max<int64_t>(J.ldx, J.K));
+    tiles += m_tiles * k.n_tiles[j];
   }
   k.tile0[a.n_jobs] = tiles;
-  if ((int64_t)(a.T + FM) * max_ld * 2 >= (int64_t)1 << 31) return hipErrorInvalidValue;
-  // K runs: about 1024 workgroups, at least two K steps each, within the partial buffer
-  int ks = std::max(1, std::min(64, 1024 / std::max(1, tiles)));
-  ks = std::min(ks, std::max(1, kmax / (2 * FK)));
-  while (ks > 1 && (int64_t)tiles * ks * FM * FN > a.partial_floats) --ks;
-  if (!a.partial) ks = 1;
-  k.chunk = ((kmax + ks - 1) / ks + FK - 1) / FK * FK;
-  k.ksplit = (kmax + k.chunk - 1) / k.chunk;
-  hipLaunchKernelGGL(k_lora_fc, dim3((unsigned)(tiles * k.ksplit)), dim3(NT), 0, s, k);
-  if (k.ksplit > 1) hipLaunchKernelGGL(k_lora_fc_reduce, dim3((unsigned)(tiles * 32)), dim3(NT), 0, s, k);
+  hipLaunchKernelGGL(k_lora_fc, dim3((unsigned)tiles), dim3(FW * 64), 0, s, k);
   return hipGetLastError();
 }
 

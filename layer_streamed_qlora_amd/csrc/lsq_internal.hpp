@@ -165,7 +165,6 @@ struct FcJob {
 struct FcArgs {
   FcJob job[kMaxFcJobs]; int32_t n_jobs = 0;
   int32_t T = 0;
-  float* partial = nullptr; int64_t partial_floats = 0;   // scratch for K runs
 };
 hipError_t launch_lora_fc(const FcArgs& a, hipStream_t s);
 

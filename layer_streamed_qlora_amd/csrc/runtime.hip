@@ -430,7 +430,6 @@ ls_status lora_down(ls_ctx* c, int l, const Dims& d, const uint16_t* x, int ldx,
   if (!any) return LS_OK;
   FcArgs a;
   a.T = d.T;
-  a.partial = c->dp<float>(c->plan.partial); a.partial_floats = (int64_t)(c->plan.partial_bytes / 4);
   FcJob& j = a.job[a.n_jobs++];
   j.X = x; j.ldx = ldx; j.W = lora_at(c, l, c->plan.a16[p0]); j.K = K; j.N = ng * d.r16; j.alpha = d.s;
   j.out = c->dp<uint16_t>(c->plan.hs) + p0 * d.r16; j.ldo = d.R7;
@@ -594,7 +593,6 @@ ls_status layer_forward(ls_ctx* c, int l, const uint8_t* blob, const Dims& d, co
 ls_status lora_grads_G(ls_ctx* c, int l, const Dims& d, int p0, int n, const uint16_t* dy, int lddy) {
   FcArgs a;
   a.T = d.T;
-  a.partial = c->dp<float>(c->plan.partial); a.partial_floats = (int64_t)(c->plan.partial_bytes / 4);
   double flop = 0.0, bytes = 0.0;
   int col = 0;
   for (int i = 0; i < n; ++i) {
