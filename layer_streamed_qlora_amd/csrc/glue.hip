@@ -82,6 +82,117 @@ __global__ void __launch_bounds__(256) k_rmsnorm_bwd(const float* dn, const XT* 
   }
 }
 
+// Row-in-registers forms of the two kernels above for rows of at most 8192 elements
+// (D % 8 == 0): 16-byte accesses, 8 consecutive elements per thread per chunk, one read
+// of every operand.
+constexpr int kRowChunks = 4;
+
+__device__ __forceinline__ void ld8(const uint16_t* p, float (&v)[8]) {
+  const uint4 u = *reinterpret_cast<const uint4*>(p);
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    v[2 * j] = __builtin_bit_cast(float, w[j] << 16);
+    v[2 * j + 1] = __builtin_bit_cast(float, w[j] & 0xFFFF0000u);
+  }
+}
+__device__ __forceinline__ void ld8(const float* p, float (&v)[8]) {
+  const float4 a = *reinterpret_cast<const float4*>(p), b = *reinterpret_cast<const float4*>(p + 4);
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+__device__ __forceinline__ void st8(uint16_t* p, const float (&v)[8]) {
+  uint32_t w[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    f32x2_t t = {v[2 * j], v[2 * j + 1]};
+    w[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector(t, bf16x2_t));
+  }
+  *reinterpret_cast<uint4*>(p) = make_uint4(w[0], w[1], w[2], w[3]);
+}
+__device__ __forceinline__ void st8(float* p, const float (&v)[8]) {
+  *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+  *reinterpret_cast<float4*>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
+}
+
+template <class XT>
+__global__ void __launch_bounds__(256) k_rmsnorm_fwd_v(const XT* x, const uint16_t* g, uint16_t* y, float* rstd,
+                                                       int D, float eps) {
+  __shared__ float red[4];
+  const int64_t row = blockIdx.x;
+  const XT* xr = x + row * D;
+  float xv[kRowChunks][8];
+  float ss = 0.f;
+#pragma unroll
+  for (int c = 0; c < kRowChunks; ++c) {
+    const int i0 = (c * 256 + threadIdx.x) * 8;
+    if (i0 < D) {
+      ld8(xr + i0, xv[c]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ss += xv[c][e] * xv[c][e];
+    }
+  }
+  ss = block_sum<256>(ss, red);
+  const float r = 1.0f / sqrtf(ss / (float)D + eps);
+  if (threadIdx.x == 0 && rstd) rstd[row] = r;
+#pragma unroll
+  for (int c = 0; c < kRowChunks; ++c) {
+    const int i0 = (c * 256 + threadIdx.x) * 8;
+    if (i0 < D) {
+      float gv[8], o[8];
+      ld8(g + i0, gv);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = xv[c][e] * r * gv[e];
+      st8(y + row * D + i0, o);
+    }
+  }
+}
+
+template <class XT>
+__global__ void __launch_bounds__(256) k_rmsnorm_bwd_v(const float* dn, const XT* x, const uint16_t* g,
+                                                       const float* rstd, const float* dres32, const uint16_t* dres16,
+                                                       float* dx32, uint16_t* dx16, int D) {
+  __shared__ float red[4];
+  const int64_t row = blockIdx.x;
+  float dv[kRowChunks][8], xv[kRowChunks][8];
+  float s = 0.f;
+#pragma unroll
+  for (int c = 0; c < kRowChunks; ++c) {
+    const int i0 = (c * 256 + threadIdx.x) * 8;
+    if (i0 < D) {
+      float gv[8];
+      ld8(dn + row * D + i0, dv[c]);
+      ld8(x + row * D + i0, xv[c]);
+      ld8(g + i0, gv);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s += dv[c][e] * gv[e] * xv[c][e];
+    }
+  }
+  s = block_sum<256>(s, red);
+  const float r = rstd[row];
+  const float cc = r * r * r / (float)D * s;
+#pragma unroll
+  for (int c = 0; c < kRowChunks; ++c) {
+    const int i0 = (c * 256 + threadIdx.x) * 8;
+    if (i0 < D) {
+      float gv[8], v[8], rv[8];
+      ld8(g + i0, gv);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = r * gv[e] * dv[c][e] - cc * xv[c][e];
+      if (dres32) {
+        ld8(dres32 + row * D + i0, rv);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] += rv[e];
+      } else if (dres16) {
+        ld8(dres16 + row * D + i0, rv);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] += rv[e];
+      }
+      if (dx32) st8(dx32 + row * D + i0, v);
+      if (dx16) st8(dx16 + row * D + i0, v);
+    }
+  }
+}
+
 // float32 -> bf16 with the inverse rotation on the first nh heads; one thread per
 // (token, column pair or lone column)
 __global__ void k_rope_bwd_convert(const float* src, uint16_t* dst, int ld, int64_t T, int seq, int nh, int hd,
@@ -106,6 +217,48 @@ __global__ void k_rope_bwd_convert(const float* src, uint16_t* dst, int ld, int6
   } else {
     const int col = nh * hd + (c - rope_pairs);
     d[col] = tobf(s[col]);
+  }
+}
+
+// Same, 4 rotated column pairs or 8 plain columns per thread (hd % 8 == 0, ld % 8 == 0)
+__global__ void k_rope_bwd_convert_v(const float* src, uint16_t* dst, int ld, int64_t T, int seq, int nh, int hd,
+                                     const float2* tab) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int half = hd / 2, gp = half / 4;
+  const int rope_groups = nh * gp;
+  const int per_row = rope_groups + (ld - nh * hd) / 8;
+  if (idx >= T * per_row) return;
+  const int64_t t = idx / per_row;
+  const int c = (int)(idx % per_row);
+  const float* sr = src + t * ld;
+  uint16_t* dr = dst + t * ld;
+  if (c < rope_groups) {
+    const int h = c / gp, i = (c % gp) * 4;
+    const int col = h * hd + i;
+    const float4 d1 = *reinterpret_cast<const float4*>(sr + col);
+    const float4 d2 = *reinterpret_cast<const float4*>(sr + col + half);
+    const float4* tp = reinterpret_cast<const float4*>(tab + (int64_t)(t % seq) * half + i);
+    const float4 c01 = tp[0], c23 = tp[1];                 // (cos, sin) of pairs i .. i+3
+    const float a1[4] = {d1.x, d1.y, d1.z, d1.w}, a2[4] = {d2.x, d2.y, d2.z, d2.w};
+    const float cs[4] = {c01.x, c01.z, c23.x, c23.z}, sn[4] = {c01.y, c01.w, c23.y, c23.w};
+    uint32_t o1[2], o2[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      f32x2_t u = {a1[2 * j] * cs[2 * j] + a2[2 * j] * sn[2 * j], a1[2 * j + 1] * cs[2 * j + 1] + a2[2 * j + 1] * sn[2 * j + 1]};
+      f32x2_t v = {a2[2 * j] * cs[2 * j] - a1[2 * j] * sn[2 * j], a2[2 * j + 1] * cs[2 * j + 1] - a1[2 * j + 1] * sn[2 * j + 1]};
+      o1[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector(u, bf16x2_t));
+      o2[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+    }
+    *reinterpret_cast<uint2*>(dr + col) = make_uint2(o1[0], o1[1]);
+    *reinterpret_cast<uint2*>(dr + col + half) = make_uint2(o2[0], o2[1]);
+  } else {
+    const int col = nh * hd + (c - rope_groups) * 8;
+    const float4 a = *reinterpret_cast<const float4*>(sr + col), b = *reinterpret_cast<const float4*>(sr + col + 4);
+    f32x2_t p0 = {a.x, a.y}, p1 = {a.z, a.w}, p2 = {b.x, b.y}, p3 = {b.z, b.w};
+    *reinterpret_cast<uint4*>(dr + col) = make_uint4(__builtin_bit_cast(uint32_t, __builtin_convertvector(p0, bf16x2_t)),
+                                                     __builtin_bit_cast(uint32_t, __builtin_convertvector(p1, bf16x2_t)),
+                                                     __builtin_bit_cast(uint32_t, __builtin_convertvector(p2, bf16x2_t)),
+                                                     __builtin_bit_cast(uint32_t, __builtin_convertvector(p3, bf16x2_t)));
   }
 }
 
@@ -175,8 +328,14 @@ static inline unsigned blocks_for(int64_t n, int t) { return (unsigned)((n + t -
 hipError_t launch_rmsnorm_fwd(const uint16_t* x16, const float* x32, const uint16_t* g, uint16_t* y, float* rstd,
                               int32_t T, int32_t D, float eps, hipStream_t s) {
   if (T <= 0) return hipSuccess;
-  if (x32) hipLaunchKernelGGL(k_rmsnorm_fwd<float>, dim3(T), dim3(256), 0, s, x32, g, y, rstd, D, eps);
-  else hipLaunchKernelGGL(k_rmsnorm_fwd<uint16_t>, dim3(T), dim3(256), 0, s, x16, g, y, rstd, D, eps);
+  const bool v = D % 8 == 0 && D <= 256 * 8 * kRowChunks;
+  if (x32) {
+    if (v) hipLaunchKernelGGL(k_rmsnorm_fwd_v<float>, dim3(T), dim3(256), 0, s, x32, g, y, rstd, D, eps);
+    else hipLaunchKernelGGL(k_rmsnorm_fwd<float>, dim3(T), dim3(256), 0, s, x32, g, y, rstd, D, eps);
+  } else {
+    if (v) hipLaunchKernelGGL(k_rmsnorm_fwd_v<uint16_t>, dim3(T), dim3(256), 0, s, x16, g, y, rstd, D, eps);
+    else hipLaunchKernelGGL(k_rmsnorm_fwd<uint16_t>, dim3(T), dim3(256), 0, s, x16, g, y, rstd, D, eps);
+  }
   return hipGetLastError();
 }
 
@@ -184,15 +343,26 @@ hipError_t launch_rmsnorm_bwd(const float* dn, const uint16_t* x16, const float*
                               const float* rstd, const float* dres32, const uint16_t* dres16, float* dx32,
                               uint16_t* dx16, int32_t T, int32_t D, hipStream_t s) {
   if (T <= 0) return hipSuccess;
-  if (x32)
-    hipLaunchKernelGGL(k_rmsnorm_bwd<float>, dim3(T), dim3(256), 0, s, dn, x32, g, rstd, dres32, dres16, dx32, dx16, D);
-  else
-    hipLaunchKernelGGL(k_rmsnorm_bwd<uint16_t>, dim3(T), dim3(256), 0, s, dn, x16, g, rstd, dres32, dres16, dx32, dx16, D);
+  const bool v = D % 8 == 0 && D <= 256 * 8 * kRowChunks;
+  if (x32) {
+    if (v) hipLaunchKernelGGL(k_rmsnorm_bwd_v<float>, dim3(T), dim3(256), 0, s, dn, x32, g, rstd, dres32, dres16, dx32, dx16, D);
+    else hipLaunchKernelGGL(k_rmsnorm_bwd<float>, dim3(T), dim3(256), 0, s, dn, x32, g, rstd, dres32, dres16, dx32, dx16, D);
+  } else {
+    if (v) hipLaunchKernelGGL(k_rmsnorm_bwd_v<uint16_t>, dim3(T), dim3(256), 0, s, dn, x16, g, rstd, dres32, dres16, dx32, dx16, D);
+    else hipLaunchKernelGGL(k_rmsnorm_bwd<uint16_t>, dim3(T), dim3(256), 0, s, dn, x16, g, rstd, dres32, dres16, dx32, dx16, D);
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_rope_bwd_convert(const float* src, uint16_t* dst, int32_t ld, int32_t T, int32_t seq, int32_t nh,
                                    int32_t hd, const float2* tab, hipStream_t s) {
+  if (hd % 8 == 0 && ld % 8 == 0 && (ld - nh * hd) % 8 == 0) {
+    const int64_t n = (int64_t)T * ((int64_t)nh * (hd / 8) + (ld - nh * hd) / 8);
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_rope_bwd_convert_v, dim3(blocks_for(n, 256)), dim3(256), 0, s, src, dst, ld, (int64_t)T, seq,
+                       nh, hd, tab);
+    return hipGetLastError();
+  }
   const int64_t per_row = (int64_t)nh * (hd / 2) + (ld - nh * hd);
   const int64_t n = (int64_t)T * per_row;
   if (n <= 0) return hipSuccess;
