@@ -76,6 +76,8 @@ __device__ __forceinline__ void dequant8(uint32_t codes, float am, const float2*
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 constexpr uint32_t kOOB = 0xFFFFFFF0u;   // offset past every buffer: the load returns 0
+// s_waitcnt operand: vector-memory count 0, the export and LDS/scalar counts unconstrained
+constexpr int kWaitVm0 = 0x0F70;
 
 __device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint64_t bytes) {
   const uint32_t n = bytes > 0xFFFFFFF0ull ? 0xFFFFFFF0u : (uint32_t)bytes;
@@ -375,6 +377,10 @@ struct AFast {
   }
   __device__ __forceinline__ void load_q(uint32_t col0, int q) {   // col0 in elements
     v[q] = bload16s(res, voff[q], col0 * 2u);
+  }
+  // as load_q, or zeros (an out-of-range offset) when `zero` (wave-uniform)
+  __device__ __forceinline__ void load_q_or_zero(uint32_t col0, int q, bool zero) {
+    v[q] = bload16s(res, zero ? kOOB : voff[q], zero ? 0u : col0 * 2u);
   }
   __device__ __forceinline__ void store_q(uint16_t* s, int q) const {
     const int c = threadIdx.x + NT_FAST * q;
@@ -1034,23 +1040,38 @@ __global__ void __launch_bounds__(NT_FAST, 1) k_gemm_fwd_fast(FwdArgs args, int 
 #pragma unroll
   for (int q = 0; q < 4; ++q) ra.load_q(0, q);
   ws.load(rw, 0);
-  if (BK < K) ws.load(rw_next, BK);
+  ws.load(rw_next, BK < K ? BK : 0);   // unconditional, like the prefetches in the loop
+  // Drain the prologue's loads once: otherwise their order here, merged into the loop
+  // head, sets the wait counts of every iteration.
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
   __syncthreads();
-  for (int it = 0; it < n_iter; ++it) {
+  // Iteration it dequantises W tile it from R and then reloads R with tile it + 2.
+  // The two register sets alternate by unrolling two iterations: a copy between them
+  // would wait on the loads still in flight into the source.  Every prefetch is issued
+  // on every path (the compiler counts only loads that are always issued when it
+  // places its waits; a skipped-load branch makes it wait for every load in flight),
+  // and the iteration count is rounded up to even: an activation tile past K loads as
+  // zeros (out-of-range offset), W past K re-reads the last tile, so the padding
+  // iteration adds exact zeros.
+  const int k_last = K - BK;
+  auto step = [&](int it, typename WFwdFast<FMT>::Regs& R) {
     const int cur = it & 1;
     uint16_t* na = sm.u.k.a[cur ^ 1];
     uint16_t* nw = sm.u.k.w[cur ^ 1];
     const int k_next = (it + 1) * BK;
-    const bool more = k_next < K;
-    const float am = FMT == WF_BF16 ? 0.f : ws.absmax(rw);
+    const bool past = k_next >= K;
+    const float am = FMT == WF_BF16 ? 0.f : ws.absmax(R);
     mma_stage<NT_FAST>(sm.u.k.a[cur], sm.u.k.w[cur], acc, [&](int q) {
       ra.store_q(na, q);
-      if (more) ra.load_q((uint32_t)k_next, q);
-      ws.store_part(rw, nw, sm.lut2, q, am);
+      ra.load_q_or_zero((uint32_t)k_next, q, past);
+      ws.store_part(R, nw, sm.lut2, q, am);
     });
-    rw = rw_next;
-    if (k_next + BK < K) ws.load(rw_next, k_next + BK);
+    ws.load(R, k_next + BK < k_last ? k_next + BK : k_last);
     __syncthreads();
+  };
+  for (int it = 0; it < n_iter; it += 2) {
+    step(it, rw);
+    step(it + 1, rw_next);
   }
 
   if constexpr (PAIRED) {
@@ -1121,9 +1142,9 @@ __global__ void __launch_bounds__(NT_FAST, 1) k_gemm_bwd_fast(BwdArgs args, int 
   typename WBwdFast<FMT>::Regs rw, rw_next;
   WBwdFast<FMT>::clear(rw);
   WBwdFast<FMT>::clear(rw_next);
+  // loads past the last tile re-read the last tile (see the forward kernel)
   auto load_w = [&](typename WBwdFast<FMT>::Regs& R, int t) {
-    if (t >= total_k) return;
-    int s, k0; seg_of(t, s, k0);
+    int s, k0; seg_of(t < total_k ? t : total_k - 1, s, k0);
     ws.load(R, args.seg[s].w, j0, k0);
   };
   {
@@ -1133,25 +1154,31 @@ __global__ void __launch_bounds__(NT_FAST, 1) k_gemm_bwd_fast(BwdArgs args, int 
   }
   load_w(rw, 0);
   load_w(rw_next, 1);
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);   // see the forward kernel
   __syncthreads();
   const int n_iter = total_k + 1;
-  for (int it = 0; it < n_iter; ++it) {
+  // as in the forward kernel: two register sets for W alternating without copies,
+  // prefetches on every path, an even iteration count with a zero padding tile
+  auto step = [&](int it, typename WBwdFast<FMT>::Regs& R) {
     const int cur = it & 1;
     uint16_t* na = sm.u.k.a[cur ^ 1];
     uint16_t* nw = sm.u.k.w[cur ^ 1];
-    const bool more = it + 1 < total_k;
-    uint32_t col = 0;
-    if (more) { int s, k0; seg_of(it + 1, s, k0); col = (uint32_t)(args.seg[s].a_col0 + k0); }
-    const float a0 = FMT == WF_BF16 ? 0.f : ws.absmax(rw, 0);
-    const float a1 = FMT == WF_BF16 ? 0.f : ws.absmax(rw, 1);
+    const bool past = it + 1 >= total_k;
+    uint32_t col;
+    { int s, k0; seg_of(past ? total_k - 1 : it + 1, s, k0); col = (uint32_t)(args.seg[s].a_col0 + k0); }
+    const float a0 = FMT == WF_BF16 ? 0.f : ws.absmax(R, 0);
+    const float a1 = FMT == WF_BF16 ? 0.f : ws.absmax(R, 1);
     mma_stage<NT_FAST>(sm.u.k.a[cur], sm.u.k.w[cur], acc, [&](int q) {
       ra.store_q(na, q);
-      if (more) ra.load_q(col, q);
-      ws.store_part(rw, nw, sm.lut2, q, a0, a1);
+      ra.load_q_or_zero(col, q, past);
+      ws.store_part(R, nw, sm.lut2, q, a0, a1);
     });
-    rw = rw_next;
-    load_w(rw_next, it + 2);
+    load_w(R, it + 2);
     __syncthreads();
+  };
+  for (int it = 0; it < n_iter; it += 2) {
+    step(it, rw);
+    step(it + 1, rw_next);
   }
 
   Epi E;
@@ -1200,7 +1227,7 @@ hipError_t launch_gemm_fwd(const FwdArgs& a, hipStream_t s) {
   for (int g = 0; g < a.n_groups; ++g) n_tiles += (a.g[g].w.n_out + BN - 1) / BN;
   const int total = m_tiles * n_tiles;
   const int padded = (total + 7) / 8 * 8;
-  const bool fast = (a.K % BK) == 0 && (a.ldx % 8) == 0;
+  const bool fast = (a.K % BK) == 0 && a.K >= BK && (a.ldx % 8) == 0;
   if (a.swiglu) {
     // paired gate | up tiles: same shape, adjacent low-rank columns, 2 kx <= 64
     if (!fast || a.n_groups != 2 || a.g[0].w.n_out != a.g[1].w.n_out || a.g[0].w.n_in != a.g[1].w.n_in ||
@@ -1232,8 +1259,9 @@ hipError_t launch_gemm_bwd(const BwdArgs& a, hipStream_t s) {
   const int padded = (total + 7) / 8 * 8;
   // fast path: whole NF4 blocks per W row, every segment a whole number of K tiles,
   // 16-byte aligned activation rows
-  bool fast = (a.N % BK) == 0 && (a.lddy % 8) == 0;
-  for (int sg = 0; sg < a.n_segs; ++sg) fast = fast && (a.seg[sg].w.n_out % BK) == 0 && (a.seg[sg].a_col0 % 8) == 0;
+  bool fast = (a.N % BK) == 0 && (a.lddy % 8) == 0 && a.n_segs > 0;
+  for (int sg = 0; sg < a.n_segs; ++sg)
+    fast = fast && (a.seg[sg].w.n_out % BK) == 0 && a.seg[sg].w.n_out >= BK && (a.seg[sg].a_col0 % 8) == 0;
   // The kernel takes the first 64 low-rank columns as one extra K tile; wider
   // low-rank terms (stacked q|k|v or gate|up at rank > 16) add the remaining columns
   // into the float32 result with a second, generic MFMA GEMM.
