@@ -35,4 +35,7 @@ model   LoRA projection and the Llama-style decoder layer, forward and hand-deri
         backward, in float64.
 stack   the layer stack (forward with checkpoints, recompute backward), the
         adapters-off reference pass, and a simulated two-slot streaming pool.
+optim   the AdamW update of the adapters (decoupled, lr-scaled weight decay).
+adapters  adapter file names (PEFT convention), the safetensors container, the
+        integrity record (per-tensor CRC-32) and a checker of a file against a stack.
 """
