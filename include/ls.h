@@ -80,6 +80,8 @@ typedef struct ls_config {
                               parity reference for the streamed mode) */
   uint64_t vram_budget;    /* bytes the plan may use; 0 = free device memory */
   int32_t profile;         /* 1 = time copies and per-layer compute with HIP events */
+  int32_t adamw;           /* 1 = also plan float32 AdamW moments (m and v) for every
+                              adapter of lora_mask and enable ls_adamw_step */
 } ls_config;
 
 /* Host-side source weights for one layer (bf16 bit patterns, host pointers). */
@@ -96,7 +98,8 @@ enum {
   LS_KC_ATTN = 2,     /* attention products and softmax */
   LS_KC_LORA = 3,     /* LoRA down projection and dA / dB / G products, operand conversion */
   LS_KC_GLUE = 4,     /* RMSNorm, rotary embedding, SwiGLU */
-  LS_KC_N = 5
+  LS_KC_OPTIM = 5,    /* AdamW update of the adapters (ls_adamw_step) */
+  LS_KC_N = 6
 };
 
 typedef struct ls_stats {
@@ -228,6 +231,87 @@ ls_status ls_pack_nf4(const uint16_t* w, uint64_t numel, int32_t double_quant, i
  * slot, then the dequant kernel).  Synchronous.  For checking the encoding.
  */
 ls_status ls_read_weight(ls_ctx* ctx, int32_t layer, int32_t proj, void* out);
+
+/* ---------------------------------------------------------------------------
+ * Training-loop closure: optimizer step and adapter files.
+ * ------------------------------------------------------------------------- */
+
+/*
+ * AdamW hyperparameters.  Only the adapters train ("Fine-Tuning an 8B Parameter Model
+ * on a 4 GB Laptop GPU", section "LoRA and QLoRA: Train a Fraction of the
+ * Parameters") and Adam keeps two float32 tensors per trained value (same page, the
+ * "Optimizer states" item of why training is memory-hungry).  The update is AdamW
+ * with learning-rate-scaled decoupled decay, for every element:
+ *     p <- p (1 - lr weight_decay)
+ *     m <- beta1 m + (1 - beta1) g ;  v <- beta2 v + (1 - beta2) g^2
+ *     p <- p - (lr / (1 - beta1^step)) m / (sqrt(v) / sqrt(1 - beta2^step) + eps)
+ */
+typedef struct ls_adamw {
+  float lr;            /* >= 0 */
+  float beta1, beta2;  /* in [0, 1) */
+  float eps;           /* > 0 */
+  float weight_decay;  /* >= 0 */
+  int32_t step;        /* 1-based step number t of this update (bias correction) */
+} ls_adamw;
+
+/*
+ * ls_adamw_step — enqueue one AdamW update of every registered adapter tensor (A and
+ * B of each (layer, proj) in lora_mask whose gradient buffer is registered) from its
+ * registered gradient (dA, dB), in one launch on the compute stream.  A and B are
+ * updated in place (the pointers given to ls_set_lora; the library writes them), the
+ * moments live in the library's plan (ls_config.adamw = 1; zero after ls_create or
+ * ls_adamw_reset).  Asynchronous.  Errors: LS_ERR_STATE (adamw not planned),
+ * LS_ERR_INVALID (hyperparameters out of range, null hp).
+ */
+ls_status ls_adamw_step(ls_ctx* ctx, const ls_adamw* hp);
+
+/* ls_adamw_reset — enqueue zeroing of every AdamW moment (a new optimizer run). */
+ls_status ls_adamw_reset(ls_ctx* ctx);
+
+/*
+ * Adapter files.  A release of the tool the pages describe saved adapters under key
+ * names that made them load without taking effect, silently (the lachieslifestyle.com
+ * how-to, "Step 2", the warning against version 0.72.0; "Soup CLI fine-tunes
+ * Llama-3.1-8B on a 4 GB laptop GPU ...", the paragraph on runs that were wrong
+ * anyway).  These files therefore carry an integrity record and a load either
+ * applies every adapter tensor or refuses.
+ *
+ * Format: safetensors (8-byte little-endian header length, JSON header, raw data).
+ * Tensor names follow the PEFT convention for Llama-style stacks,
+ *   base_model.model.model.layers.<l>.self_attn.<q|k|v|o>_proj.lora_<A|B>.weight
+ *   base_model.model.model.layers.<l>.mlp.<gate|up|down>_proj.lora_<A|B>.weight
+ * dtype F32, A [r, in], B [out, r].  __metadata__ holds format = pt, lsq.n_layers,
+ * lsq.r, lsq.mask, lsq.alpha and, per tensor, lsq.crc32.<name> = CRC-32 (the zlib
+ * polynomial) of its data bytes as 8 lowercase hex digits.
+ */
+
+/*
+ * ls_save_adapters — write every registered adapter of lora_mask to path (host
+ * string), after waiting for the compute stream; then read the file back and check
+ * it as ls_check_adapter_file does.  Synchronous.  Errors: LS_ERR_STATE (an adapter
+ * of the mask is not registered), LS_ERR_INVALID (the file cannot be written, or the
+ * check of what was written fails).
+ */
+ls_status ls_save_adapters(ls_ctx* ctx, const char* path);
+
+/*
+ * ls_load_adapters — check path against the context's stack (as ls_check_adapter_file)
+ * and, only if every check passes, copy every tensor into the registered A and B
+ * device buffers.  Synchronous.  Errors: LS_ERR_INVALID (the file fails a check; the
+ * message names the first problem; no adapter was changed), LS_ERR_STATE (an adapter
+ * of the mask is not registered).
+ */
+ls_status ls_load_adapters(ls_ctx* ctx, const char* path);
+
+/*
+ * ls_check_adapter_file — host-only check of path against cfg: exactly the expected
+ * tensor names (every layer, every projection of lora_mask, A and B; none missing,
+ * none extra), dtype F32 and the expected shapes, in-range and non-overlapping data
+ * offsets, lsq.n_layers / lsq.r / lsq.mask equal to cfg's, and every CRC-32 present
+ * and matching.  No HIP call.  Returns LS_OK or LS_ERR_INVALID; msg (host buffer of
+ * msg_len bytes, may be NULL) receives the first problem or "ok".
+ */
+ls_status ls_check_adapter_file(const ls_config* cfg, const char* path, char* msg, size_t msg_len);
 
 #ifdef __cplusplus
 }

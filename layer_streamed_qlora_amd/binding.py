@@ -18,8 +18,8 @@ LIB_PATH = os.path.join(_PKG, "liblsq.so")
 LS_OK, LS_ERR_INVALID, LS_ERR_STATE, LS_ERR_BUDGET, LS_ERR_OOM, LS_ERR_HIP = range(6)
 LS_QUANT_NF4, LS_QUANT_BF16 = 0, 1
 PROJS = ("q", "k", "v", "o", "gate", "up", "down")
-LS_KC_N = 5
-KERNEL_CLASSES = ("gemm_fwd", "gemm_bwd", "attn", "lora", "glue")
+LS_KC_N = 6
+KERNEL_CLASSES = ("gemm_fwd", "gemm_bwd", "attn", "lora", "glue", "optim")
 
 
 class LsError(RuntimeError):
@@ -35,7 +35,13 @@ class ls_config(C.Structure):
         ("quant", C.c_int32), ("nf4_block", C.c_int32), ("double_quant", C.c_int32), ("lora_r", C.c_int32),
         ("lora_alpha", C.c_float), ("lora_mask", C.c_uint32), ("n_buffers", C.c_int32), ("max_tokens", C.c_int32),
         ("max_seq", C.c_int32), ("resident", C.c_int32), ("vram_budget", C.c_uint64), ("profile", C.c_int32),
+        ("adamw", C.c_int32),
     ]
+
+
+class ls_adamw(C.Structure):
+    _fields_ = [("lr", C.c_float), ("beta1", C.c_float), ("beta2", C.c_float), ("eps", C.c_float),
+                ("weight_decay", C.c_float), ("step", C.c_int32)]
 
 
 class ls_layer_host(C.Structure):
@@ -77,6 +83,11 @@ SIGNATURES = {
     "ls_pack_nf4": (C.c_int, [C.c_void_p, C.c_uint64, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p,
                               C.c_void_p, C.c_void_p]),
     "ls_read_weight": (C.c_int, [C.c_void_p, C.c_int32, C.c_int32, C.c_void_p]),
+    "ls_adamw_step": (C.c_int, [C.c_void_p, C.POINTER(ls_adamw)]),
+    "ls_adamw_reset": (C.c_int, [C.c_void_p]),
+    "ls_save_adapters": (C.c_int, [C.c_void_p, C.c_char_p]),
+    "ls_load_adapters": (C.c_int, [C.c_void_p, C.c_char_p]),
+    "ls_check_adapter_file": (C.c_int, [C.POINTER(ls_config), C.c_char_p, C.c_char_p, C.c_size_t]),
 }
 
 _lib = None
@@ -105,7 +116,7 @@ def _check(status, ctx=None):
 
 
 def make_config(w, n_buffers=2, max_tokens=None, max_seq=None, resident=0, vram_budget=0, profile=0,
-                lora_mask=0x7F, n_layers=None) -> ls_config:
+                lora_mask=0x7F, n_layers=None, adamw=0) -> ls_config:
     """ls_config for a workload description (``synth.Workload``)."""
     return ls_config(
         n_layers=w.n_layers if n_layers is None else n_layers, hidden=w.hidden, n_heads=w.n_heads,
@@ -113,7 +124,8 @@ def make_config(w, n_buffers=2, max_tokens=None, max_seq=None, resident=0, vram_
         rope_theta=w.rope_theta, quant=LS_QUANT_NF4 if w.quant == "nf4" else LS_QUANT_BF16, nf4_block=64,
         double_quant=int(w.double_quant), lora_r=w.lora_r, lora_alpha=w.lora_alpha, lora_mask=lora_mask,
         n_buffers=n_buffers, max_tokens=w.tokens if max_tokens is None else max_tokens,
-        max_seq=w.seq if max_seq is None else max_seq, resident=resident, vram_budget=vram_budget, profile=profile)
+        max_seq=w.seq if max_seq is None else max_seq, resident=resident, vram_budget=vram_budget, profile=profile,
+        adamw=adamw)
 
 
 # ------------------------------------------------------------------ host calls
@@ -137,6 +149,13 @@ def ls_pack_nf4(w_bits: np.ndarray, double_quant: bool, n_threads: int = 0):
     _check(lib().ls_pack_nf4(ptr(w), n, int(double_quant), n_threads, ptr(packed), ptr(absmax), ptr(qabs),
                              ptr(scale2), ptr(mean)))
     return packed, absmax, qabs, scale2, (mean[0] if double_quant else None)
+
+
+def ls_check_adapter_file(cfg: ls_config, path: str):
+    """(status, message) of the library's host-only check of an adapter file."""
+    buf = C.create_string_buffer(1024)
+    st = lib().ls_check_adapter_file(C.byref(cfg), os.fsencode(path), buf, len(buf))
+    return st, buf.value.decode()
 
 
 def ls_plan_bytes(cfg: ls_config):
@@ -198,3 +217,16 @@ class Context:
 
     def read_weight(self, layer, proj, out_ptr):
         self._chk(lib().ls_read_weight(self.h, layer, proj, out_ptr))
+
+    def adamw_step(self, step, lr, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01):
+        hp = ls_adamw(lr=lr, beta1=beta1, beta2=beta2, eps=eps, weight_decay=weight_decay, step=step)
+        self._chk(lib().ls_adamw_step(self.h, C.byref(hp)))
+
+    def adamw_reset(self):
+        self._chk(lib().ls_adamw_reset(self.h))
+
+    def save_adapters(self, path):
+        self._chk(lib().ls_save_adapters(self.h, os.fsencode(path)))
+
+    def load_adapters(self, path):
+        self._chk(lib().ls_load_adapters(self.h, os.fsencode(path)))

@@ -1,5 +1,7 @@
 // Internal declarations shared by the host runtime and the HIP kernels of liblsq.
 #pragma once
+#include <string>
+#include <vector>
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -223,5 +225,44 @@ hipError_t launch_swiglu_fwd(const float* gu, int32_t I, uint16_t* act, int32_t 
 hipError_t launch_f32_to_bf16(const float* src, int64_t lds, uint16_t* dst, int64_t ldd, int32_t rows,
                               int32_t cols, int32_t pad_cols, float scale, int32_t transpose, hipStream_t s);
 hipError_t launch_dequant(const WeightRef& w, int32_t format, const float* levels, uint16_t* out, hipStream_t s);
+
+// ---- AdamW over the adapters: one launch over a table of chunks, each at most
+// kAdamChunk elements of one tensor (param p, gradient g, moments m, v).
+constexpr int kAdamChunk = 8192;
+struct AdamChunk {
+  float* p;
+  const float* g;
+  float* m;
+  float* v;
+  uint32_t n;      // elements, 1 .. kAdamChunk
+  uint32_t vec4;   // 1: every pointer 16-byte aligned and n % 4 == 0
+};
+// per-step constants, from the step count on the host in double precision
+struct AdamHyper {
+  float decay_mul;      // 1 - lr * weight_decay
+  float beta1, one_m_beta1, beta2, one_m_beta2;
+  float step_size;      // lr / (1 - beta1^t)
+  float inv_bc2_sqrt;   // 1 / sqrt(1 - beta2^t)
+  float eps;
+};
+hipError_t launch_adamw(const AdamChunk* chunks, int32_t n_chunks, const AdamHyper& h, hipStream_t s);
+
+// ---- adapter files (host only): the safetensors container with PEFT names and a
+// CRC-32 record per tensor.  names/shapes come from the stack configuration.
+struct AdapterEntry {
+  std::string name;
+  int32_t layer, proj, which;   // which: 0 = A [r, in], 1 = B [out, r]
+  int64_t rows, cols;
+  uint64_t offset = 0;          // byte offset of the data in the file's data section
+};
+std::vector<AdapterEntry> adapter_entries(const ls_config& c);
+uint32_t crc32_bytes(const void* data, size_t n);
+// Writes entries (with data[i] = host float32 rows*cols of entry i); "" or an error.
+std::string adapter_write(const ls_config& c, const std::vector<AdapterEntry>& e,
+                          const std::vector<const float*>& data, const std::string& path);
+// Checks the file against the stack; on success fills file_bytes and the entries'
+// offsets (absolute, into file_bytes).  "" or the first problem.
+std::string adapter_check(const ls_config& c, const std::string& path, std::vector<AdapterEntry>* e,
+                          std::vector<uint8_t>* file_bytes);
 
 }  // namespace lsq

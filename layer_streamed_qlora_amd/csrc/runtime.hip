@@ -57,6 +57,8 @@ struct DevPlan {
   uint64_t dya = 0, dyb = 0, dh32 = 0, dh16 = 0, dgu = 0, datt = 0, dqkv = 0, dqkv32 = 0, dn32 = 0;
   uint64_t lora = 0, lora_per_layer = 0, partial = 0, partial_bytes = 0;
   uint64_t levels = 0, rope = 0;
+  // AdamW: moments m then v (moment_elems floats each) and the chunk table
+  uint64_t moments = 0, moment_elems = 0, adam_tab = 0, adam_max_chunks = 0;
   // per-layer LoRA operand offsets (relative to the layer's LoRA base)
   uint64_t a16[LS_N_PROJ] = {}, bx16[LS_N_PROJ] = {}, bxt16[LS_N_PROJ] = {};
   uint64_t at_qkv = 0, at_o = 0, at_gu = 0, at_d = 0;
@@ -130,6 +132,15 @@ DevPlan make_plan(const ls_config& c, const BlobLayout& L) {
   P.partial = take(P.partial_bytes);
   P.levels = take(64);
   P.rope = take(8ull * (uint64_t)c.max_seq * (uint64_t)(c.head_dim / 2));
+  if (c.adamw) {
+    for (const AdapterEntry& e : adapter_entries(c)) {
+      const uint64_t n = (uint64_t)e.rows * (uint64_t)e.cols;
+      P.moment_elems += n;
+      P.adam_max_chunks += (n + kAdamChunk - 1) / kAdamChunk;
+    }
+    P.moments = take(8 * P.moment_elems);
+    P.adam_tab = take(sizeof(AdamChunk) * P.adam_max_chunks);
+  }
   P.total = align_up(off, kAlign);
   return P;
 }
@@ -172,6 +183,12 @@ struct ls_ctx {
   std::vector<hipEvent_t> ready, consumed;
   std::vector<char> ready_rec, cons_rec;
   std::vector<std::array<LoraReg, LS_N_PROJ>> lora;
+  uint64_t lora_version = 1;            // bumped by every ls_set_lora
+  // AdamW chunk table (host copy kept alive while its upload may be pending)
+  std::vector<AdamChunk> adam_host;
+  uint64_t adam_version = 0;
+  double adam_elems = 0;
+  bool prof_collected = false;
   float levels_h[16];
   // state
   bool fwd_valid = false, fwd_lora = false;
@@ -920,6 +937,7 @@ ls_status ls_set_lora(ls_ctx* c, int32_t layer, int32_t proj, const float* A, co
     return fail(c, LS_ERR_INVALID, "bad layer or projection index");
   if (!A || !B) return fail(c, LS_ERR_INVALID, "null A or B");
   c->lora[layer][proj] = {A, B, dA, dB};
+  ++c->lora_version;
   return LS_OK;
 }
 
@@ -934,6 +952,7 @@ ls_status ls_forward(ls_ctx* c, const void* X, int32_t batch, int32_t seq, int32
     if (!c->staged[l]) return fail(c, LS_ERR_STATE, "layer %d not staged", l);
   c->fwd_valid = false;
   c->prof.reset();
+  c->prof_collected = false;
   c->in_flight = true;
   if (T == 0) {
     c->fwd_valid = true; c->fwd_lora = lora_on != 0; c->fwd_T = 0; c->fwd_batch = batch; c->fwd_seq = seq;
@@ -1015,6 +1034,7 @@ ls_status ls_sync(ls_ctx* c) {
   HIPCHK(c, hipGetLastError());
   c->in_flight = false;
   collect_profile(c);
+  c->prof_collected = true;
   return LS_OK;
 }
 
@@ -1055,6 +1075,142 @@ ls_status ls_read_weight(ls_ctx* c, int32_t layer, int32_t proj, void* out) {
   HIPCHK(c, hipStreamSynchronize(c->cs));
   HIPCHK(c, hipStreamSynchronize(c->ps));
   return LS_OK;
+}
+
+// ------------------------------------------------------------ AdamW and adapter files
+ls_status ls_adamw_step(ls_ctx* c, const ls_adamw* hp) {
+  if (ls_status st = check_usable(c)) return st;
+  if (!c->cfg.adamw) return fail(c, LS_ERR_STATE, "AdamW moments were not planned (ls_config.adamw = 0)");
+  if (!hp) return fail(c, LS_ERR_INVALID, "null hyperparameters");
+  const bool ok = std::isfinite(hp->lr) && hp->lr >= 0.f && hp->beta1 >= 0.f && hp->beta1 < 1.f &&
+                  hp->beta2 >= 0.f && hp->beta2 < 1.f && std::isfinite(hp->eps) && hp->eps > 0.f &&
+                  std::isfinite(hp->weight_decay) && hp->weight_decay >= 0.f && hp->step >= 1;
+  if (!ok) return fail(c, LS_ERR_INVALID, "AdamW: need lr >= 0, beta1 and beta2 in [0, 1), eps > 0, weight_decay >= 0, step >= 1");
+  if (c->adam_version != c->lora_version) {
+    // one chunk table over every adapter tensor that has a gradient buffer; the
+    // moments follow the plan's order (layer, projection, A then B)
+    c->adam_host.clear();
+    double elems = 0;
+    float* m0 = c->dp<float>(c->plan.moments);
+    float* v0 = m0 + c->plan.moment_elems;
+    uint64_t moff = 0;
+    auto al16 = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15u) == 0; };
+    for (const AdapterEntry& e : adapter_entries(c->cfg)) {
+      const uint64_t n = (uint64_t)e.rows * (uint64_t)e.cols;
+      const LoraReg& R = c->lora[e.layer][e.proj];
+      float* prm = const_cast<float*>(e.which ? R.B : R.A);
+      const float* grd = e.which ? R.dB : R.dA;
+      if (prm && grd && R.A && R.B) {
+        for (uint64_t o = 0; o < n; o += kAdamChunk) {
+          AdamChunk ch;
+          ch.p = prm + o; ch.g = grd + o; ch.m = m0 + moff + o; ch.v = v0 + moff + o;
+          ch.n = (uint32_t)std::min<uint64_t>(kAdamChunk, n - o);
+          ch.vec4 = (ch.n % 4 == 0 && al16(ch.p) && al16(ch.g) && al16(ch.m) && al16(ch.v)) ? 1u : 0u;
+          c->adam_host.push_back(ch);
+        }
+        elems += (double)n;
+      }
+      moff += n;
+    }
+    if (c->adam_host.size() > c->plan.adam_max_chunks) return fail(c, LS_ERR_INVALID, "internal: AdamW table overflow");
+    if (!c->adam_host.empty())
+      HIPCHK(c, hipMemcpyAsync(c->dbase + c->plan.adam_tab, c->adam_host.data(), c->adam_host.size() * sizeof(AdamChunk),
+                               hipMemcpyHostToDevice, c->cs));
+    c->adam_elems = elems;
+    c->adam_version = c->lora_version;
+  }
+  AdamHyper h;
+  const double lr = hp->lr, b1 = hp->beta1, b2 = hp->beta2;
+  h.decay_mul = (float)(1.0 - lr * (double)hp->weight_decay);
+  h.beta1 = hp->beta1; h.one_m_beta1 = (float)(1.0 - b1);
+  h.beta2 = hp->beta2; h.one_m_beta2 = (float)(1.0 - b2);
+  h.step_size = (float)(lr / (1.0 - std::pow(b1, (double)hp->step)));
+  h.inv_bc2_sqrt = (float)(1.0 / std::sqrt(1.0 - std::pow(b2, (double)hp->step)));
+  h.eps = hp->eps;
+  if (c->prof_collected) { c->prof.reset(); c->prof_collected = false; }
+  if (c->cfg.profile && c->prof.origin == (size_t)-1) {
+    hipEvent_t e;
+    size_t i;
+    if (c->prof.next(&e, &i) == hipSuccess && hipEventRecord(e, c->cs) == hipSuccess) c->prof.origin = i;
+  }
+  c->in_flight = true;
+  {
+    // algorithmic bytes: p, g, m, v read and p, m, v written, float32
+    KTimer kt(c, LS_KC_OPTIM, 0.0, 28.0 * c->adam_elems);
+    HIPCHK(c, launch_adamw(reinterpret_cast<const AdamChunk*>(c->dbase + c->plan.adam_tab),
+                           (int32_t)c->adam_host.size(), h, c->cs));
+  }
+  return LS_OK;
+}
+
+ls_status ls_adamw_reset(ls_ctx* c) {
+  if (ls_status st = check_usable(c)) return st;
+  if (!c->cfg.adamw) return fail(c, LS_ERR_STATE, "AdamW moments were not planned (ls_config.adamw = 0)");
+  HIPCHK(c, launch_fill_f32(c->dp<float>(c->plan.moments), (int64_t)(2 * c->plan.moment_elems), 0.f, c->cs));
+  return LS_OK;
+}
+
+static ls_status require_adapters(ls_ctx* c, const std::vector<AdapterEntry>& es) {
+  for (const AdapterEntry& e : es)
+    if (!c->lora[e.layer][e.proj].A || !c->lora[e.layer][e.proj].B)
+      return fail(c, LS_ERR_STATE, "adapter of layer %d projection %d is not registered", e.layer, e.proj);
+  return LS_OK;
+}
+
+ls_status ls_save_adapters(ls_ctx* c, const char* path) {
+  if (ls_status st = check_usable(c)) return st;
+  if (!path) return fail(c, LS_ERR_INVALID, "null path");
+  const std::vector<AdapterEntry> es = adapter_entries(c->cfg);
+  if (ls_status st = require_adapters(c, es)) return st;
+  std::vector<std::vector<float>> host(es.size());
+  std::vector<const float*> ptrs(es.size());
+  HIPCHK(c, hipStreamSynchronize(c->cs));
+  for (size_t i = 0; i < es.size(); ++i) {
+    const LoraReg& R = c->lora[es[i].layer][es[i].proj];
+    host[i].resize((size_t)(es[i].rows * es[i].cols));
+    HIPCHK(c, hipMemcpyAsync(host[i].data(), es[i].which ? R.B : R.A, host[i].size() * sizeof(float),
+                             hipMemcpyDeviceToHost, c->cs));
+    ptrs[i] = host[i].data();
+  }
+  HIPCHK(c, hipStreamSynchronize(c->cs));
+  std::string err = adapter_write(c->cfg, es, ptrs, path);
+  if (!err.empty()) return fail(c, LS_ERR_INVALID, "%s", err.c_str());
+  err = adapter_check(c->cfg, path, nullptr, nullptr);
+  if (!err.empty()) return fail(c, LS_ERR_INVALID, "read-back check of %s failed: %s", path, err.c_str());
+  return LS_OK;
+}
+
+ls_status ls_load_adapters(ls_ctx* c, const char* path) {
+  if (ls_status st = check_usable(c)) return st;
+  if (!path) return fail(c, LS_ERR_INVALID, "null path");
+  if (ls_status st = require_adapters(c, adapter_entries(c->cfg))) return st;
+  std::vector<AdapterEntry> es;
+  std::vector<uint8_t> bytes;
+  const std::string err = adapter_check(c->cfg, path, &es, &bytes);
+  if (!err.empty()) return fail(c, LS_ERR_INVALID, "%s: %s", path, err.c_str());
+  for (const AdapterEntry& e : es) {
+    const LoraReg& R = c->lora[e.layer][e.proj];
+    HIPCHK(c, hipMemcpyAsync(const_cast<float*>(e.which ? R.B : R.A), bytes.data() + e.offset,
+                             (size_t)(4 * e.rows * e.cols), hipMemcpyHostToDevice, c->cs));
+  }
+  HIPCHK(c, hipStreamSynchronize(c->cs));
+  return LS_OK;
+}
+
+ls_status ls_check_adapter_file(const ls_config* cfg, const char* path, char* msg, size_t msg_len) {
+  auto say = [&](const std::string& m) {
+    if (msg && msg_len) {
+      const size_t n = std::min(m.size(), msg_len - 1);
+      memcpy(msg, m.data(), n);
+      msg[n] = 0;
+    }
+  };
+  if (!cfg || !path) { say("null cfg or path"); return LS_ERR_INVALID; }
+  const char* why = nullptr;
+  if (!validate_config(*cfg, &why)) { say(std::string("invalid config: ") + why); return LS_ERR_INVALID; }
+  const std::string err = adapter_check(*cfg, path, nullptr, nullptr);
+  say(err.empty() ? "ok" : err);
+  return err.empty() ? LS_OK : LS_ERR_INVALID;
 }
 
 }  // extern "C"
