@@ -71,6 +71,33 @@ def test_toy_streamed_equals_resident_bitwise():
             assert np.array_equal(a["dB"][l][p].view(np.uint32), b["dB"][l][p].view(np.uint32)), (l, p)
 
 
+@pytest.mark.parametrize("n_buffers", [3, 5])
+def test_deeper_pool_equals_resident_and_reuses_slots(n_buffers):
+    """A pool deeper than two slots on a 6-layer stack: two consecutive steps are bit for
+    bit the resident run, and in the second step every slot still holding the layer the
+    other direction needs first is reused, so it copies 2 (L - n_buffers) blobs."""
+    w = TOY
+    L = 6
+    x, dy = synth.activations(w)
+    say("case: toy pool depth", n_buffers)
+    res = H.GpuRun(w, range(L), resident=1)
+    want = res.step(x, dy, w.batch, w.seq, with_ref=True)
+    res.close()
+    run = H.GpuRun(w, range(L), n_buffers=n_buffers)
+    for s in range(2):
+        c0 = run.ctx.stats().h2d_copies
+        got = run.step(x, dy, w.batch, w.seq, with_ref=True)
+        copies = run.ctx.stats().h2d_copies - c0
+        for k in ("Y", "Y_ref", "dX"):
+            assert np.array_equal(got[k].view(np.uint32), want[k].view(np.uint32)), (s, k)
+        for l in range(L):
+            for p in H.PROJS:
+                assert np.array_equal(got["dA"][l][p].view(np.uint32), want["dA"][l][p].view(np.uint32)), (s, l, p)
+                assert np.array_equal(got["dB"][l][p].view(np.uint32), want["dB"][l][p].view(np.uint32)), (s, l, p)
+    assert copies == 2 * (L - n_buffers), copies
+    run.close()
+
+
 def test_b_zero_is_base_only_and_reference_is_lora_off():
     w = TOY
     x, dy = synth.activations(w)
