@@ -36,6 +36,8 @@ model   LoRA projection and the Llama-style decoder layer, forward and hand-deri
 stack   the layer stack (forward with checkpoints, recompute backward), the
         adapters-off reference pass, and a simulated two-slot streaming pool.
 optim   the AdamW update of the adapters (decoupled, lr-scaled weight decay).
+head    the output head (final RMSNorm, logits), SFT cross entropy and the DPO
+        objective with hand-derived logit gradients, and the head backward.
 adapters  adapter file names (PEFT convention), the safetensors container, the
         integrity record (per-tensor CRC-32) and a checker of a file against a stack.
 """
