@@ -103,6 +103,7 @@ def main():
     ap.add_argument("--buffers", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-profile", action="store_true")
+    ap.add_argument("--vocab", type=int, default=128256, help="output-head rows for the head+loss measurement (0 = none)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); this build has no multi-GPU path.",
@@ -121,7 +122,7 @@ def main():
         w = w.with_(n_layers=args.layers)
     T = w.tokens
     profile = 0 if args.no_profile else 1
-    cfg = B.make_config(w, n_buffers=args.buffers, profile=profile, adamw=1)
+    cfg = B.make_config(w, n_buffers=args.buffers, profile=profile, adamw=1, vocab=args.vocab)
     t0 = time.time()
     ctx = B.Context(cfg)
     for l in range(w.n_layers):
@@ -247,6 +248,45 @@ def main():
                             "median_launch_ms": round(o_ms, 4), "bound": "hbm",
                             "achieved": round(obytes / (o_ms * 1e-3) / 1e9, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                             "frac": round(obytes / (o_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    if profile and args.vocab:
+        # the training step with the output head and SFT loss (outside the fwd+bwd metric):
+        # forward, head + loss over the streamed vocabulary slices, backward from its dY
+        g.manual_seed(9)
+        Wh = (torch.randn((args.vocab, w.hidden), generator=g, device="cuda:0") * 0.02).to(torch.bfloat16)
+        gf = torch.ones(w.hidden, dtype=torch.bfloat16, device="cuda:0")
+        ctx.stage_head(Wh.view(torch.int16).cpu().numpy().view(np.uint16), gf.view(torch.int16).cpu().numpy().view(np.uint16))
+        del Wh
+        labels = torch.from_numpy(synth.labels(w, args.vocab, T)).to("cuda:0")
+        hout = torch.zeros(2 + 2 * w.batch, device="cuda:0")
+        dYh = torch.empty_like(X)
+
+        def head_step():
+            ctx.forward(X.data_ptr(), w.batch, w.seq, 1, Y.data_ptr())
+            ctx.head_loss(Y.data_ptr(), 0, labels.data_ptr(), B.LS_LOSS_SFT, 0.0, hout.data_ptr(), dYh.data_ptr())
+            ctx.backward(dYh.data_ptr(), dX.data_ptr(), 0)
+            ctx.sync()
+
+        head_step()
+        n_h = 3
+        hk = [0.0, 0.0]
+        c0 = ctx.stats().h2d_copies
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(n_h):
+            head_step()
+            st = ctx.stats()
+            j = B.KERNEL_CLASSES.index("head")
+            hk[0] += st.k_ms[j]; hk[1] += st.k_flop[j]
+        torch.cuda.synchronize()
+        dt = (time.perf_counter() - t0) / n_h
+        loss = float(hout[0].item())
+        assert np.isfinite(loss) and torch.isfinite(dYh.float()).all(), "non-finite head loss or gradient"
+        out["with_head"] = {"vocab": args.vocab, "loss": "SFT cross entropy, 25% of tokens unlabelled",
+                            "head_slices": -(-args.vocab // (ctx.stats().blob_bytes // (2 * w.hidden) // 256 * 256)),
+                            "ms_per_step": round(dt * 1e3, 3), "tokens_per_s": round(T / dt, 1),
+                            "head_kernel_ms_per_step": round(hk[0] / n_h, 3),
+                            "head_tflops": round(hk[1] / (hk[0] * 1e-3) / 1e12, 1) if hk[0] else None,
+                            "copies_per_step": (ctx.stats().h2d_copies - c0) / n_h, "sft_loss": round(loss, 4)}
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
         out["cpu_baseline"] = cpu_baseline(w)

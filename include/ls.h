@@ -82,6 +82,8 @@ typedef struct ls_config {
   int32_t profile;         /* 1 = time copies and per-layer compute with HIP events */
   int32_t adamw;           /* 1 = also plan float32 AdamW moments (m and v) for every
                               adapter of lora_mask and enable ls_adamw_step */
+  int32_t vocab;           /* 0 = no output head; else rows of the frozen bf16 output head
+                              [vocab, hidden] (ls_stage_head, ls_head_loss) */
 } ls_config;
 
 /* Host-side source weights for one layer (bf16 bit patterns, host pointers). */
@@ -99,8 +101,13 @@ enum {
   LS_KC_LORA = 3,     /* LoRA down projection and dA / dB / G products, operand conversion */
   LS_KC_GLUE = 4,     /* RMSNorm, rotary embedding, SwiGLU */
   LS_KC_OPTIM = 5,    /* AdamW update of the adapters (ls_adamw_step) */
-  LS_KC_N = 6
+  LS_KC_HEAD = 6,     /* output head products, softmax statistics and loss (ls_head_loss) */
+  LS_KC_N = 7
 };
+
+/* Losses of ls_head_loss. */
+enum { LS_LOSS_SFT = 0, LS_LOSS_DPO = 1 };
+#define LS_LABEL_IGNORE (-100)
 
 typedef struct ls_stats {
   uint64_t blob_bytes;         /* bytes of one layer blob (same host and device) */
@@ -312,6 +319,49 @@ ls_status ls_load_adapters(ls_ctx* ctx, const char* path);
  * msg_len bytes, may be NULL) receives the first problem or "ok".
  */
 ls_status ls_check_adapter_file(const ls_config* cfg, const char* path, char* msg, size_t msg_len);
+
+/* ---------------------------------------------------------------------------
+ * Output head and loss.  Streaming bounds the weights, not the logits: the tool the
+ * pages describe keeps the whole logits tensor resident (8.71 GB at batch 8 on a
+ * 152k-token vocabulary: "Soup CLI fine-tunes Llama-3.1-8B on a 4 GB laptop GPU ...",
+ * third and fifth paragraphs).  Here the frozen head streams through the same device
+ * slots as the layers, in vocabulary slices that fit one slot, and the loss needs only
+ * per-token softmax statistics: no [tokens, vocab] tensor is ever held.
+ * ------------------------------------------------------------------------- */
+
+/*
+ * ls_stage_head — copy the frozen head into the pinned store: w [vocab, hidden] bf16
+ * (host pointer, row-major) and the final RMSNorm weight g_final [hidden] bf16.  The
+ * head is kept in 16 bits whatever ls_config.quant says (QLoRA keeps the output layer
+ * in 16 bits).  Synchronous; the caller's buffers may be freed on return.  Errors:
+ * LS_ERR_STATE (ls_config.vocab = 0, or work in flight), LS_ERR_INVALID (null).
+ */
+ls_status ls_stage_head(ls_ctx* ctx, const uint16_t* w, const uint16_t* g_final);
+
+/*
+ * ls_head_loss — enqueue, after ls_forward and before ls_backward (same batch, seq):
+ * final RMSNorm of Y, logits = yn W^T slice by slice, the loss, and dY = dLoss/dY for
+ * ls_backward (second, reversed pass over the slices).
+ *   Y:      device bf16 [T, hidden], the ls_forward output (adapters on).
+ *   Y_ref:  device bf16 [T, hidden], the ls_forward reference output; LS_LOSS_DPO only.
+ *   labels: device int32 [T], the target id of each token in [0, vocab), or
+ *           LS_LABEL_IGNORE for a token without loss; the caller aligns targets.
+ *   kind:   LS_LOSS_SFT — mean over labelled tokens of -log softmax(logits)[label];
+ *           LS_LOSS_DPO — sequences in pairs (2i chosen, 2i+1 rejected), a sequence's
+ *           log-prob is the sum over its labelled tokens, loss = mean over pairs of
+ *           -log sigmoid(beta [(pi_c - ref_c) - (pi_r - ref_r)]) (the pages name DPO
+ *           over the streamed base, reference = adapters off: same paragraph three).
+ *   beta:   DPO temperature, > 0 (ignored for SFT).
+ *   out:    device float [2 + 2 batch]: loss, number of labelled tokens, per-sequence
+ *           log-prob sums of the policy, then (DPO) of the reference.
+ *   dY:     device bf16 [T, hidden] receives dLoss/dY.
+ * Asynchronous.  Deterministic (fixed reduction orders).  Errors: LS_ERR_STATE (no head
+ * staged, no matching forward, DPO without a reference pass), LS_ERR_INVALID (null
+ * pointers, bad kind, beta <= 0, odd batch for DPO).  Labels out of range are treated
+ * as ignored.
+ */
+ls_status ls_head_loss(ls_ctx* ctx, const void* Y, const void* Y_ref, const int32_t* labels, int32_t kind,
+                       float beta, float* out, void* dY);
 
 #ifdef __cplusplus
 }

@@ -18,8 +18,10 @@ LIB_PATH = os.path.join(_PKG, "liblsq.so")
 LS_OK, LS_ERR_INVALID, LS_ERR_STATE, LS_ERR_BUDGET, LS_ERR_OOM, LS_ERR_HIP = range(6)
 LS_QUANT_NF4, LS_QUANT_BF16 = 0, 1
 PROJS = ("q", "k", "v", "o", "gate", "up", "down")
-LS_KC_N = 6
-KERNEL_CLASSES = ("gemm_fwd", "gemm_bwd", "attn", "lora", "glue", "optim")
+LS_KC_N = 7
+KERNEL_CLASSES = ("gemm_fwd", "gemm_bwd", "attn", "lora", "glue", "optim", "head")
+LS_LOSS_SFT, LS_LOSS_DPO = 0, 1
+LS_LABEL_IGNORE = -100
 
 
 class LsError(RuntimeError):
@@ -35,7 +37,7 @@ class ls_config(C.Structure):
         ("quant", C.c_int32), ("nf4_block", C.c_int32), ("double_quant", C.c_int32), ("lora_r", C.c_int32),
         ("lora_alpha", C.c_float), ("lora_mask", C.c_uint32), ("n_buffers", C.c_int32), ("max_tokens", C.c_int32),
         ("max_seq", C.c_int32), ("resident", C.c_int32), ("vram_budget", C.c_uint64), ("profile", C.c_int32),
-        ("adamw", C.c_int32),
+        ("adamw", C.c_int32), ("vocab", C.c_int32),
     ]
 
 
@@ -88,6 +90,9 @@ SIGNATURES = {
     "ls_save_adapters": (C.c_int, [C.c_void_p, C.c_char_p]),
     "ls_load_adapters": (C.c_int, [C.c_void_p, C.c_char_p]),
     "ls_check_adapter_file": (C.c_int, [C.POINTER(ls_config), C.c_char_p, C.c_char_p, C.c_size_t]),
+    "ls_stage_head": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p]),
+    "ls_head_loss": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32, C.c_float, C.c_void_p,
+                               C.c_void_p]),
 }
 
 _lib = None
@@ -116,7 +121,7 @@ def _check(status, ctx=None):
 
 
 def make_config(w, n_buffers=2, max_tokens=None, max_seq=None, resident=0, vram_budget=0, profile=0,
-                lora_mask=0x7F, n_layers=None, adamw=0) -> ls_config:
+                lora_mask=0x7F, n_layers=None, adamw=0, vocab=0) -> ls_config:
     """ls_config for a workload description (``synth.Workload``)."""
     return ls_config(
         n_layers=w.n_layers if n_layers is None else n_layers, hidden=w.hidden, n_heads=w.n_heads,
@@ -125,7 +130,7 @@ def make_config(w, n_buffers=2, max_tokens=None, max_seq=None, resident=0, vram_
         double_quant=int(w.double_quant), lora_r=w.lora_r, lora_alpha=w.lora_alpha, lora_mask=lora_mask,
         n_buffers=n_buffers, max_tokens=w.tokens if max_tokens is None else max_tokens,
         max_seq=w.seq if max_seq is None else max_seq, resident=resident, vram_budget=vram_budget, profile=profile,
-        adamw=adamw)
+        adamw=adamw, vocab=vocab)
 
 
 # ------------------------------------------------------------------ host calls
@@ -230,3 +235,13 @@ class Context:
 
     def load_adapters(self, path):
         self._chk(lib().ls_load_adapters(self.h, os.fsencode(path)))
+
+    def stage_head(self, w_bits: np.ndarray, g_bits: np.ndarray):
+        """w_bits: uint16 [vocab, hidden] (bf16 bits), g_bits: uint16 [hidden]."""
+        w = np.ascontiguousarray(w_bits, dtype=np.uint16)
+        g = np.ascontiguousarray(g_bits, dtype=np.uint16)
+        self._chk(lib().ls_stage_head(self.h, w.ctypes.data, g.ctypes.data))
+
+    def head_loss(self, Y_ptr, Yref_ptr, labels_ptr, kind, beta, out_ptr, dY_ptr):
+        self._chk(lib().ls_head_loss(self.h, Y_ptr or None, Yref_ptr or None, labels_ptr or None, int(kind),
+                                     float(beta), out_ptr or None, dY_ptr or None))

@@ -953,6 +953,7 @@ __global__ void __launch_bounds__(NTHREADS, 1) k_gemm_bwd(BwdArgs args, int n_ti
   E.out = E.f32 ? (void*)args.out32 : (void*)args.out16;
   E.ldo = args.ldo;
   E.gu = args.gu32; E.ldgu = args.ldgu;
+  E.r32 = args.resid32; E.ldr = args.ldo;
   epilogue<NTHREADS>(sm, acc, m0, j0, args.M, args.N, E);
 }
 
@@ -1186,6 +1187,7 @@ __global__ void __launch_bounds__(NT_FAST, 1) k_gemm_bwd_fast(BwdArgs args, int 
   E.out = E.f32 ? (void*)args.out32 : (void*)args.out16;
   E.ldo = args.ldo;
   E.gu = args.gu32; E.ldgu = args.ldgu;
+  E.r32 = args.resid32; E.ldr = args.ldo;
   epilogue<NT_FAST>(sm, acc, m0, j0, args.M, args.N, E);
 }
 
@@ -1266,6 +1268,7 @@ hipError_t launch_gemm_bwd(const BwdArgs& a, hipStream_t s) {
   // low-rank terms (stacked q|k|v or gate|up at rank > 16) add the remaining columns
   // into the float32 result with a second, generic MFMA GEMM.
   if (a.kx > BK && !a.out32) return hipErrorInvalidValue;
+  if (a.resid32 && (!a.out32 || a.gu32 || a.kx > BK)) return hipErrorInvalidValue;
   if (a.gu32 && (!a.out16 || a.out32 || a.N % 4 != 0 || a.ldo % 4 != 0 || a.ldgu % 4 != 0 || a.kx > BK))
     return hipErrorInvalidValue;
   BwdArgs k = a;

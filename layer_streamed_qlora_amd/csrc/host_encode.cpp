@@ -199,6 +199,7 @@ bool validate_config(const ls_config& c, const char** why) {
   REQ(c.max_seq >= 1 && c.max_seq <= c.max_tokens && c.max_seq <= 8192, "max_seq must be in 1..min(max_tokens, 8192)");
   REQ(c.resident == 0 || c.resident == 1, "resident must be 0 or 1");
   REQ(c.adamw == 0 || c.adamw == 1, "adamw must be 0 or 1");
+  REQ(c.vocab >= 0 && c.vocab <= (1 << 24), "vocab must be in 0..2^24");
 #undef REQ
   return true;
 }

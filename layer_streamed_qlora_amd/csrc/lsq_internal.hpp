@@ -108,6 +108,9 @@ struct BwdArgs {
   const uint16_t* aext = nullptr; int32_t ldaext = 0; int32_t kx = 0;   // bf16 [M, kx]
   const uint16_t* bext = nullptr; int32_t ldbext = 0;                   // bf16 [N, kx]
   float* out32 = nullptr; uint16_t* out16 = nullptr; int32_t ldo = 0;  // exactly one set
+  // float32 [M, ldo] added to the product before it is written (may be out32 itself:
+  // every element is read and written by the same thread), nullable
+  const float* resid32 = nullptr;
   const float* levels = nullptr;
   int32_t format = WF_NF4;
   // SwiGLU backward: the product is d(act); with gate, up from gu32 (float32 [M, ldgu],
@@ -246,6 +249,22 @@ struct AdamHyper {
   float eps;
 };
 hipError_t launch_adamw(const AdamChunk* chunks, int32_t n_chunks, const AdamHyper& h, hipStream_t s);
+
+// ---- output head and loss over vocabulary slices (head.hip)
+// fold a slice's float32 logits [T, vs] (row stride ldz, vocabulary columns v0..) into
+// per-token running max m, sum s of exp(z - m), and the label's logit
+hipError_t launch_ce_stats(const float* Z, int32_t ldz, int32_t vs, int32_t v0, const int32_t* labels, int32_t T,
+                           int32_t vocab, float* m, float* s, float* zlab, bool first, hipStream_t st);
+// per-sequence log-prob sums, the loss (LS_LOSS_SFT / LS_LOSS_DPO) and the per-sequence
+// coefficient dL/dlog p; rm/rs/rz null for SFT.  out: loss, labelled tokens, policy
+// sums [T/seq], reference sums [T/seq]
+hipError_t launch_loss_finalize(int32_t kind, float beta, int32_t T, int32_t seq, int32_t vocab, const int32_t* labels,
+                                const float* pm, const float* ps, const float* pz, const float* rm, const float* rs,
+                                const float* rz, float* coef, float* out, hipStream_t st);
+// dz = coef (onehot(label) - softmax) of a slice, bf16 [T, vs] with row stride ldz
+hipError_t launch_ce_grad(const float* Z, int32_t ldz, int32_t vs, int32_t v0, const int32_t* labels, int32_t T,
+                          int32_t seq, int32_t vocab, const float* m, const float* s, const float* coef, uint16_t* dz,
+                          hipStream_t st);
 
 // ---- adapter files (host only): the safetensors container with PEFT names and a
 // CRC-32 record per tensor.  names/shapes come from the stack configuration.

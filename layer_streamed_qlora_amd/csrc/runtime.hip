@@ -59,6 +59,11 @@ struct DevPlan {
   uint64_t levels = 0, rope = 0;
   // AdamW: moments m then v (moment_elems floats each) and the chunk table
   uint64_t moments = 0, moment_elems = 0, adam_tab = 0, adam_max_chunks = 0;
+  // output head: vocabulary slices of head_rows rows, each in one slot (pool index
+  // n_layers + j); logits [T, ldz] float32, their gradient bf16, per-token statistics
+  int32_t head_rows = 0, head_slices = 0, ldz = 0;
+  uint64_t gfin = 0, hyn = 0, hynr = 0, hrstd = 0, hrstd2 = 0, hz = 0, hdz = 0, hdyn = 0;
+  uint64_t hpm = 0, hps = 0, hpz = 0, hrm = 0, hrs = 0, hrz = 0, hcoef = 0;
   // per-layer LoRA operand offsets (relative to the layer's LoRA base)
   uint64_t a16[LS_N_PROJ] = {}, bx16[LS_N_PROJ] = {}, bxt16[LS_N_PROJ] = {};
   uint64_t at_qkv = 0, at_o = 0, at_gu = 0, at_d = 0;
@@ -75,7 +80,17 @@ DevPlan make_plan(const ls_config& c, const BlobLayout& L) {
   const uint64_t qd = (uint64_t)c.n_heads * c.head_dim, kvd = (uint64_t)c.n_kv_heads * c.head_dim;
   const uint64_t qkvd = qd + 2 * kvd;
   const uint64_t r16 = r16_of(c), R7 = 7 * r16;
-  P.n_slots = c.resident ? c.n_layers : c.n_buffers;
+  if (c.vocab > 0) {
+    // rows per head slice: as many bf16 rows of the head as fit one layer slot, rounded
+    // down to a multiple of 256 (64 for small slots)
+    int64_t vs = (int64_t)(L.bytes / (2ull * (uint64_t)c.hidden));
+    vs -= vs >= 256 ? vs % 256 : vs % 64;
+    vs = std::max<int64_t>(1, std::min<int64_t>(vs, c.vocab));
+    P.head_rows = (int32_t)vs;
+    P.head_slices = (int32_t)((c.vocab + vs - 1) / vs);
+    P.ldz = (int32_t)((vs + 63) / 64 * 64);
+  }
+  P.n_slots = c.resident ? c.n_layers + P.head_slices : c.n_buffers;
   P.slots = take(L.bytes * (uint64_t)P.n_slots);
   P.ck = take(2 * T * h * (uint64_t)c.n_layers);
   P.xref = take(2 * 2 * T * h);
@@ -141,6 +156,19 @@ DevPlan make_plan(const ls_config& c, const BlobLayout& L) {
     P.moments = take(8 * P.moment_elems);
     P.adam_tab = take(sizeof(AdamChunk) * P.adam_max_chunks);
   }
+  if (c.vocab > 0) {
+    P.gfin = take(2 * h);
+    P.hyn = take(2 * T * h);
+    P.hynr = take(2 * T * h);
+    P.hrstd = take(4 * T);
+    P.hrstd2 = take(4 * T);
+    P.hz = take(4 * T * (uint64_t)P.ldz);
+    P.hdz = take(2 * T * (uint64_t)P.ldz);
+    P.hdyn = take(4 * T * h);
+    P.hpm = take(4 * T); P.hps = take(4 * T); P.hpz = take(4 * T);
+    P.hrm = take(4 * T); P.hrs = take(4 * T); P.hrz = take(4 * T);
+    P.hcoef = take(4 * T);
+  }
   P.total = align_up(off, kAlign);
   return P;
 }
@@ -189,6 +217,8 @@ struct ls_ctx {
   uint64_t adam_version = 0;
   double adam_elems = 0;
   bool prof_collected = false;
+  bool head_staged = false;
+  bool fwd_ref = false;                 // the last forward also ran the reference pass
   float levels_h[16];
   // state
   bool fwd_valid = false, fwd_lora = false;
@@ -803,7 +833,7 @@ ls_status ls_plan_bytes(const ls_config* cfg, uint64_t* device_bytes, uint64_t* 
   const BlobLayout L = make_layout(*cfg);
   const DevPlan P = make_plan(*cfg, L);
   if (device_bytes) *device_bytes = P.total;
-  if (host_bytes) *host_bytes = L.bytes * (uint64_t)cfg->n_layers;
+  if (host_bytes) *host_bytes = L.bytes * (uint64_t)(cfg->n_layers + P.head_slices);
   if (blob_bytes) *blob_bytes = L.bytes;
   return LS_OK;
 }
@@ -841,7 +871,7 @@ ls_status ls_create(const ls_config* cfg, void* compute_stream, void* copy_strea
   else { c->err = "copy stream creation failed"; return bail(LS_ERR_HIP); }
   if (gemm_dequant_init() != hipSuccess) { c->err = "kernel attribute setup failed"; return bail(LS_ERR_HIP); }
 
-  const int nb = cfg->resident ? cfg->n_layers : cfg->n_buffers;
+  const int nb = P.n_slots;
   c->slot_layer.assign(nb, -1);
   c->ready.resize(nb);
   c->consumed.resize(nb);
@@ -856,8 +886,8 @@ ls_status ls_create(const ls_config* cfg, void* compute_stream, void* copy_strea
   }
   c->lora.resize(cfg->n_layers);
   c->staged.assign(cfg->n_layers, 0);
-  c->host.assign(cfg->n_layers, nullptr);
-  for (int l = 0; l < cfg->n_layers; ++l) {
+  c->host.assign(cfg->n_layers + P.head_slices, nullptr);
+  for (int l = 0; l < cfg->n_layers + P.head_slices; ++l) {
     if (hipHostMalloc((void**)&c->host[l], L.bytes, hipHostMallocDefault) != hipSuccess) {
       c->host[l] = nullptr;
       c->err = "pinned host allocation of the layer store failed";
@@ -887,7 +917,7 @@ ls_status ls_create(const ls_config* cfg, void* compute_stream, void* copy_strea
     return bail(LS_ERR_HIP);
   }
   c->stats.blob_bytes = L.bytes;
-  c->stats.store_bytes = L.bytes * (uint64_t)cfg->n_layers;
+  c->stats.store_bytes = L.bytes * (uint64_t)(cfg->n_layers + P.head_slices);
   c->stats.device_bytes = P.total;
   *out = c;
   return LS_OK;
@@ -956,6 +986,7 @@ ls_status ls_forward(ls_ctx* c, const void* X, int32_t batch, int32_t seq, int32
   c->in_flight = true;
   if (T == 0) {
     c->fwd_valid = true; c->fwd_lora = lora_on != 0; c->fwd_T = 0; c->fwd_batch = batch; c->fwd_seq = seq;
+    c->fwd_ref = Y_ref != nullptr;
     return LS_OK;
   }
   const Dims d = dims_of(c, batch, seq);
@@ -984,6 +1015,7 @@ ls_status ls_forward(ls_ctx* c, const void* X, int32_t batch, int32_t seq, int32
     if ((st = release_layer(c, l))) return st;
   }
   c->fwd_valid = true; c->fwd_lora = lora; c->fwd_T = (int)T; c->fwd_batch = batch; c->fwd_seq = seq;
+  c->fwd_ref = Y_ref != nullptr;
   return LS_OK;
 }
 
@@ -1211,6 +1243,150 @@ ls_status ls_check_adapter_file(const ls_config* cfg, const char* path, char* ms
   const std::string err = adapter_check(*cfg, path, nullptr, nullptr);
   say(err.empty() ? "ok" : err);
   return err.empty() ? LS_OK : LS_ERR_INVALID;
+}
+
+// ------------------------------------------------------------------ output head and loss
+ls_status ls_stage_head(ls_ctx* c, const uint16_t* w, const uint16_t* g_final) {
+  if (ls_status st = check_usable(c)) return st;
+  if (c->cfg.vocab <= 0) return fail(c, LS_ERR_STATE, "no output head planned (ls_config.vocab = 0)");
+  if (!w || !g_final) return fail(c, LS_ERR_INVALID, "null head or norm weight");
+  if (c->in_flight) return fail(c, LS_ERR_STATE, "work is in flight: call ls_sync first");
+  const int L = c->cfg.n_layers, S = c->plan.head_slices, vs = c->plan.head_rows;
+  const uint64_t row = 2ull * c->cfg.hidden;
+  for (int j = 0; j < S; ++j) {
+    const int64_t r0 = (int64_t)j * vs, rows = std::min<int64_t>(vs, c->cfg.vocab - r0);
+    std::memcpy(c->host[L + j], reinterpret_cast<const uint8_t*>(w) + (uint64_t)r0 * row, (uint64_t)rows * row);
+    for (auto& sl : c->slot_layer)
+      if (sl == L + j) sl = -1;
+    if (c->cfg.resident) {
+      HIPCHK(c, hipMemcpyAsync(slot_ptr(c, L + j), c->host[L + j], c->lay.bytes, hipMemcpyHostToDevice, c->ps));
+      c->stats.h2d_bytes += c->lay.bytes;
+      c->stats.h2d_copies += 1;
+    }
+  }
+  HIPCHK(c, hipMemcpyAsync(c->dbase + c->plan.gfin, g_final, row, hipMemcpyHostToDevice, c->ps));
+  HIPCHK(c, hipStreamSynchronize(c->ps));
+  c->head_staged = true;
+  return LS_OK;
+}
+
+// the bf16 head slice j held in its slot, as the GEMMs take a weight
+static WeightRef head_ref(const ls_ctx* c, int j) {
+  WeightRef r;
+  r.w = slot_ptr(const_cast<ls_ctx*>(c), c->cfg.n_layers + j);
+  r.n_out = std::min<int32_t>(c->plan.head_rows, c->cfg.vocab - j * c->plan.head_rows);
+  r.n_in = c->cfg.hidden;
+  return r;
+}
+
+ls_status ls_head_loss(ls_ctx* c, const void* Y, const void* Y_ref, const int32_t* labels, int32_t kind, float beta,
+                       float* out, void* dY) {
+  if (ls_status st = check_usable(c)) return st;
+  if (c->cfg.vocab <= 0 || !c->head_staged) return fail(c, LS_ERR_STATE, "no output head staged");
+  if (!c->fwd_valid || c->fwd_T == 0) return fail(c, LS_ERR_STATE, "ls_head_loss needs a preceding non-empty ls_forward");
+  if (kind != LS_LOSS_SFT && kind != LS_LOSS_DPO) return fail(c, LS_ERR_INVALID, "unknown loss kind %d", kind);
+  if (!Y || !labels || !out || !dY) return fail(c, LS_ERR_INVALID, "null Y, labels, out or dY");
+  const int T = c->fwd_T, seq = c->fwd_seq, nseq = c->fwd_batch;
+  if (nseq > 1024) return fail(c, LS_ERR_INVALID, "at most 1024 sequences per call");
+  const bool dpo = kind == LS_LOSS_DPO;
+  if (dpo) {
+    if (!Y_ref) return fail(c, LS_ERR_INVALID, "DPO needs the reference output Y_ref");
+    if (!c->fwd_ref) return fail(c, LS_ERR_STATE, "DPO needs a forward that ran the reference pass");
+    if (nseq % 2 != 0) return fail(c, LS_ERR_INVALID, "DPO needs an even batch (chosen, rejected pairs)");
+    if (!(beta > 0.f) || !std::isfinite(beta)) return fail(c, LS_ERR_INVALID, "DPO beta must be > 0");
+  }
+  const int L = c->cfg.n_layers, S = c->plan.head_slices, h = c->cfg.hidden, vocab = c->cfg.vocab;
+  const int ldz = c->plan.ldz;
+  const float* lv = c->dp<float>(c->plan.levels);
+  uint16_t* yn = c->dp<uint16_t>(c->plan.hyn);
+  uint16_t* ynr = c->dp<uint16_t>(c->plan.hynr);
+  const uint16_t* gf = c->dp<uint16_t>(c->plan.gfin);
+  float* rstd = c->dp<float>(c->plan.hrstd);
+  float* Z = c->dp<float>(c->plan.hz);
+  uint16_t* dZ = c->dp<uint16_t>(c->plan.hdz);
+  float* dyn = c->dp<float>(c->plan.hdyn);
+  float *pm = c->dp<float>(c->plan.hpm), *ps = c->dp<float>(c->plan.hps), *pz = c->dp<float>(c->plan.hpz);
+  float *rm = c->dp<float>(c->plan.hrm), *rs = c->dp<float>(c->plan.hrs), *rz = c->dp<float>(c->plan.hrz);
+  float* coef = c->dp<float>(c->plan.hcoef);
+  const int32_t* lab = labels;
+  if (c->prof_collected) { c->prof.reset(); c->prof_collected = false; }
+  c->in_flight = true;
+  ls_status st;
+  auto logits = [&](const uint16_t* x, int j) -> ls_status {
+    const WeightRef w = head_ref(c, j);
+    FwdArgs a;
+    a.x = x; a.ldx = h; a.M = T; a.K = h; a.n_groups = 1;
+    a.g[0].w = w;
+    a.y32 = Z; a.ldy = ldz; a.levels = lv; a.format = WF_BF16;
+    KTimer kt(c, LS_KC_HEAD, 2.0 * T * w.n_out * h, 2.0 * T * h + 2.0 * w.n_out * h + 4.0 * T * w.n_out);
+    HIPCHK(c, launch_gemm_fwd(a, c->cs));
+    return LS_OK;
+  };
+  {
+    KTimer kt(c, LS_KC_HEAD, 0.0, (dpo ? 2.0 : 1.0) * 4.0 * T * h);
+    HIPCHK(c, launch_rmsnorm_fwd((const uint16_t*)Y, nullptr, gf, yn, rstd, T, h, c->cfg.rms_eps, c->cs));
+    if (dpo)
+      HIPCHK(c, launch_rmsnorm_fwd((const uint16_t*)Y_ref, nullptr, gf, ynr, c->dp<float>(c->plan.hrstd2), T, h,
+                                   c->cfg.rms_eps, c->cs));
+  }
+  // pass 1 over the slices: softmax statistics of the policy (and the reference)
+  if ((st = ensure_copy(c, L))) return st;
+  for (int j = 0; j < S; ++j) {
+    for (int k = 1; k < c->cfg.n_buffers && j + k < S; ++k)
+      if ((st = ensure_copy(c, L + j + k))) return st;
+    if ((st = use_layer(c, L + j))) return st;
+    {
+      Span sp(c, c->cs, false);
+      const int vs = head_ref(c, j).n_out, v0 = j * c->plan.head_rows;
+      if ((st = logits(yn, j))) return st;
+      {
+        KTimer kt(c, LS_KC_HEAD, 0.0, 4.0 * T * vs);
+        HIPCHK(c, launch_ce_stats(Z, ldz, vs, v0, lab, T, vocab, pm, ps, pz, j == 0, c->cs));
+      }
+      if (dpo) {
+        if ((st = logits(ynr, j))) return st;
+        KTimer kt(c, LS_KC_HEAD, 0.0, 4.0 * T * vs);
+        HIPCHK(c, launch_ce_stats(Z, ldz, vs, v0, lab, T, vocab, rm, rs, rz, j == 0, c->cs));
+      }
+    }
+    if ((st = release_layer(c, L + j))) return st;
+  }
+  {
+    KTimer kt(c, LS_KC_HEAD, 0.0, 16.0 * T);
+    HIPCHK(c, launch_loss_finalize(kind, beta, T, seq, vocab, lab, pm, ps, pz, dpo ? rm : nullptr, dpo ? rs : nullptr,
+                                   dpo ? rz : nullptr, coef, out, c->cs));
+  }
+  // pass 2, slices in reverse: recompute the logits, dz, and dyn += dz W_j
+  if ((st = ensure_copy(c, L + S - 1))) return st;
+  for (int j = S - 1; j >= 0; --j) {
+    for (int k = 1; k < c->cfg.n_buffers && j - k >= 0; ++k)
+      if ((st = ensure_copy(c, L + j - k))) return st;
+    if ((st = use_layer(c, L + j))) return st;
+    {
+      Span sp(c, c->cs, false);
+      const WeightRef w = head_ref(c, j);
+      const int vs = w.n_out, v0 = j * c->plan.head_rows;
+      if ((st = logits(yn, j))) return st;
+      {
+        KTimer kt(c, LS_KC_HEAD, 0.0, 4.0 * T * vs + 2.0 * T * vs);
+        HIPCHK(c, launch_ce_grad(Z, ldz, vs, v0, lab, T, seq, vocab, pm, ps, coef, dZ, c->cs));
+      }
+      BwdArgs b;
+      b.dy = dZ; b.lddy = ldz; b.M = T; b.N = h; b.n_segs = 1;
+      b.seg[0].w = w;
+      b.out32 = dyn; b.ldo = h; b.resid32 = j == S - 1 ? nullptr : dyn;
+      b.levels = lv; b.format = WF_BF16;
+      KTimer kt(c, LS_KC_HEAD, 2.0 * T * vs * h, 2.0 * T * vs + 2.0 * vs * h + 4.0 * T * h * (j == S - 1 ? 1 : 2));
+      HIPCHK(c, launch_gemm_bwd(b, c->cs));
+    }
+    if ((st = release_layer(c, L + j))) return st;
+  }
+  {
+    KTimer kt(c, LS_KC_HEAD, 0.0, 4.0 * T * h + 4.0 * T * h);
+    HIPCHK(c, launch_rmsnorm_bwd(dyn, (const uint16_t*)Y, nullptr, gf, rstd, nullptr, nullptr, nullptr, (uint16_t*)dY,
+                                 T, h, c->cs));
+  }
+  return LS_OK;
 }
 
 }  // extern "C"

@@ -169,3 +169,23 @@ def device_lora(w: Workload, layer: int, device="cuda"):
         b = torch.randn((n_out, r), generator=g, device=device) * 0.01
         out[p] = (a.contiguous(), b.contiguous())
     return out
+
+
+HEAD_W_ID, HEAD_G_ID, LABEL_ID = 90, 91, 92
+
+
+def head_weights(w: Workload, vocab: int):
+    """Frozen output head: (W [vocab, hidden] float32 of bf16 values ~ N(0, 0.02),
+    g_final [hidden] float32 of bf16 values near 1)."""
+    W = _rng(w.wid, 0, HEAD_W_ID).standard_normal((vocab, w.hidden), dtype=np.float32) * np.float32(0.02)
+    g = 1.0 + 0.1 * _rng(w.wid, 0, HEAD_G_ID).standard_normal(w.hidden, dtype=np.float32)
+    return _to_bf16_values(W), _to_bf16_values(g.astype(np.float32))
+
+
+def labels(w: Workload, vocab: int, tokens: int, ignore_frac: float = 0.25, seed: int = 0):
+    """int32 target ids in [0, vocab), a fraction of them -100 (no loss), like the
+    prompt tokens of instruction records."""
+    g = _rng(w.wid, seed, LABEL_ID)
+    lab = g.integers(0, vocab, tokens).astype(np.int32)
+    lab[g.random(tokens) < ignore_frac] = -100
+    return lab

@@ -118,3 +118,18 @@ def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(B, "_lib", None)
     with pytest.raises(RuntimeError, match="not built"):
         B.lib()
+
+
+def test_plan_holds_streamed_head():
+    """A 2000-row bf16 head on the toy stack: slices of as many whole 256-row groups as
+    fit one layer slot, each stored as one more blob of the pinned store."""
+    w = synth.WORKLOADS["toy"]
+    d0, h0, blob = B.ls_plan_bytes(B.make_config(w))
+    d1, h1, _ = B.ls_plan_bytes(B.make_config(w, vocab=2000))
+    rows = blob // (2 * w.hidden) // 256 * 256
+    slices = -(-2000 // rows)
+    assert h0 == blob * w.n_layers and h1 == blob * (w.n_layers + slices)
+    assert d1 - d0 >= 4 * w.tokens * rows + 2 * w.tokens * rows + 4 * w.tokens * w.hidden
+    bad = B.make_config(w, vocab=-1)
+    with pytest.raises(B.LsError):
+        B.ls_plan_bytes(bad)
