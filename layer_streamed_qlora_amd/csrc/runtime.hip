@@ -103,7 +103,8 @@ DevPlan make_plan(const ls_config& c, const BlobLayout& L) {
   P.act = take(2 * T * I);
   P.rstd1 = take(4 * T);
   P.rstd2 = take(4 * T);
-  P.hs = take(2 * T * R7);
+  // s X A^T of every layer, kept from the forward for the recompute and the dB products
+  P.hs = take(2 * T * R7 * (uint64_t)c.n_layers);
   P.gs = take(2 * T * R7);
   P.lse = take(4 * T * (uint64_t)c.n_heads);
   P.dd = take(4 * T * (uint64_t)c.n_heads);
@@ -386,6 +387,11 @@ ls_status release_layer(ls_ctx* c, int l) {
 }
 
 // ------------------------------------------------------------------ executor
+// s X A^T of layer l, bf16 [T, 7 r16] (row stride 7 r16), layers max_tokens rows apart
+uint16_t* hs_of(const ls_ctx* c, int l) {
+  return c->dp<uint16_t>(c->plan.hs) + (uint64_t)l * c->cfg.max_tokens * 7 * r16_of(c->cfg);
+}
+
 struct Dims {
   int T, batch, seq, h, hq, hkv, hd, qd, kvd, qkvd, I, r, r16, R7;
   float s;
@@ -479,7 +485,7 @@ ls_status lora_down(ls_ctx* c, int l, const Dims& d, const uint16_t* x, int ldx,
   a.T = d.T;
   FcJob& j = a.job[a.n_jobs++];
   j.X = x; j.ldx = ldx; j.W = lora_at(c, l, c->plan.a16[p0]); j.K = K; j.N = ng * d.r16; j.alpha = d.s;
-  j.out = c->dp<uint16_t>(c->plan.hs) + p0 * d.r16; j.ldo = d.R7;
+  j.out = hs_of(c, l) + p0 * d.r16; j.ldo = d.R7;
   KTimer kt(c, LS_KC_LORA, 2.0 * d.T * ng * d.r * K, 2.0 * d.T * K + 2.0 * ng * d.r * K + 2.0 * d.T * ng * d.r);
   HIPCHK(c, launch_lora_fc(a, c->cs));
   return LS_OK;
@@ -540,7 +546,9 @@ ls_status layer_forward(ls_ctx* c, int l, const uint8_t* blob, const Dims& d, co
   uint16_t* n2 = c->dp<uint16_t>(c->plan.n2);
   float* gu = c->dp<float>(c->plan.gu);
   uint16_t* act = c->dp<uint16_t>(c->plan.act);
-  uint16_t* hs = c->dp<uint16_t>(c->plan.hs);
+  uint16_t* hs = hs_of(c, l);
+  // the recompute reads the forward's s X A^T of this layer (same inputs, same kernel)
+  const bool down = lora && mode == MODE_FWD;
   const uint16_t* g1 = reinterpret_cast<const uint16_t*>(blob + c->lay.off_g1);
   const uint16_t* g2 = reinterpret_cast<const uint16_t*>(blob + c->lay.off_g2);
   const double tb = 2.0 * d.T;
@@ -549,7 +557,7 @@ ls_status layer_forward(ls_ctx* c, int l, const uint8_t* blob, const Dims& d, co
     KTimer kt(c, LS_KC_GLUE, 0.0, 2 * tb * d.h);
     HIPCHK(c, launch_rmsnorm_fwd(x_in, nullptr, g1, n1, c->dp<float>(c->plan.rstd1), d.T, d.h, g.rms_eps, c->cs));
   }
-  if (lora) { ls_status st = lora_down(c, l, d, n1, d.h, LS_PROJ_Q, 3, d.h); if (st) return st; }
+  if (down) { ls_status st = lora_down(c, l, d, n1, d.h, LS_PROJ_Q, 3, d.h); if (st) return st; }
   {
     FwdArgs f;
     f.x = n1; f.ldx = d.h; f.M = d.T; f.K = d.h; f.n_groups = 3;
@@ -569,7 +577,7 @@ ls_status layer_forward(ls_ctx* c, int l, const uint8_t* blob, const Dims& d, co
     HIPCHK(c, launch_gemm_fwd(f, c->cs));
   }
   { ls_status st = attn_fwd(c, d, qkv, att, mode == MODE_RECOMPUTE ? c->dp<float>(c->plan.o32) : nullptr); if (st) return st; }
-  if (lora) { ls_status st = lora_down(c, l, d, att, d.qd, LS_PROJ_O, 1, d.qd); if (st) return st; }
+  if (down) { ls_status st = lora_down(c, l, d, att, d.qd, LS_PROJ_O, 1, d.qd); if (st) return st; }
   {
     FwdArgs f;
     f.x = att; f.ldx = d.qd; f.M = d.T; f.K = d.qd; f.n_groups = 1;
@@ -586,7 +594,7 @@ ls_status layer_forward(ls_ctx* c, int l, const uint8_t* blob, const Dims& d, co
     KTimer kt(c, LS_KC_GLUE, 0.0, 2 * tb * d.h);
     HIPCHK(c, launch_rmsnorm_fwd(nullptr, hb, g2, n2, c->dp<float>(c->plan.rstd2), d.T, d.h, g.rms_eps, c->cs));
   }
-  if (lora) { ls_status st = lora_down(c, l, d, n2, d.h, LS_PROJ_GATE, 2, d.h); if (st) return st; }
+  if (down) { ls_status st = lora_down(c, l, d, n2, d.h, LS_PROJ_GATE, 2, d.h); if (st) return st; }
   const bool fuse_swiglu = 2 * d.r16 <= 64;
   {
     FwdArgs f;
@@ -616,7 +624,7 @@ ls_status layer_forward(ls_ctx* c, int l, const uint8_t* blob, const Dims& d, co
     KTimer kt(c, LS_KC_GLUE, 0.0, 5 * tb * d.I);
     HIPCHK(c, launch_swiglu_fwd(gu, d.I, act, d.T, c->cs));
   }
-  if (lora) { ls_status st = lora_down(c, l, d, act, d.I, LS_PROJ_DOWN, 1, d.I); if (st) return st; }
+  if (down) { ls_status st = lora_down(c, l, d, act, d.I, LS_PROJ_DOWN, 1, d.I); if (st) return st; }
   if (mode == MODE_RECOMPUTE) return LS_OK;
   {
     FwdArgs f;
@@ -685,7 +693,7 @@ ls_status lora_grads_AB(ls_ctx* c, int l, const Dims& d, int p0, int n, const ui
     if (on && R.dB) {
       TcJob jb;
       jb.A = dy + col; jb.lda = lddy; jb.M = P.n_out;
-      jb.B = c->dp<uint16_t>(c->plan.hs) + p * d.r16; jb.ldb = d.R7; jb.N = d.r16;
+      jb.B = hs_of(c, l) + p * d.r16; jb.ldb = d.R7; jb.N = d.r16;
       jb.C[0] = R.dB; jb.scm = d.r; jb.scn = 1; jb.ncols = d.r16; jb.nvalid = d.r;
       a.job[a.n_jobs++] = jb;
       flop += 2.0 * d.T * P.n_out * d.r;
