@@ -104,6 +104,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-profile", action="store_true")
     ap.add_argument("--vocab", type=int, default=128256, help="output-head rows for the head+loss measurement (0 = none)")
+    ap.add_argument("--store-file", default="", help="keep the frozen base in this file instead of pinned RAM")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); this build has no multi-GPU path.",
@@ -122,7 +123,8 @@ def main():
         w = w.with_(n_layers=args.layers)
     T = w.tokens
     profile = 0 if args.no_profile else 1
-    cfg = B.make_config(w, n_buffers=args.buffers, profile=profile, adamw=1, vocab=args.vocab)
+    cfg = B.make_config(w, n_buffers=args.buffers, profile=profile, adamw=1, vocab=args.vocab,
+                        store_path=args.store_file or None)
     t0 = time.time()
     ctx = B.Context(cfg)
     for l in range(w.n_layers):
@@ -205,7 +207,8 @@ def main():
                                f"SwiGLU {w.intermediate}, NF4 block 64 + double-quant absmax, "
                                f"LoRA r {w.lora_r} alpha {int(w.lora_alpha)} on 7 projections, "
                                f"streamed through {args.buffers} device slots",
-                   "batch": w.batch, "seq": w.seq, "tokens_per_step": T, "parallelism": "none (1 GPU)"},
+                   "batch": w.batch, "seq": w.seq, "tokens_per_step": T, "parallelism": "none (1 GPU)",
+                   "store": "file (page cache dropped after each read)" if args.store_file else "pinned host RAM"},
     }
     if profile:
         kern = {k: {"launches_per_step": v[0] / args.steps, "ms_per_step": v[1] / args.steps,

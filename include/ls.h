@@ -84,7 +84,16 @@ typedef struct ls_config {
                               adapter of lora_mask and enable ls_adamw_step */
   int32_t vocab;           /* 0 = no output head; else rows of the frozen bf16 output head
                               [vocab, hidden] (ls_stage_head, ls_head_loss) */
+  int32_t store;           /* LS_STORE_HOST: the frozen base in pinned host RAM;
+                              LS_STORE_FILE: in the file store_path (one blob per layer and
+                              head slice), read into one pinned staging buffer per slot */
+  char store_path[256];    /* LS_STORE_FILE: NUL-terminated path; the file is created (or
+                              truncated) by ls_create and removed by ls_destroy */
 } ls_config;
+
+/* Where the frozen base lives ("Soup CLI fine-tunes Llama-3.1-8B on a 4 GB laptop GPU
+ * ...", third paragraph: the base stays in CPU RAM or on NVMe). */
+enum { LS_STORE_HOST = 0, LS_STORE_FILE = 1 };
 
 /* Host-side source weights for one layer (bf16 bit patterns, host pointers). */
 typedef struct ls_layer_host {
@@ -116,6 +125,9 @@ typedef struct ls_stats {
   uint64_t h2d_bytes;          /* host->device layer bytes copied since create */
   uint64_t h2d_copies;         /* layer copies since create */
   uint64_t slot_hits;          /* layer reads served by a slot that already held it */
+  uint64_t store_reads;        /* LS_STORE_FILE: blobs read from the file since create */
+  uint64_t store_uncached;     /* LS_STORE_FILE: 1 if every blob is dropped from the OS page cache
+                                  after use, so each read comes from the file's device */
   double last_copy_ms;         /* profile=1: summed copy time of the last fwd+bwd */
   double last_compute_ms;      /* profile=1: summed per-layer compute time of last fwd+bwd */
   double last_overlap_ms;      /* profile=1: copy time that overlapped compute */
@@ -200,7 +212,8 @@ ls_status ls_forward(ls_ctx* ctx, const void* X, int32_t batch, int32_t seq, int
  */
 ls_status ls_backward(ls_ctx* ctx, const void* dY, void* dX, int32_t accumulate);
 
-/* ls_sync — wait for both streams; returns the first deferred HIP error. */
+/* ls_sync — wait for both streams; returns the first deferred HIP error, or LS_ERR_HIP
+ * with a message if a read from the LS_STORE_FILE store failed. */
 ls_status ls_sync(ls_ctx* ctx);
 
 /* ls_get_stats — counters since ls_create (host pointer out). */

@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(_PKG, "liblsq.so")
 
 LS_OK, LS_ERR_INVALID, LS_ERR_STATE, LS_ERR_BUDGET, LS_ERR_OOM, LS_ERR_HIP = range(6)
 LS_QUANT_NF4, LS_QUANT_BF16 = 0, 1
+LS_STORE_HOST, LS_STORE_FILE = 0, 1
 PROJS = ("q", "k", "v", "o", "gate", "up", "down")
 LS_KC_N = 7
 KERNEL_CLASSES = ("gemm_fwd", "gemm_bwd", "attn", "lora", "glue", "optim", "head")
@@ -37,7 +38,7 @@ class ls_config(C.Structure):
         ("quant", C.c_int32), ("nf4_block", C.c_int32), ("double_quant", C.c_int32), ("lora_r", C.c_int32),
         ("lora_alpha", C.c_float), ("lora_mask", C.c_uint32), ("n_buffers", C.c_int32), ("max_tokens", C.c_int32),
         ("max_seq", C.c_int32), ("resident", C.c_int32), ("vram_budget", C.c_uint64), ("profile", C.c_int32),
-        ("adamw", C.c_int32), ("vocab", C.c_int32),
+        ("adamw", C.c_int32), ("vocab", C.c_int32), ("store", C.c_int32), ("store_path", C.c_char * 256),
     ]
 
 
@@ -54,6 +55,7 @@ class ls_stats(C.Structure):
     _fields_ = [
         ("blob_bytes", C.c_uint64), ("store_bytes", C.c_uint64), ("device_bytes", C.c_uint64),
         ("h2d_bytes", C.c_uint64), ("h2d_copies", C.c_uint64), ("slot_hits", C.c_uint64),
+        ("store_reads", C.c_uint64), ("store_uncached", C.c_uint64),
         ("last_copy_ms", C.c_double), ("last_compute_ms", C.c_double), ("last_overlap_ms", C.c_double),
         ("last_span_ms", C.c_double),
         ("k_launches", C.c_uint64 * LS_KC_N), ("k_ms", C.c_double * LS_KC_N),
@@ -121,7 +123,7 @@ def _check(status, ctx=None):
 
 
 def make_config(w, n_buffers=2, max_tokens=None, max_seq=None, resident=0, vram_budget=0, profile=0,
-                lora_mask=0x7F, n_layers=None, adamw=0, vocab=0) -> ls_config:
+                lora_mask=0x7F, n_layers=None, adamw=0, vocab=0, store_path=None) -> ls_config:
     """ls_config for a workload description (``synth.Workload``)."""
     return ls_config(
         n_layers=w.n_layers if n_layers is None else n_layers, hidden=w.hidden, n_heads=w.n_heads,
@@ -130,7 +132,8 @@ def make_config(w, n_buffers=2, max_tokens=None, max_seq=None, resident=0, vram_
         double_quant=int(w.double_quant), lora_r=w.lora_r, lora_alpha=w.lora_alpha, lora_mask=lora_mask,
         n_buffers=n_buffers, max_tokens=w.tokens if max_tokens is None else max_tokens,
         max_seq=w.seq if max_seq is None else max_seq, resident=resident, vram_budget=vram_budget, profile=profile,
-        adamw=adamw, vocab=vocab)
+        adamw=adamw, vocab=vocab, store=LS_STORE_FILE if store_path else LS_STORE_HOST,
+        store_path=os.fsencode(store_path) if store_path else b"")
 
 
 # ------------------------------------------------------------------ host calls

@@ -12,8 +12,14 @@
 // same streamed layer with the adapters off (same page, third paragraph).
 #include <hip/hip_runtime.h>
 
+#include <fcntl.h>
+#include <sys/stat.h>
+#include <unistd.h>
+
 #include <algorithm>
 #include <array>
+#include <atomic>
+#include <cerrno>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -220,6 +226,20 @@ struct ls_ctx {
   bool prof_collected = false;
   bool head_staged = false;
   bool fwd_ref = false;                 // the last forward also ran the reference pass
+  // LS_STORE_FILE: the store file, one pinned staging buffer per slot, one read job per
+  // pool index (fixed contents: a job may be enqueued again before its last run ends)
+  struct ReadJob {
+    ls_ctx* c;
+    uint8_t* buf;
+    uint64_t off, len;
+  };
+  int fd = -1;
+  bool uncached = false;                // pages dropped from the OS cache after use
+  uint64_t stride = 0;                  // blob bytes rounded up to 4096 (file offsets, read sizes)
+  std::vector<uint8_t*> staging;
+  std::vector<ReadJob> jobs;
+  std::atomic<int> store_err{0};
+  std::atomic<uint64_t> store_reads{0};
   float levels_h[16];
   // state
   bool fwd_valid = false, fwd_lora = false;
@@ -347,6 +367,52 @@ void collect_profile(ls_ctx* c) {
   c->stats.last_span_ms = last;
 }
 
+// ------------------------------------------------------------------ file store
+// Host function on the copy stream: read one blob (job->len bytes at job->off) into the
+// staging buffer.  No HIP call here; a failure is recorded for ls_sync.
+void store_read(void* p) {
+  auto* j = static_cast<ls_ctx::ReadJob*>(p);
+  uint64_t done = 0;
+  while (done < j->len) {
+    const ssize_t r = pread(j->c->fd, j->buf + done, j->len - done, (off_t)(j->off + done));
+    if (r < 0 && errno == EINTR) continue;
+    if (r <= 0) {
+      int expected = 0;
+      j->c->store_err.compare_exchange_strong(expected, r < 0 ? errno : EIO);
+      return;
+    }
+    done += (uint64_t)r;
+  }
+  if (j->c->uncached) posix_fadvise(j->c->fd, (off_t)j->off, (off_t)j->len, POSIX_FADV_DONTNEED);
+  j->c->store_reads.fetch_add(1);
+}
+
+// The host buffer a layer (or head slice) is staged through: its pinned blob, or, with
+// the file store, the first staging buffer, cleared (the blob's padding stays zero).
+uint8_t* stage_buffer(ls_ctx* c, int l) {
+  if (c->fd < 0) return c->host[l];
+  std::memset(c->staging[0], 0, c->stride);
+  return c->staging[0];
+}
+
+// After staging: write the blob to its place in the store file.
+ls_status store_write(ls_ctx* c, int l, const uint8_t* blob) {
+  if (c->fd < 0) return LS_OK;
+  uint64_t done = 0;
+  while (done < c->stride) {
+    const ssize_t r = pwrite(c->fd, blob + done, c->stride - done, (off_t)((uint64_t)l * c->stride + done));
+    if (r < 0 && errno == EINTR) continue;
+    if (r <= 0) return fail(c, LS_ERR_INVALID, "write to the store file failed: %s", strerror(r < 0 ? errno : EIO));
+    done += (uint64_t)r;
+  }
+  if (c->uncached) {
+    const off_t off = (off_t)((uint64_t)l * c->stride);
+    if (fdatasync(c->fd) != 0) return fail(c, LS_ERR_INVALID, "flush of the store file failed: %s", strerror(errno));
+    posix_fadvise(c->fd, off, (off_t)c->stride, POSIX_FADV_DONTNEED);
+  }
+  return LS_OK;
+}
+
 // ------------------------------------------------------------------ pool
 uint8_t* slot_ptr(ls_ctx* c, int layer) {
   const int s = c->cfg.resident ? layer : layer % c->cfg.n_buffers;
@@ -361,7 +427,15 @@ ls_status ensure_copy(ls_ctx* c, int l) {
   if (c->cons_rec[s]) HIPCHK(c, hipStreamWaitEvent(c->ps, c->consumed[s], 0));
   {
     Span sp(c, c->ps, true);
-    HIPCHK(c, hipMemcpyAsync(slot_ptr(c, l), c->host[l], c->lay.bytes, hipMemcpyHostToDevice, c->ps));
+    if (c->fd >= 0) {
+      // read the blob from the store file into this slot's staging buffer (a host
+      // function in stream order: it runs after the previous copy out of the buffer),
+      // then copy it to the slot
+      HIPCHK(c, hipLaunchHostFunc(c->ps, store_read, &c->jobs[l]));
+      HIPCHK(c, hipMemcpyAsync(slot_ptr(c, l), c->jobs[l].buf, c->lay.bytes, hipMemcpyHostToDevice, c->ps));
+    } else {
+      HIPCHK(c, hipMemcpyAsync(slot_ptr(c, l), c->host[l], c->lay.bytes, hipMemcpyHostToDevice, c->ps));
+    }
   }
   HIPCHK(c, hipEventRecord(c->ready[s], c->ps));
   c->ready_rec[s] = 1;
@@ -841,7 +915,10 @@ ls_status ls_plan_bytes(const ls_config* cfg, uint64_t* device_bytes, uint64_t* 
   const BlobLayout L = make_layout(*cfg);
   const DevPlan P = make_plan(*cfg, L);
   if (device_bytes) *device_bytes = P.total;
-  if (host_bytes) *host_bytes = L.bytes * (uint64_t)(cfg->n_layers + P.head_slices);
+  if (host_bytes)
+    *host_bytes = cfg->store == LS_STORE_FILE
+                      ? (L.bytes + 4095) / 4096 * 4096 * (uint64_t)(cfg->resident ? 1 : cfg->n_buffers)
+                      : L.bytes * (uint64_t)(cfg->n_layers + P.head_slices);
   if (blob_bytes) *blob_bytes = L.bytes;
   return LS_OK;
 }
@@ -894,14 +971,46 @@ ls_status ls_create(const ls_config* cfg, void* compute_stream, void* copy_strea
   }
   c->lora.resize(cfg->n_layers);
   c->staged.assign(cfg->n_layers, 0);
-  c->host.assign(cfg->n_layers + P.head_slices, nullptr);
-  for (int l = 0; l < cfg->n_layers + P.head_slices; ++l) {
-    if (hipHostMalloc((void**)&c->host[l], L.bytes, hipHostMallocDefault) != hipSuccess) {
-      c->host[l] = nullptr;
-      c->err = "pinned host allocation of the layer store failed";
-      return bail(LS_ERR_OOM);
+  const int n_blobs = cfg->n_layers + P.head_slices;
+  c->host.assign(n_blobs, nullptr);
+  if (cfg->store == LS_STORE_FILE) {
+    // the store is a file of n_blobs blobs, 4096 bytes apart.  Reads go through the page
+    // cache into the pinned staging buffers (direct I/O cannot pin that memory), and
+    // every blob's pages are dropped from the cache after it is staged and after each
+    // read, so each read comes from the file's device rather than from RAM.
+    c->stride = (L.bytes + 4095) / 4096 * 4096;
+    c->fd = open(cfg->store_path, O_RDWR | O_CREAT | O_TRUNC, 0600);
+    if (c->fd < 0) {
+      c->err = std::string("cannot create the store file ") + cfg->store_path + ": " + strerror(errno);
+      return bail(LS_ERR_INVALID);
     }
-    std::memset(c->host[l], 0, L.bytes);
+    if (ftruncate(c->fd, (off_t)(c->stride * (uint64_t)n_blobs)) != 0) {
+      c->err = std::string("cannot size the store file: ") + strerror(errno);
+      return bail(LS_ERR_INVALID);
+    }
+    const int n_stage = cfg->resident ? 1 : cfg->n_buffers;
+    c->staging.assign(n_stage, nullptr);
+    for (int i = 0; i < n_stage; ++i) {
+      if (hipHostMalloc((void**)&c->staging[i], c->stride, hipHostMallocDefault) != hipSuccess) {
+        c->staging[i] = nullptr;
+        c->err = "pinned host allocation of the staging buffers failed";
+        return bail(LS_ERR_OOM);
+      }
+      std::memset(c->staging[i], 0, c->stride);
+    }
+    c->uncached = posix_fadvise(c->fd, 0, 0, POSIX_FADV_DONTNEED) == 0;
+    c->jobs.resize(n_blobs);
+    for (int l = 0; l < n_blobs; ++l)
+      c->jobs[l] = {c, c->staging[cfg->resident ? 0 : l % cfg->n_buffers], (uint64_t)l * c->stride, c->stride};
+  } else {
+    for (int l = 0; l < n_blobs; ++l) {
+      if (hipHostMalloc((void**)&c->host[l], L.bytes, hipHostMallocDefault) != hipSuccess) {
+        c->host[l] = nullptr;
+        c->err = "pinned host allocation of the layer store failed";
+        return bail(LS_ERR_OOM);
+      }
+      std::memset(c->host[l], 0, L.bytes);
+    }
   }
   if (hipMalloc((void**)&c->dbase, P.total) != hipSuccess) {
     c->dbase = nullptr;
@@ -925,7 +1034,9 @@ ls_status ls_create(const ls_config* cfg, void* compute_stream, void* copy_strea
     return bail(LS_ERR_HIP);
   }
   c->stats.blob_bytes = L.bytes;
-  c->stats.store_bytes = L.bytes * (uint64_t)(cfg->n_layers + P.head_slices);
+  c->stats.store_bytes = cfg->store == LS_STORE_FILE ? c->stride * (uint64_t)n_blobs
+                                                    : L.bytes * (uint64_t)(cfg->n_layers + P.head_slices);
+  c->stats.store_uncached = c->uncached ? 1 : 0;
   c->stats.device_bytes = P.total;
   *out = c;
   return LS_OK;
@@ -938,7 +1049,7 @@ ls_status ls_stage_layer(ls_ctx* c, int32_t layer, const ls_layer_host* w) {
   for (int p = 0; p < LS_N_PROJ; ++p)
     if (!w->w[p]) return fail(c, LS_ERR_INVALID, "null weight for projection %d", p);
   if (c->in_flight) return fail(c, LS_ERR_STATE, "a forward/backward is in flight: call ls_sync first");
-  uint8_t* blob = c->host[layer];
+  uint8_t* blob = stage_buffer(c, layer);
   std::memcpy(blob + c->lay.off_g1, w->g1, 2ull * c->cfg.hidden);
   std::memcpy(blob + c->lay.off_g2, w->g2, 2ull * c->cfg.hidden);
   for (int p = 0; p < LS_N_PROJ; ++p) {
@@ -956,6 +1067,7 @@ ls_status ls_stage_layer(ls_ctx* c, int32_t layer, const ls_layer_host* w) {
                     nullptr, nullptr);
     }
   }
+  if (ls_status st = store_write(c, layer, blob)) return st;
   c->staged[layer] = 1;
   // a slot holding the old contents of this layer is stale now
   for (auto& sl : c->slot_layer)
@@ -1075,12 +1187,17 @@ ls_status ls_sync(ls_ctx* c) {
   c->in_flight = false;
   collect_profile(c);
   c->prof_collected = true;
+  if (const int e = c->store_err.load()) {
+    c->sticky = LS_ERR_HIP;
+    return fail(c, LS_ERR_HIP, "read from the store file failed: %s", strerror(e));
+  }
   return LS_OK;
 }
 
 ls_status ls_get_stats(const ls_ctx* c, ls_stats* out) {
   if (!c || !out) return LS_ERR_INVALID;
   *out = c->stats;
+  out->store_reads = c->store_reads.load();
   return LS_OK;
 }
 
@@ -1095,6 +1212,11 @@ void ls_destroy(ls_ctx* c) {
   for (auto e : c->consumed) if (e) hipEventDestroy(e);
   if (c->dbase) hipFree(c->dbase);
   for (auto p : c->host) if (p) hipHostFree(p);
+  for (auto p : c->staging) if (p) hipHostFree(p);
+  if (c->fd >= 0) {
+    close(c->fd);
+    unlink(c->cfg.store_path);
+  }
   if (c->own_cs && c->cs) hipStreamDestroy(c->cs);
   if (c->own_ps && c->ps) hipStreamDestroy(c->ps);
   delete c;
@@ -1263,11 +1385,14 @@ ls_status ls_stage_head(ls_ctx* c, const uint16_t* w, const uint16_t* g_final) {
   const uint64_t row = 2ull * c->cfg.hidden;
   for (int j = 0; j < S; ++j) {
     const int64_t r0 = (int64_t)j * vs, rows = std::min<int64_t>(vs, c->cfg.vocab - r0);
-    std::memcpy(c->host[L + j], reinterpret_cast<const uint8_t*>(w) + (uint64_t)r0 * row, (uint64_t)rows * row);
+    uint8_t* blob = stage_buffer(c, L + j);
+    std::memcpy(blob, reinterpret_cast<const uint8_t*>(w) + (uint64_t)r0 * row, (uint64_t)rows * row);
+    if (ls_status st = store_write(c, L + j, blob)) return st;
     for (auto& sl : c->slot_layer)
       if (sl == L + j) sl = -1;
     if (c->cfg.resident) {
-      HIPCHK(c, hipMemcpyAsync(slot_ptr(c, L + j), c->host[L + j], c->lay.bytes, hipMemcpyHostToDevice, c->ps));
+      HIPCHK(c, hipMemcpyAsync(slot_ptr(c, L + j), blob, c->lay.bytes, hipMemcpyHostToDevice, c->ps));
+      HIPCHK(c, hipStreamSynchronize(c->ps));
       c->stats.h2d_bytes += c->lay.bytes;
       c->stats.h2d_copies += 1;
     }

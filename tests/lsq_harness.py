@@ -34,7 +34,7 @@ class GpuRun:
     """One context with staged layers and torch-owned adapters on cuda:0."""
 
     def __init__(self, w, layer_seeds, resident=0, n_buffers=2, profile=0, zero_b=False, max_tokens=None,
-                 max_seq=None, lora_mask=0x7F, weights=None, adamw=0, vocab=0):
+                 max_seq=None, lora_mask=0x7F, weights=None, adamw=0, vocab=0, store_path=None):
         import torch
         self.torch = torch
         self.w = w
@@ -42,7 +42,7 @@ class GpuRun:
         L = len(self.layer_seeds)
         cfg = B.make_config(w, n_buffers=n_buffers, resident=resident, profile=profile, n_layers=L,
                             max_tokens=max_tokens, max_seq=max_seq, lora_mask=lora_mask, adamw=adamw,
-                            vocab=vocab)
+                            vocab=vocab, store_path=store_path)
         self.ctx = B.Context(cfg)
         self.src = []
         for i, seed in enumerate(self.layer_seeds):

@@ -133,3 +133,17 @@ def test_plan_holds_streamed_head():
     bad = B.make_config(w, vocab=-1)
     with pytest.raises(B.LsError):
         B.ls_plan_bytes(bad)
+
+
+def test_file_store_plan_and_validation(tmp_path):
+    """With the base in a file, pinned host memory is one 4096-aligned staging blob per
+    slot instead of the whole store; a file store without a path is refused."""
+    w = synth.WORKLOADS["toy"]
+    _, h_ram, blob = B.ls_plan_bytes(B.make_config(w, n_buffers=3))
+    _, h_file, _ = B.ls_plan_bytes(B.make_config(w, n_buffers=3, store_path=str(tmp_path / "s.bin")))
+    assert h_ram == blob * w.n_layers
+    assert h_file == -(-blob // 4096) * 4096 * 3
+    bad = B.make_config(w)
+    bad.store = B.LS_STORE_FILE
+    with pytest.raises(B.LsError):
+        B.ls_plan_bytes(bad)

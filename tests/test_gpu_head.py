@@ -41,10 +41,11 @@ def oracle_labels(lab):
 
 
 class HeadRun:
-    def __init__(self, resident=0, n_buffers=2, zero_b=False):
+    def __init__(self, resident=0, n_buffers=2, zero_b=False, store_path=None):
         import torch
         self.torch = torch
-        self.run = H.GpuRun(TOY, [0, 1], resident=resident, n_buffers=n_buffers, zero_b=zero_b, vocab=V)
+        self.run = H.GpuRun(TOY, [0, 1], resident=resident, n_buffers=n_buffers, zero_b=zero_b, vocab=V,
+                            store_path=store_path)
         self.Wh, self.gf = synth.head_weights(TOY, V)
         self.run.ctx.stage_head(synth.bf16_bits(self.Wh), synth.bf16_bits(self.gf))
 
@@ -172,12 +173,12 @@ def test_dpo_parity_and_full_chain():
 
 
 @pytest.mark.parametrize("kind", [B.LS_LOSS_SFT, B.LS_LOSS_DPO])
-def test_head_streamed_equals_resident_bitwise(kind):
+def test_head_streamed_equals_resident_bitwise(kind, tmp_path):
     lab = toy_labels()
     outs = []
-    for resident, nb in ((1, 2), (0, 2), (0, 3)):
-        say("case: head kind", kind, "resident", resident, "slots", nb)
-        hr = HeadRun(resident=resident, n_buffers=nb)
+    for resident, nb, path in ((1, 2, None), (0, 2, None), (0, 3, None), (0, 2, str(tmp_path / "store.bin"))):
+        say("case: head kind", kind, "resident", resident, "slots", nb, "file store" if path else "")
+        hr = HeadRun(resident=resident, n_buffers=nb, store_path=path)
         outs.append(hr.step(kind, lab, beta=0.3))
         hr.close()
     a = outs[0]

@@ -174,3 +174,40 @@ def test_lora_ranks(rank):
     errs, fails = H.compare(gpu, ora)
     say({k: f"{v:.2e}" for k, v in errs.items() if k in ("Y", "dX")})
     assert not fails, fails
+
+
+def test_file_store_equals_host_store_bitwise(tmp_path):
+    """The base kept in a file and read through pinned staging buffers gives the same bits
+    as the pinned-RAM store, over two steps; every copy is one file read, and the file is
+    gone after ls_destroy."""
+    import os
+    w = TOY
+    L = 4
+    x, dy = synth.activations(w)
+    outs = []
+    for path in (None, str(tmp_path / "store.bin")):
+        say("case: toy store", "file" if path else "host")
+        run = H.GpuRun(w, range(L), store_path=path)
+        outs.append([run.step(x, dy, w.batch, w.seq, with_ref=True) for _ in range(2)])
+        st = run.ctx.stats()
+        if path is not None:
+            say("store reads", st.store_reads, "copies", st.h2d_copies, "uncached", st.store_uncached)
+            assert st.store_reads == st.h2d_copies > 0
+        run.close()
+        if path is not None:
+            assert not os.path.exists(path)
+    for a, b in zip(*outs):
+        for k in ("Y", "Y_ref", "dX"):
+            assert np.array_equal(a[k].view(np.uint32), b[k].view(np.uint32)), k
+        for l in range(L):
+            for p in H.PROJS:
+                assert np.array_equal(a["dA"][l][p].view(np.uint32), b["dA"][l][p].view(np.uint32)), (l, p)
+                assert np.array_equal(a["dB"][l][p].view(np.uint32), b["dB"][l][p].view(np.uint32)), (l, p)
+
+
+def test_file_store_bad_path_is_refused():
+    from layer_streamed_qlora_amd import binding as B
+    cfg = B.make_config(TOY, store_path="/nonexistent-dir/for/sure/store.bin")
+    with pytest.raises(B.LsError) as e:
+        B.Context(cfg)
+    assert e.value.status == B.LS_ERR_INVALID
