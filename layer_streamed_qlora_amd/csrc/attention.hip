@@ -75,40 +75,50 @@ __global__ void __launch_bounds__(256) k_attn_fwd(AttnArgs a) {
     }
   };
   TileMover<HD, 256> tk, tv;
-  // pass 1: row maximum m and sum l of exp2(t - m) (each lane half sums its own keys)
+  // pass 1: row maximum m and sum l of exp2(t - m) (each lane half sums its own keys),
+  // or the values an earlier forward over the same q, k recorded
   float m = -INFINITY, l = 0.f;
-  tk.load(rk, a.ldqkv, 0);
-  for (int kb = 0; kb < n_kb; ++kb) {
-    __syncthreads();                    // the previous tile is no longer read
-    tk.store_rows(sk);
-    __syncthreads();
-    if (kb + 1 < n_kb) {
-      tk.load(rk, a.ldqkv, (kb + 1) * KB);
-    } else {                            // the second pass starts from key 0
-      tk.load(rk, a.ldqkv, 0);
-      tv.load(rv, a.ldqkv, 0);
+  float lt;
+  if (a.stats_in) {
+    const float2 st = a.stats_in[(int64_t)bh * a.S + min(q, a.S - 1)];
+    m = st.x;
+    lt = st.y;
+    tk.load(rk, a.ldqkv, 0);
+    tv.load(rv, a.ldqkv, 0);
+  } else {
+    tk.load(rk, a.ldqkv, 0);
+    for (int kb = 0; kb < n_kb; ++kb) {
+      __syncthreads();                    // the previous tile is no longer read
+      tk.store_rows(sk);
+      __syncthreads();
+      if (kb + 1 < n_kb) {
+        tk.load(rk, a.ldqkv, (kb + 1) * KB);
+      } else {                            // the second pass starts from key 0
+        tk.load(rk, a.ldqkv, 0);
+        tv.load(rv, a.ldqkv, 0);
+      }
+      const int k0 = kb * KB;
+      if (k0 > qw + 31) continue;         // tile entirely after this wave's queries
+      f32x16_t s[2];
+      scores(s, k0);
+      float mb = -INFINITY;
+  #pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+  #pragma unroll
+        for (int v = 0; v < 16; ++v) mb = fmaxf(mb, s[kk][v]);
+      mb = fmaxf(mb, __shfl_xor(mb, 32));
+      const float mn = fmaxf(m, mb);
+      const float mu = mn == -INFINITY ? 0.f : mn;
+      float ls = 0.f;
+  #pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+  #pragma unroll
+        for (int v = 0; v < 16; ++v) ls += __builtin_amdgcn_exp2f(s[kk][v] - mu);
+      l = l * __builtin_amdgcn_exp2f(m - mu) + ls;
+      m = mn;
     }
-    const int k0 = kb * KB;
-    if (k0 > qw + 31) continue;         // tile entirely after this wave's queries
-    f32x16_t s[2];
-    scores(s, k0);
-    float mb = -INFINITY;
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) mb = fmaxf(mb, s[kk][v]);
-    mb = fmaxf(mb, __shfl_xor(mb, 32));
-    const float mn = fmaxf(m, mb);
-    const float mu = mn == -INFINITY ? 0.f : mn;
-    float ls = 0.f;
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) ls += __builtin_amdgcn_exp2f(s[kk][v] - mu);
-    l = l * __builtin_amdgcn_exp2f(m - mu) + ls;
-    m = mn;
+    lt = l + __shfl_xor(l, 32);
   }
-  const float lt = l + __shfl_xor(l, 32);
   const float inv = 1.f / lt;           // lt >= 1: the maximum's own term
   // pass 2: P = exp2(t - m) / l, rounded to bf16, times V
   f32x16_t o[ND];
@@ -154,6 +164,7 @@ __global__ void __launch_bounds__(256) k_attn_fwd(AttnArgs a) {
         if (dst32) *reinterpret_cast<float4*>(dst32 + col) = v4;
       }
     if (hh == 0 && a.lse) a.lse[(int64_t)bh * a.S + q] = m + __builtin_amdgcn_logf(lt);
+    if (hh == 0 && a.stats_out) a.stats_out[(int64_t)bh * a.S + q] = make_float2(m, lt);
   }
 }
 

@@ -188,6 +188,11 @@ struct AttnArgs {
   const uint16_t* dout = nullptr; int32_t lddo = 0;   // backward: dO, bf16 like O
   float* dd = nullptr;                                // backward scratch [batch * hq * S]: rowsum(dO * O)
   float* dqkv = nullptr; int32_t lddqkv = 0;          // backward: float32 dq | dk | dv, layout of qkv
+  // forward: per query row (m, l) = the row maximum of the base-2 scaled scores and the sum
+  // of exp2(t - m), [batch * hq * S]; written if stats_out is set; if stats_in holds the
+  // values of an earlier forward over the same q, k, the first pass is skipped
+  float2* stats_out = nullptr;
+  const float2* stats_in = nullptr;
 };
 // O and lse
 hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t s);

@@ -59,7 +59,7 @@ struct DevPlan {
   uint64_t total = 0;
   uint64_t slots = 0, ck = 0, xref = 0;
   uint64_t n1 = 0, qkv = 0, att = 0, hb = 0, n2 = 0, gu = 0, act = 0, rstd1 = 0, rstd2 = 0;
-  uint64_t hs = 0, gs = 0, lse = 0, dd = 0, o32 = 0;
+  uint64_t hs = 0, gs = 0, lse = 0, dd = 0, o32 = 0, astats = 0;
   uint64_t dya = 0, dyb = 0, dh32 = 0, dh16 = 0, dgu = 0, datt = 0, dqkv = 0, dqkv32 = 0, dn32 = 0;
   uint64_t lora = 0, lora_per_layer = 0, partial = 0, partial_bytes = 0;
   uint64_t levels = 0, rope = 0;
@@ -115,6 +115,8 @@ DevPlan make_plan(const ls_config& c, const BlobLayout& L) {
   P.lse = take(4 * T * (uint64_t)c.n_heads);
   P.dd = take(4 * T * (uint64_t)c.n_heads);
   P.o32 = take(4 * T * qd);
+  // attention row statistics (max, sum) of every layer's forward, read by its recompute
+  P.astats = take(8 * T * (uint64_t)c.n_heads * (uint64_t)c.n_layers);
   P.dya = take(2 * T * h);
   P.dyb = take(2 * T * h);
   P.dh32 = take(4 * T * h);
@@ -579,11 +581,16 @@ AttnArgs attn_args(ls_ctx* c, const Dims& d, const uint16_t* qkv, uint16_t* out)
 
 // Causal attention forward, O = softmax(c Q K^T) V, plus the per-row log-sum-exp the
 // backward uses to rebuild P; out32 (nullable) keeps O before rounding for the backward.
-ls_status attn_fwd(ls_ctx* c, const Dims& d, const uint16_t* qkv, uint16_t* out, float* out32) {
-  const double fl = 6.0 * d.batch * d.hq * (double)d.seq * (d.seq + 1) / 2 * d.hd;   // scores twice
+// stats_out / stats_in: the layer's per-row softmax statistics, kept by the forward and
+// read back by the recompute so that it skips the statistics pass.
+ls_status attn_fwd(ls_ctx* c, const Dims& d, const uint16_t* qkv, uint16_t* out, float* out32, float2* stats_out,
+                   const float2* stats_in) {
+  const double fl = (stats_in ? 4.0 : 6.0) * d.batch * d.hq * (double)d.seq * (d.seq + 1) / 2 * d.hd;
   KTimer kt(c, LS_KC_ATTN, fl, 2.0 * d.T * (d.qkvd + d.qd) + 4.0 * d.T * d.hq + (out32 ? 4.0 * d.T * d.qd : 0.0));
   AttnArgs a = attn_args(c, d, qkv, out);
   a.out32 = out32;
+  a.stats_out = stats_out;
+  a.stats_in = stats_in;
   HIPCHK(c, launch_attn_fwd(a, c->cs));
   return LS_OK;
 }
@@ -650,7 +657,12 @@ ls_status layer_forward(ls_ctx* c, int l, const uint8_t* blob, const Dims& d, co
               tb * d.h + wbytes(c, 0) + wbytes(c, 1) + wbytes(c, 2) + tb * d.qkvd);
     HIPCHK(c, launch_gemm_fwd(f, c->cs));
   }
-  { ls_status st = attn_fwd(c, d, qkv, att, mode == MODE_RECOMPUTE ? c->dp<float>(c->plan.o32) : nullptr); if (st) return st; }
+  {
+    float2* stats = c->dp<float2>(c->plan.astats) + (uint64_t)l * c->cfg.max_tokens * c->cfg.n_heads;
+    ls_status st = attn_fwd(c, d, qkv, att, mode == MODE_RECOMPUTE ? c->dp<float>(c->plan.o32) : nullptr,
+                            mode == MODE_FWD && lora ? stats : nullptr, mode == MODE_RECOMPUTE ? stats : nullptr);
+    if (st) return st;
+  }
   if (down) { ls_status st = lora_down(c, l, d, att, d.qd, LS_PROJ_O, 1, d.qd); if (st) return st; }
   {
     FwdArgs f;
