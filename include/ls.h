@@ -79,7 +79,7 @@ typedef struct ls_config {
   int32_t resident;        /* 1 = keep every layer on the device (same blob layout;
                               parity reference for the streamed mode) */
   uint64_t vram_budget;    /* bytes the plan may use; 0 = free device memory */
-  int32_t profile;         /* 1 = time copies and per-layer compute with HIP events */
+  int32_t profile;         /* LS_PROFILE_OFF, LS_PROFILE_ALL or LS_PROFILE_GEMM (see ls_set_profile) */
   int32_t adamw;           /* 1 = also plan float32 AdamW moments (m and v) for every
                               adapter of lora_mask and enable ls_adamw_step */
   int32_t vocab;           /* 0 = no output head; else rows of the frozen bf16 output head
@@ -215,6 +215,21 @@ ls_status ls_backward(ls_ctx* ctx, const void* dY, void* dX, int32_t accumulate)
 /* ls_sync — wait for both streams; returns the first deferred HIP error, or LS_ERR_HIP
  * with a message if a read from the LS_STORE_FILE store failed. */
 ls_status ls_sync(ls_ctx* ctx);
+
+/*
+ * Profiling levels.  Timing is HIP events recorded on the compute stream around kernel
+ * launches; each event is a packet in the stream and widens the gap before the next
+ * kernel, so a timed run should record as few as it needs.
+ *   LS_PROFILE_OFF:  no events.
+ *   LS_PROFILE_ALL:  every launch (per-class times in ls_stats) and the copy / per-layer
+ *                    compute intervals (overlap figures).
+ *   LS_PROFILE_GEMM: only the forward dequant-GEMM launches (class LS_KC_GEMM_FWD).
+ */
+enum { LS_PROFILE_OFF = 0, LS_PROFILE_ALL = 1, LS_PROFILE_GEMM = 2 };
+
+/* ls_set_profile — change the profiling level for the calls that follow (no work may be
+ * in flight: call ls_sync first).  Errors: LS_ERR_INVALID (unknown level), LS_ERR_STATE. */
+ls_status ls_set_profile(ls_ctx* ctx, int32_t profile);
 
 /* ls_get_stats — counters since ls_create (host pointer out). */
 ls_status ls_get_stats(const ls_ctx* ctx, ls_stats* out);

@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(_PKG, "liblsq.so")
 LS_OK, LS_ERR_INVALID, LS_ERR_STATE, LS_ERR_BUDGET, LS_ERR_OOM, LS_ERR_HIP = range(6)
 LS_QUANT_NF4, LS_QUANT_BF16 = 0, 1
 LS_STORE_HOST, LS_STORE_FILE = 0, 1
+LS_PROFILE_OFF, LS_PROFILE_ALL, LS_PROFILE_GEMM = 0, 1, 2
 PROJS = ("q", "k", "v", "o", "gate", "up", "down")
 LS_KC_N = 7
 KERNEL_CLASSES = ("gemm_fwd", "gemm_bwd", "attn", "lora", "glue", "optim", "head")
@@ -93,6 +94,7 @@ SIGNATURES = {
     "ls_load_adapters": (C.c_int, [C.c_void_p, C.c_char_p]),
     "ls_check_adapter_file": (C.c_int, [C.POINTER(ls_config), C.c_char_p, C.c_char_p, C.c_size_t]),
     "ls_stage_head": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p]),
+    "ls_set_profile": (C.c_int, [C.c_void_p, C.c_int32]),
     "ls_head_loss": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32, C.c_float, C.c_void_p,
                                C.c_void_p]),
 }
@@ -238,6 +240,9 @@ class Context:
 
     def load_adapters(self, path):
         self._chk(lib().ls_load_adapters(self.h, os.fsencode(path)))
+
+    def set_profile(self, level):
+        self._chk(lib().ls_set_profile(self.h, int(level)))
 
     def stage_head(self, w_bits: np.ndarray, g_bits: np.ndarray):
         """w_bits: uint16 [vocab, hidden] (bf16 bits), g_bits: uint16 [hidden]."""

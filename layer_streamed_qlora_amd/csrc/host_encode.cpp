@@ -199,6 +199,7 @@ bool validate_config(const ls_config& c, const char** why) {
   REQ(c.max_seq >= 1 && c.max_seq <= c.max_tokens && c.max_seq <= 8192, "max_seq must be in 1..min(max_tokens, 8192)");
   REQ(c.resident == 0 || c.resident == 1, "resident must be 0 or 1");
   REQ(c.adamw == 0 || c.adamw == 1, "adamw must be 0 or 1");
+  REQ(c.profile >= LS_PROFILE_OFF && c.profile <= LS_PROFILE_GEMM, "profile must be 0, 1 or 2");
   REQ(c.vocab >= 0 && c.vocab <= (1 << 24), "vocab must be in 0..2^24");
   REQ(c.store == LS_STORE_HOST || c.store == LS_STORE_FILE, "store must be LS_STORE_HOST or LS_STORE_FILE");
   REQ(c.store != LS_STORE_FILE || (c.store_path[0] != 0 && memchr(c.store_path, 0, sizeof(c.store_path)) != nullptr),

@@ -287,7 +287,9 @@ struct KTimer {
   double flop, bytes;
   size_t i0 = 0;
   bool on;
-  KTimer(ls_ctx* ctx, int k, double f, double b) : c(ctx), cls(k), flop(f), bytes(b), on(ctx->cfg.profile != 0) {
+  KTimer(ls_ctx* ctx, int k, double f, double b)
+      : c(ctx), cls(k), flop(f), bytes(b),
+        on(ctx->cfg.profile == LS_PROFILE_ALL || (ctx->cfg.profile == LS_PROFILE_GEMM && k == LS_KC_GEMM_FWD)) {
     if (on) {
       hipEvent_t e;
       if (c->prof.next(&e, &i0) == hipSuccess) hipEventRecord(e, c->cs); else on = false;
@@ -310,7 +312,7 @@ struct Span {   // copy or per-layer compute interval
   bool copy;
   size_t i0 = 0;
   bool on;
-  Span(ls_ctx* ctx, hipStream_t st, bool is_copy) : c(ctx), s(st), copy(is_copy), on(ctx->cfg.profile != 0) {
+  Span(ls_ctx* ctx, hipStream_t st, bool is_copy) : c(ctx), s(st), copy(is_copy), on(ctx->cfg.profile == LS_PROFILE_ALL) {
     if (on) {
       hipEvent_t e;
       if (c->prof.next(&e, &i0) == hipSuccess) {
@@ -339,7 +341,7 @@ void collect_profile(ls_ctx* c) {
     c->stats.k_ms[k] = c->stats.k_flop[k] = c->stats.k_bytes[k] = 0.0;
   }
   c->stats.last_copy_ms = c->stats.last_compute_ms = c->stats.last_overlap_ms = c->stats.last_span_ms = 0.0;
-  if (!c->cfg.profile || P.origin == (size_t)-1) return;
+  if (!c->cfg.profile) return;
   auto el = [&](size_t a, size_t b) {
     float ms = 0.f;
     hipEventElapsedTime(&ms, P.pool[a], P.pool[b]);
@@ -351,6 +353,7 @@ void collect_profile(ls_ctx* c) {
     c->stats.k_flop[r.cls] += r.flop;
     c->stats.k_bytes[r.cls] += r.bytes;
   }
+  if (P.origin == (size_t)-1) return;   // no copy / compute intervals were recorded
   std::vector<std::pair<double, double>> cp, cm;
   double last = 0.0;
   for (auto& iv : P.copies) { cp.push_back({el(P.origin, iv.first), el(P.origin, iv.second)}); last = std::max(last, cp.back().second); }
@@ -1302,7 +1305,7 @@ ls_status ls_adamw_step(ls_ctx* c, const ls_adamw* hp) {
   h.inv_bc2_sqrt = (float)(1.0 / std::sqrt(1.0 - std::pow(b2, (double)hp->step)));
   h.eps = hp->eps;
   if (c->prof_collected) { c->prof.reset(); c->prof_collected = false; }
-  if (c->cfg.profile && c->prof.origin == (size_t)-1) {
+  if (c->cfg.profile == LS_PROFILE_ALL && c->prof.origin == (size_t)-1) {
     hipEvent_t e;
     size_t i;
     if (c->prof.next(&e, &i) == hipSuccess && hipEventRecord(e, c->cs) == hipSuccess) c->prof.origin = i;
@@ -1531,6 +1534,17 @@ ls_status ls_head_loss(ls_ctx* c, const void* Y, const void* Y_ref, const int32_
     HIPCHK(c, launch_rmsnorm_bwd(dyn, (const uint16_t*)Y, nullptr, gf, rstd, nullptr, nullptr, nullptr, (uint16_t*)dY,
                                  T, h, c->cs));
   }
+  return LS_OK;
+}
+
+ls_status ls_set_profile(ls_ctx* c, int32_t profile) {
+  if (ls_status st = check_usable(c)) return st;
+  if (profile != LS_PROFILE_OFF && profile != LS_PROFILE_ALL && profile != LS_PROFILE_GEMM)
+    return fail(c, LS_ERR_INVALID, "unknown profiling level %d", profile);
+  if (c->in_flight) return fail(c, LS_ERR_STATE, "work is in flight: call ls_sync first");
+  c->cfg.profile = profile;
+  c->prof.reset();
+  c->prof_collected = false;
   return LS_OK;
 }
 

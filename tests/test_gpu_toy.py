@@ -211,3 +211,26 @@ def test_file_store_bad_path_is_refused():
     with pytest.raises(B.LsError) as e:
         B.Context(cfg)
     assert e.value.status == B.LS_ERR_INVALID
+
+
+def test_profiling_levels():
+    """LS_PROFILE_GEMM times only the forward dequant GEMMs; LS_PROFILE_ALL every class and
+    the copy intervals; the results do not depend on the level."""
+    from layer_streamed_qlora_amd import binding as B
+    w = TOY
+    x, dy = synth.activations(w)
+    run = H.GpuRun(w, [0, 1, 2], profile=B.LS_PROFILE_GEMM)   # 3 layers, 2 slots: every step copies
+    a = run.step(x, dy, w.batch, w.seq)
+    st = run.ctx.stats()
+    assert st.k_launches[0] > 0 and all(st.k_launches[j] == 0 for j in range(1, B.LS_KC_N))
+    assert st.last_copy_ms == 0.0
+    run.ctx.set_profile(B.LS_PROFILE_ALL)
+    b = run.step(x, dy, w.batch, w.seq)
+    st = run.ctx.stats()
+    assert all(st.k_launches[j] > 0 for j in range(0, 5)) and st.last_copy_ms > 0.0
+    for k in ("Y", "dX"):
+        assert np.array_equal(a[k].view(np.uint32), b[k].view(np.uint32)), k
+    with pytest.raises(B.LsError) as e:
+        run.ctx.set_profile(7)
+    assert e.value.status == B.LS_ERR_INVALID
+    run.close()
