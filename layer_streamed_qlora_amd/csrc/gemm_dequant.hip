@@ -1056,6 +1056,8 @@ __global__ void __launch_bounds__(NT_FAST, 1) k_gemm_fwd_fast(FwdArgs args, int 
   // iteration adds exact zeros.
   const int k_last = K - BK;
   auto step = [&](int it, typename WFwdFast<FMT>::Regs& R) {
+    // let the scheduler interleave the LDS and memory instructions with the MFMAs
+    __builtin_amdgcn_iglp_opt(0);
     const int cur = it & 1;
     uint16_t* na = sm.u.k.a[cur ^ 1];
     uint16_t* nw = sm.u.k.w[cur ^ 1];
