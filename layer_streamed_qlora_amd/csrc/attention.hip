@@ -309,63 +309,69 @@ __global__ void __launch_bounds__(128) k_attn_dkv(AttnArgs a) {
   f32x16_t dk[ND], dv[ND];
 #pragma unroll
   for (int d = 0; d < ND; ++d) { dk[d] = f32x16_t{}; dv[d] = f32x16_t{}; }
-  const int n_qb = (a.S + KB - 1) / KB;
-  for (int r = 0; r < nrep; ++r) {
+  // iterations: query tiles qb = kb .. n_qb - 1 of each q head of the group in order;
+  // the tiles (and row statistics) of iteration i + 1 load while iteration i computes
+  const int n_qt = (a.S + KB - 1) / KB - kb;
+  const int n_it = nrep * n_qt;
+  TileMover<HD, 128> tq, to;
+  float lv = 0.f, dv_ = 0.f;
+  auto fetch = [&](int i) {
+    const int r = i / n_qt;
+    const int q0 = (kb + i - r * n_qt) * KB;
     const int h = g * nrep + r;
     const int64_t bh = (int64_t)b * a.hq + h;
-    const rsrc_t rq = make_rsrc(base + h * HD, head_bytes);
-    const rsrc_t rdo = make_rsrc(a.dout + (int64_t)b * a.S * a.lddo + h * HD, (uint64_t)a.S * a.lddo * 2);
-    for (int qb = kb; qb < n_qb; ++qb) {
-      const int q0 = qb * KB;
-      TileMover<HD, 128> tq, to;
-      tq.load(rq, a.ldqkv, q0);
-      to.load(rdo, a.lddo, q0);
-      float lv = 0.f, dv_ = 0.f;
-      if (threadIdx.x < KB && q0 + (int)threadIdx.x < a.S) {
-        lv = a.lse[bh * a.S + q0 + threadIdx.x];
-        dv_ = a.dd[bh * a.S + q0 + threadIdx.x];
+    tq.load(make_rsrc(base + h * HD, head_bytes), a.ldqkv, q0);
+    to.load(make_rsrc(a.dout + (int64_t)b * a.S * a.lddo + h * HD, (uint64_t)a.S * a.lddo * 2), a.lddo, q0);
+    // row statistics of the tile's queries (threads past the tile or the sequence read 0)
+    const bool ok = threadIdx.x < KB && q0 + (int)threadIdx.x < a.S;
+    const uint32_t off = ok ? (uint32_t)(q0 + threadIdx.x) * 4u : 0xFFFFFFF0u;
+    lv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(a.lse + bh * a.S, (uint64_t)a.S * 4), off, 0, 0));
+    dv_ = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(a.dd + bh * a.S, (uint64_t)a.S * 4), off, 0, 0));
+  };
+  fetch(0);
+  for (int i = 0; i < n_it; ++i) {
+    const int q0 = (kb + i % n_qt) * KB;
+    __syncthreads();                  // the previous tiles are no longer read
+    tq.store_rows(sq);
+    tq.store_t(sqt);
+    to.store_rows(sdo);
+    to.store_t(sdot);
+    if (threadIdx.x < KB) { sL[threadIdx.x] = lv; sD[threadIdx.x] = dv_; }
+    __syncthreads();
+    fetch(i + 1 < n_it ? i + 1 : i);  // issued on every iteration (the last re-reads its tile)
+#pragma unroll
+    for (int qs = 0; qs < 2; ++qs) {
+      if (q0 + 32 * qs + 31 < kw0) continue;      // every query before this wave's keys
+      f32x16_t s = f32x16_t{}, dp = f32x16_t{};
+#pragma unroll
+      for (int st = 0; st < NS; ++st) {
+        s = mfma(*reinterpret_cast<const bf16x8_t*>(sq + (32 * qs + kl) * PR + 16 * st + 8 * hh), kf[st], s);
+        dp = mfma(*reinterpret_cast<const bf16x8_t*>(sdo + (32 * qs + kl) * PR + 16 * st + 8 * hh), vf[st], dp);
       }
-      __syncthreads();                  // the previous tiles are no longer read
-      tq.store_rows(sq);
-      tq.store_t(sqt);
-      to.store_rows(sdo);
-      to.store_t(sdot);
-      if (threadIdx.x < KB) { sL[threadIdx.x] = lv; sD[threadIdx.x] = dv_; }
-      __syncthreads();
+      // C[i = query][j = key]: register v holds query 32 qs + (v / 4) * 8 + 4 hh + v % 4
+      f32x16_t ds;
 #pragma unroll
-      for (int qs = 0; qs < 2; ++qs) {
-        if (q0 + 32 * qs + 31 < kw0) continue;      // every query before this wave's keys
-        f32x16_t s = f32x16_t{}, dp = f32x16_t{};
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int qi = 32 * qs + 8 * g4 + 4 * hh;
+        const float4 L4 = *reinterpret_cast<const float4*>(&sL[qi]);
+        const float4 D4 = *reinterpret_cast<const float4*>(&sD[qi]);
+        const float Ls[4] = {L4.x, L4.y, L4.z, L4.w}, Ds[4] = {D4.x, D4.y, D4.z, D4.w};
 #pragma unroll
-        for (int st = 0; st < NS; ++st) {
-          s = mfma(*reinterpret_cast<const bf16x8_t*>(sq + (32 * qs + kl) * PR + 16 * st + 8 * hh), kf[st], s);
-          dp = mfma(*reinterpret_cast<const bf16x8_t*>(sdo + (32 * qs + kl) * PR + 16 * st + 8 * hh), vf[st], dp);
+        for (int e = 0; e < 4; ++e) {
+          const int v = 4 * g4 + e, qg = q0 + qi + e;
+          const bool ok = key <= qg && qg < a.S && key < a.S;
+          const float p = ok ? bf16_value(__builtin_amdgcn_exp2f(s[v] * cl - Ls[e])) : 0.f;
+          s[v] = p;
+          ds[v] = a.scale * p * (dp[v] - Ds[e]);
         }
-        // C[i = query][j = key]: register v holds query 32 qs + (v / 4) * 8 + 4 hh + v % 4
-        f32x16_t ds;
+      }
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const int qi = 32 * qs + 8 * g4 + 4 * hh;
-          const float4 L4 = *reinterpret_cast<const float4*>(&sL[qi]);
-          const float4 D4 = *reinterpret_cast<const float4*>(&sD[qi]);
-          const float Ls[4] = {L4.x, L4.y, L4.z, L4.w}, Ds[4] = {D4.x, D4.y, D4.z, D4.w};
+      for (int st = 0; st < 2; ++st) {
+        const bf16x8_t pa = pack8(s, 8 * st), da = pack8(ds, 8 * st);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int v = 4 * g4 + e, qg = q0 + qi + e;
-            const bool ok = key <= qg && qg < a.S && key < a.S;
-            const float p = ok ? bf16_value(__builtin_amdgcn_exp2f(s[v] * cl - Ls[e])) : 0.f;
-            s[v] = p;
-            ds[v] = a.scale * p * (dp[v] - Ds[e]);
-          }
-        }
-#pragma unroll
-        for (int st = 0; st < 2; ++st) {
-          const bf16x8_t pa = pack8(s, 8 * st), da = pack8(ds, 8 * st);
-#pragma unroll
-          for (int d = 0; d < ND; ++d) {
-            dv[d] = mfma(pa, tfrag(sdot, 32 * d + kl, 32 * qs + 16 * st, hh), dv[d]);
-            dk[d] = mfma(da, tfrag(sqt, 32 * d + kl, 32 * qs + 16 * st, hh), dk[d]);
-          }
+        for (int d = 0; d < ND; ++d) {
+          dv[d] = mfma(pa, tfrag(sdot, 32 * d + kl, 32 * qs + 16 * st, hh), dv[d]);
+          dk[d] = mfma(da, tfrag(sqt, 32 * d + kl, 32 * qs + 16 * st, hh), dk[d]);
         }
       }
     }
