@@ -194,9 +194,11 @@ ls_status ls_set_lora(ls_ctx* ctx, int32_t layer, int32_t proj, const float* A, 
  *           same streamed slot, the adapters-off reference pass from X (the DPO
  *           reference model: "Soup CLI fine-tunes Llama-3.1-8B on a 4 GB laptop GPU
  *           ...", third paragraph).
- * The layer inputs are kept as bf16 checkpoints for ls_backward.  Asynchronous:
- * returns after enqueueing.  Errors: LS_ERR_INVALID (sizes beyond max_tokens /
- * max_seq, null pointers), LS_ERR_STATE (a layer not staged).
+ * The layer inputs are kept as bf16 checkpoints for ls_backward; X is copied to the
+ * first one before anything else reads it, so Y may alias X (Y_ref must not alias Y).
+ * Asynchronous: returns after enqueueing.  Errors: LS_ERR_INVALID (sizes beyond
+ * max_tokens / max_seq, seq not a multiple of 8, null pointers), LS_ERR_STATE (a layer
+ * not staged).
  */
 ls_status ls_forward(ls_ctx* ctx, const void* X, int32_t batch, int32_t seq, int32_t lora_on,
                      void* Y, void* Y_ref);
@@ -207,8 +209,10 @@ ls_status ls_forward(ls_ctx* ctx, const void* X, int32_t batch, int32_t seq, int
  *   dY: device bf16 [T, hidden] gradient of the last layer's output.
  *   dX: device bf16 [T, hidden] receives the gradient of the stack input.
  *   accumulate: 0 = write dA/dB, 1 = add into the registered dA/dB buffers.
- * Requires a preceding ls_forward with lora_on = 1 on this context (same T), else
- * LS_ERR_STATE.  Deterministic: no atomics, fixed reduction order.
+ * dX may alias dY: dY is read only by the last layer's backward and dX written only at
+ * the end of the first layer's.  Requires a preceding ls_forward with lora_on = 1 on
+ * this context (same T), else LS_ERR_STATE.  Deterministic: no atomics, fixed
+ * reduction order.
  */
 ls_status ls_backward(ls_ctx* ctx, const void* dY, void* dX, int32_t accumulate);
 

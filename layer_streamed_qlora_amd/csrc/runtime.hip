@@ -1142,7 +1142,8 @@ ls_status ls_forward(ls_ctx* c, const void* X, int32_t batch, int32_t seq, int32
       uint16_t* out = l + 1 < L ? ckpt(c, l + 1) : (uint16_t*)Y;
       if ((st = layer_forward(c, l, blob, d, ckpt(c, l), out, lora, MODE_FWD))) return st;
       if (Y_ref) {
-        const uint16_t* rin = l == 0 ? (const uint16_t*)X : xr[(l - 1) & 1];
+        // layer 0 reads the checkpoint copy of X, so Y may alias X
+        const uint16_t* rin = l == 0 ? ckpt(c, 0) : xr[(l - 1) & 1];
         uint16_t* rout = l + 1 < L ? xr[l & 1] : (uint16_t*)Y_ref;
         if ((st = layer_forward(c, l, blob, d, rin, rout, false, MODE_FWD))) return st;
       }

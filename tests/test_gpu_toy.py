@@ -127,6 +127,33 @@ def test_accumulate_adds():
             assert np.array_equal(b["dB"][l][p], a["dB"][l][p] * 2), (l, p)
 
 
+@pytest.mark.parametrize("n_layers", [1, 2])
+def test_outputs_may_alias_inputs(n_layers):
+    """Y written over X (with the reference pass on) and dX written over dY give the same
+    bits as separate buffers."""
+    torch = pytest.importorskip("torch")
+    w = TOY
+    x, dy = synth.activations(w)
+    say("case: toy aliasing, layers", n_layers)
+    run = H.GpuRun(w, list(range(n_layers)))
+    sep = run.step(x, dy, w.batch, w.seq, with_ref=True)
+    X = run.to_dev_bf16(x)
+    Yr = torch.empty_like(X)
+    run.ctx.forward(X.data_ptr(), w.batch, w.seq, 1, X.data_ptr(), Yr.data_ptr())   # Y over X
+    D = run.to_dev_bf16(dy)
+    run.ctx.backward(D.data_ptr(), D.data_ptr(), 0)                                   # dX over dY
+    run.ctx.sync()
+    torch.cuda.synchronize()
+    got = {"Y": run.from_dev_bf16(X), "Y_ref": run.from_dev_bf16(Yr), "dX": run.from_dev_bf16(D)}
+    dA = [{p: run.dA[l][p].cpu().numpy() for p in H.PROJS} for l in range(n_layers)]
+    run.close()
+    for k in ("Y", "Y_ref", "dX"):
+        assert np.array_equal(got[k].view(np.uint32), sep[k].view(np.uint32)), k
+    for l in range(n_layers):
+        for p in H.PROJS:
+            assert np.array_equal(dA[l][p].view(np.uint32), sep["dA"][l][p].view(np.uint32)), (l, p)
+
+
 @pytest.mark.parametrize("batch,seq", [(3, 40), (2, 8)])
 def test_ragged_shapes(batch, seq):
     """Token counts and sequence lengths that leave partial tiles everywhere."""
