@@ -71,26 +71,40 @@ def cpu_baseline(w, n_layers=1, batch=1, seq=512):
                       f"backward in {dt:.2f} s, scaled by depth ({w.n_layers}/{n_layers})"}
 
 
-def measured_traffic(kernel_class):
-    """HBM bytes per launch of the kernel class from the committed counter summary, or
-    None when the kernel source changed since the counters were taken."""
+def profile_record(name):
+    """The machine-readable line of a committed counter summary under profiles/, or None
+    when the kernel source changed since the counters were taken."""
     import hashlib
     here = os.path.dirname(os.path.abspath(__file__))
-    path = os.path.join(here, "profiles", "llama8b_gemm_traffic.md")
     try:
-        lines = open(path).read().splitlines()
+        lines = open(os.path.join(here, "profiles", name)).read().splitlines()
     except OSError:
         return None
     for line in lines:
         if line.startswith("machine-readable: "):
             rec = json.loads(line[len("machine-readable: "):])
-            if rec.get("class") != kernel_class:
-                return None
             src = os.path.join(here, rec["kernel_source"])
             if hashlib.sha256(open(src, "rb").read()).hexdigest() != rec["kernel_source_sha256"]:
                 return None
-            return float(rec["traffic_bytes_per_launch"])
+            return rec
     return None
+
+
+def measured_traffic(kernel_class):
+    """HBM bytes per launch of the kernel class (FETCH_SIZE + WRITE_SIZE counters)."""
+    rec = profile_record("llama8b_gemm_traffic.md")
+    if rec is None or rec.get("class") != kernel_class:
+        return None
+    return float(rec["traffic_bytes_per_launch"])
+
+
+def measured_mfma_busy():
+    """MFMA busy share of cycles per dequant-GEMM kernel (SQ_VALU_MFMA_BUSY_CYCLES)."""
+    rec = profile_record("llama8b_gemm_mfma_counters.md")
+    if rec is None:
+        return None
+    return {"mfma_busy": rec["mfma_busy"], "shader_clock_GHz": rec["shader_clock_GHz"],
+            "source": "profiles/llama8b_gemm_mfma_counters.md"}
 
 
 def main():
@@ -242,6 +256,7 @@ def main():
         out["mfma"] = {"dequant_gemm_tflops": round(gemm_fl / (gemm_ms * 1e-3) / 1e12, 1),
                        "frac_of_peak": round(gemm_fl / (gemm_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                        "kernels": kern,
+                       "counters": measured_mfma_busy(),
                        "breakdown_from": f"{n_b} fully profiled steps after the timed region (events around "
                                          "every launch); the timed region times the forward dequant GEMMs only"}
         copy_ms = acc["copy"] / n_b
