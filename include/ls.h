@@ -155,7 +155,10 @@ typedef struct ls_ctx ls_ctx;
  * before any allocation; if it does not fit the call returns LS_ERR_BUDGET and
  * allocates nothing (the pages' pre-flight refusal of runs that will not fit:
  * the lachieslifestyle.com how-to, "Step 7: Train and keep the log").  The library
- * owns the pinned store, the device slots, checkpoints and workspaces.
+ * owns the pinned store, the device slots, checkpoints and workspaces, and one more
+ * stream of its own (default priority) on which ls_backward runs the adapter-gradient
+ * reductions beside the compute stream; ls_backward's work on the compute stream
+ * ends with a wait for them.
  */
 ls_status ls_create(const ls_config* cfg, void* compute_stream, void* copy_stream, ls_ctx** out);
 

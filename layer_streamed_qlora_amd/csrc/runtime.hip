@@ -213,6 +213,12 @@ struct ls_ctx {
   int device = 0;
   hipStream_t cs = nullptr, ps = nullptr;
   bool own_cs = false, own_ps = false;
+  // side stream of the adapter-gradient reductions (dA, dB): they run beside the
+  // backward's dequant GEMMs, forked after each G product and joined before the next
+  // layer's recompute overwrites what they read
+  hipStream_t side = nullptr;
+  hipEvent_t fork_ev = nullptr, join_ev = nullptr;
+  bool side_pending = false;
   std::vector<uint8_t*> host;
   std::vector<char> staged;
   uint8_t* dbase = nullptr;
@@ -287,12 +293,14 @@ struct KTimer {
   double flop, bytes;
   size_t i0 = 0;
   bool on;
-  KTimer(ls_ctx* ctx, int k, double f, double b)
+  hipStream_t s;
+  KTimer(ls_ctx* ctx, int k, double f, double b, hipStream_t st = nullptr)
       : c(ctx), cls(k), flop(f), bytes(b),
-        on(ctx->cfg.profile == LS_PROFILE_ALL || (ctx->cfg.profile == LS_PROFILE_GEMM && k == LS_KC_GEMM_FWD)) {
+        on(ctx->cfg.profile == LS_PROFILE_ALL || (ctx->cfg.profile == LS_PROFILE_GEMM && k == LS_KC_GEMM_FWD)),
+        s(st ? st : ctx->cs) {
     if (on) {
       hipEvent_t e;
-      if (c->prof.next(&e, &i0) == hipSuccess) hipEventRecord(e, c->cs); else on = false;
+      if (c->prof.next(&e, &i0) == hipSuccess) hipEventRecord(e, s); else on = false;
     }
   }
   ~KTimer() {
@@ -300,7 +308,7 @@ struct KTimer {
     hipEvent_t e;
     size_t i1;
     if (c->prof.next(&e, &i1) == hipSuccess) {
-      hipEventRecord(e, c->cs);
+      hipEventRecord(e, s);
       c->prof.krecs.push_back({cls, i0, i1, flop, bytes});
     }
   }
@@ -795,14 +803,30 @@ ls_status lora_grads_AB(ls_ctx* c, int l, const Dims& d, int p0, int n, const ui
     bytes += 2.0 * d.T * n_in + 2.0 * d.T * n * d.r16 + 4.0 * n * n_in * d.r;
   }
   if (a.n_jobs == 0) return LS_OK;
-  KTimer kt(c, LS_KC_LORA, flop, bytes);
-  HIPCHK(c, launch_lora_tc(a, c->cs));
+  // everything read here was written on the compute stream before this point
+  HIPCHK(c, hipEventRecord(c->fork_ev, c->cs));
+  HIPCHK(c, hipStreamWaitEvent(c->side, c->fork_ev, 0));
+  c->side_pending = true;
+  KTimer kt(c, LS_KC_LORA, flop, bytes, c->side);
+  HIPCHK(c, launch_lora_tc(a, c->side));
+  return LS_OK;
+}
+
+// The compute stream waits for the adapter-gradient reductions enqueued so far.
+ls_status join_side(ls_ctx* c) {
+  if (!c->side_pending) return LS_OK;
+  HIPCHK(c, hipEventRecord(c->join_ev, c->side));
+  HIPCHK(c, hipStreamWaitEvent(c->cs, c->join_ev, 0));
+  c->side_pending = false;
   return LS_OK;
 }
 
 ls_status layer_backward(ls_ctx* c, int l, const uint8_t* blob, const Dims& d, const uint16_t* x_in, const uint16_t* dy,
                          uint16_t* dx, float beta) {
-  ls_status st = layer_forward(c, l, blob, d, x_in, nullptr, true, MODE_RECOMPUTE);
+  // the previous layer's reductions read activations this recompute overwrites
+  ls_status st = join_side(c);
+  if (st) return st;
+  st = layer_forward(c, l, blob, d, x_in, nullptr, true, MODE_RECOMPUTE);
   if (st) return st;
   const ls_config& g = c->cfg;
   const int fmt = wformat(g);
@@ -969,6 +993,16 @@ ls_status ls_create(const ls_config* cfg, void* compute_stream, void* copy_strea
   if (copy_stream) c->ps = (hipStream_t)copy_stream;
   else if (hipStreamCreateWithFlags(&c->ps, hipStreamNonBlocking) == hipSuccess) c->own_ps = true;
   else { c->err = "copy stream creation failed"; return bail(LS_ERR_HIP); }
+  if (hipStreamCreateWithFlags(&c->side, hipStreamNonBlocking) != hipSuccess) {
+    c->side = nullptr;
+    c->err = "side stream creation failed";
+    return bail(LS_ERR_HIP);
+  }
+  if (hipEventCreateWithFlags(&c->fork_ev, hipEventDisableTiming) != hipSuccess ||
+      hipEventCreateWithFlags(&c->join_ev, hipEventDisableTiming) != hipSuccess) {
+    c->err = "event creation failed";
+    return bail(LS_ERR_HIP);
+  }
   if (gemm_dequant_init() != hipSuccess) { c->err = "kernel attribute setup failed"; return bail(LS_ERR_HIP); }
 
   const int nb = P.n_slots;
@@ -1191,13 +1225,14 @@ ls_status ls_backward(ls_ctx* c, const void* dY, void* dX, int32_t accumulate) {
     if ((st = release_layer(c, l))) return st;
     cur = out;
   }
-  return LS_OK;
+  return join_side(c);   // the compute stream's completion covers dA and dB
 }
 
 ls_status ls_sync(ls_ctx* c) {
   if (!c) return LS_ERR_INVALID;
   if (c->sticky != LS_OK) return c->sticky;
   HIPCHK(c, hipStreamSynchronize(c->ps));
+  HIPCHK(c, hipStreamSynchronize(c->side));
   HIPCHK(c, hipStreamSynchronize(c->cs));
   HIPCHK(c, hipGetLastError());
   c->in_flight = false;
@@ -1223,7 +1258,10 @@ void ls_destroy(ls_ctx* c) {
   if (!c) return;
   if (c->cs) hipStreamSynchronize(c->cs);
   if (c->ps) hipStreamSynchronize(c->ps);
+  if (c->side) hipStreamSynchronize(c->side);
   for (auto e : c->prof.pool) hipEventDestroy(e);
+  if (c->fork_ev) hipEventDestroy(c->fork_ev);
+  if (c->join_ev) hipEventDestroy(c->join_ev);
   for (auto e : c->ready) if (e) hipEventDestroy(e);
   for (auto e : c->consumed) if (e) hipEventDestroy(e);
   if (c->dbase) hipFree(c->dbase);
@@ -1235,6 +1273,7 @@ void ls_destroy(ls_ctx* c) {
   }
   if (c->own_cs && c->cs) hipStreamDestroy(c->cs);
   if (c->own_ps && c->ps) hipStreamDestroy(c->ps);
+  if (c->side) hipStreamDestroy(c->side);
   delete c;
 }
 
