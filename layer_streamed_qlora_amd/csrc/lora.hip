@@ -16,8 +16,8 @@
 //
 // The other two products of the adapters, H = s x A^T and G = s dY B, contract over the
 // features of a token-major matrix ([T, K] against [N, K], N = r or a few stacked r):
-// `k_lora_fc` takes 16 tokens x 64 columns per workgroup over all of K, its eight waves
-// on eighths of K added in a fixed order, and writes bf16.
+// `k_lora_fc` takes 16 tokens x up to 64 columns per workgroup over all of K, its
+// sixteen waves on sixteenths of K added in a fixed order, and writes bf16.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -137,9 +137,8 @@ __global__ void __launch_bounds__(NT) k_lora_tc_reduce(TcKArgs k) {
 // lane j + 16 (k / 8); C[i][j] in lane j + 16 (i / 4), register i % 4.
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 constexpr int FT = 16;     // tokens per workgroup
-constexpr int FN = 64;     // columns per workgroup (4 blocks of 16)
-constexpr int FU = 4;      // 32-wide K steps in flight per wave
-constexpr int FW = 8;      // waves per workgroup, each on 1/FW of K
+constexpr int FN = 64;     // columns per workgroup at most (4 blocks of 16)
+constexpr int FW = 16;     // waves per workgroup, each on 1/FW of K
 
 struct FcKArgs {
   FcArgs a;
@@ -147,11 +146,15 @@ struct FcKArgs {
   int32_t n_tiles[kMaxFcJobs];
 };
 
-// Workgroup: 16 tokens x up to 64 columns over the whole of K.  Each of its FW waves
-// streams a contiguous 1/FW of K straight into MFMA operand registers (16 bytes per lane
-// per step); the partial products are added in LDS in wave order.
+// Workgroup: 16 tokens x NB blocks of 16 columns over the whole of K.  Each of its FW
+// waves streams a contiguous 1/FW of K straight into MFMA operand registers (16 bytes
+// per lane per step, FU steps in flight); the partial products are added in LDS in
+// wave order.  NB is the launch's widest job in 16-column blocks (a narrower job's
+// extra blocks read zeros).
+template <int NB>
 __global__ void __launch_bounds__(FW * 64) k_lora_fc(FcKArgs k) {
-  __shared__ __align__(16) f32x4_t red[FW][4][64];    // [wave][column block][lane]
+  constexpr int FU = NB == 1 ? 8 : 4;   // 32-wide K steps in flight per wave
+  __shared__ __align__(16) f32x4_t red[FW][NB][64];    // [wave][column block][lane]
   const FcArgs& a = k.a;
   const int flat = blockIdx.x;
   int j = 0;
@@ -159,8 +162,8 @@ __global__ void __launch_bounds__(FW * 64) k_lora_fc(FcKArgs k) {
   const FcJob& J = a.job[j];
   const int local = flat - k.tile0[j];
   const int mt = local / k.n_tiles[j], nt = local - mt * k.n_tiles[j];
-  const int t0 = mt * FT, n0 = nt * FN;
-  const int nb_used = min(4, (J.N - n0 + 15) / 16);
+  const int t0 = mt * FT, n0 = nt * (16 * NB);
+  const int nb_used = min(NB, (J.N - n0 + 15) / 16);
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int row = lane & 15, kg = (lane >> 4) * 8;
   const rsrc_t rx = make_rsrc(J.X + (int64_t)t0 * J.ldx, ((uint64_t)(a.T - t0) * J.ldx) * 2);
@@ -169,27 +172,30 @@ __global__ void __launch_bounds__(FW * 64) k_lora_fc(FcKArgs k) {
   const int steps = (J.K + 31) / 32;
   const int per = (steps + FW - 1) / FW;
   const int s_beg = w * per, s_end = min(steps, s_beg + per);
-  f32x4_t acc[4] = {f32x4_t{}, f32x4_t{}, f32x4_t{}, f32x4_t{}};
+  f32x4_t acc[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4_t{};
   for (int s = s_beg; s < s_end; s += FU) {
-    bf16x8_t av[FU], bv[FU][4];
+    bf16x8_t av[FU], bv[FU][NB];
 #pragma unroll
     for (int u = 0; u < FU; ++u) {
       const int kk = (s + u) * 32 + kg;
       const bool ok = s + u < s_end && kk < J.K;
       av[u] = as_bf8(bload16(rx, ok ? xoff + (uint32_t)kk * 2u : 0xFFFFFFF0u));
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb)
+      for (int nb = 0; nb < NB; ++nb)
         bv[u][nb] = as_bf8(bload16(rw, (ok && nb < nb_used) ? ((uint32_t)(16 * nb + row) * (uint32_t)J.K + (uint32_t)kk) * 2u
                                                             : 0xFFFFFFF0u));
     }
+    // keep every load of the group in flight before the first product waits on one
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int u = 0; u < FU; ++u)
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb)
-        if (nb < nb_used) acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[u], bv[u][nb], acc[nb], 0, 0, 0);
+      for (int nb = 0; nb < NB; ++nb) acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[u], bv[u][nb], acc[nb], 0, 0, 0);
   }
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb) red[w][nb][lane] = acc[nb];
+  for (int nb = 0; nb < NB; ++nb) red[w][nb][lane] = acc[nb];
   __syncthreads();
   if (w >= nb_used) return;
   const int nb = w;
@@ -245,6 +251,9 @@ namespace lsq {
 hipError_t launch_lora_fc(const FcArgs& a, hipStream_t s) {
   if (a.T <= 0 || a.n_jobs <= 0) return hipSuccess;
   if (a.n_jobs > kMaxFcJobs) return hipErrorInvalidValue;
+  int max_n = 0;
+  for (int j = 0; j < a.n_jobs; ++j) max_n = std::max(max_n, a.job[j].N);
+  const int nb = std::max(1, std::min(4, (max_n + 15) / 16));   // column blocks per workgroup
   FcKArgs k;
   k.a = a;
   const int m_tiles = (a.T + FT - 1) / FT;
@@ -256,11 +265,16 @@ hipError_t launch_lora_fc(const FcArgs& a, hipStream_t s) {
         (uint64_t)FN * J.K * 2 >= (1ull << 31) || (uint64_t)FT * J.ldx * 2 + (uint64_t)J.K * 2 >= (1ull << 31))
       return hipErrorInvalidValue;
     k.tile0[j] = tiles;
-    k.n_tiles[j] = (J.N + FN - 1) / FN;
+    k.n_tiles[j] = (J.N + 16 * nb - 1) / (16 * nb);
     tiles += m_tiles * k.n_tiles[j];
   }
   k.tile0[a.n_jobs] = tiles;
-  hipLaunchKernelGGL(k_lora_fc, dim3((unsigned)tiles), dim3(FW * 64), 0, s, k);
+  switch (nb) {
+    case 1: hipLaunchKernelGGL(k_lora_fc<1>, dim3((unsigned)tiles), dim3(FW * 64), 0, s, k); break;
+    case 2: hipLaunchKernelGGL(k_lora_fc<2>, dim3((unsigned)tiles), dim3(FW * 64), 0, s, k); break;
+    case 3: hipLaunchKernelGGL(k_lora_fc<3>, dim3((unsigned)tiles), dim3(FW * 64), 0, s, k); break;
+    default: hipLaunchKernelGGL(k_lora_fc<4>, dim3((unsigned)tiles), dim3(FW * 64), 0, s, k); break;
+  }
   return hipGetLastError();
 }
 
