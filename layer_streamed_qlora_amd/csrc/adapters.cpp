@@ -343,7 +343,7 @@ std::string adapter_check(const ls_config& c, const std::string& path, std::vect
   for (int i = 0; i < 8; ++i) hn |= (uint64_t)buf[i] << (8 * i);
   if (hn > buf.size() - 8 || hn > (100ull << 20)) return "header length " + std::to_string(hn) + " exceeds the file";
   const uint64_t data0 = 8 + hn, dsize = buf.size() - data0;
-  JParser P{reinterpret_cast<const char*>(buf.data()) + 8, reinterpret_cast<const char*>(buf.data()) + data0};
+  JParser P{reinterpret_cast<const char*>(buf.data()) + 8, reinterpret_cast<const char*>(buf.data()) + data0, {}};
   JVal root;
   if (!P.val(root)) return "header is not valid JSON: " + P.err;
   P.ws();

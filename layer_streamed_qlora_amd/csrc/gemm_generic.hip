@@ -22,7 +22,7 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
-constexpr int GM = 128, GN = 64, GK = 32, GP = GK + 8;   // pitch in bf16
+constexpr int GM = 128, GK = 32, GP = GK + 8;   // pitch in bf16
 constexpr int GT = 256;
 
 __device__ __forceinline__ uint16_t to_bf16(float x) {

@@ -36,16 +36,6 @@ namespace {
 constexpr int kPad = 256;    // slack after every workspace region (8-element group loads)
 constexpr int kMaxSplit = 16;
 
-// K-split for a narrow product so that about two workgroups per CU are in flight.
-int auto_split(int M, int N, int K, int nz) {
-  const int tn = N <= 32 ? 32 : 64;
-  const long base = (long)((M + 127) / 128) * ((N + tn - 1) / tn) * nz;
-  int ks = (int)std::max(1L, 512 / std::max(1L, base));
-  ks = std::min(ks, kMaxSplit);
-  ks = std::min(ks, std::max(1, K / 256));
-  return ks;
-}
-
 struct LoraReg {
   const float* A = nullptr;
   const float* B = nullptr;
@@ -300,17 +290,16 @@ struct KTimer {
         s(st ? st : ctx->cs) {
     if (on) {
       hipEvent_t e;
-      if (c->prof.next(&e, &i0) == hipSuccess) hipEventRecord(e, s); else on = false;
+      // a failed record drops this launch from the statistics (never the run)
+      if (c->prof.next(&e, &i0) != hipSuccess || hipEventRecord(e, s) != hipSuccess) on = false;
     }
   }
   ~KTimer() {
     if (!on) return;
     hipEvent_t e;
     size_t i1;
-    if (c->prof.next(&e, &i1) == hipSuccess) {
-      hipEventRecord(e, s);
+    if (c->prof.next(&e, &i1) == hipSuccess && hipEventRecord(e, s) == hipSuccess)
       c->prof.krecs.push_back({cls, i0, i1, flop, bytes});
-    }
   }
 };
 
@@ -323,9 +312,8 @@ struct Span {   // copy or per-layer compute interval
   Span(ls_ctx* ctx, hipStream_t st, bool is_copy) : c(ctx), s(st), copy(is_copy), on(ctx->cfg.profile == LS_PROFILE_ALL) {
     if (on) {
       hipEvent_t e;
-      if (c->prof.next(&e, &i0) == hipSuccess) {
+      if (c->prof.next(&e, &i0) == hipSuccess && hipEventRecord(e, s) == hipSuccess) {
         if (c->prof.origin == (size_t)-1) c->prof.origin = i0;
-        hipEventRecord(e, s);
       } else {
         on = false;
       }
@@ -335,10 +323,8 @@ struct Span {   // copy or per-layer compute interval
     if (!on) return;
     hipEvent_t e;
     size_t i1;
-    if (c->prof.next(&e, &i1) == hipSuccess) {
-      hipEventRecord(e, s);
+    if (c->prof.next(&e, &i1) == hipSuccess && hipEventRecord(e, s) == hipSuccess)
       (copy ? c->prof.copies : c->prof.computes).push_back({i0, i1});
-    }
   }
 };
 
@@ -352,7 +338,7 @@ void collect_profile(ls_ctx* c) {
   if (!c->cfg.profile) return;
   auto el = [&](size_t a, size_t b) {
     float ms = 0.f;
-    hipEventElapsedTime(&ms, P.pool[a], P.pool[b]);
+    if (hipEventElapsedTime(&ms, P.pool[a], P.pool[b]) != hipSuccess) return 0.0;
     return (double)ms;
   };
   for (const auto& r : P.krecs) {
@@ -1256,24 +1242,25 @@ const char* ls_last_error(const ls_ctx* c) { return c ? c->err.c_str() : g_creat
 
 void ls_destroy(ls_ctx* c) {
   if (!c) return;
-  if (c->cs) hipStreamSynchronize(c->cs);
-  if (c->ps) hipStreamSynchronize(c->ps);
-  if (c->side) hipStreamSynchronize(c->side);
-  for (auto e : c->prof.pool) hipEventDestroy(e);
-  if (c->fork_ev) hipEventDestroy(c->fork_ev);
-  if (c->join_ev) hipEventDestroy(c->join_ev);
-  for (auto e : c->ready) if (e) hipEventDestroy(e);
-  for (auto e : c->consumed) if (e) hipEventDestroy(e);
-  if (c->dbase) hipFree(c->dbase);
-  for (auto p : c->host) if (p) hipHostFree(p);
-  for (auto p : c->staging) if (p) hipHostFree(p);
+  // best effort: nothing can be reported from here, every release is attempted
+  if (c->cs) (void)hipStreamSynchronize(c->cs);
+  if (c->ps) (void)hipStreamSynchronize(c->ps);
+  if (c->side) (void)hipStreamSynchronize(c->side);
+  for (auto e : c->prof.pool) (void)hipEventDestroy(e);
+  if (c->fork_ev) (void)hipEventDestroy(c->fork_ev);
+  if (c->join_ev) (void)hipEventDestroy(c->join_ev);
+  for (auto e : c->ready) if (e) (void)hipEventDestroy(e);
+  for (auto e : c->consumed) if (e) (void)hipEventDestroy(e);
+  if (c->dbase) (void)hipFree(c->dbase);
+  for (auto p : c->host) if (p) (void)hipHostFree(p);
+  for (auto p : c->staging) if (p) (void)hipHostFree(p);
   if (c->fd >= 0) {
     close(c->fd);
     unlink(c->cfg.store_path);
   }
-  if (c->own_cs && c->cs) hipStreamDestroy(c->cs);
-  if (c->own_ps && c->ps) hipStreamDestroy(c->ps);
-  if (c->side) hipStreamDestroy(c->side);
+  if (c->own_cs && c->cs) (void)hipStreamDestroy(c->cs);
+  if (c->own_ps && c->ps) (void)hipStreamDestroy(c->ps);
+  if (c->side) (void)hipStreamDestroy(c->side);
   delete c;
 }
 
