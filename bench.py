@@ -150,6 +150,8 @@ def main():
         host = {k: v.view(torch.int16).cpu().numpy().view(np.uint16) for k, v in dw.items()}
         ctx.stage_layer(l, host)
         del dw, host
+        if (l + 1) % 8 == 0 and l + 1 < w.n_layers:
+            log(f"staged {l + 1} of {w.n_layers} layers ({time.time() - t0:.0f} s)")
     loras = [synth.device_lora(w, l) for l in range(w.n_layers)]
     grads = []
     for l in range(w.n_layers):
@@ -167,13 +169,15 @@ def main():
     dY = torch.randn((T, w.hidden), generator=g, device="cuda:0").to(torch.bfloat16)
     Y = torch.empty_like(X)
     dX = torch.empty_like(X)
+    # a DPO workload runs each layer's adapters-off reference pass on the same slot
+    Yr = torch.empty_like(X) if w.dpo else None
     torch.cuda.synchronize()
     log(f"setup {time.time() - t0:.1f} s: {w.n_layers} layers staged, blob {ctx.stats().blob_bytes / 1e6:.2f} MB")
     probe = h2d_probe(torch)
     log(f"host-link probe {probe:.2f} GB/s")
 
     def step():
-        ctx.forward(X.data_ptr(), w.batch, w.seq, 1, Y.data_ptr())
+        ctx.forward(X.data_ptr(), w.batch, w.seq, 1, Y.data_ptr(), Yr.data_ptr() if Yr is not None else 0)
         ctx.backward(dY.data_ptr(), dX.data_ptr(), 0)
         ctx.sync()
 
@@ -219,8 +223,15 @@ def main():
 
     copies = (s1.h2d_copies - s0.h2d_copies) / args.steps
     h2d_bytes = (s1.h2d_bytes - s0.h2d_bytes) / args.steps
+    shape = {"llama8b": "Llama-3.1-8B", "qwen3b": "Qwen2.5-3B", "qwen32b": "Qwen2.5-32B",
+             "qwen72b": "Qwen2.5-72B", "toy": "toy"}.get(args.workload, args.workload)
+    base = ("NF4 block 64 + double-quant absmax" if w.double_quant else "NF4 block 64, fp32 absmax") \
+        if w.quant == "nf4" else "bf16"
+    metric = ("train tokens/s (fwd+bwd, streamed NF4 base) @Llama-3.1-8B shape" if args.workload == "llama8b" else
+              f"train tokens/s (fwd+bwd{' + reference pass' if w.dpo else ''}, streamed {w.quant.upper()} base) "
+              f"@{shape} shape")
     out = {
-        "metric": "train tokens/s (fwd+bwd, streamed NF4 base) @Llama-3.1-8B shape",
+        "metric": metric,
         "value": round(value, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -232,11 +243,12 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": f"{args.workload}: Llama-3.1-8B-shaped decoder stack, {w.n_layers} layers, "
+        "config": {"workload": f"{args.workload}: {shape}-shaped decoder stack, {w.n_layers} layers, "
                                f"hidden {w.hidden}, {w.n_heads}/{w.n_kv_heads} heads x {w.head_dim}, "
-                               f"SwiGLU {w.intermediate}, NF4 block 64 + double-quant absmax, "
+                               f"SwiGLU {w.intermediate}, {base} base, "
                                f"LoRA r {w.lora_r} alpha {int(w.lora_alpha)} on 7 projections, "
-                               f"streamed through {args.buffers} device slots",
+                               f"streamed through {args.buffers} device slots"
+                               + (", adapters-off reference pass per layer (DPO)" if w.dpo else ""),
                    "batch": w.batch, "seq": w.seq, "tokens_per_step": T, "parallelism": "none (1 GPU)",
                    "store": "file (page cache dropped after each read)" if args.store_file else "pinned host RAM"},
     }
