@@ -200,7 +200,7 @@ __global__ void k_attn_dd(AttnArgs a) {
 // tiles up to the diagonal: S^T = K Q^T and dP^T = V dO^T (keys x queries), dS, then
 // dQ^T += K^T dS^T.
 template <int HD>
-__global__ void __launch_bounds__(256) k_attn_dq(AttnArgs a) {
+__global__ void __launch_bounds__(256, 2) k_attn_dq(AttnArgs a) {   // two workgroups per CU (52 KB LDS each)
   constexpr int NS = HD / 16, ND = HD / 32, PR = HD + 8;
   __shared__ __align__(16) uint16_t sk[KB * PR];
   __shared__ __align__(16) uint16_t sv[KB * PR];
