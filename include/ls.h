@@ -133,9 +133,11 @@ typedef struct ls_stats {
   double last_overlap_ms;      /* profile=1: copy time that overlapped compute */
   double last_span_ms;         /* profile=1: first event to last event of last fwd+bwd */
   /* profile=1, per kernel class, over the last forward (+ backward): launches, summed
-   * launch durations from HIP events on the compute stream, and the algorithmic
-   * FLOPs and bytes of those launches (2*M*N*K per contraction; operands read once,
-   * results written once). */
+   * launch durations from HIP events on the stream each launch ran on, and the
+   * algorithmic FLOPs and bytes of those launches (2*M*N*K per contraction; operands
+   * read once, results written once).  The backward's dA / dB products (LS_KC_LORA) run
+   * on the library's side stream beside the compute stream, so their durations include
+   * time shared with other kernels. */
   uint64_t k_launches[LS_KC_N];
   double k_ms[LS_KC_N];
   double k_flop[LS_KC_N];
