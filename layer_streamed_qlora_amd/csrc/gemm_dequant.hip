@@ -775,6 +775,20 @@ __device__ __forceinline__ void epilogue_swiglu(Smem& sm, f32x16_t (&acc)[4][Lay
   }
 }
 
+// (m tile, n tile) of linear tile t of an m_tiles x n_tiles grid.  Each XCD's run of
+// the linear order covers about m_tiles / 8 rows of m tiles; inside a group of that
+// many m rows the m tile varies fastest, so the tiles of one weight tile (one n) run at
+// about the same time on one XCD and share its L2, as do the tiles of one activation
+// row block across the group.
+__device__ __forceinline__ void tile_mn(int t, int m_tiles, int n_tiles, int& mt, int& nt) {
+  const int gm = m_tiles >= 16 ? m_tiles >> 3 : 1;
+  const int g = t / (gm * n_tiles);
+  const int m_in = m_tiles - g * gm < gm ? m_tiles - g * gm : gm;
+  const int r = t - g * gm * n_tiles;
+  mt = g * gm + r % m_in;
+  nt = r / m_in;
+}
+
 __device__ __forceinline__ int xcd_tile(int bid, int nblocks_padded) {
   // Workgroups go round-robin over the 8 XCDs; give each XCD a contiguous run of
   // tiles (n fastest below) so the tiles sharing activation rows share one L2.
@@ -971,8 +985,8 @@ __global__ void __launch_bounds__(NT_FAST, 1) k_gemm_fwd_fast(FwdArgs args, int 
   Smem& sm = *reinterpret_cast<Smem*>(smem_raw);
   const int tile = xcd_tile(blockIdx.x, padded);
   if (tile >= total_tiles) return;
-  const int mt = tile / n_tiles;
-  int rest = tile - mt * n_tiles;
+  int mt, rest;
+  tile_mn(tile, total_tiles / n_tiles, n_tiles, mt, rest);
   int g = 0;
   if constexpr (!PAIRED) {
     for (; g < args.n_groups - 1; ++g) {
@@ -1099,8 +1113,8 @@ __global__ void __launch_bounds__(NT_FAST, 1) k_gemm_bwd_fast(BwdArgs args, int 
   Smem& sm = *reinterpret_cast<Smem*>(smem_raw);
   const int tile = xcd_tile(blockIdx.x, padded);
   if (tile >= total_tiles) return;
-  const int mt = tile / n_tiles;
-  const int nt = tile - mt * n_tiles;
+  int mt, nt;
+  tile_mn(tile, total_tiles / n_tiles, n_tiles, mt, nt);
   const int m0 = mt * BM, j0 = nt * BN;
 
   fill_lut2(sm, args.levels);
