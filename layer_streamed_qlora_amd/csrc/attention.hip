@@ -283,9 +283,12 @@ __global__ void __launch_bounds__(256, 2) k_attn_dq(AttnArgs a) {   // two workg
 // group's q heads in order and, per head, over the 64-query tiles from the diagonal
 // on: S = Q K^T and dP = dO V^T (queries x keys: each lane holds one key), P, dS, then
 // dV += P^T dO and dK += dS^T Q.  The sums over heads and tiles stay in registers, in
-// a fixed order.
+// a fixed order.  With n_half = 2 the group's q heads are split in two halves, one
+// workgroup each: the first half's sums go to dqkv, the second's to dkv2.  The key
+// block varies slowest over the grid, so the longest workgroups (the first key blocks,
+// which see every query tile) start first and the short ones fill in behind them.
 template <int HD>
-__global__ void __launch_bounds__(128) k_attn_dkv(AttnArgs a) {
+__global__ void __launch_bounds__(128) k_attn_dkv(AttnArgs a, int n_half) {
   constexpr int NS = HD / 16, ND = HD / 32, PR = HD + 8;
   __shared__ __align__(16) uint16_t sq[KB * PR];
   __shared__ __align__(16) uint16_t sdo[KB * PR];
@@ -293,9 +296,12 @@ __global__ void __launch_bounds__(128) k_attn_dkv(AttnArgs a) {
   __shared__ __align__(16) uint16_t sdot[HD * PT];
   __shared__ __align__(16) float sL[KB];
   __shared__ __align__(16) float sD[KB];
-  const int kb = blockIdx.x;
-  const int bg = blockIdx.y, b = bg / a.hkv, g = bg % a.hkv;
+  const int n_bg = a.batch * a.hkv;
+  const int bg = (int)blockIdx.x % n_bg, rest = (int)blockIdx.x / n_bg;
+  const int hf = rest % n_half, kb = rest / n_half;
+  const int b = bg / a.hkv, g = bg % a.hkv;
   const int nrep = a.hq / a.hkv;
+  const int r0 = hf * (nrep / n_half), n_rep = nrep / n_half;   // this workgroup's q heads
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, kl = lane & 31, hh = lane >> 5;
   const int kw0 = kb * KB + 32 * w, key = kw0 + kl;
   const uint64_t head_bytes = (uint64_t)a.S * a.ldqkv * 2;
@@ -312,13 +318,13 @@ __global__ void __launch_bounds__(128) k_attn_dkv(AttnArgs a) {
   // iterations: query tiles qb = kb .. n_qb - 1 of each q head of the group in order;
   // the tiles (and row statistics) of iteration i + 1 load while iteration i computes
   const int n_qt = (a.S + KB - 1) / KB - kb;
-  const int n_it = nrep * n_qt;
+  const int n_it = n_rep * n_qt;
   TileMover<HD, 128> tq, to;
   float lv = 0.f, dv_ = 0.f;
   auto fetch = [&](int i) {
     const int r = i / n_qt;
     const int q0 = (kb + i - r * n_qt) * KB;
-    const int h = g * nrep + r;
+    const int h = g * nrep + r0 + r;
     const int64_t bh = (int64_t)b * a.hq + h;
     tq.load(make_rsrc(base + h * HD, head_bytes), a.ldqkv, q0);
     to.load(make_rsrc(a.dout + (int64_t)b * a.S * a.lddo + h * HD, (uint64_t)a.S * a.lddo * 2), a.lddo, q0);
@@ -377,15 +383,17 @@ __global__ void __launch_bounds__(128) k_attn_dkv(AttnArgs a) {
     }
   }
   // C[i = key][j = d]: lane (d + 32 hh), register v holds key (v / 4) * 8 + 4 hh + v % 4
+  float* dst = hf == 0 ? a.dqkv + a.qd : a.dkv2;
+  const int64_t ld = hf == 0 ? a.lddqkv : 2 * (int64_t)a.kvd;
 #pragma unroll
   for (int v = 0; v < 16; ++v) {
     const int kr = kw0 + (v >> 2) * 8 + 4 * hh + (v & 3);
     if (kr >= a.S) continue;
-    float* row = a.dqkv + ((int64_t)b * a.S + kr) * a.lddqkv;
+    float* row = dst + ((int64_t)b * a.S + kr) * ld;
 #pragma unroll
     for (int d = 0; d < ND; ++d) {
-      row[a.qd + g * HD + 32 * d + kl] = dk[d][v];
-      row[a.qd + a.kvd + g * HD + 32 * d + kl] = dv[d][v];
+      row[g * HD + 32 * d + kl] = dk[d][v];
+      row[a.kvd + g * HD + 32 * d + kl] = dv[d][v];
     }
   }
 }
@@ -401,7 +409,8 @@ hipError_t bwd_hd(const AttnArgs& a, hipStream_t s) {
   const int64_t rows = (int64_t)a.batch * a.S * a.hq;
   const int per_block = 256 / (HD / 8);
   hipLaunchKernelGGL(k_attn_dd<HD>, dim3((unsigned)((rows + per_block - 1) / per_block)), dim3(256), 0, s, a);
-  hipLaunchKernelGGL(k_attn_dkv<HD>, dim3((a.S + KB - 1) / KB, a.batch * a.hkv), dim3(128), 0, s, a);
+  const int n_half = a.dkv2 ? 2 : 1;
+  hipLaunchKernelGGL(k_attn_dkv<HD>, dim3((a.S + KB - 1) / KB * n_half * a.batch * a.hkv), dim3(128), 0, s, a, n_half);
   hipLaunchKernelGGL(k_attn_dq<HD>, dim3((a.S + 127) / 128, a.batch * a.hq), dim3(256), 0, s, a);
   return hipGetLastError();
 }
@@ -422,7 +431,7 @@ hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t s) {
 hipError_t launch_attn_bwd(const AttnArgs& a, hipStream_t s) {
   if (a.batch <= 0 || a.S <= 0) return hipSuccess;
   if (!shape_ok(a) || !a.qkv || !a.out32 || !a.dout || !a.lse || !a.dd || !a.dqkv || a.lddo % 8 != 0 ||
-      a.lddqkv % 4 != 0)
+      a.lddqkv % 4 != 0 || (a.dkv2 && (a.hq / a.hkv) % 2 != 0))
     return hipErrorInvalidValue;
   return a.hd == 64 ? bwd_hd<64>(a, s) : bwd_hd<128>(a, s);
 }

@@ -196,7 +196,7 @@ __global__ void __launch_bounds__(256) k_rmsnorm_bwd_v(const float* dn, const XT
 // float32 -> bf16 with the inverse rotation on the first nh heads; one thread per
 // (token, column pair or lone column)
 __global__ void k_rope_bwd_convert(const float* src, uint16_t* dst, int ld, int64_t T, int seq, int nh, int hd,
-                                   const float2* tab) {
+                                   const float2* tab, const float* add, int add_col0, int add_ld) {
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int half = hd / 2;
   const int rope_pairs = nh * half;                    // rotated column pairs per row
@@ -207,22 +207,27 @@ __global__ void k_rope_bwd_convert(const float* src, uint16_t* dst, int ld, int6
   const int c = (int)(idx % per_row);
   const float* s = src + t * ld;
   uint16_t* d = dst + t * ld;
+  auto rd = [&](int col) {     // the row's value, plus the addend's when col >= add_col0
+    float v = s[col];
+    if (add && col >= add_col0) v += add[t * add_ld + (col - add_col0)];
+    return v;
+  };
   if (c < rope_pairs) {
     const int h = c / half, i = c % half;
     const int col = h * hd + i;
     const float2 cs = tab[(int64_t)(t % seq) * half + i];
-    const float d1 = s[col], d2 = s[col + half];
+    const float d1 = rd(col), d2 = rd(col + half);
     d[col] = tobf(d1 * cs.x + d2 * cs.y);
     d[col + half] = tobf(d2 * cs.x - d1 * cs.y);
   } else {
     const int col = nh * hd + (c - rope_pairs);
-    d[col] = tobf(s[col]);
+    d[col] = tobf(rd(col));
   }
 }
 
 // Same, 4 rotated column pairs or 8 plain columns per thread (hd % 8 == 0, ld % 8 == 0)
 __global__ void k_rope_bwd_convert_v(const float* src, uint16_t* dst, int ld, int64_t T, int seq, int nh, int hd,
-                                     const float2* tab) {
+                                     const float2* tab, const float* add, int add_col0, int add_ld) {
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int half = hd / 2, gp = half / 4;
   const int rope_groups = nh * gp;
@@ -232,11 +237,20 @@ __global__ void k_rope_bwd_convert_v(const float* src, uint16_t* dst, int ld, in
   const int c = (int)(idx % per_row);
   const float* sr = src + t * ld;
   uint16_t* dr = dst + t * ld;
+  // 4 consecutive float32 of the row at col, plus the addend's when col >= add_col0
+  auto rd4 = [&](int col) {
+    float4 v = *reinterpret_cast<const float4*>(sr + col);
+    if (add && col >= add_col0) {
+      const float4 w = *reinterpret_cast<const float4*>(add + t * add_ld + (col - add_col0));
+      v.x += w.x; v.y += w.y; v.z += w.z; v.w += w.w;
+    }
+    return v;
+  };
   if (c < rope_groups) {
     const int h = c / gp, i = (c % gp) * 4;
     const int col = h * hd + i;
-    const float4 d1 = *reinterpret_cast<const float4*>(sr + col);
-    const float4 d2 = *reinterpret_cast<const float4*>(sr + col + half);
+    const float4 d1 = rd4(col);
+    const float4 d2 = rd4(col + half);
     const float4* tp = reinterpret_cast<const float4*>(tab + (int64_t)(t % seq) * half + i);
     const float4 c01 = tp[0], c23 = tp[1];                 // (cos, sin) of pairs i .. i+3
     const float a1[4] = {d1.x, d1.y, d1.z, d1.w}, a2[4] = {d2.x, d2.y, d2.z, d2.w};
@@ -253,7 +267,7 @@ __global__ void k_rope_bwd_convert_v(const float* src, uint16_t* dst, int ld, in
     *reinterpret_cast<uint2*>(dr + col + half) = make_uint2(o2[0], o2[1]);
   } else {
     const int col = nh * hd + (c - rope_groups) * 8;
-    const float4 a = *reinterpret_cast<const float4*>(sr + col), b = *reinterpret_cast<const float4*>(sr + col + 4);
+    const float4 a = rd4(col), b = rd4(col + 4);
     f32x2_t p0 = {a.x, a.y}, p1 = {a.z, a.w}, p2 = {b.x, b.y}, p3 = {b.z, b.w};
     *reinterpret_cast<uint4*>(dr + col) = make_uint4(__builtin_bit_cast(uint32_t, __builtin_convertvector(p0, bf16x2_t)),
                                                      __builtin_bit_cast(uint32_t, __builtin_convertvector(p1, bf16x2_t)),
@@ -355,19 +369,22 @@ hipError_t launch_rmsnorm_bwd(const float* dn, const uint16_t* x16, const float*
 }
 
 hipError_t launch_rope_bwd_convert(const float* src, uint16_t* dst, int32_t ld, int32_t T, int32_t seq, int32_t nh,
-                                   int32_t hd, const float2* tab, hipStream_t s) {
-  if (hd % 8 == 0 && ld % 8 == 0 && (ld - nh * hd) % 8 == 0) {
+                                   int32_t hd, const float2* tab, hipStream_t s, const float* add, int32_t add_col0,
+                                   int32_t add_ld) {
+  if (add && (add_col0 < 0 || add_col0 > ld || add_ld < ld - add_col0)) return hipErrorInvalidValue;
+  if (hd % 8 == 0 && ld % 8 == 0 && (ld - nh * hd) % 8 == 0 &&
+      (!add || (add_col0 % 4 == 0 && add_ld % 4 == 0 && (reinterpret_cast<uintptr_t>(add) & 15) == 0))) {
     const int64_t n = (int64_t)T * ((int64_t)nh * (hd / 8) + (ld - nh * hd) / 8);
     if (n <= 0) return hipSuccess;
     hipLaunchKernelGGL(k_rope_bwd_convert_v, dim3(blocks_for(n, 256)), dim3(256), 0, s, src, dst, ld, (int64_t)T, seq,
-                       nh, hd, tab);
+                       nh, hd, tab, add, add_col0, add_ld);
     return hipGetLastError();
   }
   const int64_t per_row = (int64_t)nh * (hd / 2) + (ld - nh * hd);
   const int64_t n = (int64_t)T * per_row;
   if (n <= 0) return hipSuccess;
   hipLaunchKernelGGL(k_rope_bwd_convert, dim3(blocks_for(n, 256)), dim3(256), 0, s, src, dst, ld, (int64_t)T, seq, nh,
-                     hd, tab);
+                     hd, tab, add, add_col0, add_ld);
   return hipGetLastError();
 }
 

@@ -188,6 +188,11 @@ struct AttnArgs {
   const uint16_t* dout = nullptr; int32_t lddo = 0;   // backward: dO, bf16 like O
   float* dd = nullptr;                                // backward scratch [batch * hq * S]: rowsum(dO * O)
   float* dqkv = nullptr; int32_t lddqkv = 0;          // backward: float32 dq | dk | dv, layout of qkv
+  // backward, optional: float32 [batch * S, 2 kvd] (dk | dv).  When set and each kv head
+  // has an even number of q heads, dk, dv of the second half of each group's q heads go
+  // here, those of the first half to dqkv; the caller adds the two (see
+  // launch_rope_bwd_convert).  When unset, dqkv receives the whole sums.
+  float* dkv2 = nullptr;
   // forward: per query row (m, l) = the row maximum of the base-2 scaled scores and the sum
   // of exp2(t - m), [batch * hq * S]; written if stats_out is set; if stats_in holds the
   // values of an earlier forward over the same q, k, the first pass is skipped
@@ -218,9 +223,12 @@ hipError_t launch_rmsnorm_fwd(const uint16_t* x16, const float* x32, const uint1
 hipError_t launch_rmsnorm_bwd(const float* dn, const uint16_t* x16, const float* x32, const uint16_t* g,
                               const float* rstd, const float* dres32, const uint16_t* dres16, float* dx32,
                               uint16_t* dx16, int32_t T, int32_t D, hipStream_t s);
-// float32 [T, ld] -> bf16 [T, ld], inverse rotary embedding on the first nh heads
+// float32 [T, ld] -> bf16 [T, ld], inverse rotary embedding on the first nh heads.  With
+// add set, columns [add_col0, ld) first get add[t * add_ld + column - add_col0] added
+// (float32, same rounding order on every call).
 hipError_t launch_rope_bwd_convert(const float* src, uint16_t* dst, int32_t ld, int32_t T, int32_t seq, int32_t nh,
-                                   int32_t hd, const float2* tab, hipStream_t s);
+                                   int32_t hd, const float2* tab, hipStream_t s,
+                                   const float* add = nullptr, int32_t add_col0 = 0, int32_t add_ld = 0);
 // rotary embedding in place on the first nh heads of a token-major [T, ld] bf16
 // buffer; tab[pos * hd/2 + i] = (cos, sin) of pos * theta^(-2i/hd)
 hipError_t launch_rope_tab(uint16_t* qk, int32_t ld, int32_t T, int32_t seq, int32_t nh, int32_t hd,

@@ -51,6 +51,7 @@ struct DevPlan {
   uint64_t n1 = 0, qkv = 0, att = 0, hb = 0, n2 = 0, gu = 0, act = 0, rstd1 = 0, rstd2 = 0;
   uint64_t hs = 0, gs = 0, lse = 0, dd = 0, o32 = 0, astats = 0;
   uint64_t dya = 0, dyb = 0, dh32 = 0, dh16 = 0, dgu = 0, datt = 0, dqkv = 0, dqkv32 = 0, dn32 = 0;
+  uint64_t dkv2 = 0;   // dk | dv of the second half of each kv head's q heads, float32
   uint64_t lora = 0, lora_per_layer = 0, partial = 0, partial_bytes = 0;
   uint64_t levels = 0, rope = 0;
   // AdamW: moments m then v (moment_elems floats each) and the chunk table
@@ -115,6 +116,7 @@ DevPlan make_plan(const ls_config& c, const BlobLayout& L) {
   P.datt = take(2 * T * qd);
   P.dqkv = take(2 * T * qkvd);
   P.dqkv32 = take(4 * T * qkvd);
+  P.dkv2 = take(4 * T * 2 * kvd);
   P.dn32 = take(4 * T * (std::max(h, qd)));
   // LoRA operands in bf16, per layer
   uint64_t lo = 0;
@@ -601,6 +603,9 @@ ls_status attn_bwd(ls_ctx* c, const Dims& d, const uint16_t* qkv, const uint16_t
   a.dout = dout; a.lddo = d.qd;
   a.dd = c->dp<float>(c->plan.dd);
   a.dqkv = dqkv32; a.lddqkv = d.qkvd;
+  // with an even number of q heads per kv head, dK / dV run in two halves of the heads
+  // (twice the workgroups, so the short key blocks fill in behind the long ones)
+  a.dkv2 = (d.hq / d.hkv) % 2 == 0 ? c->dp<float>(c->plan.dkv2) : nullptr;
   const double fl = 2.5 * 4.0 * d.batch * d.hq * (double)d.seq * (d.seq + 1) / 2 * d.hd;
   KTimer kt(c, LS_KC_ATTN, fl, 2.0 * d.T * (d.qkvd + d.qd) + 4.0 * d.T * (d.qkvd + d.qd) + 8.0 * d.T * d.hq);
   HIPCHK(c, launch_attn_bwd(a, c->cs));
@@ -885,7 +890,10 @@ ls_status layer_backward(ls_ctx* c, int l, const uint8_t* blob, const Dims& d, c
   if ((st = attn_bwd(c, d, qkv, att, datt, dqkv32))) return st;
   {
     KTimer kt(c, LS_KC_GLUE, 0.0, 3 * tb * d.qkvd);
-    HIPCHK(c, launch_rope_bwd_convert(dqkv32, dqkv, d.qkvd, d.T, d.seq, d.hq + d.hkv, d.hd, c->dp<float2>(c->plan.rope), c->cs));
+    // dK | dV of the second half of the q heads join here (see attn_bwd)
+    const float* dkv2 = (d.hq / d.hkv) % 2 == 0 ? c->dp<float>(c->plan.dkv2) : nullptr;
+    HIPCHK(c, launch_rope_bwd_convert(dqkv32, dqkv, d.qkvd, d.T, d.seq, d.hq + d.hkv, d.hd, c->dp<float2>(c->plan.rope),
+                                      c->cs, dkv2, d.qd, 2 * d.kvd));
   }
   // ---- q, k, v
   const int cols[3] = {0, d.qd, d.qd + d.kvd};
