@@ -47,28 +47,99 @@ def h2d_probe(torch, nbytes=256 << 20, reps=6):
     return nbytes / (best * 1e-3) / 1e9
 
 
-def cpu_baseline(w, n_layers=1, batch=1, seq=512):
-    """The oracle, untuned, on a bounded sample: n_layers of the stack at batch x seq,
-    timed for one forward + recompute backward, scaled to the stack's depth."""
-    import numpy as np
+def host_cpu():
+    """Model name, logical CPUs and physical cores of this host (/proc/cpuinfo)."""
+    model, cores, phys = None, set(), None
+    try:
+        for line in open("/proc/cpuinfo"):
+            k, _, v = line.partition(":")
+            k, v = k.strip(), v.strip()
+            if k == "model name" and model is None:
+                model = v
+            elif k == "physical id":
+                phys = v
+            elif k == "core id":
+                cores.add((phys, v))
+    except OSError:
+        pass
+    return {"model": model, "logical_cpus": os.cpu_count(), "physical_cores": len(cores) or None}
+
+
+def blas_threads():
+    from threadpoolctl import threadpool_info
+    n = [i["num_threads"] for i in threadpool_info() if i.get("user_api") == "blas"]
+    return max(n) if n else 1
+
+
+def oracle_layers(w, n_layers):
+    """(seconds spent in the oracle's packer, dequantised layers) for layers 0 .. n_layers-1."""
+    from layer_streamed_qlora_amd import synth
+    from oracle import stack
+    src = [synth.layer_weights(w, l) for l in range(n_layers)]
+    t0 = time.perf_counter()
+    enc = [stack.quantize_layer(s, w.quant, w.double_quant) for s in src]
+    t_pack = time.perf_counter() - t0
+    nbytes = sum(v.size * 2 for s in src for v in s.values())
+    return t_pack, nbytes, [stack.dequant_layer(e) for e in enc]
+
+
+def oracle_step_time(w, layers, batch, seq, threads=None):
+    """Seconds of one oracle forward + recompute backward over `layers` at batch x seq,
+    with the BLAS thread pool limited to `threads` if given."""
+    from threadpoolctl import threadpool_limits
     from layer_streamed_qlora_amd import synth
     from oracle import model, stack
-
-    sub = w.with_(n_layers=n_layers, batch=batch, seq=seq)
-    layers = [stack.dequant_layer(stack.quantize_layer(synth.layer_weights(w, l), w.quant, w.double_quant))
-              for l in range(n_layers)]
-    loras = [synth.layer_lora(w, l) for l in range(n_layers)]
+    nl = len(layers)
+    sub = w.with_(n_layers=nl, batch=batch, seq=seq)
+    loras = [synth.layer_lora(w, l) for l in range(nl)]
     x, dy = synth.activations(sub)
     shp = model.LayerShape(w.hidden, w.n_heads, w.n_kv_heads, w.head_dim, w.intermediate, w.rms_eps,
                            w.rope_theta, w.lora_r, w.lora_alpha)
-    t0 = time.perf_counter()
-    stack.train_step(x, dy, layers, loras, shp, batch, seq, parity=True)
-    dt = time.perf_counter() - t0
-    per_token_stack = dt * (w.n_layers / n_layers) / (batch * seq)
-    cores = int(os.environ.get("OMP_NUM_THREADS") or os.environ.get("OPENBLAS_NUM_THREADS") or os.cpu_count())
-    return {"value": 1.0 / per_token_stack, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"{n_layers} of {w.n_layers} layers at batch {batch} x seq {seq}, one forward + recompute "
-                      f"backward in {dt:.2f} s, scaled by depth ({w.n_layers}/{n_layers})"}
+    with threadpool_limits(threads):
+        t0 = time.perf_counter()
+        stack.train_step(x, dy, layers, loras, shp, batch, seq, parity=True, with_reference=w.dpo)
+        return time.perf_counter() - t0
+
+
+def cpu_baseline(w, full=False):
+    """The oracle, untuned, on bounded samples, scaled to the stack's depth.
+
+    The reported value: 1 of the stack's layers at batch 1 x seq 512, one forward +
+    recompute backward with every BLAS thread.  Beside it: the same layer at 1 x 128 on
+    one thread, the whole two-layer toy stack, the oracle's packer rate, and (full=True)
+    one Qwen2.5-32B-shaped layer at 1 x 256."""
+    from layer_streamed_qlora_amd import synth
+    threads = blas_threads()
+    t_pack, nbytes, layers = oracle_layers(w, 1)
+    dt = oracle_step_time(w, layers, 1, 512)
+    out = {"value": 512 / (dt * w.n_layers), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+           "sample": f"1 of {w.n_layers} layers at batch 1 x seq 512, one forward + recompute backward in "
+                     f"{dt:.2f} s, scaled by depth ({w.n_layers}/1)"}
+    dt1 = oracle_step_time(w, layers, 1, 128, threads=1)
+    toy = synth.WORKLOADS["toy"]
+    _, _, toy_layers = oracle_layers(toy, toy.n_layers)
+    dtt = oracle_step_time(toy, toy_layers, toy.batch, toy.seq)
+    dtt1 = oracle_step_time(toy, toy_layers, toy.batch, toy.seq, threads=1)
+    more = {
+        "host": host_cpu(),
+        "one_thread": {"value": 128 / (dt1 * w.n_layers), "unit": "tokens/s",
+                       "sample": f"1 of {w.n_layers} layers at batch 1 x seq 128 on 1 thread in {dt1:.2f} s, "
+                                 "scaled by depth"},
+        "toy_step": {"seconds": round(dtt, 4), "seconds_one_thread": round(dtt1, 4),
+                     "sample": f"the whole {toy.n_layers}-layer toy stack at batch {toy.batch} x seq {toy.seq}"},
+        "packer": {"MB_per_s": round(nbytes / t_pack / 1e6, 1),
+                   "sample": f"NF4{' + double-quant' if w.double_quant else ''} encoding of one layer, "
+                             f"{nbytes / 1e6:.0f} MB of bf16 weights in {t_pack:.2f} s"},
+    }
+    if full:
+        q = synth.WORKLOADS["qwen32b"]
+        _, _, ql = oracle_layers(q, 1)
+        dq = oracle_step_time(q, ql, 1, 256)
+        more["qwen32b"] = {"value": 256 / (dq * q.n_layers), "unit": "tokens/s",
+                           "sample": f"1 of {q.n_layers} Qwen2.5-32B-shaped layers at batch 1 x seq 256 in "
+                                     f"{dq:.2f} s, scaled by depth"}
+    out["more"] = more
+    return out
 
 
 def profile_record(name):
@@ -116,6 +187,8 @@ def main():
     ap.add_argument("--layers", type=int, default=0, help="override depth (0 = the workload's)")
     ap.add_argument("--buffers", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-baseline-full", action="store_true",
+                    help="also time one Qwen2.5-32B-shaped layer on the oracle (about a minute more)")
     ap.add_argument("--no-profile", action="store_true")
     ap.add_argument("--vocab", type=int, default=128256, help="output-head rows for the head+loss measurement (0 = none)")
     ap.add_argument("--store-file", default="", help="keep the frozen base in this file instead of pinned RAM")
@@ -145,10 +218,14 @@ def main():
                         store_path=args.store_file or None)
     t0 = time.time()
     ctx = B.Context(cfg)
+    t_stage, staged_bytes = 0.0, 0
     for l in range(w.n_layers):
         dw = synth.device_layer_weights(w, l)
         host = {k: v.view(torch.int16).cpu().numpy().view(np.uint16) for k, v in dw.items()}
+        ts = time.perf_counter()
         ctx.stage_layer(l, host)
+        t_stage += time.perf_counter() - ts
+        staged_bytes += sum(v.nbytes for v in host.values())
         del dw, host
         if (l + 1) % 8 == 0 and l + 1 < w.n_layers:
             log(f"staged {l + 1} of {w.n_layers} layers ({time.time() - t0:.0f} s)")
@@ -251,6 +328,9 @@ def main():
                                + (", adapters-off reference pass per layer (DPO)" if w.dpo else ""),
                    "batch": w.batch, "seq": w.seq, "tokens_per_step": T, "parallelism": "none (1 GPU)",
                    "store": "file (page cache dropped after each read)" if args.store_file else "pinned host RAM"},
+        # the library's host packer (ls_stage_layer: NF4 encoding into the pinned store)
+        "staging": {"bf16_MB_per_s": round(staged_bytes / t_stage / 1e6, 1) if t_stage else None,
+                    "layers": w.n_layers, "seconds": round(t_stage, 2)},
     }
     if profile:
         kern = {k: {"launches_per_step": v[0] / n_b, "ms_per_step": v[1] / n_b,
@@ -337,7 +417,7 @@ def main():
                             "copies_per_step": (ctx.stats().h2d_copies - c0) / n_h, "sft_loss": round(loss, 4)}
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
-        out["cpu_baseline"] = cpu_baseline(w)
+        out["cpu_baseline"] = cpu_baseline(w, full=args.cpu_baseline_full)
     ctx.close()
     print(json.dumps(out), flush=True)
 
