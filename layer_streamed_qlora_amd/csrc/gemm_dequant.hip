@@ -644,6 +644,9 @@ __device__ __forceinline__ void epilogue(Smem& sm, f32x16_t (&acc)[4][Layout<NT>
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / WNW, wn = wave % WNW;
   constexpr int OP = BN + 4;
+  constexpr int RS = NT / 64;            // rows apart of one thread's consecutive rows
+  constexpr int RPT = 128 / RS;          // rows per thread per half tile
+  constexpr int CH = RPT < 4 ? RPT : 4;  // rows per batch of global reads
   for (int half = 0; half < 2; ++half) {
     __syncthreads();
     if (wm == half) {
@@ -659,69 +662,110 @@ __device__ __forceinline__ void epilogue(Smem& sm, f32x16_t (&acc)[4][Layout<NT>
           }
     }
     __syncthreads();
+    // Thread t handles column quad q = t % 64 of rows t / 64 + RS k.  Each batch of CH
+    // rows issues all its global reads (residual, rotary table, or g and u) before it
+    // uses any of them, so a batch waits on memory once, not once per row; rows past
+    // M_lim read the last row and are not written.
     const int mbase = m0 + half * 128;
-#pragma unroll 4
-    for (int it = 0; it < 8192 / NT; ++it) {
-      const int idx = threadIdx.x + NT * it;           // 128 rows x 64 quads
-      const int r = idx >> 6, q = idx & 63;
-      const int m = mbase + r, n = n0 + 4 * q;
-      if (m >= M_lim || n >= N_lim) continue;
-      const float4 v = *reinterpret_cast<const float4*>(&sm.u.out[r * OP + 4 * q]);
-      float y[4] = {v.x, v.y, v.z, v.w};
-      if (E.gu) {   // N_lim % 4 == 0 here
-        const float4 g4 = *reinterpret_cast<const float4*>(E.gu + (int64_t)m * E.ldgu + n);
-        const float4 u4 = *reinterpret_cast<const float4*>(E.gu + (int64_t)m * E.ldgu + N_lim + n);
-        const float gs[4] = {g4.x, g4.y, g4.z, g4.w}, us[4] = {u4.x, u4.y, u4.z, u4.w};
-        float dg[4], du[4];
+    const int q = threadIdx.x & 63, rt = threadIdx.x >> 6;
+    const int n = n0 + 4 * q;
+    if (n >= N_lim) continue;           // the next half starts at a barrier every thread reaches
+    const bool full = n + 4 <= N_lim;
+    const int gc = E.col_base + n;
+    const bool rope = gc < E.rope_cols;
+    const int hh = E.hd / 2, i0 = rope ? gc % E.hd : 0;
+    const bool lo = i0 < hh;
+    // what the batch reads: g and u, the rotary table, a float32 or a bf16 residual
+    const int mode = E.gu ? 1 : rope ? 2 : (full && E.r32) ? 3 : (full && E.r16) ? 4 : 0;
+#pragma unroll 1
+    for (int c = 0; c < RPT; c += CH) {
+      float4 pre[CH][2];
+      int mrow[CH];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float sg = sigmoid_f(gs[e]);
-          dg[e] = y[e] * us[e] * sg * (1.0f + gs[e] * (1.0f - sg));
-          du[e] = y[e] * gs[e] * sg;
-        }
-        uint16_t* po = reinterpret_cast<uint16_t*>(E.out) + (int64_t)m * E.ldo + n;
-        *reinterpret_cast<uint2*>(po) = make_uint2(pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3]));
-        *reinterpret_cast<uint2*>(po + N_lim) = make_uint2(pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3]));
-        continue;
-      }
-      const int gc = E.col_base + n;
-      if (gc < E.rope_cols) {
-        const int hh = E.hd / 2, i0 = gc % E.hd;
-        const int lo = i0 < hh;
-        const float4 pv = *reinterpret_cast<const float4*>(&sm.u.out[r * OP + 4 * q + (lo ? hh : -hh)]);
-        const float pr[4] = {pv.x, pv.y, pv.z, pv.w};
-        const float2* tab = E.rope_tab + (int64_t)(m % E.seq) * hh + (i0 % hh);
+      for (int k = 0; k < CH; ++k) mrow[k] = min(mbase + rt + RS * (c + k), M_lim - 1);
+      // one branch per batch, then CH rows of reads back to back
+      if (mode == 1) {   // N_lim % 4 == 0 here
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float2 cs = tab[e];
-          y[e] = lo ? y[e] * cs.x - pr[e] * cs.y : y[e] * cs.x + pr[e] * cs.y;
+        for (int k = 0; k < CH; ++k) {
+          pre[k][0] = *reinterpret_cast<const float4*>(E.gu + (int64_t)mrow[k] * E.ldgu + n);
+          pre[k][1] = *reinterpret_cast<const float4*>(E.gu + (int64_t)mrow[k] * E.ldgu + N_lim + n);
+        }
+      } else if (mode == 2) {
+#pragma unroll
+        for (int k = 0; k < CH; ++k) {
+          const float2* tab = E.rope_tab + (int64_t)(mrow[k] % E.seq) * hh + (i0 % hh);
+          pre[k][0] = make_float4(tab[0].x, tab[0].y, tab[1].x, tab[1].y);
+          pre[k][1] = make_float4(tab[2].x, tab[2].y, tab[3].x, tab[3].y);
+        }
+      } else if (mode == 3) {
+#pragma unroll
+        for (int k = 0; k < CH; ++k) pre[k][0] = *reinterpret_cast<const float4*>(E.r32 + (int64_t)mrow[k] * E.ldr + n);
+      } else if (mode == 4) {
+#pragma unroll
+        for (int k = 0; k < CH; ++k) {
+          const uint2 rr = *reinterpret_cast<const uint2*>(E.r16 + (int64_t)mrow[k] * E.ldr + n);
+          pre[k][0] = make_float4(bf16_lo(rr.x), bf16_hi(rr.x), bf16_lo(rr.y), bf16_hi(rr.y));
         }
       }
-      const int64_t o = (int64_t)m * E.ldo + n;
-      const bool full = n + 4 <= N_lim;
-      if (E.r16 || E.r32) {
-        const int64_t ro = (int64_t)m * E.ldr + n;
-        if (E.r32) {
-          if (full) { const float4 rr = *reinterpret_cast<const float4*>(E.r32 + ro); y[0] += rr.x; y[1] += rr.y; y[2] += rr.z; y[3] += rr.w; }
-          else for (int e = 0; e < 4 && n + e < N_lim; ++e) y[e] += E.r32[ro + e];
-        } else if (full) {
-          const uint2 rr = *reinterpret_cast<const uint2*>(E.r16 + ro);
-          y[0] += bf16_lo(rr.x); y[1] += bf16_hi(rr.x); y[2] += bf16_lo(rr.y); y[3] += bf16_hi(rr.y);
+#pragma unroll
+      for (int k = 0; k < CH; ++k) {
+        const int r = rt + RS * (c + k);
+        const int m = mbase + r;
+        if (m >= M_lim) break;
+        const float4 v = *reinterpret_cast<const float4*>(&sm.u.out[r * OP + 4 * q]);
+        float y[4] = {v.x, v.y, v.z, v.w};
+        if (mode == 1) {
+          const float gs[4] = {pre[k][0].x, pre[k][0].y, pre[k][0].z, pre[k][0].w};
+          const float us[4] = {pre[k][1].x, pre[k][1].y, pre[k][1].z, pre[k][1].w};
+          float dg[4], du[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float sg = sigmoid_f(gs[e]);
+            dg[e] = y[e] * us[e] * sg * (1.0f + gs[e] * (1.0f - sg));
+            du[e] = y[e] * gs[e] * sg;
+          }
+          uint16_t* po = reinterpret_cast<uint16_t*>(E.out) + (int64_t)m * E.ldo + n;
+          *reinterpret_cast<uint2*>(po) = make_uint2(pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3]));
+          *reinterpret_cast<uint2*>(po + N_lim) = make_uint2(pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3]));
+          continue;
+        }
+        if (rope) {
+          const float4 pv = *reinterpret_cast<const float4*>(&sm.u.out[r * OP + 4 * q + (lo ? hh : -hh)]);
+          const float pr[4] = {pv.x, pv.y, pv.z, pv.w};
+          const float cx[4] = {pre[k][0].x, pre[k][0].z, pre[k][1].x, pre[k][1].z};
+          const float cy[4] = {pre[k][0].y, pre[k][0].w, pre[k][1].y, pre[k][1].w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) y[e] = lo ? y[e] * cx[e] - pr[e] * cy[e] : y[e] * cx[e] + pr[e] * cy[e];
+        }
+        const int64_t o = (int64_t)m * E.ldo + n;
+        if (E.r16 || E.r32) {
+          const int64_t ro = (int64_t)m * E.ldr + n;
+          if (mode >= 3) {   // read in the batch above
+            y[0] += pre[k][0].x; y[1] += pre[k][0].y; y[2] += pre[k][0].z; y[3] += pre[k][0].w;
+          } else if (full && E.r32) {
+            const float4 rr = *reinterpret_cast<const float4*>(E.r32 + ro);
+            y[0] += rr.x; y[1] += rr.y; y[2] += rr.z; y[3] += rr.w;
+          } else if (full) {
+            const uint2 rr = *reinterpret_cast<const uint2*>(E.r16 + ro);
+            y[0] += bf16_lo(rr.x); y[1] += bf16_hi(rr.x); y[2] += bf16_lo(rr.y); y[3] += bf16_hi(rr.y);
+          } else if (E.r32) {
+            for (int e = 0; e < 4 && n + e < N_lim; ++e) y[e] += E.r32[ro + e];
+          } else {
+            for (int e = 0; e < 4 && n + e < N_lim; ++e) y[e] += bf16_lo(E.r16[ro + e]);
+          }
+        }
+        if (E.f32) {
+          float* po = reinterpret_cast<float*>(E.out) + o;
+          if (full) *reinterpret_cast<float4*>(po) = make_float4(y[0], y[1], y[2], y[3]);
+          else for (int e = 0; e < 4 && n + e < N_lim; ++e) po[e] = y[e];
         } else {
-          for (int e = 0; e < 4 && n + e < N_lim; ++e) y[e] += bf16_lo(E.r16[ro + e]);
-        }
-      }
-      if (E.f32) {
-        float* po = reinterpret_cast<float*>(E.out) + o;
-        if (full) *reinterpret_cast<float4*>(po) = make_float4(y[0], y[1], y[2], y[3]);
-        else for (int e = 0; e < 4 && n + e < N_lim; ++e) po[e] = y[e];
-      } else {
-        uint16_t* po = reinterpret_cast<uint16_t*>(E.out) + o;
-        const uint32_t p0 = pack_bf16x2(y[0], y[1]), p1 = pack_bf16x2(y[2], y[3]);
-        if (full) *reinterpret_cast<uint2*>(po) = make_uint2(p0, p1);
-        else {
-          const uint16_t h[4] = {(uint16_t)p0, (uint16_t)(p0 >> 16), (uint16_t)p1, (uint16_t)(p1 >> 16)};
-          for (int e = 0; e < 4 && n + e < N_lim; ++e) po[e] = h[e];
+          uint16_t* po = reinterpret_cast<uint16_t*>(E.out) + o;
+          const uint32_t p0 = pack_bf16x2(y[0], y[1]), p1 = pack_bf16x2(y[2], y[3]);
+          if (full) *reinterpret_cast<uint2*>(po) = make_uint2(p0, p1);
+          else {
+            const uint16_t h[4] = {(uint16_t)p0, (uint16_t)(p0 >> 16), (uint16_t)p1, (uint16_t)(p1 >> 16)};
+            for (int e = 0; e < 4 && n + e < N_lim; ++e) po[e] = h[e];
+          }
         }
       }
     }
