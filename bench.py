@@ -328,6 +328,10 @@ def main():
                                + (", adapters-off reference pass per layer (DPO)" if w.dpo else ""),
                    "batch": w.batch, "seq": w.seq, "tokens_per_step": T, "parallelism": "none (1 GPU)",
                    "store": "file (page cache dropped after each read)" if args.store_file else "pinned host RAM"},
+        # the library's one device allocation (its plan), the caller's tensors (inputs,
+        # outputs, adapters and their gradients, allocated through torch), the pinned store
+        "memory": {"library_device_bytes": s1.device_bytes, "caller_device_bytes_peak": torch.cuda.max_memory_allocated(),
+                   "pinned_store_bytes": s1.store_bytes, "blob_bytes": s1.blob_bytes},
         # the library's host packer (ls_stage_layer: NF4 encoding into the pinned store)
         "staging": {"bf16_MB_per_s": round(staged_bytes / t_stage / 1e6, 1) if t_stage else None,
                     "layers": w.n_layers, "seconds": round(t_stage, 2)},
