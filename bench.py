@@ -194,7 +194,7 @@ def main():
     ap.add_argument("--store-file", default="", help="keep the frozen base in this file instead of pinned RAM")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for {args.gpus}); this build has no multi-GPU path.",
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}); the library has no multi-GPU path.",
               file=sys.stderr)
         sys.exit(2)
 
