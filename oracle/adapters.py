@@ -7,7 +7,7 @@ how-to, "Step 2", the warning against version 0.72.0; "Soup CLI fine-tunes
 Llama-3.1-8B on a 4 GB laptop GPU ...", the paragraph on runs that completed and were
 wrong anyway).  So a load must either apply every trained tensor or refuse.
 
-Readings taken (also listed in the design doc):
+Readings taken:
 
 * container: the safetensors layout (8-byte little-endian header length, a JSON
   header with dtype, shape and [begin, end) byte offsets per tensor and a string map

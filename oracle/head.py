@@ -12,7 +12,7 @@ What the pages fix:
 * preference training with DPO over the streamed base, whose reference model is the
   same base with the adapters switched off (the tesserapress piece, third paragraph).
 
-Readings taken where the pages are silent (also listed in the design doc):
+Readings taken where the pages are silent:
 
 * head = a final RMSNorm with frozen weight g_f, then logits = yn W^T with a frozen
   16-bit W [V, h] and no bias (QLoRA keeps the output layer in 16 bits);

@@ -9,7 +9,7 @@ how-to, section "Step 5: Enable 4-bit layer streaming", sets ``quantization: 4bi
 Block size 64 and the 8-bit / block-256 second level come from the workload
 definitions this repository is measured on.
 
-Readings taken where the pages are silent (each is also listed in the design doc):
+Readings taken where the pages are silent:
 
 * codebook: the NormalFloat construction of the QLoRA paper (section 3): 8 positive
   levels at standard-normal quantiles of equally spaced probabilities from delta down

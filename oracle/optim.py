@@ -6,7 +6,7 @@ QLoRA: Train a Fraction of the Parameters"), and Adam keeps two extra tensors pe
 trained parameter (same page, the list of what makes training memory-hungry, item
 "Optimizer states").  The pages print no update rule or hyperparameters.
 
-Reading taken (also listed in the design doc): Adam with decoupled weight decay (AdamW,
+Reading taken: Adam with decoupled weight decay (AdamW,
 Loshchilov & Hutter, "Decoupled Weight Decay Regularization", Algorithm 2), with the
 decay scaled by the learning rate as in the widely used PyTorch parametrisation:
 
