@@ -192,6 +192,8 @@ def main():
     ap.add_argument("--no-profile", action="store_true")
     ap.add_argument("--vocab", type=int, default=128256, help="output-head rows for the head+loss measurement (0 = none)")
     ap.add_argument("--store-file", default="", help="keep the frozen base in this file instead of pinned RAM")
+    ap.add_argument("--resident", action="store_true",
+                    help="keep every layer on the device (no streaming): the reference point of the streamed run")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); the library has no multi-GPU path.",
@@ -214,6 +216,7 @@ def main():
     # kernel); every event is a packet in the compute stream and widens the gap before the
     # next kernel, so the full per-class breakdown comes from extra steps afterwards
     cfg = B.make_config(w, n_buffers=args.buffers, profile=B.LS_PROFILE_GEMM if profile else 0, adamw=1,
+                        resident=1 if args.resident else 0,
                         vocab=args.vocab,
                         store_path=args.store_file or None)
     t0 = time.time()
@@ -304,8 +307,10 @@ def main():
              "qwen72b": "Qwen2.5-72B", "toy": "toy"}.get(args.workload, args.workload)
     base = ("NF4 block 64 + double-quant absmax" if w.double_quant else "NF4 block 64, fp32 absmax") \
         if w.quant == "nf4" else "bf16"
-    metric = ("train tokens/s (fwd+bwd, streamed NF4 base) @Llama-3.1-8B shape" if args.workload == "llama8b" else
-              f"train tokens/s (fwd+bwd{' + reference pass' if w.dpo else ''}, streamed {w.quant.upper()} base) "
+    metric = ("train tokens/s (fwd+bwd, streamed NF4 base) @Llama-3.1-8B shape"
+              if args.workload == "llama8b" and not args.resident else
+              f"train tokens/s (fwd+bwd{' + reference pass' if w.dpo else ''}, "
+              f"{'resident' if args.resident else 'streamed'} {w.quant.upper()} base) "
               f"@{shape} shape")
     out = {
         "metric": metric,
@@ -324,7 +329,8 @@ def main():
                                f"hidden {w.hidden}, {w.n_heads}/{w.n_kv_heads} heads x {w.head_dim}, "
                                f"SwiGLU {w.intermediate}, {base} base, "
                                f"LoRA r {w.lora_r} alpha {int(w.lora_alpha)} on 7 projections, "
-                               f"streamed through {args.buffers} device slots"
+                               + ("every layer resident on the device" if args.resident else
+                                  f"streamed through {args.buffers} device slots")
                                + (", adapters-off reference pass per layer (DPO)" if w.dpo else ""),
                    "batch": w.batch, "seq": w.seq, "tokens_per_step": T, "parallelism": "none (1 GPU)",
                    "store": "file (page cache dropped after each read)" if args.store_file else "pinned host RAM"},
