@@ -185,7 +185,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="llama8b")
     ap.add_argument("--layers", type=int, default=0, help="override depth (0 = the workload's)")
-    ap.add_argument("--buffers", type=int, default=2)
+    ap.add_argument("--buffers", type=int, default=2,
+                    help="device slots of the streaming pool (0 = as deep as half the free memory allows)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-baseline-full", action="store_true",
                     help="also time one Qwen2.5-32B-shaped layer on the oracle (about a minute more)")
@@ -330,7 +331,8 @@ def main():
                                f"SwiGLU {w.intermediate}, {base} base, "
                                f"LoRA r {w.lora_r} alpha {int(w.lora_alpha)} on 7 projections, "
                                + ("every layer resident on the device" if args.resident else
-                                  f"streamed through {args.buffers} device slots")
+                                  f"streamed through {s1.n_slots} device slots"
+                                  + (" (depth chosen by the library)" if args.buffers == 0 else ""))
                                + (", adapters-off reference pass per layer (DPO)" if w.dpo else ""),
                    "batch": w.batch, "seq": w.seq, "tokens_per_step": T, "parallelism": "none (1 GPU)",
                    "store": "file (page cache dropped after each read)" if args.store_file else "pinned host RAM"},

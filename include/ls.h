@@ -73,7 +73,9 @@ typedef struct ls_config {
   int32_t lora_r;          /* 1..64 */
   float lora_alpha;        /* LoRA scale is lora_alpha / lora_r */
   uint32_t lora_mask;      /* bit p set = adapter on projection p (bits 0..6) */
-  int32_t n_buffers;       /* device slots in the streaming pool, >= 2 */
+  int32_t n_buffers;       /* device slots in the streaming pool: 2..64, or 0 = the deepest
+                              pool (at most one slot per layer) that fits vram_budget, or half
+                              of the free device memory when vram_budget is 0 */
   int32_t max_tokens;      /* upper bound on batch * seq for every call */
   int32_t max_seq;         /* upper bound on seq (attention scratch is sized by it) */
   int32_t resident;        /* 1 = keep every layer on the device (same blob layout;
@@ -128,6 +130,7 @@ typedef struct ls_stats {
   uint64_t store_reads;        /* LS_STORE_FILE: blobs read from the file since create */
   uint64_t store_uncached;     /* LS_STORE_FILE: 1 if every blob is dropped from the OS page cache
                                   after use, so each read comes from the file's device */
+  uint64_t n_slots;            /* device slots of the pool (resident: one per blob) */
   double last_copy_ms;         /* profile=1: summed copy time of the last fwd+bwd */
   double last_compute_ms;      /* profile=1: summed per-layer compute time of last fwd+bwd */
   double last_overlap_ms;      /* profile=1: copy time that overlapped compute */

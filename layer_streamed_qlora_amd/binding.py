@@ -56,7 +56,7 @@ class ls_stats(C.Structure):
     _fields_ = [
         ("blob_bytes", C.c_uint64), ("store_bytes", C.c_uint64), ("device_bytes", C.c_uint64),
         ("h2d_bytes", C.c_uint64), ("h2d_copies", C.c_uint64), ("slot_hits", C.c_uint64),
-        ("store_reads", C.c_uint64), ("store_uncached", C.c_uint64),
+        ("store_reads", C.c_uint64), ("store_uncached", C.c_uint64), ("n_slots", C.c_uint64),
         ("last_copy_ms", C.c_double), ("last_compute_ms", C.c_double), ("last_overlap_ms", C.c_double),
         ("last_span_ms", C.c_double),
         ("k_launches", C.c_uint64 * LS_KC_N), ("k_ms", C.c_double * LS_KC_N),

@@ -194,7 +194,7 @@ bool validate_config(const ls_config& c, const char** why) {
   REQ(c.lora_r >= 1 && c.lora_r <= 64, "lora_r must be in 1..64");
   REQ(std::isfinite(c.lora_alpha), "lora_alpha must be finite");
   REQ((c.lora_mask & ~0x7Fu) == 0, "lora_mask has bits beyond the 7 projections");
-  REQ(c.n_buffers >= 2 && c.n_buffers <= 64, "n_buffers must be in 2..64");
+  REQ(c.n_buffers == 0 || (c.n_buffers >= 2 && c.n_buffers <= 64), "n_buffers must be 0 (auto) or in 2..64");
   REQ(c.max_tokens >= 1 && c.max_tokens <= (1 << 20), "max_tokens must be in 1..2^20");
   REQ(c.max_seq >= 1 && c.max_seq <= c.max_tokens && c.max_seq <= 8192, "max_seq must be in 1..min(max_tokens, 8192)");
   REQ(c.resident == 0 || c.resident == 1, "resident must be 0 or 1");

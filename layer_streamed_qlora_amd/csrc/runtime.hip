@@ -941,11 +941,28 @@ ls_status ls_pack_nf4(const uint16_t* w, uint64_t numel, int32_t double_quant, i
   return LS_OK;
 }
 
-ls_status ls_plan_bytes(const ls_config* cfg, uint64_t* device_bytes, uint64_t* host_bytes, uint64_t* blob_bytes) {
-  if (!cfg) return LS_ERR_INVALID;
+// n_buffers = 0: the deepest pool (at most 64 slots and at most one per layer) whose
+// device plan fits `budget`, else 2 (which the budget check then refuses).  Resident
+// contexts ignore the pool depth; they get 2.
+static void resolve_depth(ls_config& cfg, const BlobLayout& L, uint64_t budget) {
+  if (cfg.n_buffers != 0) return;
+  cfg.n_buffers = 2;
+  if (cfg.resident) return;
+  for (int k = std::max(2, std::min(64, (int)cfg.n_layers)); k > 2; --k) {
+    cfg.n_buffers = k;
+    if (make_plan(cfg, L).total <= budget) return;
+  }
+  cfg.n_buffers = 2;
+}
+
+ls_status ls_plan_bytes(const ls_config* cfg_in, uint64_t* device_bytes, uint64_t* host_bytes, uint64_t* blob_bytes) {
+  if (!cfg_in) return LS_ERR_INVALID;
   const char* why = nullptr;
-  if (!validate_config(*cfg, &why)) { g_create_err = why; return LS_ERR_INVALID; }
+  if (!validate_config(*cfg_in, &why)) { g_create_err = why; return LS_ERR_INVALID; }
+  ls_config resolved = *cfg_in;
+  const ls_config* cfg = &resolved;
   const BlobLayout L = make_layout(*cfg);
+  resolve_depth(resolved, L, cfg_in->vram_budget ? cfg_in->vram_budget : UINT64_MAX);
   const DevPlan P = make_plan(*cfg, L);
   if (device_bytes) *device_bytes = P.total;
   if (host_bytes)
@@ -956,14 +973,15 @@ ls_status ls_plan_bytes(const ls_config* cfg, uint64_t* device_bytes, uint64_t* 
   return LS_OK;
 }
 
-ls_status ls_create(const ls_config* cfg, void* compute_stream, void* copy_stream, ls_ctx** out) {
-  if (!cfg || !out) return fail(nullptr, LS_ERR_INVALID, "null cfg or out");
+ls_status ls_create(const ls_config* cfg_in, void* compute_stream, void* copy_stream, ls_ctx** out) {
+  if (!cfg_in || !out) return fail(nullptr, LS_ERR_INVALID, "null cfg or out");
   *out = nullptr;
   const char* why = nullptr;
-  if (!validate_config(*cfg, &why)) return fail(nullptr, LS_ERR_INVALID, "invalid config: %s", why);
+  if (!validate_config(*cfg_in, &why)) return fail(nullptr, LS_ERR_INVALID, "invalid config: %s", why);
   if (compute_stream && compute_stream == copy_stream) return fail(nullptr, LS_ERR_INVALID, "copy stream must differ from compute stream");
+  ls_config resolved = *cfg_in;
+  const ls_config* cfg = &resolved;
   const BlobLayout L = make_layout(*cfg);
-  const DevPlan P = make_plan(*cfg, L);
   uint64_t budget = cfg->vram_budget;
   if (budget == 0) {
     size_t fr = 0, tot = 0;
@@ -971,6 +989,9 @@ ls_status ls_create(const ls_config* cfg, void* compute_stream, void* copy_strea
     if (e != hipSuccess) return fail(nullptr, LS_ERR_HIP, "hipMemGetInfo failed: %s", hipGetErrorString(e));
     budget = fr;
   }
+  // an automatic pool depth leaves half of the free memory to the caller's tensors
+  resolve_depth(resolved, L, cfg_in->vram_budget ? budget : budget / 2);
+  const DevPlan P = make_plan(*cfg, L);
   if (P.total > budget)
     return fail(nullptr, LS_ERR_BUDGET, "device plan %llu bytes exceeds budget %llu bytes",
                 (unsigned long long)P.total, (unsigned long long)budget);
@@ -1080,6 +1101,7 @@ ls_status ls_create(const ls_config* cfg, void* compute_stream, void* copy_strea
   c->stats.store_bytes = cfg->store == LS_STORE_FILE ? c->stride * (uint64_t)n_blobs
                                                     : L.bytes * (uint64_t)(cfg->n_layers + P.head_slices);
   c->stats.store_uncached = c->uncached ? 1 : 0;
+  c->stats.n_slots = P.n_slots;
   c->stats.device_bytes = P.total;
   *out = c;
   return LS_OK;

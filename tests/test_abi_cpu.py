@@ -147,3 +147,20 @@ def test_file_store_plan_and_validation(tmp_path):
     bad.store = B.LS_STORE_FILE
     with pytest.raises(B.LsError):
         B.ls_plan_bytes(bad)
+
+
+def test_automatic_pool_depth_plan():
+    """n_buffers = 0 plans the deepest pool that fits vram_budget: one slot per layer (at
+    most 64) without a budget, the deepest fitting depth with one, and two slots (which
+    ls_create then refuses) when even that does not fit."""
+    w = synth.WORKLOADS["llama8b"]
+    plan = lambda **kw: B.ls_plan_bytes(B.make_config(w, **kw))[0]
+    assert plan(n_buffers=0) == plan(n_buffers=32)
+    assert plan(n_buffers=0, vram_budget=plan(n_buffers=5)) == plan(n_buffers=5)
+    assert plan(n_buffers=0, vram_budget=plan(n_buffers=5) - 1) == plan(n_buffers=4)
+    assert plan(n_buffers=0, vram_budget=1 << 20) == plan(n_buffers=2)
+    deep = synth.WORKLOADS["qwen72b"]
+    assert B.ls_plan_bytes(B.make_config(deep, n_buffers=0))[0] == B.ls_plan_bytes(B.make_config(deep, n_buffers=64))[0]
+    for bad in (1, 65):
+        with pytest.raises(B.LsError):
+            B.ls_plan_bytes(B.make_config(w, n_buffers=bad))

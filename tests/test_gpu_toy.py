@@ -71,11 +71,13 @@ def test_toy_streamed_equals_resident_bitwise():
             assert np.array_equal(a["dB"][l][p].view(np.uint32), b["dB"][l][p].view(np.uint32)), (l, p)
 
 
-@pytest.mark.parametrize("n_buffers", [3, 5])
+@pytest.mark.parametrize("n_buffers", [3, 5, 0])
 def test_deeper_pool_equals_resident_and_reuses_slots(n_buffers):
     """A pool deeper than two slots on a 6-layer stack: two consecutive steps are bit for
     bit the resident run, and in the second step every slot still holding the layer the
-    other direction needs first is reused, so it copies 2 (L - n_buffers) blobs."""
+    other direction needs first is reused, so it copies 2 (L - n_buffers) blobs.  With
+    n_buffers = 0 the library picks the depth: one slot per layer here, so the second
+    step copies nothing."""
     w = TOY
     L = 6
     x, dy = synth.activations(w)
@@ -84,6 +86,9 @@ def test_deeper_pool_equals_resident_and_reuses_slots(n_buffers):
     want = res.step(x, dy, w.batch, w.seq, with_ref=True)
     res.close()
     run = H.GpuRun(w, range(L), n_buffers=n_buffers)
+    if n_buffers == 0:
+        n_buffers = run.ctx.stats().n_slots
+        assert n_buffers == L, n_buffers
     for s in range(2):
         c0 = run.ctx.stats().h2d_copies
         got = run.step(x, dy, w.batch, w.seq, with_ref=True)
