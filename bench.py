@@ -185,6 +185,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="llama8b")
     ap.add_argument("--layers", type=int, default=0, help="override depth (0 = the workload's)")
+    ap.add_argument("--batch", type=int, default=0, help="override the batch (0 = the workload's)")
+    ap.add_argument("--seq", type=int, default=0, help="override the sequence length (0 = the workload's)")
     ap.add_argument("--buffers", type=int, default=2,
                     help="device slots of the streaming pool (0 = as deep as half the free memory allows)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -211,6 +213,8 @@ def main():
     w = synth.WORKLOADS[args.workload]
     if args.layers:
         w = w.with_(n_layers=args.layers)
+    if args.batch or args.seq:
+        w = w.with_(batch=args.batch or w.batch, seq=args.seq or w.seq)
     T = w.tokens
     profile = 0 if args.no_profile else 1
     # the timed region records events around the forward dequant GEMMs only (the roofline
