@@ -169,7 +169,10 @@ ls_status ls_create(const ls_config* cfg, void* compute_stream, void* copy_strea
 
 /*
  * ls_plan_bytes — the device and pinned-host bytes ls_create would allocate for cfg.
- * Pure host computation, no HIP call.  Returns LS_ERR_INVALID for a bad cfg.
+ * Pure host computation, no HIP call.  Returns LS_ERR_INVALID for a bad cfg.  With
+ * n_buffers = 0 it plans the depth ls_create would pick under cfg->vram_budget; with
+ * no budget either (it cannot query the device), the deepest pool: one slot per layer,
+ * at most 64.
  */
 ls_status ls_plan_bytes(const ls_config* cfg, uint64_t* device_bytes, uint64_t* host_bytes,
                         uint64_t* blob_bytes);
