@@ -41,12 +41,12 @@ def oracle_labels(lab):
 
 
 class HeadRun:
-    def __init__(self, resident=0, n_buffers=2, zero_b=False, store_path=None):
+    def __init__(self, resident=0, n_buffers=2, zero_b=False, store_path=None, vocab=V):
         import torch
         self.torch = torch
-        self.run = H.GpuRun(TOY, [0, 1], resident=resident, n_buffers=n_buffers, zero_b=zero_b, vocab=V,
+        self.run = H.GpuRun(TOY, [0, 1], resident=resident, n_buffers=n_buffers, zero_b=zero_b, vocab=vocab,
                             store_path=store_path)
-        self.Wh, self.gf = synth.head_weights(TOY, V)
+        self.Wh, self.gf = synth.head_weights(TOY, vocab)
         self.run.ctx.stage_head(synth.bf16_bits(self.Wh), synth.bf16_bits(self.gf))
 
     def step(self, kind, lab, beta=0.1, backward=True):
@@ -116,6 +116,27 @@ def test_sft_head_parity_and_full_chain():
     say({k: f"{v:.2e}" for k, v in errs.items() if k in ("Y", "dX")}, "loss", loss_o)
     assert rel(g["out"][0], loss_o) < 1e-2
     assert not fails, fails
+
+
+def test_sft_head_odd_vocabulary():
+    """1999 rows: the last slice has 463 rows, not a multiple of four, so the last
+    column quad of the head product is partial; loss and dY still match the oracle."""
+    v = 1999
+    lab = synth.labels(TOY, v, T)
+    lab[0], lab[1], lab[2] = v - 1, 1535, 1536       # the ragged slice's last row, a slice boundary
+    hr = HeadRun(vocab=v)
+    say("case: toy SFT head, vocab", v)
+    g = hr.step(B.LS_LOSS_SFT, lab, backward=False)
+    hr.close()
+    lo = np.where((lab >= 0) & (lab < v), lab, ohead.IGNORE)
+    yn, r, z = ohead.head_forward(g["Y"], hr.gf, hr.Wh, TOY.rms_eps, rnd=bf16)
+    loss, seqsum, n, dz = ohead.sft_loss(z, lo, SEQ)
+    dy = ohead.head_backward(dz, hr.Wh, g["Y"], hr.gf, r, rnd=bf16)
+    say("loss gpu", g["out"][0], "oracle", loss, "| dY rel L2", H.rel_l2(g["dY"], dy))
+    assert g["out"][1] == n
+    assert rel(g["out"][0], loss) < 1e-4
+    np.testing.assert_allclose(g["out"][2:2 + BATCH], seqsum, rtol=1e-4)
+    assert H.rel_l2(g["dY"], dy) < 2e-2
 
 
 def test_dpo_equal_policy_is_log2():
