@@ -131,6 +131,7 @@ typedef struct ls_stats {
   uint64_t store_uncached;     /* LS_STORE_FILE: 1 if every blob is dropped from the OS page cache
                                   after use, so each read comes from the file's device */
   uint64_t n_slots;            /* device slots of the pool (resident: one per blob) */
+  uint64_t poison_fills;       /* LS_DEBUG_POISON: slots filled with 0xFF before a copy */
   double last_copy_ms;         /* profile=1: summed copy time of the last fwd+bwd */
   double last_compute_ms;      /* profile=1: summed per-layer compute time of last fwd+bwd */
   double last_overlap_ms;      /* profile=1: copy time that overlapped compute */
@@ -164,6 +165,13 @@ typedef struct ls_ctx ls_ctx;
  * stream of its own (default priority) on which ls_backward runs the adapter-gradient
  * reductions beside the compute stream; ls_backward's work on the compute stream
  * ends with a wait for them.
+ * Race detection (environment, read here; for tests, results must not change):
+ *   LS_DEBUG_POISON=1        before every copy into a slot, the copy stream first fills
+ *                            the slot with 0xFF bytes (NF4 code 15, NaN scales), after
+ *                            the event that says the slot's last reader is done;
+ *   LS_DEBUG_COPY_DELAY_US=n the copy stream also sleeps n microseconds (host function,
+ *                            n <= 1e6) between that fill and the copy.
+ * A missing wait on either side of the pool then shows as changed results.
  */
 ls_status ls_create(const ls_config* cfg, void* compute_stream, void* copy_stream, ls_ctx** out);
 
@@ -181,17 +189,25 @@ ls_status ls_plan_bytes(const ls_config* cfg, uint64_t* device_bytes, uint64_t* 
  * ls_stage_layer — encode one layer into the pinned store (NF4 packing with
  * blockwise absmax and optional double quantisation, or a bf16 copy) on the host
  * CPU.  Synchronous: the caller's buffers may be freed on return.  A resident
- * context also copies the blob to its device copy of the layer.
+ * context also copies the blob to its device copy of the layer.  Staging invalidates
+ * the last forward (ls_backward returns LS_ERR_STATE until the next ls_forward).
  * Errors: LS_ERR_INVALID (layer index, null pointer), LS_ERR_STATE (a forward or
  * backward is in flight: call ls_sync first).
  */
 ls_status ls_stage_layer(ls_ctx* ctx, int32_t layer, const ls_layer_host* w);
 
 /*
- * ls_set_lora — register the adapter of (layer, proj).  A [r, in], B [out, r] and
- * the gradient buffers dA, dB (same shapes) are float32 device pointers owned by the
- * caller and borrowed until re-set or ls_destroy.  Projections outside lora_mask
- * need no registration.  dA/dB may be NULL if no gradient is wanted.
+ * ls_set_lora — register the adapter of (layer, proj).  The adapters are the only
+ * trained values and stay on the GPU while the frozen base streams (the
+ * lachieslifestyle.com how-to, its opening paragraph; kept in full precision:
+ * "Fine-Tuning an 8B Parameter Model on a 4 GB Laptop GPU", section "LoRA and QLoRA:
+ * Train a Fraction of the Parameters").  A [r, in], B [out, r] and the gradient
+ * buffers dA, dB (same shapes) are float32 device pointers owned by the caller and
+ * borrowed until re-set or ls_destroy.  Projections outside lora_mask need no
+ * registration.  dA/dB may be NULL if no gradient is wanted.  A registration
+ * invalidates the last forward: ls_backward then returns LS_ERR_STATE until the next
+ * ls_forward (the backward reuses per-layer products of the forward's adapters).
+ * Errors: LS_ERR_INVALID (index out of range, null A or B).
  */
 ls_status ls_set_lora(ls_ctx* ctx, int32_t layer, int32_t proj, const float* A, const float* B,
                       float* dA, float* dB);
@@ -216,19 +232,27 @@ ls_status ls_forward(ls_ctx* ctx, const void* X, int32_t batch, int32_t seq, int
 
 /*
  * ls_backward — enqueue the recompute backward: for l = L-1 .. 0 re-stream layer l,
- * recompute its forward from the checkpoint, and back-propagate.
+ * recompute its forward from the checkpoint, and back-propagate (every layer is read
+ * again for the backward recomputation: the lachieslifestyle.com how-to, section
+ * "What Soup layer streaming changes"; only the adapters receive gradients:
+ * "Fine-Tuning an 8B Parameter Model on a 4 GB Laptop GPU", section "LoRA and QLoRA:
+ * Train a Fraction of the Parameters").
  *   dY: device bf16 [T, hidden] gradient of the last layer's output.
  *   dX: device bf16 [T, hidden] receives the gradient of the stack input.
  *   accumulate: 0 = write dA/dB, 1 = add into the registered dA/dB buffers.
  * dX may alias dY: dY is read only by the last layer's backward and dX written only at
  * the end of the first layer's.  Requires a preceding ls_forward with lora_on = 1 on
- * this context (same T), else LS_ERR_STATE.  Deterministic: no atomics, fixed
- * reduction order.
+ * this context (same T) with no ls_stage_layer or ls_set_lora since, else LS_ERR_STATE.
+ * Deterministic: no atomics, fixed reduction order.  Errors: LS_ERR_STATE (no valid
+ * forward), LS_ERR_INVALID (null dY or dX with T > 0).
  */
 ls_status ls_backward(ls_ctx* ctx, const void* dY, void* dX, int32_t accumulate);
 
-/* ls_sync — wait for both streams; returns the first deferred HIP error, or LS_ERR_HIP
- * with a message if a read from the LS_STORE_FILE store failed. */
+/* ls_sync — wait for the copy stream, the compute stream and the library's side stream
+ * (the copies run on a dedicated stream beside the compute: "Soup CLI fine-tunes
+ * Llama-3.1-8B on a 4 GB laptop GPU ...", second paragraph).  Returns the first
+ * deferred HIP error, or LS_ERR_HIP with a message if a read from the LS_STORE_FILE
+ * store failed; either makes the context's error sticky. */
 ls_status ls_sync(ls_ctx* ctx);
 
 /*
@@ -246,14 +270,26 @@ enum { LS_PROFILE_OFF = 0, LS_PROFILE_ALL = 1, LS_PROFILE_GEMM = 2 };
  * in flight: call ls_sync first).  Errors: LS_ERR_INVALID (unknown level), LS_ERR_STATE. */
 ls_status ls_set_profile(ls_ctx* ctx, int32_t profile);
 
-/* ls_get_stats — counters since ls_create (host pointer out). */
+/* ls_get_stats — counters since ls_create (host pointer out): bytes and copies of the
+ * layer stream, slot reuse, peak device bytes and, when profiling, per-class kernel
+ * times.  These are the figures the pages report for a streamed run: throughput next
+ * to peak device memory, with the GPU's utilisation ("Soup CLI fine-tunes
+ * Llama-3.1-8B on a 4 GB laptop GPU ...", first paragraph).  Errors: LS_ERR_INVALID
+ * (null pointer).  Works on a context in the sticky error state. */
 ls_status ls_get_stats(const ls_ctx* ctx, ls_stats* out);
 
 /* ls_last_error — message of the last failing call on ctx (or of the last failing
- * ls_create when ctx is NULL).  Valid until the next call on the same context. */
+ * ls_create / ls_plan_bytes when ctx is NULL).  Valid until the next call on the same
+ * context.  A refused run says why (the how-to's "Step 7: Train and keep the log":
+ * refuse, and keep the reason, rather than run wrong). */
 const char* ls_last_error(const ls_ctx* ctx);
 
-/* ls_destroy — wait for outstanding work and free everything the library owns. */
+/* ls_destroy — wait for outstanding work and free everything the library owns: the
+ * pinned store (or the store file, which is removed), the device plan, the streams and
+ * events the library created.  Caller-owned buffers (activations, adapters, the
+ * streams passed to ls_create) are untouched.  The pool and store it releases are the
+ * ones of the pages' design ("Soup CLI fine-tunes Llama-3.1-8B on a 4 GB laptop GPU
+ * ...", second paragraph).  NULL is a no-op. */
 void ls_destroy(ls_ctx* ctx);
 
 /*
@@ -281,6 +317,28 @@ ls_status ls_pack_nf4(const uint16_t* w, uint64_t numel, int32_t double_quant, i
  * slot, then the dequant kernel).  Synchronous.  For checking the encoding.
  */
 ls_status ls_read_weight(ls_ctx* ctx, int32_t layer, int32_t proj, void* out);
+
+/*
+ * ls_base_gemm — the frozen base term of one projection group of a staged layer, run
+ * through the fused dequant-GEMM kernels that ls_forward and ls_backward launch for
+ * that group, with the adapter term off.  The 4-bit expansion the pages describe
+ * ("Fine-Tuning an 8B Parameter Model on a 4 GB Laptop GPU", section "Quantization:
+ * Shrink the Weights") happens inside those kernels; this call makes it observable:
+ * with one 1.0 per row of X and zeros elsewhere, out holds dequantised weights
+ * exactly (a float32 sum of one product w * 1.0 and zeros).
+ *   group: 0 = q|k|v (outputs q, k, v side by side), 1 = o, 2 = gate|up (outputs gate
+ *          then up; the paired gate|up kernel of the forward when both adapter terms
+ *          fit it, as in ls_forward), 3 = down.
+ *   transposed = 0: out[M, sum n_out] = X[M, n_in] deq(W)^T  (the forward orientation)
+ *   transposed = 1: out[M, n_in] = X[M, sum n_out] deq(W)   (the backward's W^T)
+ *   X: device bf16, rows of the widths above; out: device float32, row-major with
+ *   that width; 1 <= M <= max_tokens.
+ * The layer reaches a slot as in ls_forward (copied from the store unless the context is
+ * resident or the slot holds it).  Synchronous.  Errors: LS_ERR_INVALID (index, size,
+ * null pointer), LS_ERR_STATE (layer not staged, work in flight).
+ */
+ls_status ls_base_gemm(ls_ctx* ctx, int32_t layer, int32_t group, int32_t transposed, const void* X, int32_t M,
+                       float* out);
 
 /* ---------------------------------------------------------------------------
  * Training-loop closure: optimizer step and adapter files.

@@ -56,7 +56,7 @@ class ls_stats(C.Structure):
     _fields_ = [
         ("blob_bytes", C.c_uint64), ("store_bytes", C.c_uint64), ("device_bytes", C.c_uint64),
         ("h2d_bytes", C.c_uint64), ("h2d_copies", C.c_uint64), ("slot_hits", C.c_uint64),
-        ("store_reads", C.c_uint64), ("store_uncached", C.c_uint64), ("n_slots", C.c_uint64),
+        ("store_reads", C.c_uint64), ("store_uncached", C.c_uint64), ("n_slots", C.c_uint64), ("poison_fills", C.c_uint64),
         ("last_copy_ms", C.c_double), ("last_compute_ms", C.c_double), ("last_overlap_ms", C.c_double),
         ("last_span_ms", C.c_double),
         ("k_launches", C.c_uint64 * LS_KC_N), ("k_ms", C.c_double * LS_KC_N),
@@ -88,6 +88,7 @@ SIGNATURES = {
     "ls_pack_nf4": (C.c_int, [C.c_void_p, C.c_uint64, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p,
                               C.c_void_p, C.c_void_p]),
     "ls_read_weight": (C.c_int, [C.c_void_p, C.c_int32, C.c_int32, C.c_void_p]),
+    "ls_base_gemm": (C.c_int, [C.c_void_p, C.c_int32, C.c_int32, C.c_int32, C.c_void_p, C.c_int32, C.c_void_p]),
     "ls_adamw_step": (C.c_int, [C.c_void_p, C.POINTER(ls_adamw)]),
     "ls_adamw_reset": (C.c_int, [C.c_void_p]),
     "ls_save_adapters": (C.c_int, [C.c_void_p, C.c_char_p]),
@@ -227,6 +228,9 @@ class Context:
 
     def read_weight(self, layer, proj, out_ptr):
         self._chk(lib().ls_read_weight(self.h, layer, proj, out_ptr))
+
+    def base_gemm(self, layer, group, transposed, x_ptr, M, out_ptr):
+        self._chk(lib().ls_base_gemm(self.h, layer, group, transposed, x_ptr, M, out_ptr))
 
     def adamw_step(self, step, lr, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01):
         hp = ls_adamw(lr=lr, beta1=beta1, beta2=beta2, eps=eps, weight_decay=weight_decay, step=step)

@@ -335,6 +335,11 @@ __global__ void k_fill_f32(float* p, int64_t n, float v) {
   if (idx < n) p[idx] = v;
 }
 
+__global__ void k_fill_u32(uint32_t* p, int64_t n, uint32_t v) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx < n) p[idx] = v;
+}
+
 }  // namespace
 
 static inline unsigned blocks_for(int64_t n, int t) { return (unsigned)((n + t - 1) / t); }
@@ -421,6 +426,12 @@ hipError_t launch_convert_batch(const ConvBatch& b, hipStream_t s) {
 hipError_t launch_fill_f32(float* p, int64_t n, float v, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   hipLaunchKernelGGL(k_fill_f32, dim3(blocks_for(n, 256)), dim3(256), 0, s, p, n, v);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_fill_u32, dim3(blocks_for(n, 256)), dim3(256), 0, s, p, n, v);
   return hipGetLastError();
 }
 

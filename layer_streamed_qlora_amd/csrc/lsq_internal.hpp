@@ -234,6 +234,8 @@ hipError_t launch_rope_bwd_convert(const float* src, uint16_t* dst, int32_t ld, 
 hipError_t launch_rope_tab(uint16_t* qk, int32_t ld, int32_t T, int32_t seq, int32_t nh, int32_t hd,
                            const float2* tab, int32_t inverse, hipStream_t s);
 hipError_t launch_fill_f32(float* p, int64_t n, float v, hipStream_t s);
+// p[0 .. n) = v (a bit pattern; the slot poisoning of LS_DEBUG_POISON)
+hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t s);
 hipError_t gemm_dequant_init();
 // gu float32 [T, 2I] (gate | up) -> act bf16 [T, I]
 hipError_t launch_swiglu_fwd(const float* gu, int32_t I, uint16_t* act, int32_t T, hipStream_t s);

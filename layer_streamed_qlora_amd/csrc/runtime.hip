@@ -23,6 +23,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <string>
 #include <vector>
@@ -241,6 +242,12 @@ struct ls_ctx {
   std::atomic<int> store_err{0};
   std::atomic<uint64_t> store_reads{0};
   float levels_h[16];
+  // race detection (read from the environment at ls_create): LS_DEBUG_POISON=1 fills a
+  // slot with 0xFF bytes on the copy stream once its last reader is done, before the
+  // next copy lands in it; LS_DEBUG_COPY_DELAY_US=n holds the copy stream n
+  // microseconds (a host function) between that point and the copy
+  bool dbg_poison = false;
+  uint32_t dbg_delay_us = 0;
   // state
   bool fwd_valid = false, fwd_lora = false;
   int fwd_T = 0, fwd_batch = 0, fwd_seq = 0;
@@ -415,6 +422,10 @@ ls_status store_write(ls_ctx* c, int l, const uint8_t* blob) {
 }
 
 // ------------------------------------------------------------------ pool
+// Host function on the copy stream (LS_DEBUG_COPY_DELAY_US): widens every window in
+// which a missing event wait would let the compute stream read a slot being refilled.
+void copy_delay(void* p) { usleep(*static_cast<const uint32_t*>(p)); }
+
 uint8_t* slot_ptr(ls_ctx* c, int layer) {
   const int s = c->cfg.resident ? layer : layer % c->cfg.n_buffers;
   return c->dbase + c->plan.slots + (uint64_t)s * c->lay.bytes;
@@ -426,6 +437,11 @@ ls_status ensure_copy(ls_ctx* c, int l) {
   const int s = l % c->cfg.n_buffers;
   if (c->slot_layer[s] == l) { c->stats.slot_hits++; return LS_OK; }
   if (c->cons_rec[s]) HIPCHK(c, hipStreamWaitEvent(c->ps, c->consumed[s], 0));
+  if (c->dbg_poison) {
+    HIPCHK(c, launch_fill_u32(reinterpret_cast<uint32_t*>(slot_ptr(c, l)), (int64_t)(c->lay.bytes / 4), 0xFFFFFFFFu, c->ps));
+    c->stats.poison_fills += 1;
+  }
+  if (c->dbg_delay_us) HIPCHK(c, hipLaunchHostFunc(c->ps, copy_delay, &c->dbg_delay_us));
   {
     Span sp(c, c->ps, true);
     if (c->fd >= 0) {
@@ -909,6 +925,13 @@ ls_status layer_backward(ls_ctx* c, int l, const uint8_t* blob, const Dims& d, c
     KTimer kt(c, LS_KC_GEMM_BWD, bwd_flop(d.qkvd, d.h), tb * d.qkvd + wbytes(c, 0) + wbytes(c, 1) + wbytes(c, 2) + 2 * tb * d.h);
     HIPCHK(c, launch_gemm_bwd(b, c->cs));
   }
+  // dx may alias dy (a one-layer stack): the side stream's dB product of the down
+  // projection reads dy, so it must be done before dx is written over it
+  {
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(dx), b0 = reinterpret_cast<uintptr_t>(dy);
+    const uintptr_t n = (uintptr_t)tb * (uintptr_t)d.h;
+    if (a0 < b0 + n && b0 < a0 + n && (st = join_side(c))) return st;
+  }
   {
     KTimer kt(c, LS_KC_GLUE, 0.0, 4 * tb * d.h);
     HIPCHK(c, launch_rmsnorm_bwd(dn32, x_in, nullptr, g1, c->dp<float>(c->plan.rstd1), dh32, nullptr, nullptr, dx, d.T, d.h, c->cs));
@@ -1019,6 +1042,8 @@ ls_status ls_create(const ls_config* cfg_in, void* compute_stream, void* copy_st
     return bail(LS_ERR_HIP);
   }
   if (gemm_dequant_init() != hipSuccess) { c->err = "kernel attribute setup failed"; return bail(LS_ERR_HIP); }
+  if (const char* e = getenv("LS_DEBUG_POISON")) c->dbg_poison = e[0] == '1';
+  if (const char* e = getenv("LS_DEBUG_COPY_DELAY_US")) c->dbg_delay_us = (uint32_t)std::min(1000000L, std::max(0L, atol(e)));
 
   const int nb = P.n_slots;
   c->slot_layer.assign(nb, -1);
@@ -1134,6 +1159,9 @@ ls_status ls_stage_layer(ls_ctx* c, int32_t layer, const ls_layer_host* w) {
   }
   if (ls_status st = store_write(c, layer, blob)) return st;
   c->staged[layer] = 1;
+  // the backward reuses the forward's per-layer products, which were made from the
+  // old weights: it needs a new forward
+  c->fwd_valid = false;
   // a slot holding the old contents of this layer is stale now
   for (auto& sl : c->slot_layer)
     if (sl == layer) sl = -1;
@@ -1153,6 +1181,8 @@ ls_status ls_set_lora(ls_ctx* c, int32_t layer, int32_t proj, const float* A, co
   if (!A || !B) return fail(c, LS_ERR_INVALID, "null A or B");
   c->lora[layer][proj] = {A, B, dA, dB};
   ++c->lora_version;
+  // the forward's s X A^T and the adapters' bf16 copies belong to the old registration
+  c->fwd_valid = false;
   return LS_OK;
 }
 
@@ -1305,6 +1335,63 @@ ls_status ls_read_weight(ls_ctx* c, int32_t layer, int32_t proj, void* out) {
   if ((st = use_layer(c, layer))) return st;
   HIPCHK(c, launch_dequant(wref(c, slot_ptr(c, layer), proj), wformat(c->cfg), c->dp<float>(c->plan.levels),
                            (uint16_t*)out, c->cs));
+  if ((st = release_layer(c, layer))) return st;
+  HIPCHK(c, hipStreamSynchronize(c->cs));
+  HIPCHK(c, hipStreamSynchronize(c->ps));
+  return LS_OK;
+}
+
+ls_status ls_base_gemm(ls_ctx* c, int32_t layer, int32_t group, int32_t transposed, const void* X, int32_t M,
+                       float* out) {
+  if (ls_status st = check_usable(c)) return st;
+  if (layer < 0 || layer >= c->cfg.n_layers || group < 0 || group > 3 || !X || !out || M < 1 || M > c->cfg.max_tokens)
+    return fail(c, LS_ERR_INVALID, "bad layer/group index, null pointer, or M outside 1..max_tokens");
+  if (!c->staged[layer]) return fail(c, LS_ERR_STATE, "layer %d not staged", layer);
+  if (c->in_flight) return fail(c, LS_ERR_STATE, "a forward/backward is in flight: call ls_sync first");
+  const Dims d = dims_of(c, 1, 1);
+  const int fmt = wformat(c->cfg);
+  const float* lv = c->dp<float>(c->plan.levels);
+  static const int p0s[4] = {LS_PROJ_Q, LS_PROJ_O, LS_PROJ_GATE, LS_PROJ_DOWN};
+  static const int ngs[4] = {3, 1, 2, 1};
+  const int p0 = p0s[group], ng = ngs[group];
+  ls_status st;
+  if ((st = ensure_copy(c, layer))) return st;
+  if ((st = use_layer(c, layer))) return st;
+  const uint8_t* blob = slot_ptr(c, layer);
+  int out_w = 0;
+  for (int i = 0; i < ng; ++i) out_w += c->lay.p[p0 + i].n_out;
+  const int n_in = c->lay.p[p0].n_in;
+  if (!transposed) {
+    FwdArgs f;
+    f.x = (const uint16_t*)X; f.ldx = n_in; f.M = M; f.K = n_in; f.n_groups = ng;
+    int col = 0;
+    for (int i = 0; i < ng; ++i) {
+      f.g[i].w = wref(c, blob, p0 + i);
+      f.g[i].out_col0 = col;
+      col += c->lay.p[p0 + i].n_out;
+    }
+    f.levels = lv; f.format = fmt;
+    if (group == 2 && 2 * d.r16 <= 64) {
+      // the forward's paired kernel: act is written to the workspace, gate and up in
+      // float32 to out
+      f.swiglu = 1; f.y = c->dp<uint16_t>(c->plan.act); f.ldy = d.I;
+      f.gu32 = out; f.ldgu = out_w;
+    } else {
+      f.y32 = out; f.ldy = out_w;
+    }
+    HIPCHK(c, launch_gemm_fwd(f, c->cs));
+  } else {
+    BwdArgs b;
+    b.dy = (const uint16_t*)X; b.lddy = out_w; b.M = M; b.N = n_in; b.n_segs = ng;
+    int col = 0;
+    for (int i = 0; i < ng; ++i) {
+      b.seg[i].w = wref(c, blob, p0 + i);
+      b.seg[i].a_col0 = col;
+      col += c->lay.p[p0 + i].n_out;
+    }
+    b.out32 = out; b.ldo = n_in; b.levels = lv; b.format = fmt;
+    HIPCHK(c, launch_gemm_bwd(b, c->cs));
+  }
   if ((st = release_layer(c, layer))) return st;
   HIPCHK(c, hipStreamSynchronize(c->cs));
   HIPCHK(c, hipStreamSynchronize(c->ps));

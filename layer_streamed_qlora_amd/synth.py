@@ -108,14 +108,19 @@ def bf16_bits(values32: np.ndarray) -> np.ndarray:
     return (v.view(np.uint32) >> 16).astype(np.uint16)
 
 
+def layer_weight(w: Workload, layer: int, p: str) -> np.ndarray:
+    """Base weight p of one layer: float32 array of bf16 values [out, in]."""
+    x = _rng(w.wid, layer, TENSOR_ID[p]).standard_normal(w.proj_shape(p), dtype=np.float32) * np.float32(0.02)
+    return _to_bf16_values(x)
+
+
 def layer_weights(w: Workload, layer: int) -> dict:
     """Base weights of one layer: proj -> float32 array of bf16 values [out, in];
-    'g1', 'g2' -> ones [hidden]."""
-    out = {}
-    for p in PROJS:
-        shape = w.proj_shape(p)
-        x = _rng(w.wid, layer, TENSOR_ID[p]).standard_normal(shape, dtype=np.float32) * np.float32(0.02)
-        out[p] = _to_bf16_values(x)
+    'g1', 'g2' -> ones [hidden].  The seven tensors have independent streams, so they
+    are drawn on a thread pool (the values do not depend on it)."""
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(max_workers=len(PROJS)) as ex:
+        out = dict(zip(PROJS, ex.map(lambda p: layer_weight(w, layer, p), PROJS)))
     out["g1"] = np.ones(w.hidden, np.float32)
     out["g2"] = np.ones(w.hidden, np.float32)
     return out

@@ -34,7 +34,10 @@ class GpuRun:
     """One context with staged layers and torch-owned adapters on cuda:0."""
 
     def __init__(self, w, layer_seeds, resident=0, n_buffers=2, profile=0, zero_b=False, max_tokens=None,
-                 max_seq=None, lora_mask=0x7F, weights=None, adamw=0, vocab=0, store_path=None):
+                 max_seq=None, lora_mask=0x7F, weights=None, adamw=0, vocab=0, store_path=None, layer_bits=None):
+        """weights: per-layer float32 dicts of bf16 values (default: drawn from the
+        seeds); layer_bits: per-layer dicts of bf16 bit patterns, staged as they are
+        (then ``src`` is None)."""
         import torch
         self.torch = torch
         self.w = w
@@ -44,8 +47,11 @@ class GpuRun:
                             max_tokens=max_tokens, max_seq=max_seq, lora_mask=lora_mask, adamw=adamw,
                             vocab=vocab, store_path=store_path)
         self.ctx = B.Context(cfg)
-        self.src = []
+        self.src = [] if layer_bits is None else None
         for i, seed in enumerate(self.layer_seeds):
+            if layer_bits is not None:
+                self.ctx.stage_layer(i, layer_bits[i])
+                continue
             lw = weights[i] if weights is not None else synth.layer_weights(w, seed)
             self.src.append(lw)
             self.ctx.stage_layer(i, {k: synth.bf16_bits(v) for k, v in lw.items()})
@@ -120,9 +126,9 @@ def oracle_layers(w, src_layers):
     return enc, deq
 
 
-def oracle_step(w, src_layers, loras, x32, dy32, batch, seq, with_ref=False):
+def oracle_step(w, src_layers, loras, x32, dy32, batch, seq, with_ref=False, parity=True):
     _, lw = oracle_layers(w, src_layers)
-    return ostack.train_step(x32, dy32, lw, loras, oracle_shape(w), batch, seq, parity=True,
+    return ostack.train_step(x32, dy32, lw, loras, oracle_shape(w), batch, seq, parity=parity,
                              with_reference=with_ref)
 
 

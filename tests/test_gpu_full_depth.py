@@ -1,0 +1,181 @@
+"""The whole Llama-3.1-8B-shaped stack (32 layers, NF4 + double quantisation, LoRA
+r 16 / alpha 32 on all seven projections) on the GPU.
+
+* Full depth against the oracle at batch 1 x seq 128: Y, dX and every one of the 224
+  (layer, projection) dA / dB, against values the oracle wrote
+  (tests/golden/make_llama8b_depth32.py): rows of Y and dX, and seeded samples of
+  every gradient tensor, plus each tensor's full norm.
+* Teacher-forced layers 0, 1 and 31: the oracle runs one layer from the GPU's own
+  input of that layer and the GPU's own gradient arriving at its output (taken from
+  runs of the sub-stacks that follow it), and must match that layer's Y, dX, dA, dB.
+* Streamed (two slots) against resident, bit for bit, over two consecutive steps at
+  the measured configuration (8 x 512): the schedule the benchmark times, with its
+  turnaround reuse (62 copies in the first step, 60 in the second).
+* The race-detection hooks (slot poisoning and copy delays) leave a six-layer streamed
+  run bit-identical to the resident one.
+
+Streaming changes where the weights come from, not the arithmetic: the streamed run is
+bit-exact against a resident one ("Soup: Fine-Tuning an 8B Model on a 4 GB Laptop GPU,
+One Layer at a Time", second paragraph); every layer is read again for the backward
+recomputation (the lachieslifestyle.com how-to, "What Soup layer streaming changes").
+"""
+import importlib.util
+import os
+
+import numpy as np
+import pytest
+
+from layer_streamed_qlora_amd import synth
+import lsq_harness as H
+
+pytestmark = pytest.mark.gpu
+
+W8 = synth.WORKLOADS["llama8b"]
+L = W8.n_layers
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def golden_module():
+    spec = importlib.util.spec_from_file_location("make_llama8b_depth32",
+                                                  os.path.join(HERE, "golden", "make_llama8b_depth32.py"))
+    m = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(m)
+    return m
+
+
+@pytest.fixture(scope="module")
+def bits32():
+    say("drawing the 32 Llama-shaped layers ...")
+    out = []
+    for l in range(L):
+        lw = synth.layer_weights(W8, l)
+        out.append({k: synth.bf16_bits(v) for k, v in lw.items()})
+        del lw
+    return out
+
+
+def gpu_run(w, layers, bits, x, dy=None, **kw):
+    run = H.GpuRun(w, list(layers), layer_bits=[bits[l] for l in layers], **kw)
+    out = run.step(x, dy, w.batch, w.seq, backward=dy is not None)
+    out["stats"] = run.ctx.stats()
+    run.close()
+    return out
+
+
+def test_full_depth_against_stored_oracle(bits32):
+    g = golden_module()
+    ref = np.load(g.OUT)
+    w = g.workload()
+    x, dy = synth.activations(w)
+    say("case: llama8b, 32 layers, 1 x 128: GPU")
+    gpu = gpu_run(w, range(L), bits32, x, dy, max_tokens=w.tokens, max_seq=w.seq)
+    rows = ref["rows"]
+    errs = {"Y": H.rel_l2(gpu["Y"][rows], ref["Y_rows"]), "dX": H.rel_l2(gpu["dX"][rows], ref["dX_rows"])}
+    norms = {"Y": abs(np.linalg.norm(gpu["Y"].astype(np.float64)) / float(ref["Y_norm"]) - 1),
+             "dX": abs(np.linalg.norm(gpu["dX"].astype(np.float64)) / float(ref["dX_norm"]) - 1)}
+    for l in range(L):
+        for pi, p in enumerate(H.PROJS):
+            for which, t in (("dA", gpu["dA"][l][p]), ("dB", gpu["dB"][l][p])):
+                flat = t.reshape(-1)
+                idx = g.sample_indices(l, 2 * pi + (which == "dB"), flat.size)
+                key = f"{which}_{l}_{p}"
+                errs[f"{which}[{l}].{p}"] = H.rel_l2(flat[idx], ref[key])
+                norms[f"{which}[{l}].{p}"] = abs(np.linalg.norm(flat.astype(np.float64)) / float(ref[key + "_norm"]) - 1)
+    worst_g = max((k for k in errs if k[0] == "d" and k != "dX"), key=errs.get)
+    say({"Y": f"{errs['Y']:.2e}", "dX": f"{errs['dX']:.2e}", "worst grad": f"{worst_g} {errs[worst_g]:.2e}",
+         "worst norm ratio": f"{max(norms.values()):.2e}"})
+    per_layer = [max(errs[f"{wh}[{l}].{p}"] for wh in ("dA", "dB") for p in H.PROJS) for l in range(L)]
+    say("worst dA/dB per layer:", " ".join(f"{v:.1e}" for v in per_layer))
+    fails = [(k, v) for k, v in errs.items() if v > (1e-2 if k == "Y" else 2e-2) or not np.isfinite(v)]
+    fails += [("norm " + k, v) for k, v in norms.items() if v > (1e-2 if k == "Y" else 2e-2)]
+    assert not fails, fails
+
+
+def test_teacher_forced_layers_0_1_31(bits32):
+    w = W8.with_(batch=1, seq=128)
+    x, dy = synth.activations(w)
+    kw = dict(max_tokens=w.tokens, max_seq=w.seq)
+    say("case: llama8b teacher-forced layers 0, 1, 31: GPU runs")
+    full = gpu_run(w, range(L), bits32, x, dy, **kw)
+    x1 = gpu_run(w, [0], bits32, x, **kw)["Y"]
+    x2 = gpu_run(w, [0, 1], bits32, x, **kw)["Y"]
+    x31 = gpu_run(w, range(31), bits32, x, **kw)["Y"]
+    s1 = gpu_run(w, range(1, L), bits32, x1, dy, **kw)     # its dX reaches layer 0's output
+    s2 = gpu_run(w, range(2, L), bits32, x2, dy, **kw)     # ... layer 1's output
+    s31 = gpu_run(w, [31], bits32, x31, dy, **kw)          # layer 31 alone
+    # every layer's work depends only on its own inputs: the sub-stacks reproduce the
+    # full run's gradients bit for bit
+    for sub, first in ((s1, 1), (s2, 2), (s31, 31)):
+        for i, l in enumerate(range(first, L)):
+            for p in H.PROJS:
+                assert np.array_equal(sub["dA"][i][p].view(np.uint32), full["dA"][l][p].view(np.uint32)), (first, l, p)
+                assert np.array_equal(sub["dB"][i][p].view(np.uint32), full["dB"][l][p].view(np.uint32)), (first, l, p)
+    assert np.array_equal(s31["Y"].view(np.uint32), full["Y"].view(np.uint32))
+    cases = {0: (x, s1["dX"], x1, full["dX"]), 1: (x1, s2["dX"], x2, s1["dX"]), 31: (x31, dy, full["Y"], s31["dX"])}
+    for l, (x_in, dy_in, y_gpu, dx_gpu) in cases.items():
+        say(f"oracle on layer {l} from the GPU's own input and output gradient ...")
+        src = {k: (v.astype(np.uint32) << 16).view(np.float32) for k, v in bits32[l].items()}
+        ora = H.oracle_step(w, [src], [synth.layer_lora(w, l)], x_in, dy_in, 1, w.seq)
+        gpu = {"Y": y_gpu, "dX": dx_gpu, "dA": [full["dA"][l]], "dB": [full["dB"][l]]}
+        errs, fails = H.compare(gpu, ora)
+        worst = max((v for k, v in errs.items() if k.startswith("d")), default=0.0)
+        say(f"layer {l}:", {"Y": f"{errs['Y']:.2e}", "dX": f"{errs['dX']:.2e}", "worst grad": f"{worst:.2e}"})
+        assert not fails, (l, fails)
+
+
+def assert_same_bits(a, b, n_layers, what):
+    for k in ("Y", "dX"):
+        assert np.array_equal(a[k].view(np.uint32), b[k].view(np.uint32)), (what, k)
+    for l in range(n_layers):
+        for p in H.PROJS:
+            assert np.array_equal(a["dA"][l][p].view(np.uint32), b["dA"][l][p].view(np.uint32)), (what, l, p)
+            assert np.array_equal(a["dB"][l][p].view(np.uint32), b["dB"][l][p].view(np.uint32)), (what, l, p)
+
+
+def two_steps(w, layers, bits, resident, **kw):
+    """Two forward + backward steps on one context; the second swaps the roles of X and
+    dY, so anything left over from the first step would show."""
+    x, dy = synth.activations(w)
+    run = H.GpuRun(w, list(layers), layer_bits=[bits[l] for l in layers], resident=resident, **kw)
+    outs, copies = [], []
+    for a, b in ((x, dy), (dy, x)):
+        c0 = run.ctx.stats().h2d_copies
+        outs.append(run.step(a, b, w.batch, w.seq))
+        copies.append(run.ctx.stats().h2d_copies - c0)
+    st = run.ctx.stats()
+    run.close()
+    return outs, copies, st
+
+
+def test_streamed_equals_resident_32_layers_two_steps(bits32):
+    w = W8
+    say("case: llama8b 32 layers, 8 x 512, streamed (2 slots) vs resident, two steps")
+    s_out, s_copies, _ = two_steps(w, range(L), bits32, 0)
+    r_out, _, _ = two_steps(w, range(L), bits32, 1)
+    say("copies per step (streamed):", s_copies)
+    assert s_copies == [2 * L - 2, 2 * L - 4]
+    for i in range(2):
+        assert_same_bits(s_out[i], r_out[i], L, f"step {i}")
+
+
+@pytest.mark.parametrize("env", [{"LS_DEBUG_POISON": "1"}, {"LS_DEBUG_COPY_DELAY_US": "4000"},
+                                 {"LS_DEBUG_POISON": "1", "LS_DEBUG_COPY_DELAY_US": "2000"}],
+                         ids=["poison", "delay", "poison+delay"])
+def test_race_hooks_leave_streamed_bitwise_equal(bits32, env, monkeypatch):
+    w = W8
+    n = 6
+    r_out, _, _ = two_steps(w, range(n), bits32, 1)
+    for k, v in env.items():
+        monkeypatch.setenv(k, v)
+    say("case: llama8b 6 layers, 8 x 512, two steps, streamed with", env)
+    s_out, s_copies, st = two_steps(w, range(n), bits32, 0)
+    if "LS_DEBUG_POISON" in env:
+        assert st.poison_fills == sum(s_copies) > 0
+    else:
+        assert st.poison_fills == 0
+    for i in range(2):
+        assert_same_bits(s_out[i], r_out[i], n, f"step {i}")

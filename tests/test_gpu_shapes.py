@@ -140,3 +140,34 @@ def test_qwen32b_streamed_equals_resident_bitwise():
         for p in H.PROJS:
             assert np.array_equal(a["dA"][l][p].view(np.uint32), b["dA"][l][p].view(np.uint32)), (l, p)
             assert np.array_equal(a["dB"][l][p].view(np.uint32), b["dB"][l][p].view(np.uint32)), (l, p)
+
+
+@pytest.mark.parametrize("name,n_layers,seq", [("toy", 2, 128), ("llama8b", 2, 128)])
+def test_against_the_exact_oracle(name, n_layers, seq):
+    """The GPU against the oracle with no bf16 rounding at all (exact mode), next to the
+    parity-mode oracle's own distance from exact mode.  The second figure is what the
+    bf16 operands alone cost; the GPU must not add more than the bars to it."""
+    w = synth.WORKLOADS[name].with_(batch=1, seq=seq)
+    x, dy = synth.activations(w)
+    say(f"case: {name} {n_layers} layers 1 x {seq} against the exact oracle: GPU")
+    run = H.GpuRun(w, list(range(n_layers)))
+    gpu = run.step(x, dy, 1, seq)
+    src = run.src
+    run.close()
+    loras = [synth.layer_lora(w, l) for l in range(n_layers)]
+    exact = H.oracle_step(w, src, loras, x, dy, 1, seq, parity=False)
+    par = H.oracle_step(w, src, loras, x, dy, 1, seq, parity=True)
+    e_gpu, _ = H.compare(gpu, exact)
+    e_par, _ = H.compare({"Y": par["Y"], "dX": par["dX"],
+                          "dA": [{p: par["grads"][l][p][0] for p in H.PROJS} for l in range(n_layers)],
+                          "dB": [{p: par["grads"][l][p][1] for p in H.PROJS} for l in range(n_layers)]}, exact)
+    wg = max(v for k, v in e_gpu.items() if k.startswith("d"))
+    wp = max(v for k, v in e_par.items() if k.startswith("d"))
+    say({"GPU vs exact": {"Y": f"{e_gpu['Y']:.2e}", "dX": f"{e_gpu['dX']:.2e}", "worst grad": f"{wg:.2e}"},
+         "parity oracle vs exact": {"Y": f"{e_par['Y']:.2e}", "dX": f"{e_par['dX']:.2e}", "worst grad": f"{wp:.2e}"}})
+    for k, v in e_gpu.items():
+        bar = 1e-2 if k == "Y" else 2e-2
+        assert v <= e_par[k] + bar, (k, v, e_par[k])
+    if name == "toy":
+        _, fails = H.compare(gpu, exact)
+        assert not fails, fails
