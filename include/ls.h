@@ -341,6 +341,51 @@ ls_status ls_base_gemm(ls_ctx* ctx, int32_t layer, int32_t group, int32_t transp
                        float* out);
 
 /* ---------------------------------------------------------------------------
+ * One projection outside any context.  The frozen weight is already on the device in
+ * the store's encoding (e.g. from ls_pack_nf4, copied by the caller); the projection is
+ * the LoRA formula over a 4-bit base ("Fine-Tuning an 8B Parameter Model on a 4 GB
+ * Laptop GPU", section "LoRA and QLoRA: Train a Fraction of the Parameters"), computed
+ * by the kernels the streamed stack runs for each projection: the rank-r down product,
+ * then the fused dequant GEMM with the low-rank term as a K-extension.
+ * ------------------------------------------------------------------------- */
+typedef struct ls_weight {
+  int32_t quant;          /* LS_QUANT_NF4 or LS_QUANT_BF16 */
+  int32_t double_quant;   /* NF4: 1 = qabs / scale2 / mean, 0 = absmax */
+  int32_t n_out, n_in;    /* the weight is [n_out, n_in]; n_out % 4 == 0, n_in % 16 == 0 */
+  const void* w;          /* device: NF4 codes, ceil(n_out n_in / 2) bytes (element 2k in
+                             the high nibble of byte k), or bf16 [n_out, n_in] */
+  const float* absmax;    /* device float32 [ceil(n_out n_in / 64)]   (NF4, no DQ) */
+  const uint8_t* qabs;    /* device uint8 [ceil(n_out n_in / 64)]     (NF4 + DQ) */
+  const float* scale2;    /* device float32 [ceil(nblocks / 256)]     (NF4 + DQ) */
+  const float* mean;      /* device float32 [1]                       (NF4 + DQ) */
+} ls_weight;
+
+/* ls_lora_linear_workspace_bytes — bytes of device workspace ls_lora_linear needs for
+ * these sizes (0 for invalid sizes).  No HIP call. */
+uint64_t ls_lora_linear_workspace_bytes(int32_t M, int32_t n_in, int32_t n_out, int32_t r);
+
+/*
+ * ls_lora_linear — enqueue Y = X deq(W)^T + (alpha / r) (X A^T) B^T on `stream`.
+ *   w:     host pointer to the weight description (read during the call).
+ *   X:     device bf16 [M, n_in], 16-byte aligned.  Y: device bf16 [M, n_out].
+ *   A, B:  device float32 [r, n_in] and [n_out, r]; r = 0 means base term only (A, B
+ *          may then be NULL).  0 <= r <= 64.
+ *   workspace: device, 256-byte aligned, at least ls_lora_linear_workspace_bytes; the
+ *          caller owns it and must not touch it until the enqueued work is done.
+ *   stream: hipStream_t, NULL = the default stream.
+ * Every buffer is the caller's.  The first call on a device also writes the NF4 level
+ * table to that device (synchronously).  Asynchronous otherwise.  Errors:
+ * LS_ERR_INVALID (sizes, null or misaligned pointers, small workspace; message from
+ * ls_lora_linear_error), LS_ERR_HIP (a launch failed).
+ */
+ls_status ls_lora_linear(const ls_weight* w, const void* X, int32_t M, const float* A, const float* B, int32_t r,
+                         float alpha, void* Y, void* workspace, uint64_t workspace_bytes, void* stream);
+
+/* ls_lora_linear_error — message of the calling thread's last failing ls_lora_linear*
+ * call. */
+const char* ls_lora_linear_error(void);
+
+/* ---------------------------------------------------------------------------
  * Training-loop closure: optimizer step and adapter files.
  * ------------------------------------------------------------------------- */
 

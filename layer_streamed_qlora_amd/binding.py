@@ -48,6 +48,12 @@ class ls_adamw(C.Structure):
                 ("weight_decay", C.c_float), ("step", C.c_int32)]
 
 
+class ls_weight(C.Structure):
+    _fields_ = [("quant", C.c_int32), ("double_quant", C.c_int32), ("n_out", C.c_int32), ("n_in", C.c_int32),
+                ("w", C.c_void_p), ("absmax", C.c_void_p), ("qabs", C.c_void_p), ("scale2", C.c_void_p),
+                ("mean", C.c_void_p)]
+
+
 class ls_layer_host(C.Structure):
     _fields_ = [("w", C.c_void_p * 7), ("g1", C.c_void_p), ("g2", C.c_void_p)]
 
@@ -89,6 +95,10 @@ SIGNATURES = {
                               C.c_void_p, C.c_void_p]),
     "ls_read_weight": (C.c_int, [C.c_void_p, C.c_int32, C.c_int32, C.c_void_p]),
     "ls_base_gemm": (C.c_int, [C.c_void_p, C.c_int32, C.c_int32, C.c_int32, C.c_void_p, C.c_int32, C.c_void_p]),
+    "ls_lora_linear_workspace_bytes": (C.c_uint64, [C.c_int32, C.c_int32, C.c_int32, C.c_int32]),
+    "ls_lora_linear": (C.c_int, [C.POINTER(ls_weight), C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p, C.c_int32,
+                                 C.c_float, C.c_void_p, C.c_void_p, C.c_uint64, C.c_void_p]),
+    "ls_lora_linear_error": (C.c_char_p, []),
     "ls_adamw_step": (C.c_int, [C.c_void_p, C.POINTER(ls_adamw)]),
     "ls_adamw_reset": (C.c_int, [C.c_void_p]),
     "ls_save_adapters": (C.c_int, [C.c_void_p, C.c_char_p]),
@@ -160,6 +170,22 @@ def ls_pack_nf4(w_bits: np.ndarray, double_quant: bool, n_threads: int = 0):
     _check(lib().ls_pack_nf4(ptr(w), n, int(double_quant), n_threads, ptr(packed), ptr(absmax), ptr(qabs),
                              ptr(scale2), ptr(mean)))
     return packed, absmax, qabs, scale2, (mean[0] if double_quant else None)
+
+
+def ls_lora_linear_workspace_bytes(M, n_in, n_out, r) -> int:
+    return int(lib().ls_lora_linear_workspace_bytes(M, n_in, n_out, r))
+
+
+def _linear_check(st):
+    if st != LS_OK:
+        msg = lib().ls_lora_linear_error()
+        raise LsError(st, msg.decode() if msg else "")
+
+
+def ls_lora_linear(w: ls_weight, X_ptr, M, A_ptr, B_ptr, r, alpha, Y_ptr, ws_ptr, ws_bytes, stream=0):
+    """Y = X deq(W)^T + (alpha / r) (X A^T) B^T; device pointers as integers."""
+    _linear_check(lib().ls_lora_linear(C.byref(w), X_ptr, M, A_ptr or None, B_ptr or None, r, alpha, Y_ptr,
+                                       ws_ptr or None, ws_bytes, stream or None))
 
 
 def ls_check_adapter_file(cfg: ls_config, path: str):

@@ -13,7 +13,14 @@ Stored (float32 values of the float64 results, plus float64 norms):
   dA, dB      for every (layer, projection), the values at N_SAMPLE flat indices drawn
               by ``sample_indices`` (seeded), and each tensor's full norm.
 
-Run: python tests/golden/make_llama8b_depth32.py   (about 10 minutes on 8 cores)
+A second pass runs the same oracle functions, with the same bf16 rounding points, on
+float32 arrays: every product then accumulates in float32, as on the GPU.  Its samples
+are stored under the same keys with the suffix ``_f32``.  Their distance from the
+float64 results is the floor any float32-accumulating implementation sits at: a
+difference far below one bf16 unit before a rounding point flips some roundings, and
+the stack carries those flips through every later layer.
+
+Run: python tests/golden/make_llama8b_depth32.py   (about 15 minutes on 8 cores)
 """
 from __future__ import annotations
 
@@ -31,6 +38,7 @@ if ROOT not in sys.path:
 
 from layer_streamed_qlora_amd import synth  # noqa: E402
 from oracle import model as omodel  # noqa: E402
+from oracle import nf4 as onf4  # noqa: E402
 from oracle import stack as ostack  # noqa: E402
 
 OUT = os.path.join(HERE, "llama8b_depth32_1x128.npz")
@@ -77,15 +85,47 @@ def main():
 
     y, ckpts = ostack.stack_forward(x, None, loras, shp, BATCH, SEQ, True, True, weight_source=weights)
     dx, grads = ostack.stack_backward(dy, ckpts, None, loras, shp, BATCH, SEQ, True, weight_source=weights)
-    rec = {"rows": ROWS, "Y_rows": y[ROWS].astype(np.float32), "Y_norm": np.float64(np.linalg.norm(y)),
-           "dX_rows": dx[ROWS].astype(np.float32), "dX_norm": np.float64(np.linalg.norm(dx))}
+    rec = {"rows": ROWS}
+
+    def store(suffix, y, dx, grads, norms):
+        rec["Y_rows" + suffix] = np.asarray(y)[ROWS].astype(np.float32)
+        rec["dX_rows" + suffix] = np.asarray(dx)[ROWS].astype(np.float32)
+        if norms:
+            rec["Y_norm"] = np.float64(np.linalg.norm(y))
+            rec["dX_norm"] = np.float64(np.linalg.norm(dx))
+        for l in range(w.n_layers):
+            for pi, p in enumerate(synth.PROJS):
+                for which, g in (("dA", grads[l][p][0]), ("dB", grads[l][p][1])):
+                    flat = np.asarray(g, np.float64).reshape(-1)
+                    idx = sample_indices(l, 2 * pi + (which == "dB"), flat.size)
+                    rec[f"{which}_{l}_{p}{suffix}"] = flat[idx].astype(np.float32)
+                    if norms:
+                        rec[f"{which}_{l}_{p}_norm"] = np.float64(np.linalg.norm(flat))
+
+    store("", y, dx, grads, True)
+    del ckpts, grads
+    # the float32-accumulation pass: same functions, same rounding points, float32 arrays
+    f32 = np.float32
+    rnd32 = lambda a: onf4.bf16_round(a).astype(f32)
+
+    def weights32(l):
+        return {k: v.astype(f32) for k, v in weights(l).items()}
+
+    lo32 = [{p: (a.astype(f32), b.astype(f32)) for p, (a, b) in lo.items()} for lo in loras]
+    h = rnd32(x)
+    ck32 = []
     for l in range(w.n_layers):
-        for pi, p in enumerate(synth.PROJS):
-            for which, g in (("dA", grads[l][p][0]), ("dB", grads[l][p][1])):
-                flat = np.asarray(g, np.float64).reshape(-1)
-                idx = sample_indices(l, 2 * pi + (which == "dB"), flat.size)
-                rec[f"{which}_{l}_{p}"] = flat[idx].astype(np.float32)
-                rec[f"{which}_{l}_{p}_norm"] = np.float64(np.linalg.norm(flat))
+        ck32.append(h)
+        yl, _ = omodel.layer_forward(h, weights32(l), lo32[l], shp, BATCH, SEQ, True, rnd32)
+        h = rnd32(yl)
+    y32, g = h, rnd32(dy)
+    grads32 = [None] * w.n_layers
+    for l in reversed(range(w.n_layers)):
+        wl = weights32(l)
+        _, cache = omodel.layer_forward(ck32[l], wl, lo32[l], shp, BATCH, SEQ, True, rnd32)
+        dxl, grads32[l] = omodel.layer_backward(g, cache, wl, lo32[l], shp, BATCH, SEQ, rnd32)
+        g = rnd32(dxl)
+    store("_f32", y32, g, grads32, False)
     np.savez(OUT, **rec)
     print(f"wrote {OUT} ({os.path.getsize(OUT)} bytes) in {time.time() - t0:.0f} s", flush=True)
 
