@@ -381,6 +381,20 @@ uint64_t ls_lora_linear_workspace_bytes(int32_t M, int32_t n_in, int32_t n_out, 
 ls_status ls_lora_linear(const ls_weight* w, const void* X, int32_t M, const float* A, const float* B, int32_t r,
                          float alpha, void* Y, void* workspace, uint64_t workspace_bytes, void* stream);
 
+/*
+ * ls_lora_linear_noalloc — ls_lora_linear for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same computation, with its scratch in a fixed 12 MiB array of the library on each
+ * device instead of a workspace argument; it calls no allocating routine.  Sizes whose
+ * ls_lora_linear_workspace_bytes exceeds 12582912 are refused with LS_ERR_INVALID.  The
+ * first call on a device does a synchronous set-up (make it before any capture).  Every
+ * call on one device shares that array and leaves its contents behind: calls that may
+ * overlap on one device (other streams, other host threads) race and must be serialised
+ * by the caller.  Errors as ls_lora_linear.
+ */
+ls_status ls_lora_linear_noalloc(const ls_weight* w, const void* X, int32_t M, const float* A, const float* B,
+                                 int32_t r, float alpha, void* Y, void* stream);
+
 /* ls_lora_linear_error — message of the calling thread's last failing ls_lora_linear*
  * call. */
 const char* ls_lora_linear_error(void);

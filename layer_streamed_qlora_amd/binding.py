@@ -98,6 +98,8 @@ SIGNATURES = {
     "ls_lora_linear_workspace_bytes": (C.c_uint64, [C.c_int32, C.c_int32, C.c_int32, C.c_int32]),
     "ls_lora_linear": (C.c_int, [C.POINTER(ls_weight), C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p, C.c_int32,
                                  C.c_float, C.c_void_p, C.c_void_p, C.c_uint64, C.c_void_p]),
+    "ls_lora_linear_noalloc": (C.c_int, [C.POINTER(ls_weight), C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p,
+                                         C.c_int32, C.c_float, C.c_void_p, C.c_void_p]),
     "ls_lora_linear_error": (C.c_char_p, []),
     "ls_adamw_step": (C.c_int, [C.c_void_p, C.POINTER(ls_adamw)]),
     "ls_adamw_reset": (C.c_int, [C.c_void_p]),
@@ -186,6 +188,12 @@ def ls_lora_linear(w: ls_weight, X_ptr, M, A_ptr, B_ptr, r, alpha, Y_ptr, ws_ptr
     """Y = X deq(W)^T + (alpha / r) (X A^T) B^T; device pointers as integers."""
     _linear_check(lib().ls_lora_linear(C.byref(w), X_ptr, M, A_ptr or None, B_ptr or None, r, alpha, Y_ptr,
                                        ws_ptr or None, ws_bytes, stream or None))
+
+
+def ls_lora_linear_noalloc(w: ls_weight, X_ptr, M, A_ptr, B_ptr, r, alpha, Y_ptr, stream=0):
+    """ls_lora_linear with the library's fixed device scratch (no workspace)."""
+    _linear_check(lib().ls_lora_linear_noalloc(C.byref(w), X_ptr, M, A_ptr or None, B_ptr or None, r, alpha, Y_ptr,
+                                               stream or None))
 
 
 def ls_check_adapter_file(cfg: ls_config, path: str):

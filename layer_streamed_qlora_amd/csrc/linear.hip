@@ -5,9 +5,11 @@
 // "Fine-Tuning an 8B Parameter Model on a 4 GB Laptop GPU", section "LoRA and QLoRA:
 // Train a Fraction of the Parameters".
 //
-// ls_lora_linear takes its scratch as a caller workspace: s X A^T as bf16 [M, r16], A
-// in bf16 [r16, n_in] (rows r .. r16 zero), B in bf16 [n_out, r16] (columns r .. r16
-// zero), each region 256-byte aligned with 256 bytes of slack.
+// ls_lora_linear takes its scratch as a caller workspace; ls_lora_linear_noalloc uses a
+// fixed device array of this file instead, for callers that cannot allocate.  Scratch
+// layout (both): s X A^T as bf16 [M, r16], A in bf16 [r16, n_in] (rows r .. r16 zero), B
+// in bf16 [n_out, r16] (columns r .. r16 zero), each region 256-byte aligned with 256
+// bytes of slack.
 #include <hip/hip_runtime.h>
 
 #include <mutex>
@@ -19,13 +21,19 @@ using namespace lsq;
 namespace {
 
 constexpr int kMaxDevices = 64;
+constexpr uint64_t kScratchBytes = 12ull << 20;   // the fixed scratch of the no-alloc variant
 
 // The 16 NF4 levels on each device, written once at set-up.
 static __device__ float nf4_levels[16];
+// The scratch of ls_lora_linear_noalloc, one copy per device for the life of the
+// process.  In host code this name is only a stand-in, not a device address: the
+// address used everywhere is the one hipGetSymbolAddress returns for each device.
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
 
 struct DeviceState {
   bool ready = false;
   float* levels = nullptr;
+  uint8_t* scratch = nullptr;
 };
 std::mutex g_mu;
 DeviceState g_dev[kMaxDevices];
@@ -47,14 +55,19 @@ WsLayout ws_layout(int64_t M, int64_t n_in, int64_t n_out, int r16) {
   return L;
 }
 
-// Per-device set-up, once, with the device current: the level table.  Synchronous.
+// Per-device set-up, once, with the device current: the level table and the scratch
+// address.  Synchronous (a caller that captures graphs makes one call first).
 hipError_t device_setup(int dev, DeviceState** out) {
   if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
   std::lock_guard<std::mutex> lock(g_mu);
   DeviceState& d = g_dev[dev];
   if (!d.ready) {
+    void* p = nullptr;
+    hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    d.scratch = static_cast<uint8_t*>(p);
     void* q = nullptr;
-    hipError_t e = hipGetSymbolAddress(&q, HIP_SYMBOL(nf4_levels));
+    e = hipGetSymbolAddress(&q, HIP_SYMBOL(nf4_levels));
     if (e != hipSuccess) return e;
     float lv[16];
     nf4_codebook_host(lv);
@@ -171,6 +184,20 @@ ls_status ls_lora_linear(const ls_weight* w, const void* X, int32_t M, const flo
   DeviceState* d = nullptr;
   if (hipError_t e = device_setup(dev, &d); e != hipSuccess) { t_err = hipGetErrorString(e); return LS_ERR_HIP; }
   return run(w, X, M, A, B, r, alpha, Y, static_cast<uint8_t*>(workspace), L, d->levels, (hipStream_t)stream);
+}
+
+ls_status ls_lora_linear_noalloc(const ls_weight* w, const void* X, int32_t M, const float* A, const float* B,
+                                 int32_t r, float alpha, void* Y, void* stream) {
+  if (ls_status st = check_args(w, X, M, A, B, r, Y)) return st;
+  const WsLayout L = ws_layout(M, w->n_in, w->n_out, (r + 15) / 16 * 16);
+  if (L.total > kScratchBytes)
+    return bad("sizes exceed the fixed scratch of ls_lora_linear_noalloc (12 MiB: "
+               "ls_lora_linear_workspace_bytes must not exceed 12582912)");
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) { t_err = "hipGetDevice failed"; return LS_ERR_HIP; }
+  DeviceState* d = nullptr;
+  if (hipError_t e = device_setup(dev, &d); e != hipSuccess) { t_err = hipGetErrorString(e); return LS_ERR_HIP; }
+  return run(w, X, M, A, B, r, alpha, Y, d->scratch, L, d->levels, (hipStream_t)stream);
 }
 
 const char* ls_lora_linear_error(void) { return t_err.c_str(); }
