@@ -4,7 +4,18 @@ r 16 / alpha 32 on all seven projections) on the GPU.
 * Full depth against the oracle at batch 1 x seq 128: Y, dX and every one of the 224
   (layer, projection) dA / dB, against values the oracle wrote
   (tests/golden/make_llama8b_depth32.py): rows of Y and dX, and seeded samples of
-  every gradient tensor, plus each tensor's full norm.
+  every gradient tensor, plus each tensor's full norm.  Over 32 layers of bf16
+  rounding points the result is not determined to much better than a few per cent: a
+  rounding decision that flips in one layer moves everything after it, and the flips
+  compound.  The same oracle with every product accumulated in float32 instead of
+  float64 (stored by the same script under the suffix ``_f32``) lands 2.9e-2 (Y),
+  5.2e-2 (dX) and up to 8.4e-2 (gradients) from the float64 results.  The GPU must sit
+  no farther from the float64 oracle than that float32 floor, class by class (Y, dX,
+  the median and the worst of the 448 gradient samples), with 20 per cent of margin for
+  the median and 30 for single tensors; every full norm within 1e-2 (Y) and 2e-2.  A
+  mistake in one layer (a dropped term, a wrong scale) shows at order one, far above
+  this floor; mistakes below it are what the teacher-forced layers and the shape
+  tests find.
 * Teacher-forced layers 0, 1 and 31: the oracle runs one layer from the GPU's own
   input of that layer and the GPU's own gradient arriving at its output (taken from
   runs of the sub-stacks that follow it), and must match that layer's Y, dX, dA, dB.
@@ -85,12 +96,29 @@ def test_full_depth_against_stored_oracle(bits32):
                 key = f"{which}_{l}_{p}"
                 errs[f"{which}[{l}].{p}"] = H.rel_l2(flat[idx], ref[key])
                 norms[f"{which}[{l}].{p}"] = abs(np.linalg.norm(flat.astype(np.float64)) / float(ref[key + "_norm"]) - 1)
-    worst_g = max((k for k in errs if k[0] == "d" and k != "dX"), key=errs.get)
-    say({"Y": f"{errs['Y']:.2e}", "dX": f"{errs['dX']:.2e}", "worst grad": f"{worst_g} {errs[worst_g]:.2e}",
+    floor = {"Y": H.rel_l2(ref["Y_rows_f32"], ref["Y_rows"]), "dX": H.rel_l2(ref["dX_rows_f32"], ref["dX_rows"])}
+    for l in range(L):
+        for p in H.PROJS:
+            for which in ("dA", "dB"):
+                key = f"{which}_{l}_{p}"
+                floor[f"{which}[{l}].{p}"] = H.rel_l2(ref[key + "_f32"], ref[key])
+    grads = [k for k in errs if k not in ("Y", "dX")]
+    worst_g = max(grads, key=errs.get)
+    g_gpu = np.array([errs[k] for k in grads])
+    g_f32 = np.array([floor[k] for k in grads])
+    say({"Y": f"{errs['Y']:.2e} (float32 floor {floor['Y']:.2e})",
+         "dX": f"{errs['dX']:.2e} (float32 floor {floor['dX']:.2e})",
+         "grad median": f"{np.median(g_gpu):.2e} (float32 floor {np.median(g_f32):.2e})",
+         "worst grad": f"{worst_g} {errs[worst_g]:.2e} (float32 floor worst {g_f32.max():.2e})",
          "worst norm ratio": f"{max(norms.values()):.2e}"})
     per_layer = [max(errs[f"{wh}[{l}].{p}"] for wh in ("dA", "dB") for p in H.PROJS) for l in range(L)]
     say("worst dA/dB per layer:", " ".join(f"{v:.1e}" for v in per_layer))
-    fails = [(k, v) for k, v in errs.items() if v > (1e-2 if k == "Y" else 2e-2) or not np.isfinite(v)]
+    fails = [(k, v) for k, v in errs.items() if not np.isfinite(v)]
+    fails += [(k, errs[k], floor[k]) for k in ("Y", "dX") if errs[k] > 1.2 * floor[k]]
+    if np.median(g_gpu) > 1.2 * np.median(g_f32):
+        fails.append(("grad median", float(np.median(g_gpu)), float(np.median(g_f32))))
+    if g_gpu.max() > 1.3 * g_f32.max():
+        fails.append(("worst grad " + worst_g, float(g_gpu.max()), float(g_f32.max())))
     fails += [("norm " + k, v) for k, v in norms.items() if v > (1e-2 if k == "Y" else 2e-2)]
     assert not fails, fails
 
@@ -138,7 +166,8 @@ def assert_same_bits(a, b, n_layers, what):
 
 def two_steps(w, layers, bits, resident, **kw):
     """Two forward + backward steps on one context; the second swaps the roles of X and
-    dY, so anything left over from the first step would show."""
+    dY, so anything left over from the first step would show.  kw go to the context
+    (copy_split: every layer copied as four separately fenced pieces)."""
     x, dy = synth.activations(w)
     run = H.GpuRun(w, list(layers), layer_bits=[bits[l] for l in layers], resident=resident, **kw)
     outs, copies = [], []
@@ -154,25 +183,28 @@ def two_steps(w, layers, bits, resident, **kw):
 def test_streamed_equals_resident_32_layers_two_steps(bits32):
     w = W8
     say("case: llama8b 32 layers, 8 x 512, streamed (2 slots) vs resident, two steps")
-    s_out, s_copies, _ = two_steps(w, range(L), bits32, 0)
     r_out, _, _ = two_steps(w, range(L), bits32, 1)
-    say("copies per step (streamed):", s_copies)
-    assert s_copies == [2 * L - 2, 2 * L - 4]
-    for i in range(2):
-        assert_same_bits(s_out[i], r_out[i], L, f"step {i}")
+    for split in (0, 1):
+        say("streamed, split copies" if split else "streamed, whole-layer copies")
+        s_out, s_copies, _ = two_steps(w, range(L), bits32, 0, copy_split=split)
+        say("copies per step (streamed):", s_copies)
+        assert s_copies == [2 * L - 2, 2 * L - 4]
+        for i in range(2):
+            assert_same_bits(s_out[i], r_out[i], L, f"split {split} step {i}")
 
 
-@pytest.mark.parametrize("env", [{"LS_DEBUG_POISON": "1"}, {"LS_DEBUG_COPY_DELAY_US": "4000"},
-                                 {"LS_DEBUG_POISON": "1", "LS_DEBUG_COPY_DELAY_US": "2000"}],
-                         ids=["poison", "delay", "poison+delay"])
-def test_race_hooks_leave_streamed_bitwise_equal(bits32, env, monkeypatch):
+@pytest.mark.parametrize("env,split", [({"LS_DEBUG_POISON": "1"}, 0), ({"LS_DEBUG_COPY_DELAY_US": "4000"}, 0),
+                                       ({"LS_DEBUG_POISON": "1", "LS_DEBUG_COPY_DELAY_US": "2000"}, 0),
+                                       ({"LS_DEBUG_POISON": "1", "LS_DEBUG_COPY_DELAY_US": "2000"}, 1)],
+                         ids=["poison", "delay", "poison+delay", "poison+delay, split copies"])
+def test_race_hooks_leave_streamed_bitwise_equal(bits32, env, split, monkeypatch):
     w = W8
     n = 6
     r_out, _, _ = two_steps(w, range(n), bits32, 1)
     for k, v in env.items():
         monkeypatch.setenv(k, v)
-    say("case: llama8b 6 layers, 8 x 512, two steps, streamed with", env)
-    s_out, s_copies, st = two_steps(w, range(n), bits32, 0)
+    say("case: llama8b 6 layers, 8 x 512, two steps, streamed with", env, "split copies" if split else "")
+    s_out, s_copies, st = two_steps(w, range(n), bits32, 0, copy_split=split)
     if "LS_DEBUG_POISON" in env:
         assert st.poison_fills == sum(s_copies) > 0
     else:
