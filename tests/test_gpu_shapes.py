@@ -118,9 +118,9 @@ def test_llama8b_measured_configuration_sampled_sequence():
 
 def test_qwen72b_dpo_configuration_sampled_sequence():
     """Qwen2.5-72B DPO shape at its configuration: 2 chosen / rejected pairs x 512 tokens
-    with the adapters-off reference pass; one layer, sequence 2 (the second pair's
+    with the adapters-off reference pass; layers 0 and 1, sequence 2 (the second pair's
     chosen sequence) checked against the oracle."""
-    sampled_sequence_case("qwen72b", 1, 2, with_ref=True)
+    sampled_sequence_case("qwen72b", 2, 2, with_ref=True)
 
 
 def test_qwen32b_streamed_equals_resident_bitwise():
