@@ -195,6 +195,8 @@ def main():
     ap.add_argument("--no-profile", action="store_true")
     ap.add_argument("--vocab", type=int, default=128256, help="output-head rows for the head+loss measurement (0 = none)")
     ap.add_argument("--store-file", default="", help="keep the frozen base in this file instead of pinned RAM")
+    ap.add_argument("--copy-split", type=int, default=0, choices=(0, 1),
+                    help="1 = copy each layer as four separately fenced pieces (q|k|v, o, gate|up, down)")
     ap.add_argument("--resident", action="store_true",
                     help="keep every layer on the device (no streaming): the reference point of the streamed run")
     args = ap.parse_args()
@@ -223,7 +225,7 @@ def main():
     cfg = B.make_config(w, n_buffers=args.buffers, profile=B.LS_PROFILE_GEMM if profile else 0, adamw=1,
                         resident=1 if args.resident else 0,
                         vocab=args.vocab,
-                        store_path=args.store_file or None)
+                        store_path=args.store_file or None, copy_split=args.copy_split)
     t0 = time.time()
     ctx = B.Context(cfg)
     t_stage, staged_bytes = 0.0, 0
@@ -339,7 +341,9 @@ def main():
                                   + (" (depth chosen by the library)" if args.buffers == 0 else ""))
                                + (", adapters-off reference pass per layer (DPO)" if w.dpo else ""),
                    "batch": w.batch, "seq": w.seq, "tokens_per_step": T, "parallelism": "none (1 GPU)",
-                   "store": "file (page cache dropped after each read)" if args.store_file else "pinned host RAM"},
+                   "store": "file (page cache dropped after each read)" if args.store_file else "pinned host RAM",
+                   "copies": ("each layer as four separately fenced pieces (q|k|v, o, gate|up, down)"
+                              if args.copy_split else "one per layer")},
         # the library's one device allocation (its plan), the caller's tensors (inputs,
         # outputs, adapters and their gradients, allocated through torch), the pinned store
         "memory": {"library_device_bytes": s1.device_bytes, "caller_device_bytes_peak": torch.cuda.max_memory_allocated(),

@@ -91,6 +91,20 @@ typedef struct ls_config {
                               head slice), read into one pinned staging buffer per slot */
   char store_path[256];    /* LS_STORE_FILE: NUL-terminated path; the file is created (or
                               truncated) by ls_create and removed by ls_destroy */
+  int32_t copy_split;      /* 0 = each decoder layer crosses the link as one copy followed
+                              by one ready event; 1 = as four pieces in the order the layer
+                              first reads them (g1, g2 and q|k|v; o; gate|up; down), each
+                              followed by its own ready event, and the compute stream waits
+                              for a piece just before its first reader, so a layer starts
+                              while its later pieces are still in flight.  Either way a slot
+                              is refilled only after the last reader of the whole layer
+                              (one consumed event per slot).  Streamed mode only (ignored
+                              when resident); results are bitwise the same either way.  The
+                              pool's buffer count is a setting in the lachieslifestyle.com
+                              Soup how-to ("Step 5: Enable 4-bit layer streaming"), which
+                              also lists small stream buffers among the causes of slow
+                              training ("Common problems"); the split makes the unit the
+                              compute waits for one projection group instead of a layer. */
 } ls_config;
 
 /* Where the frozen base lives ("Soup CLI fine-tunes Llama-3.1-8B on a 4 GB laptop GPU

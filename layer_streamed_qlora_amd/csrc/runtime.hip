@@ -431,44 +431,83 @@ uint8_t* slot_ptr(ls_ctx* c, int layer) {
   return c->dbase + c->plan.slots + (uint64_t)s * c->lay.bytes;
 }
 
+// Pieces of a blob.  With copy_split a decoder layer crosses the link as kPieces pieces
+// in the order its forward and its recompute first read them: g1, g2 and q|k|v; o;
+// gate|up; down (contiguous in the blob layout), each followed by its own ready event,
+// so the compute stream can start on a layer whose later pieces are still in flight.
+// The slot is released as a whole (one consumed event per slot): the next copy into it
+// waits for the last reader of every piece.  Head slices, and every blob without
+// copy_split, are one piece.
+constexpr int kPieces = 4;
+
+int n_pieces(const ls_ctx* c, int l) {
+  return c->cfg.copy_split && !c->cfg.resident && l < c->cfg.n_layers ? kPieces : 1;
+}
+
+void piece_range(const ls_ctx* c, int l, int g, uint64_t* off, uint64_t* len) {
+  if (n_pieces(c, l) == 1) {
+    *off = 0;
+    *len = c->lay.bytes;
+    return;
+  }
+  const uint64_t b[kPieces + 1] = {0, c->lay.p[LS_PROJ_O].off_w, c->lay.p[LS_PROJ_GATE].off_w,
+                                   c->lay.p[LS_PROJ_DOWN].off_w, c->lay.bytes};
+  *off = b[g];
+  *len = b[g + 1] - b[g];
+}
+
 // Enqueue on the copy stream: bring layer l into its slot unless the slot still holds it.
 ls_status ensure_copy(ls_ctx* c, int l) {
   if (c->cfg.resident) return LS_OK;
   const int s = l % c->cfg.n_buffers;
   if (c->slot_layer[s] == l) { c->stats.slot_hits++; return LS_OK; }
   if (c->cons_rec[s]) HIPCHK(c, hipStreamWaitEvent(c->ps, c->consumed[s], 0));
+  uint8_t* dst = slot_ptr(c, l);
   if (c->dbg_poison) {
-    HIPCHK(c, launch_fill_u32(reinterpret_cast<uint32_t*>(slot_ptr(c, l)), (int64_t)(c->lay.bytes / 4), 0xFFFFFFFFu, c->ps));
+    HIPCHK(c, launch_fill_u32(reinterpret_cast<uint32_t*>(dst), (int64_t)(c->lay.bytes / 4), 0xFFFFFFFFu, c->ps));
     c->stats.poison_fills += 1;
   }
   if (c->dbg_delay_us) HIPCHK(c, hipLaunchHostFunc(c->ps, copy_delay, &c->dbg_delay_us));
-  {
-    Span sp(c, c->ps, true);
-    if (c->fd >= 0) {
-      // read the blob from the store file into this slot's staging buffer (a host
-      // function in stream order: it runs after the previous copy out of the buffer),
-      // then copy it to the slot
-      HIPCHK(c, hipLaunchHostFunc(c->ps, store_read, &c->jobs[l]));
-      HIPCHK(c, hipMemcpyAsync(slot_ptr(c, l), c->jobs[l].buf, c->lay.bytes, hipMemcpyHostToDevice, c->ps));
-    } else {
-      HIPCHK(c, hipMemcpyAsync(slot_ptr(c, l), c->host[l], c->lay.bytes, hipMemcpyHostToDevice, c->ps));
+  // with the file store, the blob is first read into this slot's staging buffer (a host
+  // function in stream order: it runs after the previous copy out of the buffer)
+  if (c->fd >= 0) HIPCHK(c, hipLaunchHostFunc(c->ps, store_read, &c->jobs[l]));
+  const uint8_t* src = c->fd >= 0 ? c->jobs[l].buf : c->host[l];
+  const int np = n_pieces(c, l);
+  for (int g = 0; g < np; ++g) {
+    uint64_t off, len;
+    piece_range(c, l, g, &off, &len);
+    {
+      Span sp(c, c->ps, true);
+      HIPCHK(c, hipMemcpyAsync(dst + off, src + off, len, hipMemcpyHostToDevice, c->ps));
+    }
+    // a one-piece blob records every piece's event: a reader that waits per piece (the
+    // next occupant of the slot may be split) then waits for the whole copy
+    for (int k = np == 1 ? 0 : g; k < (np == 1 ? kPieces : g + 1); ++k) {
+      HIPCHK(c, hipEventRecord(c->ready[s * kPieces + k], c->ps));
+      c->ready_rec[s * kPieces + k] = 1;
     }
   }
-  HIPCHK(c, hipEventRecord(c->ready[s], c->ps));
-  c->ready_rec[s] = 1;
   c->slot_layer[s] = l;
   c->stats.h2d_bytes += c->lay.bytes;
   c->stats.h2d_copies += 1;
   return LS_OK;
 }
 
-ls_status use_layer(ls_ctx* c, int l) {
+// The compute stream waits for piece g of layer l (use_layer: every piece).
+ls_status use_piece(ls_ctx* c, int l, int g) {
   if (c->cfg.resident) return LS_OK;
-  const int s = l % c->cfg.n_buffers;
-  if (c->ready_rec[s]) HIPCHK(c, hipStreamWaitEvent(c->cs, c->ready[s], 0));
+  const int e = (l % c->cfg.n_buffers) * kPieces + g;
+  if (c->ready_rec[e]) HIPCHK(c, hipStreamWaitEvent(c->cs, c->ready[e], 0));
   return LS_OK;
 }
 
+ls_status use_layer(ls_ctx* c, int l) {
+  for (int g = 0; g < kPieces; ++g)
+    if (ls_status st = use_piece(c, l, g)) return st;
+  return LS_OK;
+}
+
+// Every reader of layer l's slot has been enqueued on the compute stream.
 ls_status release_layer(ls_ctx* c, int l) {
   if (c->cfg.resident) return LS_OK;
   const int s = l % c->cfg.n_buffers;
@@ -476,6 +515,14 @@ ls_status release_layer(ls_ctx* c, int l) {
   c->cons_rec[s] = 1;
   return LS_OK;
 }
+
+// Per-piece waits of one pass over a split layer: the compute stream waits for a piece
+// just before its first reader.  Disabled when the caller waited for the whole layer.
+struct Fence {
+  int l = 0;
+  bool wait = false;
+};
+ls_status fence_wait(ls_ctx* c, const Fence& f, int g) { return f.wait ? use_piece(c, f.l, g) : LS_OK; }
 
 // ------------------------------------------------------------------ executor
 // s X A^T of layer l, bf16 [T, 7 r16] (row stride 7 r16), layers max_tokens rows apart
@@ -634,7 +681,7 @@ enum FwdMode { MODE_FWD = 0, MODE_RECOMPUTE = 1 };
 // recompute keeps every intermediate and skips the down projection, whose output
 // the backward does not need.
 ls_status layer_forward(ls_ctx* c, int l, const uint8_t* blob, const Dims& d, const uint16_t* x_in, uint16_t* x_out,
-                        bool lora, FwdMode mode) {
+                        bool lora, FwdMode mode, const Fence& fc) {
   const ls_config& g = c->cfg;
   const int fmt = wformat(g);
   const float* lv = c->dp<float>(c->plan.levels);
@@ -651,7 +698,9 @@ ls_status layer_forward(ls_ctx* c, int l, const uint8_t* blob, const Dims& d, co
   const uint16_t* g1 = reinterpret_cast<const uint16_t*>(blob + c->lay.off_g1);
   const uint16_t* g2 = reinterpret_cast<const uint16_t*>(blob + c->lay.off_g2);
   const double tb = 2.0 * d.T;
+  ls_status fst;
 
+  if ((fst = fence_wait(c, fc, 0))) return fst;
   {
     KTimer kt(c, LS_KC_GLUE, 0.0, 2 * tb * d.h);
     HIPCHK(c, launch_rmsnorm_fwd(x_in, nullptr, g1, n1, c->dp<float>(c->plan.rstd1), d.T, d.h, g.rms_eps, c->cs));
@@ -682,6 +731,7 @@ ls_status layer_forward(ls_ctx* c, int l, const uint8_t* blob, const Dims& d, co
     if (st) return st;
   }
   if (down) { ls_status st = lora_down(c, l, d, att, d.qd, LS_PROJ_O, 1, d.qd); if (st) return st; }
+  if ((fst = fence_wait(c, fc, 1))) return fst;
   {
     FwdArgs f;
     f.x = att; f.ldx = d.qd; f.M = d.T; f.K = d.qd; f.n_groups = 1;
@@ -698,6 +748,7 @@ ls_status layer_forward(ls_ctx* c, int l, const uint8_t* blob, const Dims& d, co
     KTimer kt(c, LS_KC_GLUE, 0.0, 2 * tb * d.h);
     HIPCHK(c, launch_rmsnorm_fwd(nullptr, hb, g2, n2, c->dp<float>(c->plan.rstd2), d.T, d.h, g.rms_eps, c->cs));
   }
+  if ((fst = fence_wait(c, fc, 2))) return fst;
   if (down) { ls_status st = lora_down(c, l, d, n2, d.h, LS_PROJ_GATE, 2, d.h); if (st) return st; }
   const bool fuse_swiglu = 2 * d.r16 <= 64;
   {
@@ -730,6 +781,7 @@ ls_status layer_forward(ls_ctx* c, int l, const uint8_t* blob, const Dims& d, co
   }
   if (down) { ls_status st = lora_down(c, l, d, act, d.I, LS_PROJ_DOWN, 1, d.I); if (st) return st; }
   if (mode == MODE_RECOMPUTE) return LS_OK;
+  if ((fst = fence_wait(c, fc, 3))) return fst;
   {
     FwdArgs f;
     f.x = act; f.ldx = d.I; f.M = d.T; f.K = d.I; f.n_groups = 1;
@@ -829,11 +881,11 @@ ls_status join_side(ls_ctx* c) {
 }
 
 ls_status layer_backward(ls_ctx* c, int l, const uint8_t* blob, const Dims& d, const uint16_t* x_in, const uint16_t* dy,
-                         uint16_t* dx, float beta) {
+                         uint16_t* dx, float beta, const Fence& fc) {
   // the previous layer's reductions read activations this recompute overwrites
   ls_status st = join_side(c);
   if (st) return st;
-  st = layer_forward(c, l, blob, d, x_in, nullptr, true, MODE_RECOMPUTE);
+  st = layer_forward(c, l, blob, d, x_in, nullptr, true, MODE_RECOMPUTE, fc);   // waits for pieces 0 .. 2
   if (st) return st;
   const ls_config& g = c->cfg;
   const int fmt = wformat(g);
@@ -861,6 +913,7 @@ ls_status layer_backward(ls_ctx* c, int l, const uint8_t* blob, const Dims& d, c
   // ---- down: y = h + act W_d^T + LoRA
   if ((st = lora_grads_G(c, l, d, LS_PROJ_DOWN, 1, dy, d.h))) return st;
   if ((st = lora_grads_AB(c, l, d, LS_PROJ_DOWN, 1, dy, d.h, act, d.I, beta))) return st;
+  if ((st = fence_wait(c, fc, 3))) return st;
   {
     BwdArgs b;
     b.dy = dy; b.lddy = d.h; b.M = d.T; b.N = d.I; b.n_segs = 1;
@@ -1047,17 +1100,15 @@ ls_status ls_create(const ls_config* cfg_in, void* compute_stream, void* copy_st
 
   const int nb = P.n_slots;
   c->slot_layer.assign(nb, -1);
-  c->ready.resize(nb);
+  // ready events: one per piece of each slot; consumed events: one per slot
+  c->ready.resize(nb * kPieces);
   c->consumed.resize(nb);
-  c->ready_rec.assign(nb, 0);
+  c->ready_rec.assign(nb * kPieces, 0);
   c->cons_rec.assign(nb, 0);
-  for (int i = 0; i < nb; ++i) {
-    if (hipEventCreateWithFlags(&c->ready[i], hipEventDisableTiming) != hipSuccess ||
-        hipEventCreateWithFlags(&c->consumed[i], hipEventDisableTiming) != hipSuccess) {
-      c->err = "event creation failed";
-      return bail(LS_ERR_HIP);
-    }
-  }
+  for (auto& e : c->ready)
+    if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess) { e = nullptr; c->err = "event creation failed"; return bail(LS_ERR_HIP); }
+  for (auto& e : c->consumed)
+    if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess) { e = nullptr; c->err = "event creation failed"; return bail(LS_ERR_HIP); }
   c->lora.resize(cfg->n_layers);
   c->staged.assign(cfg->n_layers, 0);
   const int n_blobs = cfg->n_layers + P.head_slices;
@@ -1214,18 +1265,23 @@ ls_status ls_forward(ls_ctx* c, const void* X, int32_t batch, int32_t seq, int32
   for (int l = 0; l < L; ++l) {
     for (int k = 1; k < c->cfg.n_buffers && l + k < L; ++k)
       if ((st = ensure_copy(c, l + k))) return st;
-    if ((st = use_layer(c, l))) return st;
+    // a split layer's pieces are waited for inside the (policy) pass, each before its
+    // first reader
+    const bool split = n_pieces(c, l) > 1;
+    if (!split && (st = use_layer(c, l))) return st;
     {
       Span sp(c, c->cs, false);
       const uint8_t* blob = slot_ptr(c, l);
       if (lora && (st = prep_lora(c, l, d))) return st;
       uint16_t* out = l + 1 < L ? ckpt(c, l + 1) : (uint16_t*)Y;
-      if ((st = layer_forward(c, l, blob, d, ckpt(c, l), out, lora, MODE_FWD))) return st;
+      const Fence f1{l, split};
+      if ((st = layer_forward(c, l, blob, d, ckpt(c, l), out, lora, MODE_FWD, f1))) return st;
       if (Y_ref) {
         // layer 0 reads the checkpoint copy of X, so Y may alias X
         const uint16_t* rin = l == 0 ? ckpt(c, 0) : xr[(l - 1) & 1];
         uint16_t* rout = l + 1 < L ? xr[l & 1] : (uint16_t*)Y_ref;
-        if ((st = layer_forward(c, l, blob, d, rin, rout, false, MODE_FWD))) return st;
+        const Fence f2{l, false};
+        if ((st = layer_forward(c, l, blob, d, rin, rout, false, MODE_FWD, f2))) return st;
       }
     }
     if ((st = release_layer(c, l))) return st;
@@ -1262,11 +1318,13 @@ ls_status ls_backward(ls_ctx* c, const void* dY, void* dX, int32_t accumulate) {
   for (int l = L - 1; l >= 0; --l) {
     for (int k = 1; k < c->cfg.n_buffers && l - k >= 0; ++k)
       if ((st = ensure_copy(c, l - k))) return st;
-    if ((st = use_layer(c, l))) return st;
+    const bool split = n_pieces(c, l) > 1;
+    if (!split && (st = use_layer(c, l))) return st;
     uint16_t* out = l == 0 ? (uint16_t*)dX : ping[l & 1];
     {
       Span sp(c, c->cs, false);
-      if ((st = layer_backward(c, l, slot_ptr(c, l), d, ckpt(c, l), cur, out, beta))) return st;
+      const Fence f{l, split};
+      if ((st = layer_backward(c, l, slot_ptr(c, l), d, ckpt(c, l), cur, out, beta, f))) return st;
     }
     if ((st = release_layer(c, l))) return st;
     cur = out;

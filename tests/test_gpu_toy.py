@@ -71,21 +71,22 @@ def test_toy_streamed_equals_resident_bitwise():
             assert np.array_equal(a["dB"][l][p].view(np.uint32), b["dB"][l][p].view(np.uint32)), (l, p)
 
 
-@pytest.mark.parametrize("n_buffers", [3, 5, 0])
-def test_deeper_pool_equals_resident_and_reuses_slots(n_buffers):
-    """A pool deeper than two slots on a 6-layer stack: two consecutive steps are bit for
-    bit the resident run, and in the second step every slot still holding the layer the
-    other direction needs first is reused, so it copies 2 (L - n_buffers) blobs.  With
-    n_buffers = 0 the library picks the depth: one slot per layer here, so the second
-    step copies nothing."""
+@pytest.mark.parametrize("n_buffers,split", [(3, 0), (5, 0), (0, 0), (2, 1), (3, 1)])
+def test_deeper_pool_equals_resident_and_reuses_slots(n_buffers, split):
+    """A pool of two or more slots on a 6-layer stack, with the DPO reference pass: two
+    consecutive steps are bit for bit the resident run, and in the second step every
+    slot still holding the layer the other direction needs first is reused, so it copies
+    2 (L - n_buffers) blobs.  With n_buffers = 0 the library picks the depth: one slot
+    per layer here, so the second step copies nothing.  split = 1 copies every layer as
+    four pieces, each fenced on its own (copy_split)."""
     w = TOY
     L = 6
     x, dy = synth.activations(w)
-    say("case: toy pool depth", n_buffers)
+    say("case: toy pool depth", n_buffers, "split copies" if split else "")
     res = H.GpuRun(w, range(L), resident=1)
     want = res.step(x, dy, w.batch, w.seq, with_ref=True)
     res.close()
-    run = H.GpuRun(w, range(L), n_buffers=n_buffers)
+    run = H.GpuRun(w, range(L), n_buffers=n_buffers, copy_split=split)
     if n_buffers == 0:
         n_buffers = run.ctx.stats().n_slots
         assert n_buffers == L, n_buffers
@@ -208,18 +209,20 @@ def test_lora_ranks(rank):
     assert not fails, fails
 
 
-def test_file_store_equals_host_store_bitwise(tmp_path):
+@pytest.mark.parametrize("split", [0, 1])
+def test_file_store_equals_host_store_bitwise(tmp_path, split):
     """The base kept in a file and read through pinned staging buffers gives the same bits
-    as the pinned-RAM store, over two steps; every copy is one file read, and the file is
-    gone after ls_destroy."""
+    as the pinned-RAM store, over two steps; every copy is one file read (split = 1: one
+    read per layer, copied to the slot in four pieces), and the file is gone after
+    ls_destroy."""
     import os
     w = TOY
     L = 4
     x, dy = synth.activations(w)
     outs = []
     for path in (None, str(tmp_path / "store.bin")):
-        say("case: toy store", "file" if path else "host")
-        run = H.GpuRun(w, range(L), store_path=path)
+        say("case: toy store", "file" if path else "host", "split copies" if split and path else "")
+        run = H.GpuRun(w, range(L), store_path=path, copy_split=split if path else 0)
         outs.append([run.step(x, dy, w.batch, w.seq, with_ref=True) for _ in range(2)])
         st = run.ctx.stats()
         if path is not None:
