@@ -1351,48 +1351,41 @@ __device__ __forceinline__ bf16x8_t expand8(uint32_t x, const Planes& p) {
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 struct SmemR4 {
-  union {
-    uint8_t a[2][BM * 128];          // activation stages (swizzled, see above)
-    float out[128 * (BN + 4)];       // epilogue staging, one half tile at a time
-  } u;
+  uint8_t a[2][BM * 128];            // activation stages (swizzled, see above)
 };
 
-// One wave's 64 weight rows (two column blocks of 32) in the forward orientation: loads
-// one stage's codes and scales into registers, then yields the MFMA operand of (column
-// block, step).  Rows at or past the end of the weight read as zero (range-checked).
+// One 32-row block of one weight in the forward orientation: loads one stage's codes and
+// scales into registers and yields the MFMA operand of each step.  Rows at or past the
+// end of the weight read as zero (range-checked).
 template <int FMT>
-struct WR4 {
+struct WBlk {
   struct Regs {
-    uint4 raw[2][FMT == WF_BF16 ? 4 : 1];   // NF4: 32 codes per block; bf16: 4 operands per block
-    uint32_t blk[2];                        // absmax bits (NF4) or the 8-bit code (DQ)
-    float s2[2];                            // DQ second-level scales
+    uint4 raw[FMT == WF_BF16 ? 4 : 1];   // NF4: 32 codes; bf16: the 4 operands
+    uint32_t blk;                        // absmax bits (NF4) or the 8-bit code (DQ)
+    float s2;                            // DQ second-level scale
   };
   rsrc_t codes, absq, sc2;
   float mean;
-  uint32_t voff_c, voff_a, cstep, astep, kblk, blk_lane;
-  __device__ __forceinline__ void init(const WeightRef& w, int nb, int lane) {
+  uint32_t voff_c, voff_a, blk_lane;
+  __device__ __forceinline__ void init(const WeightRef& w, int row0, int lane) {
     const int K = w.n_in;
-    const int rows = w.n_out - nb < 64 ? (w.n_out - nb > 0 ? w.n_out - nb : 0) : 64;
-    kblk = (uint32_t)K / kNF4Block;
+    const int rows = w.n_out - row0 < 32 ? (w.n_out - row0 > 0 ? w.n_out - row0 : 0) : 32;
+    const uint32_t kblk = (uint32_t)K / kNF4Block;
     const uint32_t r = (uint32_t)(lane & 31), h = (uint32_t)(lane >> 5);
     mean = 0.f;
     if constexpr (FMT == WF_BF16) {
-      codes = make_rsrc_wave(w.w + (uint64_t)nb * K * 2, (uint64_t)rows * K * 2);
+      codes = make_rsrc_wave(w.w + (uint64_t)row0 * K * 2, (uint64_t)rows * K * 2);
       voff_c = r * (uint32_t)K * 2u + 64u * h;
-      cstep = 32u * (uint32_t)K * 2u;
     } else {
-      codes = make_rsrc_wave(w.w + (uint64_t)nb * K / 2, (uint64_t)rows * K / 2);
+      codes = make_rsrc_wave(w.w + (uint64_t)row0 * K / 2, (uint64_t)rows * K / 2);
       voff_c = r * (uint32_t)K / 2u + 16u * h;
-      cstep = 32u * (uint32_t)K / 2u;
-      const uint64_t b0 = (uint64_t)nb * kblk;
+      const uint64_t b0 = (uint64_t)row0 * kblk;
       if constexpr (FMT == WF_NF4) {
         absq = make_rsrc_wave(w.absmax + b0, (uint64_t)rows * kblk * 4);
         voff_a = r * kblk * 4u;
-        astep = 32u * kblk * 4u;
       } else {
         absq = make_rsrc_wave(w.qabs + b0, (uint64_t)rows * kblk);
         voff_a = r * kblk;
-        astep = 32u * kblk;
         const uint64_t all = (uint64_t)w.n_out * kblk;
         sc2 = make_rsrc_wave(w.scale2, (all + kDQGroup - 1) / kDQGroup * 4);
         blk_lane = (uint32_t)(b0 + r * kblk);
@@ -1401,34 +1394,43 @@ struct WR4 {
     }
   }
   __device__ __forceinline__ void load(Regs& R, uint32_t k0) const {
+    if constexpr (FMT == WF_BF16) {
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
-      if constexpr (FMT == WF_BF16) {
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) R.raw[cb][ks] = bload16s(codes, voff_c, k0 * 2u + 16u * ks + cb * cstep);
+      for (int ks = 0; ks < 4; ++ks) R.raw[ks] = bload16s(codes, voff_c, k0 * 2u + 16u * ks);
+    } else {
+      R.raw[0] = bload16s(codes, voff_c, k0 / 2u);
+      const uint32_t kb = k0 / kNF4Block;
+      if constexpr (FMT == WF_NF4) {
+        R.blk = bload4s(absq, voff_a, kb * 4u);
       } else {
-        R.raw[cb][0] = bload16s(codes, voff_c, k0 / 2u + cb * cstep);
-        const uint32_t kb = k0 / kNF4Block;
-        if constexpr (FMT == WF_NF4) {
-          R.blk[cb] = bload4s(absq, voff_a, kb * 4u + cb * astep);
-        } else {
-          R.blk[cb] = bload1s(absq, voff_a, kb + cb * astep);
-          R.s2[cb] = __builtin_bit_cast(float, bload4s(sc2, ((blk_lane + 32u * kblk * cb + kb) / kDQGroup) * 4u, 0));
-        }
+        R.blk = bload1s(absq, voff_a, kb);
+        R.s2 = __builtin_bit_cast(float, bload4s(sc2, ((blk_lane + kb) / kDQGroup) * 4u, 0));
       }
     }
   }
-  __device__ __forceinline__ Planes planes(const Regs& R, int cb) const {
-    if constexpr (FMT == WF_NF4) return make_planes(__builtin_bit_cast(float, R.blk[cb]));
-    else if constexpr (FMT == WF_NF4_DQ) return make_planes(dq_absmax(R.blk[cb], R.s2[cb], mean));
+  __device__ __forceinline__ Planes planes(const Regs& R) const {
+    if constexpr (FMT == WF_NF4) return make_planes(__builtin_bit_cast(float, R.blk));
+    else if constexpr (FMT == WF_NF4_DQ) return make_planes(dq_absmax(R.blk, R.s2, mean));
     else return Planes{};
   }
-  __device__ __forceinline__ bf16x8_t operand(const Regs& R, int cb, int ks, const Planes& p) const {
-    if constexpr (FMT == WF_BF16) return __builtin_bit_cast(bf16x8_t, R.raw[cb][ks]);
-    else return expand8(reinterpret_cast<const uint32_t*>(&R.raw[cb][0])[ks], p);
+  __device__ __forceinline__ bf16x8_t operand(const Regs& R, int ks, const Planes& p) const {
+    if constexpr (FMT == WF_BF16) return __builtin_bit_cast(bf16x8_t, R.raw[ks]);
+    else return expand8(reinterpret_cast<const uint32_t*>(&R.raw[0])[ks], p);
   }
 };
 
+// 4 consecutive float32 values as 2 packed bf16 (RNE)
+__device__ __forceinline__ uint2 pack4(const float (&y)[4]) { return make_uint2(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])); }
+
+// The MFMAs take the weights as the A operand and the activations as B, so each
+// accumulator block is a transposed 32 x 32 tile of Y: a lane holds one token (its lane
+// & 31 within the row block) and, for g = 0..3, the 4 consecutive output columns
+// 8 g + 4 (lane >> 5) .. +4 of its column block.  Column blocks: wave w's block 0 is tile
+// columns 128 (w >> 1) + 32 (w & 1) .. +32 and block 1 those + 64, so each column's
+// rotary partner (hd 128: d and d + 64) is in the same lane; paired gate|up tiles give
+// block 0 the gate rows n0 + 32 w .. +32 and block 1 the same up rows, so silu(g) u is
+// formed in the lane too.  The epilogue stores straight from the accumulators (8- or
+// 16-byte accesses), without staging the tile in LDS.
 template <int FMT, bool PAIRED>
 __global__ void __launch_bounds__(NT_R4, 1) k_gemm_fwd_r4(FwdArgs args, int n_tiles, int total_tiles, int padded) {
   extern __shared__ __align__(1024) unsigned char smem_raw[];
@@ -1449,14 +1451,13 @@ __global__ void __launch_bounds__(NT_R4, 1) k_gemm_fwd_r4(FwdArgs args, int n_ti
   const int m0 = mt * BM;
   const int n0 = PAIRED ? rest * (BN / 2) : rest * BN;
   const int K = args.K;
-  const int n_out = G.w.n_out;
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  // this wave's weight and first row: paired tiles give waves 0, 1 the gate rows and
-  // waves 2, 3 the same up rows
-  const int wg = PAIRED ? w >> 1 : 0;
-  const WeightRef& W = PAIRED ? args.g[wg].w : G.w;
-  const int nb = n0 + (PAIRED ? 64 * (w & 1) : 64 * w);
+  // this wave's two column blocks: weight and first row (within that weight)
+  const WeightRef& W0 = G.w;
+  const WeightRef& W1 = PAIRED ? args.g[1].w : G.w;
+  const int col0 = PAIRED ? 32 * w : 128 * (w >> 1) + 32 * (w & 1);   // tile column of block 0
+  const int row0[2] = {n0 + col0, PAIRED ? n0 + col0 : n0 + col0 + 64};
 
   f32x16_t acc[8][2];
 #pragma unroll
@@ -1482,51 +1483,54 @@ __global__ void __launch_bounds__(NT_R4, 1) k_gemm_fwd_r4(FwdArgs args, int n_ti
   auto load_a = [&](uint32_t k0, int buf, bool zero) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      lds_ptr_t dst = (lds_ptr_t)(&sm.u.a[buf][(8 * (8 * w + i)) * 128]);
+      lds_ptr_t dst = (lds_ptr_t)(&sm.a[buf][(8 * (8 * w + i)) * 128]);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(xres, dst, 16, zero ? kOOB : a_vo[i & 1],
                                                zero ? 0u : k0 * 2u + (uint32_t)(i >> 1) * a_istep, 0, 0);
     }
   };
   auto frag = [&](int buf, int rb, int ks) {
-    return *reinterpret_cast<const bf16x8_t*>(&sm.u.a[buf][rb * 4096 + fbase + ((fch ^ (uint32_t)ks) << 4)]);
+    return *reinterpret_cast<const bf16x8_t*>(&sm.a[buf][rb * 4096 + fbase + ((fch ^ (uint32_t)ks) << 4)]);
+  };
+  auto mfma = [&](const bf16x8_t& wop, const bf16x8_t& xop, f32x16_t& c) {
+    c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wop, xop, c, 0, 0, 0);
   };
 
   // ---- the low-rank extension: one 64-deep stage before the main loop.  A columns
-  // [ext_col0, ext_col0 + kx) of aext (paired: 2 kx, gate's then up's); W operands are
-  // the bf16 copies of B ([n_out, kx], row stride kx), zero past kx (paired: a gate wave
-  // takes columns 0 .. kx, an up wave kx .. 2 kx).
+  // [ext_col0, ext_col0 + kx) of aext (paired: 2 kx, gate's then up's); the weight-side
+  // operands are the bf16 copies of B ([n_out, kx], row stride kx), zero past kx (paired:
+  // the gate block takes columns 0 .. kx, the up block kx .. 2 kx)
   {
     const int kx = args.kx;
-    const uint16_t* bx = PAIRED ? args.g[wg].bext : G.bext;
-    const bool has_ext = kx > 0 && (PAIRED ? (args.g[0].bext || args.g[1].bext) : bx != nullptr);
+    const uint16_t* bx[2] = {G.bext, PAIRED ? args.g[1].bext : G.bext};
+    const bool has_ext = kx > 0 && (bx[0] != nullptr || bx[1] != nullptr);
     if (has_ext) {
       const int ecols = PAIRED ? 2 * kx : kx;
       const rsrc_t eres = make_rsrc_wave(args.aext + (int64_t)m0 * args.ldaext, (uint64_t)arows * args.ldaext * 2);
-      // (loaded into registers and stored, so that the columns past the extension are
-      // written as zeros)
+      // loaded into registers and stored, so that the columns past the extension are zeros
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int row = 64 * w + 8 * i + lrow;
         const int c = (lane & 7) ^ ((row >> 1) & 7);
         const bool ok = 8 * c < ecols;
         const uint4 v = bload16(eres, ok ? ((uint32_t)row * (uint32_t)args.ldaext + (uint32_t)(G.ext_col0 + 8 * c)) * 2u : kOOB);
-        *reinterpret_cast<uint4*>(&sm.u.a[1][row * 128 + 16 * (lane & 7)]) = v;
+        *reinterpret_cast<uint4*>(&sm.a[1][row * 128 + 16 * (lane & 7)]) = v;
       }
-      const int brows = W.n_out - nb < 64 ? (W.n_out - nb > 0 ? W.n_out - nb : 0) : 64;
-      const bool bon = bx != nullptr;
-      const rsrc_t bres = make_rsrc_wave(bon ? bx + (int64_t)nb * kx : args.x, bon ? (uint64_t)brows * kx * 2 : 0);
-      const int c_lo = PAIRED ? wg * kx : 0;     // this wave's columns of the extension
       bf16x8_t eb[2][4];
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb)
+      for (int cb = 0; cb < 2; ++cb) {
+        const WeightRef& Wc = cb ? W1 : W0;
+        const int brows = Wc.n_out - row0[cb] < 32 ? (Wc.n_out - row0[cb] > 0 ? Wc.n_out - row0[cb] : 0) : 32;
+        const bool bon = bx[cb] != nullptr;
+        const rsrc_t bres = make_rsrc_wave(bon ? bx[cb] + (int64_t)row0[cb] * kx : args.x, bon ? (uint64_t)brows * kx * 2 : 0);
+        const int c_lo = PAIRED ? cb * kx : 0;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-          const int k = 32 * (lane >> 5) + 8 * ks;          // extension column of this operand
-          const int src = k - c_lo;
+          const int src = 32 * (lane >> 5) + 8 * ks - c_lo;   // extension column of this operand
           const bool ok = bon && src >= 0 && src < kx;
-          const uint32_t off = ok ? ((uint32_t)(32 * cb + (lane & 31)) * (uint32_t)kx + (uint32_t)src) * 2u : kOOB;
-          eb[cb][ks] = __builtin_bit_cast(bf16x8_t, bload16(bres, off));
+          eb[cb][ks] = __builtin_bit_cast(
+              bf16x8_t, bload16(bres, ok ? ((uint32_t)(lane & 31) * (uint32_t)kx + (uint32_t)src) * 2u : kOOB));
         }
+      }
       __builtin_amdgcn_s_waitcnt(kWaitVm0);
       __syncthreads();
 #pragma unroll
@@ -1534,29 +1538,32 @@ __global__ void __launch_bounds__(NT_R4, 1) k_gemm_fwd_r4(FwdArgs args, int n_ti
 #pragma unroll
         for (int rb = 0; rb < 8; ++rb) {
           const bf16x8_t a = frag(1, rb, ks);
-          acc[rb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, eb[0][ks], acc[rb][0], 0, 0, 0);
-          acc[rb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, eb[1][ks], acc[rb][1], 0, 0, 0);
+          mfma(eb[0][ks], a, acc[rb][0]);
+          mfma(eb[1][ks], a, acc[rb][1]);
         }
       __syncthreads();   // buffer 1 is refilled below
     }
   }
 
   // ---- main loop over the nk (even) stages of K
-  WR4<FMT> wr;
-  wr.init(W, nb, lane);
-  typename WR4<FMT>::Regs R[2];
+  WBlk<FMT> wb[2];
+  wb[0].init(W0, row0[0], lane);
+  wb[1].init(W1, row0[1], lane);
+  typename WBlk<FMT>::Regs R[2][2];   // [stage parity][column block]
   const int nk = K / BK;
   auto kof = [&](int s) { return (uint32_t)(s < nk ? s : nk - 1) * BK; };
   load_a(0, 0, false);
-  wr.load(R[0], 0);
-  wr.load(R[1], kof(1));
+  wb[0].load(R[0][0], 0);
+  wb[1].load(R[0][1], 0);
+  wb[0].load(R[1][0], kof(1));
+  wb[1].load(R[1][1], kof(1));
   load_a(kof(1), 1, false);
   __builtin_amdgcn_s_waitcnt(kWaitVm0);
   __syncthreads();
   Planes pl[2];
-  pl[0] = wr.planes(R[0], 0);
-  pl[1] = wr.planes(R[0], 1);
-  bf16x8_t b0 = wr.operand(R[0], 0, 0, pl[0]), b1;
+  pl[0] = wb[0].planes(R[0][0]);
+  pl[1] = wb[1].planes(R[0][1]);
+  bf16x8_t b0 = wb[0].operand(R[0][0], 0, pl[0]), b1;
   bf16x8_t af[8];
 #pragma unroll
   for (int rb = 0; rb < 8; ++rb) af[rb] = frag(0, rb, 0);
@@ -1571,23 +1578,24 @@ __global__ void __launch_bounds__(NT_R4, 1) k_gemm_fwd_r4(FwdArgs args, int n_ti
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
-      for (int rb = 0; rb < 8; ++rb) acc[rb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[rb], b0, acc[rb][0], 0, 0, 0);
-      b1 = wr.operand(R[p], 1, ks, pl[1]);
-      if (ks == 3) pl[0] = wr.planes(R[p ^ 1], 0);
+      for (int rb = 0; rb < 8; ++rb) mfma(b0, af[rb], acc[rb][0]);
+      b1 = wb[1].operand(R[p][1], ks, pl[1]);
+      if (ks == 3) pl[0] = wb[0].planes(R[p ^ 1][0]);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int rb = 0; rb < 8; ++rb) {
-        acc[rb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[rb], b1, acc[rb][1], 0, 0, 0);
+        mfma(b1, af[rb], acc[rb][1]);
         af[rb] = ks < 3 ? frag(p, rb, ks + 1) : frag(p ^ 1, rb, 0);
       }
       if (ks < 3) {
-        b0 = wr.operand(R[p], 0, ks + 1, pl[0]);
+        b0 = wb[0].operand(R[p][0], ks + 1, pl[0]);
       } else {
-        pl[1] = wr.planes(R[p ^ 1], 1);
-        b0 = wr.operand(R[p ^ 1], 0, 0, pl[0]);
+        pl[1] = wb[1].planes(R[p ^ 1][1]);
+        b0 = wb[0].operand(R[p ^ 1][0], 0, pl[0]);
         // stages past the end: activations read as zero, weights re-read the last stage
         load_a(kof(s + 2), p, s + 2 >= nk);
-        wr.load(R[p], kof(s + 2));
+        wb[0].load(R[p][0], kof(s + 2));
+        wb[1].load(R[p][1], kof(s + 2));
       }
       if (ks == 2) {
         __builtin_amdgcn_s_waitcnt(kWaitVm0);   // this wave's loads of A(s + 1) have landed
@@ -1601,34 +1609,101 @@ __global__ void __launch_bounds__(NT_R4, 1) k_gemm_fwd_r4(FwdArgs args, int n_ti
     stage(s + 1, std::integral_constant<int, 1>{});
   }
 
-  // ---- epilogue: stage each half of the tile in LDS (rows 128 h .. +128 = row blocks
-  // 4 h .. 4 h + 3 of every wave), then the shared stores
-  constexpr int OP = BN + 4;
-  auto stage_half = [&](int half) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int r = i * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
-          const int c = 64 * w + 32 * cb + (lane & 31);
-          sm.u.out[r * OP + c] = half == 0 ? acc[i][cb][v] : acc[4 + i][cb][v];
-        }
-  };
+  // ---- epilogue, straight from the accumulators.  Lane: token m0 + 32 rb + (lane & 31);
+  // columns (block cb, group q) c(cb) + 8 q + 4 (lane >> 5) + 0..3
+  const int h4 = 4 * (lane >> 5);
   if constexpr (PAIRED) {
-    epilogue_swiglu_gen<NT_R4>(sm.u.out, stage_half, m0, n0, args.M, n_out, args.y, args.ldy, args.gu32, args.ldgu);
+    const int I = W0.n_out;
+#pragma unroll
+    for (int rb = 0; rb < 8; ++rb) {
+      const int m = m0 + 32 * rb + (lane & 31);
+      if (m >= args.M) continue;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int j = n0 + col0 + 8 * q + h4;   // gate / up row = act column
+        if (j >= I) continue;                    // I % 4 == 0
+        float gt[4], up[4], a[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          gt[e] = acc[rb][0][4 * q + e];
+          up[e] = acc[rb][1][4 * q + e];
+          a[e] = gt[e] * sigmoid_f(gt[e]) * up[e];
+        }
+        *reinterpret_cast<uint2*>(args.y + (int64_t)m * args.ldy + j) = pack4(a);
+        if (args.gu32) {
+          *reinterpret_cast<float4*>(args.gu32 + (int64_t)m * args.ldgu + j) = make_float4(gt[0], gt[1], gt[2], gt[3]);
+          *reinterpret_cast<float4*>(args.gu32 + (int64_t)m * args.ldgu + I + j) = make_float4(up[0], up[1], up[2], up[3]);
+        }
+      }
+    }
   } else {
-    Epi E;
-    E.f32 = args.y32 != nullptr;
-    E.out = E.f32 ? (void*)(args.y32 + G.out_col0) : (void*)(args.y + G.out_col0);
-    E.ldo = args.ldy;
-    E.r16 = args.resid ? args.resid + G.out_col0 : nullptr;
-    E.r32 = args.resid32 ? args.resid32 + G.out_col0 : nullptr;
-    E.ldr = args.ldr;
-    E.rope_tab = args.rope_tab; E.rope_cols = args.rope_tab ? args.rope_cols : 0;
-    E.col_base = G.out_col0; E.seq = args.seq; E.hd = args.head_dim;
-    epilogue_gen<NT_R4>(sm.u.out, stage_half, m0, n0, args.M, n_out, E);
+    const int n_out = G.w.n_out;
+    const bool f32 = args.y32 != nullptr;
+    const int cbase = G.out_col0;              // this group's first column of the output
+    const bool rope = args.rope_tab && cbase + n0 < args.rope_cols;   // whole tile rotated (hd 128)
+#pragma unroll
+    for (int rb = 0; rb < 8; ++rb) {
+      const int m = m0 + 32 * rb + (lane & 31);
+      if (m >= args.M) continue;
+      const int pos = m % args.seq;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float y[2][4];
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) y[cb][e] = acc[rb][cb][4 * q + e];
+        const int d = col0 + 8 * q + h4;         // column within the tile of block 0 (block 1: + 64)
+        if (rope) {
+          // (d mod 128) < 64: block 0 holds x1 of dims i = d % 64 .. +4, block 1 their x2
+          const float4* tab = reinterpret_cast<const float4*>(args.rope_tab + (int64_t)pos * 64 + (d & 63));
+          const float4 t01 = tab[0], t23 = tab[1];
+          const float cs[4] = {t01.x, t01.z, t23.x, t23.z}, sn[4] = {t01.y, t01.w, t23.y, t23.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float x1 = y[0][e], x2 = y[1][e];
+            y[0][e] = x1 * cs[e] - x2 * sn[e];
+            y[1][e] = x2 * cs[e] + x1 * sn[e];
+          }
+        }
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) {
+          const int n = n0 + d + 64 * cb;       // column within this group
+          if (n >= n_out) continue;
+          const bool full = n + 4 <= n_out;
+          const int64_t o = (int64_t)m * args.ldy + cbase + n;
+          const int64_t ro = (int64_t)m * args.ldr + cbase + n;
+          if (args.resid32) {
+            if (full) {
+              const float4 r = *reinterpret_cast<const float4*>(args.resid32 + ro);
+              y[cb][0] += r.x; y[cb][1] += r.y; y[cb][2] += r.z; y[cb][3] += r.w;
+            } else {
+              for (int e = 0; e < 4 && n + e < n_out; ++e) y[cb][e] += args.resid32[ro + e];
+            }
+          } else if (args.resid) {
+            if (full) {
+              const uint2 r = *reinterpret_cast<const uint2*>(args.resid + ro);
+              y[cb][0] += bf16_lo(r.x); y[cb][1] += bf16_hi(r.x); y[cb][2] += bf16_lo(r.y); y[cb][3] += bf16_hi(r.y);
+            } else {
+              for (int e = 0; e < 4 && n + e < n_out; ++e) y[cb][e] += bf16_lo(args.resid[ro + e]);
+            }
+          }
+          if (f32) {
+            float* po = args.y32 + o;
+            if (full) *reinterpret_cast<float4*>(po) = make_float4(y[cb][0], y[cb][1], y[cb][2], y[cb][3]);
+            else for (int e = 0; e < 4 && n + e < n_out; ++e) po[e] = y[cb][e];
+          } else {
+            uint16_t* po = args.y + o;
+            const uint2 pk = pack4(y[cb]);
+            if (full) *reinterpret_cast<uint2*>(po) = pk;
+            else {
+              const uint16_t hv[4] = {(uint16_t)pk.x, (uint16_t)(pk.x >> 16), (uint16_t)pk.y, (uint16_t)(pk.y >> 16)};
+              for (int e = 0; e < 4 && n + e < n_out; ++e) po[e] = hv[e];
+            }
+          }
+        }
+      }
+    }
   }
 }
 
@@ -1680,7 +1755,16 @@ hipError_t launch_gemm_fwd(const FwdArgs& a, hipStream_t s) {
   const bool fast = (a.K % BK) == 0 && a.K >= BK && (a.ldx % 8) == 0;
   // the 4-wave kernel: an even number of 64-deep stages, 16-byte aligned rows of the
   // activations and of the low-rank operand
-  const bool r4 = fast && (a.K / BK) % 2 == 0 && (a.kx == 0 || a.ldaext % 8 == 0) && g_use_r4;
+  bool r4 = fast && (a.K / BK) % 2 == 0 && (a.kx == 0 || a.ldaext % 8 == 0) && a.ldy % 4 == 0 && g_use_r4;
+  if (a.rope_tab) {
+    // the rotary pairs (d, d + 64) must sit in one tile: head_dim 128, the rotated columns
+    // made of whole groups whose widths and first columns are multiples of 256
+    r4 = r4 && a.head_dim == 128 && a.rope_cols % 256 == 0;
+    for (int g = 0; g < a.n_groups; ++g)
+      r4 = r4 && (a.g[g].out_col0 >= a.rope_cols || (a.g[g].w.n_out % 256 == 0 && a.g[g].out_col0 % 256 == 0));
+  }
+  if (a.resid || a.resid32) r4 = r4 && a.ldr % 4 == 0;
+  if (a.swiglu) r4 = r4 && (!a.gu32 || a.ldgu % 4 == 0);
   if (a.swiglu) {
     // paired gate | up tiles: same shape, adjacent low-rank columns, 2 kx <= 64
     if (!fast || a.n_groups != 2 || a.g[0].w.n_out != a.g[1].w.n_out || a.g[0].w.n_in != a.g[1].w.n_in ||
