@@ -359,6 +359,62 @@ __device__ __forceinline__ float dq_absmax(uint32_t code_byte, float scale2, flo
   return prod + mean;
 }
 
+// 4-bit expansion without tables in memory: per NF4 block, the 16 products
+// bf16_rne(fp32(level[e] * absmax)) are formed once (16 multiplies, 8 conversions) and
+// kept as two byte planes (the low and the high byte of each); every 8 codes then become
+// 8 bf16 values by byte permutes (v_perm_b32): the code's low 3 bits select within each
+// half of a plane, its bit 3 selects the half (bit select), and two more permutes
+// interleave low and high bytes.  The values are those of the table path exactly.
+// the 16 NF4 levels as float32 bit patterns; gemm_dequant_init checks them bitwise
+// against the host codebook before any kernel runs
+__host__ __device__ constexpr uint32_t kNF4LevelBits[16] = {
+    0xbf800000u, 0xbf3239b1u, 0xbf066b2eu, 0xbeca329eu, 0xbe91a24bu, 0xbe3d353du, 0xbdba7869u, 0x00000000u,
+    0x3da2fb01u, 0x3e24cadfu, 0x3e7c04dau, 0x3ead0336u, 0x3ee1a4b5u, 0x3f1007a9u, 0x3f3913b0u, 0x3f800000u};
+
+struct Planes {
+  uint32_t lo[4], hi[4];   // lo[q]: low bytes of entries 4q .. 4q+3; hi[q]: their high bytes
+};
+
+__device__ __forceinline__ Planes make_planes(float am) {
+  uint32_t P[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    P[j] = pack_bf16x2(__builtin_bit_cast(float, kNF4LevelBits[2 * j]) * am,
+                       __builtin_bit_cast(float, kNF4LevelBits[2 * j + 1]) * am);
+  Planes p;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    p.lo[q] = __builtin_amdgcn_perm(P[2 * q + 1], P[2 * q], 0x06040200u);
+    p.hi[q] = __builtin_amdgcn_perm(P[2 * q + 1], P[2 * q], 0x07050301u);
+  }
+  return p;
+}
+
+// 4 codes, one per byte of s (0..15) -> bf16 values of codes 0, 1 (o0) and 2, 3 (o1)
+__device__ __forceinline__ void lookup4(uint32_t s, const Planes& p, uint32_t& o0, uint32_t& o1) {
+  const uint32_t s7 = s & 0x07070707u;
+  const uint32_t b3 = (s >> 3) & 0x01010101u;
+  const uint32_t m = (b3 << 8) - b3;                 // 0xFF in every byte whose code is >= 8
+  const uint32_t la = __builtin_amdgcn_perm(p.lo[1], p.lo[0], s7), lb = __builtin_amdgcn_perm(p.lo[3], p.lo[2], s7);
+  const uint32_t ha = __builtin_amdgcn_perm(p.hi[1], p.hi[0], s7), hb = __builtin_amdgcn_perm(p.hi[3], p.hi[2], s7);
+  const uint32_t L = (lb & m) | (la & ~m), H = (hb & m) | (ha & ~m);
+  o0 = __builtin_amdgcn_perm(H, L, 0x05010400u);
+  o1 = __builtin_amdgcn_perm(H, L, 0x07030602u);
+}
+
+// 8 codes of one dword (byte j = code[2j] << 4 | code[2j+1]) -> 8 bf16, element 0 lowest
+__device__ __forceinline__ bf16x8_t expand8(uint32_t x, const Planes& p) {
+  const uint32_t hn = (x >> 4) & 0x0F0F0F0Fu, ln = x & 0x0F0F0F0Fu;
+  const uint32_t sa = __builtin_amdgcn_perm(ln, hn, 0x05010400u), sb = __builtin_amdgcn_perm(ln, hn, 0x07030602u);
+  uint32_t o[4];
+  lookup4(sa, p, o[0], o[1]);
+  lookup4(sb, p, o[2], o[3]);
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = {o[0], o[1], o[2], o[3]};
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+
+
 constexpr int NT_FAST = 512;    // fast path: 8 waves, two per SIMD
 
 // A operand: 256 rows x 64 columns of a K-contiguous bf16 matrix (row stride ld);
@@ -1283,12 +1339,7 @@ __global__ void __launch_bounds__(NT_FAST, 1) k_gemm_bwd_fast(BwdArgs args, int 
 // either way).  A lane's 4 steps then cover the 32 contiguous k values of its half: 16
 // bytes of NF4 codes, one load per column block and stage.
 //
-// 4-bit expansion without tables in memory: per row block and stage, the 16 products
-// bf16_rne(fp32(level[e] * absmax)) are formed once (16 multiplies, 8 conversions) and
-// kept as two byte planes (the low and the high byte of each); every 8 codes then become
-// 8 bf16 values by byte permutes (v_perm_b32): the code's low 3 bits select within each
-// half of a plane, its bit 3 selects the half (bit select), and two more permutes
-// interleave low and high bytes.  The values are those of the table path exactly.
+// 4-bit expansion: byte planes per row block and stage (make_planes / expand8).
 //
 // Activations: two LDS buffers of 256 rows x 128 bytes filled by buffer loads that write
 // LDS directly; the 16-byte chunk c of row r sits at position c ^ ((r >> 1) & 7), so that
@@ -1298,55 +1349,6 @@ __global__ void __launch_bounds__(NT_FAST, 1) k_gemm_bwd_fast(BwdArgs args, int 
 // next stage's first fragments.  The stage count must be even (unrolled by two so that
 // every register set and buffer index is static).
 constexpr int NT_R4 = 256;
-
-// the 16 NF4 levels as float32 bit patterns; gemm_dequant_init checks them bitwise
-// against the host codebook before any kernel runs
-__host__ __device__ constexpr uint32_t kNF4LevelBits[16] = {
-    0xbf800000u, 0xbf3239b1u, 0xbf066b2eu, 0xbeca329eu, 0xbe91a24bu, 0xbe3d353du, 0xbdba7869u, 0x00000000u,
-    0x3da2fb01u, 0x3e24cadfu, 0x3e7c04dau, 0x3ead0336u, 0x3ee1a4b5u, 0x3f1007a9u, 0x3f3913b0u, 0x3f800000u};
-
-struct Planes {
-  uint32_t lo[4], hi[4];   // lo[q]: low bytes of entries 4q .. 4q+3; hi[q]: their high bytes
-};
-
-__device__ __forceinline__ Planes make_planes(float am) {
-  uint32_t P[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j)
-    P[j] = pack_bf16x2(__builtin_bit_cast(float, kNF4LevelBits[2 * j]) * am,
-                       __builtin_bit_cast(float, kNF4LevelBits[2 * j + 1]) * am);
-  Planes p;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    p.lo[q] = __builtin_amdgcn_perm(P[2 * q + 1], P[2 * q], 0x06040200u);
-    p.hi[q] = __builtin_amdgcn_perm(P[2 * q + 1], P[2 * q], 0x07050301u);
-  }
-  return p;
-}
-
-// 4 codes, one per byte of s (0..15) -> bf16 values of codes 0, 1 (o0) and 2, 3 (o1)
-__device__ __forceinline__ void lookup4(uint32_t s, const Planes& p, uint32_t& o0, uint32_t& o1) {
-  const uint32_t s7 = s & 0x07070707u;
-  const uint32_t b3 = (s >> 3) & 0x01010101u;
-  const uint32_t m = (b3 << 8) - b3;                 // 0xFF in every byte whose code is >= 8
-  const uint32_t la = __builtin_amdgcn_perm(p.lo[1], p.lo[0], s7), lb = __builtin_amdgcn_perm(p.lo[3], p.lo[2], s7);
-  const uint32_t ha = __builtin_amdgcn_perm(p.hi[1], p.hi[0], s7), hb = __builtin_amdgcn_perm(p.hi[3], p.hi[2], s7);
-  const uint32_t L = (lb & m) | (la & ~m), H = (hb & m) | (ha & ~m);
-  o0 = __builtin_amdgcn_perm(H, L, 0x05010400u);
-  o1 = __builtin_amdgcn_perm(H, L, 0x07030602u);
-}
-
-// 8 codes of one dword (byte j = code[2j] << 4 | code[2j+1]) -> 8 bf16, element 0 lowest
-__device__ __forceinline__ bf16x8_t expand8(uint32_t x, const Planes& p) {
-  const uint32_t hn = (x >> 4) & 0x0F0F0F0Fu, ln = x & 0x0F0F0F0Fu;
-  const uint32_t sa = __builtin_amdgcn_perm(ln, hn, 0x05010400u), sb = __builtin_amdgcn_perm(ln, hn, 0x07030602u);
-  uint32_t o[4];
-  lookup4(sa, p, o[0], o[1]);
-  lookup4(sb, p, o[2], o[3]);
-  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-  const u32x4 v = {o[0], o[1], o[2], o[3]};
-  return __builtin_bit_cast(bf16x8_t, v);
-}
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
