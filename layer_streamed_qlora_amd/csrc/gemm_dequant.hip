@@ -23,7 +23,6 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include <cstdlib>
 #include <type_traits>
 
 #include "lsq_internal.hpp"
@@ -359,62 +358,6 @@ __device__ __forceinline__ float dq_absmax(uint32_t code_byte, float scale2, flo
   return prod + mean;
 }
 
-// 4-bit expansion without tables in memory: per NF4 block, the 16 products
-// bf16_rne(fp32(level[e] * absmax)) are formed once (16 multiplies, 8 conversions) and
-// kept as two byte planes (the low and the high byte of each); every 8 codes then become
-// 8 bf16 values by byte permutes (v_perm_b32): the code's low 3 bits select within each
-// half of a plane, its bit 3 selects the half (bit select), and two more permutes
-// interleave low and high bytes.  The values are those of the table path exactly.
-// the 16 NF4 levels as float32 bit patterns; gemm_dequant_init checks them bitwise
-// against the host codebook before any kernel runs
-__host__ __device__ constexpr uint32_t kNF4LevelBits[16] = {
-    0xbf800000u, 0xbf3239b1u, 0xbf066b2eu, 0xbeca329eu, 0xbe91a24bu, 0xbe3d353du, 0xbdba7869u, 0x00000000u,
-    0x3da2fb01u, 0x3e24cadfu, 0x3e7c04dau, 0x3ead0336u, 0x3ee1a4b5u, 0x3f1007a9u, 0x3f3913b0u, 0x3f800000u};
-
-struct Planes {
-  uint32_t lo[4], hi[4];   // lo[q]: low bytes of entries 4q .. 4q+3; hi[q]: their high bytes
-};
-
-__device__ __forceinline__ Planes make_planes(float am) {
-  uint32_t P[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j)
-    P[j] = pack_bf16x2(__builtin_bit_cast(float, kNF4LevelBits[2 * j]) * am,
-                       __builtin_bit_cast(float, kNF4LevelBits[2 * j + 1]) * am);
-  Planes p;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    p.lo[q] = __builtin_amdgcn_perm(P[2 * q + 1], P[2 * q], 0x06040200u);
-    p.hi[q] = __builtin_amdgcn_perm(P[2 * q + 1], P[2 * q], 0x07050301u);
-  }
-  return p;
-}
-
-// 4 codes, one per byte of s (0..15) -> bf16 values of codes 0, 1 (o0) and 2, 3 (o1)
-__device__ __forceinline__ void lookup4(uint32_t s, const Planes& p, uint32_t& o0, uint32_t& o1) {
-  const uint32_t s7 = s & 0x07070707u;
-  const uint32_t b3 = (s >> 3) & 0x01010101u;
-  const uint32_t m = (b3 << 8) - b3;                 // 0xFF in every byte whose code is >= 8
-  const uint32_t la = __builtin_amdgcn_perm(p.lo[1], p.lo[0], s7), lb = __builtin_amdgcn_perm(p.lo[3], p.lo[2], s7);
-  const uint32_t ha = __builtin_amdgcn_perm(p.hi[1], p.hi[0], s7), hb = __builtin_amdgcn_perm(p.hi[3], p.hi[2], s7);
-  const uint32_t L = (lb & m) | (la & ~m), H = (hb & m) | (ha & ~m);
-  o0 = __builtin_amdgcn_perm(H, L, 0x05010400u);
-  o1 = __builtin_amdgcn_perm(H, L, 0x07030602u);
-}
-
-// 8 codes of one dword (byte j = code[2j] << 4 | code[2j+1]) -> 8 bf16, element 0 lowest
-__device__ __forceinline__ bf16x8_t expand8(uint32_t x, const Planes& p) {
-  const uint32_t hn = (x >> 4) & 0x0F0F0F0Fu, ln = x & 0x0F0F0F0Fu;
-  const uint32_t sa = __builtin_amdgcn_perm(ln, hn, 0x05010400u), sb = __builtin_amdgcn_perm(ln, hn, 0x07030602u);
-  uint32_t o[4];
-  lookup4(sa, p, o[0], o[1]);
-  lookup4(sb, p, o[2], o[3]);
-  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-  const u32x4 v = {o[0], o[1], o[2], o[3]};
-  return __builtin_bit_cast(bf16x8_t, v);
-}
-
-
 constexpr int NT_FAST = 512;    // fast path: 8 waves, two per SIMD
 
 // A operand: 256 rows x 64 columns of a K-contiguous bf16 matrix (row stride ld);
@@ -694,19 +637,30 @@ struct Epi {
 
 __device__ __forceinline__ float sigmoid_f(float z) { return 1.0f / (1.0f + __expf(-z)); }
 
-// The store part, shared by every kernel: stage_half(h) writes rows h*128 .. +128 of the
-// float32 tile into out (row pitch BN + 4); every thread then stores from there.
-template <int NT, class StageHalf>
-__device__ __forceinline__ void epilogue_gen(float* out, StageHalf&& stage_half, int m0, int n0, int M_lim, int N_lim,
-                                             const Epi& E) {
+template <int NT>
+__device__ __forceinline__ void epilogue(Smem& sm, f32x16_t (&acc)[4][Layout<NT>::JB], int m0, int n0, int M_lim,
+                                         int N_lim, const Epi& E) {
+  constexpr int WNW = Layout<NT>::WNW, JB = Layout<NT>::JB;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave / WNW, wn = wave % WNW;
   constexpr int OP = BN + 4;
   constexpr int RS = NT / 64;            // rows apart of one thread's consecutive rows
   constexpr int RPT = 128 / RS;          // rows per thread per half tile
   constexpr int CH = RPT < 4 ? RPT : 4;  // rows per batch of global reads
-#pragma unroll
   for (int half = 0; half < 2; ++half) {
     __syncthreads();
-    stage_half(half);
+    if (wm == half) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < JB; ++j)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int r = i * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
+            const int c = wn * (32 * JB) + j * 32 + (lane & 31);
+            sm.u.out[r * OP + c] = acc[i][j][v];
+          }
+    }
     __syncthreads();
     // Thread t handles column quad q = t % 64 of rows t / 64 + RS k.  Each batch of CH
     // rows issues all its global reads (residual, rotary table, or g and u) before it
@@ -758,7 +712,7 @@ __device__ __forceinline__ void epilogue_gen(float* out, StageHalf&& stage_half,
         const int r = rt + RS * (c + k);
         const int m = mbase + r;
         if (m >= M_lim) break;
-        const float4 v = *reinterpret_cast<const float4*>(&out[r * OP + 4 * q]);
+        const float4 v = *reinterpret_cast<const float4*>(&sm.u.out[r * OP + 4 * q]);
         float y[4] = {v.x, v.y, v.z, v.w};
         if (mode == 1) {
           const float gs[4] = {pre[k][0].x, pre[k][0].y, pre[k][0].z, pre[k][0].w};
@@ -776,7 +730,7 @@ __device__ __forceinline__ void epilogue_gen(float* out, StageHalf&& stage_half,
           continue;
         }
         if (rope) {
-          const float4 pv = *reinterpret_cast<const float4*>(&out[r * OP + 4 * q + (lo ? hh : -hh)]);
+          const float4 pv = *reinterpret_cast<const float4*>(&sm.u.out[r * OP + 4 * q + (lo ? hh : -hh)]);
           const float pr[4] = {pv.x, pv.y, pv.z, pv.w};
           const float cx[4] = {pre[k][0].x, pre[k][0].z, pre[k][1].x, pre[k][1].z};
           const float cy[4] = {pre[k][0].y, pre[k][0].w, pre[k][1].y, pre[k][1].w};
@@ -818,39 +772,30 @@ __device__ __forceinline__ void epilogue_gen(float* out, StageHalf&& stage_half,
   }
 }
 
+// SwiGLU forward epilogue of a paired tile: columns 0..127 are gate, 128..255 up, for
+// outputs j0 .. j0 + 127.  act = bf16(silu(g) u); with gu set, g and u are also kept in
+// float32 (gu [M, ldgu], up at column + I).
 template <int NT>
-__device__ __forceinline__ void epilogue(Smem& sm, f32x16_t (&acc)[4][Layout<NT>::JB], int m0, int n0, int M_lim,
-                                         int N_lim, const Epi& E) {
+__device__ __forceinline__ void epilogue_swiglu(Smem& sm, f32x16_t (&acc)[4][Layout<NT>::JB], int m0, int j0, int M_lim,
+                                                int I, uint16_t* act, int ldact, float* gu, int ldgu) {
   constexpr int WNW = Layout<NT>::WNW, JB = Layout<NT>::JB;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / WNW, wn = wave % WNW;
   constexpr int OP = BN + 4;
-  epilogue_gen<NT>(sm.u.out, [&](int half) {
-    if (wm != half) return;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < JB; ++j)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int r = i * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
-          const int c = wn * (32 * JB) + j * 32 + (lane & 31);
-          sm.u.out[r * OP + c] = acc[i][j][v];
-        }
-  }, m0, n0, M_lim, N_lim, E);
-}
-
-// SwiGLU forward epilogue of a paired tile: columns 0..127 are gate, 128..255 up, for
-// outputs j0 .. j0 + 127.  act = bf16(silu(g) u); with gu set, g and u are also kept in
-// float32 (gu [M, ldgu], up at column + I).
-template <int NT, class StageHalf>
-__device__ __forceinline__ void epilogue_swiglu_gen(float* out, StageHalf&& stage_half, int m0, int j0, int M_lim, int I,
-                                                    uint16_t* act, int ldact, float* gu, int ldgu) {
-  constexpr int OP = BN + 4;
-#pragma unroll
   for (int half = 0; half < 2; ++half) {
     __syncthreads();
-    stage_half(half);
+    if (wm == half) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < JB; ++j)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int r = i * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
+            const int c = wn * (32 * JB) + j * 32 + (lane & 31);
+            sm.u.out[r * OP + c] = acc[i][j][v];
+          }
+    }
     __syncthreads();
     const int mbase = m0 + half * 128;
 #pragma unroll 4
@@ -859,8 +804,8 @@ __device__ __forceinline__ void epilogue_swiglu_gen(float* out, StageHalf&& stag
       const int r = idx >> 5, q = idx & 31;
       const int m = mbase + r, j = j0 + 4 * q;
       if (m >= M_lim || j >= I) continue;              // I % 4 == 0
-      const float4 g4 = *reinterpret_cast<const float4*>(&out[r * OP + 4 * q]);
-      const float4 u4 = *reinterpret_cast<const float4*>(&out[r * OP + 128 + 4 * q]);
+      const float4 g4 = *reinterpret_cast<const float4*>(&sm.u.out[r * OP + 4 * q]);
+      const float4 u4 = *reinterpret_cast<const float4*>(&sm.u.out[r * OP + 128 + 4 * q]);
       const float gs[4] = {g4.x, g4.y, g4.z, g4.w}, us[4] = {u4.x, u4.y, u4.z, u4.w};
       float a[4];
 #pragma unroll
@@ -872,28 +817,6 @@ __device__ __forceinline__ void epilogue_swiglu_gen(float* out, StageHalf&& stag
       }
     }
   }
-}
-
-template <int NT>
-__device__ __forceinline__ void epilogue_swiglu(Smem& sm, f32x16_t (&acc)[4][Layout<NT>::JB], int m0, int j0, int M_lim,
-                                                int I, uint16_t* act, int ldact, float* gu, int ldgu) {
-  constexpr int WNW = Layout<NT>::WNW, JB = Layout<NT>::JB;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave / WNW, wn = wave % WNW;
-  constexpr int OP = BN + 4;
-  epilogue_swiglu_gen<NT>(sm.u.out, [&](int half) {
-    if (wm != half) return;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < JB; ++j)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int r = i * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
-          const int c = wn * (32 * JB) + j * 32 + (lane & 31);
-          sm.u.out[r * OP + c] = acc[i][j][v];
-        }
-  }, m0, j0, M_lim, I, act, ldact, gu, ldgu);
 }
 
 // (m tile, n tile) of linear tile t of an m_tiles x n_tiles grid.  Each XCD's run of
@@ -1328,387 +1251,6 @@ __global__ void __launch_bounds__(NT_FAST, 1) k_gemm_bwd_fast(BwdArgs args, int 
   epilogue<NT_FAST>(sm, acc, m0, j0, args.M, args.N, E);
 }
 
-// ------------------------------------------- forward, 4 waves, W expanded in registers
-// 256 threads, one wave per SIMD, each owning all 256 rows of the tile and 64 of its
-// columns (8 x 2 blocks of 32 x 32: 256 accumulators in AGPRs).  Only the activations
-// pass through LDS; every wave expands its own 64 weight rows straight into MFMA
-// operand registers, so the weights cost no LDS traffic and no level-table reads.
-//
-// K order inside a 64-wide stage.  MFMA step ks (of 4) takes, in lane half h = lane / 32,
-// the 8 k values 32 h + 8 ks .. +8 (for A and for W alike; the product sums over all 64
-// either way).  A lane's 4 steps then cover the 32 contiguous k values of its half: 16
-// bytes of NF4 codes, one load per column block and stage.
-//
-// 4-bit expansion: byte planes per row block and stage (make_planes / expand8).
-//
-// Activations: two LDS buffers of 256 rows x 128 bytes filled by buffer loads that write
-// LDS directly; the 16-byte chunk c of row r sits at position c ^ ((r >> 1) & 7), so that
-// each group of 16 lanes reading one chunk of 16 consecutive rows hits 16 different bank
-// groups.  Stage s reads buffer s % 2; A(s + 1) lands in the other one during stage s - 1
-// and is published by the barrier after step 2 of stage s, so step 3 already reads the
-// next stage's first fragments.  The stage count must be even (unrolled by two so that
-// every register set and buffer index is static).
-constexpr int NT_R4 = 256;
-
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-
-struct SmemR4 {
-  uint8_t a[2][BM * 128];            // activation stages (swizzled, see above)
-};
-
-// One 32-row block of one weight in the forward orientation: loads one stage's codes and
-// scales into registers and yields the MFMA operand of each step.  Rows at or past the
-// end of the weight read as zero (range-checked).
-template <int FMT>
-struct WBlk {
-  struct Regs {
-    uint4 raw[FMT == WF_BF16 ? 4 : 1];   // NF4: 32 codes; bf16: the 4 operands
-    uint32_t blk;                        // absmax bits (NF4) or the 8-bit code (DQ)
-    float s2;                            // DQ second-level scale
-  };
-  rsrc_t codes, absq, sc2;
-  float mean;
-  uint32_t voff_c, voff_a, blk_lane;
-  __device__ __forceinline__ void init(const WeightRef& w, int row0, int lane) {
-    const int K = w.n_in;
-    const int rows = w.n_out - row0 < 32 ? (w.n_out - row0 > 0 ? w.n_out - row0 : 0) : 32;
-    const uint32_t kblk = (uint32_t)K / kNF4Block;
-    const uint32_t r = (uint32_t)(lane & 31), h = (uint32_t)(lane >> 5);
-    mean = 0.f;
-    if constexpr (FMT == WF_BF16) {
-      codes = make_rsrc_wave(w.w + (uint64_t)row0 * K * 2, (uint64_t)rows * K * 2);
-      voff_c = r * (uint32_t)K * 2u + 64u * h;
-    } else {
-      codes = make_rsrc_wave(w.w + (uint64_t)row0 * K / 2, (uint64_t)rows * K / 2);
-      voff_c = r * (uint32_t)K / 2u + 16u * h;
-      const uint64_t b0 = (uint64_t)row0 * kblk;
-      if constexpr (FMT == WF_NF4) {
-        absq = make_rsrc_wave(w.absmax + b0, (uint64_t)rows * kblk * 4);
-        voff_a = r * kblk * 4u;
-      } else {
-        absq = make_rsrc_wave(w.qabs + b0, (uint64_t)rows * kblk);
-        voff_a = r * kblk;
-        const uint64_t all = (uint64_t)w.n_out * kblk;
-        sc2 = make_rsrc_wave(w.scale2, (all + kDQGroup - 1) / kDQGroup * 4);
-        blk_lane = (uint32_t)(b0 + r * kblk);
-        mean = *w.mean;
-      }
-    }
-  }
-  __device__ __forceinline__ void load(Regs& R, uint32_t k0) const {
-    if constexpr (FMT == WF_BF16) {
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) R.raw[ks] = bload16s(codes, voff_c, k0 * 2u + 16u * ks);
-    } else {
-      R.raw[0] = bload16s(codes, voff_c, k0 / 2u);
-      const uint32_t kb = k0 / kNF4Block;
-      if constexpr (FMT == WF_NF4) {
-        R.blk = bload4s(absq, voff_a, kb * 4u);
-      } else {
-        R.blk = bload1s(absq, voff_a, kb);
-        R.s2 = __builtin_bit_cast(float, bload4s(sc2, ((blk_lane + kb) / kDQGroup) * 4u, 0));
-      }
-    }
-  }
-  __device__ __forceinline__ Planes planes(const Regs& R) const {
-    if constexpr (FMT == WF_NF4) return make_planes(__builtin_bit_cast(float, R.blk));
-    else if constexpr (FMT == WF_NF4_DQ) return make_planes(dq_absmax(R.blk, R.s2, mean));
-    else return Planes{};
-  }
-  __device__ __forceinline__ bf16x8_t operand(const Regs& R, int ks, const Planes& p) const {
-    if constexpr (FMT == WF_BF16) return __builtin_bit_cast(bf16x8_t, R.raw[ks]);
-    else return expand8(reinterpret_cast<const uint32_t*>(&R.raw[0])[ks], p);
-  }
-};
-
-// 4 consecutive float32 values as 2 packed bf16 (RNE)
-__device__ __forceinline__ uint2 pack4(const float (&y)[4]) { return make_uint2(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])); }
-
-// The MFMAs take the weights as the A operand and the activations as B, so each
-// accumulator block is a transposed 32 x 32 tile of Y: a lane holds one token (its lane
-// & 31 within the row block) and, for g = 0..3, the 4 consecutive output columns
-// 8 g + 4 (lane >> 5) .. +4 of its column block.  Column blocks: wave w's block 0 is tile
-// columns 128 (w >> 1) + 32 (w & 1) .. +32 and block 1 those + 64, so each column's
-// rotary partner (hd 128: d and d + 64) is in the same lane; paired gate|up tiles give
-// block 0 the gate rows n0 + 32 w .. +32 and block 1 the same up rows, so silu(g) u is
-// formed in the lane too.  The epilogue stores straight from the accumulators (8- or
-// 16-byte accesses), without staging the tile in LDS.
-template <int FMT, bool PAIRED>
-__global__ void __launch_bounds__(NT_R4, 1) k_gemm_fwd_r4(FwdArgs args, int n_tiles, int total_tiles, int padded) {
-  extern __shared__ __align__(1024) unsigned char smem_raw[];
-  SmemR4& sm = *reinterpret_cast<SmemR4*>(smem_raw);
-  const int tile = xcd_tile(blockIdx.x, padded);
-  if (tile >= total_tiles) return;
-  int mt, rest;
-  tile_mn(tile, total_tiles / n_tiles, n_tiles, mt, rest);
-  int g = 0;
-  if constexpr (!PAIRED) {
-    for (; g < args.n_groups - 1; ++g) {
-      const int nt_g = (args.g[g].w.n_out + BN - 1) / BN;
-      if (rest < nt_g) break;
-      rest -= nt_g;
-    }
-  }
-  const FwdGroup& G = args.g[g];
-  const int m0 = mt * BM;
-  const int n0 = PAIRED ? rest * (BN / 2) : rest * BN;
-  const int K = args.K;
-  const int lane = threadIdx.x & 63;
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  // this wave's two column blocks: weight and first row (within that weight)
-  const WeightRef& W0 = G.w;
-  const WeightRef& W1 = PAIRED ? args.g[1].w : G.w;
-  const int col0 = PAIRED ? 32 * w : 128 * (w >> 1) + 32 * (w & 1);   // tile column of block 0
-  const int row0[2] = {n0 + col0, PAIRED ? n0 + col0 : n0 + col0 + 64};
-
-  f32x16_t acc[8][2];
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16_t{};
-
-  const int rows_left = args.M - m0;
-  const int arows = rows_left < BM ? rows_left : BM;
-  const rsrc_t xres = make_rsrc_wave(args.x + (int64_t)m0 * args.ldx, (uint64_t)arows * args.ldx * 2);
-  const int lrow = lane >> 3;
-  // activation loads: load i of wave w fills LDS rows 64 w + 8 i + lrow at position
-  // lane & 7; the row's swizzle (row >> 1) & 7 = (lrow >> 1) ^ 4 (i & 1)
-  uint32_t a_vo[2];
-#pragma unroll
-  for (int e = 0; e < 2; ++e)
-    a_vo[e] = ((uint32_t)(64 * w + 8 * e + lrow) * (uint32_t)args.ldx +
-               8u * (uint32_t)((lane & 7) ^ ((lrow >> 1) ^ (4 * e)))) * 2u;
-  const uint32_t a_istep = 16u * (uint32_t)args.ldx * 2u;   // rows 16 apart (loads i, i + 2)
-  const uint32_t swz = ((lane & 31) >> 1) & 7;
-  const uint32_t fbase = (uint32_t)(lane & 31) * 128u;
-  const uint32_t fch = (uint32_t)(4 * (lane >> 5)) ^ swz;
-  auto load_a = [&](uint32_t k0, int buf, bool zero) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      lds_ptr_t dst = (lds_ptr_t)(&sm.a[buf][(8 * (8 * w + i)) * 128]);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(xres, dst, 16, zero ? kOOB : a_vo[i & 1],
-                                               zero ? 0u : k0 * 2u + (uint32_t)(i >> 1) * a_istep, 0, 0);
-    }
-  };
-  auto frag = [&](int buf, int rb, int ks) {
-    return *reinterpret_cast<const bf16x8_t*>(&sm.a[buf][rb * 4096 + fbase + ((fch ^ (uint32_t)ks) << 4)]);
-  };
-  auto mfma = [&](const bf16x8_t& wop, const bf16x8_t& xop, f32x16_t& c) {
-    c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wop, xop, c, 0, 0, 0);
-  };
-
-  // ---- the low-rank extension: one 64-deep stage before the main loop.  A columns
-  // [ext_col0, ext_col0 + kx) of aext (paired: 2 kx, gate's then up's); the weight-side
-  // operands are the bf16 copies of B ([n_out, kx], row stride kx), zero past kx (paired:
-  // the gate block takes columns 0 .. kx, the up block kx .. 2 kx)
-  {
-    const int kx = args.kx;
-    const uint16_t* bx[2] = {G.bext, PAIRED ? args.g[1].bext : G.bext};
-    const bool has_ext = kx > 0 && (bx[0] != nullptr || bx[1] != nullptr);
-    if (has_ext) {
-      const int ecols = PAIRED ? 2 * kx : kx;
-      const rsrc_t eres = make_rsrc_wave(args.aext + (int64_t)m0 * args.ldaext, (uint64_t)arows * args.ldaext * 2);
-      // loaded into registers and stored, so that the columns past the extension are zeros
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int row = 64 * w + 8 * i + lrow;
-        const int c = (lane & 7) ^ ((row >> 1) & 7);
-        const bool ok = 8 * c < ecols;
-        const uint4 v = bload16(eres, ok ? ((uint32_t)row * (uint32_t)args.ldaext + (uint32_t)(G.ext_col0 + 8 * c)) * 2u : kOOB);
-        *reinterpret_cast<uint4*>(&sm.a[1][row * 128 + 16 * (lane & 7)]) = v;
-      }
-      bf16x8_t eb[2][4];
-#pragma unroll
-      for (int cb = 0; cb < 2; ++cb) {
-        const WeightRef& Wc = cb ? W1 : W0;
-        const int brows = Wc.n_out - row0[cb] < 32 ? (Wc.n_out - row0[cb] > 0 ? Wc.n_out - row0[cb] : 0) : 32;
-        const bool bon = bx[cb] != nullptr;
-        const rsrc_t bres = make_rsrc_wave(bon ? bx[cb] + (int64_t)row0[cb] * kx : args.x, bon ? (uint64_t)brows * kx * 2 : 0);
-        const int c_lo = PAIRED ? cb * kx : 0;
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          const int src = 32 * (lane >> 5) + 8 * ks - c_lo;   // extension column of this operand
-          const bool ok = bon && src >= 0 && src < kx;
-          eb[cb][ks] = __builtin_bit_cast(
-              bf16x8_t, bload16(bres, ok ? ((uint32_t)(lane & 31) * (uint32_t)kx + (uint32_t)src) * 2u : kOOB));
-        }
-      }
-      __builtin_amdgcn_s_waitcnt(kWaitVm0);
-      __syncthreads();
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-        for (int rb = 0; rb < 8; ++rb) {
-          const bf16x8_t a = frag(1, rb, ks);
-          mfma(eb[0][ks], a, acc[rb][0]);
-          mfma(eb[1][ks], a, acc[rb][1]);
-        }
-      __syncthreads();   // buffer 1 is refilled below
-    }
-  }
-
-  // ---- main loop over the nk (even) stages of K
-  WBlk<FMT> wb[2];
-  wb[0].init(W0, row0[0], lane);
-  wb[1].init(W1, row0[1], lane);
-  typename WBlk<FMT>::Regs R[2][2];   // [stage parity][column block]
-  const int nk = K / BK;
-  auto kof = [&](int s) { return (uint32_t)(s < nk ? s : nk - 1) * BK; };
-  load_a(0, 0, false);
-  wb[0].load(R[0][0], 0);
-  wb[1].load(R[0][1], 0);
-  wb[0].load(R[1][0], kof(1));
-  wb[1].load(R[1][1], kof(1));
-  load_a(kof(1), 1, false);
-  __builtin_amdgcn_s_waitcnt(kWaitVm0);
-  __syncthreads();
-  Planes pl[2];
-  pl[0] = wb[0].planes(R[0][0]);
-  pl[1] = wb[1].planes(R[0][1]);
-  bf16x8_t b0 = wb[0].operand(R[0][0], 0, pl[0]), b1;
-  bf16x8_t af[8];
-#pragma unroll
-  for (int rb = 0; rb < 8; ++rb) af[rb] = frag(0, rb, 0);
-  // stage s (parity p): in step ks, pass 0 multiplies with column block 0 while block 1's
-  // operand of the step is expanded; pass 1 multiplies with block 1, refills each A
-  // fragment for the next step, and expands block 0's operand of the next step.  The
-  // planes of stage s + 1 are built in step 3 after the last use of those of stage s;
-  // A(s + 2) and the codes of stage s + 2 are loaded in step 3 into buffer p (read for
-  // the last time in step 2, before the barrier) and register set p.
-  auto stage = [&](int s, auto pc) {
-    constexpr int p = decltype(pc)::value;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-#pragma unroll
-      for (int rb = 0; rb < 8; ++rb) mfma(b0, af[rb], acc[rb][0]);
-      b1 = wb[1].operand(R[p][1], ks, pl[1]);
-      if (ks == 3) pl[0] = wb[0].planes(R[p ^ 1][0]);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int rb = 0; rb < 8; ++rb) {
-        mfma(b1, af[rb], acc[rb][1]);
-        af[rb] = ks < 3 ? frag(p, rb, ks + 1) : frag(p ^ 1, rb, 0);
-      }
-      if (ks < 3) {
-        b0 = wb[0].operand(R[p][0], ks + 1, pl[0]);
-      } else {
-        pl[1] = wb[1].planes(R[p ^ 1][1]);
-        b0 = wb[0].operand(R[p ^ 1][0], 0, pl[0]);
-        // stages past the end: activations read as zero, weights re-read the last stage
-        load_a(kof(s + 2), p, s + 2 >= nk);
-        wb[0].load(R[p][0], kof(s + 2));
-        wb[1].load(R[p][1], kof(s + 2));
-      }
-      if (ks == 2) {
-        __builtin_amdgcn_s_waitcnt(kWaitVm0);   // this wave's loads of A(s + 1) have landed
-        __syncthreads();                        // ... and every wave's; buffer p is free
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  };
-  for (int s = 0; s < nk; s += 2) {
-    stage(s, std::integral_constant<int, 0>{});
-    stage(s + 1, std::integral_constant<int, 1>{});
-  }
-
-  // ---- epilogue, straight from the accumulators.  Lane: token m0 + 32 rb + (lane & 31);
-  // columns (block cb, group q) c(cb) + 8 q + 4 (lane >> 5) + 0..3
-  const int h4 = 4 * (lane >> 5);
-  if constexpr (PAIRED) {
-    const int I = W0.n_out;
-#pragma unroll
-    for (int rb = 0; rb < 8; ++rb) {
-      const int m = m0 + 32 * rb + (lane & 31);
-      if (m >= args.M) continue;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int j = n0 + col0 + 8 * q + h4;   // gate / up row = act column
-        if (j >= I) continue;                    // I % 4 == 0
-        float gt[4], up[4], a[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          gt[e] = acc[rb][0][4 * q + e];
-          up[e] = acc[rb][1][4 * q + e];
-          a[e] = gt[e] * sigmoid_f(gt[e]) * up[e];
-        }
-        *reinterpret_cast<uint2*>(args.y + (int64_t)m * args.ldy + j) = pack4(a);
-        if (args.gu32) {
-          *reinterpret_cast<float4*>(args.gu32 + (int64_t)m * args.ldgu + j) = make_float4(gt[0], gt[1], gt[2], gt[3]);
-          *reinterpret_cast<float4*>(args.gu32 + (int64_t)m * args.ldgu + I + j) = make_float4(up[0], up[1], up[2], up[3]);
-        }
-      }
-    }
-  } else {
-    const int n_out = G.w.n_out;
-    const bool f32 = args.y32 != nullptr;
-    const int cbase = G.out_col0;              // this group's first column of the output
-    const bool rope = args.rope_tab && cbase + n0 < args.rope_cols;   // whole tile rotated (hd 128)
-#pragma unroll
-    for (int rb = 0; rb < 8; ++rb) {
-      const int m = m0 + 32 * rb + (lane & 31);
-      if (m >= args.M) continue;
-      const int pos = m % args.seq;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        float y[2][4];
-#pragma unroll
-        for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) y[cb][e] = acc[rb][cb][4 * q + e];
-        const int d = col0 + 8 * q + h4;         // column within the tile of block 0 (block 1: + 64)
-        if (rope) {
-          // (d mod 128) < 64: block 0 holds x1 of dims i = d % 64 .. +4, block 1 their x2
-          const float4* tab = reinterpret_cast<const float4*>(args.rope_tab + (int64_t)pos * 64 + (d & 63));
-          const float4 t01 = tab[0], t23 = tab[1];
-          const float cs[4] = {t01.x, t01.z, t23.x, t23.z}, sn[4] = {t01.y, t01.w, t23.y, t23.w};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float x1 = y[0][e], x2 = y[1][e];
-            y[0][e] = x1 * cs[e] - x2 * sn[e];
-            y[1][e] = x2 * cs[e] + x1 * sn[e];
-          }
-        }
-#pragma unroll
-        for (int cb = 0; cb < 2; ++cb) {
-          const int n = n0 + d + 64 * cb;       // column within this group
-          if (n >= n_out) continue;
-          const bool full = n + 4 <= n_out;
-          const int64_t o = (int64_t)m * args.ldy + cbase + n;
-          const int64_t ro = (int64_t)m * args.ldr + cbase + n;
-          if (args.resid32) {
-            if (full) {
-              const float4 r = *reinterpret_cast<const float4*>(args.resid32 + ro);
-              y[cb][0] += r.x; y[cb][1] += r.y; y[cb][2] += r.z; y[cb][3] += r.w;
-            } else {
-              for (int e = 0; e < 4 && n + e < n_out; ++e) y[cb][e] += args.resid32[ro + e];
-            }
-          } else if (args.resid) {
-            if (full) {
-              const uint2 r = *reinterpret_cast<const uint2*>(args.resid + ro);
-              y[cb][0] += bf16_lo(r.x); y[cb][1] += bf16_hi(r.x); y[cb][2] += bf16_lo(r.y); y[cb][3] += bf16_hi(r.y);
-            } else {
-              for (int e = 0; e < 4 && n + e < n_out; ++e) y[cb][e] += bf16_lo(args.resid[ro + e]);
-            }
-          }
-          if (f32) {
-            float* po = args.y32 + o;
-            if (full) *reinterpret_cast<float4*>(po) = make_float4(y[cb][0], y[cb][1], y[cb][2], y[cb][3]);
-            else for (int e = 0; e < 4 && n + e < n_out; ++e) po[e] = y[cb][e];
-          } else {
-            uint16_t* po = args.y + o;
-            const uint2 pk = pack4(y[cb]);
-            if (full) *reinterpret_cast<uint2*>(po) = pk;
-            else {
-              const uint16_t hv[4] = {(uint16_t)pk.x, (uint16_t)(pk.x >> 16), (uint16_t)pk.y, (uint16_t)(pk.y >> 16)};
-              for (int e = 0; e < 4 && n + e < n_out; ++e) po[e] = hv[e];
-            }
-          }
-        }
-      }
-    }
-  }
-}
-
 // --------------------------------------------------------- standalone dequant
 template <int FMT>
 __global__ void k_dequant(WeightRef w, const float* levels, uint16_t* out) {
@@ -1739,13 +1281,6 @@ hipError_t launch_fmt(int format, F&& f) {
 
 }  // namespace
 
-// the 4-wave forward kernel is used where it applies when LS_GEMM_FWD_R4=1 (it is not
-// yet faster than the 8-wave kernel on the measured shapes)
-static const bool g_use_r4 = [] {
-  const char* e = getenv("LS_GEMM_FWD_R4");
-  return e && e[0] == '1';
-}();
-
 hipError_t launch_gemm_fwd(const FwdArgs& a, hipStream_t s) {
   if (a.M <= 0 || a.n_groups <= 0) return hipSuccess;
   if (a.kx > BK) return hipErrorInvalidValue;   // one extension tile in the forward
@@ -1755,18 +1290,6 @@ hipError_t launch_gemm_fwd(const FwdArgs& a, hipStream_t s) {
   const int total = m_tiles * n_tiles;
   const int padded = (total + 7) / 8 * 8;
   const bool fast = (a.K % BK) == 0 && a.K >= BK && (a.ldx % 8) == 0;
-  // the 4-wave kernel: an even number of 64-deep stages, 16-byte aligned rows of the
-  // activations and of the low-rank operand
-  bool r4 = fast && (a.K / BK) % 2 == 0 && (a.kx == 0 || a.ldaext % 8 == 0) && a.ldy % 4 == 0 && g_use_r4;
-  if (a.rope_tab) {
-    // the rotary pairs (d, d + 64) must sit in one tile: head_dim 128, the rotated columns
-    // made of whole groups whose widths and first columns are multiples of 256
-    r4 = r4 && a.head_dim == 128 && a.rope_cols % 256 == 0;
-    for (int g = 0; g < a.n_groups; ++g)
-      r4 = r4 && (a.g[g].out_col0 >= a.rope_cols || (a.g[g].w.n_out % 256 == 0 && a.g[g].out_col0 % 256 == 0));
-  }
-  if (a.resid || a.resid32) r4 = r4 && a.ldr % 4 == 0;
-  if (a.swiglu) r4 = r4 && (!a.gu32 || a.ldgu % 4 == 0);
   if (a.swiglu) {
     // paired gate | up tiles: same shape, adjacent low-rank columns, 2 kx <= 64
     if (!fast || a.n_groups != 2 || a.g[0].w.n_out != a.g[1].w.n_out || a.g[0].w.n_in != a.g[1].w.n_in ||
@@ -1778,17 +1301,13 @@ hipError_t launch_gemm_fwd(const FwdArgs& a, hipStream_t s) {
     const int ppadded = (ptotal + 7) / 8 * 8;
     return launch_fmt(a.format, [&](auto fmt) {
       constexpr int F = decltype(fmt)::value;
-      if (r4)
-        hipLaunchKernelGGL((k_gemm_fwd_r4<F, true>), dim3(ppadded), dim3(NT_R4), sizeof(SmemR4), s, a, pt, ptotal, ppadded);
-      else
-        hipLaunchKernelGGL((k_gemm_fwd_fast<F, true>), dim3(ppadded), dim3(NT_FAST), sizeof(Smem), s, a, pt, ptotal, ppadded);
+      hipLaunchKernelGGL((k_gemm_fwd_fast<F, true>), dim3(ppadded), dim3(NT_FAST), sizeof(Smem), s, a, pt, ptotal, ppadded);
       return hipGetLastError();
     });
   }
   return launch_fmt(a.format, [&](auto fmt) {
     constexpr int F = decltype(fmt)::value;
-    if (r4) hipLaunchKernelGGL((k_gemm_fwd_r4<F, false>), dim3(padded), dim3(NT_R4), sizeof(SmemR4), s, a, n_tiles, total, padded);
-    else if (fast) hipLaunchKernelGGL((k_gemm_fwd_fast<F, false>), dim3(padded), dim3(NT_FAST), sizeof(Smem), s, a, n_tiles, total, padded);
+    if (fast) hipLaunchKernelGGL((k_gemm_fwd_fast<F, false>), dim3(padded), dim3(NT_FAST), sizeof(Smem), s, a, n_tiles, total, padded);
     else hipLaunchKernelGGL((k_gemm_fwd<F, false>), dim3(padded), dim3(NTHREADS), sizeof(Smem), s, a, n_tiles, total, padded);
     return hipGetLastError();
   });
@@ -1863,21 +1382,6 @@ hipError_t gemm_dequant_init() {
   set((const void*)k_gemm_bwd_fast<WF_NF4>);
   set((const void*)k_gemm_bwd_fast<WF_NF4_DQ>);
   set((const void*)k_gemm_bwd_fast<WF_BF16>);
-  auto set4 = [&](const void* k) {
-    hipError_t r = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(SmemR4));
-    if (r != hipSuccess) e = r;
-  };
-  set4((const void*)k_gemm_fwd_r4<WF_NF4, false>);
-  set4((const void*)k_gemm_fwd_r4<WF_NF4, true>);
-  set4((const void*)k_gemm_fwd_r4<WF_NF4_DQ, false>);
-  set4((const void*)k_gemm_fwd_r4<WF_NF4_DQ, true>);
-  set4((const void*)k_gemm_fwd_r4<WF_BF16, false>);
-  set4((const void*)k_gemm_fwd_r4<WF_BF16, true>);
-  // the 4-wave kernel's embedded levels must be the host codebook, bit for bit
-  float lv[16];
-  nf4_codebook_host(lv);
-  for (int i = 0; i < 16; ++i)
-    if (__builtin_bit_cast(uint32_t, lv[i]) != kNF4LevelBits[i]) return hipErrorInvalidValue;
   return e;
 }
 
