@@ -136,7 +136,8 @@ def test_accumulate_adds():
 @pytest.mark.parametrize("n_layers", [1, 2])
 def test_outputs_may_alias_inputs(n_layers):
     """Y written over X (with the reference pass on) and dX written over dY give the same
-    bits as separate buffers."""
+    bits as separate buffers, dA and dB included: the down projection's dB reads dY on the
+    side stream, which must finish before the last layer writes dX over it."""
     torch = pytest.importorskip("torch")
     w = TOY
     x, dy = synth.activations(w)
@@ -152,12 +153,14 @@ def test_outputs_may_alias_inputs(n_layers):
     torch.cuda.synchronize()
     got = {"Y": run.from_dev_bf16(X), "Y_ref": run.from_dev_bf16(Yr), "dX": run.from_dev_bf16(D)}
     dA = [{p: run.dA[l][p].cpu().numpy() for p in H.PROJS} for l in range(n_layers)]
+    dB = [{p: run.dB[l][p].cpu().numpy() for p in H.PROJS} for l in range(n_layers)]
     run.close()
     for k in ("Y", "Y_ref", "dX"):
         assert np.array_equal(got[k].view(np.uint32), sep[k].view(np.uint32)), k
     for l in range(n_layers):
         for p in H.PROJS:
             assert np.array_equal(dA[l][p].view(np.uint32), sep["dA"][l][p].view(np.uint32)), (l, p)
+            assert np.array_equal(dB[l][p].view(np.uint32), sep["dB"][l][p].view(np.uint32)), (l, p)
 
 
 @pytest.mark.parametrize("batch,seq", [(3, 40), (2, 8)])
