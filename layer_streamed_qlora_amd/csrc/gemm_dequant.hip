@@ -621,6 +621,34 @@ __device__ __forceinline__ void mma_stage(const uint16_t* sa, const uint16_t* sw
   }
 }
 
+// The low-rank stage: only its first ks_n k16 steps hold non-zero columns (the rank
+// padded to 16, or 0 without adapters), so only those are multiplied; the work of all
+// four steps still runs (it fills the next stage).  ks_n is wave-uniform.
+template <int NT, class Work>
+__device__ __forceinline__ void mma_stage_n(const uint16_t* sa, const uint16_t* sw, f32x16_t (&acc)[4][Layout<NT>::JB],
+                                            int ks_n, Work&& work) {
+  constexpr int WNW = Layout<NT>::WNW, JB = Layout<NT>::JB;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave / WNW, wn = wave % WNW;
+  const uint16_t* pa = sa + (wm * 128 + (lane & 31)) * PITCH + (lane >> 5) * 8;
+  const uint16_t* pw = sw + (wn * (32 * JB) + (lane & 31)) * PITCH + (lane >> 5) * 8;
+#pragma unroll
+  for (int kk = 0; kk < BK / 16; ++kk) {
+    if (kk < ks_n) {
+      bf16x8_t fa[4], fb[JB];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) fa[i] = *reinterpret_cast<const bf16x8_t*>(pa + i * 32 * PITCH + kk * 16);
+#pragma unroll
+      for (int j = 0; j < JB; ++j) fb[j] = *reinterpret_cast<const bf16x8_t*>(pw + j * 32 * PITCH + kk * 16);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < JB; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    }
+    work(kk);
+  }
+}
+
 // Epilogue through LDS: half a tile (128 rows) at a time, each thread then moves
 // 4 consecutive columns per step with one 8- or 16-byte global access.
 // out(m, n) for m < M_lim, n < N_lim; a bf16 or float32 residual is added first; the
@@ -1108,12 +1136,14 @@ __global__ void __launch_bounds__(NT_FAST, 1) k_gemm_fwd_fast(FwdArgs args, int 
   // The two register sets alternate by unrolling two iterations: a copy between them
   // would wait on the loads still in flight into the source.  Every prefetch is issued
   // on every path (the compiler counts only loads that are always issued when it
-  // places its waits; a skipped-load branch makes it wait for every load in flight),
-  // and the iteration count is rounded up to even: an activation tile past K loads as
-  // zeros (out-of-range offset), W past K re-reads the last tile, so the padding
-  // iteration adds exact zeros.
+  // places its waits; a skipped-load branch makes it wait for every load in flight).
+  // Iteration 0, the low-rank stage, multiplies only its non-zero k steps; the K
+  // stages follow in pairs, and an odd count of them gets one padding stage: an
+  // activation tile past K loads as zeros (out-of-range offset), W past K re-reads the
+  // last tile, so the padding stage adds exact zeros.
   const int k_last = K - BK;
-  auto step = [&](int it, typename WFwdFast<FMT>::Regs& R) {
+  const int ext_cols = PAIRED ? (args.kx > 0 ? 2 * args.kx : 0) : (args.kx > 0 && G.bext != nullptr ? args.kx : 0);
+  auto step = [&](int it, typename WFwdFast<FMT>::Regs& R, auto low_rank) {
     // let the scheduler interleave the LDS and memory instructions with the MFMAs
     __builtin_amdgcn_iglp_opt(0);
     const int cur = it & 1;
@@ -1122,17 +1152,22 @@ __global__ void __launch_bounds__(NT_FAST, 1) k_gemm_fwd_fast(FwdArgs args, int 
     const int k_next = (it + 1) * BK;
     const bool past = k_next >= K;
     const float am = FMT == WF_BF16 ? 0.f : ws.absmax(R);
-    mma_stage<NT_FAST>(sm.u.k.a[cur], sm.u.k.w[cur], acc, [&](int q) {
+    auto work = [&](int q) {
       ra.store_q(na, q);
       ra.load_q_or_zero((uint32_t)k_next, q, past);
       ws.store_part(R, nw, sm.lut2, q, am);
-    });
+    };
+    if constexpr (decltype(low_rank)::value)
+      mma_stage_n<NT_FAST>(sm.u.k.a[cur], sm.u.k.w[cur], acc, (ext_cols + 15) / 16, work);
+    else
+      mma_stage<NT_FAST>(sm.u.k.a[cur], sm.u.k.w[cur], acc, work);
     ws.load(R, k_next + BK < k_last ? k_next + BK : k_last);
     __syncthreads();
   };
-  for (int it = 0; it < n_iter; it += 2) {
-    step(it, rw);
-    step(it + 1, rw_next);
+  step(0, rw, std::true_type{});
+  for (int it = 1; it < n_iter; it += 2) {
+    step(it, rw_next, std::false_type{});
+    step(it + 1, rw, std::false_type{});
   }
 
   if constexpr (PAIRED) {
@@ -1219,8 +1254,9 @@ __global__ void __launch_bounds__(NT_FAST, 1) k_gemm_bwd_fast(BwdArgs args, int 
   __syncthreads();
   const int n_iter = total_k + 1;
   // as in the forward kernel: two register sets for W alternating without copies,
-  // prefetches on every path, an even iteration count with a zero padding tile
-  auto step = [&](int it, typename WBwdFast<FMT>::Regs& R) {
+  // prefetches on every path, the low-rank stage multiplying only its non-zero k
+  // steps, then the K stages in pairs (one zero padding stage if their count is odd)
+  auto step = [&](int it, typename WBwdFast<FMT>::Regs& R, auto low_rank) {
     const int cur = it & 1;
     uint16_t* na = sm.u.k.a[cur ^ 1];
     uint16_t* nw = sm.u.k.w[cur ^ 1];
@@ -1229,17 +1265,22 @@ __global__ void __launch_bounds__(NT_FAST, 1) k_gemm_bwd_fast(BwdArgs args, int 
     { int s, k0; seg_of(past ? total_k - 1 : it + 1, s, k0); col = (uint32_t)(args.seg[s].a_col0 + k0); }
     const float a0 = FMT == WF_BF16 ? 0.f : ws.absmax(R, 0);
     const float a1 = FMT == WF_BF16 ? 0.f : ws.absmax(R, 1);
-    mma_stage<NT_FAST>(sm.u.k.a[cur], sm.u.k.w[cur], acc, [&](int q) {
+    auto work = [&](int q) {
       ra.store_q(na, q);
       ra.load_q_or_zero(col, q, past);
       ws.store_part(R, nw, sm.lut2, q, a0, a1);
-    });
+    };
+    if constexpr (decltype(low_rank)::value)
+      mma_stage_n<NT_FAST>(sm.u.k.a[cur], sm.u.k.w[cur], acc, (args.kx + 15) / 16, work);
+    else
+      mma_stage<NT_FAST>(sm.u.k.a[cur], sm.u.k.w[cur], acc, work);
     load_w(R, it + 2);
     __syncthreads();
   };
-  for (int it = 0; it < n_iter; it += 2) {
-    step(it, rw);
-    step(it + 1, rw_next);
+  step(0, rw, std::true_type{});
+  for (int it = 1; it < n_iter; it += 2) {
+    step(it, rw_next, std::false_type{});
+    step(it + 1, rw, std::false_type{});
   }
 
   Epi E;
