@@ -116,6 +116,19 @@ def test_llama8b_measured_configuration_sampled_sequence():
     sampled_sequence_case("llama8b", 2, 5)
 
 
+def test_qwen3b_configuration_sampled_sequence():
+    """Qwen2.5-3B shape with its bf16 base at its configuration, 4 x 1024 tokens: two
+    streamed layers, sequence 3 checked against the oracle."""
+    sampled_sequence_case("qwen3b", 2, 3)
+
+
+def test_qwen32b_throughput_configuration_sampled_sequence():
+    """Qwen2.5-32B shape (251.5 MB NF4 + double-quant layers) at its throughput
+    configuration, 2 x 1024 tokens: two streamed layers, sequence 1 checked against the
+    oracle."""
+    sampled_sequence_case("qwen32b", 2, 1)
+
+
 def test_qwen72b_dpo_configuration_sampled_sequence():
     """Qwen2.5-72B DPO shape at its configuration: 2 chosen / rejected pairs x 512 tokens
     with the adapters-off reference pass; layers 0 and 1, sequence 2 (the second pair's
