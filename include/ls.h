@@ -262,21 +262,25 @@ ls_status ls_forward(ls_ctx* ctx, const void* X, int32_t batch, int32_t seq, int
  */
 ls_status ls_backward(ls_ctx* ctx, const void* dY, void* dX, int32_t accumulate);
 
-/* ls_sync — wait for the copy stream, the compute stream and the library's side stream
- * (the copies run on a dedicated stream beside the compute: "Soup CLI fine-tunes
+/* ls_sync — wait for the copy stream, the compute stream and the library's side and
+ * recompute streams (the copies run on a dedicated stream beside the compute: "Soup CLI fine-tunes
  * Llama-3.1-8B on a 4 GB laptop GPU ...", second paragraph).  Returns the first
  * deferred HIP error, or LS_ERR_HIP with a message if a read from the LS_STORE_FILE
  * store failed; either makes the context's error sticky. */
 ls_status ls_sync(ls_ctx* ctx);
 
 /*
- * Profiling levels.  Timing is HIP events recorded on the compute stream around kernel
- * launches; each event is a packet in the stream and widens the gap before the next
- * kernel, so a timed run should record as few as it needs.
+ * Profiling levels.  Timing is HIP events recorded around kernel launches on the
+ * stream each runs on; each event is a packet in the stream and widens the gap before
+ * the next kernel, so a timed run should record as few as it needs.  The backward runs
+ * each layer's recompute on a stream of its own beside the previous layer's backward,
+ * so a recompute kernel's time includes the time it shares the GPU.
  *   LS_PROFILE_OFF:  no events.
  *   LS_PROFILE_ALL:  every launch (per-class times in ls_stats) and the copy / per-layer
  *                    compute intervals (overlap figures).
- *   LS_PROFILE_GEMM: only the forward dequant-GEMM launches (class LS_KC_GEMM_FWD).
+ *   LS_PROFILE_GEMM: only the forward pass's dequant-GEMM launches (class
+ *                    LS_KC_GEMM_FWD; the recompute's launches of that kernel, which
+ *                    share the GPU with the backward, are not timed).
  */
 enum { LS_PROFILE_OFF = 0, LS_PROFILE_ALL = 1, LS_PROFILE_GEMM = 2 };
 

@@ -49,8 +49,12 @@ struct LoraReg {
 struct DevPlan {
   uint64_t total = 0;
   uint64_t slots = 0, ck = 0, xref = 0;
-  uint64_t n1 = 0, qkv = 0, att = 0, hb = 0, n2 = 0, gu = 0, act = 0, rstd1 = 0, rstd2 = 0;
-  uint64_t hs = 0, gs = 0, lse = 0, dd = 0, o32 = 0, astats = 0;
+  // the activations a layer's forward or recompute writes and its backward reads: two
+  // sets, layer l using set l % 2, so that the recompute of layer l - 1 can run while
+  // the backward of layer l still reads its own
+  uint64_t n1[2] = {}, qkv[2] = {}, att[2] = {}, hb[2] = {}, n2[2] = {}, gu[2] = {}, act[2] = {};
+  uint64_t rstd1[2] = {}, rstd2[2] = {}, lse[2] = {}, o32[2] = {};
+  uint64_t hs = 0, gs = 0, dd = 0, astats = 0;
   uint64_t dya = 0, dyb = 0, dh32 = 0, dh16 = 0, dgu = 0, datt = 0, dqkv = 0, dqkv32 = 0, dn32 = 0;
   uint64_t dkv2 = 0;   // dk | dv of the second half of each kv head's q heads, float32
   uint64_t lora = 0, lora_per_layer = 0, partial = 0, partial_bytes = 0;
@@ -92,21 +96,23 @@ DevPlan make_plan(const ls_config& c, const BlobLayout& L) {
   P.slots = take(L.bytes * (uint64_t)P.n_slots);
   P.ck = take(2 * T * h * (uint64_t)c.n_layers);
   P.xref = take(2 * 2 * T * h);
-  P.n1 = take(2 * T * h);
-  P.qkv = take(2 * T * qkvd);
-  P.att = take(2 * T * qd);
-  P.hb = take(4 * T * h);             // residual stream after attention, float32
-  P.n2 = take(2 * T * h);
-  P.gu = take(4 * T * 2 * I);         // gate | up outputs, float32
-  P.act = take(2 * T * I);
-  P.rstd1 = take(4 * T);
-  P.rstd2 = take(4 * T);
+  for (int k = 0; k < 2; ++k) {
+    P.n1[k] = take(2 * T * h);
+    P.qkv[k] = take(2 * T * qkvd);
+    P.att[k] = take(2 * T * qd);
+    P.hb[k] = take(4 * T * h);        // residual stream after attention, float32
+    P.n2[k] = take(2 * T * h);
+    P.gu[k] = take(4 * T * 2 * I);    // gate | up outputs, float32
+    P.act[k] = take(2 * T * I);
+    P.rstd1[k] = take(4 * T);
+    P.rstd2[k] = take(4 * T);
+    P.lse[k] = take(4 * T * (uint64_t)c.n_heads);
+    P.o32[k] = take(4 * T * qd);
+  }
   // s X A^T of every layer, kept from the forward for the recompute and the dB products
   P.hs = take(2 * T * R7 * (uint64_t)c.n_layers);
   P.gs = take(2 * T * R7);
-  P.lse = take(4 * T * (uint64_t)c.n_heads);
   P.dd = take(4 * T * (uint64_t)c.n_heads);
-  P.o32 = take(4 * T * qd);
   // attention row statistics (max, sum) of every layer's forward, read by its recompute
   P.astats = take(8 * T * (uint64_t)c.n_heads * (uint64_t)c.n_layers);
   P.dya = take(2 * T * h);
@@ -212,6 +218,14 @@ struct ls_ctx {
   hipStream_t side = nullptr;
   hipEvent_t fork_ev = nullptr, join_ev = nullptr;
   bool side_pending = false;
+  // the backward's recompute stream: the recompute of layer l - 1 runs on it while the
+  // compute stream runs the backward of layer l.  Per activation set k (layer % 2):
+  // rec_done[k] after a recompute, bp_done[k] after the backward that read the set,
+  // side_done[k] after that backward's adapter-gradient reductions
+  hipStream_t rs = nullptr;
+  hipEvent_t rec_done[2] = {}, bp_done[2] = {}, side_done[2] = {};
+  bool bp_rec[2] = {}, side_rec[2] = {};
+  bool in_recompute = false;            // enqueueing a recompute (LS_PROFILE_GEMM skips it)
   std::vector<uint8_t*> host;
   std::vector<char> staged;
   uint8_t* dbase = nullptr;
@@ -295,7 +309,8 @@ struct KTimer {
   hipStream_t s;
   KTimer(ls_ctx* ctx, int k, double f, double b, hipStream_t st = nullptr)
       : c(ctx), cls(k), flop(f), bytes(b),
-        on(ctx->cfg.profile == LS_PROFILE_ALL || (ctx->cfg.profile == LS_PROFILE_GEMM && k == LS_KC_GEMM_FWD)),
+        on(ctx->cfg.profile == LS_PROFILE_ALL ||
+           (ctx->cfg.profile == LS_PROFILE_GEMM && k == LS_KC_GEMM_FWD && !ctx->in_recompute)),
         s(st ? st : ctx->cs) {
     if (on) {
       hipEvent_t e;
@@ -361,6 +376,15 @@ void collect_profile(ls_ctx* c) {
   double last = 0.0;
   for (auto& iv : P.copies) { cp.push_back({el(P.origin, iv.first), el(P.origin, iv.second)}); last = std::max(last, cp.back().second); }
   for (auto& iv : P.computes) { cm.push_back({el(P.origin, iv.first), el(P.origin, iv.second)}); last = std::max(last, cm.back().second); }
+  // compute intervals of the compute and the recompute stream overlap each other: merge
+  // them into their union before measuring the overlap with the copies
+  std::sort(cm.begin(), cm.end());
+  std::vector<std::pair<double, double>> um;
+  for (auto& a : cm) {
+    if (!um.empty() && a.first <= um.back().second) um.back().second = std::max(um.back().second, a.second);
+    else um.push_back(a);
+  }
+  cm.swap(um);
   double cps = 0, cms = 0, ov = 0;
   for (auto& a : cp) cps += a.second - a.first;
   for (auto& a : cm) cms += a.second - a.first;
@@ -493,17 +517,18 @@ ls_status ensure_copy(ls_ctx* c, int l) {
   return LS_OK;
 }
 
-// The compute stream waits for piece g of layer l (use_layer: every piece).
-ls_status use_piece(ls_ctx* c, int l, int g) {
+// Stream s (the compute stream unless given) waits for piece g of layer l (use_layer:
+// every piece).
+ls_status use_piece(ls_ctx* c, int l, int g, hipStream_t s = nullptr) {
   if (c->cfg.resident) return LS_OK;
   const int e = (l % c->cfg.n_buffers) * kPieces + g;
-  if (c->ready_rec[e]) HIPCHK(c, hipStreamWaitEvent(c->cs, c->ready[e], 0));
+  if (c->ready_rec[e]) HIPCHK(c, hipStreamWaitEvent(s ? s : c->cs, c->ready[e], 0));
   return LS_OK;
 }
 
-ls_status use_layer(ls_ctx* c, int l) {
+ls_status use_layer(ls_ctx* c, int l, hipStream_t s = nullptr) {
   for (int g = 0; g < kPieces; ++g)
-    if (ls_status st = use_piece(c, l, g)) return st;
+    if (ls_status st = use_piece(c, l, g, s)) return st;
   return LS_OK;
 }
 
@@ -516,18 +541,32 @@ ls_status release_layer(ls_ctx* c, int l) {
   return LS_OK;
 }
 
-// Per-piece waits of one pass over a split layer: the compute stream waits for a piece
+// Per-piece waits of one pass over a split layer: the pass's stream waits for a piece
 // just before its first reader.  Disabled when the caller waited for the whole layer.
 struct Fence {
   int l = 0;
   bool wait = false;
 };
-ls_status fence_wait(ls_ctx* c, const Fence& f, int g) { return f.wait ? use_piece(c, f.l, g) : LS_OK; }
+ls_status fence_wait(ls_ctx* c, const Fence& f, int g, hipStream_t s) { return f.wait ? use_piece(c, f.l, g, s) : LS_OK; }
 
 // ------------------------------------------------------------------ executor
 // s X A^T of layer l, bf16 [T, 7 r16] (row stride 7 r16), layers max_tokens rows apart
 uint16_t* hs_of(const ls_ctx* c, int l) {
   return c->dp<uint16_t>(c->plan.hs) + (uint64_t)l * c->cfg.max_tokens * 7 * r16_of(c->cfg);
+}
+
+// The activation workspaces of set k (layer l uses set l % 2).
+struct Acts {
+  uint16_t *n1, *qkv, *att, *n2, *act;
+  float *hb, *gu, *rstd1, *rstd2, *lse, *o32;
+};
+Acts acts_of(ls_ctx* c, int l) {
+  const int k = l & 1;
+  const DevPlan& P = c->plan;
+  return Acts{c->dp<uint16_t>(P.n1[k]), c->dp<uint16_t>(P.qkv[k]), c->dp<uint16_t>(P.att[k]),
+              c->dp<uint16_t>(P.n2[k]), c->dp<uint16_t>(P.act[k]), c->dp<float>(P.hb[k]),
+              c->dp<float>(P.gu[k]), c->dp<float>(P.rstd1[k]), c->dp<float>(P.rstd2[k]),
+              c->dp<float>(P.lse[k]), c->dp<float>(P.o32[k])};
 }
 
 struct Dims {
@@ -631,13 +670,13 @@ ls_status lora_down(ls_ctx* c, int l, const Dims& d, const uint16_t* x, int ldx,
 
 double fwd_gemm_flop(const Dims& d, int n_out, int K, bool lora) { return 2.0 * d.T * n_out * K + (lora ? 2.0 * d.T * n_out * d.r : 0.0); }
 
-AttnArgs attn_args(ls_ctx* c, const Dims& d, const uint16_t* qkv, uint16_t* out) {
+AttnArgs attn_args(const Dims& d, const uint16_t* qkv, uint16_t* out, float* lse) {
   AttnArgs a;
   a.qkv = qkv; a.ldqkv = d.qkvd; a.qd = d.qd; a.kvd = d.kvd;
   a.batch = d.batch; a.S = d.seq; a.hq = d.hq; a.hkv = d.hkv; a.hd = d.hd;
   a.scale = 1.0f / std::sqrt((float)d.hd);
   a.out = out; a.ldo = d.qd;
-  a.lse = c->dp<float>(c->plan.lse);
+  a.lse = lse;
   return a;
 }
 
@@ -645,24 +684,23 @@ AttnArgs attn_args(ls_ctx* c, const Dims& d, const uint16_t* qkv, uint16_t* out)
 // backward uses to rebuild P; out32 (nullable) keeps O before rounding for the backward.
 // stats_out / stats_in: the layer's per-row softmax statistics, kept by the forward and
 // read back by the recompute so that it skips the statistics pass.
-ls_status attn_fwd(ls_ctx* c, const Dims& d, const uint16_t* qkv, uint16_t* out, float* out32, float2* stats_out,
-                   const float2* stats_in) {
+ls_status attn_fwd(ls_ctx* c, const Dims& d, const uint16_t* qkv, uint16_t* out, float* lse, float* out32,
+                   float2* stats_out, const float2* stats_in, hipStream_t s) {
   const double fl = (stats_in ? 4.0 : 6.0) * d.batch * d.hq * (double)d.seq * (d.seq + 1) / 2 * d.hd;
-  KTimer kt(c, LS_KC_ATTN, fl, 2.0 * d.T * (d.qkvd + d.qd) + 4.0 * d.T * d.hq + (out32 ? 4.0 * d.T * d.qd : 0.0));
-  AttnArgs a = attn_args(c, d, qkv, out);
+  KTimer kt(c, LS_KC_ATTN, fl, 2.0 * d.T * (d.qkvd + d.qd) + 4.0 * d.T * d.hq + (out32 ? 4.0 * d.T * d.qd : 0.0), s);
+  AttnArgs a = attn_args(d, qkv, out, lse);
   a.out32 = out32;
   a.stats_out = stats_out;
   a.stats_in = stats_in;
-  HIPCHK(c, launch_attn_fwd(a, c->cs));
+  HIPCHK(c, launch_attn_fwd(a, s));
   return LS_OK;
 }
 
 // Attention backward from dO (datt), O (att) and the log-sum-exp of the recompute ->
 // float32 dq, dk, dv in dqkv32 (dk, dv summed over a kv head's q heads, fixed order).
-ls_status attn_bwd(ls_ctx* c, const Dims& d, const uint16_t* qkv, const uint16_t* out, const uint16_t* dout,
-                   float* dqkv32) {
-  AttnArgs a = attn_args(c, d, qkv, const_cast<uint16_t*>(out));
-  a.out32 = c->dp<float>(c->plan.o32);
+ls_status attn_bwd(ls_ctx* c, const Dims& d, const Acts& x, const uint16_t* dout, float* dqkv32) {
+  AttnArgs a = attn_args(d, x.qkv, x.att, x.lse);
+  a.out32 = x.o32;
   a.dout = dout; a.lddo = d.qd;
   a.dd = c->dp<float>(c->plan.dd);
   a.dqkv = dqkv32; a.lddqkv = d.qkvd;
@@ -680,18 +718,22 @@ enum FwdMode { MODE_FWD = 0, MODE_RECOMPUTE = 1 };
 // One decoder layer forward from x_in (bf16 [T, h]).  MODE_FWD writes x_out; the
 // recompute keeps every intermediate and skips the down projection, whose output
 // the backward does not need.
+// One layer's forward (MODE_FWD) or the backward's recompute of it (MODE_RECOMPUTE:
+// no down projection, gate and up kept in float32, attention output kept in float32),
+// every launch on stream s, into the layer's activation set.
 ls_status layer_forward(ls_ctx* c, int l, const uint8_t* blob, const Dims& d, const uint16_t* x_in, uint16_t* x_out,
-                        bool lora, FwdMode mode, const Fence& fc) {
+                        bool lora, FwdMode mode, const Fence& fc, hipStream_t s) {
   const ls_config& g = c->cfg;
   const int fmt = wformat(g);
   const float* lv = c->dp<float>(c->plan.levels);
-  uint16_t* n1 = c->dp<uint16_t>(c->plan.n1);
-  uint16_t* qkv = c->dp<uint16_t>(c->plan.qkv);
-  uint16_t* att = c->dp<uint16_t>(c->plan.att);
-  float* hb = c->dp<float>(c->plan.hb);
-  uint16_t* n2 = c->dp<uint16_t>(c->plan.n2);
-  float* gu = c->dp<float>(c->plan.gu);
-  uint16_t* act = c->dp<uint16_t>(c->plan.act);
+  const Acts x = acts_of(c, l);
+  uint16_t* n1 = x.n1;
+  uint16_t* qkv = x.qkv;
+  uint16_t* att = x.att;
+  float* hb = x.hb;
+  uint16_t* n2 = x.n2;
+  float* gu = x.gu;
+  uint16_t* act = x.act;
   uint16_t* hs = hs_of(c, l);
   // the recompute reads the forward's s X A^T of this layer (same inputs, same kernel)
   const bool down = lora && mode == MODE_FWD;
@@ -700,10 +742,10 @@ ls_status layer_forward(ls_ctx* c, int l, const uint8_t* blob, const Dims& d, co
   const double tb = 2.0 * d.T;
   ls_status fst;
 
-  if ((fst = fence_wait(c, fc, 0))) return fst;
+  if ((fst = fence_wait(c, fc, 0, s))) return fst;
   {
-    KTimer kt(c, LS_KC_GLUE, 0.0, 2 * tb * d.h);
-    HIPCHK(c, launch_rmsnorm_fwd(x_in, nullptr, g1, n1, c->dp<float>(c->plan.rstd1), d.T, d.h, g.rms_eps, c->cs));
+    KTimer kt(c, LS_KC_GLUE, 0.0, 2 * tb * d.h, s);
+    HIPCHK(c, launch_rmsnorm_fwd(x_in, nullptr, g1, n1, x.rstd1, d.T, d.h, g.rms_eps, s));
   }
   if (down) { ls_status st = lora_down(c, l, d, n1, d.h, LS_PROJ_Q, 3, d.h); if (st) return st; }
   {
@@ -721,17 +763,17 @@ ls_status layer_forward(ls_ctx* c, int l, const uint8_t* blob, const Dims& d, co
     // q and k leave the GEMM rotated (rotary embedding applied in float32 before rounding)
     f.rope_tab = c->dp<float2>(c->plan.rope); f.rope_cols = d.qd + d.kvd; f.seq = d.seq; f.head_dim = d.hd;
     KTimer kt(c, LS_KC_GEMM_FWD, fwd_gemm_flop(d, d.qkvd, d.h, lora),
-              tb * d.h + wbytes(c, 0) + wbytes(c, 1) + wbytes(c, 2) + tb * d.qkvd);
-    HIPCHK(c, launch_gemm_fwd(f, c->cs));
+              tb * d.h + wbytes(c, 0) + wbytes(c, 1) + wbytes(c, 2) + tb * d.qkvd, s);
+    HIPCHK(c, launch_gemm_fwd(f, s));
   }
   {
     float2* stats = c->dp<float2>(c->plan.astats) + (uint64_t)l * c->cfg.max_tokens * c->cfg.n_heads;
-    ls_status st = attn_fwd(c, d, qkv, att, mode == MODE_RECOMPUTE ? c->dp<float>(c->plan.o32) : nullptr,
-                            mode == MODE_FWD && lora ? stats : nullptr, mode == MODE_RECOMPUTE ? stats : nullptr);
+    ls_status st = attn_fwd(c, d, qkv, att, x.lse, mode == MODE_RECOMPUTE ? x.o32 : nullptr,
+                            mode == MODE_FWD && lora ? stats : nullptr, mode == MODE_RECOMPUTE ? stats : nullptr, s);
     if (st) return st;
   }
   if (down) { ls_status st = lora_down(c, l, d, att, d.qd, LS_PROJ_O, 1, d.qd); if (st) return st; }
-  if ((fst = fence_wait(c, fc, 1))) return fst;
+  if ((fst = fence_wait(c, fc, 1, s))) return fst;
   {
     FwdArgs f;
     f.x = att; f.ldx = d.qd; f.M = d.T; f.K = d.qd; f.n_groups = 1;
@@ -741,14 +783,14 @@ ls_status layer_forward(ls_ctx* c, int l, const uint8_t* blob, const Dims& d, co
     f.aext = hs; f.ldaext = d.R7; f.kx = lora ? d.r16 : 0;
     f.resid = x_in; f.ldr = d.h;
     f.y32 = hb; f.ldy = d.h; f.levels = lv; f.format = fmt;
-    KTimer kt(c, LS_KC_GEMM_FWD, fwd_gemm_flop(d, d.h, d.qd, lora), tb * d.qd + wbytes(c, 3) + 3 * tb * d.h);
-    HIPCHK(c, launch_gemm_fwd(f, c->cs));
+    KTimer kt(c, LS_KC_GEMM_FWD, fwd_gemm_flop(d, d.h, d.qd, lora), tb * d.qd + wbytes(c, 3) + 3 * tb * d.h, s);
+    HIPCHK(c, launch_gemm_fwd(f, s));
   }
   {
-    KTimer kt(c, LS_KC_GLUE, 0.0, 2 * tb * d.h);
-    HIPCHK(c, launch_rmsnorm_fwd(nullptr, hb, g2, n2, c->dp<float>(c->plan.rstd2), d.T, d.h, g.rms_eps, c->cs));
+    KTimer kt(c, LS_KC_GLUE, 0.0, 2 * tb * d.h, s);
+    HIPCHK(c, launch_rmsnorm_fwd(nullptr, hb, g2, n2, x.rstd2, d.T, d.h, g.rms_eps, s));
   }
-  if ((fst = fence_wait(c, fc, 2))) return fst;
+  if ((fst = fence_wait(c, fc, 2, s))) return fst;
   if (down) { ls_status st = lora_down(c, l, d, n2, d.h, LS_PROJ_GATE, 2, d.h); if (st) return st; }
   const bool fuse_swiglu = 2 * d.r16 <= 64;
   {
@@ -772,16 +814,16 @@ ls_status layer_forward(ls_ctx* c, int l, const uint8_t* blob, const Dims& d, co
       f.y32 = gu; f.ldy = 2 * d.I;
     }
     const double out_bytes = fuse_swiglu ? tb * d.I + (mode == MODE_RECOMPUTE ? 2 * tb * 2 * d.I : 0.0) : 2 * tb * 2 * d.I;
-    KTimer kt(c, LS_KC_GEMM_FWD, fwd_gemm_flop(d, 2 * d.I, d.h, lora), tb * d.h + wbytes(c, 4) + wbytes(c, 5) + out_bytes);
-    HIPCHK(c, launch_gemm_fwd(f, c->cs));
+    KTimer kt(c, LS_KC_GEMM_FWD, fwd_gemm_flop(d, 2 * d.I, d.h, lora), tb * d.h + wbytes(c, 4) + wbytes(c, 5) + out_bytes, s);
+    HIPCHK(c, launch_gemm_fwd(f, s));
   }
   if (!fuse_swiglu) {
-    KTimer kt(c, LS_KC_GLUE, 0.0, 5 * tb * d.I);
-    HIPCHK(c, launch_swiglu_fwd(gu, d.I, act, d.T, c->cs));
+    KTimer kt(c, LS_KC_GLUE, 0.0, 5 * tb * d.I, s);
+    HIPCHK(c, launch_swiglu_fwd(gu, d.I, act, d.T, s));
   }
   if (down) { ls_status st = lora_down(c, l, d, act, d.I, LS_PROJ_DOWN, 1, d.I); if (st) return st; }
   if (mode == MODE_RECOMPUTE) return LS_OK;
-  if ((fst = fence_wait(c, fc, 3))) return fst;
+  if ((fst = fence_wait(c, fc, 3, s))) return fst;
   {
     FwdArgs f;
     f.x = act; f.ldx = d.I; f.M = d.T; f.K = d.I; f.n_groups = 1;
@@ -791,8 +833,8 @@ ls_status layer_forward(ls_ctx* c, int l, const uint8_t* blob, const Dims& d, co
     f.aext = hs; f.ldaext = d.R7; f.kx = lora ? d.r16 : 0;
     f.resid32 = hb; f.ldr = d.h;
     f.y = x_out; f.ldy = d.h; f.levels = lv; f.format = fmt;
-    KTimer kt(c, LS_KC_GEMM_FWD, fwd_gemm_flop(d, d.h, d.I, lora), tb * d.I + wbytes(c, 6) + 3 * tb * d.h);
-    HIPCHK(c, launch_gemm_fwd(f, c->cs));
+    KTimer kt(c, LS_KC_GEMM_FWD, fwd_gemm_flop(d, d.h, d.I, lora), tb * d.I + wbytes(c, 6) + 3 * tb * d.h, s);
+    HIPCHK(c, launch_gemm_fwd(f, s));
   }
   return LS_OK;
 }
@@ -880,23 +922,23 @@ ls_status join_side(ls_ctx* c) {
   return LS_OK;
 }
 
+// The backward of layer l on the compute stream, after its recompute (layer_forward in
+// MODE_RECOMPUTE, enqueued by the caller) filled the layer's activation set.
 ls_status layer_backward(ls_ctx* c, int l, const uint8_t* blob, const Dims& d, const uint16_t* x_in, const uint16_t* dy,
                          uint16_t* dx, float beta, const Fence& fc) {
-  // the previous layer's reductions read activations this recompute overwrites
+  // the previous layer's reductions read the gradient buffers this layer overwrites
   ls_status st = join_side(c);
-  if (st) return st;
-  st = layer_forward(c, l, blob, d, x_in, nullptr, true, MODE_RECOMPUTE, fc);   // waits for pieces 0 .. 2
   if (st) return st;
   const ls_config& g = c->cfg;
   const int fmt = wformat(g);
   const float* lv = c->dp<float>(c->plan.levels);
-  uint16_t* n1 = c->dp<uint16_t>(c->plan.n1);
-  uint16_t* qkv = c->dp<uint16_t>(c->plan.qkv);
-  uint16_t* att = c->dp<uint16_t>(c->plan.att);
-  float* hb = c->dp<float>(c->plan.hb);
-  uint16_t* n2 = c->dp<uint16_t>(c->plan.n2);
-  float* gu = c->dp<float>(c->plan.gu);
-  uint16_t* act = c->dp<uint16_t>(c->plan.act);
+  const Acts x = acts_of(c, l);
+  uint16_t* n1 = x.n1;
+  uint16_t* att = x.att;
+  float* hb = x.hb;
+  uint16_t* n2 = x.n2;
+  float* gu = x.gu;
+  uint16_t* act = x.act;
   uint16_t* gs = c->dp<uint16_t>(c->plan.gs);
   float* dh32 = c->dp<float>(c->plan.dh32);
   uint16_t* dh16 = c->dp<uint16_t>(c->plan.dh16);
@@ -913,7 +955,7 @@ ls_status layer_backward(ls_ctx* c, int l, const uint8_t* blob, const Dims& d, c
   // ---- down: y = h + act W_d^T + LoRA
   if ((st = lora_grads_G(c, l, d, LS_PROJ_DOWN, 1, dy, d.h))) return st;
   if ((st = lora_grads_AB(c, l, d, LS_PROJ_DOWN, 1, dy, d.h, act, d.I, beta))) return st;
-  if ((st = fence_wait(c, fc, 3))) return st;
+  if ((st = fence_wait(c, fc, 3, c->cs))) return st;
   {
     BwdArgs b;
     b.dy = dy; b.lddy = d.h; b.M = d.T; b.N = d.I; b.n_segs = 1;
@@ -941,7 +983,7 @@ ls_status layer_backward(ls_ctx* c, int l, const uint8_t* blob, const Dims& d, c
   }
   {
     KTimer kt(c, LS_KC_GLUE, 0.0, 4 * tb * d.h);
-    HIPCHK(c, launch_rmsnorm_bwd(dn32, nullptr, hb, g2, c->dp<float>(c->plan.rstd2), nullptr, dy, dh32, dh16, d.T, d.h, c->cs));
+    HIPCHK(c, launch_rmsnorm_bwd(dn32, nullptr, hb, g2, x.rstd2, nullptr, dy, dh32, dh16, d.T, d.h, c->cs));
   }
   // ---- o: h = x + att W_o^T + LoRA
   if ((st = lora_grads_G(c, l, d, LS_PROJ_O, 1, dh16, d.h))) return st;
@@ -956,7 +998,7 @@ ls_status layer_backward(ls_ctx* c, int l, const uint8_t* blob, const Dims& d, c
     KTimer kt(c, LS_KC_GEMM_BWD, bwd_flop(d.h, d.qd), tb * d.h + wbytes(c, 3) + tb * d.qd);
     HIPCHK(c, launch_gemm_bwd(b, c->cs));
   }
-  if ((st = attn_bwd(c, d, qkv, att, datt, dqkv32))) return st;
+  if ((st = attn_bwd(c, d, x, datt, dqkv32))) return st;
   {
     KTimer kt(c, LS_KC_GLUE, 0.0, 3 * tb * d.qkvd);
     // dK | dV of the second half of the q heads join here (see attn_bwd)
@@ -987,7 +1029,18 @@ ls_status layer_backward(ls_ctx* c, int l, const uint8_t* blob, const Dims& d, c
   }
   {
     KTimer kt(c, LS_KC_GLUE, 0.0, 4 * tb * d.h);
-    HIPCHK(c, launch_rmsnorm_bwd(dn32, x_in, nullptr, g1, c->dp<float>(c->plan.rstd1), dh32, nullptr, nullptr, dx, d.T, d.h, c->cs));
+    HIPCHK(c, launch_rmsnorm_bwd(dn32, x_in, nullptr, g1, x.rstd1, dh32, nullptr, nullptr, dx, d.T, d.h, c->cs));
+  }
+  // the set is free for the recompute of layer l - 2 once this backward and its
+  // reductions are done with it
+  const int k = l & 1;
+  HIPCHK(c, hipEventRecord(c->bp_done[k], c->cs));
+  c->bp_rec[k] = true;
+  if (c->side_pending) {
+    HIPCHK(c, hipEventRecord(c->side_done[k], c->side));
+    c->side_rec[k] = true;
+  } else {
+    c->side_rec[k] = false;
   }
   return LS_OK;
 }
@@ -1089,11 +1142,23 @@ ls_status ls_create(const ls_config* cfg_in, void* compute_stream, void* copy_st
     c->err = "side stream creation failed";
     return bail(LS_ERR_HIP);
   }
+  if (hipStreamCreateWithFlags(&c->rs, hipStreamNonBlocking) != hipSuccess) {
+    c->rs = nullptr;
+    c->err = "recompute stream creation failed";
+    return bail(LS_ERR_HIP);
+  }
   if (hipEventCreateWithFlags(&c->fork_ev, hipEventDisableTiming) != hipSuccess ||
       hipEventCreateWithFlags(&c->join_ev, hipEventDisableTiming) != hipSuccess) {
     c->err = "event creation failed";
     return bail(LS_ERR_HIP);
   }
+  for (int k = 0; k < 2; ++k)
+    if (hipEventCreateWithFlags(&c->rec_done[k], hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&c->bp_done[k], hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&c->side_done[k], hipEventDisableTiming) != hipSuccess) {
+      c->err = "event creation failed";
+      return bail(LS_ERR_HIP);
+    }
   if (gemm_dequant_init() != hipSuccess) { c->err = "kernel attribute setup failed"; return bail(LS_ERR_HIP); }
   if (const char* e = getenv("LS_DEBUG_POISON")) c->dbg_poison = e[0] == '1';
   if (const char* e = getenv("LS_DEBUG_COPY_DELAY_US")) c->dbg_delay_us = (uint32_t)std::min(1000000L, std::max(0L, atol(e)));
@@ -1275,13 +1340,13 @@ ls_status ls_forward(ls_ctx* c, const void* X, int32_t batch, int32_t seq, int32
       if (lora && (st = prep_lora(c, l, d))) return st;
       uint16_t* out = l + 1 < L ? ckpt(c, l + 1) : (uint16_t*)Y;
       const Fence f1{l, split};
-      if ((st = layer_forward(c, l, blob, d, ckpt(c, l), out, lora, MODE_FWD, f1))) return st;
+      if ((st = layer_forward(c, l, blob, d, ckpt(c, l), out, lora, MODE_FWD, f1, c->cs))) return st;
       if (Y_ref) {
         // layer 0 reads the checkpoint copy of X, so Y may alias X
         const uint16_t* rin = l == 0 ? ckpt(c, 0) : xr[(l - 1) & 1];
         uint16_t* rout = l + 1 < L ? xr[l & 1] : (uint16_t*)Y_ref;
         const Fence f2{l, false};
-        if ((st = layer_forward(c, l, blob, d, rin, rout, false, MODE_FWD, f2))) return st;
+        if ((st = layer_forward(c, l, blob, d, rin, rout, false, MODE_FWD, f2, c->cs))) return st;
       }
     }
     if ((st = release_layer(c, l))) return st;
@@ -1314,16 +1379,46 @@ ls_status ls_backward(ls_ctx* c, const void* dY, void* dX, int32_t accumulate) {
   uint16_t* ping[2] = {c->dp<uint16_t>(c->plan.dya), c->dp<uint16_t>(c->plan.dyb)};
   const uint16_t* cur = (const uint16_t*)dY;
   ls_status st;
+  // The recompute of layer l runs on the recompute stream: it waits for the layer's
+  // pieces and for its activation set to be free (the backward of layer l + 2 and that
+  // backward's reductions done with it).  The backward of layer l, on the compute
+  // stream, waits for its recompute.  The recompute of layer l - 1 is enqueued before
+  // the backward of layer l, so the two run side by side.  Everything the forward left
+  // (checkpoints, s X A^T, row statistics, the activation sets) is ordered before the
+  // first recompute by an event on the compute stream.
+  HIPCHK(c, hipEventRecord(c->fork_ev, c->cs));
+  HIPCHK(c, hipStreamWaitEvent(c->rs, c->fork_ev, 0));
+  auto recompute = [&](int l) -> ls_status {
+    const int k = l & 1;
+    if (c->bp_rec[k]) HIPCHK(c, hipStreamWaitEvent(c->rs, c->bp_done[k], 0));
+    if (c->side_rec[k]) HIPCHK(c, hipStreamWaitEvent(c->rs, c->side_done[k], 0));
+    const bool split = n_pieces(c, l) > 1;
+    ls_status s2;
+    if (!split && (s2 = use_layer(c, l, c->rs))) return s2;
+    {
+      Span sp(c, c->rs, false);
+      const Fence f{l, split};   // pieces 0 .. 2
+      c->in_recompute = true;
+      s2 = layer_forward(c, l, slot_ptr(c, l), d, ckpt(c, l), nullptr, true, MODE_RECOMPUTE, f, c->rs);
+      c->in_recompute = false;
+      if (s2) return s2;
+    }
+    HIPCHK(c, hipEventRecord(c->rec_done[k], c->rs));
+    return LS_OK;
+  };
   if ((st = ensure_copy(c, L - 1))) return st;
+  if ((st = recompute(L - 1))) return st;
   for (int l = L - 1; l >= 0; --l) {
     for (int k = 1; k < c->cfg.n_buffers && l - k >= 0; ++k)
       if ((st = ensure_copy(c, l - k))) return st;
+    if (l >= 1 && (st = recompute(l - 1))) return st;
     const bool split = n_pieces(c, l) > 1;
+    HIPCHK(c, hipStreamWaitEvent(c->cs, c->rec_done[l & 1], 0));
     if (!split && (st = use_layer(c, l))) return st;
     uint16_t* out = l == 0 ? (uint16_t*)dX : ping[l & 1];
     {
       Span sp(c, c->cs, false);
-      const Fence f{l, split};
+      const Fence f{l, split};   // piece 3
       if ((st = layer_backward(c, l, slot_ptr(c, l), d, ckpt(c, l), cur, out, beta, f))) return st;
     }
     if ((st = release_layer(c, l))) return st;
@@ -1337,6 +1432,7 @@ ls_status ls_sync(ls_ctx* c) {
   if (c->sticky != LS_OK) return c->sticky;
   HIPCHK(c, hipStreamSynchronize(c->ps));
   HIPCHK(c, hipStreamSynchronize(c->side));
+  HIPCHK(c, hipStreamSynchronize(c->rs));
   HIPCHK(c, hipStreamSynchronize(c->cs));
   HIPCHK(c, hipGetLastError());
   c->in_flight = false;
@@ -1364,9 +1460,15 @@ void ls_destroy(ls_ctx* c) {
   if (c->cs) (void)hipStreamSynchronize(c->cs);
   if (c->ps) (void)hipStreamSynchronize(c->ps);
   if (c->side) (void)hipStreamSynchronize(c->side);
+  if (c->rs) (void)hipStreamSynchronize(c->rs);
   for (auto e : c->prof.pool) (void)hipEventDestroy(e);
   if (c->fork_ev) (void)hipEventDestroy(c->fork_ev);
   if (c->join_ev) (void)hipEventDestroy(c->join_ev);
+  for (int k = 0; k < 2; ++k) {
+    if (c->rec_done[k]) (void)hipEventDestroy(c->rec_done[k]);
+    if (c->bp_done[k]) (void)hipEventDestroy(c->bp_done[k]);
+    if (c->side_done[k]) (void)hipEventDestroy(c->side_done[k]);
+  }
   for (auto e : c->ready) if (e) (void)hipEventDestroy(e);
   for (auto e : c->consumed) if (e) (void)hipEventDestroy(e);
   if (c->dbase) (void)hipFree(c->dbase);
@@ -1379,6 +1481,7 @@ void ls_destroy(ls_ctx* c) {
   if (c->own_cs && c->cs) (void)hipStreamDestroy(c->cs);
   if (c->own_ps && c->ps) (void)hipStreamDestroy(c->ps);
   if (c->side) (void)hipStreamDestroy(c->side);
+  if (c->rs) (void)hipStreamDestroy(c->rs);
   delete c;
 }
 
@@ -1432,7 +1535,7 @@ ls_status ls_base_gemm(ls_ctx* c, int32_t layer, int32_t group, int32_t transpos
     if (group == 2 && 2 * d.r16 <= 64) {
       // the forward's paired kernel: act is written to the workspace, gate and up in
       // float32 to out
-      f.swiglu = 1; f.y = c->dp<uint16_t>(c->plan.act); f.ldy = d.I;
+      f.swiglu = 1; f.y = c->dp<uint16_t>(c->plan.act[0]); f.ldy = d.I;
       f.gu32 = out; f.ldgu = out_w;
     } else {
       f.y32 = out; f.ldy = out_w;
