@@ -274,10 +274,12 @@ ls_status ls_sync(ls_ctx* ctx);
  * stream each runs on; each event is a packet in the stream and widens the gap before
  * the next kernel, so a timed run should record as few as it needs.  The backward runs
  * each layer's recompute on a stream of its own beside the previous layer's backward,
- * so a recompute kernel's time includes the time it shares the GPU.
+ * where a kernel's time would include the time it shares the GPU.
  *   LS_PROFILE_OFF:  no events.
  *   LS_PROFILE_ALL:  every launch (per-class times in ls_stats) and the copy / per-layer
- *                    compute intervals (overlap figures).
+ *                    compute intervals (overlap figures); the backward then runs each
+ *                    recompute after the previous layer's backward, so that no
+ *                    recompute kernel shares the GPU with another layer's backward.
  *   LS_PROFILE_GEMM: only the forward pass's dequant-GEMM launches (class
  *                    LS_KC_GEMM_FWD; the recompute's launches of that kernel, which
  *                    share the GPU with the backward, are not timed).

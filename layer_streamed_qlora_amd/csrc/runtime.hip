@@ -1385,9 +1385,16 @@ ls_status ls_backward(ls_ctx* c, const void* dY, void* dX, int32_t accumulate) {
   // stream, waits for its recompute.  The recompute of layer l - 1 is enqueued before
   // the backward of layer l, so the two run side by side.  Everything the forward left
   // (checkpoints, s X A^T, row statistics, the activation sets) is ordered before the
-  // first recompute by an event on the compute stream.
-  HIPCHK(c, hipEventRecord(c->fork_ev, c->cs));
-  HIPCHK(c, hipStreamWaitEvent(c->rs, c->fork_ev, 0));
+  // first recompute by an event on the compute stream.  With LS_PROFILE_ALL every
+  // recompute instead follows the backward before it (one kernel at a time), so that
+  // each kernel's timing is its own.
+  const bool serial = c->cfg.profile == LS_PROFILE_ALL;
+  auto rs_after_cs = [&]() -> ls_status {
+    HIPCHK(c, hipEventRecord(c->fork_ev, c->cs));
+    HIPCHK(c, hipStreamWaitEvent(c->rs, c->fork_ev, 0));
+    return LS_OK;
+  };
+  if ((st = rs_after_cs())) return st;
   auto recompute = [&](int l) -> ls_status {
     const int k = l & 1;
     if (c->bp_rec[k]) HIPCHK(c, hipStreamWaitEvent(c->rs, c->bp_done[k], 0));
@@ -1407,11 +1414,15 @@ ls_status ls_backward(ls_ctx* c, const void* dY, void* dX, int32_t accumulate) {
     return LS_OK;
   };
   if ((st = ensure_copy(c, L - 1))) return st;
-  if ((st = recompute(L - 1))) return st;
+  if (!serial && (st = recompute(L - 1))) return st;
   for (int l = L - 1; l >= 0; --l) {
     for (int k = 1; k < c->cfg.n_buffers && l - k >= 0; ++k)
       if ((st = ensure_copy(c, l - k))) return st;
-    if (l >= 1 && (st = recompute(l - 1))) return st;
+    if (serial) {
+      if ((st = rs_after_cs()) || (st = recompute(l))) return st;
+    } else if (l >= 1 && (st = recompute(l - 1))) {
+      return st;
+    }
     const bool split = n_pieces(c, l) > 1;
     HIPCHK(c, hipStreamWaitEvent(c->cs, c->rec_done[l & 1], 0));
     if (!split && (st = use_layer(c, l))) return st;
