@@ -124,9 +124,9 @@ def test_qwen3b_configuration_sampled_sequence():
 
 def test_qwen32b_throughput_configuration_sampled_sequence():
     """Qwen2.5-32B shape (251.5 MB NF4 + double-quant layers) at its throughput
-    configuration, 2 x 1024 tokens: two streamed layers, sequence 1 checked against the
-    oracle."""
-    sampled_sequence_case("qwen32b", 2, 1)
+    configuration, 2 x 1024 tokens: one streamed layer, sequence 1 checked against the
+    oracle (the first two layers are checked at batch 1 x 256 above)."""
+    sampled_sequence_case("qwen32b", 1, 1)
 
 
 def test_qwen72b_dpo_configuration_sampled_sequence():
