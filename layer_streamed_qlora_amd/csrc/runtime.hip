@@ -1386,8 +1386,8 @@ ls_status ls_backward(ls_ctx* c, const void* dY, void* dX, int32_t accumulate) {
   // the backward of layer l, so the two run side by side.  Everything the forward left
   // (checkpoints, s X A^T, row statistics, the activation sets) is ordered before the
   // first recompute by an event on the compute stream.  With LS_PROFILE_ALL every
-  // recompute instead follows the backward before it (one kernel at a time), so that
-  // each kernel's timing is its own.
+  // recompute instead follows the backward before it, so that no recompute kernel's
+  // timing includes time it shares the GPU with another layer's backward.
   const bool serial = c->cfg.profile == LS_PROFILE_ALL;
   auto rs_after_cs = [&]() -> ls_status {
     HIPCHK(c, hipEventRecord(c->fork_ev, c->cs));
