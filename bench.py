@@ -196,6 +196,8 @@ def main():
     ap.add_argument("--no-profile", action="store_true")
     ap.add_argument("--vocab", type=int, default=128256, help="output-head rows for the head+loss measurement (0 = none)")
     ap.add_argument("--store-file", default="", help="keep the frozen base in this file instead of pinned RAM")
+    ap.add_argument("--profile-stride", type=int, default=4,
+                    help="time the forward GEMMs of every k-th layer in the timed region (1 = every layer)")
     ap.add_argument("--copy-split", type=int, default=0, choices=(0, 1),
                     help="1 = copy each layer as four separately fenced pieces (q|k|v, o, gate|up, down)")
     ap.add_argument("--resident", action="store_true",
@@ -220,10 +222,12 @@ def main():
         w = w.with_(batch=args.batch or w.batch, seq=args.seq or w.seq)
     T = w.tokens
     profile = 0 if args.no_profile else 1
-    # the timed region records events around the forward pass's dequant GEMMs only (the
-    # roofline kernel); every event is a packet in the stream and widens the gap before the
-    # next kernel, so the full per-class breakdown comes from extra steps afterwards
+    # the timed region records events around the forward pass's dequant GEMMs of every
+    # profile_stride-th layer only (the roofline kernel; every layer has the same shapes);
+    # every event is a packet in the stream and widens the gap before the next kernel, so
+    # the full per-class breakdown comes from extra steps afterwards
     cfg = B.make_config(w, n_buffers=args.buffers, profile=B.LS_PROFILE_GEMM if profile else 0, adamw=1,
+                        profile_stride=args.profile_stride,
                         resident=1 if args.resident else 0,
                         vocab=args.vocab,
                         store_path=args.store_file or None, copy_split=args.copy_split)
@@ -360,9 +364,11 @@ def main():
         dom = "gemm_fwd"    # the dominant class (largest summed time in the breakdown below)
         kl, kms, kfl, kby = kacc[dom]
         achieved = kfl / (kms * 1e-3) / 1e12
-        # the class is timed on the forward pass's launches (4 per layer), where it runs
-        # alone; the recompute's launches share the GPU with the previous layer's backward
-        out["roofline"] = {"bound": "mfma", "kernel": f"fused dequant GEMM ({dom}, forward-pass launches)",
+        # the class is timed on the forward pass's launches (4 per layer, of every
+        # profile_stride-th layer), where it runs alone; the recompute's launches share the
+        # GPU with the previous layer's backward
+        out["roofline"] = {"bound": "mfma", "kernel": f"fused dequant GEMM ({dom}, forward-pass launches"
+                                                      + (f" of every {args.profile_stride}th layer" if args.profile_stride > 1 else "") + ")",
                            "launches_per_step": kl / args.steps, "achieved": round(achieved, 1),
                            "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                            "traffic": measured_traffic(dom), "avg_launch_ms": round(kms / kl, 4),

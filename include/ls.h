@@ -105,6 +105,11 @@ typedef struct ls_config {
                               also lists small stream buffers among the causes of slow
                               training ("Common problems"); the split makes the unit the
                               compute waits for one projection group instead of a layer. */
+  int32_t profile_stride;  /* LS_PROFILE_GEMM: time the forward dequant-GEMM launches of
+                              every profile_stride-th layer only (layers 0, stride, 2 stride,
+                              ...; 0 or 1 = every layer).  Every layer has the same shapes,
+                              so a sample times the class while recording fewer events in
+                              the stream. */
 } ls_config;
 
 /* Where the frozen base lives ("Soup CLI fine-tunes Llama-3.1-8B on a 4 GB laptop GPU
@@ -282,7 +287,8 @@ ls_status ls_sync(ls_ctx* ctx);
  *                    recompute kernel shares the GPU with another layer's backward.
  *   LS_PROFILE_GEMM: only the forward pass's dequant-GEMM launches (class
  *                    LS_KC_GEMM_FWD; the recompute's launches of that kernel, which
- *                    share the GPU with the backward, are not timed).
+ *                    share the GPU with the backward, are not timed), of every layer
+ *                    or of every ls_config.profile_stride-th layer.
  */
 enum { LS_PROFILE_OFF = 0, LS_PROFILE_ALL = 1, LS_PROFILE_GEMM = 2 };
 

@@ -40,7 +40,7 @@ class ls_config(C.Structure):
         ("lora_alpha", C.c_float), ("lora_mask", C.c_uint32), ("n_buffers", C.c_int32), ("max_tokens", C.c_int32),
         ("max_seq", C.c_int32), ("resident", C.c_int32), ("vram_budget", C.c_uint64), ("profile", C.c_int32),
         ("adamw", C.c_int32), ("vocab", C.c_int32), ("store", C.c_int32), ("store_path", C.c_char * 256),
-        ("copy_split", C.c_int32),
+        ("copy_split", C.c_int32), ("profile_stride", C.c_int32),
     ]
 
 
@@ -139,7 +139,8 @@ def _check(status, ctx=None):
 
 
 def make_config(w, n_buffers=2, max_tokens=None, max_seq=None, resident=0, vram_budget=0, profile=0,
-                lora_mask=0x7F, n_layers=None, adamw=0, vocab=0, store_path=None, copy_split=0) -> ls_config:
+                lora_mask=0x7F, n_layers=None, adamw=0, vocab=0, store_path=None, copy_split=0,
+                profile_stride=0) -> ls_config:
     """ls_config for a workload description (``synth.Workload``)."""
     return ls_config(
         n_layers=w.n_layers if n_layers is None else n_layers, hidden=w.hidden, n_heads=w.n_heads,
@@ -149,7 +150,8 @@ def make_config(w, n_buffers=2, max_tokens=None, max_seq=None, resident=0, vram_
         n_buffers=n_buffers, max_tokens=w.tokens if max_tokens is None else max_tokens,
         max_seq=w.seq if max_seq is None else max_seq, resident=resident, vram_budget=vram_budget, profile=profile,
         adamw=adamw, vocab=vocab, store=LS_STORE_FILE if store_path else LS_STORE_HOST,
-        store_path=os.fsencode(store_path) if store_path else b"", copy_split=copy_split)
+        store_path=os.fsencode(store_path) if store_path else b"", copy_split=copy_split,
+        profile_stride=profile_stride)
 
 
 # ------------------------------------------------------------------ host calls

@@ -203,6 +203,7 @@ bool validate_config(const ls_config& c, const char** why) {
   REQ(c.vocab >= 0 && c.vocab <= (1 << 24), "vocab must be in 0..2^24");
   REQ(c.store == LS_STORE_HOST || c.store == LS_STORE_FILE, "store must be LS_STORE_HOST or LS_STORE_FILE");
   REQ(c.copy_split == 0 || c.copy_split == 1, "copy_split must be 0 or 1");
+  REQ(c.profile_stride >= 0 && c.profile_stride <= 1 << 20, "profile_stride must be >= 0");
   REQ(c.store != LS_STORE_FILE || (c.store_path[0] != 0 && memchr(c.store_path, 0, sizeof(c.store_path)) != nullptr),
       "LS_STORE_FILE needs a NUL-terminated store_path");
 #undef REQ

@@ -226,6 +226,7 @@ struct ls_ctx {
   hipEvent_t rec_done[2] = {}, bp_done[2] = {}, side_done[2] = {};
   bool bp_rec[2] = {}, side_rec[2] = {};
   bool in_recompute = false;            // enqueueing a recompute (LS_PROFILE_GEMM skips it)
+  int prof_layer = -1;                  // the forward's layer being enqueued (profile_stride)
   std::vector<uint8_t*> host;
   std::vector<char> staged;
   uint8_t* dbase = nullptr;
@@ -310,7 +311,8 @@ struct KTimer {
   KTimer(ls_ctx* ctx, int k, double f, double b, hipStream_t st = nullptr)
       : c(ctx), cls(k), flop(f), bytes(b),
         on(ctx->cfg.profile == LS_PROFILE_ALL ||
-           (ctx->cfg.profile == LS_PROFILE_GEMM && k == LS_KC_GEMM_FWD && !ctx->in_recompute)),
+           (ctx->cfg.profile == LS_PROFILE_GEMM && k == LS_KC_GEMM_FWD && !ctx->in_recompute &&
+            (ctx->cfg.profile_stride <= 1 || (ctx->prof_layer >= 0 && ctx->prof_layer % ctx->cfg.profile_stride == 0)))),
         s(st ? st : ctx->cs) {
     if (on) {
       hipEvent_t e;
@@ -1340,13 +1342,19 @@ ls_status ls_forward(ls_ctx* c, const void* X, int32_t batch, int32_t seq, int32
       if (lora && (st = prep_lora(c, l, d))) return st;
       uint16_t* out = l + 1 < L ? ckpt(c, l + 1) : (uint16_t*)Y;
       const Fence f1{l, split};
-      if ((st = layer_forward(c, l, blob, d, ckpt(c, l), out, lora, MODE_FWD, f1, c->cs))) return st;
+      c->prof_layer = l;
+      st = layer_forward(c, l, blob, d, ckpt(c, l), out, lora, MODE_FWD, f1, c->cs);
+      c->prof_layer = -1;
+      if (st) return st;
       if (Y_ref) {
         // layer 0 reads the checkpoint copy of X, so Y may alias X
         const uint16_t* rin = l == 0 ? ckpt(c, 0) : xr[(l - 1) & 1];
         uint16_t* rout = l + 1 < L ? xr[l & 1] : (uint16_t*)Y_ref;
         const Fence f2{l, false};
-        if ((st = layer_forward(c, l, blob, d, rin, rout, false, MODE_FWD, f2, c->cs))) return st;
+        c->prof_layer = l;
+        st = layer_forward(c, l, blob, d, rin, rout, false, MODE_FWD, f2, c->cs);
+        c->prof_layer = -1;
+        if (st) return st;
       }
     }
     if ((st = release_layer(c, l))) return st;

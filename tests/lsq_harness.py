@@ -35,7 +35,7 @@ class GpuRun:
 
     def __init__(self, w, layer_seeds, resident=0, n_buffers=2, profile=0, zero_b=False, max_tokens=None,
                  max_seq=None, lora_mask=0x7F, weights=None, adamw=0, vocab=0, store_path=None, layer_bits=None,
-                 copy_split=0):
+                 copy_split=0, profile_stride=0):
         """weights: per-layer float32 dicts of bf16 values (default: drawn from the
         seeds); layer_bits: per-layer dicts of bf16 bit patterns, staged as they are
         (then ``src`` is None)."""
@@ -46,7 +46,8 @@ class GpuRun:
         L = len(self.layer_seeds)
         cfg = B.make_config(w, n_buffers=n_buffers, resident=resident, profile=profile, n_layers=L,
                             max_tokens=max_tokens, max_seq=max_seq, lora_mask=lora_mask, adamw=adamw,
-                            vocab=vocab, store_path=store_path, copy_split=copy_split)
+                            vocab=vocab, store_path=store_path, copy_split=copy_split,
+                            profile_stride=profile_stride)
         self.ctx = B.Context(cfg)
         self.src = [] if layer_bits is None else None
         for i, seed in enumerate(self.layer_seeds):

@@ -104,7 +104,8 @@ def test_budget_refusal_allocates_nothing():
 
 @pytest.mark.parametrize("field,value", [("nf4_block", 32), ("lora_r", 0), ("n_buffers", 1), ("head_dim", 96),
                                          ("n_kv_heads", 3), ("hidden", 100), ("lora_mask", 0x80),
-                                         ("max_seq", 0), ("double_quant", 2), ("copy_split", 2)])
+                                         ("max_seq", 0), ("double_quant", 2), ("copy_split", 2),
+                                         ("profile_stride", -1)])
 def test_invalid_config(field, value):
     cfg = B.make_config(synth.WORKLOADS["toy"], vram_budget=1 << 40)
     setattr(cfg, field, value)

@@ -252,16 +252,24 @@ def test_file_store_bad_path_is_refused():
 
 
 def test_profiling_levels():
-    """LS_PROFILE_GEMM times only the forward dequant GEMMs; LS_PROFILE_ALL every class and
-    the copy intervals; the results do not depend on the level."""
+    """LS_PROFILE_GEMM times only the forward pass's dequant GEMMs (4 per layer; the
+    recompute's are not timed), of every profile_stride-th layer if that is set;
+    LS_PROFILE_ALL every class and the copy intervals; the results do not depend on the
+    level."""
     from layer_streamed_qlora_amd import binding as B
     w = TOY
     x, dy = synth.activations(w)
     run = H.GpuRun(w, [0, 1, 2], profile=B.LS_PROFILE_GEMM)   # 3 layers, 2 slots: every step copies
     a = run.step(x, dy, w.batch, w.seq)
     st = run.ctx.stats()
-    assert st.k_launches[0] > 0 and all(st.k_launches[j] == 0 for j in range(1, B.LS_KC_N))
+    assert st.k_launches[0] == 4 * 3 and all(st.k_launches[j] == 0 for j in range(1, B.LS_KC_N))
     assert st.last_copy_ms == 0.0
+    sampled = H.GpuRun(w, [0, 1, 2], profile=B.LS_PROFILE_GEMM, profile_stride=2)   # layers 0 and 2
+    c = sampled.step(x, dy, w.batch, w.seq)
+    assert sampled.ctx.stats().k_launches[0] == 4 * 2
+    sampled.close()
+    for k in ("Y", "dX"):
+        assert np.array_equal(a[k].view(np.uint32), c[k].view(np.uint32)), k
     run.ctx.set_profile(B.LS_PROFILE_ALL)
     b = run.step(x, dy, w.batch, w.seq)
     st = run.ctx.stats()
