@@ -14,6 +14,10 @@
 // as float32 or decoded from the 8-bit second level as
 // fp32(fp32(fp32(c/127) * scale2) + mean) with no fused multiply-add.
 //
+// A launch whose tiles leave the last round of compute units part full cuts each tile
+// of that round along K into pieces that fill it; the piece that finishes last adds
+// the pieces' float32 sums (piece_of, combine_pieces).
+//
 // Tile: 256 x 256 outputs per 256-thread workgroup, 2 x 2 waves of 128 x 128
 // (4 x 4 MFMA blocks of 32 x 32, 256 float accumulators per lane), K step 64,
 // two LDS stages (row pitch 72 bf16 = 144 B keeps ds_read_b128 conflict-free).
@@ -116,6 +120,7 @@ struct Smem {
     } k;
     float out[128 * (BN + 4)];       // epilogue staging, one half tile (128 rows) at a time
   } u;
+  uint32_t sk_flag;                  // a split tile's arrival count, read back by every thread
 };
 
 __device__ __forceinline__ void fill_lut2(Smem& sm, const float* levels) {
@@ -868,6 +873,95 @@ __device__ __forceinline__ int xcd_tile(int bid, int nblocks_padded) {
   return (bid & 7) * per + (bid >> 3);
 }
 
+// ---- work of one fast-path workgroup: K stages [ks, ke) of one tile.  Without split
+// tiles a workgroup runs one whole tile (xcd_tile order).  With them, the launch's
+// tiles are n_whole whole tiles (full rounds of the compute units) plus a tail of
+// fewer tiles than compute units, each cut into `split` pieces of about nk / split
+// K stages, so the last round is full too.  Every XCD (bid & 7) gets the same share
+// of both: its first n_whole / 8 workgroups run whole tiles, the rest the pieces of
+// its tail / 8 tail tiles.
+struct Piece { int tile, ks, ke, slot, idx; };
+__device__ __forceinline__ Piece piece_of(int total_tiles, int nk, int padded, int n_whole, int split) {
+  Piece p;
+  if (split <= 1) {
+    p.tile = xcd_tile(blockIdx.x, padded);
+    p.ks = 0; p.ke = p.tile < total_tiles ? nk : 0;
+    p.slot = -1; p.idx = 0;
+    return p;
+  }
+  const int x = blockIdx.x & 7, li = blockIdx.x >> 3;
+  const int wx = n_whole / 8, tx = (total_tiles - n_whole) / 8;
+  if (li < wx) {
+    p.tile = x * wx + li;
+    p.ks = 0; p.ke = nk;
+    p.slot = -1; p.idx = 0;
+  } else {
+    const int q = li - wx;
+    p.slot = x * tx + q / split;
+    p.tile = n_whole + p.slot;
+    p.idx = q - (q / split) * split;
+    p.ks = p.idx * nk / split;
+    p.ke = (p.idx + 1) * nk / split;
+    if (q >= tx * split) p.ke = p.ks;   // past the XCD's pieces (none when the grid is exact)
+  }
+  return p;
+}
+
+// A tail tile's `split` pieces meet in part[slot][piece] and cnt[slot].  Each piece
+// writes its float32 sums and then counts itself; the piece that counts last reads
+// all of them back and adds them in piece order (so the result does not depend on
+// which piece comes last), writes the tile and sets the counter back to zero.  Nobody
+// waits on another piece.  The partial sums are written and read at device scope
+// (the sc1 cache policy: through to the point where every XCD sees them, the form
+// the compiler gives device-scope atomic loads and stores), so they need no L2
+// write-back or invalidation; the writes are complete (vmcnt 0) before the count.
+// Returns whether this workgroup writes the tile.
+constexpr int kScopeDevice = 16;   // buffer cache-policy bits: sc1 = device scope
+
+template <int NT>
+__device__ __forceinline__ bool combine_pieces(f32x16_t (&acc)[4][Layout<NT>::JB], float* part, uint32_t* cnt,
+                                               int slot, int piece, int split, uint32_t* flag) {
+  constexpr int JB = Layout<NT>::JB;
+  constexpr int TILE = BM * BN;
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  const rsrc_t pres = make_rsrc_wave(part + (size_t)slot * split * TILE, (uint64_t)split * TILE * 4);
+  const uint32_t own = (uint32_t)piece * (TILE * 4u);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < JB; ++j)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const f32x4 t = {acc[i][j][4 * v], acc[i][j][4 * v + 1], acc[i][j][4 * v + 2], acc[i][j][4 * v + 3]};
+        const uint32_t off = (uint32_t)((((i * JB + j) * 4 + v) * NT + threadIdx.x) * 16);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, t), pres, own + off, 0, kScopeDevice);
+      }
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  __syncthreads();
+  if (threadIdx.x == 0) *flag = atomicAdd(cnt + slot, 1u);
+  __syncthreads();
+  if (*flag != (uint32_t)(split - 1)) return false;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < JB; ++j)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const uint32_t off = (uint32_t)((((i * JB + j) * 4 + v) * NT + threadIdx.x) * 16);
+        f32x4 t = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(pres, off, 0, kScopeDevice));
+        for (int pc = 1; pc < split; ++pc)
+          t += __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(pres, (uint32_t)pc * (TILE * 4u) + off,
+                                                                               0, kScopeDevice));
+        acc[i][j][4 * v] = t.x;
+        acc[i][j][4 * v + 1] = t.y;
+        acc[i][j][4 * v + 2] = t.z;
+        acc[i][j][4 * v + 3] = t.w;
+      }
+  if (threadIdx.x == 0) cnt[slot] = 0;
+  return true;
+}
+
 // ------------------------------------------------------------------ forward
 template <int FMT, bool ALIGNED>
 __global__ void __launch_bounds__(NTHREADS, 1) k_gemm_fwd(FwdArgs args, int n_tiles, int total_tiles, int padded) {
@@ -1052,244 +1146,258 @@ __global__ void __launch_bounds__(NTHREADS, 1) k_gemm_bwd(BwdArgs args, int n_ti
 // epilogue writes silu(gate) * up.  The low-rank terms become one 2 kx wide extension:
 // [H_gate | H_up] against [B_gate | 0] for the gate half and [0 | B_up] for the up half.
 template <int FMT, bool PAIRED>
-__global__ void __launch_bounds__(NT_FAST, 1) k_gemm_fwd_fast(FwdArgs args, int n_tiles, int total_tiles, int padded) {
+__global__ void __launch_bounds__(NT_FAST, 1) k_gemm_fwd_fast(FwdArgs args, int n_tiles, int total_tiles, int padded,
+                                                              int n_whole, int split) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   Smem& sm = *reinterpret_cast<Smem*>(smem_raw);
-  const int tile = xcd_tile(blockIdx.x, padded);
-  if (tile >= total_tiles) return;
-  int mt, rest;
-  tile_mn(tile, total_tiles / n_tiles, n_tiles, mt, rest);
-  int g = 0;
-  if constexpr (!PAIRED) {
-    for (; g < args.n_groups - 1; ++g) {
-      const int nt_g = (args.g[g].w.n_out + BN - 1) / BN;
-      if (rest < nt_g) break;
-      rest -= nt_g;
-    }
-  }
-  const FwdGroup& G = args.g[g];
-  const int m0 = mt * BM;
-  const int n0 = PAIRED ? rest * (BN / 2) : rest * BN;
   const int K = args.K;
-  const int n_out = G.w.n_out;
+  const int nk = K / BK;
+  const Piece pc = piece_of(total_tiles, nk, padded, n_whole, split);
+  if (pc.ks >= pc.ke) return;
+  const int tile = pc.tile, ks = pc.ks, ke = pc.ke;
 
   fill_lut2(sm, args.levels);
 
-  constexpr int JB = Layout<NT_FAST>::JB;
-  f32x16_t acc[4][JB];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < JB; ++j) acc[i][j] = f32x16_t{};
-
-  const int rows_left = args.M - m0;
-  const int arows = rows_left < BM ? rows_left : BM;
-  const rsrc_t xres = make_rsrc(args.x + (int64_t)m0 * args.ldx, (uint64_t)arows * args.ldx * 2);
-  const int nk = K / BK;
-  const int n_iter = nk + 1;   // iteration 0: the low-rank term
-  if constexpr (PAIRED) {
-    const int kx = args.kx;
-    const bool has_ext = kx > 0;
-    const rsrc_t ares = make_rsrc(has_ext ? args.aext + (int64_t)m0 * args.ldaext : args.x,
-                                  has_ext ? (uint64_t)arows * args.ldaext * 2 : 0);
-    ext_tile(sm.u.k.a[0], ares, (uint32_t)G.ext_col0 * 2u, args.ldaext, has_ext ? arows : 0, 2 * kx);
-    const int brows = n_out - n0 < BN / 2 ? n_out - n0 : BN / 2;
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-      const uint16_t* bx = args.g[hf].bext;
-      const bool on = has_ext && bx != nullptr;
-      const rsrc_t bres = make_rsrc(on ? bx + (int64_t)n0 * kx : args.x, on ? (uint64_t)brows * kx * 2 : 0);
-      ext_tile<2>(sm.u.k.w[0] + hf * (BN / 2) * PITCH, bres, 0, kx, on ? brows : 0, kx, hf * kx);
-    }
-  } else {
-    const bool has_ext = args.kx > 0 && G.bext != nullptr;
-    const int brows = n_out - n0 < BN ? n_out - n0 : BN;
-    const rsrc_t ares = make_rsrc(has_ext ? args.aext + (int64_t)m0 * args.ldaext : args.x,
-                                  has_ext ? (uint64_t)arows * args.ldaext * 2 : 0);
-    const rsrc_t bres = make_rsrc(has_ext ? G.bext + (int64_t)n0 * args.kx : args.x,
-                                  has_ext ? (uint64_t)brows * args.kx * 2 : 0);
-    ext_tile(sm.u.k.a[0], ares, (uint32_t)G.ext_col0 * 2u, args.ldaext, has_ext ? arows : 0, args.kx);
-    ext_tile(sm.u.k.w[0], bres, 0, args.kx, has_ext ? brows : 0, args.kx);
-  }
-  // A: one register set, each quarter reloaded for tile it+1 right after it is
-  // stored; W: current and next tile in registers.  Loads past K are skipped.
-  AFast ra;
-  ra.init(xres, args.ldx);
-  WFwdFast<FMT> ws;
   {
-    const WeightRef& wsel = PAIRED ? args.g[threadIdx.x >> 8].w : G.w;   // wave-uniform
-    const uint32_t r = PAIRED ? (threadIdx.x >> 1) & 127u : threadIdx.x >> 1;
-    ws.init(wsel, n0, r, PAIRED ? BN / 2 : BN);
-  }
-  typename WFwdFast<FMT>::Regs rw, rw_next;
-  WFwdFast<FMT>::clear(rw);
-  WFwdFast<FMT>::clear(rw_next);
-#pragma unroll
-  for (int q = 0; q < 4; ++q) ra.load_q(0, q);
-  ws.load(rw, 0);
-  ws.load(rw_next, BK < K ? BK : 0);   // unconditional, like the prefetches in the loop
-  // Drain the prologue's loads once: otherwise their order here, merged into the loop
-  // head, sets the wait counts of every iteration.
-  __builtin_amdgcn_s_waitcnt(kWaitVm0);
-  __syncthreads();
-  // Iteration it dequantises W tile it from R and then reloads R with tile it + 2.
-  // The two register sets alternate by unrolling two iterations: a copy between them
-  // would wait on the loads still in flight into the source.  Every prefetch is issued
-  // on every path (the compiler counts only loads that are always issued when it
-  // places its waits; a skipped-load branch makes it wait for every load in flight).
-  // Iteration 0, the low-rank stage, multiplies only its non-zero k steps; the K
-  // stages follow in pairs, and an odd count of them gets one padding stage: an
-  // activation tile past K loads as zeros (out-of-range offset), W past K re-reads the
-  // last tile, so the padding stage adds exact zeros.
-  const int k_last = K - BK;
-  const int ext_cols = PAIRED ? (args.kx > 0 ? 2 * args.kx : 0) : (args.kx > 0 && G.bext != nullptr ? args.kx : 0);
-  auto step = [&](int it, typename WFwdFast<FMT>::Regs& R, auto low_rank) {
-    // let the scheduler interleave the LDS and memory instructions with the MFMAs
-    __builtin_amdgcn_iglp_opt(0);
-    const int cur = it & 1;
-    uint16_t* na = sm.u.k.a[cur ^ 1];
-    uint16_t* nw = sm.u.k.w[cur ^ 1];
-    const int k_next = (it + 1) * BK;
-    const bool past = k_next >= K;
-    const float am = FMT == WF_BF16 ? 0.f : ws.absmax(R);
-    auto work = [&](int q) {
-      ra.store_q(na, q);
-      ra.load_q_or_zero((uint32_t)k_next, q, past);
-      ws.store_part(R, nw, sm.lut2, q, am);
-    };
-    if constexpr (decltype(low_rank)::value)
-      mma_stage_n<NT_FAST>(sm.u.k.a[cur], sm.u.k.w[cur], acc, (ext_cols + 15) / 16, work);
-    else
-      mma_stage<NT_FAST>(sm.u.k.a[cur], sm.u.k.w[cur], acc, work);
-    ws.load(R, k_next + BK < k_last ? k_next + BK : k_last);
-    __syncthreads();
-  };
-  step(0, rw, std::true_type{});
-  for (int it = 1; it < n_iter; it += 2) {
-    step(it, rw_next, std::false_type{});
-    step(it + 1, rw, std::false_type{});
-  }
+    int mt, rest;
+    tile_mn(tile, total_tiles / n_tiles, n_tiles, mt, rest);
+    int g = 0;
+    if constexpr (!PAIRED) {
+      for (; g < args.n_groups - 1; ++g) {
+        const int nt_g = (args.g[g].w.n_out + BN - 1) / BN;
+        if (rest < nt_g) break;
+        rest -= nt_g;
+      }
+    }
+    const FwdGroup& G = args.g[g];
+    const int m0 = mt * BM;
+    const int n0 = PAIRED ? rest * (BN / 2) : rest * BN;
+    const int n_out = G.w.n_out;
 
-  if constexpr (PAIRED) {
-    epilogue_swiglu<NT_FAST>(sm, acc, m0, n0, args.M, n_out, args.y, args.ldy, args.gu32, args.ldgu);
-  } else {
-    Epi E;
-    E.f32 = args.y32 != nullptr;
-    E.out = E.f32 ? (void*)(args.y32 + G.out_col0) : (void*)(args.y + G.out_col0);
-    E.ldo = args.ldy;
-    E.r16 = args.resid ? args.resid + G.out_col0 : nullptr;
-    E.r32 = args.resid32 ? args.resid32 + G.out_col0 : nullptr;
-    E.ldr = args.ldr;
-    E.rope_tab = args.rope_tab; E.rope_cols = args.rope_tab ? args.rope_cols : 0;
-    E.col_base = G.out_col0; E.seq = args.seq; E.hd = args.head_dim;
-    epilogue<NT_FAST>(sm, acc, m0, n0, args.M, n_out, E);
+    constexpr int JB = Layout<NT_FAST>::JB;
+    f32x16_t acc[4][JB];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < JB; ++j) acc[i][j] = f32x16_t{};
+
+    const int rows_left = args.M - m0;
+    const int arows = rows_left < BM ? rows_left : BM;
+    const rsrc_t xres = make_rsrc(args.x + (int64_t)m0 * args.ldx, (uint64_t)arows * args.ldx * 2);
+    const int n_iter = ke - ks + 1;   // iteration 0: the low-rank term (first piece only)
+    // The low-rank term goes with the tile's first piece; a later piece leaves stage
+    // 0 unread (its low-rank stage multiplies nothing).
+    const int ext_cols = ks > 0 ? 0
+                         : PAIRED ? (args.kx > 0 ? 2 * args.kx : 0)
+                                  : (args.kx > 0 && G.bext != nullptr ? args.kx : 0);
+    if (ext_cols > 0) {
+      if constexpr (PAIRED) {
+        const int kx = args.kx;
+        const rsrc_t ares = make_rsrc(args.aext + (int64_t)m0 * args.ldaext, (uint64_t)arows * args.ldaext * 2);
+        ext_tile(sm.u.k.a[0], ares, (uint32_t)G.ext_col0 * 2u, args.ldaext, arows, 2 * kx);
+        const int brows = n_out - n0 < BN / 2 ? n_out - n0 : BN / 2;
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          const uint16_t* bx = args.g[hf].bext;
+          const bool on = bx != nullptr;
+          const rsrc_t bres = make_rsrc(on ? bx + (int64_t)n0 * kx : args.x, on ? (uint64_t)brows * kx * 2 : 0);
+          ext_tile<2>(sm.u.k.w[0] + hf * (BN / 2) * PITCH, bres, 0, kx, on ? brows : 0, kx, hf * kx);
+        }
+      } else {
+        const int brows = n_out - n0 < BN ? n_out - n0 : BN;
+        const rsrc_t ares = make_rsrc(args.aext + (int64_t)m0 * args.ldaext, (uint64_t)arows * args.ldaext * 2);
+        const rsrc_t bres = make_rsrc(G.bext + (int64_t)n0 * args.kx, (uint64_t)brows * args.kx * 2);
+        ext_tile(sm.u.k.a[0], ares, (uint32_t)G.ext_col0 * 2u, args.ldaext, arows, args.kx);
+        ext_tile(sm.u.k.w[0], bres, 0, args.kx, brows, args.kx);
+      }
+    }
+    // A: one register set, each quarter reloaded for tile it+1 right after it is
+    // stored; W: current and next tile in registers.  Loads past the piece are skipped.
+    AFast ra;
+    ra.init(xres, args.ldx);
+    WFwdFast<FMT> ws;
+    {
+      const WeightRef& wsel = PAIRED ? args.g[threadIdx.x >> 8].w : G.w;   // wave-uniform
+      const uint32_t r = PAIRED ? (threadIdx.x >> 1) & 127u : threadIdx.x >> 1;
+      ws.init(wsel, n0, r, PAIRED ? BN / 2 : BN);
+    }
+    typename WFwdFast<FMT>::Regs rw, rw_next;
+    WFwdFast<FMT>::clear(rw);
+    WFwdFast<FMT>::clear(rw_next);
+    const int k_first = ks * BK, k_end = ke * BK, k_last = k_end - BK;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) ra.load_q((uint32_t)k_first, q);
+    ws.load(rw, k_first);
+    ws.load(rw_next, k_first + BK < k_end ? k_first + BK : k_first);   // unconditional, like the loop's prefetches
+    // Drain the prologue's loads once: otherwise their order here, merged into the loop
+    // head, sets the wait counts of every iteration.
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    __syncthreads();
+    // Iteration it dequantises W tile ks + it from R and then reloads R with tile
+    // ks + it + 2.  The two register sets alternate by unrolling two iterations: a copy
+    // between them would wait on the loads still in flight into the source.  Every
+    // prefetch is issued on every path (the compiler counts only loads that are always
+    // issued when it places its waits; a skipped-load branch makes it wait for every
+    // load in flight).  Iteration 0, the low-rank stage, multiplies only its non-zero k
+    // steps; the K stages follow in pairs, and an odd count of them gets one padding
+    // stage: an activation tile past the piece loads as zeros (out-of-range offset), W
+    // past it re-reads the piece's last tile, so the padding stage adds exact zeros.
+    auto step = [&](int it, typename WFwdFast<FMT>::Regs& R, auto low_rank) {
+      // let the scheduler interleave the LDS and memory instructions with the MFMAs
+      __builtin_amdgcn_iglp_opt(0);
+      const int cur = it & 1;
+      uint16_t* na = sm.u.k.a[cur ^ 1];
+      uint16_t* nw = sm.u.k.w[cur ^ 1];
+      const int k_next = k_first + (it + 1) * BK;
+      const bool past = k_next >= k_end;
+      const float am = FMT == WF_BF16 ? 0.f : ws.absmax(R);
+      auto work = [&](int q) {
+        ra.store_q(na, q);
+        ra.load_q_or_zero((uint32_t)k_next, q, past);
+        ws.store_part(R, nw, sm.lut2, q, am);
+      };
+      if constexpr (decltype(low_rank)::value)
+        mma_stage_n<NT_FAST>(sm.u.k.a[cur], sm.u.k.w[cur], acc, (ext_cols + 15) / 16, work);
+      else
+        mma_stage<NT_FAST>(sm.u.k.a[cur], sm.u.k.w[cur], acc, work);
+      ws.load(R, k_next + BK < k_last ? k_next + BK : k_last);
+      __syncthreads();
+    };
+    step(0, rw, std::true_type{});
+    for (int it = 1; it < n_iter; it += 2) {
+      step(it, rw_next, std::false_type{});
+      step(it + 1, rw, std::false_type{});
+    }
+
+    if (pc.slot >= 0 && !combine_pieces<NT_FAST>(acc, args.sk.part, args.sk.cnt, pc.slot, pc.idx, split, &sm.sk_flag))
+      return;
+    if constexpr (PAIRED) {
+      epilogue_swiglu<NT_FAST>(sm, acc, m0, n0, args.M, n_out, args.y, args.ldy, args.gu32, args.ldgu);
+    } else {
+      Epi E;
+      E.f32 = args.y32 != nullptr;
+      E.out = E.f32 ? (void*)(args.y32 + G.out_col0) : (void*)(args.y + G.out_col0);
+      E.ldo = args.ldy;
+      E.r16 = args.resid ? args.resid + G.out_col0 : nullptr;
+      E.r32 = args.resid32 ? args.resid32 + G.out_col0 : nullptr;
+      E.ldr = args.ldr;
+      E.rope_tab = args.rope_tab; E.rope_cols = args.rope_tab ? args.rope_cols : 0;
+      E.col_base = G.out_col0; E.seq = args.seq; E.hd = args.head_dim;
+      epilogue<NT_FAST>(sm, acc, m0, n0, args.M, n_out, E);
+    }
   }
 }
 
 template <int FMT>
-__global__ void __launch_bounds__(NT_FAST, 1) k_gemm_bwd_fast(BwdArgs args, int n_tiles, int total_tiles, int padded) {
+__global__ void __launch_bounds__(NT_FAST, 1) k_gemm_bwd_fast(BwdArgs args, int n_tiles, int total_tiles, int padded,
+                                                              int n_whole, int split) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   Smem& sm = *reinterpret_cast<Smem*>(smem_raw);
-  const int tile = xcd_tile(blockIdx.x, padded);
-  if (tile >= total_tiles) return;
-  int mt, nt;
-  tile_mn(tile, total_tiles / n_tiles, n_tiles, mt, nt);
-  const int m0 = mt * BM, j0 = nt * BN;
-
-  fill_lut2(sm, args.levels);
-
-  constexpr int JB = Layout<NT_FAST>::JB;
-  f32x16_t acc[4][JB];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < JB; ++j) acc[i][j] = f32x16_t{};
-
-  const int rows_left = args.M - m0;
-  const int arows = rows_left < BM ? rows_left : BM;
-  const rsrc_t dres = make_rsrc(args.dy + (int64_t)m0 * args.lddy, (uint64_t)arows * args.lddy * 2);
   int seg_tiles[kMaxGroups];
   int total_k = 0;
   for (int s = 0; s < args.n_segs; ++s) {
     seg_tiles[s] = args.seg[s].w.n_out / BK;
     total_k += seg_tiles[s];
   }
-  // iteration 0: the low-rank term (kx <= 64)
-  {
-    const bool has_ext = args.kx > 0;
-    const int brows = args.N - j0 < BN ? args.N - j0 : BN;
-    const rsrc_t ares = make_rsrc(has_ext ? args.aext + (int64_t)m0 * args.ldaext : args.dy,
-                                  has_ext ? (uint64_t)arows * args.ldaext * 2 : 0);
-    const rsrc_t bres = make_rsrc(has_ext ? args.bext + (int64_t)j0 * args.ldbext : args.dy,
-                                  has_ext ? (uint64_t)brows * args.ldbext * 2 : 0);
-    ext_tile(sm.u.k.a[0], ares, 0, args.ldaext, has_ext ? arows : 0, args.kx);
-    ext_tile(sm.u.k.w[0], bres, 0, args.ldbext, has_ext ? brows : 0, args.kx);
-  }
+  const Piece pc = piece_of(total_tiles, total_k, padded, n_whole, split);
+  if (pc.ks >= pc.ke) return;
+  const int tile = pc.tile, ks = pc.ks, ke = pc.ke;
+
+  fill_lut2(sm, args.levels);
+
   // stacked K tile t < total_k -> segment and first row
   auto seg_of = [&](int t, int& s_out, int& k0_out) {
     int s = 0;
     while (t >= seg_tiles[s]) { t -= seg_tiles[s]; ++s; }
     s_out = s; k0_out = t * BK;
   };
-  AFast ra;
-  ra.init(dres, args.lddy);
   WBwdFast<FMT> ws;
   ws.init_lane(args.N);
-  typename WBwdFast<FMT>::Regs rw, rw_next;
-  WBwdFast<FMT>::clear(rw);
-  WBwdFast<FMT>::clear(rw_next);
-  // loads past the last tile re-read the last tile (see the forward kernel)
-  auto load_w = [&](typename WBwdFast<FMT>::Regs& R, int t) {
-    int s, k0; seg_of(t < total_k ? t : total_k - 1, s, k0);
-    ws.load(R, args.seg[s].w, j0, k0);
-  };
-  {
-    int s, k0; seg_of(0, s, k0);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) ra.load_q((uint32_t)(args.seg[s].a_col0 + k0), q);
-  }
-  load_w(rw, 0);
-  load_w(rw_next, 1);
-  __builtin_amdgcn_s_waitcnt(kWaitVm0);   // see the forward kernel
-  __syncthreads();
-  const int n_iter = total_k + 1;
-  // as in the forward kernel: two register sets for W alternating without copies,
-  // prefetches on every path, the low-rank stage multiplying only its non-zero k
-  // steps, then the K stages in pairs (one zero padding stage if their count is odd)
-  auto step = [&](int it, typename WBwdFast<FMT>::Regs& R, auto low_rank) {
-    const int cur = it & 1;
-    uint16_t* na = sm.u.k.a[cur ^ 1];
-    uint16_t* nw = sm.u.k.w[cur ^ 1];
-    const bool past = it + 1 >= total_k;
-    uint32_t col;
-    { int s, k0; seg_of(past ? total_k - 1 : it + 1, s, k0); col = (uint32_t)(args.seg[s].a_col0 + k0); }
-    const float a0 = FMT == WF_BF16 ? 0.f : ws.absmax(R, 0);
-    const float a1 = FMT == WF_BF16 ? 0.f : ws.absmax(R, 1);
-    auto work = [&](int q) {
-      ra.store_q(na, q);
-      ra.load_q_or_zero(col, q, past);
-      ws.store_part(R, nw, sm.lut2, q, a0, a1);
-    };
-    if constexpr (decltype(low_rank)::value)
-      mma_stage_n<NT_FAST>(sm.u.k.a[cur], sm.u.k.w[cur], acc, (args.kx + 15) / 16, work);
-    else
-      mma_stage<NT_FAST>(sm.u.k.a[cur], sm.u.k.w[cur], acc, work);
-    load_w(R, it + 2);
-    __syncthreads();
-  };
-  step(0, rw, std::true_type{});
-  for (int it = 1; it < n_iter; it += 2) {
-    step(it, rw_next, std::false_type{});
-    step(it + 1, rw, std::false_type{});
-  }
 
-  Epi E;
-  E.f32 = args.out32 != nullptr;
-  E.out = E.f32 ? (void*)args.out32 : (void*)args.out16;
-  E.ldo = args.ldo;
-  E.gu = args.gu32; E.ldgu = args.ldgu;
-  E.r32 = args.resid32; E.ldr = args.ldo;
-  epilogue<NT_FAST>(sm, acc, m0, j0, args.M, args.N, E);
+  {
+    int mt, nt;
+    tile_mn(tile, total_tiles / n_tiles, n_tiles, mt, nt);
+    const int m0 = mt * BM, j0 = nt * BN;
+
+    constexpr int JB = Layout<NT_FAST>::JB;
+    f32x16_t acc[4][JB];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < JB; ++j) acc[i][j] = f32x16_t{};
+
+    const int rows_left = args.M - m0;
+    const int arows = rows_left < BM ? rows_left : BM;
+    const rsrc_t dres = make_rsrc(args.dy + (int64_t)m0 * args.lddy, (uint64_t)arows * args.lddy * 2);
+    // iteration 0: the low-rank term (kx <= 64), in the tile's first piece only
+    const int ext_cols = ks > 0 ? 0 : args.kx;
+    if (ext_cols > 0) {
+      const int brows = args.N - j0 < BN ? args.N - j0 : BN;
+      const rsrc_t ares = make_rsrc(args.aext + (int64_t)m0 * args.ldaext, (uint64_t)arows * args.ldaext * 2);
+      const rsrc_t bres = make_rsrc(args.bext + (int64_t)j0 * args.ldbext, (uint64_t)brows * args.ldbext * 2);
+      ext_tile(sm.u.k.a[0], ares, 0, args.ldaext, arows, args.kx);
+      ext_tile(sm.u.k.w[0], bres, 0, args.ldbext, brows, args.kx);
+    }
+    AFast ra;
+    ra.init(dres, args.lddy);
+    typename WBwdFast<FMT>::Regs rw, rw_next;
+    WBwdFast<FMT>::clear(rw);
+    WBwdFast<FMT>::clear(rw_next);
+    // loads past the piece re-read its last tile (see the forward kernel)
+    auto load_w = [&](typename WBwdFast<FMT>::Regs& R, int t) {
+      int s, k0; seg_of(t < ke ? t : ke - 1, s, k0);
+      ws.load(R, args.seg[s].w, j0, k0);
+    };
+    {
+      int s, k0; seg_of(ks, s, k0);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) ra.load_q((uint32_t)(args.seg[s].a_col0 + k0), q);
+    }
+    load_w(rw, ks);
+    load_w(rw_next, ks + 1);
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);   // see the forward kernel
+    __syncthreads();
+    const int n_iter = ke - ks + 1;
+    // as in the forward kernel: two register sets for W alternating without copies,
+    // prefetches on every path, the low-rank stage multiplying only its non-zero k
+    // steps, then the K stages in pairs (one zero padding stage if their count is odd)
+    auto step = [&](int it, typename WBwdFast<FMT>::Regs& R, auto low_rank) {
+      const int cur = it & 1;
+      uint16_t* na = sm.u.k.a[cur ^ 1];
+      uint16_t* nw = sm.u.k.w[cur ^ 1];
+      const bool past = ks + it + 1 >= ke;
+      uint32_t col;
+      { int s, k0; seg_of(past ? ke - 1 : ks + it + 1, s, k0); col = (uint32_t)(args.seg[s].a_col0 + k0); }
+      const float a0 = FMT == WF_BF16 ? 0.f : ws.absmax(R, 0);
+      const float a1 = FMT == WF_BF16 ? 0.f : ws.absmax(R, 1);
+      auto work = [&](int q) {
+        ra.store_q(na, q);
+        ra.load_q_or_zero(col, q, past);
+        ws.store_part(R, nw, sm.lut2, q, a0, a1);
+      };
+      if constexpr (decltype(low_rank)::value)
+        mma_stage_n<NT_FAST>(sm.u.k.a[cur], sm.u.k.w[cur], acc, (ext_cols + 15) / 16, work);
+      else
+        mma_stage<NT_FAST>(sm.u.k.a[cur], sm.u.k.w[cur], acc, work);
+      load_w(R, ks + it + 2);
+      __syncthreads();
+    };
+    step(0, rw, std::true_type{});
+    for (int it = 1; it < n_iter; it += 2) {
+      step(it, rw_next, std::false_type{});
+      step(it + 1, rw, std::false_type{});
+    }
+
+    if (pc.slot >= 0 && !combine_pieces<NT_FAST>(acc, args.sk.part, args.sk.cnt, pc.slot, pc.idx, split, &sm.sk_flag))
+      return;
+    Epi E;
+    E.f32 = args.out32 != nullptr;
+    E.out = E.f32 ? (void*)args.out32 : (void*)args.out16;
+    E.ldo = args.ldo;
+    E.gu = args.gu32; E.ldgu = args.ldgu;
+    E.r32 = args.resid32; E.ldr = args.ldo;
+    epilogue<NT_FAST>(sm, acc, m0, j0, args.M, args.N, E);
+  }
 }
 
 // --------------------------------------------------------- standalone dequant
@@ -1320,6 +1428,40 @@ hipError_t launch_fmt(int format, F&& f) {
   }
 }
 
+// compute units of the current device, read once per device
+int cu_count() {
+  static int cached[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess) cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+// Grid of a fast launch of `total` tiles of nk K stages.  Split the tail (the tiles
+// past the last full round of compute units) when scratch is given and the tail would
+// leave the last round at most 7/8 full: each tail tile becomes `split` pieces, as
+// many as fill the round (at most 8, each at least 4 K stages).
+void plan_split(const SplitTiles& sk, int total, int nk, int& grid, int& n_whole, int& split) {
+  grid = (total + 7) / 8 * 8;
+  n_whole = total;
+  split = 1;
+  if (!sk.part || !sk.cnt) return;
+  const int P = cu_count();
+  if (P <= 0 || P % 8 != 0 || sk.slots < P) return;
+  const int tail = total % P;
+  if (tail == 0 || tail % 8 != 0 || tail > P / 8 * 7) return;
+  int S = P / tail;
+  if (S > 8) S = 8;
+  if (S > nk / 4) S = nk / 4;
+  if (S < 2) return;
+  n_whole = total - tail;
+  split = S;
+  grid = n_whole + tail * S;
+}
+
 }  // namespace
 
 hipError_t launch_gemm_fwd(const FwdArgs& a, hipStream_t s) {
@@ -1339,16 +1481,22 @@ hipError_t launch_gemm_fwd(const FwdArgs& a, hipStream_t s) {
       return hipErrorInvalidValue;
     const int pt = (a.g[0].w.n_out + BN / 2 - 1) / (BN / 2);
     const int ptotal = m_tiles * pt;
-    const int ppadded = (ptotal + 7) / 8 * 8;
+    int grid, n_whole, split;
+    plan_split(a.sk, ptotal, a.K / BK, grid, n_whole, split);
     return launch_fmt(a.format, [&](auto fmt) {
       constexpr int F = decltype(fmt)::value;
-      hipLaunchKernelGGL((k_gemm_fwd_fast<F, true>), dim3(ppadded), dim3(NT_FAST), sizeof(Smem), s, a, pt, ptotal, ppadded);
+      hipLaunchKernelGGL((k_gemm_fwd_fast<F, true>), dim3(grid), dim3(NT_FAST), sizeof(Smem), s, a, pt, ptotal, grid,
+                         n_whole, split);
       return hipGetLastError();
     });
   }
+  int grid = padded, n_whole = total, split = 1;
+  if (fast) plan_split(a.sk, total, a.K / BK, grid, n_whole, split);
   return launch_fmt(a.format, [&](auto fmt) {
     constexpr int F = decltype(fmt)::value;
-    if (fast) hipLaunchKernelGGL((k_gemm_fwd_fast<F, false>), dim3(padded), dim3(NT_FAST), sizeof(Smem), s, a, n_tiles, total, padded);
+    if (fast)
+      hipLaunchKernelGGL((k_gemm_fwd_fast<F, false>), dim3(grid), dim3(NT_FAST), sizeof(Smem), s, a, n_tiles, total, grid,
+                         n_whole, split);
     else hipLaunchKernelGGL((k_gemm_fwd<F, false>), dim3(padded), dim3(NTHREADS), sizeof(Smem), s, a, n_tiles, total, padded);
     return hipGetLastError();
   });
@@ -1374,9 +1522,17 @@ hipError_t launch_gemm_bwd(const BwdArgs& a, hipStream_t s) {
     return hipErrorInvalidValue;
   BwdArgs k = a;
   if (k.kx > BK) k.kx = BK;
+  int grid = padded, n_whole = total, split = 1;
+  if (fast) {
+    int total_k = 0;
+    for (int sg = 0; sg < a.n_segs; ++sg) total_k += a.seg[sg].w.n_out / BK;
+    plan_split(a.sk, total, total_k, grid, n_whole, split);
+  }
   hipError_t e = launch_fmt(a.format, [&](auto fmt) {
     constexpr int F = decltype(fmt)::value;
-    if (fast) hipLaunchKernelGGL(k_gemm_bwd_fast<F>, dim3(padded), dim3(NT_FAST), sizeof(Smem), s, k, n_tiles, total, padded);
+    if (fast)
+      hipLaunchKernelGGL(k_gemm_bwd_fast<F>, dim3(grid), dim3(NT_FAST), sizeof(Smem), s, k, n_tiles, total, grid, n_whole,
+                         split);
     else hipLaunchKernelGGL((k_gemm_bwd<F, false>), dim3(padded), dim3(NTHREADS), sizeof(Smem), s, k, n_tiles, total, padded);
     return hipGetLastError();
   });

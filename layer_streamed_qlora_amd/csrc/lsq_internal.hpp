@@ -72,6 +72,18 @@ struct FwdGroup {
   int32_t ext_col0 = 0;            // first column of this group's extension operand in Aext
   const uint16_t* bext = nullptr;  // bf16 [n_out, kx]: LoRA B (already in bf16), row stride kx
 };
+// Scratch for split tiles (stream-K) in the fused dequant GEMMs.  With `part` set, a
+// launch whose tile count is above the number of compute units and not a multiple of
+// it runs one workgroup per compute unit over equal shares of its (tile, K stage)
+// work; a tile cut between two workgroups meets in part ([slots][2][256 * 256]
+// float32) and cnt ([slots], zero before the launch and left zero after it).  slots
+// must be at least the number of compute units.  Launches that share one scratch
+// must not overlap in time (one stream per scratch).
+struct SplitTiles {
+  float* part = nullptr;
+  uint32_t* cnt = nullptr;
+  int32_t slots = 0;
+};
 struct FwdArgs {
   const uint16_t* x = nullptr; int32_t ldx = 0;     // bf16 [M, K]
   int32_t M = 0, K = 0;
@@ -91,6 +103,7 @@ struct FwdArgs {
   // is set, gate and up in float32 ([M, ldgu], up at column + n_out)
   int32_t swiglu = 0;
   float* gu32 = nullptr; int32_t ldgu = 0;
+  SplitTiles sk;
 };
 hipError_t launch_gemm_fwd(const FwdArgs& a, hipStream_t s);
 
@@ -116,6 +129,7 @@ struct BwdArgs {
   // SwiGLU backward: the product is d(act); with gate, up from gu32 (float32 [M, ldgu],
   // up at column + N) out16 receives dgate | dup (bf16 [M, ldo], dup at column + N)
   const float* gu32 = nullptr; int32_t ldgu = 0;
+  SplitTiles sk;
 };
 hipError_t launch_gemm_bwd(const BwdArgs& a, hipStream_t s);
 

@@ -36,6 +36,9 @@ namespace {
 
 constexpr int kPad = 256;    // slack after every workspace region (8-element group loads)
 constexpr int kMaxSplit = 16;
+// compute units the split-tile scratch of the dequant GEMMs serves (MI355X: 256); on
+// a device with more, the GEMMs run whole tiles only
+constexpr int kSplitSlots = 256;
 
 struct LoraReg {
   const float* A = nullptr;
@@ -58,6 +61,9 @@ struct DevPlan {
   uint64_t dya = 0, dyb = 0, dh32 = 0, dh16 = 0, dgu = 0, datt = 0, dqkv = 0, dqkv32 = 0, dn32 = 0;
   uint64_t dkv2 = 0;   // dk | dv of the second half of each kv head's q heads, float32
   uint64_t lora = 0, lora_per_layer = 0, partial = 0, partial_bytes = 0;
+  // split-tile scratch of the dequant GEMMs, one set per stream that launches them
+  // (the compute stream and the recompute stream): float32 partial tiles, counters
+  uint64_t skpart[2] = {}, skcnt[2] = {};
   uint64_t levels = 0, rope = 0;
   // AdamW: moments m then v (moment_elems floats each) and the chunk table
   uint64_t moments = 0, moment_elems = 0, adam_tab = 0, adam_max_chunks = 0;
@@ -153,6 +159,15 @@ DevPlan make_plan(const ls_config& c, const BlobLayout& L) {
   // split-K partials of the rank-r reductions: up to kMaxSplit chunks of [rows, r16]
   P.partial_bytes = 4ull * kMaxSplit * std::max<uint64_t>(std::max<uint64_t>(T, I), std::max<uint64_t>(h, qkvd)) * 3 * r16;
   P.partial = take(P.partial_bytes);
+  {
+    // only when some dequant GEMM has more 256 x 256 tiles than one round of compute units
+    const uint64_t widest = std::max<uint64_t>(std::max<uint64_t>(qkvd, 2 * I), std::max<uint64_t>(std::max(h, qd), (uint64_t)P.head_rows));
+    if ((T + 255) / 256 * ((widest + 255) / 256) > (uint64_t)kSplitSlots)
+      for (int k = 0; k < 2; ++k) {
+        P.skpart[k] = take(4ull * 256 * 256 * kSplitSlots);
+        P.skcnt[k] = take(4ull * kSplitSlots);
+      }
+  }
   P.levels = take(64);
   P.rope = take(8ull * (uint64_t)c.max_seq * (uint64_t)(c.head_dim / 2));
   if (c.adamw) {
@@ -273,6 +288,17 @@ struct ls_ctx {
   Prof prof;
 
   template <class T> T* dp(uint64_t off) const { return reinterpret_cast<T*>(dbase + off); }
+  // split-tile scratch of the dequant GEMMs launched on stream s (the recompute stream
+  // has its own set: its GEMMs run beside the compute stream's)
+  SplitTiles split_scratch(hipStream_t s) const {
+    SplitTiles t;
+    const int k = s == rs ? 1 : 0;
+    if (plan.skpart[k] == 0) return t;
+    t.part = dp<float>(plan.skpart[k]);
+    t.cnt = dp<uint32_t>(plan.skcnt[k]);
+    t.slots = kSplitSlots;
+    return t;
+  }
 };
 
 static std::string g_create_err;
@@ -766,6 +792,7 @@ ls_status layer_forward(ls_ctx* c, int l, const uint8_t* blob, const Dims& d, co
     f.rope_tab = c->dp<float2>(c->plan.rope); f.rope_cols = d.qd + d.kvd; f.seq = d.seq; f.head_dim = d.hd;
     KTimer kt(c, LS_KC_GEMM_FWD, fwd_gemm_flop(d, d.qkvd, d.h, lora),
               tb * d.h + wbytes(c, 0) + wbytes(c, 1) + wbytes(c, 2) + tb * d.qkvd, s);
+    f.sk = c->split_scratch(s);
     HIPCHK(c, launch_gemm_fwd(f, s));
   }
   {
@@ -786,6 +813,7 @@ ls_status layer_forward(ls_ctx* c, int l, const uint8_t* blob, const Dims& d, co
     f.resid = x_in; f.ldr = d.h;
     f.y32 = hb; f.ldy = d.h; f.levels = lv; f.format = fmt;
     KTimer kt(c, LS_KC_GEMM_FWD, fwd_gemm_flop(d, d.h, d.qd, lora), tb * d.qd + wbytes(c, 3) + 3 * tb * d.h, s);
+    f.sk = c->split_scratch(s);
     HIPCHK(c, launch_gemm_fwd(f, s));
   }
   {
@@ -817,6 +845,7 @@ ls_status layer_forward(ls_ctx* c, int l, const uint8_t* blob, const Dims& d, co
     }
     const double out_bytes = fuse_swiglu ? tb * d.I + (mode == MODE_RECOMPUTE ? 2 * tb * 2 * d.I : 0.0) : 2 * tb * 2 * d.I;
     KTimer kt(c, LS_KC_GEMM_FWD, fwd_gemm_flop(d, 2 * d.I, d.h, lora), tb * d.h + wbytes(c, 4) + wbytes(c, 5) + out_bytes, s);
+    f.sk = c->split_scratch(s);
     HIPCHK(c, launch_gemm_fwd(f, s));
   }
   if (!fuse_swiglu) {
@@ -836,6 +865,7 @@ ls_status layer_forward(ls_ctx* c, int l, const uint8_t* blob, const Dims& d, co
     f.resid32 = hb; f.ldr = d.h;
     f.y = x_out; f.ldy = d.h; f.levels = lv; f.format = fmt;
     KTimer kt(c, LS_KC_GEMM_FWD, fwd_gemm_flop(d, d.h, d.I, lora), tb * d.I + wbytes(c, 6) + 3 * tb * d.h, s);
+    f.sk = c->split_scratch(s);
     HIPCHK(c, launch_gemm_fwd(f, s));
   }
   return LS_OK;
@@ -967,6 +997,7 @@ ls_status layer_backward(ls_ctx* c, int l, const uint8_t* blob, const Dims& d, c
     // SwiGLU backward in the epilogue: dgate | dup from d(act) and the recomputed gate, up
     b.out16 = dgu; b.ldo = 2 * d.I; b.gu32 = gu; b.ldgu = 2 * d.I; b.levels = lv; b.format = fmt;
     KTimer kt(c, LS_KC_GEMM_BWD, bwd_flop(d.h, d.I), tb * d.h + wbytes(c, 6) + 2 * tb * 2 * d.I + tb * 2 * d.I);
+    b.sk = c->split_scratch(c->cs);
     HIPCHK(c, launch_gemm_bwd(b, c->cs));
   }
   // ---- gate / up
@@ -981,6 +1012,7 @@ ls_status layer_backward(ls_ctx* c, int l, const uint8_t* blob, const Dims& d, c
     b.bext = lora_at(c, l, c->plan.at_gu); b.ldbext = 2 * d.r16;
     b.out32 = dn32; b.ldo = d.h; b.levels = lv; b.format = fmt;
     KTimer kt(c, LS_KC_GEMM_BWD, 2 * bwd_flop(d.I, d.h), tb * 2 * d.I + wbytes(c, 4) + wbytes(c, 5) + 2 * tb * d.h);
+    b.sk = c->split_scratch(c->cs);
     HIPCHK(c, launch_gemm_bwd(b, c->cs));
   }
   {
@@ -998,6 +1030,7 @@ ls_status layer_backward(ls_ctx* c, int l, const uint8_t* blob, const Dims& d, c
     b.bext = lora_at(c, l, c->plan.at_o); b.ldbext = d.r16;
     b.out16 = datt; b.ldo = d.qd; b.levels = lv; b.format = fmt;
     KTimer kt(c, LS_KC_GEMM_BWD, bwd_flop(d.h, d.qd), tb * d.h + wbytes(c, 3) + tb * d.qd);
+    b.sk = c->split_scratch(c->cs);
     HIPCHK(c, launch_gemm_bwd(b, c->cs));
   }
   if ((st = attn_bwd(c, d, x, datt, dqkv32))) return st;
@@ -1020,6 +1053,7 @@ ls_status layer_backward(ls_ctx* c, int l, const uint8_t* blob, const Dims& d, c
     b.bext = lora_at(c, l, c->plan.at_qkv); b.ldbext = 3 * d.r16;
     b.out32 = dn32; b.ldo = d.h; b.levels = lv; b.format = fmt;
     KTimer kt(c, LS_KC_GEMM_BWD, bwd_flop(d.qkvd, d.h), tb * d.qkvd + wbytes(c, 0) + wbytes(c, 1) + wbytes(c, 2) + 2 * tb * d.h);
+    b.sk = c->split_scratch(c->cs);
     HIPCHK(c, launch_gemm_bwd(b, c->cs));
   }
   // dx may alias dy (a one-layer stack): the side stream's dB product of the down
@@ -1559,6 +1593,7 @@ ls_status ls_base_gemm(ls_ctx* c, int32_t layer, int32_t group, int32_t transpos
     } else {
       f.y32 = out; f.ldy = out_w;
     }
+    f.sk = c->split_scratch(c->cs);
     HIPCHK(c, launch_gemm_fwd(f, c->cs));
   } else {
     BwdArgs b;
@@ -1570,6 +1605,7 @@ ls_status ls_base_gemm(ls_ctx* c, int32_t layer, int32_t group, int32_t transpos
       col += c->lay.p[p0 + i].n_out;
     }
     b.out32 = out; b.ldo = n_in; b.levels = lv; b.format = fmt;
+    b.sk = c->split_scratch(c->cs);
     HIPCHK(c, launch_gemm_bwd(b, c->cs));
   }
   if ((st = release_layer(c, layer))) return st;
@@ -1790,6 +1826,7 @@ ls_status ls_head_loss(ls_ctx* c, const void* Y, const void* Y_ref, const int32_
     a.x = x; a.ldx = h; a.M = T; a.K = h; a.n_groups = 1;
     a.g[0].w = w;
     a.y32 = Z; a.ldy = ldz; a.levels = lv; a.format = WF_BF16;
+    a.sk = c->split_scratch(c->cs);
     KTimer kt(c, LS_KC_HEAD, 2.0 * T * w.n_out * h, 2.0 * T * h + 2.0 * w.n_out * h + 4.0 * T * w.n_out);
     HIPCHK(c, launch_gemm_fwd(a, c->cs));
     return LS_OK;
@@ -1849,6 +1886,7 @@ ls_status ls_head_loss(ls_ctx* c, const void* Y, const void* Y_ref, const int32_
       b.out32 = dyn; b.ldo = h; b.resid32 = j == S - 1 ? nullptr : dyn;
       b.levels = lv; b.format = WF_BF16;
       KTimer kt(c, LS_KC_HEAD, 2.0 * T * vs * h, 2.0 * T * vs + 2.0 * vs * h + 4.0 * T * h * (j == S - 1 ? 1 : 2));
+      b.sk = c->split_scratch(c->cs);
       HIPCHK(c, launch_gemm_bwd(b, c->cs));
     }
     if ((st = release_layer(c, L + j))) return st;
