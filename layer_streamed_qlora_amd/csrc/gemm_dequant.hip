@@ -14,9 +14,9 @@
 // as float32 or decoded from the 8-bit second level as
 // fp32(fp32(fp32(c/127) * scale2) + mean) with no fused multiply-add.
 //
-// A launch whose tiles leave the last round of compute units part full cuts each tile
-// of that round along K into pieces that fill it; the piece that finishes last adds
-// the pieces' float32 sums (piece_of, combine_pieces).
+// A launch whose tiles leave the last (or only) round of compute units part full cuts
+// each tile of that round along K into pieces that fill it; the piece that finishes
+// last adds the pieces' float32 sums (piece_of, combine_pieces).
 //
 // Tile: 256 x 256 outputs per 256-thread workgroup, 2 x 2 waves of 128 x 128
 // (4 x 4 MFMA blocks of 32 x 32, 256 float accumulators per lane), K step 64,
@@ -875,9 +875,9 @@ __device__ __forceinline__ int xcd_tile(int bid, int nblocks_padded) {
 
 // ---- work of one fast-path workgroup: K stages [ks, ke) of one tile.  Without split
 // tiles a workgroup runs one whole tile (xcd_tile order).  With them, the launch's
-// tiles are n_whole whole tiles (full rounds of the compute units) plus a tail of
-// fewer tiles than compute units, each cut into `split` pieces of about nk / split
-// K stages, so the last round is full too.  Every XCD (bid & 7) gets the same share
+// tiles are n_whole whole tiles (full rounds of the compute units, possibly none) plus
+// a tail of fewer tiles than compute units, each cut into `split` pieces of about
+// nk / split K stages, so the last round is fuller.  Every XCD (bid & 7) gets the same share
 // of both: its first n_whole / 8 workgroups run whole tiles, the rest the pieces of
 // its tail / 8 tail tiles.
 struct Piece { int tile, ks, ke, slot, idx; };
@@ -1441,9 +1441,10 @@ int cu_count() {
 }
 
 // Grid of a fast launch of `total` tiles of nk K stages.  Split the tail (the tiles
-// past the last full round of compute units) when scratch is given and the tail would
-// leave the last round at most 7/8 full: each tail tile becomes `split` pieces, as
-// many as fill the round (at most 8, each at least 4 K stages).
+// past the last full round of compute units, or all of them when there are fewer tiles
+// than units) when scratch is given and the tail would leave the last round at most
+// 7/8 full: each tail tile becomes `split` pieces, as many as fit the round (at most
+// 8, each at least 4 K stages).
 void plan_split(const SplitTiles& sk, int total, int nk, int& grid, int& n_whole, int& split) {
   grid = (total + 7) / 8 * 8;
   n_whole = total;

@@ -72,13 +72,13 @@ struct FwdGroup {
   int32_t ext_col0 = 0;            // first column of this group's extension operand in Aext
   const uint16_t* bext = nullptr;  // bf16 [n_out, kx]: LoRA B (already in bf16), row stride kx
 };
-// Scratch for split tiles (stream-K) in the fused dequant GEMMs.  With `part` set, a
-// launch whose tile count is above the number of compute units and not a multiple of
-// it runs one workgroup per compute unit over equal shares of its (tile, K stage)
-// work; a tile cut between two workgroups meets in part ([slots][2][256 * 256]
-// float32) and cnt ([slots], zero before the launch and left zero after it).  slots
-// must be at least the number of compute units.  Launches that share one scratch
-// must not overlap in time (one stream per scratch).
+// Scratch for split tiles in the fused dequant GEMMs.  With `part` set, a launch whose
+// last (or only) round of 256 x 256 tiles leaves at least 1/8 of the compute units idle
+// cuts each tile of that round along K into pieces, one workgroup each; the pieces of
+// a tile meet in part (float32 partial tiles, room for `slots` tiles) and cnt ([slots]
+// arrival counters, zero before the launch and left zero after it).  slots must be at
+// least the number of compute units.  Launches that share one scratch must not overlap
+// in time (one stream per scratch).
 struct SplitTiles {
   float* part = nullptr;
   uint32_t* cnt = nullptr;

@@ -113,41 +113,43 @@ def test_qwen32b_layer_251mb_blob():
 
 def test_llama8b_split_tiles_random_activations():
     """The tail-split launches (the tiles past the last full round of compute units cut
-    into K ranges whose float32 sums are added by the piece that finishes last): at
-    4096 rows the Llama-3.1-8B-shaped q|k|v forward (384 tiles of 256 x 256) and the
-    down projection's W^T orientation (896 tiles) both take them.  With random
-    activations every sampled output row must match the float64 product of the same
-    bf16 activations and the oracle's dequantised weights within the float32
-    accumulation bound K 2^-23 sum |x w|, and a second call must give the same bits."""
+    into K ranges whose float32 sums the piece that finishes last adds in piece order),
+    with random activations on the Llama-3.1-8B shapes: the q|k|v forward at 4096 rows
+    (384 tiles of 256 x 256: two pieces per tail tile), the down projection's W^T
+    orientation at 4096 rows (896 tiles: two pieces), the down forward at 1024 rows (64
+    tiles: four pieces) and the q|k|v W^T orientation at 512 rows (32 tiles: eight
+    pieces).  Every sampled output row must match the float64 product of the same bf16
+    activations and the oracle's dequantised weights within the float32 accumulation
+    bound K 2^-23 sum |x w|, and a second call must give the same bits."""
     torch = pytest.importorskip("torch")
     w = synth.WORKLOADS["llama8b"].with_(batch=1, seq=128)
-    say("case: split-tile dequant GEMMs, llama8b layer 7, random activations, 4096 rows")
+    say("case: split-tile dequant GEMMs, llama8b layer 7, random activations")
     run = H.GpuRun(w, [7], max_tokens=M_MAX, max_seq=128)
     deq = oracle_dequant(w, run.src[0])
     run.src = None
     g = torch.Generator(device="cpu").manual_seed(1234)
-    rows = np.concatenate([np.arange(mt * 256, mt * 256 + 256, 37) for mt in range(M_MAX // 256)])
-    for gi, transposed in ((0, 0), (3, 1)):
+    for gi, transposed, m in ((0, 0, 4096), (3, 1, 4096), (3, 0, 1024), (0, 1, 512)):
         projs = GROUPS[gi]
         wmat = np.concatenate([deq[p] for p in projs], axis=0).astype(np.float64)   # [sum n_out, n_in]
         b = wmat if transposed else wmat.T                                          # [K, N]
         k_dim, n_dim = b.shape
-        x = torch.randn((M_MAX, k_dim), generator=g).to(torch.bfloat16)
+        x = torch.randn((m, k_dim), generator=g).to(torch.bfloat16)
         xd = x.to("cuda:0")
         outs = []
         for _ in range(2):
-            out = torch.empty((M_MAX, n_dim), dtype=torch.float32, device="cuda:0")
-            run.ctx.base_gemm(0, gi, transposed, xd.data_ptr(), M_MAX, out.data_ptr())
+            out = torch.empty((m, n_dim), dtype=torch.float32, device="cuda:0")
+            run.ctx.base_gemm(0, gi, transposed, xd.data_ptr(), m, out.data_ptr())
             outs.append(out.cpu().numpy())
             del out
         assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32)), (projs, "not deterministic")
+        rows = np.concatenate([np.arange(mt * 256, min(m, mt * 256 + 256), 37) for mt in range((m + 255) // 256)])
         xs = x.float().numpy().astype(np.float64)[rows]
         exp = xs @ b
         bound = k_dim * 2.0 ** -23 * (np.abs(xs) @ np.abs(b)) + 1e-30
         err = np.abs(outs[0][rows].astype(np.float64) - exp)
         worst = float((err / bound).max())
-        say(f"{'+'.join(projs)} {'W^T' if transposed else 'W'}: {len(rows)} rows x {n_dim}, "
+        say(f"{'+'.join(projs)} {'W^T' if transposed else 'W'} at {m} rows: {len(rows)} rows x {n_dim}, "
             f"worst error / bound {worst:.3g}")
-        assert worst <= 1.0, (projs, transposed, worst)
+        assert worst <= 1.0, (projs, transposed, m, worst)
         del xd
     run.close()
