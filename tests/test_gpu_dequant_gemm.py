@@ -117,8 +117,8 @@ def test_llama8b_split_tiles_random_activations():
     with random activations on the Llama-3.1-8B shapes: the q|k|v forward at 4096 rows
     (384 tiles of 256 x 256: two pieces per tail tile), the down projection's W^T
     orientation at 4096 rows (896 tiles: two pieces), the down forward at 1024 rows (64
-    tiles: four pieces) and the q|k|v W^T orientation at 512 rows (32 tiles: eight
-    pieces).  Every sampled output row must match the float64 product of the same bf16
+    tiles: four pieces; again at 1000 rows, a ragged last row block) and the q|k|v W^T
+    orientation at 512 rows (32 tiles: eight pieces).  Every sampled output row must match the float64 product of the same bf16
     activations and the oracle's dequantised weights within the float32 accumulation
     bound K 2^-23 sum |x w|, and a second call must give the same bits."""
     torch = pytest.importorskip("torch")
@@ -128,7 +128,7 @@ def test_llama8b_split_tiles_random_activations():
     deq = oracle_dequant(w, run.src[0])
     run.src = None
     g = torch.Generator(device="cpu").manual_seed(1234)
-    for gi, transposed, m in ((0, 0, 4096), (3, 1, 4096), (3, 0, 1024), (0, 1, 512)):
+    for gi, transposed, m in ((0, 0, 4096), (3, 1, 4096), (3, 0, 1024), (0, 1, 512), (3, 0, 1000)):
         projs = GROUPS[gi]
         wmat = np.concatenate([deq[p] for p in projs], axis=0).astype(np.float64)   # [sum n_out, n_in]
         b = wmat if transposed else wmat.T                                          # [K, N]
