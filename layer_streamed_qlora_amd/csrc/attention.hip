@@ -21,6 +21,7 @@
 #include <cmath>
 
 #include "lsq_internal.hpp"
+#include "rope.hpp"
 #include "tiles.hpp"
 
 namespace lsq {
@@ -267,7 +268,27 @@ __global__ void __launch_bounds__(256, 2) k_attn_dq(AttnArgs a) {   // two workg
       }
     }
   }
-  if (qok) {
+  if (qok && a.dq16) {
+    // bf16 with the inverse rotation: column c (< HD/2) pairs with c + HD/2, which this
+    // lane holds in block d + ND/2 of the same register positions
+    uint16_t* dst = a.dq16 + ((int64_t)b * a.S + q) * a.lddq16 + h * HD;
+    const float2* tab = a.rope_tab + (int64_t)q * (HD / 2);
+#pragma unroll
+    for (int d = 0; d < ND / 2; ++d)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int col = 32 * d + 8 * g4 + 4 * hh;
+        const float4 t01 = *reinterpret_cast<const float4*>(tab + col);
+        const float4 t23 = *reinterpret_cast<const float4*>(tab + col + 2);
+        const float2 cs[4] = {make_float2(t01.x, t01.y), make_float2(t01.z, t01.w), make_float2(t23.x, t23.y),
+                              make_float2(t23.z, t23.w)};
+        float2 g[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) g[e] = rope_inverse(dq[d][4 * g4 + e], dq[d + ND / 2][4 * g4 + e], cs[e]);
+        *reinterpret_cast<uint2*>(dst + col) = make_uint2(pack2(g[0].x, g[1].x), pack2(g[2].x, g[3].x));
+        *reinterpret_cast<uint2*>(dst + col + HD / 2) = make_uint2(pack2(g[0].y, g[1].y), pack2(g[2].y, g[3].y));
+      }
+  } else if (qok) {
     float* dst = a.dqkv + ((int64_t)b * a.S + q) * a.lddqkv + h * HD;
 #pragma unroll
     for (int d = 0; d < ND; ++d)
@@ -432,6 +453,9 @@ hipError_t launch_attn_bwd(const AttnArgs& a, hipStream_t s) {
   if (a.batch <= 0 || a.S <= 0) return hipSuccess;
   if (!shape_ok(a) || !a.qkv || !a.out32 || !a.dout || !a.lse || !a.dd || !a.dqkv || a.lddo % 8 != 0 ||
       a.lddqkv % 4 != 0 || (a.dkv2 && (a.hq / a.hkv) % 2 != 0))
+    return hipErrorInvalidValue;
+  if (a.dq16 && (!a.rope_tab || a.lddq16 < a.qd || a.lddq16 % 4 != 0 || (reinterpret_cast<uintptr_t>(a.dq16) & 7) ||
+                 (reinterpret_cast<uintptr_t>(a.rope_tab) & 15)))
     return hipErrorInvalidValue;
   return a.hd == 64 ? bwd_hd<64>(a, s) : bwd_hd<128>(a, s);
 }

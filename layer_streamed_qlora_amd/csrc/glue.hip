@@ -12,6 +12,7 @@
 #include <stdint.h>
 
 #include "lsq_internal.hpp"
+#include "rope.hpp"
 
 namespace lsq {
 namespace {
@@ -193,14 +194,14 @@ __global__ void __launch_bounds__(256) k_rmsnorm_bwd_v(const float* dn, const XT
   }
 }
 
-// float32 -> bf16 with the inverse rotation on the first nh heads; one thread per
-// (token, column pair or lone column)
-__global__ void k_rope_bwd_convert(const float* src, uint16_t* dst, int ld, int64_t T, int seq, int nh, int hd,
-                                   const float2* tab, const float* add, int add_col0, int add_ld) {
+// float32 -> bf16 with the inverse rotation on the first nh heads of each row's first
+// `width` columns (row stride ld); one thread per (token, column pair or lone column)
+__global__ void k_rope_bwd_convert(const float* src, uint16_t* dst, int ld, int width, int64_t T, int seq, int nh,
+                                   int hd, const float2* tab, const float* add, int add_col0, int add_ld) {
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int half = hd / 2;
   const int rope_pairs = nh * half;                    // rotated column pairs per row
-  const int rest = ld - nh * hd;                        // plain columns per row
+  const int rest = width - nh * hd;                     // plain columns per row
   const int per_row = rope_pairs + rest;
   if (idx >= T * per_row) return;
   const int64_t t = idx / per_row;
@@ -216,9 +217,9 @@ __global__ void k_rope_bwd_convert(const float* src, uint16_t* dst, int ld, int6
     const int h = c / half, i = c % half;
     const int col = h * hd + i;
     const float2 cs = tab[(int64_t)(t % seq) * half + i];
-    const float d1 = rd(col), d2 = rd(col + half);
-    d[col] = tobf(d1 * cs.x + d2 * cs.y);
-    d[col + half] = tobf(d2 * cs.x - d1 * cs.y);
+    const float2 g = rope_inverse(rd(col), rd(col + half), cs);
+    d[col] = tobf(g.x);
+    d[col + half] = tobf(g.y);
   } else {
     const int col = nh * hd + (c - rope_pairs);
     d[col] = tobf(rd(col));
@@ -226,12 +227,12 @@ __global__ void k_rope_bwd_convert(const float* src, uint16_t* dst, int ld, int6
 }
 
 // Same, 4 rotated column pairs or 8 plain columns per thread (hd % 8 == 0, ld % 8 == 0)
-__global__ void k_rope_bwd_convert_v(const float* src, uint16_t* dst, int ld, int64_t T, int seq, int nh, int hd,
-                                     const float2* tab, const float* add, int add_col0, int add_ld) {
+__global__ void k_rope_bwd_convert_v(const float* src, uint16_t* dst, int ld, int width, int64_t T, int seq, int nh,
+                                     int hd, const float2* tab, const float* add, int add_col0, int add_ld) {
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int half = hd / 2, gp = half / 4;
   const int rope_groups = nh * gp;
-  const int per_row = rope_groups + (ld - nh * hd) / 8;
+  const int per_row = rope_groups + (width - nh * hd) / 8;
   if (idx >= T * per_row) return;
   const int64_t t = idx / per_row;
   const int c = (int)(idx % per_row);
@@ -258,8 +259,10 @@ __global__ void k_rope_bwd_convert_v(const float* src, uint16_t* dst, int ld, in
     uint32_t o1[2], o2[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      f32x2_t u = {a1[2 * j] * cs[2 * j] + a2[2 * j] * sn[2 * j], a1[2 * j + 1] * cs[2 * j + 1] + a2[2 * j + 1] * sn[2 * j + 1]};
-      f32x2_t v = {a2[2 * j] * cs[2 * j] - a1[2 * j] * sn[2 * j], a2[2 * j + 1] * cs[2 * j + 1] - a1[2 * j + 1] * sn[2 * j + 1]};
+      const float2 g0 = rope_inverse(a1[2 * j], a2[2 * j], make_float2(cs[2 * j], sn[2 * j]));
+      const float2 g1 = rope_inverse(a1[2 * j + 1], a2[2 * j + 1], make_float2(cs[2 * j + 1], sn[2 * j + 1]));
+      f32x2_t u = {g0.x, g1.x};
+      f32x2_t v = {g0.y, g1.y};
       o1[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector(u, bf16x2_t));
       o2[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
     }
@@ -373,23 +376,25 @@ hipError_t launch_rmsnorm_bwd(const float* dn, const uint16_t* x16, const float*
   return hipGetLastError();
 }
 
-hipError_t launch_rope_bwd_convert(const float* src, uint16_t* dst, int32_t ld, int32_t T, int32_t seq, int32_t nh,
-                                   int32_t hd, const float2* tab, hipStream_t s, const float* add, int32_t add_col0,
-                                   int32_t add_ld) {
-  if (add && (add_col0 < 0 || add_col0 > ld || add_ld < ld - add_col0)) return hipErrorInvalidValue;
-  if (hd % 8 == 0 && ld % 8 == 0 && (ld - nh * hd) % 8 == 0 &&
+hipError_t launch_rope_bwd_convert(const float* src, uint16_t* dst, int32_t ld, int32_t width, int32_t T, int32_t seq,
+                                   int32_t nh, int32_t hd, const float2* tab, hipStream_t s, const float* add,
+                                   int32_t add_col0, int32_t add_ld) {
+  if (width < nh * hd || width > ld) return hipErrorInvalidValue;
+  if (add && (add_col0 < 0 || add_col0 > width || add_ld < width - add_col0)) return hipErrorInvalidValue;
+  if (hd % 8 == 0 && ld % 8 == 0 && (width - nh * hd) % 8 == 0 && (reinterpret_cast<uintptr_t>(src) & 15) == 0 &&
+      (reinterpret_cast<uintptr_t>(dst) & 15) == 0 &&
       (!add || (add_col0 % 4 == 0 && add_ld % 4 == 0 && (reinterpret_cast<uintptr_t>(add) & 15) == 0))) {
-    const int64_t n = (int64_t)T * ((int64_t)nh * (hd / 8) + (ld - nh * hd) / 8);
+    const int64_t n = (int64_t)T * ((int64_t)nh * (hd / 8) + (width - nh * hd) / 8);
     if (n <= 0) return hipSuccess;
-    hipLaunchKernelGGL(k_rope_bwd_convert_v, dim3(blocks_for(n, 256)), dim3(256), 0, s, src, dst, ld, (int64_t)T, seq,
-                       nh, hd, tab, add, add_col0, add_ld);
+    hipLaunchKernelGGL(k_rope_bwd_convert_v, dim3(blocks_for(n, 256)), dim3(256), 0, s, src, dst, ld, width, (int64_t)T,
+                       seq, nh, hd, tab, add, add_col0, add_ld);
     return hipGetLastError();
   }
-  const int64_t per_row = (int64_t)nh * (hd / 2) + (ld - nh * hd);
+  const int64_t per_row = (int64_t)nh * (hd / 2) + (width - nh * hd);
   const int64_t n = (int64_t)T * per_row;
   if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_rope_bwd_convert, dim3(blocks_for(n, 256)), dim3(256), 0, s, src, dst, ld, (int64_t)T, seq, nh,
-                     hd, tab, add, add_col0, add_ld);
+  hipLaunchKernelGGL(k_rope_bwd_convert, dim3(blocks_for(n, 256)), dim3(256), 0, s, src, dst, ld, width, (int64_t)T, seq,
+                     nh, hd, tab, add, add_col0, add_ld);
   return hipGetLastError();
 }
 

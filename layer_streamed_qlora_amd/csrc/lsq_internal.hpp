@@ -207,6 +207,11 @@ struct AttnArgs {
   // here, those of the first half to dqkv; the caller adds the two (see
   // launch_rope_bwd_convert).  When unset, dqkv receives the whole sums.
   float* dkv2 = nullptr;
+  // backward, optional: dq in bf16 with the inverse rotary embedding already applied
+  // (rope.hpp; rope_tab[pos * hd/2 + i] = (cos, sin)), [batch * S, lddq16], instead of
+  // float32 in dqkv (whose q columns are then left as they were)
+  uint16_t* dq16 = nullptr; int32_t lddq16 = 0;
+  const float2* rope_tab = nullptr;
   // forward: per query row (m, l) = the row maximum of the base-2 scaled scores and the sum
   // of exp2(t - m), [batch * hq * S]; written if stats_out is set; if stats_in holds the
   // values of an earlier forward over the same q, k, the first pass is skipped
@@ -237,11 +242,12 @@ hipError_t launch_rmsnorm_fwd(const uint16_t* x16, const float* x32, const uint1
 hipError_t launch_rmsnorm_bwd(const float* dn, const uint16_t* x16, const float* x32, const uint16_t* g,
                               const float* rstd, const float* dres32, const uint16_t* dres16, float* dx32,
                               uint16_t* dx16, int32_t T, int32_t D, hipStream_t s);
-// float32 [T, ld] -> bf16 [T, ld], inverse rotary embedding on the first nh heads.  With
-// add set, columns [add_col0, ld) first get add[t * add_ld + column - add_col0] added
+// The first `width` columns of float32 rows [T, stride ld] -> bf16 rows of the same
+// stride, inverse rotary embedding (rope.hpp) on the first nh heads.  With add set,
+// columns [add_col0, width) first get add[t * add_ld + column - add_col0] added
 // (float32, same rounding order on every call).
-hipError_t launch_rope_bwd_convert(const float* src, uint16_t* dst, int32_t ld, int32_t T, int32_t seq, int32_t nh,
-                                   int32_t hd, const float2* tab, hipStream_t s,
+hipError_t launch_rope_bwd_convert(const float* src, uint16_t* dst, int32_t ld, int32_t width, int32_t T, int32_t seq,
+                                   int32_t nh, int32_t hd, const float2* tab, hipStream_t s,
                                    const float* add = nullptr, int32_t add_col0 = 0, int32_t add_ld = 0);
 // rotary embedding in place on the first nh heads of a token-major [T, ld] bf16
 // buffer; tab[pos * hd/2 + i] = (cos, sin) of pos * theta^(-2i/hd)

@@ -725,13 +725,17 @@ ls_status attn_fwd(ls_ctx* c, const Dims& d, const uint16_t* qkv, uint16_t* out,
 }
 
 // Attention backward from dO (datt), O (att) and the log-sum-exp of the recompute ->
-// float32 dq, dk, dv in dqkv32 (dk, dv summed over a kv head's q heads, fixed order).
-ls_status attn_bwd(ls_ctx* c, const Dims& d, const Acts& x, const uint16_t* dout, float* dqkv32) {
+// dq in bf16, rotated back, in the q columns of dqkv16; float32 dk, dv in dqkv32 (summed
+// over a kv head's q heads, fixed order).
+ls_status attn_bwd(ls_ctx* c, const Dims& d, const Acts& x, const uint16_t* dout, float* dqkv32, uint16_t* dqkv16) {
   AttnArgs a = attn_args(d, x.qkv, x.att, x.lse);
   a.out32 = x.o32;
   a.dout = dout; a.lddo = d.qd;
   a.dd = c->dp<float>(c->plan.dd);
   a.dqkv = dqkv32; a.lddqkv = d.qkvd;
+  // dq leaves the kernel in bf16 with the inverse rotation applied, straight into the
+  // q columns of the bf16 dq | dk | dv the q|k|v backward reads
+  a.dq16 = dqkv16; a.lddq16 = d.qkvd; a.rope_tab = c->dp<float2>(c->plan.rope);
   // with an even number of q heads per kv head, dK / dV run in two halves of the heads
   // (twice the workgroups, so the short key blocks fill in behind the long ones)
   a.dkv2 = (d.hq / d.hkv) % 2 == 0 ? c->dp<float>(c->plan.dkv2) : nullptr;
@@ -1033,13 +1037,14 @@ ls_status layer_backward(ls_ctx* c, int l, const uint8_t* blob, const Dims& d, c
     b.sk = c->split_scratch(c->cs);
     HIPCHK(c, launch_gemm_bwd(b, c->cs));
   }
-  if ((st = attn_bwd(c, d, x, datt, dqkv32))) return st;
+  if ((st = attn_bwd(c, d, x, datt, dqkv32, dqkv))) return st;
   {
-    KTimer kt(c, LS_KC_GLUE, 0.0, 3 * tb * d.qkvd);
-    // dK | dV of the second half of the q heads join here (see attn_bwd)
+    // dk | dv: the second half of the q heads joins here (see attn_bwd), then the
+    // inverse rotation on dk and bf16 (dq is already in place)
+    KTimer kt(c, LS_KC_GLUE, 0.0, 3 * tb * 2 * d.kvd);
     const float* dkv2 = (d.hq / d.hkv) % 2 == 0 ? c->dp<float>(c->plan.dkv2) : nullptr;
-    HIPCHK(c, launch_rope_bwd_convert(dqkv32, dqkv, d.qkvd, d.T, d.seq, d.hq + d.hkv, d.hd, c->dp<float2>(c->plan.rope),
-                                      c->cs, dkv2, d.qd, 2 * d.kvd));
+    HIPCHK(c, launch_rope_bwd_convert(dqkv32 + d.qd, dqkv + d.qd, d.qkvd, 2 * d.kvd, d.T, d.seq, d.hkv, d.hd,
+                                      c->dp<float2>(c->plan.rope), c->cs, dkv2, 0, 2 * d.kvd));
   }
   // ---- q, k, v
   const int cols[3] = {0, d.qd, d.qd + d.kvd};
