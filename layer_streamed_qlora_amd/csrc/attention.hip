@@ -169,6 +169,33 @@ __global__ void __launch_bounds__(256) k_attn_fwd(AttnArgs a) {
   }
 }
 
+// ------------------------------------------------------- backward: rowsum(dO * O)
+template <int HD>
+__global__ void k_attn_dd(AttnArgs a) {
+  constexpr int TPR = HD / 8;                       // threads per (row, head)
+  const int64_t idx = (int64_t)blockIdx.x * (256 / TPR) + threadIdx.x / TPR;   // row * hq + head
+  const int part = threadIdx.x % TPR;
+  const int64_t n = (int64_t)a.batch * a.S * a.hq;
+  float acc = 0.f;
+  const bool ok = idx < n;
+  const int64_t row = ok ? idx / a.hq : 0;
+  const int head = ok ? (int)(idx % a.hq) : 0;
+  if (ok) {
+    // O in float32 (the product P V before rounding): sum_d dO O = sum_j P_j dP_j
+    const uint4 x = *reinterpret_cast<const uint4*>(a.dout + row * a.lddo + head * HD + 8 * part);
+    const float4 y0 = *reinterpret_cast<const float4*>(a.out32 + row * a.ldo + head * HD + 8 * part);
+    const float4 y1 = *reinterpret_cast<const float4*>(a.out32 + row * a.ldo + head * HD + 8 * part + 4);
+    acc = bf_lo(x.x) * y0.x + bf_hi(x.x) * y0.y + bf_lo(x.y) * y0.z + bf_hi(x.y) * y0.w +
+          bf_lo(x.z) * y1.x + bf_hi(x.z) * y1.y + bf_lo(x.w) * y1.z + bf_hi(x.w) * y1.w;
+  }
+#pragma unroll
+  for (int sh = TPR / 2; sh > 0; sh >>= 1) acc += __shfl_xor(acc, sh);
+  if (ok && part == 0) {
+    const int64_t bq = row / a.S, pos = row % a.S;
+    a.dd[(bq * a.hq + head) * a.S + pos] = acc;
+  }
+}
+
 // ------------------------------------------------------------ backward: dQ
 // Workgroup: 128 queries of one (batch, q head), 4 waves x 32 queries, over the key
 // tiles up to the diagonal: S^T = K Q^T and dP^T = V dO^T (keys x queries), dS, then
@@ -195,23 +222,7 @@ __global__ void __launch_bounds__(256, 2) k_attn_dq(AttnArgs a) {   // two workg
   row_frags<HD>(of, rdo, a.lddo, q, hh);
   const bool qok = q < a.S;
   const float L = qok ? a.lse[(int64_t)bh * a.S + q] : 0.f;
-  // D = rowsum(dO * O) with O in float32 (the product P V before rounding), which is
-  // sum_j P_j dP_j: this lane sums the columns of its dO fragments, its partner lane
-  // (hh ^ 1) the others; written out for the dK / dV kernel
-  float Dp = 0.f;
-  if (qok) {
-    const float* o32 = a.out32 + ((int64_t)b * a.S + q) * a.ldo + h * HD;
-#pragma unroll
-    for (int st = 0; st < NS; ++st) {
-      const uint4 x = __builtin_bit_cast(uint4, of[st]);
-      const float4 y0 = *reinterpret_cast<const float4*>(o32 + 16 * st + 8 * hh);
-      const float4 y1 = *reinterpret_cast<const float4*>(o32 + 16 * st + 8 * hh + 4);
-      Dp += bf_lo(x.x) * y0.x + bf_hi(x.x) * y0.y + bf_lo(x.y) * y0.z + bf_hi(x.y) * y0.w +
-            bf_lo(x.z) * y1.x + bf_hi(x.z) * y1.y + bf_lo(x.w) * y1.z + bf_hi(x.w) * y1.w;
-    }
-  }
-  const float D = Dp + __shfl_xor(Dp, 32);
-  if (qok && hh == 0) a.dd[(int64_t)bh * a.S + q] = D;
+  const float D = qok ? a.dd[(int64_t)bh * a.S + q] : 0.f;
 
   const int last_key = min(qb * 128 + 127, a.S - 1);
   const int n_kb = last_key / KB + 1;
@@ -416,10 +427,12 @@ hipError_t fwd_hd(const AttnArgs& a, hipStream_t s) {
 
 template <int HD>
 hipError_t bwd_hd(const AttnArgs& a, hipStream_t s) {
-  // dQ first: it also writes rowsum(dO * O), which dK / dV reads
-  hipLaunchKernelGGL(k_attn_dq<HD>, dim3((a.S + 127) / 128, a.batch * a.hq), dim3(256), 0, s, a);
+  const int64_t rows = (int64_t)a.batch * a.S * a.hq;
+  const int per_block = 256 / (HD / 8);
+  hipLaunchKernelGGL(k_attn_dd<HD>, dim3((unsigned)((rows + per_block - 1) / per_block)), dim3(256), 0, s, a);
   const int n_half = a.dkv2 ? 2 : 1;
   hipLaunchKernelGGL(k_attn_dkv<HD>, dim3((a.S + KB - 1) / KB * n_half * a.batch * a.hkv), dim3(128), 0, s, a, n_half);
+  hipLaunchKernelGGL(k_attn_dq<HD>, dim3((a.S + 127) / 128, a.batch * a.hq), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
