@@ -877,9 +877,9 @@ __device__ __forceinline__ int xcd_tile(int bid, int nblocks_padded) {
 // tiles a workgroup runs one whole tile (xcd_tile order).  With them, the launch's
 // tiles are n_whole whole tiles (full rounds of the compute units, possibly none) plus
 // a tail of fewer tiles than compute units, each cut into `split` pieces of about
-// nk / split K stages, so the last round is fuller.  Every XCD (bid & 7) gets the same share
-// of both: its first n_whole / 8 workgroups run whole tiles, the rest the pieces of
-// its tail / 8 tail tiles.
+// nk / split K stages, so the last round is fuller.  Every XCD (bid & 7) gets the same
+// share of both: its first n_whole / 8 workgroups run whole tiles, the rest the pieces
+// of its tail / 8 tail tiles (so the pieces of one tile share an XCD).
 struct Piece { int tile, ks, ke, slot, idx; };
 __device__ __forceinline__ Piece piece_of(int total_tiles, int nk, int padded, int n_whole, int split) {
   Piece p;
