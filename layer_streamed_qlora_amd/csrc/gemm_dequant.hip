@@ -670,6 +670,15 @@ struct Epi {
 
 __device__ __forceinline__ float sigmoid_f(float z) { return 1.0f / (1.0f + __expf(-z)); }
 
+// SwiGLU backward of one element: with act = silu(g) u and silu(g) = g sigmoid(g),
+// dgate = y u sigmoid(g) (1 + g (1 - sigmoid(g))) and dup = y g sigmoid(g) for
+// y = d(act).  Both epilogues that run it use this one routine.
+__device__ __forceinline__ void swiglu_bwd(float y, float g, float u, float& dg, float& du) {
+  const float sg = sigmoid_f(g);
+  dg = y * u * sg * (1.0f + g * (1.0f - sg));
+  du = y * g * sg;
+}
+
 template <int NT>
 __device__ __forceinline__ void epilogue(Smem& sm, f32x16_t (&acc)[4][Layout<NT>::JB], int m0, int n0, int M_lim,
                                          int N_lim, const Epi& E) {
@@ -752,11 +761,7 @@ __device__ __forceinline__ void epilogue(Smem& sm, f32x16_t (&acc)[4][Layout<NT>
           const float us[4] = {pre[k][1].x, pre[k][1].y, pre[k][1].z, pre[k][1].w};
           float dg[4], du[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float sg = sigmoid_f(gs[e]);
-            dg[e] = y[e] * us[e] * sg * (1.0f + gs[e] * (1.0f - sg));
-            du[e] = y[e] * gs[e] * sg;
-          }
+          for (int e = 0; e < 4; ++e) swiglu_bwd(y[e], gs[e], us[e], dg[e], du[e]);
           uint16_t* po = reinterpret_cast<uint16_t*>(E.out) + (int64_t)m * E.ldo + n;
           *reinterpret_cast<uint2*>(po) = make_uint2(pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3]));
           *reinterpret_cast<uint2*>(po + N_lim) = make_uint2(pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3]));
@@ -807,10 +812,13 @@ __device__ __forceinline__ void epilogue(Smem& sm, f32x16_t (&acc)[4][Layout<NT>
 
 // SwiGLU forward epilogue of a paired tile: columns 0..127 are gate, 128..255 up, for
 // outputs j0 .. j0 + 127.  act = bf16(silu(g) u); with gu set, g and u are also kept in
-// float32 (gu [M, ldgu], up at column + I).
+// float32 (gu [M, ldgu], up at column + I); with dact set (float32 d(act), [M, ldda]),
+// the SwiGLU backward runs here as well and dgu ([M, lddgu], dup at column + I)
+// receives dgate | dup in bf16.
 template <int NT>
 __device__ __forceinline__ void epilogue_swiglu(Smem& sm, f32x16_t (&acc)[4][Layout<NT>::JB], int m0, int j0, int M_lim,
-                                                int I, uint16_t* act, int ldact, float* gu, int ldgu) {
+                                                int I, uint16_t* act, int ldact, float* gu, int ldgu,
+                                                const float* dact, int ldda, uint16_t* dgu, int lddgu) {
   constexpr int WNW = Layout<NT>::WNW, JB = Layout<NT>::JB;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / WNW, wn = wave % WNW;
@@ -847,6 +855,16 @@ __device__ __forceinline__ void epilogue_swiglu(Smem& sm, f32x16_t (&acc)[4][Lay
       if (gu) {
         *reinterpret_cast<float4*>(gu + (int64_t)m * ldgu + j) = g4;
         *reinterpret_cast<float4*>(gu + (int64_t)m * ldgu + I + j) = u4;
+      }
+      if (dact) {
+        const float4 d4 = *reinterpret_cast<const float4*>(dact + (int64_t)m * ldda + j);
+        const float ys[4] = {d4.x, d4.y, d4.z, d4.w};
+        float dg[4], du[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) swiglu_bwd(ys[e], gs[e], us[e], dg[e], du[e]);
+        uint16_t* po = dgu + (int64_t)m * lddgu + j;
+        *reinterpret_cast<uint2*>(po) = make_uint2(pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3]));
+        *reinterpret_cast<uint2*>(po + I) = make_uint2(pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3]));
       }
     }
   }
@@ -1272,7 +1290,8 @@ __global__ void __launch_bounds__(NT_FAST, 1) k_gemm_fwd_fast(FwdArgs args, int 
     if (pc.slot >= 0 && !combine_pieces<NT_FAST>(acc, args.sk.part, args.sk.cnt, pc.slot, pc.idx, split, &sm.sk_flag))
       return;
     if constexpr (PAIRED) {
-      epilogue_swiglu<NT_FAST>(sm, acc, m0, n0, args.M, n_out, args.y, args.ldy, args.gu32, args.ldgu);
+      epilogue_swiglu<NT_FAST>(sm, acc, m0, n0, args.M, n_out, args.y, args.ldy, args.gu32, args.ldgu, args.dact,
+                               args.ldda, args.dgu, args.lddgu);
     } else {
       Epi E;
       E.f32 = args.y32 != nullptr;
@@ -1478,7 +1497,9 @@ hipError_t launch_gemm_fwd(const FwdArgs& a, hipStream_t s) {
     // paired gate | up tiles: same shape, adjacent low-rank columns, 2 kx <= 64
     if (!fast || a.n_groups != 2 || a.g[0].w.n_out != a.g[1].w.n_out || a.g[0].w.n_in != a.g[1].w.n_in ||
         a.g[0].w.n_out % 4 != 0 || 2 * a.kx > BK || (a.kx > 0 && a.g[1].ext_col0 != a.g[0].ext_col0 + a.kx) ||
-        !a.y || a.y32 || a.resid || a.resid32 || a.rope_tab || a.ldy % 4 != 0 || (a.gu32 && a.ldgu % 4 != 0))
+        !a.y || a.y32 || a.resid || a.resid32 || a.rope_tab || a.ldy % 4 != 0 || (a.gu32 && a.ldgu % 4 != 0) ||
+        (a.dact && (a.gu32 || !a.dgu || a.ldda % 4 != 0 || a.lddgu % 4 != 0 ||
+                    (reinterpret_cast<uintptr_t>(a.dact) & 15) || (reinterpret_cast<uintptr_t>(a.dgu) & 7))))
       return hipErrorInvalidValue;
     const int pt = (a.g[0].w.n_out + BN / 2 - 1) / (BN / 2);
     const int ptotal = m_tiles * pt;
@@ -1491,6 +1512,7 @@ hipError_t launch_gemm_fwd(const FwdArgs& a, hipStream_t s) {
       return hipGetLastError();
     });
   }
+  if (a.dact) return hipErrorInvalidValue;   // the SwiGLU backward rides on the paired tiles only
   int grid = padded, n_whole = total, split = 1;
   if (fast) plan_split(a.sk, total, a.K / BK, grid, n_whole, split);
   return launch_fmt(a.format, [&](auto fmt) {

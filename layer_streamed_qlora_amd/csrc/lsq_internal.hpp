@@ -103,6 +103,11 @@ struct FwdArgs {
   // is set, gate and up in float32 ([M, ldgu], up at column + n_out)
   int32_t swiglu = 0;
   float* gu32 = nullptr; int32_t ldgu = 0;
+  // SwiGLU backward in the same epilogue (the recomputed gate | up, run inside the
+  // backward once d(act) is known): with dact (float32 [M, ldda]) set, dgu (bf16
+  // [M, lddgu], dup at column + n_out) receives dgate | dup; gu32 must then be null
+  const float* dact = nullptr; int32_t ldda = 0;
+  uint16_t* dgu = nullptr; int32_t lddgu = 0;
   SplitTiles sk;
 };
 hipError_t launch_gemm_fwd(const FwdArgs& a, hipStream_t s);

@@ -108,7 +108,9 @@ DevPlan make_plan(const ls_config& c, const BlobLayout& L) {
     P.att[k] = take(2 * T * qd);
     P.hb[k] = take(4 * T * h);        // residual stream after attention, float32
     P.n2[k] = take(2 * T * h);
-    P.gu[k] = take(4 * T * 2 * I);    // gate | up outputs, float32
+    // float32 gate | up outputs, or, with the paired gate | up kernel (2 r16 <= 64),
+    // the down projection's float32 d(act) in the backward
+    P.gu[k] = take(4 * T * (2 * r16 <= 64 ? 1 : 2) * I);
     P.act[k] = take(2 * T * I);
     P.rstd1[k] = take(4 * T);
     P.rstd2[k] = take(4 * T);
@@ -747,12 +749,34 @@ ls_status attn_bwd(ls_ctx* c, const Dims& d, const Acts& x, const uint16_t* dout
 
 enum FwdMode { MODE_FWD = 0, MODE_RECOMPUTE = 1 };
 
-// One decoder layer forward from x_in (bf16 [T, h]).  MODE_FWD writes x_out; the
-// recompute keeps every intermediate and skips the down projection, whose output
-// the backward does not need.
-// One layer's forward (MODE_FWD) or the backward's recompute of it (MODE_RECOMPUTE:
-// no down projection, gate and up kept in float32, attention output kept in float32),
-// every launch on stream s, into the layer's activation set.
+// The gate | up projection of layer l over n2 (bf16 [T, h]): weights, low-rank term
+// (s X A^T columns from hs against the layer's B), levels; outputs are the caller's.
+FwdArgs gate_up_args(ls_ctx* c, int l, const uint8_t* blob, const Dims& d, bool lora, const uint16_t* n2,
+                     const uint16_t* hs) {
+  FwdArgs f;
+  f.x = n2; f.ldx = d.h; f.M = d.T; f.K = d.h; f.n_groups = 2;
+  for (int i = 0; i < 2; ++i) {
+    const int p = LS_PROJ_GATE + i;
+    f.g[i].w = wref(c, blob, p);
+    f.g[i].out_col0 = i * d.I;
+    f.g[i].ext_col0 = p * d.r16;
+    f.g[i].bext = lora && lora_active(c, l, p) ? lora_at(c, l, c->plan.bx16[p]) : nullptr;
+  }
+  f.aext = hs; f.ldaext = d.R7; f.kx = lora ? d.r16 : 0;
+  f.levels = c->dp<float>(c->plan.levels); f.format = wformat(c->cfg);
+  return f;
+}
+
+// SwiGLU rides in the gate | up GEMM's epilogue (paired gate / up tiles) when both
+// low-rank terms fit one 64-column extension
+bool paired_swiglu(const Dims& d) { return 2 * d.r16 <= 64; }
+
+// One decoder layer forward from x_in (bf16 [T, h]), every launch on stream s, into
+// the layer's activation set.  MODE_FWD writes x_out.  MODE_RECOMPUTE (the backward's
+// recompute) keeps the attention output in float32 and skips the down projection,
+// whose output the backward does not need; with the paired gate | up kernel it also
+// stops before gate | up, which the backward runs (layer_backward), and otherwise it
+// keeps gate and up in float32.
 ls_status layer_forward(ls_ctx* c, int l, const uint8_t* blob, const Dims& d, const uint16_t* x_in, uint16_t* x_out,
                         bool lora, FwdMode mode, const Fence& fc, hipStream_t s) {
   const ls_config& g = c->cfg;
@@ -824,30 +848,20 @@ ls_status layer_forward(ls_ctx* c, int l, const uint8_t* blob, const Dims& d, co
     KTimer kt(c, LS_KC_GLUE, 0.0, 2 * tb * d.h, s);
     HIPCHK(c, launch_rmsnorm_fwd(nullptr, hb, g2, n2, x.rstd2, d.T, d.h, g.rms_eps, s));
   }
+  const bool fuse_swiglu = paired_swiglu(d);
+  // with the paired kernel the recompute ends here: the backward runs the gate | up
+  // GEMM itself, once d(act) is known, and does the SwiGLU backward in its epilogue
+  if (mode == MODE_RECOMPUTE && fuse_swiglu) return LS_OK;
   if ((fst = fence_wait(c, fc, 2, s))) return fst;
   if (down) { ls_status st = lora_down(c, l, d, n2, d.h, LS_PROJ_GATE, 2, d.h); if (st) return st; }
-  const bool fuse_swiglu = 2 * d.r16 <= 64;
   {
-    FwdArgs f;
-    f.x = n2; f.ldx = d.h; f.M = d.T; f.K = d.h; f.n_groups = 2;
-    for (int i = 0; i < 2; ++i) {
-      const int p = LS_PROJ_GATE + i;
-      f.g[i].w = wref(c, blob, p);
-      f.g[i].out_col0 = i * d.I;
-      f.g[i].ext_col0 = p * d.r16;
-      f.g[i].bext = lora && lora_active(c, l, p) ? lora_at(c, l, c->plan.bx16[p]) : nullptr;
-    }
-    f.aext = hs; f.ldaext = d.R7; f.kx = lora ? d.r16 : 0;
-    f.levels = lv; f.format = fmt;
-    // SwiGLU in the GEMM's epilogue (paired gate / up tiles) when both low-rank terms
-    // fit one 64-column extension; the recompute also keeps gate and up in float32
+    FwdArgs f = gate_up_args(c, l, blob, d, lora, n2, hs);
     if (fuse_swiglu) {
       f.swiglu = 1; f.y = act; f.ldy = d.I;
-      f.gu32 = mode == MODE_RECOMPUTE ? gu : nullptr; f.ldgu = 2 * d.I;
-    } else {
+    } else {   // the recompute keeps gate and up in float32 for the down projection's dX GEMM
       f.y32 = gu; f.ldy = 2 * d.I;
     }
-    const double out_bytes = fuse_swiglu ? tb * d.I + (mode == MODE_RECOMPUTE ? 2 * tb * 2 * d.I : 0.0) : 2 * tb * 2 * d.I;
+    const double out_bytes = fuse_swiglu ? tb * d.I : 2 * tb * 2 * d.I;
     KTimer kt(c, LS_KC_GEMM_FWD, fwd_gemm_flop(d, 2 * d.I, d.h, lora), tb * d.h + wbytes(c, 4) + wbytes(c, 5) + out_bytes, s);
     f.sk = c->split_scratch(s);
     HIPCHK(c, launch_gemm_fwd(f, s));
@@ -989,8 +1003,14 @@ ls_status layer_backward(ls_ctx* c, int l, const uint8_t* blob, const Dims& d, c
   auto bwd_flop = [&](int n_out, int n_in) { return 2.0 * d.T * n_out * n_in + 2.0 * d.T * n_in * d.r; };
 
   // ---- down: y = h + act W_d^T + LoRA
+  // With the paired gate | up kernel, the recompute stopped before gate | up: the down
+  // projection's dX GEMM writes d(act) in float32 (into the gate | up buffer), then the
+  // gate | up GEMM runs here and its epilogue writes act and, from d(act) and its own
+  // float32 gate and up, dgate | dup.  Otherwise the recompute kept gate and up in
+  // float32 and the dX GEMM's epilogue does the SwiGLU backward from them.
+  const bool fuse_swiglu = paired_swiglu(d);
   if ((st = lora_grads_G(c, l, d, LS_PROJ_DOWN, 1, dy, d.h))) return st;
-  if ((st = lora_grads_AB(c, l, d, LS_PROJ_DOWN, 1, dy, d.h, act, d.I, beta))) return st;
+  if (!fuse_swiglu && (st = lora_grads_AB(c, l, d, LS_PROJ_DOWN, 1, dy, d.h, act, d.I, beta))) return st;
   if ((st = fence_wait(c, fc, 3, c->cs))) return st;
   {
     BwdArgs b;
@@ -998,11 +1018,35 @@ ls_status layer_backward(ls_ctx* c, int l, const uint8_t* blob, const Dims& d, c
     b.seg[0].w = wref(c, blob, LS_PROJ_DOWN); b.seg[0].a_col0 = 0;
     b.aext = gs + LS_PROJ_DOWN * d.r16; b.ldaext = d.R7; b.kx = d.r16;
     b.bext = lora_at(c, l, c->plan.at_d); b.ldbext = d.r16;
-    // SwiGLU backward in the epilogue: dgate | dup from d(act) and the recomputed gate, up
-    b.out16 = dgu; b.ldo = 2 * d.I; b.gu32 = gu; b.ldgu = 2 * d.I; b.levels = lv; b.format = fmt;
-    KTimer kt(c, LS_KC_GEMM_BWD, bwd_flop(d.h, d.I), tb * d.h + wbytes(c, 6) + 2 * tb * 2 * d.I + tb * 2 * d.I);
+    b.levels = lv; b.format = fmt;
+    if (fuse_swiglu) {
+      b.out32 = gu; b.ldo = d.I;
+    } else {
+      b.out16 = dgu; b.ldo = 2 * d.I; b.gu32 = gu; b.ldgu = 2 * d.I;
+    }
+    const double out_bytes = fuse_swiglu ? 2 * tb * d.I : 2 * tb * 2 * d.I + tb * 2 * d.I;
+    KTimer kt(c, LS_KC_GEMM_BWD, bwd_flop(d.h, d.I), tb * d.h + wbytes(c, 6) + out_bytes);
     b.sk = c->split_scratch(c->cs);
     HIPCHK(c, launch_gemm_bwd(b, c->cs));
+  }
+  if (fuse_swiglu) {
+    if ((st = fence_wait(c, fc, 2, c->cs))) return st;
+    {
+      FwdArgs f = gate_up_args(c, l, blob, d, true, n2, hs_of(c, l));
+      f.swiglu = 1; f.y = act; f.ldy = d.I;
+      f.dact = gu; f.ldda = d.I; f.dgu = dgu; f.lddgu = 2 * d.I;
+      // the recompute's GEMM: not one of the forward pass's launches LS_PROFILE_GEMM times
+      c->in_recompute = true;
+      {
+        KTimer kt(c, LS_KC_GEMM_FWD, fwd_gemm_flop(d, 2 * d.I, d.h, true),
+                  tb * d.h + wbytes(c, 4) + wbytes(c, 5) + tb * d.I + 2 * tb * d.I + tb * 2 * d.I);
+        f.sk = c->split_scratch(c->cs);
+        const hipError_t e = launch_gemm_fwd(f, c->cs);
+        c->in_recompute = false;
+        HIPCHK(c, e);
+      }
+    }
+    if ((st = lora_grads_AB(c, l, d, LS_PROJ_DOWN, 1, dy, d.h, act, d.I, beta))) return st;
   }
   // ---- gate / up
   if ((st = lora_grads_G(c, l, d, LS_PROJ_GATE, 2, dgu, 2 * d.I))) return st;
@@ -1451,7 +1495,7 @@ ls_status ls_backward(ls_ctx* c, const void* dY, void* dX, int32_t accumulate) {
     if (!split && (s2 = use_layer(c, l, c->rs))) return s2;
     {
       Span sp(c, c->rs, false);
-      const Fence f{l, split};   // pieces 0 .. 2
+      const Fence f{l, split};   // pieces 0, 1 (and 2 without the paired gate | up kernel)
       c->in_recompute = true;
       s2 = layer_forward(c, l, slot_ptr(c, l), d, ckpt(c, l), nullptr, true, MODE_RECOMPUTE, f, c->rs);
       c->in_recompute = false;
@@ -1476,7 +1520,7 @@ ls_status ls_backward(ls_ctx* c, const void* dY, void* dX, int32_t accumulate) {
     uint16_t* out = l == 0 ? (uint16_t*)dX : ping[l & 1];
     {
       Span sp(c, c->cs, false);
-      const Fence f{l, split};   // piece 3
+      const Fence f{l, split};   // pieces 3 and (with the paired gate | up kernel) 2
       if ((st = layer_backward(c, l, slot_ptr(c, l), d, ckpt(c, l), cur, out, beta, f))) return st;
     }
     if ((st = release_layer(c, l))) return st;
