@@ -60,18 +60,25 @@ __global__ void __launch_bounds__(256) k_attn_fwd(AttnArgs a) {
   const int last_key = min(qb * 128 + 127, a.S - 1);
   const int n_kb = last_key / KB + 1;
   const float cl = a.scale * kLog2e;
-  // scaled scores (base 2) of the key tile at k0 against this lane's query, masked
+  // scaled scores (base 2) of the key tile at k0 against this lane's query, masked; a
+  // tile whose keys all precede the wave's first query needs no mask (same values)
   auto scores = [&](f32x16_t (&s)[2], int k0) {
+    const bool inside = k0 + KB - 1 <= qw && k0 + KB - 1 < a.S;
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       s[kk] = f32x16_t{};
 #pragma unroll
       for (int st = 0; st < NS; ++st)
         s[kk] = mfma(*reinterpret_cast<const bf16x8_t*>(sk + (32 * kk + ql) * PR + 16 * st + 8 * hh), qf[st], s[kk]);
+      if (inside) {
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int key = k0 + 32 * kk + (v >> 2) * 8 + 4 * hh + (v & 3);
-        s[kk][v] = (key <= q && key < a.S) ? s[kk][v] * cl : -INFINITY;
+        for (int v = 0; v < 16; ++v) s[kk][v] = s[kk][v] * cl;
+      } else {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int key = k0 + 32 * kk + (v >> 2) * 8 + 4 * hh + (v & 3);
+          s[kk][v] = (key <= q && key < a.S) ? s[kk][v] * cl : -INFINITY;
+        }
       }
     }
   };
@@ -245,6 +252,7 @@ __global__ void __launch_bounds__(256, 2) k_attn_dq(AttnArgs a) {   // two workg
     }
     const int k0 = kb * KB;
     if (k0 > qw + 31) continue;
+    const bool inside = k0 + KB - 1 <= qw && k0 + KB - 1 < a.S;
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       f32x16_t s = f32x16_t{}, dp = f32x16_t{};
@@ -253,12 +261,20 @@ __global__ void __launch_bounds__(256, 2) k_attn_dq(AttnArgs a) {   // two workg
         s = mfma(*reinterpret_cast<const bf16x8_t*>(sk + (32 * kk + ql) * PR + 16 * st + 8 * hh), qf[st], s);
         dp = mfma(*reinterpret_cast<const bf16x8_t*>(sv + (32 * kk + ql) * PR + 16 * st + 8 * hh), of[st], dp);
       }
+      if (inside) {   // every key of the tile precedes the wave's first query
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int key = k0 + 32 * kk + (v >> 2) * 8 + 4 * hh + (v & 3);
-        const bool ok = qok && key <= q && key < a.S;
-        const float p = ok ? bf16_value(__builtin_amdgcn_exp2f(s[v] * cl - L)) : 0.f;
-        s[v] = a.scale * p * (dp[v] - D);
+        for (int v = 0; v < 16; ++v) {
+          const float p = qok ? bf16_value(__builtin_amdgcn_exp2f(s[v] * cl - L)) : 0.f;
+          s[v] = a.scale * p * (dp[v] - D);
+        }
+      } else {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int key = k0 + 32 * kk + (v >> 2) * 8 + 4 * hh + (v & 3);
+          const bool ok = qok && key <= q && key < a.S;
+          const float p = ok ? bf16_value(__builtin_amdgcn_exp2f(s[v] * cl - L)) : 0.f;
+          s[v] = a.scale * p * (dp[v] - D);
+        }
       }
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
@@ -375,7 +391,9 @@ __global__ void __launch_bounds__(128) k_attn_dkv(AttnArgs a, int n_half) {
         s = mfma(*reinterpret_cast<const bf16x8_t*>(sq + (32 * qs + kl) * PR + 16 * st + 8 * hh), kf[st], s);
         dp = mfma(*reinterpret_cast<const bf16x8_t*>(sdo + (32 * qs + kl) * PR + 16 * st + 8 * hh), vf[st], dp);
       }
-      // C[i = query][j = key]: register v holds query 32 qs + (v / 4) * 8 + 4 hh + v % 4
+      // C[i = query][j = key]: register v holds query 32 qs + (v / 4) * 8 + 4 hh + v % 4;
+      // no mask when every query of the slice follows every key of the wave
+      const bool inside = q0 + 32 * qs >= kw0 + 31 && q0 + 32 * qs + 31 < a.S && kw0 + 31 < a.S;
       f32x16_t ds;
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
@@ -383,13 +401,23 @@ __global__ void __launch_bounds__(128) k_attn_dkv(AttnArgs a, int n_half) {
         const float4 L4 = *reinterpret_cast<const float4*>(&sL[qi]);
         const float4 D4 = *reinterpret_cast<const float4*>(&sD[qi]);
         const float Ls[4] = {L4.x, L4.y, L4.z, L4.w}, Ds[4] = {D4.x, D4.y, D4.z, D4.w};
+        if (inside) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int v = 4 * g4 + e, qg = q0 + qi + e;
-          const bool ok = key <= qg && qg < a.S && key < a.S;
-          const float p = ok ? bf16_value(__builtin_amdgcn_exp2f(s[v] * cl - Ls[e])) : 0.f;
-          s[v] = p;
-          ds[v] = a.scale * p * (dp[v] - Ds[e]);
+          for (int e = 0; e < 4; ++e) {
+            const int v = 4 * g4 + e;
+            const float p = bf16_value(__builtin_amdgcn_exp2f(s[v] * cl - Ls[e]));
+            s[v] = p;
+            ds[v] = a.scale * p * (dp[v] - Ds[e]);
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int v = 4 * g4 + e, qg = q0 + qi + e;
+            const bool ok = key <= qg && qg < a.S && key < a.S;
+            const float p = ok ? bf16_value(__builtin_amdgcn_exp2f(s[v] * cl - Ls[e])) : 0.f;
+            s[v] = p;
+            ds[v] = a.scale * p * (dp[v] - Ds[e]);
+          }
         }
       }
 #pragma unroll
