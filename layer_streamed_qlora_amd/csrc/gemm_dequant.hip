@@ -654,6 +654,64 @@ __device__ __forceinline__ void mma_stage_n(const uint16_t* sa, const uint16_t* 
   }
 }
 
+// Fragments of one k16 step: the wave's 4 row blocks of the activation tile and its JB
+// column blocks of the weight tile.
+template <int NT> struct Frag {
+  bf16x8_t a[4], b[Layout<NT>::JB];
+};
+
+template <int NT>
+__device__ __forceinline__ void read_frag(Frag<NT>& f, const uint16_t* sa, const uint16_t* sw, int kk) {
+  constexpr int WNW = Layout<NT>::WNW, JB = Layout<NT>::JB;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave / WNW, wn = wave % WNW;
+  const uint16_t* pa = sa + (wm * 128 + (lane & 31)) * PITCH + (lane >> 5) * 8 + kk * 16;
+  const uint16_t* pw = sw + (wn * (32 * JB) + (lane & 31)) * PITCH + (lane >> 5) * 8 + kk * 16;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) f.a[i] = *reinterpret_cast<const bf16x8_t*>(pa + i * 32 * PITCH);
+#pragma unroll
+  for (int j = 0; j < JB; ++j) f.b[j] = *reinterpret_cast<const bf16x8_t*>(pw + j * 32 * PITCH);
+}
+
+// One LDS stage whose workgroup barrier comes before its last k16 step, so that no wave
+// starts a stage waiting on LDS.  The fragments of step kk + 1 are read while step kk
+// multiplies.  The next stage's stores (work(q), q = 0..3) go after steps 0, 1, 2 and 2;
+// `sync` (the barrier, and whatever must precede it) follows them, and step 3 then
+// reads the next stage's first fragments from the other buffer (nsa, nsw) while it
+// multiplies.  f[0] holds this stage's step-0 fragments on entry and the next stage's
+// on exit.  Only steps below n_mul multiply (4; the low-rank stage: its non-zero k
+// steps); n_mul is wave-uniform.  The products and their order per accumulator are
+// those of one k16 step after another, as in mma_stage.
+template <int NT, class Work, class Sync>
+__device__ __forceinline__ void mma_stage_early(const uint16_t* sa, const uint16_t* sw, const uint16_t* nsa,
+                                                const uint16_t* nsw, f32x16_t (&acc)[4][Layout<NT>::JB],
+                                                Frag<NT> (&f)[2], int n_mul, Work&& work, Sync&& sync) {
+  constexpr int JB = Layout<NT>::JB;
+#pragma unroll
+  for (int kk = 0; kk < BK / 16; ++kk) {
+    const int c = kk & 1;
+    if (kk + 1 < BK / 16) {
+      if (kk + 1 < n_mul) read_frag<NT>(f[c ^ 1], sa, sw, kk + 1);
+    } else {
+      read_frag<NT>(f[0], nsa, nsw, 0);
+    }
+    if (kk < n_mul) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < JB; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[c].a[i], f[c].b[j], acc[i][j], 0, 0, 0);
+    }
+    if (kk < 2) {
+      work(kk);
+    } else if (kk == 2) {
+      work(2);
+      work(3);
+      sync();
+    }
+  }
+}
+
 // Epilogue through LDS: half a tile (128 rows) at a time, each thread then moves
 // 4 consecutive columns per step with one 8- or 16-byte global access.
 // out(m, n) for m < M_lim, n < N_lim; a bf16 or float32 residual is added first; the
@@ -1251,6 +1309,8 @@ __global__ void __launch_bounds__(NT_FAST, 1) k_gemm_fwd_fast(FwdArgs args, int 
     // head, sets the wait counts of every iteration.
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
     __syncthreads();
+    Frag<NT_FAST> fr[2];
+    read_frag<NT_FAST>(fr[0], sm.u.k.a[0], sm.u.k.w[0], 0);
     // Iteration it dequantises W tile ks + it from R and then reloads R with tile
     // ks + it + 2.  The two register sets alternate by unrolling two iterations: a copy
     // between them would wait on the loads still in flight into the source.  Every
@@ -1260,9 +1320,8 @@ __global__ void __launch_bounds__(NT_FAST, 1) k_gemm_fwd_fast(FwdArgs args, int 
     // steps; the K stages follow in pairs, and an odd count of them gets one padding
     // stage: an activation tile past the piece loads as zeros (out-of-range offset), W
     // past it re-reads the piece's last tile, so the padding stage adds exact zeros.
+    // Each stage's barrier comes before its last k16 step (mma_stage_early).
     auto step = [&](int it, typename WFwdFast<FMT>::Regs& R, auto low_rank) {
-      // let the scheduler interleave the LDS and memory instructions with the MFMAs
-      __builtin_amdgcn_iglp_opt(0);
       const int cur = it & 1;
       uint16_t* na = sm.u.k.a[cur ^ 1];
       uint16_t* nw = sm.u.k.w[cur ^ 1];
@@ -1274,12 +1333,16 @@ __global__ void __launch_bounds__(NT_FAST, 1) k_gemm_fwd_fast(FwdArgs args, int 
         ra.load_q_or_zero((uint32_t)k_next, q, past);
         ws.store_part(R, nw, sm.lut2, q, am);
       };
-      if constexpr (decltype(low_rank)::value)
-        mma_stage_n<NT_FAST>(sm.u.k.a[cur], sm.u.k.w[cur], acc, (ext_cols + 15) / 16, work);
-      else
-        mma_stage<NT_FAST>(sm.u.k.a[cur], sm.u.k.w[cur], acc, work);
-      ws.load(R, k_next + BK < k_last ? k_next + BK : k_last);
-      __syncthreads();
+      auto sync = [&]() {
+        ws.load(R, k_next + BK < k_last ? k_next + BK : k_last);
+        __syncthreads();
+        // let the scheduler interleave the next stage's fragment reads with the last
+        // step's MFMAs (the same hint before the barrier, or with the plain NF4 scales,
+        // costs spilled registers)
+        if constexpr (FMT != WF_NF4) __builtin_amdgcn_iglp_opt(0);
+      };
+      mma_stage_early<NT_FAST>(sm.u.k.a[cur], sm.u.k.w[cur], na, nw, acc, fr,
+                               decltype(low_rank)::value ? (ext_cols + 15) / 16 : BK / 16, work, sync);
     };
     step(0, rw, std::true_type{});
     for (int it = 1; it < n_iter; it += 2) {
