@@ -45,8 +45,10 @@ __global__ void __launch_bounds__(256) k_attn_fwd(AttnArgs a) {
   __shared__ __align__(16) uint16_t sk[KB * PR];
   __shared__ __align__(16) uint16_t svt[HD * PT];
   const int nqb = (a.S + 127) / 128;
-  const int qb = nqb - 1 - (int)blockIdx.x;          // longest rows first
-  const int bh = blockIdx.y, b = bh / a.hq, h = bh % a.hq, g = h / (a.hq / a.hkv);
+  // the grid runs (batch, head) fastest and the query blocks longest first, so every
+  // workgroup of the longest rows is dispatched before any of the next length
+  const int qb = nqb - 1 - (int)blockIdx.y;
+  const int bh = blockIdx.x, b = bh / a.hq, h = bh % a.hq, g = h / (a.hq / a.hkv);
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, ql = lane & 31, hh = lane >> 5;
   const int qw = qb * 128 + 32 * w, q = qw + ql;
   const uint64_t head_bytes = (uint64_t)a.S * a.ldqkv * 2;
@@ -214,8 +216,8 @@ __global__ void __launch_bounds__(256, 2) k_attn_dq(AttnArgs a) {   // two workg
   __shared__ __align__(16) uint16_t sv[KB * PR];
   __shared__ __align__(16) uint16_t skt[HD * PT];
   const int nqb = (a.S + 127) / 128;
-  const int qb = nqb - 1 - (int)blockIdx.x;
-  const int bh = blockIdx.y, b = bh / a.hq, h = bh % a.hq, g = h / (a.hq / a.hkv);
+  const int qb = nqb - 1 - (int)blockIdx.y;   // longest rows first, as in the forward
+  const int bh = blockIdx.x, b = bh / a.hq, h = bh % a.hq, g = h / (a.hq / a.hkv);
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, ql = lane & 31, hh = lane >> 5;
   const int qw = qb * 128 + 32 * w, q = qw + ql;
   const uint64_t head_bytes = (uint64_t)a.S * a.ldqkv * 2;
@@ -449,7 +451,7 @@ __global__ void __launch_bounds__(128) k_attn_dkv(AttnArgs a, int n_half) {
 
 template <int HD>
 hipError_t fwd_hd(const AttnArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(k_attn_fwd<HD>, dim3((a.S + 127) / 128, a.batch * a.hq), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(k_attn_fwd<HD>, dim3(a.batch * a.hq, (a.S + 127) / 128), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -460,7 +462,7 @@ hipError_t bwd_hd(const AttnArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(k_attn_dd<HD>, dim3((unsigned)((rows + per_block - 1) / per_block)), dim3(256), 0, s, a);
   const int n_half = a.dkv2 ? 2 : 1;
   hipLaunchKernelGGL(k_attn_dkv<HD>, dim3((a.S + KB - 1) / KB * n_half * a.batch * a.hkv), dim3(128), 0, s, a, n_half);
-  hipLaunchKernelGGL(k_attn_dq<HD>, dim3((a.S + 127) / 128, a.batch * a.hq), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(k_attn_dq<HD>, dim3(a.batch * a.hq, (a.S + 127) / 128), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
