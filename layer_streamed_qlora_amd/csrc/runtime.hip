@@ -1418,11 +1418,13 @@ ls_status ls_forward(ls_ctx* c, const void* X, int32_t batch, int32_t seq, int32
     // a split layer's pieces are waited for inside the (policy) pass, each before its
     // first reader
     const bool split = n_pieces(c, l) > 1;
+    // the adapters' bf16 copies do not read the layer's blob: they go ahead of the wait
+    // for its copy
+    if (lora && (st = prep_lora(c, l, d))) return st;
     if (!split && (st = use_layer(c, l))) return st;
     {
       Span sp(c, c->cs, false);
       const uint8_t* blob = slot_ptr(c, l);
-      if (lora && (st = prep_lora(c, l, d))) return st;
       uint16_t* out = l + 1 < L ? ckpt(c, l + 1) : (uint16_t*)Y;
       const Fence f1{l, split};
       c->prof_layer = l;
